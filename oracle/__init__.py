@@ -1,0 +1,41 @@
+"""fp64 CPU oracle for the invariant sampled-token logprob forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call, link
+or execute anything in this package.  Its only callers are ``tests/``,
+``__graft_entry__.smoke()`` (to check one small GPU invocation) and the
+``cpu_baseline`` leg of ``bench.py`` (to time it beside the GPU).  It shares no
+code, constants or helpers with the HIP library and imports nothing from it.
+
+What it computes is the plain definition, per sequence *alone* (which is
+itself the batch-invariance reference): plain NumPy in float64; bf16 rounding
+(round-to-nearest-even, straight from float64) only where the numerical
+contract stores a bf16 value; everything else float64.
+
+Sources (cited by page title and section):
+  * "vLLM Achieves Bitwise-Consistent RL Training: Eliminating Numerical Drift
+    to Zero KL Divergence on DeepSeek-V4-Flash at 91% Throughput" -- called
+    "Bitwise-consistent RL post" below;
+  * "zero-mismatch-rl" GitHub README -- called "zero-mismatch-rl README".
+
+Parity status per function is given in each docstring ("pinned by ..." names
+the independent checks in ``tests/test_oracle_pins.py``).
+"""
+
+from .numerics import (  # noqa: F401
+    bf16,
+    widen,
+    rmsnorm,
+    log_softmax_at,
+    lm_head_logprob,
+    attention_row,
+)
+from .models import (  # noqa: F401
+    tiny_decoder_prefill,
+    tiny_decoder_decode,
+    gqa_row_attention,
+    gqa_row_logprob,
+    mla_row_attention,
+    indexer_scores,
+    topk_select,
+)
+from .metrics import diff_stats, k3_mean  # noqa: F401

@@ -1,0 +1,387 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+Every check here is independent of the oracle's own code: closed forms,
+library routines (torch's RNE conversion, scaled_dot_product_attention,
+rms_norm, scipy's log_softmax), brute force on tiny inputs, invariants, and
+the one worked example the pages print (the top-k tie caption).  The
+``test_planted_*`` cases plant a plausible mistake into a copy of an oracle
+function and assert that the matching pin rejects it.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import models as om
+from oracle import numerics as on
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# pin checks (take the implementation under test as an argument)
+# ---------------------------------------------------------------------------
+
+def check_bf16(fn):
+    """fn must equal torch's fp32 -> bf16 round-to-nearest-even on fp32 inputs."""
+    x32 = np.concatenate([
+        RNG.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** RNG.integers(-30, 30, 20000).astype(np.float32),
+        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 1.0 + 2 ** -8 + 2 ** -20,
+                  2 ** -130, 3 * 2 ** -134, 2 ** -149, 0.0, -0.0, 65504.0, 3.3895314e38],
+                 dtype=np.float32),
+    ])
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = fn(x32.astype(np.float64))
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    return bool(np.all(same) and np.array_equal(np.signbit(got), np.signbit(ref)))
+
+
+def check_rmsnorm(fn):
+    g = _golden("closed_forms.json")["rmsnorm_constant"]
+    y = fn(np.full(g["d"], g["c"]), None, g["eps"])
+    if not np.allclose(y, g["expected"], rtol=0, atol=1e-15):
+        return False
+    x = RNG.standard_normal((5, 96))
+    gain = RNG.standard_normal(96)
+    ref = F.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(gain), eps=1e-6).numpy()
+    return bool(np.allclose(fn(x, gain, 1e-6), ref, rtol=1e-13, atol=1e-13))
+
+
+def check_log_softmax(fn):
+    cf = _golden("closed_forms.json")["uniform_logprob"]
+    if fn(np.zeros(2048), 7) != cf["vocab_2048"]:
+        return False
+    if abs(fn(np.zeros(129280), 129279) - cf["vocab_129280"]) > 1e-15:
+        return False
+    l = RNG.standard_normal(3000) * 4
+    ref = scipy.special.log_softmax(l)
+    got = np.array([fn(l, t) for t in range(0, 3000, 7)])
+    if not np.allclose(got, ref[::7], rtol=0, atol=1e-12):
+        return False
+    full = np.array([fn(l, t) for t in range(3000)])
+    return bool(abs(np.exp(full).sum() - 1.0) < 1e-12 and np.all(full <= 0))
+
+
+def check_attention(fn):
+    # one key -> its value exactly
+    v0 = RNG.standard_normal((1, 8))
+    if not np.array_equal(fn(RNG.standard_normal(8), RNG.standard_normal((1, 8)), v0, 0.3), v0[0]):
+        return False
+    # equal keys -> mean of values
+    k = np.tile(RNG.standard_normal(8), (6, 1))
+    V = RNG.standard_normal((6, 8))
+    if not np.allclose(fn(RNG.standard_normal(8), k, V, 0.5), V.mean(0), atol=1e-14):
+        return False
+    # library routine: torch SDPA in float64 (scale passed explicitly)
+    for n, dk, dv, sc in [(7, 16, 16, 0.25), (33, 64, 48, 1 / math.sqrt(64)), (5, 576, 512, 1 / math.sqrt(192))]:
+        q = RNG.standard_normal(dk)
+        K = RNG.standard_normal((n, dk))
+        V = RNG.standard_normal((n, dv))
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None, None, None],
+                                             torch.from_numpy(K)[None, None],
+                                             torch.from_numpy(V)[None, None], scale=sc)[0, 0, 0].numpy()
+        if not np.allclose(fn(q, K, V, sc), ref, rtol=1e-12, atol=1e-12):
+            return False
+    # brute force: per-element Python loops
+    q = RNG.standard_normal(3)
+    K = RNG.standard_normal((4, 3))
+    V = RNG.standard_normal((4, 2))
+    s = [0.7 * sum(q[d] * K[j][d] for d in range(3)) for j in range(4)]
+    e = [math.exp(x) for x in s]
+    bf = [sum(e[j] * V[j][c] for j in range(4)) / sum(e) for c in range(2)]
+    return bool(np.allclose(fn(q, K, V, 0.7), bf, rtol=1e-13, atol=1e-14))
+
+
+def check_gqa_grouping(fn):
+    """Each kv head holds a constant distinct value; q head h must read kv head h*Hkv//Hq."""
+    Hq, Hkv, D, n = 8, 2, 4, 5
+    K = RNG.standard_normal((n, Hkv, D))
+    V = np.zeros((n, Hkv, D))
+    for g in range(Hkv):
+        V[:, g, :] = 10.0 * (g + 1)
+    o = fn(RNG.standard_normal((Hq, D)), K, V, 0.5)
+    want = np.array([[10.0 * (h * Hkv // Hq + 1)] * D for h in range(Hq)])
+    return bool(np.allclose(o, want, atol=1e-12))
+
+
+def check_topk(fn):
+    g = _golden("topk_tie_example.json")
+    s = np.full(g["n"], g["default_score"])
+    for pos, val in g["scores"].items():
+        s[int(pos)] = val
+    if list(fn(s, g["k"], tie="highest")) != g["expected_larger_position_rule"]:
+        return False
+    if list(fn(s, g["k"], tie="lowest")) != g["expected_lowest_index_rule"]:
+        return False
+    p = g["k4_with_padding_n3"]
+    if list(fn(np.array(p["scores"]), p["k"], tie="lowest")) != p["expected_lowest_index_rule"]:
+        return False
+    # brute force on small integer-valued scores (many ties)
+    for n, k in [(40, 7), (100, 33), (16, 16), (9, 12)]:
+        s = RNG.integers(0, 5, n).astype(np.float64)
+        ranked = sorted(range(n), key=lambda j: (-s[j], j))[:k]
+        want = sorted(ranked, reverse=True) + [-1] * (k - min(k, n))
+        if list(fn(s, k, tie="lowest")) != want:
+            return False
+    return True
+
+
+def check_tiny_prefill_vs_decode(prefill, decode):
+    """Brute-force tiny decoders: prefill and token-by-token decode agree to 1e-12."""
+    for (L, d, Hq, Hkv, D, V, n_prompt, seed) in [(9, 16, 2, 1, 8, 11, 3, 1), (12, 32, 4, 2, 8, 29, 1, 2),
+                                                 (7, 16, 2, 2, 8, 13, 7, 3)]:
+        r = np.random.default_rng(seed)
+        p = {
+            "embed": on.bf16(r.standard_normal((V, d)) * 0.5),
+            "w_qkv": on.bf16(r.standard_normal(((Hq + 2 * Hkv) * D, d)) * 0.3),
+            "w_o": on.bf16(r.standard_normal((d, Hq * D)) * 0.3),
+            "norm_attn": np.ones(d), "norm_final": on.bf16(1 + 0.1 * r.standard_normal(d)),
+            "w_lm": on.bf16(r.standard_normal((V, d)) * 0.3),
+        }
+        tok = r.integers(0, V, L)
+        tgt = r.integers(0, V, L)
+        a = prefill(p, tok, tgt, Hq, Hkv, D)
+        b = decode(p, tok, tgt, n_prompt, Hq, Hkv, D)
+        if a.shape != (L,) or not np.allclose(a, b, rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+# ---------------------------------------------------------------------------
+# pins on the real oracle
+# ---------------------------------------------------------------------------
+
+def test_bf16_matches_torch_rne():
+    assert check_bf16(oracle.bf16)
+
+
+def test_bf16_direct_from_float64_ties():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even -> 1; a hair above rounds up.
+    assert oracle.bf16(1.0 + 2 ** -8) == 1.0
+    assert oracle.bf16(1.0 + 2 ** -8 + 2 ** -40) == 1.0 + 2 ** -7
+    assert oracle.bf16(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6
+    assert oracle.bf16(2.0 ** 200) == np.inf
+
+
+def test_rmsnorm_pins():
+    assert check_rmsnorm(oracle.rmsnorm)
+
+
+def test_log_softmax_pins():
+    assert check_log_softmax(oracle.log_softmax_at)
+
+
+def test_lm_head_uniform_when_weights_zero():
+    cf = _golden("closed_forms.json")["uniform_logprob"]
+    z = oracle.bf16(RNG.standard_normal(256))
+    assert oracle.lm_head_logprob(z, np.zeros((2048, 256), np.float32), 5, chunk=300) == cf["vocab_2048"]
+
+
+def test_lm_head_integer_inputs_exact():
+    # integer-valued logits: the float64 sum is exact, so lm_head_logprob equals the
+    # closed form computed from an exact integer matmul.
+    W = RNG.integers(-2, 3, (50, 64)).astype(np.float32)
+    z = RNG.integers(-2, 3, 64).astype(np.float64)
+    logits = (W.astype(np.int64) @ z.astype(np.int64)).astype(np.float64)
+    want = float(logits[3] - scipy.special.logsumexp(logits))
+    assert abs(oracle.lm_head_logprob(z, W, 3, chunk=7) - want) < 1e-12
+
+
+def test_attention_pins():
+    assert check_attention(oracle.attention_row)
+
+
+def test_gqa_grouping_pin():
+    assert check_gqa_grouping(oracle.gqa_row_attention)
+
+
+def test_gqa_row_logprob_matches_sdpa_composition():
+    # Attention via torch SDPA (enable_gqa) in float64, the rest as the contract says.
+    Hq, Hkv, D, n, V = 8, 2, 16, 37, 300
+    q = oracle.bf16(RNG.standard_normal((Hq, D)))
+    K = oracle.bf16(RNG.standard_normal((n, Hkv, D)))
+    Vv = oracle.bf16(RNG.standard_normal((n, Hkv, D)))
+    W = oracle.bf16(RNG.standard_normal((V, Hq * D)) * 0.05)
+    o = F.scaled_dot_product_attention(torch.from_numpy(q)[None, :, None],
+                                       torch.from_numpy(K).permute(1, 0, 2)[None],
+                                       torch.from_numpy(Vv).permute(1, 0, 2)[None],
+                                       scale=0.25, enable_gqa=True)[0, :, 0].numpy()
+    z = oracle.bf16(F.rms_norm(torch.from_numpy(oracle.bf16(o).reshape(-1)), (Hq * D,), eps=1e-6).numpy())
+    want = float(torch.log_softmax(torch.from_numpy(W @ z), 0)[17])
+    assert abs(oracle.gqa_row_logprob(q, K, Vv, 0.25, W, 17) - want) < 1e-12
+
+
+def test_gqa_row_with_output_projection_zero():
+    # W_o = 0 -> the normalised input is 0 -> uniform logprob.
+    q = oracle.bf16(RNG.standard_normal((4, 8)))
+    K = oracle.bf16(RNG.standard_normal((3, 2, 8)))
+    lp = oracle.gqa_row_logprob(q, K, K, 0.3, RNG.standard_normal((2048, 16)), 9,
+                                w_o=np.zeros((16, 32)))
+    assert abs(lp - _golden("closed_forms.json")["uniform_logprob"]["vocab_2048"]) < 1e-12
+
+
+def test_mla_matches_sdpa():
+    H, dqk, dv, n = 3, 576, 512, 19
+    q = oracle.bf16(RNG.standard_normal((H, dqk)))
+    C = oracle.bf16(RNG.standard_normal((n, dqk)))
+    sc = 1 / math.sqrt(192)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[:, None], torch.from_numpy(C)[None].expand(H, n, dqk),
+                                         torch.from_numpy(C[:, :dv])[None].expand(H, n, dv), scale=sc)[:, 0].numpy()
+    assert np.allclose(oracle.mla_row_attention(q, C, sc, dv), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_brute_force():
+    q = RNG.standard_normal((3, 4))
+    K = RNG.standard_normal((6, 4))
+    want = [sum(max(0.0, sum(q[h][d] * K[s][d] for d in range(4))) for h in range(3)) for s in range(6)]
+    assert np.allclose(oracle.indexer_scores(q, K), want, rtol=1e-14, atol=1e-14)
+
+
+def test_topk_pins():
+    assert check_topk(oracle.topk_select)
+
+
+def test_tiny_decoder_prefill_equals_decode():
+    assert check_tiny_prefill_vs_decode(oracle.tiny_decoder_prefill, oracle.tiny_decoder_decode)
+
+
+def test_tiny_decoder_zero_projection_closed_form():
+    # Wq = Wk = 0 -> uniform attention; W_o = 0 -> y = x; then z = bf16(rms(E[t])) and the
+    # logprob is the plain log-softmax of z . W_lm, checked with scipy.
+    w = wl.TinyDecoder(d_model=32, n_q_heads=2, n_kv_heads=2, head_dim=8, vocab=40, lengths=(6,))
+    p = {k: oracle.widen(v) for k, v in wl.tiny_weights(w).items()}
+    p["w_o"] = np.zeros_like(p["w_o"])
+    tok = np.array([3, 1, 4, 1, 5, 9])
+    tgt = np.array([1, 4, 1, 5, 9, 2])
+    lp = oracle.tiny_decoder_prefill(p, tok, tgt, 2, 2, 8)
+    z = oracle.bf16(oracle.bf16(p["embed"][tok]) / np.sqrt(np.mean(p["embed"][tok] ** 2, 1, keepdims=True) + 1e-6))
+    ref = scipy.special.log_softmax(z @ p["w_lm"].T, axis=1)[np.arange(6), tgt]
+    assert np.allclose(lp, ref, rtol=0, atol=1e-12)
+
+
+def test_metrics_closed_forms():
+    cf = _golden("closed_forms.json")["k3"]
+    a = RNG.standard_normal(100)
+    s = oracle.diff_stats(a, a)
+    assert s["max"] == s["mean"] == s["std"] == s["p_max"] == 0.0
+    assert oracle.k3_mean(a, a) == 0.0
+    assert abs(oracle.k3_mean(np.array([math.log(2.0)]), np.array([0.0])) - cf["delta_ln2"]) < 1e-15
+    d = oracle.diff_stats(np.array([0.0, -1.0]), np.array([-0.5, -1.0]))
+    assert d["max"] == 0.5 and d["mean"] == 0.25 and d["std"] == 0.25
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each pin must reject a plausible bug
+# ---------------------------------------------------------------------------
+
+def test_planted_bf16_truncation_is_caught():
+    def trunc(x):
+        x = np.asarray(x, np.float64)
+        _, E = np.frexp(x)
+        q = np.ldexp(1.0, np.maximum(E - 1, -126) - 7)
+        return np.trunc(x / q) * q
+    assert not check_bf16(trunc)
+
+
+def test_planted_bf16_via_float16_is_caught():
+    with np.errstate(over='ignore'):
+        assert not check_bf16(lambda x: np.asarray(x, np.float16).astype(np.float64))
+
+
+def test_planted_rmsnorm_without_eps_is_caught():
+    def bad(x, gain=None, eps=1e-6):
+        return on.rmsnorm(x, gain, 0.0)
+    assert not check_rmsnorm(bad)
+
+
+def test_planted_rmsnorm_mean_abs_is_caught():
+    def bad(x, gain=None, eps=1e-6):
+        x = np.asarray(x, np.float64)
+        y = x / (np.mean(np.abs(x), -1, keepdims=True) + eps)
+        return y if gain is None else y * gain
+    assert not check_rmsnorm(bad)
+
+
+def test_planted_log_softmax_missing_max_shift_sign_is_caught():
+    def bad(l, t):
+        l = np.asarray(l, np.float64)
+        m = l.max()
+        return float(l[t] - m - np.log(np.sum(np.exp(l + m))))
+    assert not check_log_softmax(bad)
+
+
+def test_planted_attention_wrong_scale_is_caught():
+    assert not check_attention(lambda q, K, V, sc: on.attention_row(q, K, V, sc * sc))
+
+
+def test_planted_attention_values_from_keys_is_caught():
+    def bad(q, K, V, sc):
+        K = np.asarray(K, np.float64)
+        return on.attention_row(q, K, K[:, : np.shape(V)[1]], sc)
+    assert not check_attention(bad)
+
+
+def test_planted_attention_softmax_without_normalisation_is_caught():
+    def bad(q, K, V, sc):
+        s = sc * (np.asarray(K) @ np.asarray(q))
+        return np.exp(s - s.max()) @ np.asarray(V)
+    assert not check_attention(bad)
+
+
+def test_planted_interleaved_grouping_is_caught():
+    def bad(q, K, V, sc):
+        q, K, V = map(np.asarray, (q, K, V))
+        return np.stack([on.attention_row(q[h], K[:, h % K.shape[1]], V[:, h % K.shape[1]], sc)
+                         for h in range(q.shape[0])])
+    assert not check_gqa_grouping(bad)
+
+
+def test_planted_topk_reversed_tie_is_caught():
+    def bad(s, k, tie="lowest"):
+        return om.topk_select(s, k, tie={"lowest": "highest", "highest": "lowest"}[tie])
+    assert not check_topk(bad)
+
+
+def test_planted_topk_ascending_order_is_caught():
+    def bad(s, k, tie="lowest"):
+        out = om.topk_select(s, k, tie)
+        v = np.sort(out[out >= 0])
+        return np.concatenate([v, out[out < 0]])
+    assert not check_topk(bad)
+
+
+def test_planted_causal_off_by_one_is_caught():
+    def bad_prefill(params, tokens, targets, Hq, Hkv, D, eps=1e-6):
+        # attends to one position fewer than allowed (excludes itself)
+        real = on.attention_row
+
+        def shifted(q, K, V, sc):
+            return real(q, K[:-1], V[:-1], sc) if K.shape[0] > 1 else real(q, K, V, sc)
+        om.attention_row = shifted
+        try:
+            return om.tiny_decoder_prefill(params, tokens, targets, Hq, Hkv, D, eps)
+        finally:
+            om.attention_row = real
+    assert not check_tiny_prefill_vs_decode(bad_prefill, oracle.tiny_decoder_decode)
+
+
+def test_planted_residual_dropped_is_caught():
+    def bad_decode(params, tokens, targets, n_prompt, Hq, Hkv, D, eps=1e-6):
+        p = dict(params)
+        p["w_o"] = np.asarray(params["w_o"]) * 0.0
+        return om.tiny_decoder_decode(p, tokens, targets, n_prompt, Hq, Hkv, D, eps)
+    assert not check_tiny_prefill_vs_decode(oracle.tiny_decoder_prefill, bad_decode)

@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs for the invariant-logprob path.
+
+This module is the one place that both the GPU path's tests/bench and the
+fp64 oracle draw their inputs from.  It holds none of the method's arithmetic:
+it only draws random numbers, rounds them to the storage type, and describes the
+workload shapes.
+
+Every tensor is keyed by (workload seed, tensor kind, sequence id[, extra]),
+never by a batch slot, so a sequence receives the same data in every batch it
+is placed in (a requirement for the batch-invariance checks: the data generator
+must not leak batch position into the values).
+
+Random draws use ``torch.Generator`` seeded from a SplitMix64 hash of the key.
+The draws are made on whichever device the caller asks for; CPU and GPU draws
+differ (different engines), so a test generates once and copies the exact bf16
+bits to the other side.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Sequence, Tuple
+
+import torch
+
+_MASK64 = (1 << 64) - 1
+
+
+def _splitmix64(x: int) -> int:
+    x = (x + 0x9E3779B97F4A7C15) & _MASK64
+    z = x
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+    return z ^ (z >> 31)
+
+
+def key(*parts) -> int:
+    """Stable 63-bit key from ints and strings (order-sensitive)."""
+    h = 0x1234_5678_9ABC_DEF0
+    for p in parts:
+        if isinstance(p, str):
+            v = 0
+            for ch in p.encode():
+                v = ((v * 131) + ch) & _MASK64
+        else:
+            v = int(p) & _MASK64
+        h = _splitmix64(h ^ v)
+    return h & ((1 << 63) - 1)
+
+
+def _gen(k: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(k)
+    return g
+
+
+def randn(shape, k: int, std: float = 1.0, device="cpu", dtype=torch.bfloat16) -> torch.Tensor:
+    """N(0, std^2) draws rounded (RNE) to ``dtype``; keyed by ``k``."""
+    x = torch.randn(tuple(shape), generator=_gen(k, device), device=device, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(dtype)
+
+
+def randint(lo: int, hi_inclusive: int, shape, k: int, device="cpu") -> torch.Tensor:
+    """Uniform integers in [lo, hi_inclusive] (int32); keyed by ``k``."""
+    return torch.randint(lo, hi_inclusive + 1, tuple(shape), generator=_gen(k, device),
+                         device=device, dtype=torch.int64).to(torch.int32)
+
+
+# --------------------------------------------------------------------------
+# Workload shapes.  Names say what the workload is; sizes are the workloads'.
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class TinyDecoder:
+    """One pre-norm decoder layer + final RMSNorm + lm-head, token input."""
+    d_model: int = 256
+    n_q_heads: int = 4
+    n_kv_heads: int = 4
+    head_dim: int = 64
+    vocab: int = 2048
+    lengths: Tuple[int, ...] = (33, 64, 97, 128)
+    prompt_tokens: int = 16
+    init_std: float = 0.02
+    rms_eps: float = 1e-6
+    page_tokens: int = 16
+    seed: int = 0
+
+
+@dataclasses.dataclass(frozen=True)
+class GQADecode:
+    """Paged GQA decode rows with q/K/V given, attention output -> RMSNorm -> lm-head."""
+    rows: int = 64
+    n_q_heads: int = 32
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    ctx_lo: int = 512
+    ctx_hi: int = 8192
+    vocab: int = 129280
+    d_head: int = 4096
+    o_proj_out: int = 0          # 0: no output projection before the final norm
+    init_std: float = 0.02
+    rms_eps: float = 1e-6
+    page_tokens: int = 16
+    recompute_tokens: int = 64   # q is drawn for the last this-many positions of each row
+    seed: int = 1
+
+
+TINY = TinyDecoder()
+GQA_DECODE_B64 = GQADecode()
+# Long-context GQA (64 q / 8 kv heads) with an 8192 -> 4096 output projection.
+GQA_LONG = GQADecode(rows=256, n_q_heads=64, n_kv_heads=8, head_dim=128, ctx_lo=1024,
+                     ctx_hi=131072, vocab=129280, d_head=4096, o_proj_out=4096, seed=4)
+
+
+# --------------------------------------------------------------------------
+# Tiny decoder inputs
+# --------------------------------------------------------------------------
+
+def tiny_weights(w: TinyDecoder = TINY, device="cpu") -> Dict[str, torch.Tensor]:
+    """bf16 weights in nn.Linear layout ([out, in]); RMSNorm gains are 1."""
+    d, hq, hkv, hd, v = w.d_model, w.n_q_heads, w.n_kv_heads, w.head_dim, w.vocab
+    s = w.seed
+    return {
+        "embed": randn((v, d), key(s, "embed"), w.init_std, device),
+        "w_qkv": randn(((hq + 2 * hkv) * hd, d), key(s, "w_qkv"), w.init_std, device),
+        "w_o": randn((d, hq * hd), key(s, "w_o"), w.init_std, device),
+        "norm_attn": torch.ones(d, dtype=torch.bfloat16, device=device),
+        "norm_final": torch.ones(d, dtype=torch.bfloat16, device=device),
+        "w_lm": randn((v, d), key(s, "w_lm"), w.init_std, device),
+    }
+
+
+def tiny_tokens(seq_id: int, w: TinyDecoder = TINY, device="cpu") -> torch.Tensor:
+    """Token ids of sequence ``seq_id`` (length ``w.lengths[seq_id]``), uniform in [0, vocab)."""
+    n = w.lengths[seq_id]
+    return randint(0, w.vocab - 1, (n,), key(w.seed, "tokens", seq_id), device)
+
+
+# --------------------------------------------------------------------------
+# GQA decode rows
+# --------------------------------------------------------------------------
+
+def gqa_ctx(row: int, w: GQADecode = GQA_DECODE_B64) -> int:
+    """Context length of row ``row`` (including the token being decoded)."""
+    return int(randint(w.ctx_lo, w.ctx_hi, (1,), key(w.seed, "ctx", row))[0])
+
+
+def gqa_head_weights(w: GQADecode = GQA_DECODE_B64, device="cpu") -> Dict[str, torch.Tensor]:
+    out = {"w_lm": randn((w.vocab, w.d_head), key(w.seed, "w_lm"), w.init_std, device)}
+    if w.o_proj_out:
+        out["w_o"] = randn((w.o_proj_out, w.n_q_heads * w.head_dim), key(w.seed, "w_o"),
+                           w.init_std, device)
+    return out
+
+
+def gqa_row(row: int, w: GQADecode = GQA_DECODE_B64, device="cpu", ctx: int = None):
+    """Data of one row: K, V for every position, q and targets for the last positions.
+
+    Returns dict(ctx, k [ctx, Hkv, D], v [ctx, Hkv, D], q [R, Hq, D], target [R]) where
+    q[j] and target[j] belong to position ctx - R + j (R = recompute_tokens, clipped to ctx).
+    """
+    L = gqa_ctx(row, w) if ctx is None else int(ctx)
+    R = min(w.recompute_tokens, L)
+    s = w.seed
+    return {
+        "ctx": L,
+        "k": randn((L, w.n_kv_heads, w.head_dim), key(s, "k", row, L), 1.0, device),
+        "v": randn((L, w.n_kv_heads, w.head_dim), key(s, "v", row, L), 1.0, device),
+        "q": randn((R, w.n_q_heads, w.head_dim), key(s, "q", row, L), 1.0, device),
+        "target": randint(0, w.vocab - 1, (R,), key(s, "target", row, L), device),
+    }
+
+
+def scaled(w: GQADecode, **changes) -> GQADecode:
+    """A smaller variant of a workload for oracle-sized parity runs."""
+    return dataclasses.replace(w, **changes)
+
