@@ -1,0 +1,201 @@
+/*
+ * ril.h -- C ABI of the invariant sampled-token logprob forward on MI355X (gfx950).
+ *
+ * What it computes.  For every token it is given, the library returns the fp32
+ * logprob of that token's target id under one attention layer followed by an
+ * RMSNorm and an lm-head with a log-softmax over the vocabulary.  The value is
+ * bitwise identical whether the token comes through prefill_logprobs (a
+ * whole-prefix or chunked pass: the trainer's recompute) or through
+ * decode_step_logprobs (one token per row: the rollout), and whatever batch,
+ * row order, page placement or prefill chunk size it is computed with.  This
+ * is the "diff = 0" contract of "vLLM Achieves Bitwise-Consistent RL
+ * Training" (section 2: kernel determinism, batch independence and phase
+ * consistency; section 3.1: the same kernels define the values on both
+ * sides).
+ *
+ * How: one numerical path shared by both entry points -- a paged KV cache with
+ * one write path (section 4.2), attention whose KV split is a fixed number of
+ * tokens (the zero-mismatch-rl README, key-features table: fixed-split
+ * attention), split states merged left to right in split order, GEMMs with one
+ * MFMA instruction and one K order for every M and no split-K (section 4.1),
+ * and a vocabulary log-softmax reduced over fixed 256-column tiles in a fixed
+ * tree, gathering the target's logit.
+ *
+ * Conventions for every entry point.
+ *   Ownership: the caller owns every device buffer (weights, KV pool, page
+ *     tables, inputs, outputs, workspace) and the stream.  The library never
+ *     allocates or frees device memory, never synchronises the stream or the
+ *     device, and never reads device memory from the host.  Device pointers
+ *     must stay valid until the enqueued work has completed.
+ *   Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream).  All work of a call is enqueued on it in order.
+ *   Errors: every argument is validated on the host before anything is
+ *     enqueued; on any status other than RIL_OK nothing has been enqueued,
+ *     except RIL_EHIP (a launch failed: earlier kernels of the call may have
+ *     been enqueued).  ril_last_error() returns a thread-local message for the
+ *     last failing call.  Device-side values the host cannot check (a page id
+ *     outside the pool, a context beyond the call's bound) never cause an
+ *     out-of-bounds access: the affected row's logprob is written as NaN.
+ *   Threading: handles are not thread-safe; distinct handles may be used from
+ *     different threads.
+ *   Alignment: every device pointer must be 16-byte aligned.
+ *   Layouts are row-major; bf16 is IEEE bfloat16 stored as uint16.
+ */
+#ifndef RIL_H
+#define RIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ril_status {
+  RIL_OK = 0,
+  RIL_EINVAL = -1,        /* a pointer, size or layout argument is invalid */
+  RIL_ERANGE = -2,        /* a size exceeds a limit fixed at model_create */
+  RIL_ENOSPC = -3,        /* the KV pool has too few free pages */
+  RIL_EUNSUPPORTED = -4,  /* a valid configuration this build does not implement */
+  RIL_EHIP = -5           /* the HIP runtime reported an error */
+} ril_status;
+
+enum { RIL_ATTN_GQA = 0 };
+enum { RIL_INPUT_TOKENS = 0, RIL_INPUT_QKV = 1 };
+
+/* Model description.  All sizes are fixed for the life of the handle; the
+ * split and page sizes are model constants, never derived from a batch, a
+ * context length or the GPU (Bitwise-consistent RL post, section 2: no
+ * kernel choice by batch size, no dynamic split count).                     */
+typedef struct ril_model_desc {
+  int32_t attn_kind;     /* RIL_ATTN_GQA */
+  int32_t input_mode;    /* RIL_INPUT_TOKENS: token ids -> embedding -> RMSNorm -> QKV GEMM
+                            -> attention -> O GEMM + residual -> RMSNorm -> lm-head;
+                            RIL_INPUT_QKV: q/k/v given -> attention -> [O GEMM] -> RMSNorm
+                            -> lm-head */
+  int32_t d_model;       /* TOKENS: residual width (multiple of 32); QKV: ignored */
+  int32_t n_q_heads;     /* Hq */
+  int32_t n_kv_heads;    /* Hkv; Hq/Hkv must be 1, 2, 4, 8 or 16 (q head h reads kv head h*Hkv/Hq) */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t d_head;        /* width the final RMSNorm and lm-head consume (multiple of 32):
+                            TOKENS: = d_model; QKV: = o-proj out width if w_o, else Hq*D */
+  int32_t vocab;         /* V >= 1 */
+  int32_t page_tokens;   /* tokens per KV page: 16 */
+  int32_t split_tokens;  /* attention KV split in tokens: a multiple of 64 (512 by default) */
+  int32_t max_rows;      /* most rows one decode call may carry */
+  int32_t max_tokens;    /* most tokens one prefill call may carry */
+  int32_t max_ctx;       /* longest context (tokens, including the current one) */
+  float softmax_scale;   /* multiplies q.k (1/sqrt(D) for the workloads here) */
+  float rms_eps;         /* RMSNorm epsilon */
+  /* device weights, bf16, nn.Linear layout [out, in]; caller-owned */
+  const void *embed;      /* [V, d_model]                   TOKENS only            */
+  const void *w_qkv;      /* [(Hq + 2 Hkv) D, d_model]      TOKENS only: q|k|v rows */
+  const void *w_o;        /* [d_head, Hq D]                 TOKENS: required; QKV: optional */
+  const void *norm_attn;  /* [d_model] RMSNorm gain          TOKENS only; NULL = 1   */
+  const void *norm_final; /* [d_head]  RMSNorm gain          NULL = 1                */
+  const void *w_lm;       /* [V, d_head]                     required                */
+} ril_model_desc;
+
+typedef struct ril_model ril_model;  /* opaque: copy of the description + derived sizes */
+typedef struct ril_kv ril_kv;        /* opaque: KV pool pointer + host free list */
+
+/* Create a model handle.  Validates the description (sizes, required weight
+ * pointers, alignment).  The weights are referenced, not copied. */
+ril_status ril_model_create(const ril_model_desc *desc, ril_model **out);
+void ril_model_destroy(ril_model *m);
+
+/* Bytes of device workspace every prefill/decode call on `m` needs.  Depends
+ * only on the model's static limits (section 4.6 of the post: workspaces are
+ * sized by model limits so they can be allocated once, before capture). */
+size_t ril_workspace_bytes(const ril_model *m);
+
+/* Bytes of one KV page: Hkv x 2 (K, V) x page_tokens x D x 2 bytes. */
+size_t ril_kv_page_bytes(const ril_model *m);
+
+/* S1: page assignment.  Wrap a caller-owned device pool of `pool_bytes`
+ * bytes (16-byte aligned) as floor(pool_bytes / page_bytes) pages and build a
+ * host free list over them.  shuffle_seed != 0 permutes the free list with a
+ * seeded Fisher-Yates shuffle (random page tables); 0 hands pages out in
+ * order.  Launches nothing. */
+ril_status ril_kv_alloc(const ril_model *m, void *pool_dev, size_t pool_bytes,
+                        uint64_t shuffle_seed, ril_kv **out);
+/* Take `n_pages` pages off the free list; their ids are written to the host
+ * array `page_ids_out`.  RIL_ENOSPC (and nothing taken) if fewer are free. */
+ril_status ril_kv_assign(ril_kv *kv, int32_t n_pages, int32_t *page_ids_out);
+/* Return pages to the free list.  RIL_EINVAL (and nothing returned) if an id
+ * is out of range or not currently assigned. */
+ril_status ril_kv_release(ril_kv *kv, int32_t n_pages, const int32_t *page_ids);
+int32_t ril_kv_free_pages(const ril_kv *kv);
+int32_t ril_kv_total_pages(const ril_kv *kv);
+void ril_kv_free(ril_kv *kv);
+
+/* A prefill batch: n_seqs sequences, each contributing a contiguous run of
+ * tokens at consecutive positions start_pos[s], start_pos[s]+1, ...
+ * Tokens are packed: sequence s owns tokens cu_tokens[s] .. cu_tokens[s+1]-1.
+ * A one-token sequence is exactly a decode row, so a mixed continuous batch
+ * (prefill chunks + decode rows) is one prefill call.
+ * Every position before start_pos[s] must already be in the KV cache (written
+ * by an earlier prefill/decode call or by ril_kv_write). */
+typedef struct ril_prefill_batch {
+  int32_t n_seqs;           /* 1 .. max_rows */
+  int32_t total_tokens;     /* host copy of cu_tokens[n_seqs]: 1 .. max_tokens */
+  int32_t max_ctx_bound;    /* host upper bound on start_pos[s] + len_s over the batch
+                               (<= model max_ctx); grids are sized from it */
+  const int32_t *cu_tokens; /* device [n_seqs + 1], cu_tokens[0] = 0, non-decreasing */
+  const int32_t *start_pos; /* device [n_seqs] */
+  const int32_t *page_table;/* device [n_seqs, page_stride]: page ids of positions
+                               16j .. 16j+15 of sequence s at [s * page_stride + j] */
+  int32_t page_stride;      /* >= ceil(max_ctx_bound / page_tokens) */
+  const int32_t *target_ids;/* device [total_tokens]: id whose logprob is returned */
+  const int32_t *token_ids; /* TOKENS: device [total_tokens] */
+  const void *q;            /* QKV: device bf16 [total_tokens, Hq, D] */
+  const void *k;            /* QKV: device bf16 [total_tokens, Hkv, D] */
+  const void *v;            /* QKV: device bf16 [total_tokens, Hkv, D] */
+} ril_prefill_batch;
+
+/* A decode batch: n_rows rows, one new token each, at position ctx_len[r]-1. */
+typedef struct ril_decode_batch {
+  int32_t n_rows;           /* 1 .. max_rows */
+  int32_t max_ctx_bound;    /* host upper bound on ctx_len[r] (<= model max_ctx) */
+  const int32_t *ctx_len;   /* device [n_rows]: context including the new token, >= 1 */
+  const int32_t *page_table;/* device [n_rows, page_stride] */
+  int32_t page_stride;      /* >= ceil(max_ctx_bound / page_tokens) */
+  const int32_t *target_ids;/* device [n_rows] */
+  const int32_t *token_ids; /* TOKENS: device [n_rows] */
+  const void *q;            /* QKV: device bf16 [n_rows, Hq, D] */
+  const void *k;            /* QKV: device bf16 [n_rows, Hkv, D] (the new token's) */
+  const void *v;            /* QKV: device bf16 [n_rows, Hkv, D] */
+} ril_decode_batch;
+
+/* Trainer-side recompute: writes every batch token's K/V into its page
+ * (S5), attends causally over the cache (S10), then the head (S4, S3, S11,
+ * S12).  logprob_out: device fp32 [total_tokens].  ws: device workspace of at
+ * least ril_workspace_bytes(m) bytes. */
+ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b,
+                                float *logprob_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Rollout-side step: writes each row's new K/V into its page (S5), attends
+ * over the row's ctx_len[r] positions with fixed-size splits (S8) merged in
+ * split order (S9), then the head.  logprob_out: device fp32 [n_rows]. */
+ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                    float *logprob_out, void *ws, size_t ws_bytes, void *stream);
+
+/* The shared KV write path alone (S5): writes the batch's k/v (QKV layout
+ * of ril_prefill_batch; target_ids, token_ids and q are ignored) into the
+ * pages, nothing else.  Used to lay down history that no logprob is asked
+ * for.  Needs no workspace, so n_seqs and total_tokens are not bounded by
+ * max_tokens. */
+ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b, void *stream);
+
+/* Debug/test view: the attention output of the last call on this thread's
+ * workspace is bf16 [rows, Hq, D] at byte offset ril_ws_attn_offset(m) of
+ * `ws`.  Lets tests compare attention outputs, not just logprobs. */
+size_t ril_ws_attn_offset(const ril_model *m);
+
+/* Thread-local message describing the last non-OK status. */
+const char *ril_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RIL_H */

@@ -1,0 +1,203 @@
+"""Python binding of libril.so, the C ABI declared in include/ril.h.
+
+Argument marshalling only: every step of the forward runs in the library's HIP
+kernels.  The functions keep the C names (ril_model_create, ril_kv_alloc,
+ril_prefill_logprobs, ril_decode_step_logprobs, ...) and take torch tensors where
+the C side takes device pointers; torch supplies device memory and the stream.
+
+Importing this package fails loudly if libril.so is missing or does not load:
+there is no fallback of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libril.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m invariant_rl_logprob_amd.build` "
+        "(or __graft_entry__.build()); there is no fallback path")
+_lib = ctypes.CDLL(LIB_PATH)
+
+RIL_OK, RIL_EINVAL, RIL_ERANGE, RIL_ENOSPC, RIL_EUNSUPPORTED, RIL_EHIP = 0, -1, -2, -3, -4, -5
+RIL_ATTN_GQA = 0
+RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
+
+_c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+
+
+class ril_model_desc(ctypes.Structure):
+    _fields_ = [
+        ("attn_kind", _c_int), ("input_mode", _c_int), ("d_model", _c_int),
+        ("n_q_heads", _c_int), ("n_kv_heads", _c_int), ("head_dim", _c_int),
+        ("d_head", _c_int), ("vocab", _c_int), ("page_tokens", _c_int),
+        ("split_tokens", _c_int), ("max_rows", _c_int), ("max_tokens", _c_int),
+        ("max_ctx", _c_int), ("softmax_scale", _c_float), ("rms_eps", _c_float),
+        ("embed", _vp), ("w_qkv", _vp), ("w_o", _vp), ("norm_attn", _vp),
+        ("norm_final", _vp), ("w_lm", _vp),
+    ]
+
+
+class ril_prefill_batch(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", _c_int), ("total_tokens", _c_int), ("max_ctx_bound", _c_int),
+        ("cu_tokens", _vp), ("start_pos", _vp), ("page_table", _vp), ("page_stride", _c_int),
+        ("target_ids", _vp), ("token_ids", _vp), ("q", _vp), ("k", _vp), ("v", _vp),
+    ]
+
+
+class ril_decode_batch(ctypes.Structure):
+    _fields_ = [
+        ("n_rows", _c_int), ("max_ctx_bound", _c_int), ("ctx_len", _vp), ("page_table", _vp),
+        ("page_stride", _c_int), ("target_ids", _vp), ("token_ids", _vp),
+        ("q", _vp), ("k", _vp), ("v", _vp),
+    ]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_model_create = _sig("ril_model_create", _c_int, [ctypes.POINTER(ril_model_desc), ctypes.POINTER(_vp)])
+_model_destroy = _sig("ril_model_destroy", None, [_vp])
+_workspace_bytes = _sig("ril_workspace_bytes", ctypes.c_size_t, [_vp])
+_kv_page_bytes = _sig("ril_kv_page_bytes", ctypes.c_size_t, [_vp])
+_ws_attn_offset = _sig("ril_ws_attn_offset", ctypes.c_size_t, [_vp])
+_kv_alloc = _sig("ril_kv_alloc", _c_int, [_vp, _vp, ctypes.c_size_t, ctypes.c_uint64, ctypes.POINTER(_vp)])
+_kv_assign = _sig("ril_kv_assign", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)])
+_kv_release = _sig("ril_kv_release", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)])
+_kv_free_pages = _sig("ril_kv_free_pages", _c_int, [_vp])
+_kv_total_pages = _sig("ril_kv_total_pages", _c_int, [_vp])
+_kv_free = _sig("ril_kv_free", None, [_vp])
+_prefill = _sig("ril_prefill_logprobs", _c_int,
+                [_vp, _vp, ctypes.POINTER(ril_prefill_batch), _vp, _vp, ctypes.c_size_t, _vp])
+_decode = _sig("ril_decode_step_logprobs", _c_int,
+               [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp, ctypes.c_size_t, _vp])
+_kv_write = _sig("ril_kv_write", _c_int, [_vp, _vp, ctypes.POINTER(ril_prefill_batch), _vp])
+_last_error = _sig("ril_last_error", ctypes.c_char_p, [])
+
+EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril_kv_page_bytes",
+            "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
+            "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
+            "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error")
+
+
+class RilError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what} failed with status {status}: {ril_last_error()}")
+
+
+def _check(status, what):
+    if status != RIL_OK:
+        raise RilError(status, what)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or None."""
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream
+
+
+def ril_last_error() -> str:
+    s = _last_error()
+    return s.decode() if s else ""
+
+
+def ril_model_create(desc: ril_model_desc) -> int:
+    h = _vp()
+    _check(_model_create(ctypes.byref(desc), ctypes.byref(h)), "ril_model_create")
+    return h.value
+
+
+def ril_model_destroy(model: int) -> None:
+    _model_destroy(model)
+
+
+def ril_workspace_bytes(model: int) -> int:
+    return int(_workspace_bytes(model))
+
+
+def ril_kv_page_bytes(model: int) -> int:
+    return int(_kv_page_bytes(model))
+
+
+def ril_ws_attn_offset(model: int) -> int:
+    return int(_ws_attn_offset(model))
+
+
+def ril_kv_alloc(model: int, pool, shuffle_seed: int = 0) -> int:
+    """Wrap a device byte tensor as the KV pool; returns the kv handle."""
+    h = _vp()
+    nbytes = pool.numel() * pool.element_size()
+    _check(_kv_alloc(model, _ptr(pool), nbytes, shuffle_seed, ctypes.byref(h)), "ril_kv_alloc")
+    return h.value
+
+
+def ril_kv_assign(kv: int, n_pages: int):
+    arr = (_c_int * max(1, n_pages))()
+    _check(_kv_assign(kv, n_pages, arr), "ril_kv_assign")
+    return [arr[i] for i in range(n_pages)]
+
+
+def ril_kv_release(kv: int, page_ids) -> None:
+    arr = (_c_int * max(1, len(page_ids)))(*page_ids)
+    _check(_kv_release(kv, len(page_ids), arr), "ril_kv_release")
+
+
+def ril_kv_free_pages(kv: int) -> int:
+    return int(_kv_free_pages(kv))
+
+
+def ril_kv_total_pages(kv: int) -> int:
+    return int(_kv_total_pages(kv))
+
+
+def ril_kv_free(kv: int) -> None:
+    _kv_free(kv)
+
+
+def make_prefill_batch(*, cu_tokens, start_pos, page_table, max_ctx_bound, target_ids=None,
+                       token_ids=None, q=None, k=None, v=None, total_tokens=None) -> ril_prefill_batch:
+    """Build the C descriptor from device tensors (the tensors must outlive the call)."""
+    n = cu_tokens.numel() - 1
+    if total_tokens is None:
+        raise ValueError("total_tokens (a host integer) is required")
+    return ril_prefill_batch(n, int(total_tokens), int(max_ctx_bound), _ptr(cu_tokens), _ptr(start_pos),
+                             _ptr(page_table), page_table.shape[1], _ptr(target_ids), _ptr(token_ids),
+                             _ptr(q), _ptr(k), _ptr(v))
+
+
+def make_decode_batch(*, ctx_len, page_table, max_ctx_bound, target_ids, token_ids=None, q=None,
+                      k=None, v=None) -> ril_decode_batch:
+    return ril_decode_batch(ctx_len.numel(), int(max_ctx_bound), _ptr(ctx_len), _ptr(page_table),
+                            page_table.shape[1], _ptr(target_ids), _ptr(token_ids), _ptr(q), _ptr(k), _ptr(v))
+
+
+def ril_prefill_logprobs(model: int, kv: int, batch: ril_prefill_batch, logprob_out, ws,
+                         stream=None) -> None:
+    _check(_prefill(model, kv, ctypes.byref(batch), _ptr(logprob_out), _ptr(ws),
+                    ws.numel() * ws.element_size(), _stream(stream)), "ril_prefill_logprobs")
+
+
+def ril_decode_step_logprobs(model: int, kv: int, batch: ril_decode_batch, logprob_out, ws,
+                             stream=None) -> None:
+    _check(_decode(model, kv, ctypes.byref(batch), _ptr(logprob_out), _ptr(ws),
+                   ws.numel() * ws.element_size(), _stream(stream)), "ril_decode_step_logprobs")
+
+
+def ril_kv_write(model: int, kv: int, batch: ril_prefill_batch, stream=None) -> None:
+    _check(_kv_write(model, kv, ctypes.byref(batch), _stream(stream)), "ril_kv_write")

@@ -1,0 +1,380 @@
+// C ABI of the invariant logprob forward: validation, the host page allocator (S1),
+// workspace layout from static limits, and the launch sequence on the caller's stream.
+// The host never reads device memory and never synchronises (Bitwise-consistent RL
+// post, section 4.6: no host sync or batch-dependent shapes on the hot path).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <climits>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "ril.h"
+
+using namespace ril;
+
+struct ril_model {
+  ril_model_desc d;
+  int G;            // q heads per kv head
+  int n_vt;         // vocabulary tiles of 256 columns
+  int max_splits;   // splits of the longest context
+  float cscale;     // softmax_scale * log2(e), rounded once to fp32
+  size_t page_bytes;
+  // workspace segment offsets (bytes) and total
+  size_t off_x, off_h, off_qkv, off_attn, off_y, off_z, off_vpart, off_tgt, off_po, off_pml;
+  size_t ws_total;
+};
+
+struct ril_kv {
+  size_t page_bytes;
+  void *pool;
+  int32_t n_pages;
+  std::vector<int32_t> free_list;  // popped from the back
+  std::vector<uint8_t> assigned;
+};
+
+static thread_local std::string g_err;
+
+static ril_status fail(ril_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+extern "C" const char *ril_last_error(void) { return g_err.c_str(); }
+
+extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **out) {
+  if (!desc || !out) return fail(RIL_EINVAL, "model_create: null argument");
+  const ril_model_desc &d = *desc;
+  if (d.attn_kind != RIL_ATTN_GQA) return fail(RIL_EUNSUPPORTED, "model_create: attn_kind %d", d.attn_kind);
+  if (d.input_mode != RIL_INPUT_TOKENS && d.input_mode != RIL_INPUT_QKV)
+    return fail(RIL_EINVAL, "model_create: input_mode %d", d.input_mode);
+  if (d.head_dim != 64 && d.head_dim != 128)
+    return fail(RIL_EUNSUPPORTED, "model_create: head_dim %d (64 or 128)", d.head_dim);
+  if (d.n_q_heads < 1 || d.n_kv_heads < 1 || d.n_q_heads % d.n_kv_heads)
+    return fail(RIL_EINVAL, "model_create: heads %d/%d", d.n_q_heads, d.n_kv_heads);
+  const int G = d.n_q_heads / d.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(RIL_EUNSUPPORTED, "model_create: group size %d (1, 2, 4, 8 or 16)", G);
+  if (d.page_tokens != 16) return fail(RIL_EUNSUPPORTED, "model_create: page_tokens %d (16)", d.page_tokens);
+  if (d.split_tokens <= 0 || d.split_tokens % 64)
+    return fail(RIL_EINVAL, "model_create: split_tokens %d (positive multiple of 64)", d.split_tokens);
+  if (d.vocab < 1) return fail(RIL_EINVAL, "model_create: vocab %d", d.vocab);
+  if (d.max_rows < 1 || d.max_tokens < 1 || d.max_ctx < 1)
+    return fail(RIL_EINVAL, "model_create: limits %d/%d/%d", d.max_rows, d.max_tokens, d.max_ctx);
+  if (!(d.softmax_scale > 0.f) || !std::isfinite(d.softmax_scale))
+    return fail(RIL_EINVAL, "model_create: softmax_scale");
+  if (!(d.rms_eps >= 0.f) || !std::isfinite(d.rms_eps)) return fail(RIL_EINVAL, "model_create: rms_eps");
+  const int qw = d.n_q_heads * d.head_dim;
+  if (d.input_mode == RIL_INPUT_TOKENS) {
+    if (d.d_model <= 0 || d.d_model % 32) return fail(RIL_EINVAL, "model_create: d_model %d", d.d_model);
+    if (!d.embed || !d.w_qkv || !d.w_o) return fail(RIL_EINVAL, "model_create: TOKENS needs embed, w_qkv, w_o");
+    if (d.d_head != d.d_model) return fail(RIL_EINVAL, "model_create: TOKENS needs d_head == d_model");
+    if (qw % 32) return fail(RIL_EINVAL, "model_create: Hq*D %d not a multiple of 32", qw);
+  } else {
+    if (d.w_o ? (d.d_head <= 0 || d.d_head % 32) : (d.d_head != qw))
+      return fail(RIL_EINVAL, "model_create: d_head %d", d.d_head);
+  }
+  if (!d.w_lm) return fail(RIL_EINVAL, "model_create: w_lm is required");
+  const void *ptrs[] = {d.embed, d.w_qkv, d.w_o, d.norm_attn, d.norm_final, d.w_lm};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(RIL_EINVAL, "model_create: weight pointer not 16-byte aligned");
+
+  ril_model *m = new ril_model();
+  m->d = d;
+  m->G = G;
+  m->n_vt = (d.vocab + 255) / 256;
+  m->max_splits = (d.max_ctx + d.split_tokens - 1) / d.split_tokens;
+  m->cscale = (float)((double)d.softmax_scale * 1.4426950408889634);
+  m->page_bytes = (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * 2;
+  const size_t R = (size_t)std::max(d.max_rows, d.max_tokens);
+  const bool tok = d.input_mode == RIL_INPUT_TOKENS;
+  size_t o = 0;
+  auto seg = [&](size_t bytes) { size_t at = o; o += round256(bytes); return at; };
+  m->off_x = seg(tok ? R * d.d_model * 2 : 0);
+  m->off_h = seg(tok ? R * d.d_model * 2 : 0);
+  m->off_qkv = seg(tok ? R * (size_t)(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim * 2 : 0);
+  m->off_attn = seg(R * qw * 2);
+  m->off_y = seg(d.w_o ? R * d.d_head * 2 : 0);
+  m->off_z = seg(R * d.d_head * 2);
+  m->off_vpart = seg(R * m->n_vt * 2 * sizeof(float));
+  m->off_tgt = seg(R * sizeof(float));
+  m->off_po = seg((size_t)d.max_rows * d.n_q_heads * m->max_splits * d.head_dim * sizeof(float));
+  m->off_pml = seg((size_t)d.max_rows * d.n_q_heads * m->max_splits * 2 * sizeof(float));
+  m->ws_total = o;
+  *out = m;
+  return RIL_OK;
+}
+
+extern "C" void ril_model_destroy(ril_model *m) { delete m; }
+extern "C" size_t ril_workspace_bytes(const ril_model *m) { return m ? m->ws_total : 0; }
+extern "C" size_t ril_kv_page_bytes(const ril_model *m) { return m ? m->page_bytes : 0; }
+extern "C" size_t ril_ws_attn_offset(const ril_model *m) { return m ? m->off_attn : 0; }
+
+// ---------------------------------------------------------------------------
+// S1: page allocator
+// ---------------------------------------------------------------------------
+
+static uint64_t splitmix64(uint64_t &s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+extern "C" ril_status ril_kv_alloc(const ril_model *m, void *pool_dev, size_t pool_bytes,
+                                   uint64_t shuffle_seed, ril_kv **out) {
+  if (!m || !pool_dev || !out) return fail(RIL_EINVAL, "kv_alloc: null argument");
+  if (!aligned16(pool_dev)) return fail(RIL_EINVAL, "kv_alloc: pool not 16-byte aligned");
+  const size_t n = pool_bytes / m->page_bytes;
+  if (n < 1) return fail(RIL_ENOSPC, "kv_alloc: pool smaller than one page (%zu bytes)", m->page_bytes);
+  if (n > (size_t)INT32_MAX) return fail(RIL_ERANGE, "kv_alloc: too many pages");
+  ril_kv *kv = new ril_kv();
+  kv->page_bytes = m->page_bytes;
+  kv->pool = pool_dev;
+  kv->n_pages = (int32_t)n;
+  kv->free_list.resize(n);
+  // pop_back hands out ids in free_list order reversed; store so that 0 comes first
+  for (size_t i = 0; i < n; ++i) kv->free_list[i] = (int32_t)(n - 1 - i);
+  if (shuffle_seed) {
+    uint64_t s = shuffle_seed;
+    for (size_t i = n - 1; i > 0; --i) {
+      const size_t j = (size_t)(splitmix64(s) % (uint64_t)(i + 1));
+      std::swap(kv->free_list[i], kv->free_list[j]);
+    }
+  }
+  kv->assigned.assign(n, 0);
+  *out = kv;
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_kv_assign(ril_kv *kv, int32_t n_pages, int32_t *page_ids_out) {
+  if (!kv || n_pages < 0 || (n_pages > 0 && !page_ids_out)) return fail(RIL_EINVAL, "kv_assign: bad argument");
+  if ((size_t)n_pages > kv->free_list.size())
+    return fail(RIL_ENOSPC, "kv_assign: %d pages asked, %zu free", n_pages, kv->free_list.size());
+  for (int32_t i = 0; i < n_pages; ++i) {
+    const int32_t id = kv->free_list.back();
+    kv->free_list.pop_back();
+    kv->assigned[id] = 1;
+    page_ids_out[i] = id;
+  }
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_kv_release(ril_kv *kv, int32_t n_pages, const int32_t *ids) {
+  if (!kv || n_pages < 0 || (n_pages > 0 && !ids)) return fail(RIL_EINVAL, "kv_release: bad argument");
+  std::vector<uint8_t> seen;
+  for (int32_t i = 0; i < n_pages; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= kv->n_pages || !kv->assigned[id])
+      return fail(RIL_EINVAL, "kv_release: page %d is not assigned", id);
+    if (seen.empty()) seen.assign(kv->n_pages, 0);
+    if (seen[id]) return fail(RIL_EINVAL, "kv_release: page %d listed twice", id);
+    seen[id] = 1;
+  }
+  for (int32_t i = 0; i < n_pages; ++i) {
+    kv->assigned[ids[i]] = 0;
+    kv->free_list.push_back(ids[i]);
+  }
+  return RIL_OK;
+}
+
+extern "C" int32_t ril_kv_free_pages(const ril_kv *kv) { return kv ? (int32_t)kv->free_list.size() : 0; }
+extern "C" int32_t ril_kv_total_pages(const ril_kv *kv) { return kv ? kv->n_pages : 0; }
+extern "C" void ril_kv_free(ril_kv *kv) { delete kv; }
+
+// ---------------------------------------------------------------------------
+// forward passes
+// ---------------------------------------------------------------------------
+
+static bf16_t *wsb(void *ws, size_t off) { return reinterpret_cast<bf16_t *>(static_cast<char *>(ws) + off); }
+static float *wsf(void *ws, size_t off) { return reinterpret_cast<float *>(static_cast<char *>(ws) + off); }
+
+#define RIL_LAUNCH(expr)                                                               \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(RIL_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+static ril_status check_common(const ril_model *m, ril_kv *kv, void *ws, size_t ws_bytes,
+                               int ctx_bound, const void *page_table, int page_stride, const char *who) {
+  if (!m || !kv) return fail(RIL_EINVAL, "%s: null model or kv", who);
+  if (kv->page_bytes != m->page_bytes) return fail(RIL_EINVAL, "%s: kv pool made for another page size", who);
+  if (!ws || !aligned16(ws)) return fail(RIL_EINVAL, "%s: workspace null or misaligned", who);
+  if (ws_bytes < m->ws_total)
+    return fail(RIL_ERANGE, "%s: workspace %zu bytes, %zu needed", who, ws_bytes, m->ws_total);
+  if (ctx_bound < 1 || ctx_bound > m->d.max_ctx)
+    return fail(RIL_ERANGE, "%s: max_ctx_bound %d outside [1, %d]", who, ctx_bound, m->d.max_ctx);
+  if (!page_table || !aligned4(page_table)) return fail(RIL_EINVAL, "%s: page_table", who);
+  if (page_stride < (ctx_bound + 15) / 16)
+    return fail(RIL_EINVAL, "%s: page_stride %d < %d pages", who, page_stride, (ctx_bound + 15) / 16);
+  return RIL_OK;
+}
+
+// Attention output (in the workspace) -> [O GEMM (+ residual)] -> RMSNorm -> lm-head.
+static ril_status run_head(const ril_model *m, int rows, const int32_t *targets, float *out, void *ws,
+                           hipStream_t st) {
+  const ril_model_desc &d = *&m->d;
+  const int qw = d.n_q_heads * d.head_dim;
+  const bf16_t *src = wsb(ws, m->off_attn);
+  int ld = qw;
+  if (d.w_o) {
+    const bool tok = d.input_mode == RIL_INPUT_TOKENS;
+    GemmArgs g{src, qw, (const bf16_t *)d.w_o, qw, wsb(ws, m->off_y), d.d_head,
+               tok ? wsb(ws, m->off_x) : nullptr, d.d_model, rows, d.d_head, qw};
+    RIL_LAUNCH(launch_gemm(g, st));
+    src = wsb(ws, m->off_y);
+    ld = d.d_head;
+  }
+  RmsNormArgs r{src, ld, nullptr, nullptr, d.vocab, d.d_head, (const bf16_t *)d.norm_final, d.rms_eps,
+                wsb(ws, m->off_z), d.d_head, nullptr, 0, rows};
+  RIL_LAUNCH(launch_rmsnorm(r, st));
+  LmHeadArgs lh{wsb(ws, m->off_z), d.d_head, (const bf16_t *)d.w_lm, d.d_head, d.vocab, targets, rows,
+                wsf(ws, m->off_vpart), wsf(ws, m->off_tgt), out};
+  RIL_LAUNCH(launch_lm_head(lh, st));
+  return RIL_OK;
+}
+
+// TOKENS mode front: embedding + RMSNorm + QKV projection into the workspace.
+static ril_status run_token_front(const ril_model *m, int rows, const int32_t *tok, void *ws, hipStream_t st) {
+  const ril_model_desc &d = m->d;
+  const int wqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  RmsNormArgs r{nullptr, 0, tok, (const bf16_t *)d.embed, d.vocab, d.d_model, (const bf16_t *)d.norm_attn,
+                d.rms_eps, wsb(ws, m->off_h), d.d_model, wsb(ws, m->off_x), d.d_model, rows};
+  RIL_LAUNCH(launch_rmsnorm(r, st));
+  GemmArgs g{wsb(ws, m->off_h), d.d_model, (const bf16_t *)d.w_qkv, d.d_model, wsb(ws, m->off_qkv), wqkv,
+             nullptr, 0, rows, wqkv, d.d_model};
+  RIL_LAUNCH(launch_gemm(g, st));
+  return RIL_OK;
+}
+
+static ril_status check_prefill(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b, void *ws,
+                                size_t ws_bytes, bool need_logprob, const char *who) {
+  if (!b) return fail(RIL_EINVAL, "%s: null batch", who);
+  ril_status s = check_common(m, kv, ws, need_logprob ? ws_bytes : m->ws_total, b->max_ctx_bound,
+                              b->page_table, b->page_stride, who);
+  if (s != RIL_OK) return s;
+  // The history writer uses no workspace, so only the logprob calls are held to max_tokens.
+  const int lim = need_logprob ? m->d.max_tokens : INT32_MAX;
+  if (b->n_seqs < 1 || b->n_seqs > lim)
+    return fail(RIL_ERANGE, "%s: n_seqs %d outside [1, %d]", who, b->n_seqs, lim);
+  if (b->total_tokens < 1 || b->total_tokens > lim)
+    return fail(RIL_ERANGE, "%s: total_tokens %d outside [1, %d]", who, b->total_tokens, lim);
+  if (!b->cu_tokens || !b->start_pos || !aligned4(b->cu_tokens) || !aligned4(b->start_pos))
+    return fail(RIL_EINVAL, "%s: cu_tokens/start_pos", who);
+  const bool tok = m->d.input_mode == RIL_INPUT_TOKENS;
+  if (need_logprob) {
+    if (!b->target_ids || !aligned4(b->target_ids)) return fail(RIL_EINVAL, "%s: target_ids", who);
+    if (tok && (!b->token_ids || !aligned4(b->token_ids))) return fail(RIL_EINVAL, "%s: token_ids", who);
+    if (!tok && (!b->q || !aligned16(b->q))) return fail(RIL_EINVAL, "%s: q", who);
+  }
+  if ((!tok || !need_logprob) && (!b->k || !b->v || !aligned16(b->k) || !aligned16(b->v)))
+    return fail(RIL_EINVAL, "%s: k/v", who);
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b, void *stream) {
+  if (!m) return fail(RIL_EINVAL, "kv_write: null model");
+  // the history writer needs no workspace; pass a dummy aligned pointer through the checks
+  static char dummy alignas(16)[16];
+  ril_status s = check_prefill(m, kv, b, dummy, 0, false, "kv_write");
+  if (s != RIL_OK) return s;
+  const ril_model_desc &d = m->d;
+  KvWriteArgs a{(const bf16_t *)b->k, (const bf16_t *)b->v, d.n_kv_heads * d.head_dim, b->total_tokens, 0,
+                b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table, b->page_stride,
+                (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
+  RIL_LAUNCH(launch_kv_write(a, (hipStream_t)stream));
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b,
+                                           float *logprob_out, void *ws, size_t ws_bytes, void *stream) {
+  ril_status s = check_prefill(m, kv, b, ws, ws_bytes, true, "prefill_logprobs");
+  if (s != RIL_OK) return s;
+  if (!logprob_out || !aligned4(logprob_out)) return fail(RIL_EINVAL, "prefill_logprobs: logprob_out");
+  const ril_model_desc &d = m->d;
+  hipStream_t st = (hipStream_t)stream;
+  const int T = b->total_tokens;
+  const bool tok = d.input_mode == RIL_INPUT_TOKENS;
+  const int wqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const bf16_t *q, *k, *v;
+  int q_stride, kv_stride;
+  if (tok) {
+    s = run_token_front(m, T, b->token_ids, ws, st);
+    if (s != RIL_OK) return s;
+    q = wsb(ws, m->off_qkv);
+    k = q + d.n_q_heads * d.head_dim;
+    v = k + d.n_kv_heads * d.head_dim;
+    q_stride = kv_stride = wqkv;
+  } else {
+    q = (const bf16_t *)b->q;
+    k = (const bf16_t *)b->k;
+    v = (const bf16_t *)b->v;
+    q_stride = d.n_q_heads * d.head_dim;
+    kv_stride = d.n_kv_heads * d.head_dim;
+  }
+  KvWriteArgs kw{k, v, kv_stride, T, 0, b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table,
+                 b->page_stride, (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
+  RIL_LAUNCH(launch_kv_write(kw, st));
+  AttnPrefillArgs ap{q, q_stride, b->cu_tokens, b->start_pos, b->n_seqs, T, b->page_table, b->page_stride,
+                     (const bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, m->G, d.head_dim, d.split_tokens,
+                     b->max_ctx_bound, m->cscale, wsb(ws, m->off_attn)};
+  RIL_LAUNCH(launch_attn_prefill(ap, st));
+  return run_head(m, T, b->target_ids, logprob_out, ws, st);
+}
+
+extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                               float *logprob_out, void *ws, size_t ws_bytes, void *stream) {
+  if (!b) return fail(RIL_EINVAL, "decode_step_logprobs: null batch");
+  ril_status s = check_common(m, kv, ws, ws_bytes, b->max_ctx_bound, b->page_table, b->page_stride,
+                              "decode_step_logprobs");
+  if (s != RIL_OK) return s;
+  const ril_model_desc &d = m->d;
+  if (b->n_rows < 1 || b->n_rows > d.max_rows)
+    return fail(RIL_ERANGE, "decode_step_logprobs: n_rows %d outside [1, %d]", b->n_rows, d.max_rows);
+  if (!b->ctx_len || !aligned4(b->ctx_len) || !b->target_ids || !aligned4(b->target_ids))
+    return fail(RIL_EINVAL, "decode_step_logprobs: ctx_len/target_ids");
+  if (!logprob_out || !aligned4(logprob_out)) return fail(RIL_EINVAL, "decode_step_logprobs: logprob_out");
+  const bool tok = d.input_mode == RIL_INPUT_TOKENS;
+  if (tok && (!b->token_ids || !aligned4(b->token_ids))) return fail(RIL_EINVAL, "decode_step_logprobs: token_ids");
+  if (!tok && (!b->q || !b->k || !b->v || !aligned16(b->q) || !aligned16(b->k) || !aligned16(b->v)))
+    return fail(RIL_EINVAL, "decode_step_logprobs: q/k/v");
+  hipStream_t st = (hipStream_t)stream;
+  const int R = b->n_rows;
+  const int wqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const bf16_t *q, *k, *v;
+  int q_stride, kv_stride;
+  if (tok) {
+    s = run_token_front(m, R, b->token_ids, ws, st);
+    if (s != RIL_OK) return s;
+    q = wsb(ws, m->off_qkv);
+    k = q + d.n_q_heads * d.head_dim;
+    v = k + d.n_kv_heads * d.head_dim;
+    q_stride = kv_stride = wqkv;
+  } else {
+    q = (const bf16_t *)b->q;
+    k = (const bf16_t *)b->k;
+    v = (const bf16_t *)b->v;
+    q_stride = d.n_q_heads * d.head_dim;
+    kv_stride = d.n_kv_heads * d.head_dim;
+  }
+  KvWriteArgs kw{k, v, kv_stride, R, 1, nullptr, nullptr, 0, b->ctx_len, b->page_table, b->page_stride,
+                 (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
+  RIL_LAUNCH(launch_kv_write(kw, st));
+  AttnDecodeArgs ad{q, q_stride, b->ctx_len, b->page_table, b->page_stride, (const bf16_t *)kv->pool,
+                    kv->n_pages, d.n_kv_heads, m->G, d.head_dim, d.split_tokens, b->max_ctx_bound, R,
+                    m->max_splits, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn)};
+  RIL_LAUNCH(launch_attn_decode(ad, st));
+  return run_head(m, R, b->target_ids, logprob_out, ws, st);
+}

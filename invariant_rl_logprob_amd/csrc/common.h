@@ -1,0 +1,112 @@
+// Device helpers shared by every kernel of the invariant path (gfx950 / CDNA4).
+//
+// Invariance rules these helpers encode (Bitwise-consistent RL post, section 2):
+//  * one MFMA instruction for every contraction (v_mfma_f32_16x16x32_bf16), so an
+//    output element's rounding never depends on which kernel or tile size computed it;
+//  * bf16 rounding is round-to-nearest-even, written out on the bits (section 4.4,
+//    condition 1: one elementwise round-to-nearest rule everywhere);
+//  * every reduction is a fixed tree over a fixed element->lane map: lane-local
+//    sequential sums, then xor-butterflies whose adds are commutative, so all lanes
+//    of a butterfly end with the same bits;
+//  * exp2/log2 are the hardware v_exp_f32 / v_log_f32, used identically everywhere;
+//  * the library is compiled with -ffp-contract=off: an FMA appears only where
+//    written as __builtin_fmaf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ril {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // storage type of bf16 values
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPage = 16;        // tokens per KV page
+constexpr int kTile = 64;        // tokens per attention KV tile
+constexpr int kVocabTile = 256;  // lm-head columns per vocabulary tile
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2f_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quietened).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Sum over the 16 lanes that share (lane >> 4): xor 1, 2, 4, 8.  Each add is
+// commutative, so every lane of the group ends with identical bits.
+__device__ __forceinline__ float sum16(float v) {
+  v = v + shfl_xor_f(v, 1);
+  v = v + shfl_xor_f(v, 2);
+  v = v + shfl_xor_f(v, 4);
+  v = v + shfl_xor_f(v, 8);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 1));
+  v = fmaxf(v, shfl_xor_f(v, 2));
+  v = fmaxf(v, shfl_xor_f(v, 4));
+  v = fmaxf(v, shfl_xor_f(v, 8));
+  return v;
+}
+// Across the 4 lane groups (lanes l, l^16, l^32, l^48): xor 16 then xor 32.
+__device__ __forceinline__ float sum_groups(float v) {
+  v = v + shfl_xor_f(v, 16);
+  v = v + shfl_xor_f(v, 32);
+  return v;
+}
+__device__ __forceinline__ float max_groups(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  v = fmaxf(v, shfl_xor_f(v, 32));
+  return v;
+}
+// Whole-wave sum: xor 32, 16, 8, 4, 2, 1.
+__device__ __forceinline__ float sum64(float v) {
+  v = v + shfl_xor_f(v, 32);
+  v = v + shfl_xor_f(v, 16);
+  v = v + shfl_xor_f(v, 8);
+  v = v + shfl_xor_f(v, 4);
+  v = v + shfl_xor_f(v, 2);
+  v = v + shfl_xor_f(v, 1);
+  return v;
+}
+
+// Sequence lookup for packed token j: the s with cu[s] <= j < cu[s+1].
+__device__ __forceinline__ int locate_seq(const int32_t *__restrict__ cu, int n_seqs, int j) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace ril

@@ -1,0 +1,316 @@
+// Dense parts of the path: embedding gather + RMSNorm (S2, S3), projection GEMMs with
+// one MFMA K order and no split-K (S4), the lm-head with per-vocabulary-tile softmax
+// partials and target-logit capture (S11), and the fixed-tree vocabulary merge that
+// yields the logprob (S12).
+//
+// Batch invariance of the GEMMs (Bitwise-consistent RL post, section 4.1: one
+// accumulation order for every M): each output element is one chain of
+// v_mfma_f32_16x16x32_bf16 over K in 32-wide steps, k = 0, 32, 64, ... in order,
+// starting from 0.  The M/N tile a workgroup owns, the grid and the number of rows
+// never change that chain, and no K range is ever split across waves.
+#include "common.h"
+#include "kernels.h"
+
+namespace ril {
+
+// ---------------------------------------------------------------------------
+// S2 + S3: y = bf16((x * rsqrt(mean(x^2) + eps)) * g), x = E[token] or a dense row.
+// One wave per row.  Lane l owns 8-element chunks l, l+64, ...; the sum of squares is
+// a lane-sequential fma chain followed by a whole-wave xor butterfly.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void rmsnorm_kernel(
+    const bf16_t *__restrict__ x, int ldx, const int32_t *__restrict__ tok,
+    const bf16_t *__restrict__ embed, int vocab, int d, const bf16_t *__restrict__ gain, float eps,
+    bf16_t *__restrict__ y, int ldy, bf16_t *__restrict__ x_copy, int ldc) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const bf16_t *src;
+  bool poison = false;
+  if (tok) {
+    int t = tok[row];
+    if (t < 0 || t >= vocab) {
+      poison = true;
+      t = 0;
+    }
+    src = embed + (long)t * d;
+  } else {
+    src = x + (long)row * ldx;
+  }
+  const int n8 = d / 8;
+  float acc = 0.f;
+  for (int e = lane; e < n8; e += 64) {
+    const u32x4 v = ld16(src + e * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = bf2f((bf16_t)(v[w] & 0xffffu)), b = bf2f((bf16_t)(v[w] >> 16));
+      acc = __builtin_fmaf(a, a, acc);
+      acc = __builtin_fmaf(b, b, acc);
+    }
+  }
+  acc = sum64(acc);
+  const float mean = __fdiv_rn(acc, (float)d);
+  float r = __fdiv_rn(1.0f, __fsqrt_rn(mean + eps));
+  if (poison) r = __builtin_nanf("");
+  for (int e = lane; e < n8; e += 64) {
+    const u32x4 v = ld16(src + e * 8);
+    u32x4 g = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
+    if (gain) g = ld16(gain + e * 8);
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = bf2f((bf16_t)(v[w] & 0xffffu)), b = bf2f((bf16_t)(v[w] >> 16));
+      const float ga = bf2f((bf16_t)(g[w] & 0xffffu)), gb = bf2f((bf16_t)(g[w] >> 16));
+      out[w] = pack2((a * r) * ga, (b * r) * gb);
+    }
+    st16(y + (long)row * ldy + e * 8, out);
+    if (x_copy) st16(x_copy + (long)row * ldc + e * 8, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S4: C[M,N] = bf16(A[M,K] W[N,K]^T) or bf16(R + bf16(A W^T)).
+// Workgroup = 4 waves side by side along N; a wave owns MB x NB 16x16 blocks.
+// ---------------------------------------------------------------------------
+template <int MB, int NB>
+__global__ __launch_bounds__(256) void gemm_kernel(const bf16_t *__restrict__ A, int lda,
+                                                   const bf16_t *__restrict__ W, int ldw,
+                                                   bf16_t *__restrict__ C, int ldc,
+                                                   const bf16_t *__restrict__ R, int ldr, int M,
+                                                   int N, int K) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int m0 = blockIdx.y * 16 * MB;
+  const int n0 = (blockIdx.x * 4 + wave) * 16 * NB;
+  if (n0 >= N) return;
+  const bf16_t *ap[MB];
+  const bf16_t *wp[NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) ap[mb] = A + (long)min(m0 + 16 * mb + r16, M - 1) * lda + grp * 8;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wp[nb] = W + (long)min(n0 + 16 * nb + r16, N - 1) * ldw + grp * 8;
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; k += 32) {
+    bf16x8 a[MB], b[NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[mb] = as_bf16x8(ld16(ap[mb] + k));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) b[nb] = as_bf16x8(ld16(wp[nb] + k));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = n0 + 16 * nb + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * mb + 4 * grp + i;
+        if (row < M && col < N) {
+          float v = bf2f(f2bf(acc[mb][nb][i]));
+          if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+          C[(long)row * ldc + col] = f2bf(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S11: logits of one 256-column vocabulary tile, never stored.  The tile's column
+// layout is fixed: wave w owns columns 64w .. 64w+63 as four 16-column MFMA blocks,
+// column 16nb + lane%16.  Per row: tile max, then
+//   s_t = ((S_0 + S_1) + S_2) + S_3,  S_w = xor-butterfly over 16 lanes of
+//         (((e_0 + e_1) + e_2) + e_3),  e = exp2((l - max) * log2 e)
+// and the target's logit if the target falls in the tile.  M rows per workgroup
+// (16*MB) are free: they never touch a row's reduction tree.
+// ---------------------------------------------------------------------------
+template <int MB>
+__global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__ Z, int ldz,
+                                                      const bf16_t *__restrict__ W, int K, int V,
+                                                      const int32_t *__restrict__ target, int M,
+                                                      float *__restrict__ part,
+                                                      float *__restrict__ tgt_logit, int n_vt) {
+  __shared__ float red[4][16 * MB];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int tile = blockIdx.x;
+  const int m0 = blockIdx.y * 16 * MB;
+  const int c0 = tile * kVocabTile + wave * 64;
+  const bf16_t *ap[MB];
+  const bf16_t *wp[4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) ap[mb] = Z + (long)min(m0 + 16 * mb + r16, M - 1) * ldz + grp * 8;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) wp[nb] = W + (long)min(c0 + 16 * nb + r16, V - 1) * K + grp * 8;
+  f32x4 acc[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; k += 32) {
+    bf16x8 a[MB], b[4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[mb] = as_bf16x8(ld16(ap[mb] + k));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) b[nb] = as_bf16x8(ld16(wp[nb] + k));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
+  }
+  bool cval[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) cval[nb] = (c0 + 16 * nb + r16) < V;
+  // tile max per row
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = neg_inf();
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) mx = fmaxf(mx, cval[nb] ? acc[mb][nb][i] : neg_inf());
+      mx = max16(mx);
+      if (r16 == 0) red[wave][16 * mb + 4 * grp + i] = mx;
+    }
+  }
+  __syncthreads();
+  float mt[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mb + 4 * grp + i;
+      mt[mb][i] = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+    }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float e[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        e[nb] = cval[nb] ? exp2f_hw((acc[mb][nb][i] - mt[mb][i]) * kLog2e) : 0.f;
+      float sm = ((e[0] + e[1]) + e[2]) + e[3];
+      sm = sum16(sm);
+      if (r16 == 0) red[wave][16 * mb + 4 * grp + i] = sm;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mb + 4 * grp + i;
+      const int row = m0 + r;
+      if (row >= M) continue;
+      if (wave == 0 && r16 == 0) {
+        const float st = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
+        part[((long)row * n_vt + tile) * 2] = mt[mb][i];
+        part[((long)row * n_vt + tile) * 2 + 1] = st;
+      }
+      const int tg = target[row];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        if (cval[nb] && c0 + 16 * nb + r16 == tg) tgt_logit[row] = acc[mb][nb][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S12: per row, merge the (max, sum) of every vocabulary tile with a fixed tree
+// (lane j folds tiles j, j+64, ... left to right; then lanes combine by halving,
+// the lower lane on the left) and return lp = (l_target - m) - ln(s).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_vocab(float &m, float &s, float mb, float sb) {
+  if (mb == neg_inf()) return;
+  if (m == neg_inf()) {
+    m = mb;
+    s = sb;
+    return;
+  }
+  const float mn = fmaxf(m, mb);
+  s = __builtin_fmaf(s, exp2f_hw((m - mn) * kLog2e), sb * exp2f_hw((mb - mn) * kLog2e));
+  m = mn;
+}
+
+__global__ __launch_bounds__(64) void vocab_merge_kernel(const float *__restrict__ part,
+                                                         const float *__restrict__ tgt_logit,
+                                                         const int32_t *__restrict__ target,
+                                                         int n_vt, int V, float *__restrict__ out) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  float m = neg_inf(), s = 0.f;
+  for (int t = lane; t < n_vt; t += 64)
+    merge_vocab(m, s, part[((long)row * n_vt + t) * 2], part[((long)row * n_vt + t) * 2 + 1]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float mo = __shfl_down(m, off, 64);
+    const float so = __shfl_down(s, off, 64);
+    if (lane < off) merge_vocab(m, s, mo, so);
+  }
+  if (lane == 0) {
+    const int tg = target[row];
+    float lp;
+    if (tg < 0 || tg >= V)
+      lp = __builtin_nanf("");
+    else
+      lp = (tgt_logit[row] - m) - log2f_hw(s) * kLn2;
+    out[row] = lp;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(a.rows), dim3(64), 0, st, a.x, a.ldx, a.tok, a.embed,
+                     a.vocab, a.d, a.gain, a.eps, a.y, a.ldy, a.x_copy, a.ldc);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  if (a.M <= 16) {
+    dim3 grid((a.N + 63) / 64, (a.M + 15) / 16);
+    hipLaunchKernelGGL((gemm_kernel<1, 1>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C,
+                       a.ldc, a.R, a.ldr, a.M, a.N, a.K);
+  } else if (a.M <= 64) {
+    dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+    hipLaunchKernelGGL((gemm_kernel<4, 1>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C,
+                       a.ldc, a.R, a.ldr, a.M, a.N, a.K);
+  } else {
+    dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
+    hipLaunchKernelGGL((gemm_kernel<4, 2>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C,
+                       a.ldc, a.R, a.ldr, a.M, a.N, a.K);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  const int n_vt = (a.V + kVocabTile - 1) / kVocabTile;
+  if (a.M <= 16) {
+    dim3 grid(n_vt, (a.M + 15) / 16);
+    hipLaunchKernelGGL(lm_head_kernel<1>, grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
+                       a.target, a.M, a.part, a.tgt_logit, n_vt);
+  } else {
+    dim3 grid(n_vt, (a.M + 63) / 64);
+    hipLaunchKernelGGL(lm_head_kernel<4>, grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
+                       a.target, a.M, a.part, a.tgt_logit, n_vt);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vocab_merge_kernel, dim3(a.M), dim3(64), 0, st, a.part, a.tgt_logit,
+                     a.target, n_vt, a.V, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace ril

@@ -1,0 +1,90 @@
+// Host-side launch interface of the HIP kernels (argument bundles + launchers).
+// Every launcher enqueues on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ril {
+
+typedef uint16_t bf16_t;
+
+struct KvWriteArgs {
+  const bf16_t *k, *v;  // [n_tok, row_stride] rows, kv head g at g*D
+  int row_stride, n_tok, mode;  // mode 0: packed prefill tokens; 1: decode rows
+  const int32_t *cu, *start_pos;
+  int n_seqs;
+  const int32_t *ctx_len, *page_table;
+  int page_stride;
+  bf16_t *pool;
+  int n_pages, Hkv, D;
+};
+
+struct AttnDecodeArgs {
+  const bf16_t *q;  // row r at q + r*q_row_stride, head h at +h*D
+  int q_row_stride;
+  const int32_t *ctx_len, *page_table;
+  int page_stride;
+  const bf16_t *pool;
+  int n_pages, Hkv, G, D, split_tokens, ctx_bound, n_rows, max_splits;
+  float cscale;
+  float *part_o, *part_ml;
+  bf16_t *out;  // [rows, Hq, D]
+};
+
+struct AttnPrefillArgs {
+  const bf16_t *q;
+  int q_row_stride;
+  const int32_t *cu, *start_pos;
+  int n_seqs, n_tok;
+  const int32_t *page_table;
+  int page_stride;
+  const bf16_t *pool;
+  int n_pages, Hkv, G, D, split_tokens, ctx_bound;
+  float cscale;
+  bf16_t *out;  // [n_tok, Hq, D]
+};
+
+struct RmsNormArgs {
+  const bf16_t *x;
+  int ldx;
+  const int32_t *tok;
+  const bf16_t *embed;
+  int vocab, d;
+  const bf16_t *gain;
+  float eps;
+  bf16_t *y;
+  int ldy;
+  bf16_t *x_copy;
+  int ldc, rows;
+};
+
+struct GemmArgs {
+  const bf16_t *A;
+  int lda;
+  const bf16_t *W;
+  int ldw;
+  bf16_t *C;
+  int ldc;
+  const bf16_t *R;
+  int ldr, M, N, K;
+};
+
+struct LmHeadArgs {
+  const bf16_t *Z;
+  int ldz;
+  const bf16_t *W;
+  int K, V;
+  const int32_t *target;
+  int M;
+  float *part, *tgt_logit, *out;
+};
+
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t st);
+hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t st);
+hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st);
+hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
+hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);  // lm-head + vocab merge
+
+}  // namespace ril

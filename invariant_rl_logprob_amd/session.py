@@ -1,0 +1,151 @@
+"""Host-side resource handling around the C ABI (no arithmetic of the method).
+
+A ``Session`` owns one model handle, its workspace, a KV pool with its host page
+allocator, and a page list per sequence.  It turns per-sequence torch tensors into
+the C batch descriptors and calls the library on the current torch stream.  Device
+memory comes from torch; every computation happens in libril.so.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import (RIL_ATTN_GQA, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch, make_prefill_batch,
+               ril_decode_step_logprobs, ril_kv_alloc, ril_kv_assign, ril_kv_free, ril_kv_page_bytes,
+               ril_kv_release, ril_kv_write, ril_model_create, ril_model_desc, ril_model_destroy,
+               ril_prefill_logprobs, ril_workspace_bytes, ril_ws_attn_offset)
+
+PAGE = 16
+
+
+def _i32(x, device):
+    return torch.as_tensor(x, dtype=torch.int32).to(device)
+
+
+class Session:
+    """One model + one KV pool on one device."""
+
+    def __init__(self, *, n_q_heads, n_kv_heads, head_dim, vocab, d_head, w_lm, max_rows, max_tokens,
+                 max_ctx, pool_pages, softmax_scale, rms_eps=1e-6, split_tokens=512, shuffle_seed=0,
+                 input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
+                 norm_final=None, device="cuda"):
+        self.device = torch.device(device)
+        self._keep = [w_lm, embed, w_qkv, w_o, norm_attn, norm_final]
+        p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        self.desc = ril_model_desc(RIL_ATTN_GQA, input_mode, d_model, n_q_heads, n_kv_heads, head_dim,
+                                   d_head, vocab, PAGE, split_tokens, max_rows, max_tokens, max_ctx,
+                                   softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o), p(norm_attn),
+                                   p(norm_final), p(w_lm))
+        self.model = ril_model_create(self.desc)
+        self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
+        self.max_ctx = max_ctx
+        self.ws = torch.empty(ril_workspace_bytes(self.model), dtype=torch.uint8, device=self.device)
+        self.page_bytes = ril_kv_page_bytes(self.model)
+        self.pool = torch.empty(pool_pages * self.page_bytes, dtype=torch.uint8, device=self.device)
+        self.kv = ril_kv_alloc(self.model, self.pool, shuffle_seed)
+        self.pages: Dict[object, List[int]] = {}
+
+    def close(self):
+        if getattr(self, "kv", None):
+            ril_kv_free(self.kv)
+            self.kv = None
+        if getattr(self, "model", None):
+            ril_model_destroy(self.model)
+            self.model = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- pages ---------------------------------------------------------------
+    def ensure(self, seq, n_tokens: int) -> None:
+        have = self.pages.setdefault(seq, [])
+        need = math.ceil(n_tokens / PAGE) - len(have)
+        if need > 0:
+            have.extend(ril_kv_assign(self.kv, need))
+
+    def release(self, seq) -> None:
+        ids = self.pages.pop(seq, [])
+        if ids:
+            ril_kv_release(self.kv, ids)
+
+    def page_table(self, seqs: Sequence, ctx_bound: int) -> torch.Tensor:
+        stride = max(1, math.ceil(ctx_bound / PAGE))
+        t = torch.full((len(seqs), stride), -1, dtype=torch.int32)
+        for i, s in enumerate(seqs):
+            ids = self.pages[s][:stride]
+            t[i, : len(ids)] = torch.tensor(ids, dtype=torch.int32)
+        return t.to(self.device)
+
+    # -- calls -----------------------------------------------------------------
+    def _packed(self, seqs, starts, lens):
+        cu = [0]
+        for n in lens:
+            cu.append(cu[-1] + int(n))
+        bound = max(int(s) + int(n) for s, n in zip(starts, lens))
+        for s, st, n in zip(seqs, starts, lens):
+            self.ensure(s, int(st) + int(n))
+        return cu, bound
+
+    def write_kv(self, seqs, starts, ks, vs) -> None:
+        """The shared write path alone: k/v [n_i, Hkv, D] of sequence i at positions starts[i].."""
+        lens = [k.shape[0] for k in ks]
+        cu, bound = self._packed(seqs, starts, lens)
+        k = torch.cat(list(ks)).contiguous()
+        v = torch.cat(list(vs)).contiguous()
+        cu_t, st_t = _i32(cu, self.device), _i32(list(starts), self.device)
+        pt = self.page_table(seqs, bound)
+        b = make_prefill_batch(cu_tokens=cu_t, start_pos=st_t, page_table=pt, max_ctx_bound=bound,
+                               k=k, v=v, total_tokens=cu[-1])
+        ril_kv_write(self.model, self.kv, b)
+        self._last = (k, v, cu_t, st_t, pt)
+
+    def prefill(self, seqs, starts, *, targets, qs=None, ks=None, vs=None, tokens=None,
+                ctx_bound: Optional[int] = None) -> torch.Tensor:
+        """Packed prefill of sequences seqs[i] at positions starts[i].. ; returns fp32 [total]."""
+        src = tokens if tokens is not None else qs
+        lens = [t.shape[0] for t in src]
+        cu, bound = self._packed(seqs, starts, lens)
+        bound = ctx_bound or bound
+        cat = lambda xs: None if xs is None else torch.cat(list(xs)).contiguous()  # noqa: E731
+        q, k, v, tok = cat(qs), cat(ks), cat(vs), cat(tokens)
+        tgt = torch.cat(list(targets)).to(torch.int32).contiguous()
+        cu_t, st_t = _i32(cu, self.device), _i32(list(starts), self.device)
+        pt = self.page_table(seqs, bound)
+        out = torch.empty(cu[-1], dtype=torch.float32, device=self.device)
+        b = make_prefill_batch(cu_tokens=cu_t, start_pos=st_t, page_table=pt, max_ctx_bound=bound,
+                               target_ids=tgt, token_ids=tok, q=q, k=k, v=v, total_tokens=cu[-1])
+        ril_prefill_logprobs(self.model, self.kv, b, out, self.ws)
+        self._last = (q, k, v, tok, tgt, cu_t, st_t, pt)
+        return out
+
+    def decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None,
+               ctx_bound: Optional[int] = None) -> torch.Tensor:
+        """One decode step: row i of sequence seqs[i] at context ctx[i]; returns fp32 [rows]."""
+        ctx = [int(c) for c in ctx]
+        for s, c in zip(seqs, ctx):
+            self.ensure(s, c)
+        bound = ctx_bound or max(ctx)
+        ctx_t = _i32(ctx, self.device)
+        pt = self.page_table(seqs, bound)
+        tgt = targets.to(torch.int32).contiguous()
+        out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
+        b = make_decode_batch(ctx_len=ctx_t, page_table=pt, max_ctx_bound=bound, target_ids=tgt,
+                              token_ids=None if tokens is None else tokens.contiguous(),
+                              q=None if q is None else q.contiguous(),
+                              k=None if k is None else k.contiguous(),
+                              v=None if v is None else v.contiguous())
+        ril_decode_step_logprobs(self.model, self.kv, b, out, self.ws)
+        self._last = (ctx_t, pt, tgt, tokens, q, k, v)
+        return out
+
+    def attn_out(self, rows: int) -> torch.Tensor:
+        """bf16 [rows, Hq, D] attention output of the last call (a workspace view)."""
+        off = ril_ws_attn_offset(self.model)
+        n = rows * self.H * self.D
+        return self.ws[off: off + 2 * n].view(torch.bfloat16).view(rows, self.H, self.D)
