@@ -81,7 +81,7 @@ typedef struct ril_model_desc {
                             TOKENS: = d_model; QKV: = o-proj out width if w_o, else Hq*D */
   int32_t vocab;         /* V >= 1 */
   int32_t page_tokens;   /* tokens per KV page: 16 */
-  int32_t split_tokens;  /* attention KV split in tokens: a multiple of 64 (512 by default) */
+  int32_t split_tokens;  /* attention KV split in tokens: a multiple of 64, <= 1024 (512 here) */
   int32_t max_rows;      /* most rows one decode call may carry */
   int32_t max_tokens;    /* most tokens one prefill call may carry */
   int32_t max_ctx;       /* longest context (tokens, including the current one) */
@@ -186,6 +186,26 @@ ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_de
  * for.  Needs no workspace, so n_seqs and total_tokens are not bounded by
  * max_tokens. */
 ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b, void *stream);
+
+/* Kernel trace, a profiling hook.  While enabled, every launch of the kernels
+ * below is bracketed by two hipEvents recorded on the launch stream (the
+ * kernels themselves are unchanged).  ril_trace_read waits for the events
+ * recorded so far -- a host wait, so call it outside a timed loop -- and
+ * returns the summed elapsed milliseconds and the launch count of one kernel
+ * since the last ril_trace_enable.  Process-wide; not for concurrent use. */
+enum {
+  RIL_K_KV_WRITE = 0,     /* S5 */
+  RIL_K_ATTN_SPLIT = 1,   /* S8  decode split-KV attention */
+  RIL_K_ATTN_MERGE = 2,   /* S9  decode split merge */
+  RIL_K_ATTN_PREFILL = 3, /* S10 */
+  RIL_K_RMSNORM = 4,      /* S2/S3 */
+  RIL_K_GEMM = 5,         /* S4 */
+  RIL_K_LM_HEAD = 6,      /* S11 */
+  RIL_K_VOCAB_MERGE = 7,  /* S12 */
+  RIL_K_COUNT = 8
+};
+ril_status ril_trace_enable(int on);
+ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches);
 
 /* Debug/test view: the attention output of the last call on this thread's
  * workspace is bf16 [rows, Hq, D] at byte offset ril_ws_attn_offset(m) of

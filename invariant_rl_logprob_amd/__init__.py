@@ -82,11 +82,21 @@ _decode = _sig("ril_decode_step_logprobs", _c_int,
                [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp, ctypes.c_size_t, _vp])
 _kv_write = _sig("ril_kv_write", _c_int, [_vp, _vp, ctypes.POINTER(ril_prefill_batch), _vp])
 _last_error = _sig("ril_last_error", ctypes.c_char_p, [])
+_trace_enable = _sig("ril_trace_enable", _c_int, [_c_int])
+_trace_read = _sig("ril_trace_read", _c_int, [_c_int, ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(ctypes.c_int64)])
 
 EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril_kv_page_bytes",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
-            "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error")
+            "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_trace_enable",
+            "ril_trace_read")
+
+# kernel ids of the trace hook
+RIL_K_KV_WRITE, RIL_K_ATTN_SPLIT, RIL_K_ATTN_MERGE, RIL_K_ATTN_PREFILL = 0, 1, 2, 3
+RIL_K_RMSNORM, RIL_K_GEMM, RIL_K_LM_HEAD, RIL_K_VOCAB_MERGE, RIL_K_COUNT = 4, 5, 6, 7, 8
+KERNEL_NAMES = ("kv_write", "attn_split", "attn_merge", "attn_prefill", "rmsnorm", "gemm", "lm_head",
+                "vocab_merge")
 
 
 class RilError(RuntimeError):
@@ -201,3 +211,15 @@ def ril_decode_step_logprobs(model: int, kv: int, batch: ril_decode_batch, logpr
 
 def ril_kv_write(model: int, kv: int, batch: ril_prefill_batch, stream=None) -> None:
     _check(_kv_write(model, kv, ctypes.byref(batch), _stream(stream)), "ril_kv_write")
+
+
+def ril_trace_enable(on: bool) -> None:
+    _check(_trace_enable(1 if on else 0), "ril_trace_enable")
+
+
+def ril_trace_read(kernel: int):
+    """(total milliseconds, launches) of one kernel since the last ril_trace_enable."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(_trace_read(kernel, ctypes.byref(ms), ctypes.byref(n)), "ril_trace_read")
+    return ms.value, n.value

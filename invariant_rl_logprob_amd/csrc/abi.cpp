@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <climits>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -68,8 +69,8 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
     return fail(RIL_EUNSUPPORTED, "model_create: group size %d (1, 2, 4, 8 or 16)", G);
   if (d.page_tokens != 16) return fail(RIL_EUNSUPPORTED, "model_create: page_tokens %d (16)", d.page_tokens);
-  if (d.split_tokens <= 0 || d.split_tokens % 64)
-    return fail(RIL_EINVAL, "model_create: split_tokens %d (positive multiple of 64)", d.split_tokens);
+  if (d.split_tokens <= 0 || d.split_tokens % 64 || d.split_tokens > 1024)
+    return fail(RIL_EINVAL, "model_create: split_tokens %d (a multiple of 64, at most 1024)", d.split_tokens);
   if (d.vocab < 1) return fail(RIL_EINVAL, "model_create: vocab %d", d.vocab);
   if (d.max_rows < 1 || d.max_tokens < 1 || d.max_ctx < 1)
     return fail(RIL_EINVAL, "model_create: limits %d/%d/%d", d.max_rows, d.max_tokens, d.max_ctx);
@@ -201,10 +202,90 @@ extern "C" void ril_kv_free(ril_kv *kv) { delete kv; }
 static bf16_t *wsb(void *ws, size_t off) { return reinterpret_cast<bf16_t *>(static_cast<char *>(ws) + off); }
 static float *wsf(void *ws, size_t off) { return reinterpret_cast<float *>(static_cast<char *>(ws) + off); }
 
-#define RIL_LAUNCH(expr)                                                               \
-  do {                                                                                 \
-    hipError_t e_ = (expr);                                                            \
-    if (e_ != hipSuccess) return fail(RIL_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+// ---------------------------------------------------------------------------
+// kernel trace: hipEvent pairs recorded around launches while enabled
+// ---------------------------------------------------------------------------
+
+namespace {
+struct TraceRec {
+  int k;
+  hipEvent_t a, b;
+};
+std::mutex g_tr_mu;
+bool g_tr_on = false;
+std::vector<TraceRec> g_tr_pending;
+std::vector<hipEvent_t> g_tr_pool;
+double g_tr_ms[RIL_K_COUNT];
+int64_t g_tr_n[RIL_K_COUNT];
+
+hipEvent_t trace_event() {
+  if (!g_tr_pool.empty()) {
+    hipEvent_t e = g_tr_pool.back();
+    g_tr_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void trace_drain() {  // caller holds g_tr_mu
+  for (const TraceRec &r : g_tr_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      g_tr_ms[r.k] += ms;
+      g_tr_n[r.k] += 1;
+    }
+    g_tr_pool.push_back(r.a);
+    g_tr_pool.push_back(r.b);
+  }
+  g_tr_pending.clear();
+}
+
+// Launch `fn` and, while tracing, bracket it with events on `st`.
+template <typename F>
+hipError_t traced(int k, hipStream_t st, F fn) {
+  if (!g_tr_on) return fn();
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  hipEvent_t a = trace_event(), b = trace_event();
+  const bool ra = a && hipEventRecord(a, st) == hipSuccess;
+  hipError_t e = fn();
+  const bool rb = b && hipEventRecord(b, st) == hipSuccess;
+  if (ra && rb) {
+    g_tr_pending.push_back({k, a, b});
+  } else {
+    if (a) g_tr_pool.push_back(a);
+    if (b) g_tr_pool.push_back(b);
+  }
+  return e;
+}
+}  // namespace
+
+extern "C" ril_status ril_trace_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  trace_drain();
+  for (int k = 0; k < RIL_K_COUNT; ++k) {
+    g_tr_ms[k] = 0.0;
+    g_tr_n[k] = 0;
+  }
+  g_tr_on = on != 0;
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches) {
+  if (kernel < 0 || kernel >= RIL_K_COUNT || !total_ms || !launches)
+    return fail(RIL_EINVAL, "trace_read: bad argument");
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  trace_drain();
+  *total_ms = g_tr_ms[kernel];
+  *launches = g_tr_n[kernel];
+  return RIL_OK;
+}
+
+#define RIL_LAUNCH(kid, expr)                                                                 \
+  do {                                                                                        \
+    hipError_t e_ = traced((kid), st, [&]() { return (expr); });                              \
+    if (e_ != hipSuccess) return fail(RIL_EHIP, "%s: %s", #expr, hipGetErrorString(e_));      \
   } while (0)
 
 static ril_status check_common(const ril_model *m, ril_kv *kv, void *ws, size_t ws_bytes,
@@ -233,16 +314,17 @@ static ril_status run_head(const ril_model *m, int rows, const int32_t *targets,
     const bool tok = d.input_mode == RIL_INPUT_TOKENS;
     GemmArgs g{src, qw, (const bf16_t *)d.w_o, qw, wsb(ws, m->off_y), d.d_head,
                tok ? wsb(ws, m->off_x) : nullptr, d.d_model, rows, d.d_head, qw};
-    RIL_LAUNCH(launch_gemm(g, st));
+    RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
     src = wsb(ws, m->off_y);
     ld = d.d_head;
   }
   RmsNormArgs r{src, ld, nullptr, nullptr, d.vocab, d.d_head, (const bf16_t *)d.norm_final, d.rms_eps,
                 wsb(ws, m->off_z), d.d_head, nullptr, 0, rows};
-  RIL_LAUNCH(launch_rmsnorm(r, st));
+  RIL_LAUNCH(RIL_K_RMSNORM, launch_rmsnorm(r, st));
   LmHeadArgs lh{wsb(ws, m->off_z), d.d_head, (const bf16_t *)d.w_lm, d.d_head, d.vocab, targets, rows,
                 wsf(ws, m->off_vpart), wsf(ws, m->off_tgt), out};
-  RIL_LAUNCH(launch_lm_head(lh, st));
+  RIL_LAUNCH(RIL_K_LM_HEAD, launch_lm_head(lh, st));
+  RIL_LAUNCH(RIL_K_VOCAB_MERGE, launch_vocab_merge(lh, st));
   return RIL_OK;
 }
 
@@ -252,10 +334,10 @@ static ril_status run_token_front(const ril_model *m, int rows, const int32_t *t
   const int wqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   RmsNormArgs r{nullptr, 0, tok, (const bf16_t *)d.embed, d.vocab, d.d_model, (const bf16_t *)d.norm_attn,
                 d.rms_eps, wsb(ws, m->off_h), d.d_model, wsb(ws, m->off_x), d.d_model, rows};
-  RIL_LAUNCH(launch_rmsnorm(r, st));
+  RIL_LAUNCH(RIL_K_RMSNORM, launch_rmsnorm(r, st));
   GemmArgs g{wsb(ws, m->off_h), d.d_model, (const bf16_t *)d.w_qkv, d.d_model, wsb(ws, m->off_qkv), wqkv,
              nullptr, 0, rows, wqkv, d.d_model};
-  RIL_LAUNCH(launch_gemm(g, st));
+  RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
   return RIL_OK;
 }
 
@@ -294,7 +376,8 @@ extern "C" ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_pre
   KvWriteArgs a{(const bf16_t *)b->k, (const bf16_t *)b->v, d.n_kv_heads * d.head_dim, b->total_tokens, 0,
                 b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table, b->page_stride,
                 (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
-  RIL_LAUNCH(launch_kv_write(a, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(a, st));
   return RIL_OK;
 }
 
@@ -326,11 +409,11 @@ extern "C" ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const
   }
   KvWriteArgs kw{k, v, kv_stride, T, 0, b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table,
                  b->page_stride, (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
-  RIL_LAUNCH(launch_kv_write(kw, st));
+  RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(kw, st));
   AttnPrefillArgs ap{q, q_stride, b->cu_tokens, b->start_pos, b->n_seqs, T, b->page_table, b->page_stride,
                      (const bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, m->G, d.head_dim, d.split_tokens,
                      b->max_ctx_bound, m->cscale, wsb(ws, m->off_attn)};
-  RIL_LAUNCH(launch_attn_prefill(ap, st));
+  RIL_LAUNCH(RIL_K_ATTN_PREFILL, launch_attn_prefill(ap, st));
   return run_head(m, T, b->target_ids, logprob_out, ws, st);
 }
 
@@ -371,10 +454,11 @@ extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, c
   }
   KvWriteArgs kw{k, v, kv_stride, R, 1, nullptr, nullptr, 0, b->ctx_len, b->page_table, b->page_stride,
                  (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
-  RIL_LAUNCH(launch_kv_write(kw, st));
+  RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(kw, st));
   AttnDecodeArgs ad{q, q_stride, b->ctx_len, b->page_table, b->page_stride, (const bf16_t *)kv->pool,
                     kv->n_pages, d.n_kv_heads, m->G, d.head_dim, d.split_tokens, b->max_ctx_bound, R,
                     m->max_splits, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn)};
-  RIL_LAUNCH(launch_attn_decode(ad, st));
+  RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_attn_split(ad, st));
+  RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_attn_merge(ad, st));
   return run_head(m, R, b->target_ids, logprob_out, ws, st);
 }

@@ -92,34 +92,61 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n_valid) {
   return v;
 }
 
+// One 64-token tile of K and V in MFMA operand registers (16-byte loads per lane).
+//   k[2kc+h][c] : A operand of S^T = K Q^T for M-block (kc, h), dims 32c .. 32c+31;
+//                 row r <-> token 32kc + 8(r/4) + 4h + r%4
+//   v[kc][db]   : A operand of o^T += V^T P^T for 32-token step kc, dims 16db .. 16db+15;
+//                 k-slot 8(lane/16) + j <-> token 32kc + 8(lane/16) + j
+template <int D>
+struct KVTile {
+  u32x4 k[4][D / 32];
+  u32x4 v[2][D / 16];
+};
+
+// pg[k]: K block of the tile's k-th page (its V block follows at +16*D).
+template <int D>
+__device__ __forceinline__ void load_tile(KVTile<D> &t, const bf16_t *const (&pg)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int rq = r16 >> 2, ri = r16 & 3;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16_t *kb = pg[2 * kc + (rq >> 1)] + grp * 128 + h * 64 + (rq & 1) * 32 + ri * 8;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) t.k[2 * kc + h][c] = ld16(kb + c * 512);
+    }
+  }
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const bf16_t *vb = pg[2 * kc + (grp >> 1)] + 16 * D + (grp & 1) * (8 * D) + r16 * 8;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) t.v[kc][db] = ld16(vb + db * 128);
+  }
+}
+
 // One 64-token KV tile for the 16 query rows (MFMA columns) of this wave.
-//   pg[k]   : K block of the tile's k-th page (V block at +16*D)
 //   qop     : B operand of S^T = K Q^T (lane: column lane%16, dims 32c + 8(lane/16) ..)
 //   pos     : this lane's column's query position (-1: padding column)
 //   vbound  : V values of tokens >= vbound are read as 0 (beyond any column's context)
 // State per lane = its column's (m, l) and o^T[16db + 4(lane/16) + i].
 // MAYBE_INACTIVE: some column may have pos < tile_start; such columns keep their state.
 template <int D, bool MAYBE_INACTIVE>
-__device__ __forceinline__ void attn_tile(const bf16_t *const (&pg)[4], int tile_start,
+__device__ __forceinline__ void attn_tile(const KVTile<D> &t, int tile_start,
                                           const bf16x8 (&qop)[D / 32], int pos, int vbound,
                                           float cscale, float &m, float &l, f32x4 (&o)[D / 16]) {
   const int lane = threadIdx.x & 63;
-  const int grp = lane >> 4, r16 = lane & 15;
-  // S^T for M-block (kc, h): row r <-> token 32kc + 8(r/4) + 4h + r%4.
+  const int grp = lane >> 4;
   f32x4 s[4];
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
+  for (int mb = 0; mb < 4; ++mb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rq = r16 >> 2, ri = r16 & 3;
-      const bf16_t *kb = pg[2 * kc + (rq >> 1)] + grp * 128 + h * 64 + (rq & 1) * 32 + ri * 8;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) acc = mfma(as_bf16x8(ld16(kb + c * 512)), qop[c], acc);
-      s[2 * kc + h] = acc;
-    }
+    for (int c = 0; c < D / 32; ++c) acc = mfma(as_bf16x8(t.k[mb][c]), qop[c], acc);
+    s[mb] = acc;
   }
-  // Output lane holds rows 4*grp + i -> token tile_start + 32kc + 8grp + 4h + i.
+  // Output lane holds rows 4*grp + i -> token tile_start + 32kc + 8grp + 4h + i (mb = 2kc + h).
   float tmax = neg_inf();
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -162,11 +189,10 @@ __device__ __forceinline__ void attn_tile(const bf16_t *const (&pg)[4], int tile
   for (int db = 0; db < D / 16; ++db) on[db] = o[db] * alpha;
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
-    const bf16_t *vb = pg[2 * kc + (grp >> 1)] + 16 * D + (grp & 1) * (8 * D) + r16 * 8;
     const int n_valid = vbound - (tile_start + 32 * kc + 8 * grp);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      u32x4 vv = ld16(vb + db * 128);
+      u32x4 vv = t.v[kc][db];
       if (n_valid < 8) vv = keep_first(vv, n_valid);
       on[db] = mfma(as_bf16x8(vv), pop[kc], on[db]);
     }
@@ -212,18 +238,35 @@ __device__ __forceinline__ void load_qop(bf16x8 (&qop)[D / 32], const bf16_t *qr
   }
 }
 
-__device__ __forceinline__ const bf16_t *page_ptr(const bf16_t *pool, const int32_t *pt, int pi,
-                                                  int n_pages, int Hkv, int g, int D, bool &bad) {
-  int pid = pt[pi];
-  if ((unsigned)pid >= (unsigned)n_pages) {
-    bad = true;
-    pid = 0;
-  }
-  return pool + ((long)pid * Hkv + g) * (32 * D);
+// Page ids of one split, one per lane: lane i holds the id of page index
+// min(first + i, last) of the sequence (the clamp keeps reads in bounds; tokens beyond
+// the context are masked).  Returns whether any id in range lies outside the pool.
+__device__ __forceinline__ bool split_pages(const int32_t *pt, int first, int last, int n_pages,
+                                            int &pid) {
+  const int lane = threadIdx.x & 63;
+  int p = pt[min(first + lane, last)];
+  const bool bad = (unsigned)p >= (unsigned)n_pages;
+  pid = bad ? 0 : p;
+  return __any(bad);
+}
+
+// K block base of page slot `idx` of the split (0 .. 4*tiles-1): a wave-uniform readlane.
+__device__ __forceinline__ const bf16_t *page_base(const bf16_t *pool, int pid_lane, int idx, int Hkv,
+                                                   int g, int D) {
+  const int p = __builtin_amdgcn_readlane(pid_lane, idx);
+  return pool + ((long)p * Hkv + g) * (32 * D);
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pages(const bf16_t *(&pg)[4], const bf16_t *pool, int pid_lane,
+                                           int tile, int Hkv, int g) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pg[k] = page_base(pool, pid_lane, 4 * tile + k, Hkv, g, D);
 }
 
 // ---------------------------------------------------------------------------
-// S8: decode split kernel.  grid (max splits, Hkv, rows), one wave each.
+// S8: decode split kernel.  grid (max splits, Hkv, rows), one wave each.  The next
+// tile's K/V loads are issued before the current tile is computed.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_split_kernel(
@@ -239,22 +282,34 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   const int Hq = Hkv * G;
   const int n = lane & 15, grp = lane >> 4;
   const bool col_ok = n < G;
+  const int s1 = min(ctx, s0 + split_tokens);
+  const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
+  int pid;
+  const bool bad = split_pages(page_table + (long)row * page_stride, s0 / kPage, (ctx - 1) / kPage,
+                               n_pages, pid);
+  KVTile<D> buf0, buf1;
+  const bf16_t *pg[4];
+  tile_pages<D>(pg, pool, pid, 0, Hkv, g);
+  load_tile<D>(buf0, pg);
   bf16x8 qop[D / 32];
   load_qop<D>(qop, q + (long)row * q_row_stride + (g * G + (col_ok ? n : 0)) * D, col_ok);
   float m = neg_inf(), l = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int s1 = min(ctx, s0 + split_tokens);
-  const int last_page = (ctx - 1) / kPage;
-  const int32_t *pt = page_table + (long)row * page_stride;
-  bool bad = false;
-  for (int t0 = s0; t0 < s1; t0 += kTile) {
-    const bf16_t *pg[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      pg[k] = page_ptr(pool, pt, min(t0 / kPage + k, last_page), n_pages, Hkv, g, D, bad);
-    attn_tile<D, false>(pg, t0, qop, ctx - 1, ctx, cscale, m, l, o);
+  for (int t = 0; t < n_tiles; t += 2) {
+    if (t + 1 < n_tiles) {
+      tile_pages<D>(pg, pool, pid, t + 1, Hkv, g);
+      load_tile<D>(buf1, pg);
+    }
+    attn_tile<D, false>(buf0, s0 + t * kTile, qop, ctx - 1, ctx, cscale, m, l, o);
+    if (t + 1 < n_tiles) {
+      if (t + 2 < n_tiles) {
+        tile_pages<D>(pg, pool, pid, t + 2, Hkv, g);
+        load_tile<D>(buf0, pg);
+      }
+      attn_tile<D, false>(buf1, s0 + (t + 1) * kTile, qop, ctx - 1, ctx, cscale, m, l, o);
+    }
   }
   if (bad) l = __builtin_nanf("");
   if (!col_ok) return;
@@ -366,22 +421,24 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(
   const int last_page = p_max / kPage;
   bool bad = false;
   const int n_splits = p_max / split_tokens + 1;
+  KVTile<D> tile;
   for (int si = 0; si < n_splits; ++si) {
     const int s0 = si * split_tokens;
     const int s1 = min(p_max + 1, s0 + split_tokens);
+    int pid;
+    bad |= split_pages(pt, s0 / kPage, last_page, n_pages, pid);
     float m = neg_inf(), l = 0.f;
     f32x4 o[D / 16];
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int t0 = s0; t0 < s1; t0 += kTile) {
       const bf16_t *pg[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        pg[k] = page_ptr(pool, pt, min(t0 / kPage + k, last_page), n_pages, Hkv, g, D, bad);
+      tile_pages<D>(pg, pool, pid, (t0 - s0) / kTile, Hkv, g);
+      load_tile<D>(tile, pg);
       if (t0 <= p_min)
-        attn_tile<D, false>(pg, t0, qop, pos, p_max + 1, cscale, m, l, o);
+        attn_tile<D, false>(tile, t0, qop, pos, p_max + 1, cscale, m, l, o);
       else
-        attn_tile<D, true>(pg, t0, qop, pos, p_max + 1, cscale, m, l, o);
+        attn_tile<D, true>(tile, t0, qop, pos, p_max + 1, cscale, m, l, o);
     }
     if (s0 <= pos) {
       float os[D / 4];
@@ -429,22 +486,28 @@ hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t st) {
+hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st) {
   const int n_split_grid = (a.ctx_bound + a.split_tokens - 1) / a.split_tokens;
-  dim3 g1(n_split_grid, a.Hkv, a.n_rows), g2(a.Hkv * a.G, a.n_rows);
-  if (a.D == 128) {
-    hipLaunchKernelGGL(attn_decode_split_kernel<128>, g1, dim3(64), 0, st, a.q, a.q_row_stride, a.ctx_len,
-                       a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G, a.split_tokens,
-                       a.ctx_bound, a.cscale, a.part_o, a.part_ml, a.max_splits);
-    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, g2, dim3(64), 0, st, a.ctx_len, a.ctx_bound,
+  dim3 grid(n_split_grid, a.Hkv, a.n_rows);
+  if (a.D == 128)
+    hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(64), 0, st, a.q, a.q_row_stride,
+                       a.ctx_len, a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G,
+                       a.split_tokens, a.ctx_bound, a.cscale, a.part_o, a.part_ml, a.max_splits);
+  else
+    hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(64), 0, st, a.q, a.q_row_stride,
+                       a.ctx_len, a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G,
+                       a.split_tokens, a.ctx_bound, a.cscale, a.part_o, a.part_ml, a.max_splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st) {
+  dim3 grid(a.Hkv * a.G, a.n_rows);
+  if (a.D == 128)
+    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, grid, dim3(64), 0, st, a.ctx_len, a.ctx_bound,
                        a.split_tokens, a.Hkv * a.G, a.max_splits, a.part_o, a.part_ml, a.out);
-  } else {
-    hipLaunchKernelGGL(attn_decode_split_kernel<64>, g1, dim3(64), 0, st, a.q, a.q_row_stride, a.ctx_len,
-                       a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G, a.split_tokens,
-                       a.ctx_bound, a.cscale, a.part_o, a.part_ml, a.max_splits);
-    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, g2, dim3(64), 0, st, a.ctx_len, a.ctx_bound,
+  else
+    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, grid, dim3(64), 0, st, a.ctx_len, a.ctx_bound,
                        a.split_tokens, a.Hkv * a.G, a.max_splits, a.part_o, a.part_ml, a.out);
-  }
   return hipGetLastError();
 }
 

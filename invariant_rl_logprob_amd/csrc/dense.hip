@@ -67,6 +67,113 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The K loop of every GEMM here: acc[mb][nb] += A_mb(k) B_nb(k)^T for k = 0, 32, 64, ...
+// in order, one v_mfma_f32_16x16x32_bf16 per step and block.  Operand loads run PF steps
+// ahead through a register ring (issue order only; the accumulation order is fixed).
+// ---------------------------------------------------------------------------
+template <int MB, int NB, int PF>
+__device__ __forceinline__ void kloop(f32x4 (&acc)[MB][NB], const bf16_t *const (&ap)[MB],
+                                      const bf16_t *const (&wp)[NB], int K) {
+  constexpr int S = PF + 1;
+  u32x4 ra[S][MB], rb[S][NB];
+  const int nk = K / 32;
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    if (s < nk) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) ra[s][mb] = ld16(ap[mb] + s * 32);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) rb[s][nb] = ld16(wp[nb] + s * 32);
+    }
+  }
+  for (int k0 = 0; k0 < nk; k0 += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int ks = k0 + j;
+      if (ks < nk) {
+        const int kp = ks + PF;
+        if (kp < nk) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) ra[(j + PF) % S][mb] = ld16(ap[mb] + kp * 32);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) rb[(j + PF) % S][nb] = ld16(wp[nb] + kp * 32);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = mfma(as_bf16x8(ra[j][mb]), as_bf16x8(rb[j][nb]), acc[mb][nb]);
+      }
+    }
+  }
+}
+
+// The lm-head's K loop.  Every output column of vocabulary tile `tile` accumulates its
+// 32-wide K steps in the fixed rotated order r, r+1, ..., nk-1, 0, ..., r-1 with
+// r = (37 * tile) mod nk: one order per column, chosen by the column alone (never by M,
+// the batch or the grid), which spreads the 505 tiles' concurrent weight reads over the
+// HBM channels instead of having every tile read the same K offset at the same time.
+// The activation operand is staged through LDS in chunks of 8 K steps (each of the four
+// waves loads two steps for the whole workgroup); weight operands run PF steps ahead in
+// a register ring.  All four waves must call this (it synchronises the workgroup).
+constexpr int kLdsSteps = 8;
+__device__ __forceinline__ int lm_rot(int tile, int nk) { return (37 * tile) % nk; }
+
+template <int MB, int PF>
+__device__ __forceinline__ void kloop_lm(f32x4 (&acc)[MB][4], const bf16_t *const (&ap)[MB],
+                                         const bf16_t *const (&wp)[4], int K, int rot,
+                                         u32x4 (*lds)[kLdsSteps * MB * 64]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int S = PF + 1;
+  const int nk = K / 32;
+  auto kidx = [&](int s) {
+    const int t = s + rot;
+    return t >= nk ? t - nk : t;
+  };
+  u32x4 rb[S][4];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    if (s < nk) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) rb[s][nb] = ld16(wp[nb] + kidx(s) * 32);
+    }
+  }
+  for (int k0 = 0; k0 < nk; k0 += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int ks = k0 + j;
+      if (ks < nk) {
+        if (ks % kLdsSteps == 0) {
+          __syncthreads();  // every wave is done with the buffer about to be refilled
+          const int buf = (ks / kLdsSteps) & 1;
+#pragma unroll
+          for (int q = 0; q < kLdsSteps / 4; ++q) {
+            const int st = wave * (kLdsSteps / 4) + q;
+            if (ks + st < nk) {
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) lds[buf][(st * MB + mb) * 64 + lane] = ld16(ap[mb] + kidx(ks + st) * 32);
+            }
+          }
+          __syncthreads();
+        }
+        const int kp = ks + PF;
+        if (kp < nk) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) rb[(j + PF) % S][nb] = ld16(wp[nb] + kidx(kp) * 32);
+        }
+        const int buf = (ks / kLdsSteps) & 1, st = ks % kLdsSteps;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x8 a = as_bf16x8(lds[buf][(st * MB + mb) * 64 + lane]);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(a, as_bf16x8(rb[j][nb]), acc[mb][nb]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // S4: C[M,N] = bf16(A[M,K] W[N,K]^T) or bf16(R + bf16(A W^T)).
 // Workgroup = 4 waves side by side along N; a wave owns MB x NB 16x16 blocks.
 // ---------------------------------------------------------------------------
@@ -92,17 +199,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t *__restrict__ A,
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < K; k += 32) {
-    bf16x8 a[MB], b[NB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) a[mb] = as_bf16x8(ld16(ap[mb] + k));
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) b[nb] = as_bf16x8(ld16(wp[nb] + k));
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
-  }
+  kloop<MB, NB, 3>(acc, ap, wp, K);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -137,6 +234,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
                                                       float *__restrict__ part,
                                                       float *__restrict__ tgt_logit, int n_vt) {
   __shared__ float red[4][16 * MB];
+  __shared__ u32x4 lds_a[2][kLdsSteps * MB * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
   const int tile = blockIdx.x;
@@ -153,17 +251,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < K; k += 32) {
-    bf16x8 a[MB], b[4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) a[mb] = as_bf16x8(ld16(ap[mb] + k));
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) b[nb] = as_bf16x8(ld16(wp[nb] + k));
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
-  }
+  kloop_lm<MB, 7>(acc, ap, wp, K, lm_rot(tile, K / 32), lds_a);
   bool cval[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) cval[nb] = (c0 + 16 * nb + r16) < V;
@@ -306,8 +394,12 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(lm_head_kernel<4>, grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
                        a.target, a.M, a.part, a.tgt_logit, n_vt);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_vocab_merge(const LmHeadArgs &a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  const int n_vt = (a.V + kVocabTile - 1) / kVocabTile;
   hipLaunchKernelGGL(vocab_merge_kernel, dim3(a.M), dim3(64), 0, st, a.part, a.tgt_logit,
                      a.target, n_vt, a.V, a.out);
   return hipGetLastError();

@@ -1,5 +1,6 @@
 // Host-side launch interface of the HIP kernels (argument bundles + launchers).
-// Every launcher enqueues on the given stream and returns hipGetLastError().
+// Every launcher enqueues exactly one kernel on the given stream and returns
+// hipGetLastError().
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -81,10 +82,12 @@ struct LmHeadArgs {
 };
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t st);
-hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t st);
+hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st);
+hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st);
 hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
-hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);  // lm-head + vocab merge
+hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);
+hipError_t launch_vocab_merge(const LmHeadArgs &a, hipStream_t st);
 
 }  // namespace ril

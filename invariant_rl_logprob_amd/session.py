@@ -144,6 +144,33 @@ class Session:
         self._last = (ctx_t, pt, tgt, tokens, q, k, v)
         return out
 
+    def prepare_decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None,
+                       ctx_bound: Optional[int] = None):
+        """Build a decode batch once; returns (launch, out) where launch() enqueues the step
+        on the current stream with no host-side tensor work (for timed loops)."""
+        ctx = [int(c) for c in ctx]
+        for s, c in zip(seqs, ctx):
+            self.ensure(s, c)
+        bound = ctx_bound or max(ctx)
+        keep = {
+            "ctx": _i32(ctx, self.device), "pt": self.page_table(seqs, bound),
+            "tgt": targets.to(torch.int32).contiguous(),
+            "tok": None if tokens is None else tokens.contiguous(),
+            "q": None if q is None else q.contiguous(), "k": None if k is None else k.contiguous(),
+            "v": None if v is None else v.contiguous(),
+        }
+        out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
+        b = make_decode_batch(ctx_len=keep["ctx"], page_table=keep["pt"], max_ctx_bound=bound,
+                              target_ids=keep["tgt"], token_ids=keep["tok"], q=keep["q"], k=keep["k"],
+                              v=keep["v"])
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+
+        def launch():
+            ril_decode_step_logprobs(self.model, self.kv, b, out, self.ws, stream)
+
+        launch.keep = keep  # the descriptor's tensors live as long as the launcher
+        return launch, out
+
     def attn_out(self, rows: int) -> torch.Tensor:
         """bf16 [rows, Hq, D] attention output of the last call (a workspace view)."""
         off = ril_ws_attn_offset(self.model)
