@@ -35,6 +35,24 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per launch (fetch + write) from the committed rocprofv3 PMC summary,
+    scaled by the copy calibration; None if the kernel's sources changed since."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for s in rec["sources"]:
+        with open(os.path.join(ROOT, "invariant_rl_logprob_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec["source_sha16"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,7 +148,8 @@ def main():
     else:
         roof = {"kernel": "lm_head", "achieved": lm_gbps, "bytes_per_launch": lm_bytes}
     roofline = {"bound": "hbm", "achieved": round(roof["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(roof["achieved"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(roof["achieved"] / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic("attn_decode_split" if roof["kernel"] == "attn_decode_split" else "lm_head"),
                 "kernel": roof["kernel"], "algorithmic_bytes_per_launch": roof["bytes_per_launch"],
                 "avg_launch_us": round(split_us if roof["kernel"] == "attn_decode_split" else kern["lm_head"]["avg_us"], 2)}
 
