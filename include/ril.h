@@ -60,7 +60,13 @@ typedef enum ril_status {
   RIL_EHIP = -5           /* the HIP runtime reported an error */
 } ril_status;
 
-enum { RIL_ATTN_GQA = 0 };
+/* Attention kinds.
+ *   GQA: per-kv-head K and V of head_dim each; q head h reads kv head h*Hkv/Hq.
+ *   MLA: absorbed multi-head latent attention; every q head reads one shared cached
+ *        latent row per token of head_dim + rope_dim values (512 + 64); scores use
+ *        all of it, values its first head_dim (Bitwise-consistent RL post, section 3:
+ *        MLA compresses KV before caching). */
+enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1 };
 enum { RIL_INPUT_TOKENS = 0, RIL_INPUT_QKV = 1 };
 
 /* Model description.  All sizes are fixed for the life of the handle; the
@@ -68,20 +74,22 @@ enum { RIL_INPUT_TOKENS = 0, RIL_INPUT_QKV = 1 };
  * context length or the GPU (Bitwise-consistent RL post, section 2: no
  * kernel choice by batch size, no dynamic split count).                     */
 typedef struct ril_model_desc {
-  int32_t attn_kind;     /* RIL_ATTN_GQA */
+  int32_t attn_kind;     /* RIL_ATTN_GQA | RIL_ATTN_MLA */
   int32_t input_mode;    /* RIL_INPUT_TOKENS: token ids -> embedding -> RMSNorm -> QKV GEMM
                             -> attention -> O GEMM + residual -> RMSNorm -> lm-head;
                             RIL_INPUT_QKV: q/k/v given -> attention -> [O GEMM] -> RMSNorm
                             -> lm-head */
   int32_t d_model;       /* TOKENS: residual width (multiple of 32); QKV: ignored */
-  int32_t n_q_heads;     /* Hq */
-  int32_t n_kv_heads;    /* Hkv; Hq/Hkv must be 1, 2, 4, 8 or 16 (q head h reads kv head h*Hkv/Hq) */
-  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t n_q_heads;     /* Hq (MLA: a multiple of 64) */
+  int32_t n_kv_heads;    /* GQA: Hkv, Hq/Hkv in {1, 2, 4, 8, 16}; MLA: 1 */
+  int32_t head_dim;      /* D = value width per head: GQA 64 or 128; MLA 512 (latent rank) */
+  int32_t rope_dim;      /* MLA: extra score-only dims of the latent row (64); GQA: 0 */
   int32_t d_head;        /* width the final RMSNorm and lm-head consume (multiple of 32):
                             TOKENS: = d_model; QKV: = o-proj out width if w_o, else Hq*D */
   int32_t vocab;         /* V >= 1 */
   int32_t page_tokens;   /* tokens per KV page: 16 */
-  int32_t split_tokens;  /* attention KV split in tokens: a multiple of 64, <= 1024 (512 here) */
+  int32_t split_tokens;  /* attention KV split in tokens: a multiple of 64; GQA <= 1024,
+                            MLA <= 2048 (512 for GQA and 2048 for MLA here) */
   int32_t max_rows;      /* most rows one decode call may carry */
   int32_t max_tokens;    /* most tokens one prefill call may carry */
   int32_t max_ctx;       /* longest context (tokens, including the current one) */
@@ -148,9 +156,9 @@ typedef struct ril_prefill_batch {
   int32_t page_stride;      /* >= ceil(max_ctx_bound / page_tokens) */
   const int32_t *target_ids;/* device [total_tokens]: id whose logprob is returned */
   const int32_t *token_ids; /* TOKENS: device [total_tokens] */
-  const void *q;            /* QKV: device bf16 [total_tokens, Hq, D] */
-  const void *k;            /* QKV: device bf16 [total_tokens, Hkv, D] */
-  const void *v;            /* QKV: device bf16 [total_tokens, Hkv, D] */
+  const void *q;            /* QKV: device bf16 [total_tokens, Hq, D]  (MLA: [.., Hq, D + rope]) */
+  const void *k;            /* QKV: device bf16 [total_tokens, Hkv, D] (MLA: latent [.., D + rope]) */
+  const void *v;            /* QKV: device bf16 [total_tokens, Hkv, D] (MLA: unused, may be NULL) */
 } ril_prefill_batch;
 
 /* A decode batch: n_rows rows, one new token each, at position ctx_len[r]-1. */
@@ -162,9 +170,10 @@ typedef struct ril_decode_batch {
   int32_t page_stride;      /* >= ceil(max_ctx_bound / page_tokens) */
   const int32_t *target_ids;/* device [n_rows] */
   const int32_t *token_ids; /* TOKENS: device [n_rows] */
-  const void *q;            /* QKV: device bf16 [n_rows, Hq, D] */
-  const void *k;            /* QKV: device bf16 [n_rows, Hkv, D] (the new token's) */
-  const void *v;            /* QKV: device bf16 [n_rows, Hkv, D] */
+  const void *q;            /* QKV: device bf16 [n_rows, Hq, D]  (MLA: [n_rows, Hq, D + rope]) */
+  const void *k;            /* QKV: device bf16 [n_rows, Hkv, D] (the new token's; MLA: latent
+                               [n_rows, D + rope]) */
+  const void *v;            /* QKV: device bf16 [n_rows, Hkv, D] (MLA: unused, may be NULL) */
 } ril_decode_batch;
 
 /* Trainer-side recompute: writes every batch token's K/V into its page

@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 RIL_OK, RIL_EINVAL, RIL_ERANGE, RIL_ENOSPC, RIL_EUNSUPPORTED, RIL_EHIP = 0, -1, -2, -3, -4, -5
-RIL_ATTN_GQA = 0
+RIL_ATTN_GQA, RIL_ATTN_MLA = 0, 1
 RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
 
 _c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
@@ -33,7 +33,7 @@ _c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 class ril_model_desc(ctypes.Structure):
     _fields_ = [
         ("attn_kind", _c_int), ("input_mode", _c_int), ("d_model", _c_int),
-        ("n_q_heads", _c_int), ("n_kv_heads", _c_int), ("head_dim", _c_int),
+        ("n_q_heads", _c_int), ("n_kv_heads", _c_int), ("head_dim", _c_int), ("rope_dim", _c_int),
         ("d_head", _c_int), ("vocab", _c_int), ("page_tokens", _c_int),
         ("split_tokens", _c_int), ("max_rows", _c_int), ("max_tokens", _c_int),
         ("max_ctx", _c_int), ("softmax_scale", _c_float), ("rms_eps", _c_float),

@@ -58,19 +58,33 @@ extern "C" const char *ril_last_error(void) { return g_err.c_str(); }
 extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **out) {
   if (!desc || !out) return fail(RIL_EINVAL, "model_create: null argument");
   const ril_model_desc &d = *desc;
-  if (d.attn_kind != RIL_ATTN_GQA) return fail(RIL_EUNSUPPORTED, "model_create: attn_kind %d", d.attn_kind);
+  if (d.attn_kind != RIL_ATTN_GQA && d.attn_kind != RIL_ATTN_MLA)
+    return fail(RIL_EUNSUPPORTED, "model_create: attn_kind %d", d.attn_kind);
+  const bool mla = d.attn_kind == RIL_ATTN_MLA;
   if (d.input_mode != RIL_INPUT_TOKENS && d.input_mode != RIL_INPUT_QKV)
     return fail(RIL_EINVAL, "model_create: input_mode %d", d.input_mode);
-  if (d.head_dim != 64 && d.head_dim != 128)
-    return fail(RIL_EUNSUPPORTED, "model_create: head_dim %d (64 or 128)", d.head_dim);
-  if (d.n_q_heads < 1 || d.n_kv_heads < 1 || d.n_q_heads % d.n_kv_heads)
-    return fail(RIL_EINVAL, "model_create: heads %d/%d", d.n_q_heads, d.n_kv_heads);
-  const int G = d.n_q_heads / d.n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
-    return fail(RIL_EUNSUPPORTED, "model_create: group size %d (1, 2, 4, 8 or 16)", G);
+  int G = 1;
+  if (mla) {
+    if (d.head_dim != 512 || d.rope_dim != 64 || d.n_kv_heads != 1)
+      return fail(RIL_EUNSUPPORTED, "model_create: MLA needs head_dim 512, rope_dim 64, n_kv_heads 1");
+    if (d.n_q_heads < 64 || d.n_q_heads % 64)
+      return fail(RIL_EUNSUPPORTED, "model_create: MLA n_q_heads %d (a multiple of 64)", d.n_q_heads);
+    if (d.input_mode != RIL_INPUT_QKV) return fail(RIL_EUNSUPPORTED, "model_create: MLA takes q/latent input");
+    if (d.split_tokens <= 0 || d.split_tokens % 64 || d.split_tokens > 2048)
+      return fail(RIL_EINVAL, "model_create: split_tokens %d (a multiple of 64, at most 2048)", d.split_tokens);
+  } else {
+    if (d.head_dim != 64 && d.head_dim != 128)
+      return fail(RIL_EUNSUPPORTED, "model_create: head_dim %d (64 or 128)", d.head_dim);
+    if (d.rope_dim != 0) return fail(RIL_EINVAL, "model_create: rope_dim is for MLA");
+    if (d.n_q_heads < 1 || d.n_kv_heads < 1 || d.n_q_heads % d.n_kv_heads)
+      return fail(RIL_EINVAL, "model_create: heads %d/%d", d.n_q_heads, d.n_kv_heads);
+    G = d.n_q_heads / d.n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+      return fail(RIL_EUNSUPPORTED, "model_create: group size %d (1, 2, 4, 8 or 16)", G);
+    if (d.split_tokens <= 0 || d.split_tokens % 64 || d.split_tokens > 1024)
+      return fail(RIL_EINVAL, "model_create: split_tokens %d (a multiple of 64, at most 1024)", d.split_tokens);
+  }
   if (d.page_tokens != 16) return fail(RIL_EUNSUPPORTED, "model_create: page_tokens %d (16)", d.page_tokens);
-  if (d.split_tokens <= 0 || d.split_tokens % 64 || d.split_tokens > 1024)
-    return fail(RIL_EINVAL, "model_create: split_tokens %d (a multiple of 64, at most 1024)", d.split_tokens);
   if (d.vocab < 1) return fail(RIL_EINVAL, "model_create: vocab %d", d.vocab);
   if (d.max_rows < 1 || d.max_tokens < 1 || d.max_ctx < 1)
     return fail(RIL_EINVAL, "model_create: limits %d/%d/%d", d.max_rows, d.max_tokens, d.max_ctx);
@@ -98,7 +112,8 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->n_vt = (d.vocab + 255) / 256;
   m->max_splits = (d.max_ctx + d.split_tokens - 1) / d.split_tokens;
   m->cscale = (float)((double)d.softmax_scale * 1.4426950408889634);
-  m->page_bytes = (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * 2;
+  m->page_bytes = mla ? (size_t)16 * (d.head_dim + d.rope_dim) * 2
+                      : (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * 2;
   const size_t R = (size_t)std::max(d.max_rows, d.max_tokens);
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
   size_t o = 0;
@@ -361,8 +376,26 @@ static ril_status check_prefill(const ril_model *m, ril_kv *kv, const ril_prefil
     if (tok && (!b->token_ids || !aligned4(b->token_ids))) return fail(RIL_EINVAL, "%s: token_ids", who);
     if (!tok && (!b->q || !aligned16(b->q))) return fail(RIL_EINVAL, "%s: q", who);
   }
-  if ((!tok || !need_logprob) && (!b->k || !b->v || !aligned16(b->k) || !aligned16(b->v)))
+  const bool need_v = m->d.attn_kind != RIL_ATTN_MLA;
+  if ((!tok || !need_logprob) && (!b->k || !aligned16(b->k) || (need_v && (!b->v || !aligned16(b->v)))))
     return fail(RIL_EINVAL, "%s: k/v", who);
+  return RIL_OK;
+}
+
+// MLA attention for `rows` rows (mode 0: decode rows; mode 1: packed prefill tokens,
+// enqueued in groups of max_rows rows that reuse the split partials in stream order).
+static ril_status run_mla(const ril_model *m, ril_kv *kv, const bf16_t *q, int mode, int rows,
+                          const int32_t *ctx_len, const int32_t *cu, const int32_t *start_pos, int n_seqs,
+                          const int32_t *page_table, int page_stride, int ctx_bound, void *ws, hipStream_t st) {
+  const ril_model_desc &d = m->d;
+  for (int r0 = 0; r0 < rows; r0 += d.max_rows) {
+    const int n = std::min(d.max_rows, rows - r0);
+    MlaAttnArgs a{q, mode, r0, n, ctx_len, cu, start_pos, n_seqs, page_table, page_stride,
+                  (const bf16_t *)kv->pool, kv->n_pages, d.n_q_heads, d.split_tokens, ctx_bound, m->max_splits,
+                  m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn)};
+    RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_mla_split(a, st));
+    RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_mla_merge(a, st));
+  }
   return RIL_OK;
 }
 
@@ -373,10 +406,17 @@ extern "C" ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_pre
   ril_status s = check_prefill(m, kv, b, dummy, 0, false, "kv_write");
   if (s != RIL_OK) return s;
   const ril_model_desc &d = m->d;
+  hipStream_t st = (hipStream_t)stream;
+  if (d.attn_kind == RIL_ATTN_MLA) {
+    MlaKvWriteArgs a{(const bf16_t *)b->k, d.head_dim + d.rope_dim, b->total_tokens, 0, b->cu_tokens,
+                     b->start_pos, b->n_seqs, nullptr, b->page_table, b->page_stride, (bf16_t *)kv->pool,
+                     kv->n_pages};
+    RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(a, st));
+    return RIL_OK;
+  }
   KvWriteArgs a{(const bf16_t *)b->k, (const bf16_t *)b->v, d.n_kv_heads * d.head_dim, b->total_tokens, 0,
                 b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table, b->page_stride,
                 (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
-  hipStream_t st = (hipStream_t)stream;
   RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(a, st));
   return RIL_OK;
 }
@@ -389,6 +429,15 @@ extern "C" ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const
   const ril_model_desc &d = m->d;
   hipStream_t st = (hipStream_t)stream;
   const int T = b->total_tokens;
+  if (d.attn_kind == RIL_ATTN_MLA) {
+    MlaKvWriteArgs kw{(const bf16_t *)b->k, d.head_dim + d.rope_dim, T, 0, b->cu_tokens, b->start_pos,
+                      b->n_seqs, nullptr, b->page_table, b->page_stride, (bf16_t *)kv->pool, kv->n_pages};
+    RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(kw, st));
+    s = run_mla(m, kv, (const bf16_t *)b->q, 1, T, nullptr, b->cu_tokens, b->start_pos, b->n_seqs, b->page_table,
+                b->page_stride, b->max_ctx_bound, ws, st);
+    if (s != RIL_OK) return s;
+    return run_head(m, T, b->target_ids, logprob_out, ws, st);
+  }
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
   const int wqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   const bf16_t *q, *k, *v;
@@ -431,10 +480,20 @@ extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, c
   if (!logprob_out || !aligned4(logprob_out)) return fail(RIL_EINVAL, "decode_step_logprobs: logprob_out");
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
   if (tok && (!b->token_ids || !aligned4(b->token_ids))) return fail(RIL_EINVAL, "decode_step_logprobs: token_ids");
-  if (!tok && (!b->q || !b->k || !b->v || !aligned16(b->q) || !aligned16(b->k) || !aligned16(b->v)))
+  const bool need_v = d.attn_kind != RIL_ATTN_MLA;
+  if (!tok && (!b->q || !b->k || !aligned16(b->q) || !aligned16(b->k) || (need_v && (!b->v || !aligned16(b->v)))))
     return fail(RIL_EINVAL, "decode_step_logprobs: q/k/v");
   hipStream_t st = (hipStream_t)stream;
   const int R = b->n_rows;
+  if (d.attn_kind == RIL_ATTN_MLA) {
+    MlaKvWriteArgs kw{(const bf16_t *)b->k, d.head_dim + d.rope_dim, R, 1, nullptr, nullptr, 0, b->ctx_len,
+                      b->page_table, b->page_stride, (bf16_t *)kv->pool, kv->n_pages};
+    RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(kw, st));
+    s = run_mla(m, kv, (const bf16_t *)b->q, 0, R, b->ctx_len, nullptr, nullptr, 0, b->page_table, b->page_stride,
+                b->max_ctx_bound, ws, st);
+    if (s != RIL_OK) return s;
+    return run_head(m, R, b->target_ids, logprob_out, ws, st);
+  }
   const int wqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   const bf16_t *q, *k, *v;
   int q_stride, kv_stride;

@@ -27,7 +27,7 @@
 //   K (t, d) -> (d/32)*512 + ((d%32)/8)*128 + ((t%8)/4)*64 + (t/8)*32 + (t%4)*8 + d%8
 //   V (t, d) -> (t/8)*8D + d*8 + t%8
 // A page of the pool holds all kv heads: page p, kv head g starts at (p*Hkv + g)*32D.
-#include "common.h"
+#include "attn_common.h"
 #include "kernels.h"
 
 namespace ril {
@@ -66,8 +66,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   bf16_t *vb = kb + 16 * D;
   const int t = pos % kPage;
   const u32x4 kv8 = ld16(k + (long)j * row_stride + g * D + d0);
-  const int koff = (d0 / 32) * 512 + ((d0 % 32) / 8) * 128 + ((t % 8) / 4) * 64 + (t / 8) * 32 + (t % 4) * 8;
-  st16(kb + koff, kv8);
+  st16(kb + k_page_offset(t, d0), kv8);
   const u32x4 vv8 = ld16(v + (long)j * row_stride + g * D + d0);
   bf16_t *vt = vb + (t / 8) * (8 * D) + t % 8;
 #pragma unroll
@@ -80,17 +79,6 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 // ---------------------------------------------------------------------------
 // The tile routine shared by decode and prefill
 // ---------------------------------------------------------------------------
-
-// Zero the bf16 elements j >= n_valid of a lane's 8-element vector.
-__device__ __forceinline__ u32x4 keep_first(u32x4 v, int n_valid) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = (2 * w < n_valid) ? 0x0000ffffu : 0u;
-    const uint32_t hi = (2 * w + 1 < n_valid) ? 0xffff0000u : 0u;
-    v[w] &= (lo | hi);
-  }
-  return v;
-}
 
 // One 64-token tile of K and V in MFMA operand registers (16-byte loads per lane).
 //   k[2kc+h][c] : A operand of S^T = K Q^T for M-block (kc, h), dims 32c .. 32c+31;
@@ -146,44 +134,9 @@ __device__ __forceinline__ void attn_tile(const KVTile<D> &t, int tile_start,
     for (int c = 0; c < D / 32; ++c) acc = mfma(as_bf16x8(t.k[mb][c]), qop[c], acc);
     s[mb] = acc;
   }
-  // Output lane holds rows 4*grp + i -> token tile_start + 32kc + 8grp + 4h + i (mb = 2kc + h).
-  float tmax = neg_inf();
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = tile_start + 32 * (mb >> 1) + 8 * grp + 4 * (mb & 1) + i;
-      const float x = s[mb][i] * cscale;
-      s[mb][i] = (tok <= pos) ? x : neg_inf();
-      tmax = fmaxf(tmax, s[mb][i]);
-    }
-  }
-  tmax = max_groups(tmax);
-  const float m_new = fmaxf(m, tmax);
-  const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-  const float alpha = exp2f_hw(m - m_use);
-  float rs = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[mb][i] = exp2f_hw(s[mb][i] - m_use);
-    const float r = ((s[mb][0] + s[mb][1]) + s[mb][2]) + s[mb][3];
-    rs = (mb == 0) ? r : rs + r;
-  }
-  rs = sum_groups(rs);
-  const float l_new = __builtin_fmaf(l, alpha, rs);
-  // P^T operand for 32-token step kc: k-slot j of lane group grp <-> token 32kc + 8grp + j,
-  // i.e. S^T M-block (kc, j/4), register j%4.
   bf16x8 pop[2];
-#pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
-    u32x4 w;
-    w[0] = pack2(s[2 * kc][0], s[2 * kc][1]);
-    w[1] = pack2(s[2 * kc][2], s[2 * kc][3]);
-    w[2] = pack2(s[2 * kc + 1][0], s[2 * kc + 1][1]);
-    w[3] = pack2(s[2 * kc + 1][2], s[2 * kc + 1][3]);
-    pop[kc] = as_bf16x8(w);
-  }
+  float alpha, m_new, l_new;
+  tile_softmax(s, tile_start, pos, cscale, m, l, pop, alpha, m_new, l_new);
   f32x4 on[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) on[db] = o[db] * alpha;
@@ -212,19 +165,6 @@ __device__ __forceinline__ void attn_tile(const KVTile<D> &t, int tile_start,
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[db] = on[db];
   }
-}
-
-// merged <- merge(merged, split): the one merge rule of decode and prefill.
-template <int N>
-__device__ __forceinline__ void merge_state(float &M, float &L, float (&O)[N], float ms, float ls,
-                                            const float (&os)[N]) {
-  const float mn = fmaxf(M, ms);
-  const float a = exp2f_hw(M - mn);
-  const float b = exp2f_hw(ms - mn);
-  L = __builtin_fmaf(L, a, ls * b);
-#pragma unroll
-  for (int j = 0; j < N; ++j) O[j] = __builtin_fmaf(O[j], a, os[j] * b);
-  M = mn;
 }
 
 template <int D>
@@ -340,19 +280,7 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
     return;
   }
   const int ns = (ctx + split_tokens - 1) / split_tokens;
-  const long base = ((long)row * Hq + h) * max_splits;
-  float M = part_ml[base * 2], L = part_ml[base * 2 + 1];
-  float O[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) O[j] = part_o[base * D + lane * PER + j];
-  for (int s = 1; s < ns; ++s) {
-    float os[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) os[j] = part_o[(base + s) * D + lane * PER + j];
-    merge_state<PER>(M, L, O, part_ml[(base + s) * 2], part_ml[(base + s) * 2 + 1], os);
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) op[j] = f2bf(__fdiv_rn(O[j], L));
+  merge_partials<D>(part_o, part_ml, ((long)row * Hq + h) * max_splits, ns, op - lane * PER);
 }
 
 // ---------------------------------------------------------------------------

@@ -81,7 +81,35 @@ struct LmHeadArgs {
   float *part, *tgt_logit, *out;
 };
 
+struct MlaKvWriteArgs {
+  const bf16_t *c;  // latent rows [n_tok, row_stride], 576 dims used
+  int row_stride, n_tok, mode;
+  const int32_t *cu, *start_pos;
+  int n_seqs;
+  const int32_t *ctx_len, *page_table;
+  int page_stride;
+  bf16_t *pool;
+  int n_pages;
+};
+
+struct MlaAttnArgs {
+  const bf16_t *q;  // [rows or tokens, H, 576]
+  int mode, row0, n_rows;  // mode 0: decode rows; 1: prefill tokens row0 .. row0+n_rows-1
+  const int32_t *ctx_len, *cu, *start_pos;
+  int n_seqs;
+  const int32_t *page_table;
+  int page_stride;
+  const bf16_t *pool;
+  int n_pages, H, split_tokens, ctx_bound, max_splits;
+  float cscale;
+  float *part_o, *part_ml;
+  bf16_t *out;  // [rows or tokens, H, 512]
+};
+
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t st);
+hipError_t launch_mla_kv_write(const MlaKvWriteArgs &a, hipStream_t st);
+hipError_t launch_mla_split(const MlaAttnArgs &a, hipStream_t st);
+hipError_t launch_mla_merge(const MlaAttnArgs &a, hipStream_t st);
 hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st);
 hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st);

@@ -31,11 +31,11 @@ class Session:
     def __init__(self, *, n_q_heads, n_kv_heads, head_dim, vocab, d_head, w_lm, max_rows, max_tokens,
                  max_ctx, pool_pages, softmax_scale, rms_eps=1e-6, split_tokens=512, shuffle_seed=0,
                  input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
-                 norm_final=None, device="cuda"):
+                 norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, device="cuda"):
         self.device = torch.device(device)
         self._keep = [w_lm, embed, w_qkv, w_o, norm_attn, norm_final]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-        self.desc = ril_model_desc(RIL_ATTN_GQA, input_mode, d_model, n_q_heads, n_kv_heads, head_dim,
+        self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
                                    d_head, vocab, PAGE, split_tokens, max_rows, max_tokens, max_ctx,
                                    softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o), p(norm_attn),
                                    p(norm_final), p(w_lm))
@@ -97,7 +97,7 @@ class Session:
         lens = [k.shape[0] for k in ks]
         cu, bound = self._packed(seqs, starts, lens)
         k = torch.cat(list(ks)).contiguous()
-        v = torch.cat(list(vs)).contiguous()
+        v = None if vs is None else torch.cat(list(vs)).contiguous()
         cu_t, st_t = _i32(cu, self.device), _i32(list(starts), self.device)
         pt = self.page_table(seqs, bound)
         b = make_prefill_batch(cu_tokens=cu_t, start_pos=st_t, page_table=pt, max_ctx_bound=bound,

@@ -34,6 +34,7 @@ from .models import (  # noqa: F401
     tiny_decoder_decode,
     gqa_row_attention,
     gqa_row_logprob,
+    head_logprob,
     mla_row_attention,
     indexer_scores,
     topk_select,

@@ -148,7 +148,13 @@ def gqa_row_logprob(q, K, V, scale, w_lm, target, eps=1e-6, w_o=None, gain=None)
     ``w_o`` (bf16 output), normalised by RMSNorm (gain 1 unless given, bf16
     output) and fed to the lm-head; logits stay float64.
     """
-    o = bf16(gqa_row_attention(q, K, V, scale)).reshape(-1)
+    return head_logprob(gqa_row_attention(q, K, V, scale), w_lm, target, eps, w_o, gain)
+
+
+def head_logprob(o, w_lm, target, eps=1e-6, w_o=None, gain=None) -> float:
+    """The head after attention: bf16 attention output, flattened head-major, an
+    optional projection (bf16 output), bf16(RMSNorm), then the lm-head logprob."""
+    o = bf16(np.asarray(o, dtype=np.float64)).reshape(-1)
     if w_o is not None:
         o = bf16(widen(w_o) @ o)
     z = bf16(rmsnorm(o, gain, eps))

@@ -173,7 +173,57 @@ def gqa_row(row: int, w: GQADecode = GQA_DECODE_B64, device="cpu", ctx: int = No
     }
 
 
-def scaled(w: GQADecode, **changes) -> GQADecode:
+@dataclasses.dataclass(frozen=True)
+class MLADecode:
+    """Absorbed-MLA decode rows: q [H, 576] per position, one shared latent row
+    [576] = 512 latent + 64 rope dims per cached token; softmax scale 1/sqrt(192)."""
+    rows: int = 128
+    n_heads: int = 128
+    kv_rank: int = 512
+    rope_dim: int = 64
+    scale_dim: int = 192
+    ctx_lo: int = 4096
+    ctx_hi: int = 32768
+    vocab: int = 129280
+    d_head: int = 4096           # width after the absorbed value/output projection
+    init_std: float = 0.02
+    rms_eps: float = 1e-6
+    page_tokens: int = 16
+    recompute_tokens: int = 16
+    seed: int = 2
+
+
+MLA_DECODE_B128 = MLADecode()
+
+
+def mla_ctx(row: int, w: MLADecode = MLA_DECODE_B128) -> int:
+    return int(randint(w.ctx_lo, w.ctx_hi, (1,), key(w.seed, "ctx", row))[0])
+
+
+def mla_head_weights(w: MLADecode = MLA_DECODE_B128, device="cpu") -> Dict[str, torch.Tensor]:
+    """Absorbed value-up + output projection [d_head, H*512] and the lm-head [V, d_head]."""
+    return {
+        "w_o": randn((w.d_head, w.n_heads * w.kv_rank), key(w.seed, "w_vo"), w.init_std, device),
+        "w_lm": randn((w.vocab, w.d_head), key(w.seed, "w_lm"), w.init_std, device),
+    }
+
+
+def mla_row(row: int, w: MLADecode = MLA_DECODE_B128, device="cpu", ctx: int = None):
+    """Latent rows c [ctx, 576] of every position; q [R, H, 576] and targets [R] of the
+    last R = recompute_tokens positions (q[j] belongs to position ctx - R + j)."""
+    L = mla_ctx(row, w) if ctx is None else int(ctx)
+    R = min(w.recompute_tokens, L)
+    s = w.seed
+    dq = w.kv_rank + w.rope_dim
+    return {
+        "ctx": L,
+        "c": randn((L, dq), key(s, "c", row, L), 1.0, device),
+        "q": randn((R, w.n_heads, dq), key(s, "q", row, L), 1.0, device),
+        "target": randint(0, w.vocab - 1, (R,), key(s, "target", row, L), device),
+    }
+
+
+def scaled(w, **changes):
     """A smaller variant of a workload for oracle-sized parity runs."""
     return dataclasses.replace(w, **changes)
 
