@@ -1,23 +1,28 @@
 #!/usr/bin/env python3
 """Invariant decode tokens/s + attention HBM GB/s at diff = 0 (prefill vs decode), one MI355X.
 
-Workload ("gqa_decode_b64"): 64 paged GQA decode rows, 32 q / 8 kv heads, head_dim 128,
-bf16 KV in 16-token pages with a random page table, contexts uniform in [512, 8192],
-q/K/V ~ N(0, 1); attention output -> RMSNorm -> lm-head 4096 x 129280 (N(0, 0.02)) ->
-logprob of a sampled token id per row.  Synthetic, seeded inputs (workloads module),
-resident in HBM before timing starts.
+Default workload ("gqa_decode_b64"): 64 paged GQA decode rows, 32 q / 8 kv heads,
+head_dim 128, bf16 KV in 16-token pages with a random page table, contexts uniform in
+[512, 8192], q/K/V ~ N(0, 1); attention output -> RMSNorm -> lm-head 4096 x 129280
+(N(0, 0.02)) -> logprob of a sampled token id per row.
 
-A step = one ril_decode_step_logprobs call for all 64 rows: KV write, fixed-split
-attention, split merge, RMSNorm, lm-head with vocabulary-tile partials, vocabulary
-merge.  Before timing, every row's last 16 positions are produced both by 16 decode
-steps and by one prefill recompute; the JSON line reports their diff (must be 0).
+--workload mla_decode_b128: 128 absorbed-MLA decode rows, 128 heads sharing one paged
+latent row of 512 + 64 dims, contexts uniform in [4096, 32768], scale 1/sqrt(192);
+attention output -> absorbed value/output projection 65536 -> 4096 -> RMSNorm -> the
+same lm-head.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--cpu-rows R] [--no-cpu]
+Synthetic, seeded inputs (workloads module), resident in HBM before timing starts.
+A step = one ril_decode_step_logprobs call for all rows.  Before timing, every row's
+last 16 positions are produced both by 16 decode steps and by one prefill recompute;
+the JSON line reports their diff (must be 0, bit for bit).
+
+    python bench.py [--workload W] [--steps K] [--warmup W] [--gpus 1] [--cpu-rows R] [--no-cpu]
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,7 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 sys.path.insert(0, os.path.join(ROOT, "tests"))
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "invariant decode tokens/s + attn HBM GB/s at diff=0 (prefill vs decode)"
 
 
 def log(*a):
@@ -38,7 +45,6 @@ def log(*a):
 def measured_traffic(kernel: str):
     """HBM bytes per launch (fetch + write) from the committed rocprofv3 PMC summary,
     scaled by the copy calibration; None if the kernel's sources changed since."""
-    import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
             rec = json.load(f)[kernel]
@@ -53,11 +59,208 @@ def measured_traffic(kernel: str):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count()
+
+
+def timed_steps(launch, steps, warmup):
+    """Warm up, then time `steps` launches between two synchronisations with HIP events
+    on the launch stream; the library's trace hook times each kernel on that stream."""
+    import torch
+    import invariant_rl_logprob_amd as ril
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ril.ril_trace_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        launch()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kern = {}
+    for kid, name in enumerate(ril.KERNEL_NAMES):
+        tot, cnt = ril.ril_trace_read(kid)
+        if cnt:
+            kern[name] = {"avg_us": 1e3 * tot / cnt, "launches": cnt}
+    ril.ril_trace_enable(False)
+    return ms, kern
+
+
+def diff_check(case, rows, n=16):
+    """n decode steps per row vs one prefill recompute of the same n positions."""
+    import torch
+    from invariant_rl_logprob_amd.metrics import mismatch
+    case.write_history("d", rows, n)
+    dec = torch.stack([case.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
+    case.write_history("p", rows, n)
+    pre = case.prefill_last("p", rows, n)
+    torch.cuda.synchronize()
+    d = mismatch(dec, pre)
+    log(f"prefill vs decode over {d['tokens']} tokens: {d}")
+    return dec, d
+
+
+def roofline_hbm(kernel, achieved_gbps, bytes_per_launch, avg_us):
+    return {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(kernel),
+            "kernel": kernel, "algorithmic_bytes_per_launch": int(bytes_per_launch),
+            "avg_launch_us": round(avg_us, 2)}
+
+
+# ---------------------------------------------------------------------------
+# GQA decode, 64 rows
+# ---------------------------------------------------------------------------
+
+def bench_gqa(args):
+    import numpy as np
+    import torch
+    import workloads as wl
+    from gqa_case import GQACase
+
+    w = wl.GQA_DECODE_B64
+    rows = list(range(w.rows))
+    t0 = time.time()
+    case = GQACase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_tokens=w.rows * 16)
+    ctx = [case.ctx(r) for r in rows]
+    log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
+    dec, diff = diff_check(case, rows)
+
+    q, k, v, tgt, c = case.step_inputs(rows, 1)
+    launch, out = case.sess.prepare_decode([("d", r) for r in rows], c, targets=tgt, q=q, k=k, v=v)
+    ms_step, kern = timed_steps(launch, args.steps, args.warmup)
+    last_equal = bool(np.array_equal(out.cpu().view(torch.int32).numpy(),
+                                     dec[:, -1].cpu().view(torch.int32).numpy()))
+
+    Hkv, D, Hq = w.n_kv_heads, w.head_dim, w.n_q_heads
+    kv_bytes = sum(ctx) * Hkv * D * 2 * 2           # each K/V byte once per kv head
+    q_bytes = len(rows) * Hq * D * 2
+    out_bytes = len(rows) * Hq * D * 2
+    lm_bytes = w.vocab * w.d_head * 2 + len(rows) * w.d_head * 2
+    split_us, merge_us, lm_us = kern["attn_split"]["avg_us"], kern["attn_merge"]["avg_us"], kern["lm_head"]["avg_us"]
+    attn_gbps = (kv_bytes + q_bytes + out_bytes) / ((split_us + merge_us) * 1e-6) / 1e9
+    split_gbps = (kv_bytes + q_bytes) / (split_us * 1e-6) / 1e9
+    lm_gbps = lm_bytes / (lm_us * 1e-6) / 1e9
+    if split_us >= lm_us:
+        roof = roofline_hbm("attn_decode_split", split_gbps, kv_bytes + q_bytes, split_us)
+    else:
+        roof = roofline_hbm("lm_head", lm_gbps, lm_bytes, lm_us)
+
+    cpu = None
+    if not args.no_cpu and args.cpu_rows > 0:
+        import oracle  # the cpu_baseline leg: the fp64 oracle as it stands
+        sample = rows[: args.cpu_rows]
+        w_lm_cpu = case.head["w_lm"].cpu()
+        host = {r: {key: case.data[r][key].cpu() for key in ("q", "k", "v", "target")} for r in sample}
+        t1 = time.time()
+        got = [oracle.gqa_row_logprob(host[r]["q"][-1], host[r]["k"][: case.ctx(r)], host[r]["v"][: case.ctx(r)],
+                                      1.0 / math.sqrt(D), w_lm_cpu, int(host[r]["target"][-1]), w.rms_eps)
+               for r in sample]
+        secs = time.time() - t1
+        cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{len(sample)} of the {len(rows)} decode rows (full attention over each row's "
+                         f"context + the 4096x129280 lm-head in fp64), {secs:.1f} s",
+               "max_abs_diff_vs_gpu": float(np.max(np.abs(np.array(got) - out.cpu().numpy()[: len(sample)])))}
+        log(f"oracle: {cpu}")
+
+    return {
+        "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+        "config": {"workload": "gqa_decode_b64: 64 paged decode rows, 32 q / 8 kv heads, head_dim 128, "
+                               "ctx U[512,8192], 16-token pages, random page table, lm-head 4096x129280",
+                   "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 512, "vocab_tile": 256,
+                   "parallelism": "none (1 GPU)"},
+        "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "lm_head_gbps": round(lm_gbps, 1), "diff": diff, "timed_step_equals_checked_decode": last_equal,
+        "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+
+
+# ---------------------------------------------------------------------------
+# absorbed MLA decode, 128 rows
+# ---------------------------------------------------------------------------
+
+def bench_mla(args):
+    import numpy as np
+    import torch
+    import workloads as wl
+    from mla_case import MLACase
+
+    w = wl.MLA_DECODE_B128
+    rows = list(range(w.rows))
+    t0 = time.time()
+    case = MLACase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_rows=w.rows,
+                   max_tokens=w.rows * w.recompute_tokens)
+    ctx = [case.ctx(r) for r in rows]
+    log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
+    dec, diff = diff_check(case, rows)
+
+    q = torch.stack([case.data[r]["q"][-1] for r in rows])
+    cl = torch.stack([case.data[r]["c"][case.ctx(r) - 1] for r in rows])
+    tgt = torch.stack([case.data[r]["target"][-1] for r in rows])
+    launch, out = case.sess.prepare_decode([("d", r) for r in rows], ctx, targets=tgt, q=q, k=cl)
+    ms_step, kern = timed_steps(launch, args.steps, args.warmup)
+    last_equal = bool(np.array_equal(out.cpu().view(torch.int32).numpy(),
+                                     dec[:, -1].cpu().view(torch.int32).numpy()))
+
+    H = w.n_heads
+    kv_bytes = sum(ctx) * (w.kv_rank + w.rope_dim) * 2
+    flops = sum(ctx) * H * 2 * ((w.kv_rank + w.rope_dim) + w.kv_rank)
+    split_us, merge_us = kern["attn_split"]["avg_us"], kern["attn_merge"]["avg_us"]
+    attn_gbps = kv_bytes / ((split_us + merge_us) * 1e-6) / 1e9
+    split_gbps = kv_bytes / (split_us * 1e-6) / 1e9
+    tflops = flops / (split_us * 1e-6) / 1e12
+    roof = roofline_hbm("mla_split", split_gbps, kv_bytes, split_us)
+    roof["mfma"] = {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": int(flops)}
+
+    cpu = None
+    if not args.no_cpu and args.cpu_rows > 0:
+        import oracle  # the cpu_baseline leg
+        sample = rows[: max(1, args.cpu_rows // 4)]
+        w_lm_cpu = case.head["w_lm"].cpu()
+        w_o_cpu = case.head["w_o"].cpu()
+        host = {r: {key: case.data[r][key].cpu() for key in ("q", "c", "target")} for r in sample}
+        t1 = time.time()
+        got = []
+        for r in sample:
+            o = oracle.mla_row_attention(host[r]["q"][-1], host[r]["c"][: case.ctx(r)], case.scale, w.kv_rank)
+            got.append(oracle.head_logprob(o, w_lm_cpu, int(host[r]["target"][-1]), w.rms_eps, w_o=w_o_cpu))
+        secs = time.time() - t1
+        cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{len(sample)} of the {len(rows)} decode rows (MLA over each row's context, the "
+                         f"65536x4096 projection and the lm-head in fp64), {secs:.1f} s",
+               "max_abs_diff_vs_gpu": float(np.max(np.abs(np.array(got) - out.cpu().numpy()[: len(sample)])))}
+        log(f"oracle: {cpu}")
+
+    return {
+        "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+        "config": {"workload": "mla_decode_b128: 128 absorbed-MLA decode rows, 128 heads, latent 512 + rope 64, "
+                               "ctx U[4096,32768], 16-token pages, random page table, o-proj 65536x4096, "
+                               "lm-head 4096x129280",
+                   "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 2048, "parallelism": "none (1 GPU)"},
+        "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "diff": diff, "timed_step_equals_checked_decode": last_equal,
+        "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+
+
+WORKLOADS = {"gqa_decode_b64": bench_gqa, "mla_decode_b128": bench_mla}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_decode_b64", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=12, help="rows of the oracle timing sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -69,7 +272,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_calibration:
@@ -81,122 +283,11 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
         return
 
-    import invariant_rl_logprob_amd as ril
-    import workloads as wl
-    from gqa_case import GQACase
-
-    w = wl.GQA_DECODE_B64
-    rows = list(range(w.rows))
-    t0 = time.time()
-    case = GQACase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_tokens=w.rows * 16)
-    ctx = [case.ctx(r) for r in rows]
-    log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
-
-    # ---- diff = 0 check: 16 decode steps vs one prefill recompute of the same positions
-    n = 16
-    case.write_history("d", rows, n)
-    dec = torch.stack([case.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
-    case.write_history("p", rows, n)
-    pre = case.prefill_last("p", rows, n)
-    torch.cuda.synchronize()
-    import oracle  # metrics only (fp64 diff/k3 on the host)
-    a = dec.double().cpu().numpy().ravel()
-    b = pre.double().cpu().numpy().ravel()
-    bit_equal = bool(np.array_equal(dec.cpu().view(torch.int32).numpy(), pre.cpu().view(torch.int32).numpy()))
-    dstat = oracle.diff_stats(a, b)
-    diff = {"max": dstat["max"], "mean": dstat["mean"], "std": dstat["std"],
-            "k3": oracle.k3_mean(b, a), "tokens": int(a.size), "bitwise_equal": bit_equal}
-    log(f"prefill vs decode over {a.size} tokens: {diff}")
-
-    # ---- timed decode steps (position ctx-1 of every row; rewriting its K/V is idempotent)
-    q, k, v, tgt, c = case.step_inputs(rows, 1)
-    launch, out = case.sess.prepare_decode([("d", r) for r in rows], c, targets=tgt, q=q, k=k, v=v)
-    for _ in range(args.warmup):
-        launch()
-    torch.cuda.synchronize()
-    ril.ril_trace_enable(True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        launch()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    kern = {}
-    for kid, name in enumerate(ril.KERNEL_NAMES):
-        tot, cnt = ril.ril_trace_read(kid)
-        if cnt:
-            kern[name] = {"avg_us": 1e3 * tot / cnt, "launches": cnt}
-    ril.ril_trace_enable(False)
-    last_equal = bool(np.array_equal(out.cpu().view(torch.int32).numpy(),
-                                     dec[:, -1].cpu().view(torch.int32).numpy()))
-
-    # ---- algorithmic bytes (per launch)
-    Hkv, D, Hq = w.n_kv_heads, w.head_dim, w.n_q_heads
-    kv_bytes = sum(ctx) * Hkv * D * 2 * 2           # each K/V byte once per kv head
-    q_bytes = len(rows) * Hq * D * 2
-    attn_out_bytes = len(rows) * Hq * D * 2
-    lm_bytes = w.vocab * w.d_head * 2 + len(rows) * w.d_head * 2
-    split_us = kern["attn_split"]["avg_us"]
-    merge_us = kern["attn_merge"]["avg_us"]
-    attn_gbps = (kv_bytes + q_bytes + attn_out_bytes) / ((split_us + merge_us) * 1e-6) / 1e9
-    split_gbps = (kv_bytes + q_bytes) / (split_us * 1e-6) / 1e9
-    lm_gbps = lm_bytes / (kern["lm_head"]["avg_us"] * 1e-6) / 1e9
-    if split_us >= kern["lm_head"]["avg_us"]:
-        roof = {"kernel": "attn_decode_split", "achieved": split_gbps, "bytes_per_launch": kv_bytes + q_bytes}
-    else:
-        roof = {"kernel": "lm_head", "achieved": lm_gbps, "bytes_per_launch": lm_bytes}
-    roofline = {"bound": "hbm", "achieved": round(roof["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(roof["achieved"] / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic("attn_decode_split" if roof["kernel"] == "attn_decode_split" else "lm_head"),
-                "kernel": roof["kernel"], "algorithmic_bytes_per_launch": roof["bytes_per_launch"],
-                "avg_launch_us": round(split_us if roof["kernel"] == "attn_decode_split" else kern["lm_head"]["avg_us"], 2)}
-
-    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same rows
-    cpu = None
-    if not args.no_cpu and args.cpu_rows > 0:
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:
-            cores = os.cpu_count()
-        sample = rows[: args.cpu_rows]
-        w_lm_cpu = case.head["w_lm"].cpu()
-        host = {r: {key: case.data[r][key].cpu() for key in ("q", "k", "v", "target")} for r in sample}
-        t1 = time.time()
-        got = []
-        for r in sample:
-            d = host[r]
-            L = case.ctx(r)
-            got.append(oracle.gqa_row_logprob(d["q"][-1], d["k"][:L], d["v"][:L], 1.0 / math.sqrt(D), w_lm_cpu,
-                                              int(d["target"][-1]), w.rms_eps))
-        secs = time.time() - t1
-        err = float(np.max(np.abs(np.array(got) - out.cpu().numpy()[: len(sample)])))
-        cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"{len(sample)} of the {len(rows)} decode rows (full attention over each row's "
-                         f"context + the 4096x129280 lm-head in fp64), {secs:.1f} s",
-               "max_abs_diff_vs_gpu": err}
-        log(f"oracle: {cpu}")
-
-    tok_s = len(rows) / (ms_step * 1e-3)
-    line = {
-        "metric": "invariant decode tokens/s + attn HBM GB/s at diff=0 (prefill vs decode)",
-        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "gqa_decode_b64: 64 paged decode rows, 32 q / 8 kv heads, head_dim 128, "
-                               "ctx U[512,8192], 16-token pages, random page table, lm-head 4096x129280",
-                   "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 512, "vocab_tile": 256,
-                   "parallelism": "none (1 GPU)"},
-        "attn_hbm_gbps": round(attn_gbps, 1),
-        "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
-        "lm_head_gbps": round(lm_gbps, 1),
-        "diff": diff, "timed_step_equals_checked_decode": last_equal,
-        "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-    }
+    res = WORKLOADS[args.workload](args)
+    line = {"metric": METRIC, "value": res.pop("value"), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    line.update(res)
     print(json.dumps(line), flush=True)
 
 
