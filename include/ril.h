@@ -65,8 +65,17 @@ typedef enum ril_status {
  *   MLA: absorbed multi-head latent attention; every q head reads one shared cached
  *        latent row per token of head_dim + rope_dim values (512 + 64); scores use
  *        all of it, values its first head_dim (Bitwise-consistent RL post, section 3:
- *        MLA compresses KV before caching). */
-enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1 };
+ *        MLA compresses KV before caching).
+ *   MLA_SPARSE: MLA over the top-k history positions a lightweight indexer selects
+ *        (post sections 3 and 4.3).  Per position an fp32 indexer key is cached beside
+ *        the latent; per query an fp32 indexer query of index_heads x index_dim.
+ *        Scores I[s] = sum_h relu(q_h . k_s) in fp32, one rounding per multiply and
+ *        add, d then h in order; the k best (score, position) keys win, equal scores
+ *        going to the lower position; the list is ordered by descending position
+ *        (-1 padding last) and the attention accumulates in that order, splitting it
+ *        into runs of split_tokens entries.  Contexts of at most k positions select
+ *        every position. */
+enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1, RIL_ATTN_MLA_SPARSE = 2 };
 enum { RIL_INPUT_TOKENS = 0, RIL_INPUT_QKV = 1 };
 
 /* Model description.  All sizes are fixed for the life of the handle; the
@@ -74,7 +83,7 @@ enum { RIL_INPUT_TOKENS = 0, RIL_INPUT_QKV = 1 };
  * context length or the GPU (Bitwise-consistent RL post, section 2: no
  * kernel choice by batch size, no dynamic split count).                     */
 typedef struct ril_model_desc {
-  int32_t attn_kind;     /* RIL_ATTN_GQA | RIL_ATTN_MLA */
+  int32_t attn_kind;     /* RIL_ATTN_GQA | RIL_ATTN_MLA | RIL_ATTN_MLA_SPARSE */
   int32_t input_mode;    /* RIL_INPUT_TOKENS: token ids -> embedding -> RMSNorm -> QKV GEMM
                             -> attention -> O GEMM + residual -> RMSNorm -> lm-head;
                             RIL_INPUT_QKV: q/k/v given -> attention -> [O GEMM] -> RMSNorm
@@ -84,6 +93,9 @@ typedef struct ril_model_desc {
   int32_t n_kv_heads;    /* GQA: Hkv, Hq/Hkv in {1, 2, 4, 8, 16}; MLA: 1 */
   int32_t head_dim;      /* D = value width per head: GQA 64 or 128; MLA 512 (latent rank) */
   int32_t rope_dim;      /* MLA: extra score-only dims of the latent row (64); GQA: 0 */
+  int32_t index_heads;   /* MLA_SPARSE: indexer heads (64); else 0 */
+  int32_t index_dim;     /* MLA_SPARSE: indexer dim (128); else 0 */
+  int32_t topk;          /* MLA_SPARSE: positions kept, a power of two in [64, 4096]; else 0 */
   int32_t d_head;        /* width the final RMSNorm and lm-head consume (multiple of 32):
                             TOKENS: = d_model; QKV: = o-proj out width if w_o, else Hq*D */
   int32_t vocab;         /* V >= 1 */
@@ -159,6 +171,10 @@ typedef struct ril_prefill_batch {
   const void *q;            /* QKV: device bf16 [total_tokens, Hq, D]  (MLA: [.., Hq, D + rope]) */
   const void *k;            /* QKV: device bf16 [total_tokens, Hkv, D] (MLA: latent [.., D + rope]) */
   const void *v;            /* QKV: device bf16 [total_tokens, Hkv, D] (MLA: unused, may be NULL) */
+  const float *q_index;     /* MLA_SPARSE: device fp32 [total_tokens, index_heads, index_dim] */
+  const float *k_index;     /* MLA_SPARSE: device fp32 [total_tokens, index_dim] (cached per position) */
+  int32_t *selected_out;    /* MLA_SPARSE, optional: device int32 [total_tokens, topk] receives each
+                               token's selection list; NULL = not returned */
 } ril_prefill_batch;
 
 /* A decode batch: n_rows rows, one new token each, at position ctx_len[r]-1. */
@@ -174,6 +190,9 @@ typedef struct ril_decode_batch {
   const void *k;            /* QKV: device bf16 [n_rows, Hkv, D] (the new token's; MLA: latent
                                [n_rows, D + rope]) */
   const void *v;            /* QKV: device bf16 [n_rows, Hkv, D] (MLA: unused, may be NULL) */
+  const float *q_index;     /* MLA_SPARSE: device fp32 [n_rows, index_heads, index_dim] */
+  const float *k_index;     /* MLA_SPARSE: device fp32 [n_rows, index_dim] (the new token's) */
+  int32_t *selected_out;    /* MLA_SPARSE, optional: device int32 [n_rows, topk] */
 } ril_decode_batch;
 
 /* Trainer-side recompute: writes every batch token's K/V into its page
@@ -211,7 +230,9 @@ enum {
   RIL_K_GEMM = 5,         /* S4 */
   RIL_K_LM_HEAD = 6,      /* S11 */
   RIL_K_VOCAB_MERGE = 7,  /* S12 */
-  RIL_K_COUNT = 8
+  RIL_K_INDEXER = 8,      /* S6 */
+  RIL_K_TOPK = 9,         /* S7 */
+  RIL_K_COUNT = 10
 };
 ril_status ril_trace_enable(int on);
 ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches);

@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 RIL_OK, RIL_EINVAL, RIL_ERANGE, RIL_ENOSPC, RIL_EUNSUPPORTED, RIL_EHIP = 0, -1, -2, -3, -4, -5
-RIL_ATTN_GQA, RIL_ATTN_MLA = 0, 1
+RIL_ATTN_GQA, RIL_ATTN_MLA, RIL_ATTN_MLA_SPARSE = 0, 1, 2
 RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
 
 _c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
@@ -34,6 +34,7 @@ class ril_model_desc(ctypes.Structure):
     _fields_ = [
         ("attn_kind", _c_int), ("input_mode", _c_int), ("d_model", _c_int),
         ("n_q_heads", _c_int), ("n_kv_heads", _c_int), ("head_dim", _c_int), ("rope_dim", _c_int),
+        ("index_heads", _c_int), ("index_dim", _c_int), ("topk", _c_int),
         ("d_head", _c_int), ("vocab", _c_int), ("page_tokens", _c_int),
         ("split_tokens", _c_int), ("max_rows", _c_int), ("max_tokens", _c_int),
         ("max_ctx", _c_int), ("softmax_scale", _c_float), ("rms_eps", _c_float),
@@ -47,6 +48,7 @@ class ril_prefill_batch(ctypes.Structure):
         ("n_seqs", _c_int), ("total_tokens", _c_int), ("max_ctx_bound", _c_int),
         ("cu_tokens", _vp), ("start_pos", _vp), ("page_table", _vp), ("page_stride", _c_int),
         ("target_ids", _vp), ("token_ids", _vp), ("q", _vp), ("k", _vp), ("v", _vp),
+        ("q_index", _vp), ("k_index", _vp), ("selected_out", _vp),
     ]
 
 
@@ -54,7 +56,7 @@ class ril_decode_batch(ctypes.Structure):
     _fields_ = [
         ("n_rows", _c_int), ("max_ctx_bound", _c_int), ("ctx_len", _vp), ("page_table", _vp),
         ("page_stride", _c_int), ("target_ids", _vp), ("token_ids", _vp),
-        ("q", _vp), ("k", _vp), ("v", _vp),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("q_index", _vp), ("k_index", _vp), ("selected_out", _vp),
     ]
 
 
@@ -94,9 +96,10 @@ EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril
 
 # kernel ids of the trace hook
 RIL_K_KV_WRITE, RIL_K_ATTN_SPLIT, RIL_K_ATTN_MERGE, RIL_K_ATTN_PREFILL = 0, 1, 2, 3
-RIL_K_RMSNORM, RIL_K_GEMM, RIL_K_LM_HEAD, RIL_K_VOCAB_MERGE, RIL_K_COUNT = 4, 5, 6, 7, 8
+RIL_K_RMSNORM, RIL_K_GEMM, RIL_K_LM_HEAD, RIL_K_VOCAB_MERGE = 4, 5, 6, 7
+RIL_K_INDEXER, RIL_K_TOPK, RIL_K_COUNT = 8, 9, 10
 KERNEL_NAMES = ("kv_write", "attn_split", "attn_merge", "attn_prefill", "rmsnorm", "gemm", "lm_head",
-                "vocab_merge")
+                "vocab_merge", "indexer", "topk")
 
 
 class RilError(RuntimeError):
@@ -181,20 +184,22 @@ def ril_kv_free(kv: int) -> None:
 
 
 def make_prefill_batch(*, cu_tokens, start_pos, page_table, max_ctx_bound, target_ids=None,
-                       token_ids=None, q=None, k=None, v=None, total_tokens=None) -> ril_prefill_batch:
+                       token_ids=None, q=None, k=None, v=None, q_index=None, k_index=None,
+                       selected_out=None, total_tokens=None) -> ril_prefill_batch:
     """Build the C descriptor from device tensors (the tensors must outlive the call)."""
     n = cu_tokens.numel() - 1
     if total_tokens is None:
         raise ValueError("total_tokens (a host integer) is required")
     return ril_prefill_batch(n, int(total_tokens), int(max_ctx_bound), _ptr(cu_tokens), _ptr(start_pos),
                              _ptr(page_table), page_table.shape[1], _ptr(target_ids), _ptr(token_ids),
-                             _ptr(q), _ptr(k), _ptr(v))
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(q_index), _ptr(k_index), _ptr(selected_out))
 
 
 def make_decode_batch(*, ctx_len, page_table, max_ctx_bound, target_ids, token_ids=None, q=None,
-                      k=None, v=None) -> ril_decode_batch:
+                      k=None, v=None, q_index=None, k_index=None, selected_out=None) -> ril_decode_batch:
     return ril_decode_batch(ctx_len.numel(), int(max_ctx_bound), _ptr(ctx_len), _ptr(page_table),
-                            page_table.shape[1], _ptr(target_ids), _ptr(token_ids), _ptr(q), _ptr(k), _ptr(v))
+                            page_table.shape[1], _ptr(target_ids), _ptr(token_ids), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(q_index), _ptr(k_index), _ptr(selected_out))
 
 
 def ril_prefill_logprobs(model: int, kv: int, batch: ril_prefill_batch, logprob_out, ws,

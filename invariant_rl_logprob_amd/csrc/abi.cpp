@@ -24,8 +24,10 @@ struct ril_model {
   int max_splits;   // splits of the longest context
   float cscale;     // softmax_scale * log2(e), rounded once to fp32
   size_t page_bytes;
+  bool mla, sparse;
   // workspace segment offsets (bytes) and total
   size_t off_x, off_h, off_qkv, off_attn, off_y, off_z, off_vpart, off_tgt, off_po, off_pml;
+  size_t off_scores, off_sel;  // sparse: indexer scores [max_rows, max_ctx], selections [max_rows, topk]
   size_t ws_total;
 };
 
@@ -58,9 +60,18 @@ extern "C" const char *ril_last_error(void) { return g_err.c_str(); }
 extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **out) {
   if (!desc || !out) return fail(RIL_EINVAL, "model_create: null argument");
   const ril_model_desc &d = *desc;
-  if (d.attn_kind != RIL_ATTN_GQA && d.attn_kind != RIL_ATTN_MLA)
+  if (d.attn_kind != RIL_ATTN_GQA && d.attn_kind != RIL_ATTN_MLA && d.attn_kind != RIL_ATTN_MLA_SPARSE)
     return fail(RIL_EUNSUPPORTED, "model_create: attn_kind %d", d.attn_kind);
-  const bool mla = d.attn_kind == RIL_ATTN_MLA;
+  const bool sparse = d.attn_kind == RIL_ATTN_MLA_SPARSE;
+  const bool mla = d.attn_kind == RIL_ATTN_MLA || sparse;
+  if (sparse) {
+    if (d.index_heads != 64 || d.index_dim != 128)
+      return fail(RIL_EUNSUPPORTED, "model_create: indexer must be 64 heads x 128 dims");
+    if (d.topk < 64 || d.topk > 4096 || (d.topk & (d.topk - 1)))
+      return fail(RIL_EINVAL, "model_create: topk %d (a power of two in [64, 4096])", d.topk);
+  } else if (d.index_heads || d.index_dim || d.topk) {
+    return fail(RIL_EINVAL, "model_create: index_heads/index_dim/topk are for MLA_SPARSE");
+  }
   if (d.input_mode != RIL_INPUT_TOKENS && d.input_mode != RIL_INPUT_QKV)
     return fail(RIL_EINVAL, "model_create: input_mode %d", d.input_mode);
   int G = 1;
@@ -112,7 +123,11 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->n_vt = (d.vocab + 255) / 256;
   m->max_splits = (d.max_ctx + d.split_tokens - 1) / d.split_tokens;
   m->cscale = (float)((double)d.softmax_scale * 1.4426950408889634);
-  m->page_bytes = mla ? (size_t)16 * (d.head_dim + d.rope_dim) * 2
+  m->mla = mla;
+  m->sparse = sparse;
+  if (sparse)  // split count of the selection, not of the context
+    m->max_splits = (std::min(d.max_ctx, d.topk) + d.split_tokens - 1) / d.split_tokens;
+  m->page_bytes = mla ? (size_t)16 * (d.head_dim + d.rope_dim) * 2 + (sparse ? (size_t)16 * d.index_dim * 4 : 0)
                       : (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * 2;
   const size_t R = (size_t)std::max(d.max_rows, d.max_tokens);
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
@@ -128,6 +143,8 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->off_tgt = seg(R * sizeof(float));
   m->off_po = seg((size_t)d.max_rows * d.n_q_heads * m->max_splits * d.head_dim * sizeof(float));
   m->off_pml = seg((size_t)d.max_rows * d.n_q_heads * m->max_splits * 2 * sizeof(float));
+  m->off_scores = seg(sparse ? (size_t)d.max_rows * d.max_ctx * sizeof(float) : 0);
+  m->off_sel = seg(sparse ? (size_t)d.max_rows * d.topk * sizeof(int32_t) : 0);
   m->ws_total = o;
   *out = m;
   return RIL_OK;
@@ -376,23 +393,52 @@ static ril_status check_prefill(const ril_model *m, ril_kv *kv, const ril_prefil
     if (tok && (!b->token_ids || !aligned4(b->token_ids))) return fail(RIL_EINVAL, "%s: token_ids", who);
     if (!tok && (!b->q || !aligned16(b->q))) return fail(RIL_EINVAL, "%s: q", who);
   }
-  const bool need_v = m->d.attn_kind != RIL_ATTN_MLA;
+  const bool need_v = !m->mla;
   if ((!tok || !need_logprob) && (!b->k || !aligned16(b->k) || (need_v && (!b->v || !aligned16(b->v)))))
     return fail(RIL_EINVAL, "%s: k/v", who);
+  if (m->sparse) {
+    if (!b->k_index || !aligned16(b->k_index)) return fail(RIL_EINVAL, "%s: k_index", who);
+    if (need_logprob && (!b->q_index || !aligned16(b->q_index))) return fail(RIL_EINVAL, "%s: q_index", who);
+    if (b->selected_out && !aligned4(b->selected_out)) return fail(RIL_EINVAL, "%s: selected_out", who);
+  }
   return RIL_OK;
 }
 
-// MLA attention for `rows` rows (mode 0: decode rows; mode 1: packed prefill tokens,
-// enqueued in groups of max_rows rows that reuse the split partials in stream order).
-static ril_status run_mla(const ril_model *m, ril_kv *kv, const bf16_t *q, int mode, int rows,
-                          const int32_t *ctx_len, const int32_t *cu, const int32_t *start_pos, int n_seqs,
-                          const int32_t *page_table, int page_stride, int ctx_bound, void *ws, hipStream_t st) {
+// The shared latent (and indexer key) write of both MLA kinds.
+static ril_status run_mla_write(const ril_model *m, ril_kv *kv, const bf16_t *c, const float *kidx, int n_tok,
+                                int mode, const int32_t *cu, const int32_t *start_pos, int n_seqs,
+                                const int32_t *ctx_len, const int32_t *page_table, int page_stride, hipStream_t st) {
   const ril_model_desc &d = m->d;
+  MlaKvWriteArgs a{c, d.head_dim + d.rope_dim, m->sparse ? kidx : nullptr, n_tok, mode, cu, start_pos, n_seqs,
+                   ctx_len, page_table, page_stride, (bf16_t *)kv->pool, (int)(m->page_bytes / 2), kv->n_pages};
+  RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(a, st));
+  return RIL_OK;
+}
+
+// MLA attention for `rows` rows (mode 0: decode rows; mode 1: packed prefill tokens),
+// enqueued in groups of max_rows rows that reuse the workspace in stream order.  The
+// sparse kind first scores every history position (S6) and selects the top-k (S7).
+static ril_status run_mla(const ril_model *m, ril_kv *kv, const bf16_t *q, const float *q_index,
+                          int32_t *sel_out, int mode, int rows, const int32_t *ctx_len, const int32_t *cu,
+                          const int32_t *start_pos, int n_seqs, const int32_t *page_table, int page_stride,
+                          int ctx_bound, void *ws, hipStream_t st) {
+  const ril_model_desc &d = m->d;
+  const int page_elems = (int)(m->page_bytes / 2);
   for (int r0 = 0; r0 < rows; r0 += d.max_rows) {
     const int n = std::min(d.max_rows, rows - r0);
+    int32_t *sel = nullptr;
+    if (m->sparse) {
+      sel = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + m->off_sel);
+      IndexerArgs ia{q_index, mode, r0, n, ctx_len, cu, start_pos, n_seqs, page_table, page_stride,
+                     (const bf16_t *)kv->pool, page_elems, kv->n_pages, ctx_bound, wsf(ws, m->off_scores),
+                     d.max_ctx, d.topk, sel, sel_out};
+      RIL_LAUNCH(RIL_K_INDEXER, launch_indexer(ia, st));
+      RIL_LAUNCH(RIL_K_TOPK, launch_topk(ia, st));
+    }
     MlaAttnArgs a{q, mode, r0, n, ctx_len, cu, start_pos, n_seqs, page_table, page_stride,
-                  (const bf16_t *)kv->pool, kv->n_pages, d.n_q_heads, d.split_tokens, ctx_bound, m->max_splits,
-                  m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn)};
+                  (const bf16_t *)kv->pool, page_elems, kv->n_pages, d.n_q_heads, d.split_tokens, ctx_bound,
+                  m->max_splits, sel, d.topk, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml),
+                  wsb(ws, m->off_attn)};
     RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_mla_split(a, st));
     RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_mla_merge(a, st));
   }
@@ -407,13 +453,9 @@ extern "C" ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_pre
   if (s != RIL_OK) return s;
   const ril_model_desc &d = m->d;
   hipStream_t st = (hipStream_t)stream;
-  if (d.attn_kind == RIL_ATTN_MLA) {
-    MlaKvWriteArgs a{(const bf16_t *)b->k, d.head_dim + d.rope_dim, b->total_tokens, 0, b->cu_tokens,
-                     b->start_pos, b->n_seqs, nullptr, b->page_table, b->page_stride, (bf16_t *)kv->pool,
-                     kv->n_pages};
-    RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(a, st));
-    return RIL_OK;
-  }
+  if (m->mla)
+    return run_mla_write(m, kv, (const bf16_t *)b->k, b->k_index, b->total_tokens, 0, b->cu_tokens, b->start_pos,
+                         b->n_seqs, nullptr, b->page_table, b->page_stride, st);
   KvWriteArgs a{(const bf16_t *)b->k, (const bf16_t *)b->v, d.n_kv_heads * d.head_dim, b->total_tokens, 0,
                 b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table, b->page_stride,
                 (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
@@ -429,12 +471,12 @@ extern "C" ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const
   const ril_model_desc &d = m->d;
   hipStream_t st = (hipStream_t)stream;
   const int T = b->total_tokens;
-  if (d.attn_kind == RIL_ATTN_MLA) {
-    MlaKvWriteArgs kw{(const bf16_t *)b->k, d.head_dim + d.rope_dim, T, 0, b->cu_tokens, b->start_pos,
-                      b->n_seqs, nullptr, b->page_table, b->page_stride, (bf16_t *)kv->pool, kv->n_pages};
-    RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(kw, st));
-    s = run_mla(m, kv, (const bf16_t *)b->q, 1, T, nullptr, b->cu_tokens, b->start_pos, b->n_seqs, b->page_table,
-                b->page_stride, b->max_ctx_bound, ws, st);
+  if (m->mla) {
+    s = run_mla_write(m, kv, (const bf16_t *)b->k, b->k_index, T, 0, b->cu_tokens, b->start_pos, b->n_seqs,
+                      nullptr, b->page_table, b->page_stride, st);
+    if (s != RIL_OK) return s;
+    s = run_mla(m, kv, (const bf16_t *)b->q, b->q_index, b->selected_out, 1, T, nullptr, b->cu_tokens,
+                b->start_pos, b->n_seqs, b->page_table, b->page_stride, b->max_ctx_bound, ws, st);
     if (s != RIL_OK) return s;
     return run_head(m, T, b->target_ids, logprob_out, ws, st);
   }
@@ -480,17 +522,20 @@ extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, c
   if (!logprob_out || !aligned4(logprob_out)) return fail(RIL_EINVAL, "decode_step_logprobs: logprob_out");
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
   if (tok && (!b->token_ids || !aligned4(b->token_ids))) return fail(RIL_EINVAL, "decode_step_logprobs: token_ids");
-  const bool need_v = d.attn_kind != RIL_ATTN_MLA;
+  const bool need_v = !m->mla;
   if (!tok && (!b->q || !b->k || !aligned16(b->q) || !aligned16(b->k) || (need_v && (!b->v || !aligned16(b->v)))))
     return fail(RIL_EINVAL, "decode_step_logprobs: q/k/v");
+  if (m->sparse && (!b->q_index || !b->k_index || !aligned16(b->q_index) || !aligned16(b->k_index) ||
+                    (b->selected_out && !aligned4(b->selected_out))))
+    return fail(RIL_EINVAL, "decode_step_logprobs: q_index/k_index/selected_out");
   hipStream_t st = (hipStream_t)stream;
   const int R = b->n_rows;
-  if (d.attn_kind == RIL_ATTN_MLA) {
-    MlaKvWriteArgs kw{(const bf16_t *)b->k, d.head_dim + d.rope_dim, R, 1, nullptr, nullptr, 0, b->ctx_len,
-                      b->page_table, b->page_stride, (bf16_t *)kv->pool, kv->n_pages};
-    RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(kw, st));
-    s = run_mla(m, kv, (const bf16_t *)b->q, 0, R, b->ctx_len, nullptr, nullptr, 0, b->page_table, b->page_stride,
-                b->max_ctx_bound, ws, st);
+  if (m->mla) {
+    s = run_mla_write(m, kv, (const bf16_t *)b->k, b->k_index, R, 1, nullptr, nullptr, 0, b->ctx_len, b->page_table,
+                      b->page_stride, st);
+    if (s != RIL_OK) return s;
+    s = run_mla(m, kv, (const bf16_t *)b->q, b->q_index, b->selected_out, 0, R, b->ctx_len, nullptr, nullptr, 0,
+                b->page_table, b->page_stride, b->max_ctx_bound, ws, st);
     if (s != RIL_OK) return s;
     return run_head(m, R, b->target_ids, logprob_out, ws, st);
   }

@@ -1,0 +1,224 @@
+// The lightweight indexer and the stable top-k selection of sparse attention (S6, S7).
+//
+// The indexer scores every history position of a query (Bitwise-consistent RL post,
+// sections 3 and 4.3).  Its formula is a reading (the pages give none):
+//   I[s] = sum_h relu(q_h . k_s),  64 heads x 128 dims, unit head weights,
+// computed in fp32 with one rounding per multiply and per add, in the fixed order
+// d = 0..127 inside a head and h = 0..63 across heads.  The selection is an integer
+// decided by these floats, so the arithmetic is kept reproducible exactly: the same
+// bits on every path, and in a float32 reference outside this library.
+//
+// The selection ranks positions by the unique key (score, position): higher score
+// first, equal scores broken toward the lower position (post section 4.3 breaks ties
+// toward the larger position; the workload spec asks for the lowest index), keeps the
+// best k, and lists them by descending position with -1 padding, the order the
+// attention then accumulates in.  Contexts of at most k positions select every
+// position (the same list any longer path would produce: no shortcut changes it).
+#include "attn_common.h"
+#include "kernels.h"
+
+namespace ril {
+
+constexpr int kIdxHeads = 64, kIdxDim = 128;
+constexpr int kIdxKeyOffset = kPage * 576;  // bf16 elements: the keys follow the latent block
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkMax = 4096;
+
+__device__ __forceinline__ void index_row(int mode, int r, int row0, const int32_t *ctx_len, const int32_t *cu,
+                                          const int32_t *start_pos, int n_seqs, int &seq, int &ctx, long &qrow) {
+  if (mode == 0) {
+    seq = r;
+    ctx = ctx_len[r];
+    qrow = r;
+  } else {
+    const int j = row0 + r;
+    seq = locate_seq(cu, n_seqs, j);
+    ctx = start_pos[seq] + (j - cu[seq]) + 1;
+    qrow = j;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S6: grid (ceil(ctx_bound / 256), rows), one thread per history position.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void indexer_kernel(
+    const float *__restrict__ q, int mode, int row0, const int32_t *__restrict__ ctx_len,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
+    const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool, int page_elems,
+    int n_pages, int ctx_bound, float *__restrict__ scores, int score_stride) {
+  const int r = blockIdx.y;
+  int seq, ctx;
+  long qrow;
+  index_row(mode, r, row0, ctx_len, cu, start_pos, n_seqs, seq, ctx, qrow);
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (ctx < 1 || ctx > ctx_bound || s >= ctx) return;
+  float *out = scores + (long)r * score_stride + s;
+  const int pid = page_table[(long)seq * page_stride + s / kPage];
+  if ((unsigned)pid >= (unsigned)n_pages) {
+    *out = __builtin_nanf("");
+    return;
+  }
+  const float *kp = reinterpret_cast<const float *>(pool + (long)pid * page_elems + kIdxKeyOffset) + (s % kPage) * kIdxDim;
+  float k[kIdxDim];
+#pragma unroll
+  for (int i = 0; i < kIdxDim / 4; ++i) {
+    const u32x4 v = ld16(kp + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[4 * i + j] = __uint_as_float(v[j]);
+  }
+  const float *qr = q + qrow * (kIdxHeads * kIdxDim);  // the same for the whole workgroup
+  float total = 0.f;
+  for (int h = 0; h < kIdxHeads; ++h) {
+    float acc = 0.f;
+#pragma unroll
+    for (int d = 0; d < kIdxDim; ++d) acc = __fadd_rn(acc, __fmul_rn(qr[h * kIdxDim + d], k[d]));
+    total = __fadd_rn(total, acc > 0.f ? acc : 0.f);
+  }
+  *out = total;
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t ord32(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// S7: grid (rows), 1024 threads.  Radix select of the k-th largest score over four
+// 8-bit digits (histograms in LDS: their counts do not depend on thread order), then
+// the lowest-position ties at the threshold by a wave-ordered prefix count, then a
+// bitonic sort of the k positions into descending order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    const float *__restrict__ scores, int score_stride, int mode, int row0, const int32_t *__restrict__ ctx_len,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs, int ctx_bound, int K,
+    int32_t *__restrict__ sel, int32_t *__restrict__ sel_copy) {
+  __shared__ int hist[256];
+  __shared__ int buf[kTopkMax];
+  __shared__ int wave_cnt[kTopkThreads / 64];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need, s_ties, s_count, s_taken;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int seq, ctx;
+  long qrow;
+  index_row(mode, r, row0, ctx_len, cu, start_pos, n_seqs, seq, ctx, qrow);
+  int32_t *out = sel + (long)r * K;
+  int32_t *cpy = sel_copy ? sel_copy + (row0 + (long)r) * K : nullptr;
+  if (ctx < 1 || ctx > ctx_bound || ctx <= K) {
+    // every position, descending (an invalid row selects nothing; its attention is NaN)
+    const int n = (ctx < 1 || ctx > ctx_bound) ? 0 : ctx;
+    for (int i = tid; i < K; i += kTopkThreads) {
+      const int v = i < n ? n - 1 - i : -1;
+      out[i] = v;
+      if (cpy) cpy[i] = v;
+    }
+    return;
+  }
+  const int n = ctx;
+  const float *sc = scores + (long)r * score_stride;
+  if (tid == 0) {
+    s_prefix = 0u;
+    s_need = K;
+  }
+  uint32_t mask = 0u;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int b = tid; b < 256; b += kTopkThreads) hist[b] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+    for (int s = tid; s < n; s += kTopkThreads) {
+      const uint32_t u = ord32(sc[s]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, need = s_need;
+      for (int b = 255; b >= 0; --b) {
+        if (cum + hist[b] >= need) {
+          s_prefix = prefix | ((uint32_t)b << shift);
+          s_need = need - cum;
+          s_ties = hist[b];
+          break;
+        }
+        cum += hist[b];
+      }
+    }
+    mask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = s_prefix;
+  const int need = s_need, ties = s_ties;
+  if (tid == 0) {
+    s_count = 0;
+    s_taken = 0;
+  }
+  __syncthreads();
+  // everything above the threshold, in any order (the sort below fixes the order)
+  for (int s = tid; s < n; s += kTopkThreads) {
+    const uint32_t u = ord32(sc[s]);
+    if (u > thr || (u == thr && need == ties)) buf[atomicAdd(&s_count, 1)] = s;
+  }
+  if (need < ties) {
+    // the `need` lowest positions among the scores equal to the threshold
+    for (int c0 = 0; c0 < n; c0 += kTopkThreads) {
+      __syncthreads();
+      const int s = c0 + tid;
+      const bool flag = s < n && ord32(sc[s]) == thr;
+      const unsigned long long bal = __ballot(flag);
+      const int below = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int before = s_taken;
+      for (int w = 0; w < wave; ++w) before += wave_cnt[w];
+      if (flag && before + below < need) buf[atomicAdd(&s_count, 1)] = s;
+      __syncthreads();
+      if (tid == 0) {
+        int t = 0;
+        for (int w = 0; w < kTopkThreads / 64; ++w) t += wave_cnt[w];
+        s_taken += t;
+      }
+      __syncthreads();
+      if (s_taken >= need) break;
+    }
+  }
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= K; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < K / 2; i += kTopkThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const int a = buf[lo], b = buf[hi];
+        if ((a < b) == desc) {
+          buf[lo] = b;
+          buf[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < K; i += kTopkThreads) {
+    out[i] = buf[i];
+    if (cpy) cpy[i] = buf[i];
+  }
+}
+
+hipError_t launch_indexer(const IndexerArgs &a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  dim3 grid((a.ctx_bound + 255) / 256, a.n_rows);
+  hipLaunchKernelGGL(indexer_kernel, grid, dim3(256), 0, st, a.q, a.mode, a.row0, a.ctx_len, a.cu, a.start_pos,
+                     a.n_seqs, a.page_table, a.page_stride, a.pool, a.page_elems, a.n_pages, a.ctx_bound, a.scores,
+                     a.score_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const IndexerArgs &a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(a.n_rows), dim3(kTopkThreads), 0, st, a.scores, a.score_stride, a.mode,
+                     a.row0, a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.ctx_bound, a.topk, a.sel, a.sel_copy);
+  return hipGetLastError();
+}
+
+}  // namespace ril

@@ -83,13 +83,15 @@ struct LmHeadArgs {
 
 struct MlaKvWriteArgs {
   const bf16_t *c;  // latent rows [n_tok, row_stride], 576 dims used
-  int row_stride, n_tok, mode;
+  int row_stride;
+  const float *kidx;  // sparse only: fp32 indexer keys [n_tok, 128], else null
+  int n_tok, mode;
   const int32_t *cu, *start_pos;
   int n_seqs;
   const int32_t *ctx_len, *page_table;
   int page_stride;
   bf16_t *pool;
-  int n_pages;
+  int page_elems, n_pages;
 };
 
 struct MlaAttnArgs {
@@ -100,11 +102,32 @@ struct MlaAttnArgs {
   const int32_t *page_table;
   int page_stride;
   const bf16_t *pool;
-  int n_pages, H, split_tokens, ctx_bound, max_splits;
+  int page_elems, n_pages, H, split_tokens, ctx_bound, max_splits;
+  const int32_t *sel;  // sparse: selection lists [n_rows, topk] (rows of this launch), else null
+  int topk;
   float cscale;
   float *part_o, *part_ml;
   bf16_t *out;  // [rows or tokens, H, 512]
 };
+
+struct IndexerArgs {
+  const float *q;  // [rows or tokens, 64, 128] fp32
+  int mode, row0, n_rows;
+  const int32_t *ctx_len, *cu, *start_pos;
+  int n_seqs;
+  const int32_t *page_table;
+  int page_stride;
+  const bf16_t *pool;
+  int page_elems, n_pages, ctx_bound;
+  float *scores;  // [n_rows, score_stride] (rows of this launch)
+  int score_stride;
+  int topk;
+  int32_t *sel;  // [n_rows, topk]
+  int32_t *sel_copy;  // optional caller copy [all rows, topk] at row0, or null
+};
+
+hipError_t launch_indexer(const IndexerArgs &a, hipStream_t st);
+hipError_t launch_topk(const IndexerArgs &a, hipStream_t st);
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t st);
 hipError_t launch_mla_kv_write(const MlaKvWriteArgs &a, hipStream_t st);

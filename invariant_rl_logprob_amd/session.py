@@ -25,20 +25,29 @@ def _i32(x, device):
     return torch.as_tensor(x, dtype=torch.int32).to(device)
 
 
+def _cat(xs):
+    return None if xs is None else torch.cat(list(xs)).contiguous()
+
+
+def _c(x):
+    return None if x is None else x.contiguous()
+
+
 class Session:
     """One model + one KV pool on one device."""
 
     def __init__(self, *, n_q_heads, n_kv_heads, head_dim, vocab, d_head, w_lm, max_rows, max_tokens,
                  max_ctx, pool_pages, softmax_scale, rms_eps=1e-6, split_tokens=512, shuffle_seed=0,
                  input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
-                 norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, device="cuda"):
+                 norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, index_heads=0, index_dim=0, topk=0,
+                 device="cuda"):
         self.device = torch.device(device)
         self._keep = [w_lm, embed, w_qkv, w_o, norm_attn, norm_final]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
-                                   d_head, vocab, PAGE, split_tokens, max_rows, max_tokens, max_ctx,
-                                   softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o), p(norm_attn),
-                                   p(norm_final), p(w_lm))
+                                   index_heads, index_dim, topk, d_head, vocab, PAGE, split_tokens, max_rows,
+                                   max_tokens, max_ctx, softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o),
+                                   p(norm_attn), p(norm_final), p(w_lm))
         self.model = ril_model_create(self.desc)
         self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
         self.max_ctx = max_ctx
@@ -92,77 +101,67 @@ class Session:
             self.ensure(s, int(st) + int(n))
         return cu, bound
 
-    def write_kv(self, seqs, starts, ks, vs) -> None:
-        """The shared write path alone: k/v [n_i, Hkv, D] of sequence i at positions starts[i].."""
+    def write_kv(self, seqs, starts, ks, vs, k_index=None) -> None:
+        """The shared write path alone: k/v [n_i, ...] (and indexer keys) of sequence i at
+        positions starts[i].."""
         lens = [k.shape[0] for k in ks]
         cu, bound = self._packed(seqs, starts, lens)
-        k = torch.cat(list(ks)).contiguous()
-        v = None if vs is None else torch.cat(list(vs)).contiguous()
+        k, v, ki = _cat(ks), _cat(vs), _cat(k_index)
         cu_t, st_t = _i32(cu, self.device), _i32(list(starts), self.device)
         pt = self.page_table(seqs, bound)
         b = make_prefill_batch(cu_tokens=cu_t, start_pos=st_t, page_table=pt, max_ctx_bound=bound,
-                               k=k, v=v, total_tokens=cu[-1])
+                               k=k, v=v, k_index=ki, total_tokens=cu[-1])
         ril_kv_write(self.model, self.kv, b)
-        self._last = (k, v, cu_t, st_t, pt)
+        self._last = (k, v, ki, cu_t, st_t, pt)
 
-    def prefill(self, seqs, starts, *, targets, qs=None, ks=None, vs=None, tokens=None,
-                ctx_bound: Optional[int] = None) -> torch.Tensor:
+    def prefill(self, seqs, starts, *, targets, qs=None, ks=None, vs=None, tokens=None, q_index=None,
+                k_index=None, selected_out=None, ctx_bound: Optional[int] = None) -> torch.Tensor:
         """Packed prefill of sequences seqs[i] at positions starts[i].. ; returns fp32 [total]."""
         src = tokens if tokens is not None else qs
         lens = [t.shape[0] for t in src]
         cu, bound = self._packed(seqs, starts, lens)
         bound = ctx_bound or bound
-        cat = lambda xs: None if xs is None else torch.cat(list(xs)).contiguous()  # noqa: E731
-        q, k, v, tok = cat(qs), cat(ks), cat(vs), cat(tokens)
+        q, k, v, tok, qi, ki = _cat(qs), _cat(ks), _cat(vs), _cat(tokens), _cat(q_index), _cat(k_index)
         tgt = torch.cat(list(targets)).to(torch.int32).contiguous()
         cu_t, st_t = _i32(cu, self.device), _i32(list(starts), self.device)
         pt = self.page_table(seqs, bound)
         out = torch.empty(cu[-1], dtype=torch.float32, device=self.device)
         b = make_prefill_batch(cu_tokens=cu_t, start_pos=st_t, page_table=pt, max_ctx_bound=bound,
-                               target_ids=tgt, token_ids=tok, q=q, k=k, v=v, total_tokens=cu[-1])
+                               target_ids=tgt, token_ids=tok, q=q, k=k, v=v, q_index=qi, k_index=ki,
+                               selected_out=selected_out, total_tokens=cu[-1])
         ril_prefill_logprobs(self.model, self.kv, b, out, self.ws)
-        self._last = (q, k, v, tok, tgt, cu_t, st_t, pt)
+        self._last = (q, k, v, tok, qi, ki, tgt, cu_t, st_t, pt)
         return out
 
-    def decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None,
-               ctx_bound: Optional[int] = None) -> torch.Tensor:
-        """One decode step: row i of sequence seqs[i] at context ctx[i]; returns fp32 [rows]."""
+    def _decode_batch(self, seqs, ctx, targets, q, k, v, tokens, q_index, k_index, selected_out, ctx_bound):
         ctx = [int(c) for c in ctx]
         for s, c in zip(seqs, ctx):
             self.ensure(s, c)
         bound = ctx_bound or max(ctx)
-        ctx_t = _i32(ctx, self.device)
-        pt = self.page_table(seqs, bound)
-        tgt = targets.to(torch.int32).contiguous()
-        out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
-        b = make_decode_batch(ctx_len=ctx_t, page_table=pt, max_ctx_bound=bound, target_ids=tgt,
-                              token_ids=None if tokens is None else tokens.contiguous(),
-                              q=None if q is None else q.contiguous(),
-                              k=None if k is None else k.contiguous(),
-                              v=None if v is None else v.contiguous())
-        ril_decode_step_logprobs(self.model, self.kv, b, out, self.ws)
-        self._last = (ctx_t, pt, tgt, tokens, q, k, v)
-        return out
-
-    def prepare_decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None,
-                       ctx_bound: Optional[int] = None):
-        """Build a decode batch once; returns (launch, out) where launch() enqueues the step
-        on the current stream with no host-side tensor work (for timed loops)."""
-        ctx = [int(c) for c in ctx]
-        for s, c in zip(seqs, ctx):
-            self.ensure(s, c)
-        bound = ctx_bound or max(ctx)
-        keep = {
-            "ctx": _i32(ctx, self.device), "pt": self.page_table(seqs, bound),
-            "tgt": targets.to(torch.int32).contiguous(),
-            "tok": None if tokens is None else tokens.contiguous(),
-            "q": None if q is None else q.contiguous(), "k": None if k is None else k.contiguous(),
-            "v": None if v is None else v.contiguous(),
-        }
-        out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
+        keep = {"ctx": _i32(ctx, self.device), "pt": self.page_table(seqs, bound),
+                "tgt": targets.to(torch.int32).contiguous(), "tok": _c(tokens), "q": _c(q), "k": _c(k),
+                "v": _c(v), "qi": _c(q_index), "ki": _c(k_index)}
         b = make_decode_batch(ctx_len=keep["ctx"], page_table=keep["pt"], max_ctx_bound=bound,
                               target_ids=keep["tgt"], token_ids=keep["tok"], q=keep["q"], k=keep["k"],
-                              v=keep["v"])
+                              v=keep["v"], q_index=keep["qi"], k_index=keep["ki"], selected_out=selected_out)
+        return b, keep
+
+    def decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None, q_index=None, k_index=None,
+               selected_out=None, ctx_bound: Optional[int] = None) -> torch.Tensor:
+        """One decode step: row i of sequence seqs[i] at context ctx[i]; returns fp32 [rows]."""
+        b, keep = self._decode_batch(seqs, ctx, targets, q, k, v, tokens, q_index, k_index, selected_out,
+                                     ctx_bound)
+        out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
+        ril_decode_step_logprobs(self.model, self.kv, b, out, self.ws)
+        self._last = keep
+        return out
+
+    def prepare_decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None, q_index=None,
+                       k_index=None, ctx_bound: Optional[int] = None):
+        """Build a decode batch once; returns (launch, out) where launch() enqueues the step
+        on the current stream with no host-side tensor work (for timed loops)."""
+        b, keep = self._decode_batch(seqs, ctx, targets, q, k, v, tokens, q_index, k_index, None, ctx_bound)
+        out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
         stream = torch.cuda.current_stream(self.device).cuda_stream
 
         def launch():

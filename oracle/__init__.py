@@ -37,6 +37,8 @@ from .models import (  # noqa: F401
     head_logprob,
     mla_row_attention,
     indexer_scores,
+    indexer_scores_fp32,
+    sparse_mla_row_attention,
     topk_select,
 )
 from .metrics import diff_stats, k3_mean  # noqa: F401

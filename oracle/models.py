@@ -190,6 +190,40 @@ def indexer_scores(q_idx, K_idx) -> np.ndarray:
     return np.maximum(K @ q.T, 0.0).sum(axis=1)
 
 
+def indexer_scores_fp32(q_idx, K_idx) -> np.ndarray:
+    """The indexer in the precision the selection is decided in: float32, one rounding
+    per multiply and per add, accumulated in a fixed order.
+
+    A top-k selection is an integer decided by floating point, so both sides must
+    decide it in the same arithmetic (a one-ulp difference can swap a selected
+    position, Bitwise-consistent RL post section 4.3).  The order: for head h = 0..63,
+    acc_h = (((0 + q_h0 k_0) + q_h1 k_1) + ...) over d = 0..D-1; then
+    I = (((0 + relu(acc_0)) + relu(acc_1)) + ...) over h.  relu(x) = x if x > 0 else +0.
+    q [Hi, D], K [n, D] (float32 values) -> float32 [n].  Pinned by: a pure-Python
+    float32 loop on tiny inputs; agreement with indexer_scores within the fp32 bound.
+    """
+    q = np.asarray(widen(q_idx), dtype=np.float32)
+    K = np.asarray(widen(K_idx), dtype=np.float32)
+    n = K.shape[0]
+    total = np.zeros(n, dtype=np.float32)
+    for h in range(q.shape[0]):
+        acc = np.zeros(n, dtype=np.float32)
+        for d in range(q.shape[1]):
+            acc = acc + q[h, d] * K[:, d]
+        total = total + np.where(acc > 0, acc, np.float32(0))
+    return total
+
+
+def sparse_mla_row_attention(q, C, selected, scale: float, dv: int) -> np.ndarray:
+    """MLA attention of one query over the selected history positions only (the list
+    may be padded with -1).  The set is what matters in float64; the order the kernel
+    accumulates in is the list order (descending position)."""
+    sel = np.asarray(selected)
+    sel = sel[sel >= 0]
+    C = widen(C)
+    return mla_row_attention(q, C[sel], scale, dv)
+
+
 def topk_select(scores, k: int, tie: str = "lowest") -> np.ndarray:
     """Stable top-k: the k best (score, position) keys, listed by descending position.
 

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 def _desc(**kw):
     # fake device addresses: model_create only validates them (16-byte aligned, non-null)
     base = dict(attn_kind=0, input_mode=ril.RIL_INPUT_QKV, d_model=0, n_q_heads=32, n_kv_heads=8,
-                head_dim=128, rope_dim=0, d_head=4096, vocab=129280, page_tokens=16, split_tokens=512,
+                head_dim=128, rope_dim=0, index_heads=0, index_dim=0, topk=0, d_head=4096, vocab=129280, page_tokens=16, split_tokens=512,
                 max_rows=64, max_tokens=1024, max_ctx=8192, softmax_scale=0.088388, rms_eps=1e-6,
                 embed=None, w_qkv=None, w_o=None, norm_attn=None, norm_final=None, w_lm=0x10000)
     base.update(kw)

@@ -251,6 +251,48 @@ def test_indexer_brute_force():
     assert np.allclose(oracle.indexer_scores(q, K), want, rtol=1e-14, atol=1e-14)
 
 
+def test_indexer_fp32_brute_force_float32_loop():
+    # pure-Python loop over numpy float32 scalars: one rounding per multiply and add
+    q = RNG.standard_normal((3, 5)).astype(np.float32)
+    K = RNG.standard_normal((7, 5)).astype(np.float32)
+    want = []
+    for s in range(7):
+        tot = np.float32(0)
+        for h in range(3):
+            acc = np.float32(0)
+            for d in range(5):
+                acc = np.float32(acc + np.float32(q[h, d] * K[s, d]))
+            tot = np.float32(tot + (acc if acc > 0 else np.float32(0)))
+        want.append(tot)
+    got = oracle.indexer_scores_fp32(q, K)
+    assert got.dtype == np.float32 and np.array_equal(got, np.array(want, dtype=np.float32))
+
+
+def test_indexer_fp32_within_error_bound_of_fp64():
+    # |fl32 - exact| <= gamma_n * sum_h sum_d |q_hd k_d| with n = D + H (sequential sums)
+    q = RNG.standard_normal((64, 128)).astype(np.float32)
+    K = RNG.standard_normal((300, 128)).astype(np.float32)
+    exact = oracle.indexer_scores(q, K)
+    got = oracle.indexer_scores_fp32(q, K).astype(np.float64)
+    u = 2.0 ** -24
+    n = 128 + 64
+    bound = (n * u / (1 - n * u)) * (np.abs(K.astype(np.float64)) @ np.abs(q.astype(np.float64)).T).sum(1)
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_sparse_mla_equals_dense_over_selection():
+    q = oracle.bf16(RNG.standard_normal((2, 576)))
+    C = oracle.bf16(RNG.standard_normal((40, 576)))
+    sel = np.array([31, 17, 5, 2, -1, -1])
+    sc = 1 / math.sqrt(192)
+    got = oracle.sparse_mla_row_attention(q, C, sel, sc, 512)
+    want = oracle.mla_row_attention(q, C[[31, 17, 5, 2]], sc, 512)
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+    # all positions selected == dense attention
+    assert np.allclose(oracle.sparse_mla_row_attention(q, C, np.arange(40)[::-1], sc, 512),
+                       oracle.mla_row_attention(q, C, sc, 512), rtol=1e-13, atol=1e-14)
+
+
 def test_topk_pins():
     assert check_topk(oracle.topk_select)
 

@@ -223,6 +223,59 @@ def mla_row(row: int, w: MLADecode = MLA_DECODE_B128, device="cpu", ctx: int = N
     }
 
 
+@dataclasses.dataclass(frozen=True)
+class SparseMLADecode:
+    """MLA decode over the top-k positions an indexer selects: per position an fp32
+    indexer key [128] beside the bf16 latent row; per query an fp32 indexer query
+    [64, 128].  tie_stress > 0 copies the indexer key of one position into that many
+    other positions so exact score ties occur at known places."""
+    rows: int = 32
+    n_heads: int = 128
+    kv_rank: int = 512
+    rope_dim: int = 64
+    scale_dim: int = 192
+    index_heads: int = 64
+    index_dim: int = 128
+    topk: int = 2048
+    ctx_lo: int = 65536
+    ctx_hi: int = 65536
+    vocab: int = 129280
+    d_head: int = 4096
+    init_std: float = 0.02
+    rms_eps: float = 1e-6
+    page_tokens: int = 16
+    recompute_tokens: int = 16
+    tie_stress: int = 0
+    seed: int = 3
+
+
+SPARSE_MLA_B32 = SparseMLADecode()
+
+
+def sparse_row(row: int, w: SparseMLADecode = SPARSE_MLA_B32, device="cpu", ctx: int = None):
+    """As mla_row, plus k_index [ctx, 128] fp32 and q_index [R, 64, 128] fp32."""
+    L = int(randint(w.ctx_lo, w.ctx_hi, (1,), key(w.seed, "ctx", row))[0]) if ctx is None else int(ctx)
+    R = min(w.recompute_tokens, L)
+    s = w.seed
+    dq = w.kv_rank + w.rope_dim
+    k_index = randn((L, w.index_dim), key(s, "k_index", row, L), 1.0, device, dtype=torch.float32)
+    if w.tie_stress:
+        # one large key copied into tie_stress positions: those positions score exactly
+        # alike and (being 8x larger) at the top, so the tie rule decides the selection
+        big = randn((w.index_dim,), key(s, "tie_key", row, L), 8.0, device, dtype=torch.float32)
+        dst = randint(0, L - 1, (w.tie_stress,), key(s, "tie_dst", row, L)).to(torch.int64).to(device)
+        k_index[dst] = big
+    return {
+        "ctx": L,
+        "c": randn((L, dq), key(s, "c", row, L), 1.0, device),
+        "q": randn((R, w.n_heads, dq), key(s, "q", row, L), 1.0, device),
+        "k_index": k_index,
+        "q_index": randn((R, w.index_heads, w.index_dim), key(s, "q_index", row, L), 1.0, device,
+                         dtype=torch.float32),
+        "target": randint(0, w.vocab - 1, (R,), key(s, "target", row, L), device),
+    }
+
+
 def scaled(w, **changes):
     """A smaller variant of a workload for oracle-sized parity runs."""
     return dataclasses.replace(w, **changes)
