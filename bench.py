@@ -252,7 +252,79 @@ def bench_mla(args):
     }
 
 
-WORKLOADS = {"gqa_decode_b64": bench_gqa, "mla_decode_b128": bench_mla}
+# ---------------------------------------------------------------------------
+# sparse MLA over the indexer's top-2048, 32 rows of 65536 positions
+# ---------------------------------------------------------------------------
+
+def bench_sparse(args):
+    import numpy as np
+    import torch
+    import workloads as wl
+    from sparse_case import SparseCase
+
+    w = wl.SPARSE_MLA_B32
+    rows = list(range(w.rows))
+    t0 = time.time()
+    case = SparseCase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_rows=w.rows,
+                      max_tokens=w.rows * w.recompute_tokens)
+    ctx = [case.ctx(r) for r in rows]
+    log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
+    dec, diff = diff_check(case, rows)
+
+    d = case.data
+    q = torch.stack([d[r]["q"][-1] for r in rows])
+    qi = torch.stack([d[r]["q_index"][-1] for r in rows])
+    cl = torch.stack([d[r]["c"][case.ctx(r) - 1] for r in rows])
+    ki = torch.stack([d[r]["k_index"][case.ctx(r) - 1] for r in rows])
+    tgt = torch.stack([d[r]["target"][-1] for r in rows])
+    launch, out = case.sess.prepare_decode([("d", r) for r in rows], ctx, targets=tgt, q=q, k=cl, q_index=qi,
+                                           k_index=ki)
+    ms_step, kern = timed_steps(launch, args.steps, args.warmup)
+    last_equal = bool(np.array_equal(out.cpu().view(torch.int32).numpy(),
+                                     dec[:, -1].cpu().view(torch.int32).numpy()))
+
+    # indexer: every position's fp32 key (512 B) once per row; 2 flops per multiply-add
+    idx_bytes = sum(ctx) * w.index_dim * 4
+    idx_flops = sum(ctx) * w.index_heads * w.index_dim * 2
+    idx_us = kern["indexer"]["avg_us"]
+    idx_gbps = idx_bytes / (idx_us * 1e-6) / 1e9
+    idx_tflops = idx_flops / (idx_us * 1e-6) / 1e12
+    FP32_VALU_PEAK_TFLOPS = 157.3
+    roof = {"bound": "alu", "achieved": round(idx_tflops, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(idx_tflops / FP32_VALU_PEAK_TFLOPS, 4), "traffic": measured_traffic("indexer"),
+            "kernel": "indexer", "algorithmic_flops_per_launch": int(idx_flops), "avg_launch_us": round(idx_us, 2),
+            "hbm_gbps": round(idx_gbps, 1)}
+    sel_n = sum(min(c_, w.topk) for c_ in ctx)
+    attn_bytes = sel_n * (w.kv_rank + w.rope_dim) * 2
+    attn_us = kern["attn_split"]["avg_us"] + kern["attn_merge"]["avg_us"]
+
+    cpu = None
+    if not args.no_cpu and args.cpu_rows > 0:
+        import oracle  # the cpu_baseline leg
+        sample = rows[: max(1, args.cpu_rows // 6)]
+        t1 = time.time()
+        got = [case.oracle_row(r)[0] for r in sample]
+        secs = time.time() - t1
+        cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{len(sample)} of the {len(rows)} decode rows (fp32 indexer over 65536 positions, "
+                         f"top-2048, sparse MLA, projection and lm-head in fp64), {secs:.1f} s",
+               "max_abs_diff_vs_gpu": float(np.max(np.abs(np.array(got) - out.cpu().numpy()[: len(sample)])))}
+        log(f"oracle: {cpu}")
+
+    return {
+        "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+        "config": {"workload": "sparse_mla_b32: 32 decode rows of 65536 positions, fp32 indexer 64 heads x 128, "
+                               "stable top-2048 (ties to the lower position), MLA 128 heads over the selection, "
+                               "o-proj 65536x4096, lm-head 4096x129280",
+                   "rows": len(rows), "sum_ctx": sum(ctx), "split_entries": 256, "parallelism": "none (1 GPU)"},
+        "attn_hbm_gbps": round(attn_bytes / (attn_us * 1e-6) / 1e9, 1),
+        "diff": diff, "timed_step_equals_checked_decode": last_equal,
+        "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+
+
+WORKLOADS = {"gqa_decode_b64": bench_gqa, "mla_decode_b128": bench_mla, "sparse_mla_b32": bench_sparse}
 
 
 def main():
