@@ -113,7 +113,8 @@ typedef struct ril_model_desc {
   const void *w_o;        /* [d_head, Hq D]                 TOKENS: required; QKV: optional */
   const void *norm_attn;  /* [d_model] RMSNorm gain          TOKENS only; NULL = 1   */
   const void *norm_final; /* [d_head]  RMSNorm gain          NULL = 1                */
-  const void *w_lm;       /* [V, d_head]                     required                */
+  const void *w_lm;       /* [V, d_head] in the packed lm-head layout written by
+                             ril_pack_lm_head (ril_lm_head_packed_bytes)      required */
 } ril_model_desc;
 
 typedef struct ril_model ril_model;  /* opaque: copy of the description + derived sizes */
@@ -131,6 +132,26 @@ size_t ril_workspace_bytes(const ril_model *m);
 
 /* Bytes of one KV page: Hkv x 2 (K, V) x page_tokens x D x 2 bytes. */
 size_t ril_kv_page_bytes(const ril_model *m);
+
+/* S11 weight layout.  The lm-head reads its weight in a packed form: per vocabulary
+ * tile of 256 columns, per 16-column MFMA block, per 32-wide K step, that block's
+ * MFMA operand in lane order, so each weight load of a wavefront is one contiguous
+ * 1 KB read (the row-major [V, K] matrix would be read 64 bytes per row per step).
+ * Element (column c, k) of W sits at
+ *   ((((c/256)*16 + (c%256)/16) * (K/32) + k/32) * 64 + ((k%32)/8)*16 + c%16) * 8 + k%8
+ * and the columns past V in the last tile are zero.  Only the addresses change: the
+ * lm-head's arithmetic (its K order included) is the same for any layout.
+ *
+ * ril_lm_head_packed_bytes: size of the packed weight, ceil(V/256)*256*K*2 bytes
+ * (0 for V < 1 or K not a positive multiple of 32).
+ * ril_pack_lm_head: enqueue, on `stream`, the packing of the row-major bf16 device
+ * matrix src[V, K] (row stride K) into dst (device, packed_bytes >= the size above,
+ * 16-byte aligned, not overlapping src).  Call it again after every weight update.
+ * Returns RIL_EINVAL on bad sizes, alignment or a short dst, RIL_EHIP on a launch
+ * error; nothing is enqueued on error. */
+size_t ril_lm_head_packed_bytes(int32_t vocab, int32_t d_head);
+ril_status ril_pack_lm_head(const void *src, int32_t vocab, int32_t d_head, void *dst, size_t packed_bytes,
+                            void *stream);
 
 /* S1: page assignment.  Wrap a caller-owned device pool of `pool_bytes`
  * bytes (16-byte aligned) as floor(pool_bytes / page_bytes) pages and build a

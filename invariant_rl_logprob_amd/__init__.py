@@ -71,6 +71,8 @@ _model_create = _sig("ril_model_create", _c_int, [ctypes.POINTER(ril_model_desc)
 _model_destroy = _sig("ril_model_destroy", None, [_vp])
 _workspace_bytes = _sig("ril_workspace_bytes", ctypes.c_size_t, [_vp])
 _kv_page_bytes = _sig("ril_kv_page_bytes", ctypes.c_size_t, [_vp])
+_lm_head_packed_bytes = _sig("ril_lm_head_packed_bytes", ctypes.c_size_t, [_c_int, _c_int])
+_pack_lm_head = _sig("ril_pack_lm_head", _c_int, [_vp, _c_int, _c_int, _vp, ctypes.c_size_t, _vp])
 _ws_attn_offset = _sig("ril_ws_attn_offset", ctypes.c_size_t, [_vp])
 _kv_alloc = _sig("ril_kv_alloc", _c_int, [_vp, _vp, ctypes.c_size_t, ctypes.c_uint64, ctypes.POINTER(_vp)])
 _kv_assign = _sig("ril_kv_assign", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)])
@@ -89,6 +91,7 @@ _trace_read = _sig("ril_trace_read", _c_int, [_c_int, ctypes.POINTER(ctypes.c_do
                                               ctypes.POINTER(ctypes.c_int64)])
 
 EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril_kv_page_bytes",
+            "ril_lm_head_packed_bytes", "ril_pack_lm_head",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
             "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_trace_enable",
@@ -146,6 +149,18 @@ def ril_workspace_bytes(model: int) -> int:
 
 def ril_kv_page_bytes(model: int) -> int:
     return int(_kv_page_bytes(model))
+
+
+def ril_lm_head_packed_bytes(vocab: int, d_head: int) -> int:
+    return int(_lm_head_packed_bytes(vocab, d_head))
+
+
+def ril_pack_lm_head(w, packed, stream=None) -> None:
+    """Pack the row-major bf16 device matrix w [V, K] into `packed` (a device byte
+    tensor of at least ril_lm_head_packed_bytes(V, K) bytes), on the stream."""
+    V, K = w.shape
+    _check(_pack_lm_head(_ptr(w), V, K, _ptr(packed), packed.numel() * packed.element_size(), _stream(stream)),
+           "ril_pack_lm_head")
 
 
 def ril_ws_attn_offset(model: int) -> int:

@@ -153,6 +153,26 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
 extern "C" void ril_model_destroy(ril_model *m) { delete m; }
 extern "C" size_t ril_workspace_bytes(const ril_model *m) { return m ? m->ws_total : 0; }
 extern "C" size_t ril_kv_page_bytes(const ril_model *m) { return m ? m->page_bytes : 0; }
+
+extern "C" size_t ril_lm_head_packed_bytes(int32_t vocab, int32_t d_head) {
+  if (vocab < 1 || d_head < 32 || d_head % 32 != 0) return 0;
+  return (size_t)ril::lm_head_packed_elems(vocab, d_head) * sizeof(uint16_t);
+}
+
+extern "C" ril_status ril_pack_lm_head(const void *src, int32_t vocab, int32_t d_head, void *dst,
+                                       size_t packed_bytes, void *stream) {
+  const size_t need = ril_lm_head_packed_bytes(vocab, d_head);
+  if (need == 0) return fail(RIL_EINVAL, "pack_lm_head: vocab must be >= 1 and d_head a positive multiple of 32");
+  if (!src || !dst) return fail(RIL_EINVAL, "pack_lm_head: src and dst are required");
+  if (((uintptr_t)src | (uintptr_t)dst) % 16) return fail(RIL_EINVAL, "pack_lm_head: pointers must be 16-byte aligned");
+  if (packed_bytes < need) return fail(RIL_EINVAL, "pack_lm_head: dst is smaller than ril_lm_head_packed_bytes");
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (size_t)vocab * d_head * 2, d0 = (uintptr_t)dst, d1 = d0 + need;
+  if (s0 < d1 && d0 < s1) return fail(RIL_EINVAL, "pack_lm_head: src and dst overlap");
+  const hipError_t e = ril::launch_pack_lm_head((const bf16_t *)src, vocab, d_head, (bf16_t *)dst,
+                                                (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "pack_lm_head: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
 extern "C" size_t ril_ws_attn_offset(const ril_model *m) { return m ? m->off_attn : 0; }
 
 // ---------------------------------------------------------------------------

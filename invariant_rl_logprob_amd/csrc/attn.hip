@@ -80,20 +80,20 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 // The tile routine shared by decode and prefill
 // ---------------------------------------------------------------------------
 
-// One 64-token tile of K and V in MFMA operand registers (16-byte loads per lane).
-//   k[2kc+h][c] : A operand of S^T = K Q^T for M-block (kc, h), dims 32c .. 32c+31;
-//                 row r <-> token 32kc + 8(r/4) + 4h + r%4
-//   v[kc][db]   : A operand of o^T += V^T P^T for 32-token step kc, dims 16db .. 16db+15;
-//                 k-slot 8(lane/16) + j <-> token 32kc + 8(lane/16) + j
+// Half of a 64-token tile in MFMA operand registers (D/8 16-byte values per lane):
+// either its K half or its V half.
+//   K half, r[mb*(D/32) + c]  : A operand of S^T = K Q^T for M-block mb = 2kc + h,
+//                               dims 32c .. 32c+31; row r <-> token 32kc + 8(r/4) + 4h + r%4
+//   V half, r[kc*(D/16) + db] : A operand of o^T += V^T P^T for 32-token step kc, dims
+//                               16db .. 16db+15; k-slot 8(lane/16) + j <-> token 32kc + 8(lane/16) + j
 template <int D>
-struct KVTile {
-  u32x4 k[4][D / 32];
-  u32x4 v[2][D / 16];
+struct Half {
+  u32x4 r[D / 8];
 };
 
 // pg[k]: K block of the tile's k-th page (its V block follows at +16*D).
 template <int D>
-__device__ __forceinline__ void load_tile(KVTile<D> &t, const bf16_t *const (&pg)[4]) {
+__device__ __forceinline__ void load_k(Half<D> &t, const bf16_t *const (&pg)[4]) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
   const int rq = r16 >> 2, ri = r16 & 3;
@@ -103,40 +103,51 @@ __device__ __forceinline__ void load_tile(KVTile<D> &t, const bf16_t *const (&pg
     for (int h = 0; h < 2; ++h) {
       const bf16_t *kb = pg[2 * kc + (rq >> 1)] + grp * 128 + h * 64 + (rq & 1) * 32 + ri * 8;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) t.k[2 * kc + h][c] = ld16(kb + c * 512);
+      for (int c = 0; c < D / 32; ++c) t.r[(2 * kc + h) * (D / 32) + c] = ld16(kb + c * 512);
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(Half<D> &t, const bf16_t *const (&pg)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
     const bf16_t *vb = pg[2 * kc + (grp >> 1)] + 16 * D + (grp & 1) * (8 * D) + r16 * 8;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) t.v[kc][db] = ld16(vb + db * 128);
+    for (int db = 0; db < D / 16; ++db) t.r[kc * (D / 16) + db] = ld16(vb + db * 128);
   }
 }
 
-// One 64-token KV tile for the 16 query rows (MFMA columns) of this wave.
-//   qop     : B operand of S^T = K Q^T (lane: column lane%16, dims 32c + 8(lane/16) ..)
-//   pos     : this lane's column's query position (-1: padding column)
-//   vbound  : V values of tokens >= vbound are read as 0 (beyond any column's context)
-// State per lane = its column's (m, l) and o^T[16db + 4(lane/16) + i].
-// MAYBE_INACTIVE: some column may have pos < tile_start; such columns keep their state.
-template <int D, bool MAYBE_INACTIVE>
-__device__ __forceinline__ void attn_tile(const KVTile<D> &t, int tile_start,
-                                          const bf16x8 (&qop)[D / 32], int pos, int vbound,
-                                          float cscale, float &m, float &l, f32x4 (&o)[D / 16]) {
-  const int lane = threadIdx.x & 63;
-  const int grp = lane >> 4;
+// First half of the tile update for the 16 query rows (MFMA columns) of this wave:
+// scores from the K half, then the online-softmax step (tile_softmax).
+//   qop : B operand of S^T = K Q^T (lane: column lane%16, dims 32c + 8(lane/16) ..)
+//   pos : this lane's column's query position (-1: padding column)
+template <int D>
+__device__ __forceinline__ void attn_scores(const Half<D> &k, int tile_start, const bf16x8 (&qop)[D / 32],
+                                            int pos, float cscale, float m, float l, bf16x8 (&pop)[2],
+                                            float &alpha, float &m_new, float &l_new) {
   f32x4 s[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) acc = mfma(as_bf16x8(t.k[mb][c]), qop[c], acc);
+    for (int c = 0; c < D / 32; ++c) acc = mfma(as_bf16x8(k.r[mb * (D / 32) + c]), qop[c], acc);
     s[mb] = acc;
   }
-  bf16x8 pop[2];
-  float alpha, m_new, l_new;
   tile_softmax(s, tile_start, pos, cscale, m, l, pop, alpha, m_new, l_new);
+}
+
+// Second half: o = o * alpha + MFMA(bf16 P, V), two 32-token steps in token order.
+//   vbound : V values of tokens >= vbound are read as 0 (beyond any column's context)
+// State per lane = its column's (m, l) and o^T[16db + 4(lane/16) + i].
+// MAYBE_INACTIVE: some column may have pos < tile_start; such columns keep their state.
+template <int D, bool MAYBE_INACTIVE>
+__device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, int pos, int vbound,
+                                            const bf16x8 (&pop)[2], float alpha, float m_new, float l_new,
+                                            float &m, float &l, f32x4 (&o)[D / 16]) {
+  const int grp = (threadIdx.x & 63) >> 4;
   f32x4 on[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) on[db] = o[db] * alpha;
@@ -145,7 +156,7 @@ __device__ __forceinline__ void attn_tile(const KVTile<D> &t, int tile_start,
     const int n_valid = vbound - (tile_start + 32 * kc + 8 * grp);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      u32x4 vv = t.v[kc][db];
+      u32x4 vv = v.r[kc * (D / 16) + db];
       if (n_valid < 8) vv = keep_first(vv, n_valid);
       on[db] = mfma(as_bf16x8(vv), pop[kc], on[db]);
     }
@@ -165,6 +176,17 @@ __device__ __forceinline__ void attn_tile(const KVTile<D> &t, int tile_start,
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[db] = on[db];
   }
+}
+
+// One whole 64-token tile update (both halves).
+template <int D, bool MAYBE_INACTIVE>
+__device__ __forceinline__ void attn_tile(const Half<D> &k, const Half<D> &v, int tile_start,
+                                          const bf16x8 (&qop)[D / 32], int pos, int vbound,
+                                          float cscale, float &m, float &l, f32x4 (&o)[D / 16]) {
+  bf16x8 pop[2];
+  float alpha, m_new, l_new;
+  attn_scores<D>(k, tile_start, qop, pos, cscale, m, l, pop, alpha, m_new, l_new);
+  attn_values<D, MAYBE_INACTIVE>(v, tile_start, pos, vbound, pop, alpha, m_new, l_new, m, l, o);
 }
 
 template <int D>
@@ -205,50 +227,90 @@ __device__ __forceinline__ void tile_pages(const bf16_t *(&pg)[4], const bf16_t 
 }
 
 // ---------------------------------------------------------------------------
-// S8: decode split kernel.  grid (max splits, Hkv, rows), one wave each.  The next
-// tile's K/V loads are issued before the current tile is computed.
+// S8: decode split kernel, one wave per (row, kv head, split).  The 1-D grid lists the
+// work longest first, so the hardware dispatcher fills the machine with full splits and
+// ends on the short ones: slots [0, n_sg*R*Hkv) are the full splits, split-major (the
+// kv heads of one page adjacent); then for c = n_cls .. 1 one slot per (row, kv head)
+// whose partial last split has c tiles.  Slots with no such work exit at once.  Which
+// wave computes a split never changes its arithmetic.  K/V loads run up to two tiles
+// ahead of the tile being computed.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     const bf16_t *__restrict__ q, int q_row_stride, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool,
-    int n_pages, int Hkv, int G, int split_tokens, int ctx_bound, float cscale,
+    int n_pages, int Hkv, int G, int split_tokens, int ctx_bound, int n_rows, int n_sg, float cscale,
     float *__restrict__ part_o, float *__restrict__ part_ml, int max_splits) {
-  const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
   const int lane = threadIdx.x;
-  const int ctx = ctx_len[row];
-  const int s0 = split * split_tokens;
-  if (ctx < 1 || ctx > ctx_bound || s0 >= ctx) return;
-  const int Hq = Hkv * G;
+  const int per_s = Hkv * n_rows;
+  const int b = blockIdx.x;
+  const bool full = b < n_sg * per_s;
+  const int rem = full ? b % per_s : (b - n_sg * per_s) % per_s;
+  const int row = rem / Hkv, g = rem % Hkv;
+  const int cls = full ? 0 : split_tokens / kTile - (b - n_sg * per_s) / per_s;
   const int n = lane & 15, grp = lane >> 4;
   const bool col_ok = n < G;
-  const int s1 = min(ctx, s0 + split_tokens);
-  const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
-  int pid;
-  const bool bad = split_pages(page_table + (long)row * page_stride, s0 / kPage, (ctx - 1) / kPage,
-                               n_pages, pid);
-  KVTile<D> buf0, buf1;
-  const bf16_t *pg[4];
-  tile_pages<D>(pg, pool, pid, 0, Hkv, g);
-  load_tile<D>(buf0, pg);
+  const int32_t *pt = page_table + (long)row * page_stride;
+  // Loads that do not depend on the context length are issued together with it.
+  const int ctx = ctx_len[row];
+  int split = full ? b / per_s : 0;
+  int p_raw = full ? pt[min(split * (split_tokens / kPage) + lane, page_stride - 1)] : 0;
   bf16x8 qop[D / 32];
   load_qop<D>(qop, q + (long)row * q_row_stride + (g * G + (col_ok ? n : 0)) * D, col_ok);
+  if (ctx < 1 || ctx > ctx_bound) return;
+  if (full) {
+    if ((split + 1) * split_tokens > ctx) return;
+  } else {
+    const int tail = ctx % split_tokens;
+    if (tail == 0 || (tail + kTile - 1) / kTile != cls) return;
+    split = ctx / split_tokens;
+    p_raw = pt[min(split * (split_tokens / kPage) + lane, page_stride - 1)];
+  }
+  const int Hq = Hkv * G;
+  const int s0 = split * split_tokens;
+  const int s1 = min(ctx, s0 + split_tokens);
+  const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
+  // lane i: id of page s0/16 + i when that page holds context, else page 0 (its tokens
+  // are masked); an id outside the pool marks the row NaN.
+  const bool in_ctx = s0 / kPage + lane <= (ctx - 1) / kPage;
+  const bool bad_lane = in_ctx && (unsigned)p_raw >= (unsigned)n_pages;
+  const int pid = (in_ctx && !bad_lane) ? p_raw : 0;
+  const bool bad = __any(bad_lane);
+  // Five half-tile slots: while the scores of tile t run, the V half of t and both halves
+  // of t+1 and the K half of t+2 are in flight (64 KB per wave for D = 128).
+  // Half-tile h (K of tile h/2 if h is even, else its V) lives in slot h % 5.
+  Half<D> ring[5];
+  const bf16_t *pg[4];
+  tile_pages<D>(pg, pool, pid, 0, Hkv, g);
+  load_k<D>(ring[0], pg);
+  load_v<D>(ring[1], pg);
+  if (n_tiles > 1) {
+    tile_pages<D>(pg, pool, pid, 1, Hkv, g);
+    load_k<D>(ring[2], pg);
+    load_v<D>(ring[3], pg);
+  }
   float m = neg_inf(), l = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) {
-      tile_pages<D>(pg, pool, pid, t + 1, Hkv, g);
-      load_tile<D>(buf1, pg);
-    }
-    attn_tile<D, false>(buf0, s0 + t * kTile, qop, ctx - 1, ctx, cscale, m, l, o);
-    if (t + 1 < n_tiles) {
-      if (t + 2 < n_tiles) {
-        tile_pages<D>(pg, pool, pid, t + 2, Hkv, g);
-        load_tile<D>(buf0, pg);
+  for (int t0 = 0; t0 < n_tiles; t0 += 5) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int t = t0 + j;
+      if (t < n_tiles) {
+        const bool ahead = t + 2 < n_tiles;
+        if (ahead) {
+          tile_pages<D>(pg, pool, pid, t + 2, Hkv, g);
+          load_k<D>(ring[(2 * j + 4) % 5], pg);  // the slot of V(t-1), already consumed
+        }
+        bf16x8 pop[2];
+        float alpha, m_new, l_new;
+        attn_scores<D>(ring[(2 * j) % 5], s0 + t * kTile, qop, ctx - 1, cscale, m, l, pop, alpha, m_new,
+                       l_new);
+        if (ahead) load_v<D>(ring[(2 * j) % 5], pg);  // the slot of K(t), just consumed
+        attn_values<D, false>(ring[(2 * j + 1) % 5], s0 + t * kTile, ctx - 1, ctx, pop, alpha, m_new, l_new,
+                              m, l, o);
       }
-      attn_tile<D, false>(buf1, s0 + (t + 1) * kTile, qop, ctx - 1, ctx, cscale, m, l, o);
     }
   }
   if (bad) l = __builtin_nanf("");
@@ -349,7 +411,7 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(
   const int last_page = p_max / kPage;
   bool bad = false;
   const int n_splits = p_max / split_tokens + 1;
-  KVTile<D> tile;
+  Half<D> tk, tv;
   for (int si = 0; si < n_splits; ++si) {
     const int s0 = si * split_tokens;
     const int s1 = min(p_max + 1, s0 + split_tokens);
@@ -362,11 +424,12 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(
     for (int t0 = s0; t0 < s1; t0 += kTile) {
       const bf16_t *pg[4];
       tile_pages<D>(pg, pool, pid, (t0 - s0) / kTile, Hkv, g);
-      load_tile<D>(tile, pg);
+      load_k<D>(tk, pg);
+      load_v<D>(tv, pg);
       if (t0 <= p_min)
-        attn_tile<D, false>(tile, t0, qop, pos, p_max + 1, cscale, m, l, o);
+        attn_tile<D, false>(tk, tv, t0, qop, pos, p_max + 1, cscale, m, l, o);
       else
-        attn_tile<D, true>(tile, t0, qop, pos, p_max + 1, cscale, m, l, o);
+        attn_tile<D, true>(tk, tv, t0, qop, pos, p_max + 1, cscale, m, l, o);
     }
     if (s0 <= pos) {
       float os[D / 4];
@@ -415,16 +478,21 @@ hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st) {
-  const int n_split_grid = (a.ctx_bound + a.split_tokens - 1) / a.split_tokens;
-  dim3 grid(n_split_grid, a.Hkv, a.n_rows);
+  if (a.n_rows == 0) return hipSuccess;
+  const int n_sg = a.ctx_bound / a.split_tokens;  // full splits a row can have
+  const long slots = (long)(n_sg + a.split_tokens / kTile) * a.Hkv * a.n_rows;
+  if (slots > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)slots);
   if (a.D == 128)
     hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(64), 0, st, a.q, a.q_row_stride,
                        a.ctx_len, a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G,
-                       a.split_tokens, a.ctx_bound, a.cscale, a.part_o, a.part_ml, a.max_splits);
+                       a.split_tokens, a.ctx_bound, a.n_rows, n_sg, a.cscale, a.part_o, a.part_ml,
+                       a.max_splits);
   else
     hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(64), 0, st, a.q, a.q_row_stride,
                        a.ctx_len, a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G,
-                       a.split_tokens, a.ctx_bound, a.cscale, a.part_o, a.part_ml, a.max_splits);
+                       a.split_tokens, a.ctx_bound, a.n_rows, n_sg, a.cscale, a.part_o, a.part_ml,
+                       a.max_splits);
   return hipGetLastError();
 }
 

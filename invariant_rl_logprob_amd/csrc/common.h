@@ -54,10 +54,14 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ u32x4 ld16(const void *p) {
-  return *reinterpret_cast<const u32x4 *>(p);
-}
-__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// 16-byte loads and stores of global (device) memory; p must point into global memory,
+// never into LDS.  The explicit address space makes these global_load/global_store
+// instructions: a flat access would also count against the LDS/scalar counter, so every
+// wait for an LDS or scalar result would drain all loads in flight.
+typedef const u32x4 __attribute__((address_space(1))) *gptr_c16;
+typedef u32x4 __attribute__((address_space(1))) *gptr_16;
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *(gptr_c16)(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *(gptr_16)(p) = v; }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

@@ -115,7 +115,9 @@ __device__ __forceinline__ void kloop(f32x4 (&acc)[MB][NB], const bf16_t *const 
 // HBM channels instead of having every tile read the same K offset at the same time.
 // The activation operand is staged through LDS in chunks of 8 K steps (each of the four
 // waves loads two steps for the whole workgroup); weight operands run PF steps ahead in
-// a register ring.  All four waves must call this (it synchronises the workgroup).
+// a register ring.  wp[nb] points at the packed weight block of MFMA block nb (one
+// contiguous 1 KB operand per K step).  All four waves must call this (it synchronises
+// the workgroup).
 constexpr int kLdsSteps = 8;
 __device__ __forceinline__ int lm_rot(int tile, int nk) { return (37 * tile) % nk; }
 
@@ -135,7 +137,7 @@ __device__ __forceinline__ void kloop_lm(f32x4 (&acc)[MB][4], const bf16_t *cons
   for (int s = 0; s < PF; ++s) {
     if (s < nk) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) rb[s][nb] = ld16(wp[nb] + kidx(s) * 32);
+      for (int nb = 0; nb < 4; ++nb) rb[s][nb] = ld16(wp[nb] + kidx(s) * 512);
     }
   }
   for (int k0 = 0; k0 < nk; k0 += S) {
@@ -159,7 +161,7 @@ __device__ __forceinline__ void kloop_lm(f32x4 (&acc)[MB][4], const bf16_t *cons
         const int kp = ks + PF;
         if (kp < nk) {
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) rb[(j + PF) % S][nb] = ld16(wp[nb] + kidx(kp) * 32);
+          for (int nb = 0; nb < 4; ++nb) rb[(j + PF) % S][nb] = ld16(wp[nb] + kidx(kp) * 512);
         }
         const int buf = (ks / kLdsSteps) & 1, st = ks % kLdsSteps;
 #pragma unroll
@@ -227,6 +229,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t *__restrict__ A,
 // and the target's logit if the target falls in the tile.  M rows per workgroup
 // (16*MB) are free: they never touch a row's reduction tree.
 // ---------------------------------------------------------------------------
+// The weight W is in the packed layout written by pack_lm_head_kernel: per vocabulary
+// tile, per 16-column MFMA block, per 32-wide K step, the block's B operand in lane order
+// (1 KB), so every weight load of a wave is one contiguous 1 KB read.
+//   W(c, k) -> ((((c/256)*16 + (c%256)/16) * (K/32) + k/32) * 64 + ((k%32)/8)*16 + c%16) * 8 + k%8
+// Columns past V in the last tile are zero.
+__global__ __launch_bounds__(256) void pack_lm_head_kernel(const bf16_t *__restrict__ src, int V, int K,
+                                                           bf16_t *__restrict__ dst, long n_chunks) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_chunks) return;
+  const int nk = K / 32;
+  const int lane = (int)(i % 64);
+  const long blk_step = i / 64;  // (tile*16 + block) * nk + step
+  const int step = (int)(blk_step % nk);
+  const long blk = blk_step / nk;
+  const long c = blk * 16 + lane % 16;
+  const int k = step * 32 + (lane / 16) * 8;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (c < V) v = ld16(src + c * K + k);
+  st16(dst + i * 8, v);
+}
+
 template <int MB>
 __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__ Z, int ldz,
                                                       const bf16_t *__restrict__ W, int K, int V,
@@ -245,7 +268,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) ap[mb] = Z + (long)min(m0 + 16 * mb + r16, M - 1) * ldz + grp * 8;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) wp[nb] = W + (long)min(c0 + 16 * nb + r16, V - 1) * K + grp * 8;
+  for (int nb = 0; nb < 4; ++nb) wp[nb] = W + (long)(tile * 16 + wave * 4 + nb) * (K / 32) * 512 + lane * 8;
   f32x4 acc[MB][4];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -394,6 +417,20 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(lm_head_kernel<4>, grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
                        a.target, a.M, a.part, a.tgt_logit, n_vt);
   }
+  return hipGetLastError();
+}
+
+long lm_head_packed_elems(int V, int K) {
+  const long n_vt = (V + kVocabTile - 1) / kVocabTile;
+  return n_vt * kVocabTile * (long)K;
+}
+
+hipError_t launch_pack_lm_head(const bf16_t *src, int V, int K, bf16_t *dst, hipStream_t st) {
+  const long n_chunks = lm_head_packed_elems(V, K) / 8;
+  if (n_chunks == 0) return hipSuccess;
+  const long blocks = (n_chunks + 255) / 256;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_lm_head_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, V, K, dst, n_chunks);
   return hipGetLastError();
 }
 

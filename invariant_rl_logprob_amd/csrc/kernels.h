@@ -140,5 +140,7 @@ hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);
 hipError_t launch_vocab_merge(const LmHeadArgs &a, hipStream_t st);
+long lm_head_packed_elems(int V, int K);
+hipError_t launch_pack_lm_head(const bf16_t *src, int V, int K, bf16_t *dst, hipStream_t st);
 
 }  // namespace ril

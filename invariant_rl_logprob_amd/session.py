@@ -15,8 +15,9 @@ import torch
 
 from . import (RIL_ATTN_GQA, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch, make_prefill_batch,
                ril_decode_step_logprobs, ril_kv_alloc, ril_kv_assign, ril_kv_free, ril_kv_page_bytes,
-               ril_kv_release, ril_kv_write, ril_model_create, ril_model_desc, ril_model_destroy,
-               ril_prefill_logprobs, ril_workspace_bytes, ril_ws_attn_offset)
+               ril_kv_release, ril_kv_write, ril_lm_head_packed_bytes, ril_model_create, ril_model_desc,
+               ril_model_destroy, ril_pack_lm_head, ril_prefill_logprobs, ril_workspace_bytes,
+               ril_ws_attn_offset)
 
 PAGE = 16
 
@@ -42,12 +43,17 @@ class Session:
                  norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, index_heads=0, index_dim=0, topk=0,
                  device="cuda"):
         self.device = torch.device(device)
-        self._keep = [w_lm, embed, w_qkv, w_o, norm_attn, norm_final]
+        # the lm-head weight lives in the library's packed layout (w_lm stays row-major)
+        w_lm = w_lm.contiguous()
+        self.w_lm_packed = torch.empty(ril_lm_head_packed_bytes(vocab, d_head), dtype=torch.uint8,
+                                       device=self.device)
+        ril_pack_lm_head(w_lm, self.w_lm_packed)
+        self._keep = [embed, w_qkv, w_o, norm_attn, norm_final]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
                                    index_heads, index_dim, topk, d_head, vocab, PAGE, split_tokens, max_rows,
                                    max_tokens, max_ctx, softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o),
-                                   p(norm_attn), p(norm_final), p(w_lm))
+                                   p(norm_attn), p(norm_final), p(self.w_lm_packed))
         self.model = ril_model_create(self.desc)
         self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
         self.max_ctx = max_ctx

@@ -127,3 +127,27 @@ def test_calls_fail_validation_without_enqueueing():
         ril.ril_prefill_logprobs(m, kv, pb, out, ws, stream=0)
     ril.ril_kv_free(kv)
     ril.ril_model_destroy(m)
+
+
+def test_lm_head_packed_bytes_and_pack_validation():
+    # ceil(V/256) vocabulary tiles of 256 columns, K bf16 each
+    assert ril.ril_lm_head_packed_bytes(129280, 4096) == 505 * 256 * 4096 * 2
+    assert ril.ril_lm_head_packed_bytes(1000, 64) == 4 * 256 * 64 * 2
+    for v, k in ((0, 64), (1000, 48), (1000, 0), (-1, 64)):
+        assert ril.ril_lm_head_packed_bytes(v, k) == 0
+    lib = ctypes.CDLL(ril.LIB_PATH)
+    f = lib.ril_pack_lm_head
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    need = ril.ril_lm_head_packed_bytes(1000, 64)
+    src, dst = 0x100000, 0x800000
+    bad = [(None, 1000, 64, dst, need),            # null source
+           (src, 1000, 64, None, need),            # null destination
+           (src + 8, 1000, 64, dst, need),         # misaligned
+           (src, 1000, 64, dst, need - 1),         # short destination
+           (src, 1000, 48, dst, need),             # K not a multiple of 32
+           (src, 1000, 64, src + 1024, need)]      # overlap
+    for args in bad:
+        assert f(*args, None) == ril.RIL_EINVAL, args
+        assert ril.ril_last_error()
