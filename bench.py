@@ -114,6 +114,51 @@ def roofline_hbm(kernel, achieved_gbps, bytes_per_launch, avg_us):
             "avg_launch_us": round(avg_us, 2)}
 
 
+def comparator(sess, prepare, rows, ref_last, attn_bytes, splits, args):
+    """X1: the same kernels with shape-derived work splits (ril_set_policy
+    RIL_POLICY_SHAPE_DERIVED): the KV split from the batch (or each fixed override in
+    `splits`, so the comparator is tuned as hard as the invariant build) and split-K
+    for small projection grids.  Reports the best X1 step at the full batch, its diff
+    against the invariant result (nonzero: X1 decode no longer equals prefill), and
+    invariant vs X1 (shape rule) over batch sizes 1, 8 and all rows."""
+    import invariant_rl_logprob_amd as ril
+    from invariant_rl_logprob_amd.metrics import mismatch
+    steps, warmup = max(10, args.steps // 2), max(2, args.warmup)
+
+    def run(rs, policy, split=0):
+        sess.set_policy(policy, split)
+        launch, out = prepare(rs)
+        ms, kern = timed_steps(launch, steps, warmup)
+        attn_us = kern["attn_split"]["avg_us"] + kern["attn_merge"]["avg_us"]
+        return ms, attn_us, kern, out
+
+    try:
+        trials = []
+        for sp in [0] + list(splits):
+            ms, attn_us, kern, out = run(rows, ril.RIL_POLICY_SHAPE_DERIVED, sp)
+            t = {"attn_split": "shape rule" if sp == 0 else sp, "ms_per_step": round(ms, 4),
+                 "tokens_per_s": round(len(rows) / (ms * 1e-3), 1),
+                 "attn_hbm_gbps": round(attn_bytes / (attn_us * 1e-6) / 1e9, 1),
+                 "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()}}
+            if sp == 0:
+                t["diff_vs_invariant"] = mismatch(out[:, None], ref_last[:, None])
+            trials.append(t)
+        best = min(trials, key=lambda t: t["ms_per_step"])
+        sweep = []
+        for b in sorted({1, 8, len(rows)}):
+            rs = rows[:b]
+            inv_ms = run(rs, ril.RIL_POLICY_INVARIANT)[0]
+            x1_ms = run(rs, ril.RIL_POLICY_SHAPE_DERIVED)[0]
+            sweep.append({"rows": b, "invariant_tokens_per_s": round(b / (inv_ms * 1e-3), 1),
+                          "x1_tokens_per_s": round(b / (x1_ms * 1e-3), 1),
+                          "invariant_over_x1": round(x1_ms / inv_ms, 4)})
+    finally:
+        sess.set_policy(ril.RIL_POLICY_INVARIANT)
+    log(f"comparator: best {best['attn_split']} {best['tokens_per_s']} tok/s; sweep {sweep}")
+    return {"kind": "same kernels, shape-derived split-KV and split-K (non-invariant)",
+            "best": best, "trials": trials, "batch_sweep": sweep}
+
+
 # ---------------------------------------------------------------------------
 # GQA decode, 64 rows
 # ---------------------------------------------------------------------------
@@ -152,6 +197,14 @@ def bench_gqa(args):
     else:
         roof = roofline_hbm("lm_head", lm_gbps, lm_bytes, lm_us)
 
+    x1 = None
+    if not args.no_comparator:
+        def prepare(rs):
+            q_, k_, v_, t_, c_ = case.step_inputs(rs, 1)
+            return case.sess.prepare_decode([("d", r) for r in rs], c_, targets=t_, q=q_, k=k_, v=v_)
+        x1 = comparator(case.sess, prepare, rows, dec[:, -1], kv_bytes + q_bytes + out_bytes, (256, 512, 1024), args)
+        x1["invariant_over_x1_best"] = round(x1["best"]["ms_per_step"] / ms_step, 4)
+
     cpu = None
     if not args.no_cpu and args.cpu_rows > 0:
         import oracle  # the cpu_baseline leg: the fp64 oracle as it stands
@@ -178,7 +231,7 @@ def bench_gqa(args):
         "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "lm_head_gbps": round(lm_gbps, 1), "diff": diff, "timed_step_equals_checked_decode": last_equal,
         "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
-        "roofline": roof, "cpu_baseline": cpu,
+        "comparator_x1": x1, "roofline": roof, "cpu_baseline": cpu,
     }
 
 
@@ -335,6 +388,7 @@ def main():
     ap.add_argument("--workload", default="gqa_decode_b64", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=12, help="rows of the oracle timing sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-comparator", action="store_true", help="skip the shape-derived comparator leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")
     args = ap.parse_args()

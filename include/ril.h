@@ -133,6 +133,24 @@ size_t ril_workspace_bytes(const ril_model *m);
 /* Bytes of one KV page: Hkv x 2 (K, V) x page_tokens x D x 2 bytes. */
 size_t ril_kv_page_bytes(const ril_model *m);
 
+/* Comparator, for benchmarking only.  RIL_POLICY_INVARIANT (the default) is the
+ * method: every reduction order is fixed by the model alone.  RIL_POLICY_SHAPE_DERIVED
+ * makes the same kernels choose their work split from the call's shape, as a
+ * throughput-first engine would, so that the price of invariance can be measured:
+ *   - decode attention's KV split (tokens): attn_split_tokens if non-zero (a multiple
+ *     of 64, at most 1024 for GQA and 2048 for MLA), else enough splits for two waves
+ *     per SIMD of the device, ceil(max_ctx_bound / splits) rounded up to 64, widened
+ *     until the partials fit the invariant workspace;
+ *   - projection GEMMs whose tile grid is smaller than the device's compute-unit count
+ *     split their K loop (at most 16 chunks of at least 256) and add the fp32 chunk
+ *     results in a second kernel.
+ * Under it, results depend on the batch and decode no longer equals prefill.  Setting
+ * it queries the current device's compute-unit count and enlarges
+ * ril_workspace_bytes(m) by the split-K partial buffer.  Returns RIL_EINVAL for an
+ * unknown policy or a bad override, RIL_EHIP if the device cannot be queried. */
+enum { RIL_POLICY_INVARIANT = 0, RIL_POLICY_SHAPE_DERIVED = 1 };
+ril_status ril_set_policy(ril_model *m, int32_t policy, int32_t attn_split_tokens);
+
 /* S11 weight layout.  The lm-head reads its weight in a packed form: per vocabulary
  * tile of 256 columns, per 16-column MFMA block, per 32-wide K step, that block's
  * MFMA operand in lane order, so each weight load of a wavefront is one contiguous

@@ -26,6 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 RIL_OK, RIL_EINVAL, RIL_ERANGE, RIL_ENOSPC, RIL_EUNSUPPORTED, RIL_EHIP = 0, -1, -2, -3, -4, -5
 RIL_ATTN_GQA, RIL_ATTN_MLA, RIL_ATTN_MLA_SPARSE = 0, 1, 2
 RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
+RIL_POLICY_INVARIANT, RIL_POLICY_SHAPE_DERIVED = 0, 1
 
 _c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -86,6 +87,7 @@ _decode = _sig("ril_decode_step_logprobs", _c_int,
                [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp, ctypes.c_size_t, _vp])
 _kv_write = _sig("ril_kv_write", _c_int, [_vp, _vp, ctypes.POINTER(ril_prefill_batch), _vp])
 _last_error = _sig("ril_last_error", ctypes.c_char_p, [])
+_set_policy = _sig("ril_set_policy", _c_int, [_vp, _c_int, _c_int])
 _trace_enable = _sig("ril_trace_enable", _c_int, [_c_int])
 _trace_read = _sig("ril_trace_read", _c_int, [_c_int, ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(ctypes.c_int64)])
@@ -94,7 +96,7 @@ EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril
             "ril_lm_head_packed_bytes", "ril_pack_lm_head",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
-            "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_trace_enable",
+            "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_set_policy", "ril_trace_enable",
             "ril_trace_read")
 
 # kernel ids of the trace hook
@@ -231,6 +233,12 @@ def ril_decode_step_logprobs(model: int, kv: int, batch: ril_decode_batch, logpr
 
 def ril_kv_write(model: int, kv: int, batch: ril_prefill_batch, stream=None) -> None:
     _check(_kv_write(model, kv, ctypes.byref(batch), _stream(stream)), "ril_kv_write")
+
+
+def ril_set_policy(model: int, policy: int, attn_split_tokens: int = 0) -> None:
+    """Comparator switch (benchmarking only): RIL_POLICY_SHAPE_DERIVED lets the kernels
+    choose their splits from the call's shape; RIL_POLICY_INVARIANT restores the method."""
+    _check(_set_policy(model, policy, attn_split_tokens), "ril_set_policy")
 
 
 def ril_trace_enable(on: bool) -> None:

@@ -28,7 +28,13 @@ struct ril_model {
   // workspace segment offsets (bytes) and total
   size_t off_x, off_h, off_qkv, off_attn, off_y, off_z, off_vpart, off_tgt, off_po, off_pml;
   size_t off_scores, off_sel;  // sparse: indexer scores [max_rows, max_ctx], selections [max_rows, topk]
-  size_t ws_total;
+  size_t ws_base;   // end of the invariant path's segments
+  size_t ws_total;  // ws_base + the comparator's split-K partials when that policy is on
+  // comparator (benchmarking only): RIL_POLICY_SHAPE_DERIVED picks splits from the batch
+  int policy = RIL_POLICY_INVARIANT;
+  int attn_split_override = 0;
+  int n_cu = 0;
+  size_t off_gpart = 0;
 };
 
 struct ril_kv {
@@ -145,12 +151,82 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->off_pml = seg((size_t)d.max_rows * d.n_q_heads * m->max_splits * 2 * sizeof(float));
   m->off_scores = seg(sparse ? (size_t)d.max_rows * d.max_ctx * sizeof(float) : 0);
   m->off_sel = seg(sparse ? (size_t)d.max_rows * d.topk * sizeof(int32_t) : 0);
-  m->ws_total = o;
+  m->ws_base = m->ws_total = o;
   *out = m;
   return RIL_OK;
 }
 
 extern "C" void ril_model_destroy(ril_model *m) { delete m; }
+
+static bf16_t *wsb(void *ws, size_t off) { return reinterpret_cast<bf16_t *>(static_cast<char *>(ws) + off); }
+static float *wsf(void *ws, size_t off) { return reinterpret_cast<float *>(static_cast<char *>(ws) + off); }
+
+// Comparator: the widest projection output, for the split-K partial buffer.
+static int widest_gemm_n(const ril_model_desc &d) {
+  int n = d.w_o ? d.d_head : 0;
+  if (d.input_mode == RIL_INPUT_TOKENS) n = std::max(n, (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim);
+  return n;
+}
+static constexpr int kMaxSplitK = 16;
+
+extern "C" ril_status ril_set_policy(ril_model *m, int32_t policy, int32_t attn_split_tokens) {
+  if (!m) return fail(RIL_EINVAL, "set_policy: null model");
+  if (policy != RIL_POLICY_INVARIANT && policy != RIL_POLICY_SHAPE_DERIVED)
+    return fail(RIL_EINVAL, "set_policy: policy %d", policy);
+  const int max_split = m->mla ? 2048 : 1024;
+  if (attn_split_tokens != 0 && (attn_split_tokens % 64 || attn_split_tokens < 64 || attn_split_tokens > max_split))
+    return fail(RIL_EINVAL, "set_policy: attn_split_tokens %d (0, or a multiple of 64 in [64, %d])",
+                attn_split_tokens, max_split);
+  if (policy == RIL_POLICY_SHAPE_DERIVED && m->n_cu == 0) {
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1)
+      return fail(RIL_EHIP, "set_policy: cannot read the device's compute-unit count");
+    m->n_cu = cu;
+  }
+  m->policy = policy;
+  m->attn_split_override = attn_split_tokens;
+  m->ws_total = m->ws_base;
+  m->off_gpart = 0;
+  if (policy == RIL_POLICY_SHAPE_DERIVED) {
+    const size_t R = (size_t)std::max(m->d.max_rows, m->d.max_tokens);
+    m->off_gpart = m->ws_base;
+    m->ws_total = m->ws_base + round256((size_t)kMaxSplitK * R * widest_gemm_n(m->d) * sizeof(float));
+  }
+  return RIL_OK;
+}
+
+// Comparator: the KV split a throughput-first engine would choose for this batch (two
+// waves per SIMD of work items), or the caller's override; widened until the partials
+// fit the invariant path's buffer.  `bound` is the longest context (or selection).
+static int shape_split(const ril_model *m, int rows, int bound) {
+  const ril_model_desc &d = m->d;
+  const int max_split = m->mla ? 2048 : 1024;
+  int split = m->attn_split_override;
+  if (split == 0) {
+    const long want = 2L * 4 * m->n_cu;
+    const long items = (long)rows * (m->mla ? d.n_q_heads / 64 : d.n_kv_heads);
+    const long per = std::max(1L, (want + items - 1) / items);
+    split = (int)(((bound + per - 1) / per + 63) / 64 * 64);
+  }
+  split = std::min(std::max(split, 64), max_split);
+  const long cap = (long)d.max_rows * m->max_splits;
+  while ((long)rows * ((bound + split - 1) / split) > cap && split < max_split) split = std::min(2 * split, max_split);
+  return split;
+}
+
+// Comparator split-K for a projection of M x N: chunks when the tile grid is smaller
+// than the machine, at least 256 K per chunk.
+static void shape_split_k(const ril_model *m, GemmArgs &g, void *ws) {
+  if (m->policy != RIL_POLICY_SHAPE_DERIVED) return;
+  const int tiles = gemm_tiles(g.M, g.N);
+  if (tiles >= m->n_cu) return;
+  int sk = std::min(kMaxSplitK, (2 * m->n_cu + tiles - 1) / tiles);
+  sk = std::min(sk, g.K / 256);
+  if (sk < 2) return;
+  g.split_k = sk;
+  g.part = wsf(ws, m->off_gpart);
+}
 extern "C" size_t ril_workspace_bytes(const ril_model *m) { return m ? m->ws_total : 0; }
 extern "C" size_t ril_kv_page_bytes(const ril_model *m) { return m ? m->page_bytes : 0; }
 
@@ -251,8 +327,6 @@ extern "C" void ril_kv_free(ril_kv *kv) { delete kv; }
 // forward passes
 // ---------------------------------------------------------------------------
 
-static bf16_t *wsb(void *ws, size_t off) { return reinterpret_cast<bf16_t *>(static_cast<char *>(ws) + off); }
-static float *wsf(void *ws, size_t off) { return reinterpret_cast<float *>(static_cast<char *>(ws) + off); }
 
 // ---------------------------------------------------------------------------
 // kernel trace: hipEvent pairs recorded around launches while enabled
@@ -366,6 +440,7 @@ static ril_status run_head(const ril_model *m, int rows, const int32_t *targets,
     const bool tok = d.input_mode == RIL_INPUT_TOKENS;
     GemmArgs g{src, qw, (const bf16_t *)d.w_o, qw, wsb(ws, m->off_y), d.d_head,
                tok ? wsb(ws, m->off_x) : nullptr, d.d_model, rows, d.d_head, qw};
+    shape_split_k(m, g, ws);
     RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
     src = wsb(ws, m->off_y);
     ld = d.d_head;
@@ -389,6 +464,7 @@ static ril_status run_token_front(const ril_model *m, int rows, const int32_t *t
   RIL_LAUNCH(RIL_K_RMSNORM, launch_rmsnorm(r, st));
   GemmArgs g{wsb(ws, m->off_h), d.d_model, (const bf16_t *)d.w_qkv, d.d_model, wsb(ws, m->off_qkv), wqkv,
              nullptr, 0, rows, wqkv, d.d_model};
+  shape_split_k(m, g, ws);
   RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
   return RIL_OK;
 }
@@ -455,9 +531,15 @@ static ril_status run_mla(const ril_model *m, ril_kv *kv, const bf16_t *q, const
       RIL_LAUNCH(RIL_K_INDEXER, launch_indexer(ia, st));
       RIL_LAUNCH(RIL_K_TOPK, launch_topk(ia, st));
     }
+    int split = d.split_tokens, max_splits = m->max_splits;
+    if (m->policy == RIL_POLICY_SHAPE_DERIVED && mode == 0) {
+      const int bound = m->sparse ? std::min(ctx_bound, d.topk) : ctx_bound;
+      split = shape_split(m, n, bound);
+      max_splits = (bound + split - 1) / split;
+    }
     MlaAttnArgs a{q, mode, r0, n, ctx_len, cu, start_pos, n_seqs, page_table, page_stride,
-                  (const bf16_t *)kv->pool, page_elems, kv->n_pages, d.n_q_heads, d.split_tokens, ctx_bound,
-                  m->max_splits, sel, d.topk, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml),
+                  (const bf16_t *)kv->pool, page_elems, kv->n_pages, d.n_q_heads, split, ctx_bound,
+                  max_splits, sel, d.topk, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml),
                   wsb(ws, m->off_attn)};
     RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_mla_split(a, st));
     RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_mla_merge(a, st));
@@ -579,9 +661,14 @@ extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, c
   KvWriteArgs kw{k, v, kv_stride, R, 1, nullptr, nullptr, 0, b->ctx_len, b->page_table, b->page_stride,
                  (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
   RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(kw, st));
+  int split = d.split_tokens, max_splits = m->max_splits;
+  if (m->policy == RIL_POLICY_SHAPE_DERIVED) {
+    split = shape_split(m, R, b->max_ctx_bound);
+    max_splits = (b->max_ctx_bound + split - 1) / split;
+  }
   AttnDecodeArgs ad{q, q_stride, b->ctx_len, b->page_table, b->page_stride, (const bf16_t *)kv->pool,
-                    kv->n_pages, d.n_kv_heads, m->G, d.head_dim, d.split_tokens, b->max_ctx_bound, R,
-                    m->max_splits, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn)};
+                    kv->n_pages, d.n_kv_heads, m->G, d.head_dim, split, b->max_ctx_bound, R,
+                    max_splits, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn)};
   RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_attn_split(ad, st));
   RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_attn_merge(ad, st));
   return run_head(m, R, b->target_ids, logprob_out, ws, st);

@@ -179,29 +179,34 @@ __device__ __forceinline__ void kloop_lm(f32x4 (&acc)[MB][4], const bf16_t *cons
 // S4: C[M,N] = bf16(A[M,K] W[N,K]^T) or bf16(R + bf16(A W^T)).
 // Workgroup = 4 waves side by side along N; a wave owns MB x NB 16x16 blocks.
 // ---------------------------------------------------------------------------
+// The invariant path always runs with gridDim.z == 1 and part == nullptr: one sequential
+// K loop per output element.  gridDim.z > 1 (K chunk kchunk, fp32 partials to `part`,
+// reduced by gemm_reduce_kernel) is the shape-derived comparator's split-K only.
 template <int MB, int NB>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t *__restrict__ A, int lda,
                                                    const bf16_t *__restrict__ W, int ldw,
                                                    bf16_t *__restrict__ C, int ldc,
                                                    const bf16_t *__restrict__ R, int ldr, int M,
-                                                   int N, int K) {
+                                                   int N, int K, int kchunk, float *__restrict__ part) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
   const int m0 = blockIdx.y * 16 * MB;
   const int n0 = (blockIdx.x * 4 + wave) * 16 * NB;
   if (n0 >= N) return;
+  const int k0 = blockIdx.z * kchunk;
+  const int klen = min(kchunk, K - k0);
   const bf16_t *ap[MB];
   const bf16_t *wp[NB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) ap[mb] = A + (long)min(m0 + 16 * mb + r16, M - 1) * lda + grp * 8;
+  for (int mb = 0; mb < MB; ++mb) ap[mb] = A + (long)min(m0 + 16 * mb + r16, M - 1) * lda + k0 + grp * 8;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wp[nb] = W + (long)min(n0 + 16 * nb + r16, N - 1) * ldw + grp * 8;
+  for (int nb = 0; nb < NB; ++nb) wp[nb] = W + (long)min(n0 + 16 * nb + r16, N - 1) * ldw + k0 + grp * 8;
   f32x4 acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  kloop<MB, NB, 3>(acc, ap, wp, K);
+  kloop<MB, NB, 3>(acc, ap, wp, klen);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -211,13 +216,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t *__restrict__ A,
       for (int i = 0; i < 4; ++i) {
         const int row = m0 + 16 * mb + 4 * grp + i;
         if (row < M && col < N) {
-          float v = bf2f(f2bf(acc[mb][nb][i]));
-          if (R) v = bf2f(R[(long)row * ldr + col]) + v;
-          C[(long)row * ldc + col] = f2bf(v);
+          if (part) {
+            part[((long)blockIdx.z * M + row) * N + col] = acc[mb][nb][i];
+          } else {
+            float v = bf2f(f2bf(acc[mb][nb][i]));
+            if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+            C[(long)row * ldc + col] = f2bf(v);
+          }
         }
       }
     }
   }
+}
+
+// Comparator split-K: C = bf16(sum_z part[z]) (+ residual as in gemm_kernel).
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ part, int nz, int M, int N,
+                                                          bf16_t *__restrict__ C, int ldc,
+                                                          const bf16_t *__restrict__ R, int ldr) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)M * N) return;
+  const int row = (int)(i / N), col = (int)(i % N);
+  float s = part[i];
+  for (int z = 1; z < nz; ++z) s += part[(long)z * M * N + i];
+  float v = bf2f(f2bf(s));
+  if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+  C[(long)row * ldc + col] = f2bf(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -387,20 +410,39 @@ hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+int gemm_tiles(int M, int N) {
+  if (M <= 16) return ((N + 63) / 64) * ((M + 15) / 16);
+  if (M <= 64) return ((N + 63) / 64) * ((M + 63) / 64);
+  return ((N + 127) / 128) * ((M + 63) / 64);
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  int kchunk = a.K, nz = 1;
+  float *part = nullptr;
+  if (a.split_k > 1 && a.part) {
+    kchunk = ((a.K + a.split_k - 1) / a.split_k + 31) / 32 * 32;
+    nz = (a.K + kchunk - 1) / kchunk;
+    if (nz > 1) part = a.part;
+    else kchunk = a.K;
+  }
   if (a.M <= 16) {
-    dim3 grid((a.N + 63) / 64, (a.M + 15) / 16);
+    dim3 grid((a.N + 63) / 64, (a.M + 15) / 16, nz);
     hipLaunchKernelGGL((gemm_kernel<1, 1>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C,
-                       a.ldc, a.R, a.ldr, a.M, a.N, a.K);
+                       a.ldc, a.R, a.ldr, a.M, a.N, a.K, kchunk, part);
   } else if (a.M <= 64) {
-    dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+    dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, nz);
     hipLaunchKernelGGL((gemm_kernel<4, 1>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C,
-                       a.ldc, a.R, a.ldr, a.M, a.N, a.K);
+                       a.ldc, a.R, a.ldr, a.M, a.N, a.K, kchunk, part);
   } else {
-    dim3 grid((a.N + 127) / 128, (a.M + 63) / 64);
+    dim3 grid((a.N + 127) / 128, (a.M + 63) / 64, nz);
     hipLaunchKernelGGL((gemm_kernel<4, 2>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C,
-                       a.ldc, a.R, a.ldr, a.M, a.N, a.K);
+                       a.ldc, a.R, a.ldr, a.M, a.N, a.K, kchunk, part);
+  }
+  if (part) {
+    const long n = (long)a.M * a.N;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, nz, a.M,
+                       a.N, a.C, a.ldc, a.R, a.ldr);
   }
   return hipGetLastError();
 }

@@ -69,6 +69,10 @@ struct GemmArgs {
   int ldc;
   const bf16_t *R;
   int ldr, M, N, K;
+  // comparator only: K split into split_k chunks with fp32 partials in `part`
+  // ([split_k, M, N]); 1 / nullptr on the invariant path
+  int split_k = 1;
+  float *part = nullptr;
 };
 
 struct LmHeadArgs {
@@ -138,6 +142,7 @@ hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st);
 hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
+int gemm_tiles(int M, int N);
 hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);
 hipError_t launch_vocab_merge(const LmHeadArgs &a, hipStream_t st);
 long lm_head_packed_elems(int V, int K);

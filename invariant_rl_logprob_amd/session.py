@@ -16,8 +16,8 @@ import torch
 from . import (RIL_ATTN_GQA, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch, make_prefill_batch,
                ril_decode_step_logprobs, ril_kv_alloc, ril_kv_assign, ril_kv_free, ril_kv_page_bytes,
                ril_kv_release, ril_kv_write, ril_lm_head_packed_bytes, ril_model_create, ril_model_desc,
-               ril_model_destroy, ril_pack_lm_head, ril_prefill_logprobs, ril_workspace_bytes,
-               ril_ws_attn_offset)
+               ril_model_destroy, ril_pack_lm_head, ril_prefill_logprobs, ril_set_policy,
+               ril_workspace_bytes, ril_ws_attn_offset)
 
 PAGE = 16
 
@@ -62,6 +62,14 @@ class Session:
         self.pool = torch.empty(pool_pages * self.page_bytes, dtype=torch.uint8, device=self.device)
         self.kv = ril_kv_alloc(self.model, self.pool, shuffle_seed)
         self.pages: Dict[object, List[int]] = {}
+
+    def set_policy(self, policy: int, attn_split_tokens: int = 0) -> None:
+        """Switch the comparator policy (benchmarking only) and grow the workspace if
+        the policy needs more."""
+        ril_set_policy(self.model, policy, attn_split_tokens)
+        need = ril_workspace_bytes(self.model)
+        if need > self.ws.numel():
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
 
     def close(self):
         if getattr(self, "kv", None):
