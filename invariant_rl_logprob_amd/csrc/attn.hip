@@ -91,8 +91,18 @@ struct Half {
   u32x4 r[D / 8];
 };
 
+// Operand loads from global memory or from an LDS copy of the same page blocks.
+struct FromGlobal {
+  static __device__ __forceinline__ u32x4 ld(const bf16_t *p) { return ld16(p); }
+};
+struct FromLds {
+  static __device__ __forceinline__ u32x4 ld(const bf16_t *p) {
+    return *(const __attribute__((address_space(3))) u32x4 *)(p);
+  }
+};
+
 // pg[k]: K block of the tile's k-th page (its V block follows at +16*D).
-template <int D>
+template <int D, typename Mem = FromGlobal>
 __device__ __forceinline__ void load_k(Half<D> &t, const bf16_t *const (&pg)[4]) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
@@ -103,12 +113,12 @@ __device__ __forceinline__ void load_k(Half<D> &t, const bf16_t *const (&pg)[4])
     for (int h = 0; h < 2; ++h) {
       const bf16_t *kb = pg[2 * kc + (rq >> 1)] + grp * 128 + h * 64 + (rq & 1) * 32 + ri * 8;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) t.r[(2 * kc + h) * (D / 32) + c] = ld16(kb + c * 512);
+      for (int c = 0; c < D / 32; ++c) t.r[(2 * kc + h) * (D / 32) + c] = Mem::ld(kb + c * 512);
     }
   }
 }
 
-template <int D>
+template <int D, typename Mem = FromGlobal>
 __device__ __forceinline__ void load_v(Half<D> &t, const bf16_t *const (&pg)[4]) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
@@ -116,7 +126,7 @@ __device__ __forceinline__ void load_v(Half<D> &t, const bf16_t *const (&pg)[4])
   for (int kc = 0; kc < 2; ++kc) {
     const bf16_t *vb = pg[2 * kc + (grp >> 1)] + 16 * D + (grp & 1) * (8 * D) + r16 * 8;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) t.r[kc * (D / 16) + db] = ld16(vb + db * 128);
+    for (int db = 0; db < D / 16; ++db) t.r[kc * (D / 16) + db] = Mem::ld(vb + db * 128);
   }
 }
 
@@ -198,18 +208,6 @@ __device__ __forceinline__ void load_qop(bf16x8 (&qop)[D / 32], const bf16_t *qr
     if (!ok) v = u32x4{0u, 0u, 0u, 0u};
     qop[c] = as_bf16x8(v);
   }
-}
-
-// Page ids of one split, one per lane: lane i holds the id of page index
-// min(first + i, last) of the sequence (the clamp keeps reads in bounds; tokens beyond
-// the context are masked).  Returns whether any id in range lies outside the pool.
-__device__ __forceinline__ bool split_pages(const int32_t *pt, int first, int last, int n_pages,
-                                            int &pid) {
-  const int lane = threadIdx.x & 63;
-  int p = pt[min(first + lane, last)];
-  const bool bad = (unsigned)p >= (unsigned)n_pages;
-  pid = bad ? 0 : p;
-  return __any(bad);
 }
 
 // K block base of page slot `idx` of the split (0 .. 4*tiles-1): a wave-uniform readlane.
@@ -346,24 +344,50 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// S10: prefill attention.  grid (block bound, Hkv), one wave per 16 query columns
-// (16/G tokens x G heads of one sequence).  Splits and tiles run in order; the split
-// state and the merged state both stay in registers.
+// S10: prefill attention.  grid (workgroup bound, Hkv); a workgroup of 4 waves covers
+// QT = 4*NCB*(16/G) consecutive query tokens of one sequence for one kv head, wave w
+// owning NCB column blocks of 16 columns (16/G tokens x G heads).  The workgroup walks
+// the 64-token KV tiles of its context in order; each tile is copied once into LDS
+// (double-buffered, one page per wave, direct-to-LDS loads) and read by every wave.
+// Per column the arithmetic is the decode chain exactly: the same attn_scores /
+// attn_values per tile, a fresh state per split, merge_state at each split's end, with
+// per-column predication (MAYBE_INACTIVE) for tiles and splits past the column's
+// position.  Split and merged states stay in registers.
 // ---------------------------------------------------------------------------
+// LDS slot of one page block (K then V, 16*D bf16 each), padded by 128 bytes so the two
+// pages one K-operand load touches fall on different banks.
 template <int D>
-__global__ __launch_bounds__(64) void attn_prefill_kernel(
+constexpr int lds_page() { return 32 * D + 64; }
+
+// Page ids [64c, 64c+64) of a sequence, one per lane; ids past `last` read as page 0
+// (their tokens are masked), ids outside the pool set `bad`.
+__device__ __forceinline__ int page_chunk(const int32_t *pt, int c, int last, int n_pages, bool &bad) {
+  const int idx = 64 * c + (threadIdx.x & 63);
+  const bool in = idx <= last;
+  const int p = pt[min(idx, last)];
+  const bool b = in && (unsigned)p >= (unsigned)n_pages;
+  bad |= b;
+  return (in && !b) ? p : 0;
+}
+
+template <int D, int NCB>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(
     const bf16_t *__restrict__ q, int q_row_stride, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ start_pos, int n_seqs, const int32_t *__restrict__ page_table,
     int page_stride, const bf16_t *__restrict__ pool, int n_pages, int Hkv, int G,
     int split_tokens, int ctx_bound, float cscale, bf16_t *__restrict__ out) {
+  constexpr int kSlot = lds_page<D>();
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2][4 * kSlot];
   const int g = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tpb = 16 / G;
-  // Block -> (sequence, first token): wave-wide prefix sum of per-sequence block counts.
+  const int QT = 4 * NCB * tpb;
+  // Block -> (sequence, first token): wave-wide prefix sum of per-sequence block counts
+  // (every wave computes the same answer).
   int remaining = blockIdx.x, seq = -1, tok0 = 0;
   for (int base = 0; base < n_seqs; base += 64) {
     const int i = base + lane;
-    const int nb = (i < n_seqs) ? (cu[i + 1] - cu[i] + tpb - 1) / tpb : 0;
+    const int nb = (i < n_seqs) ? (cu[i + 1] - cu[i] + QT - 1) / QT : 0;
     int incl = nb;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -376,84 +400,154 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(
       const int first = __ffsll((long long)mask) - 1;
       const int excl = __shfl(incl - nb, first, 64);
       seq = base + first;
-      tok0 = (remaining - excl) * tpb;
+      tok0 = (remaining - excl) * QT;
       break;
     }
     remaining -= total;
   }
-  if (seq < 0) return;
+  if (seq < 0) return;  // the same for the whole workgroup
   const int Hq = Hkv * G;
   const int n_tok = cu[seq + 1] - cu[seq];
   const int sp = start_pos[seq];
   const int n = lane & 15, grp = lane >> 4;
-  const int tl = n / G, hh = n % G;
-  const bool col_ok = tok0 + tl < n_tok;
-  const long j = cu[seq] + tok0 + (col_ok ? tl : 0);
-  const int pos = col_ok ? sp + tok0 + tl : -1;
-  const int tok_hi = min(tok0 + tpb, n_tok);
-  const int p_max = sp + tok_hi - 1, p_min = sp + tok0;
-  bf16_t *op = out + (j * Hq + g * G + hh) * D + grp * 4;
+  const int hh = n % G;
+  const int wtok0 = tok0 + wave * NCB * tpb;  // first token of this wave
+  int pos[NCB];
+  long jrow[NCB];
+  bool col_ok[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int tok = wtok0 + cb * tpb + n / G;
+    col_ok[cb] = tok < n_tok;
+    jrow[cb] = cu[seq] + (col_ok[cb] ? tok : 0);
+    pos[cb] = col_ok[cb] ? sp + tok : -1;
+  }
+  const int p_max = sp + min(tok0 + QT, n_tok) - 1;  // the workgroup's last position
   if (sp < 0 || p_max + 1 > ctx_bound || (p_max / kPage) >= page_stride) {
-    if (col_ok) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      if (!col_ok[cb]) continue;
+      bf16_t *op = out + (jrow[cb] * Hq + g * G + hh) * D + grp * 4;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
         for (int i = 0; i < 4; ++i) op[db * 16 + i] = (bf16_t)0x7fc0u;
     }
     return;
   }
-  bf16x8 qop[D / 32];
-  load_qop<D>(qop, q + j * q_row_stride + (g * G + hh) * D, col_ok);
-  float M = neg_inf(), L = 0.f;
-  float O[D / 4];
+  const int w_min = sp + wtok0;                                   // this wave's first position
+  const int w_max = sp + min(wtok0 + NCB * tpb, n_tok) - 1;       // and last (< w_min if none)
+  bf16x8 qop[NCB][D / 32];
 #pragma unroll
-  for (int e = 0; e < D / 4; ++e) O[e] = 0.f;
+  for (int cb = 0; cb < NCB; ++cb) load_qop<D>(qop[cb], q + jrow[cb] * q_row_stride + (g * G + hh) * D, col_ok[cb]);
+
   const int32_t *pt = page_table + (long)seq * page_stride;
   const int last_page = p_max / kPage;
+  const int n_tiles = p_max / kTile + 1;
   bool bad = false;
-  const int n_splits = p_max / split_tokens + 1;
-  Half<D> tk, tv;
-  for (int si = 0; si < n_splits; ++si) {
-    const int s0 = si * split_tokens;
-    const int s1 = min(p_max + 1, s0 + split_tokens);
-    int pid;
-    bad |= split_pages(pt, s0 / kPage, last_page, n_pages, pid);
-    float m = neg_inf(), l = 0.f;
-    f32x4 o[D / 16];
+  int pid_c = page_chunk(pt, 0, last_page, n_pages, bad);
+  int pid_n = (n_tiles > 16) ? page_chunk(pt, 1, last_page, n_pages, bad) : 0;
+  float M[NCB], L[NCB], m[NCB], l[NCB];
+  float O[NCB][D / 4];
+  f32x4 o[NCB][D / 16];
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int t0 = s0; t0 < s1; t0 += kTile) {
-      const bf16_t *pg[4];
-      tile_pages<D>(pg, pool, pid, (t0 - s0) / kTile, Hkv, g);
-      load_k<D>(tk, pg);
-      load_v<D>(tv, pg);
-      if (t0 <= p_min)
-        attn_tile<D, false>(tk, tv, t0, qop, pos, p_max + 1, cscale, m, l, o);
-      else
-        attn_tile<D, true>(tk, tv, t0, qop, pos, p_max + 1, cscale, m, l, o);
+  for (int cb = 0; cb < NCB; ++cb) {
+    M[cb] = neg_inf();
+    L[cb] = 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) O[cb][e] = 0.f;
+  }
+  // wave w copies page 4T+w of tile T into slot w of buffer T&1 (direct-to-LDS loads,
+  // lane i -> 16 bytes at dst + 8i); its id comes from the chunk register holding it
+  auto copy_page = [&](int T, int pid_lo, int pid_hi, int chunk_lo) {
+    const int P = 4 * T + wave;
+    if (P > last_page) return;
+    const int c = P / 64;
+    const int pid = (c == chunk_lo) ? __builtin_amdgcn_readlane(pid_lo, P % 64)
+                                    : __builtin_amdgcn_readlane(pid_hi, P % 64);
+    const bf16_t *src = pool + ((long)pid * Hkv + g) * (32 * D) + lane * 8;
+    bf16_t *dst = &lds[T & 1][wave * kSlot];
+#pragma unroll
+    for (int j = 0; j < 32 * D / 512; ++j) __builtin_amdgcn_global_load_lds(src + j * 512, dst + j * 512, 16, 0, 0);
+  };
+  copy_page(0, pid_c, pid_n, 0);
+  for (int T = 0; T < n_tiles; ++T) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // tile T is in LDS; every wave is done with tile T-1's buffer
+    if (T % 16 == 0 && T > 0) {
+      pid_c = pid_n;
+      if (16 * (T / 16 + 1) < n_tiles) pid_n = page_chunk(pt, T / 16 + 1, last_page, n_pages, bad);
     }
-    if (s0 <= pos) {
-      float os[D / 4];
+    if (T + 1 < n_tiles) copy_page(T + 1, pid_c, pid_n, T / 16);
+    const int t0 = T * kTile;
+    const int s0 = t0 - t0 % split_tokens;
+    if (t0 == s0) {
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
+      for (int cb = 0; cb < NCB; ++cb) {
+        m[cb] = neg_inf();
+        l[cb] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) os[db * 4 + i] = o[db][i];
-      if (si == 0) {
-        M = m;
-        L = l;
+        for (int db = 0; db < D / 16; ++db) o[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    if (t0 <= w_max) {
+      const bf16_t *pg[4];
 #pragma unroll
-        for (int e = 0; e < D / 4; ++e) O[e] = os[e];
+      for (int k = 0; k < 4; ++k) pg[k] = &lds[T & 1][k * kSlot];
+      Half<D> hk;
+      load_k<D, FromLds>(hk, pg);
+      bf16x8 pop[NCB][2];
+      float alpha[NCB], m_new[NCB], l_new[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        attn_scores<D>(hk, t0, qop[cb], pos[cb], cscale, m[cb], l[cb], pop[cb], alpha[cb], m_new[cb], l_new[cb]);
+      Half<D> hv;
+      load_v<D, FromLds>(hv, pg);
+      if (t0 <= w_min) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          attn_values<D, false>(hv, t0, pos[cb], p_max + 1, pop[cb], alpha[cb], m_new[cb], l_new[cb], m[cb], l[cb],
+                                o[cb]);
       } else {
-        merge_state<D / 4>(M, L, O, m, l, os);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          attn_values<D, true>(hv, t0, pos[cb], p_max + 1, pop[cb], alpha[cb], m_new[cb], l_new[cb], m[cb], l[cb],
+                               o[cb]);
+      }
+    }
+    // end of a split: fold its state into the merged state of every column it reached
+    if (t0 + kTile >= min(s0 + split_tokens, p_max + 1)) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        if (s0 <= pos[cb]) {
+          float os[D / 4];
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) os[db * 4 + i] = o[cb][db][i];
+          if (s0 == 0) {
+            M[cb] = m[cb];
+            L[cb] = l[cb];
+#pragma unroll
+            for (int e = 0; e < D / 4; ++e) O[cb][e] = os[e];
+          } else {
+            merge_state<D / 4>(M[cb], L[cb], O[cb], m[cb], l[cb], os);
+          }
+        }
       }
     }
   }
-  if (bad) L = __builtin_nanf("");
-  if (!col_ok) return;
+  bad = __any(bad);
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    uint32_t w0 = pack2(__fdiv_rn(O[db * 4 + 0], L), __fdiv_rn(O[db * 4 + 1], L));
-    uint32_t w1 = pack2(__fdiv_rn(O[db * 4 + 2], L), __fdiv_rn(O[db * 4 + 3], L));
-    *reinterpret_cast<uint2 *>(op + db * 16) = make_uint2(w0, w1);
+  for (int cb = 0; cb < NCB; ++cb) {
+    if (!col_ok[cb]) continue;
+    const float Lc = bad ? __builtin_nanf("") : L[cb];
+    bf16_t *op = out + (jrow[cb] * Hq + g * G + hh) * D + grp * 4;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      uint32_t w0 = pack2(__fdiv_rn(O[cb][db * 4 + 0], Lc), __fdiv_rn(O[cb][db * 4 + 1], Lc));
+      uint32_t w1 = pack2(__fdiv_rn(O[cb][db * 4 + 2], Lc), __fdiv_rn(O[cb][db * 4 + 3], Lc));
+      *reinterpret_cast<uint2 *>(op + db * 16) = make_uint2(w0, w1);
+    }
   }
 }
 
@@ -508,15 +602,17 @@ hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st) {
-  const int tpb = 16 / a.G;
-  const int blocks = (a.n_tok + tpb - 1) / tpb + a.n_seqs;
-  dim3 grid(blocks, a.Hkv);
+  constexpr int NCB = 2;
+  const int QT = 4 * NCB * (16 / a.G);
+  const long blocks = (long)(a.n_tok + QT - 1) / QT + a.n_seqs;  // bound on sum of ceil(n_s / QT)
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks, a.Hkv);
   if (a.D == 128)
-    hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(64), 0, st, a.q, a.q_row_stride, a.cu,
+    hipLaunchKernelGGL((attn_prefill_kernel<128, NCB>), grid, dim3(256), 0, st, a.q, a.q_row_stride, a.cu,
                        a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.n_pages,
                        a.Hkv, a.G, a.split_tokens, a.ctx_bound, a.cscale, a.out);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(64), 0, st, a.q, a.q_row_stride, a.cu,
+    hipLaunchKernelGGL((attn_prefill_kernel<64, NCB>), grid, dim3(256), 0, st, a.q, a.q_row_stride, a.cu,
                        a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.n_pages,
                        a.Hkv, a.G, a.split_tokens, a.ctx_bound, a.cscale, a.out);
   return hipGetLastError();
