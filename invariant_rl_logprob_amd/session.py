@@ -62,6 +62,7 @@ class Session:
         self.pool = torch.empty(pool_pages * self.page_bytes, dtype=torch.uint8, device=self.device)
         self.kv = ril_kv_alloc(self.model, self.pool, shuffle_seed)
         self.pages: Dict[object, List[int]] = {}
+        self._ids: Dict[object, torch.Tensor] = {}  # page lists as int32 tensors, per sequence
 
     def set_policy(self, policy: int, attn_split_tokens: int = 0) -> None:
         """Switch the comparator policy (benchmarking only) and grow the workspace if
@@ -94,15 +95,25 @@ class Session:
 
     def release(self, seq) -> None:
         ids = self.pages.pop(seq, [])
+        self._ids.pop(seq, None)
         if ids:
             ril_kv_release(self.kv, ids)
+
+    def _page_ids(self, seq) -> torch.Tensor:
+        lst = self.pages[seq]
+        t = self._ids.get(seq)
+        if t is None or t.numel() != len(lst):
+            t = torch.tensor(lst, dtype=torch.int32)
+            self._ids[seq] = t
+        return t
 
     def page_table(self, seqs: Sequence, ctx_bound: int) -> torch.Tensor:
         stride = max(1, math.ceil(ctx_bound / PAGE))
         t = torch.full((len(seqs), stride), -1, dtype=torch.int32)
         for i, s in enumerate(seqs):
-            ids = self.pages[s][:stride]
-            t[i, : len(ids)] = torch.tensor(ids, dtype=torch.int32)
+            ids = self._page_ids(s)
+            n = min(stride, ids.numel())
+            t[i, :n] = ids[:n]
         return t.to(self.device)
 
     # -- calls -----------------------------------------------------------------

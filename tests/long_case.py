@@ -1,0 +1,133 @@
+"""Harness for the long-context mixed batch: long sequences prefilled in chunks, each
+prefill call also carrying the decode rows that advance in that step (as one-token
+segments), in a seeded order.  Every computation goes through the C ABI; the oracle
+is called only from oracle_long / oracle_decode."""
+
+from __future__ import annotations
+
+import math
+from collections import defaultdict
+from typing import Dict, Sequence
+
+import torch
+
+import workloads as wl
+from invariant_rl_logprob_amd.session import Session
+
+
+class LongMixCase:
+    def __init__(self, w: wl.LongMix = wl.LONG_MIX, *, n_seqs: int = None, seq_len: int = None,
+                 rows: int = None, decode_ctx: Sequence[int] = None, device="cuda", shuffle_seed=99,
+                 max_chunk: int = None):
+        m = w.decode
+        self.w, self.m, self.device = w, m, device
+        self.L = seq_len or w.seq_len
+        self.nd = w.decode_tokens
+        self.seqs = list(range(n_seqs if n_seqs is not None else w.n_seqs))
+        self.rows = list(range(rows if rows is not None else m.rows))
+        self.ctx = {r: int(decode_ctx[i]) if decode_ctx is not None else wl.gqa_ctx(r, m)
+                    for i, r in enumerate(self.rows)}
+        assert all(c >= self.nd for c in self.ctx.values())
+        self.scale = 1.0 / math.sqrt(m.head_dim)
+        self.head = wl.gqa_head_weights(m, device=device)
+        self.long = {s: wl.long_seq(s, w, device=device, length=self.L) for s in self.seqs}
+        max_chunk = max_chunk or max(w.chunks)
+        pages = (sum(math.ceil(c / 16) for c in self.ctx.values())
+                 + 2 * len(self.seqs) * math.ceil(self.L / 16) + 64)
+        self.sess = Session(n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads, head_dim=m.head_dim, vocab=m.vocab,
+                            d_head=m.d_head, w_lm=self.head["w_lm"], w_o=self.head["w_o"],
+                            max_rows=max(1, len(self.rows)),
+                            max_tokens=len(self.seqs) * max_chunk + len(self.rows),
+                            max_ctx=max([self.L] + list(self.ctx.values())), pool_pages=pages,
+                            softmax_scale=self.scale, rms_eps=m.rms_eps, shuffle_seed=shuffle_seed, device=device)
+        # decode rows: history [0, ctx - nd) in the pool; keep the inputs of the last nd positions
+        self.dec: Dict[int, dict] = {}
+        for r in self.rows:
+            d = wl.gqa_row(r, m, device=device, ctx=self.ctx[r])
+            n = self.ctx[r] - self.nd
+            if n > 0:
+                self.sess.write_kv([("D", r)], [0], [d["k"][:n]], [d["v"][:n]])
+            R = d["q"].shape[0]
+            self.dec[r] = {key: d[key][R - self.nd:].clone() for key in ("q", "target")}
+            self.dec[r].update({key: d[key][n:].clone() for key in ("k", "v")})
+            torch.cuda.synchronize()
+            del d
+
+    def decode_reference(self) -> torch.Tensor:
+        """The decode rows' last nd positions by plain decode steps (all rows per call):
+        fp32 [rows, nd]."""
+        out = []
+        for j in range(self.nd):
+            st = lambda key: torch.stack([self.dec[r][key][j] for r in self.rows])  # noqa: E731
+            ctx = [self.ctx[r] - self.nd + j + 1 for r in self.rows]
+            out.append(self.sess.decode([("D", r) for r in self.rows], ctx, targets=st("target"), q=st("q"),
+                                        k=st("k"), v=st("v")))
+        return torch.stack(out, dim=1)
+
+    def run_schedule(self, chunk: int, mix: int, tag) -> tuple:
+        """Prefill every long sequence in chunks of `chunk` tokens, one prefill call per
+        step carrying each sequence's next chunk plus the decode rows that the seeded mix
+        advances in that step, in a seeded segment order.  Returns (fp32 [n_seqs, L] long
+        logprobs, fp32 [rows, nd] decode logprobs)."""
+        steps_of, order_key = wl.mix_schedule(self.w, chunk, mix, self.rows, self.L)
+        at_step = defaultdict(list)
+        for r, st in steps_of.items():
+            for j, i in enumerate(st):
+                at_step[i].append((r, j))
+        g = torch.Generator().manual_seed(order_key)
+        lp_long = torch.empty((len(self.seqs), self.L), dtype=torch.float32, device=self.device)
+        lp_dec = torch.empty((len(self.rows), self.nd), dtype=torch.float32, device=self.device)
+        row_idx = {r: i for i, r in enumerate(self.rows)}
+        for i in range(-(-self.L // chunk)):
+            segs = []
+            a, b = i * chunk, min(self.L, (i + 1) * chunk)
+            for si, s in enumerate(self.seqs):
+                d = self.long[s]
+                segs.append((("L", tag, s), a, d["q"][a:b], d["k"][a:b], d["v"][a:b], d["target"][a:b], (0, si, a)))
+            for r, j in at_step.get(i, []):
+                d = self.dec[r]
+                p = self.ctx[r] - self.nd + j
+                segs.append((("D", r), p, d["q"][j:j + 1], d["k"][j:j + 1], d["v"][j:j + 1], d["target"][j:j + 1],
+                             (1, row_idx[r], j)))
+            segs = [segs[k] for k in torch.randperm(len(segs), generator=g).tolist()]
+            out = self.sess.prefill([x[0] for x in segs], [x[1] for x in segs], targets=[x[5] for x in segs],
+                                    qs=[x[2] for x in segs], ks=[x[3] for x in segs], vs=[x[4] for x in segs])
+            off = 0
+            for x in segs:
+                n = x[2].shape[0]
+                kind, idx, at = x[6]
+                if kind == 0:
+                    lp_long[idx, at: at + n] = out[off: off + n]
+                else:
+                    lp_dec[idx, at] = out[off]
+                off += n
+        for s in self.seqs:
+            self.sess.release(("L", tag, s))
+        torch.cuda.synchronize()
+        return lp_long, lp_dec
+
+    # -- oracle ----------------------------------------------------------------
+    def _head_np(self):
+        if not hasattr(self, "_np_head"):
+            self._np_head = (self.head["w_lm"].float().cpu().numpy(), self.head["w_o"].float().cpu().numpy())
+        return self._np_head
+
+    def oracle_long(self, s: int, p: int) -> float:
+        """fp64 oracle logprob of long sequence s at position p."""
+        import oracle
+        d = self.long[s]
+        w_lm, w_o = self._head_np()
+        return oracle.gqa_row_logprob(oracle.widen(d["q"][p]), oracle.widen(d["k"][: p + 1]),
+                                      oracle.widen(d["v"][: p + 1]), self.scale, w_lm, int(d["target"][p]),
+                                      self.m.rms_eps, w_o=w_o)
+
+    def oracle_decode(self, r: int, j: int) -> float:
+        """fp64 oracle logprob of decode row r at its j-th decoded position."""
+        import oracle
+        d = wl.gqa_row(r, self.m, device=self.device, ctx=self.ctx[r])
+        p = self.ctx[r] - self.nd + j
+        R = d["q"].shape[0]
+        w_lm, w_o = self._head_np()
+        return oracle.gqa_row_logprob(oracle.widen(d["q"][R - self.nd + j]), oracle.widen(d["k"][: p + 1]),
+                                      oracle.widen(d["v"][: p + 1]), self.scale, w_lm,
+                                      int(d["target"][R - self.nd + j]), self.m.rms_eps, w_o=w_o)

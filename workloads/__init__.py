@@ -174,6 +174,52 @@ def gqa_row(row: int, w: GQADecode = GQA_DECODE_B64, device="cpu", ctx: int = No
 
 
 @dataclasses.dataclass(frozen=True)
+class LongMix:
+    """Chunked prefill of long sequences mixed with decode rows (GQA_LONG's model):
+    n_seqs sequences of seq_len tokens prefilled in chunks of each size in ``chunks``,
+    interleaved with the decode rows of ``decode`` (contexts in [ctx_lo, ctx_hi]), each of
+    which decodes its last ``decode_tokens`` positions during the prefill."""
+    n_seqs: int = 8
+    seq_len: int = 131072
+    chunks: Tuple[int, ...] = (512, 2048, 8192)
+    decode_tokens: int = 16
+    decode: GQADecode = GQA_LONG
+    seed: int = 4
+
+
+LONG_MIX = LongMix()
+
+
+def long_seq(seq: int, w: LongMix = LONG_MIX, device="cpu", length: int = None):
+    """One long sequence: k, v [L, Hkv, D], q [L, Hq, D] and target [L] for every position."""
+    m = w.decode
+    L = w.seq_len if length is None else int(length)
+    s = w.seed
+    return {
+        "len": L,
+        "k": randn((L, m.n_kv_heads, m.head_dim), key(s, "long-k", seq, L), 1.0, device),
+        "v": randn((L, m.n_kv_heads, m.head_dim), key(s, "long-v", seq, L), 1.0, device),
+        "q": randn((L, m.n_q_heads, m.head_dim), key(s, "long-q", seq, L), 1.0, device),
+        "target": randint(0, m.vocab - 1, (L,), key(s, "long-target", seq, L), device),
+    }
+
+
+def mix_schedule(w: LongMix, chunk: int, mix: int, rows: Sequence[int], seq_len: int = None):
+    """A seeded batch mix: for each prefill step (one chunk of every long sequence), the
+    decode rows that advance one position in it, and the order of the step's segments.
+    Returns (steps_of_row {row: sorted step list of length decode_tokens}, order_seed)."""
+    L = w.seq_len if seq_len is None else int(seq_len)
+    n_steps = -(-L // chunk)
+    assert n_steps >= w.decode_tokens, "every decode position needs a step of its own"
+    g = _gen(key(w.seed, "mix", chunk, mix), "cpu")
+    steps = {}
+    for r in rows:
+        pick = torch.randperm(n_steps, generator=g)[: w.decode_tokens]
+        steps[r] = sorted(int(x) for x in pick)
+    return steps, key(w.seed, "order", chunk, mix)
+
+
+@dataclasses.dataclass(frozen=True)
 class MLADecode:
     """Absorbed-MLA decode rows: q [H, 576] per position, one shared latent row
     [576] = 512 latent + 64 rope dims per cached token; softmax scale 1/sqrt(192)."""
