@@ -377,7 +377,105 @@ def bench_sparse(args):
     }
 
 
-WORKLOADS = {"gqa_decode_b64": bench_gqa, "mla_decode_b128": bench_mla, "sparse_mla_b32": bench_sparse}
+# ---------------------------------------------------------------------------
+# long context: 256 decode rows at contexts up to 128K, and the chunked prefill of
+# 8 x 131072-token sequences mixed with those rows
+# ---------------------------------------------------------------------------
+
+def bench_long(args):
+    import numpy as np
+    import torch
+    import invariant_rl_logprob_amd as ril
+    import workloads as wl
+    from invariant_rl_logprob_amd.metrics import mismatch
+    from long_case import LongMixCase
+
+    w = wl.LONG_MIX
+    m = w.decode
+    t0 = time.time()
+    case = LongMixCase(w, progress=log)
+    rows = case.rows
+    ctx = [case.ctx[r] for r in rows]
+    log(f"data ready in {time.time() - t0:.1f}s; decode sum ctx = {sum(ctx)}")
+    ref = case.decode_reference()
+    st = lambda key: torch.stack([case.dec[r][key][-1] for r in rows])  # noqa: E731
+    launch, out = case.sess.prepare_decode([("D", r) for r in rows], ctx, targets=st("target"), q=st("q"),
+                                           k=st("k"), v=st("v"))
+    ms_step, kern = timed_steps(launch, args.steps, args.warmup)
+    last_equal = bool(np.array_equal(out.cpu().view(torch.int32).numpy(), ref[:, -1].cpu().view(torch.int32).numpy()))
+    kv_bytes = sum(ctx) * m.n_kv_heads * m.head_dim * 2 * 2
+    q_bytes = len(rows) * m.n_q_heads * m.head_dim * 2
+    split_us, merge_us = kern["attn_split"]["avg_us"], kern["attn_merge"]["avg_us"]
+    split_gbps = (kv_bytes + q_bytes) / (split_us * 1e-6) / 1e9
+    roof = roofline_hbm("attn_decode_split", split_gbps, kv_bytes + q_bytes, split_us)
+    log(f"decode: {ms_step:.3f} ms/step, split {split_us:.1f} us ({split_gbps:.0f} GB/s)")
+
+    # chunked prefill mixed with the decode rows; the trace hook times every kernel
+    sched = [(8192, 0), (2048, 1)] + ([(512, 2)] if args.long_all_chunks else [])
+    runs, prefill = [], {}
+    L, S = case.L, len(case.seqs)
+    pos_sum = S * L * (L + 1) // 2  # sum over long positions of (p + 1)
+    attn_flops = 4 * m.head_dim * m.n_q_heads * pos_sum
+    for chunk, mix in sched:
+        torch.cuda.synchronize()
+        ril.ril_trace_enable(True)
+        t1 = time.time()
+        lp_long, lp_dec = case.run_schedule(chunk, mix, ("bench", chunk, mix))
+        secs = time.time() - t1
+        kt = {}
+        for kid, name in enumerate(ril.KERNEL_NAMES):
+            tot, cnt = ril.ril_trace_read(kid)
+            if cnt:
+                kt[name] = round(tot, 3)
+        ril.ril_trace_enable(False)
+        runs.append((lp_long, lp_dec))
+        toks = S * L + len(rows) * case.nd
+        ap_ms = kt.get("attn_prefill", float("nan"))
+        lm_ms = kt.get("lm_head", float("nan"))
+        prefill[f"chunk_{chunk}_mix_{mix}"] = {
+            "wall_s": round(secs, 2), "tokens": toks, "tokens_per_s": round(toks / secs, 1),
+            "kernel_ms": kt,
+            "attn_prefill_tflops": round(attn_flops / (ap_ms * 1e-3) / 1e12, 1),
+            "attn_prefill_frac_of_bf16_peak": round(attn_flops / (ap_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "lm_head_tflops": round(2.0 * toks * m.d_head * m.vocab / (lm_ms * 1e-3) / 1e12, 1)}
+        log(f"prefill chunk {chunk} mix {mix}: {prefill[f'chunk_{chunk}_mix_{mix}']}")
+    long0, dec0 = runs[0]
+    diff_long = mismatch(long0.reshape(-1), runs[1][0].reshape(-1))
+    diff_dec = mismatch(dec0.reshape(-1), ref.reshape(-1))
+    for lp_long, lp_dec in runs[2:]:
+        diff_long = max(diff_long, mismatch(long0.reshape(-1), lp_long.reshape(-1)), key=lambda d: d["max"])
+    log(f"long positions across chunk sizes/mixes: {diff_long}; decode rows in mixes vs decode steps: {diff_dec}")
+
+    cpu = None
+    if not args.no_cpu and args.cpu_rows > 0:
+        import oracle  # the cpu_baseline leg
+        picks = [(0, 0), (0, L - 1), (1, 8191), (1, 8192)][: max(1, args.cpu_rows // 3)]
+        t1 = time.time()
+        got = [case.oracle_long(s_, p_) for s_, p_ in picks]
+        secs = time.time() - t1
+        gpu = long0.cpu().numpy()
+        cpu = {"value": round(len(picks) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{len(picks)} long-sequence positions {picks} (attention over up to 131072 positions, "
+                         f"8192->4096 projection and lm-head in fp64), {secs:.1f} s",
+               "max_abs_diff_vs_gpu": float(max(abs(gpu[s_, p_] - g_) for (s_, p_), g_ in zip(picks, got)))}
+        log(f"oracle: {cpu}")
+
+    return {
+        "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+        "config": {"workload": "long_mix: 256 GQA decode rows (64 q / 8 kv heads, head_dim 128) at contexts "
+                               "U[1024,131072], o-proj 8192x4096, lm-head 4096x129280; plus the chunked prefill "
+                               "of 8 x 131072-token sequences mixed with those rows",
+                   "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 512, "parallelism": "none (1 GPU)"},
+        "attn_split_hbm_gbps": round(split_gbps, 1), "decode_diff_vs_mixed_prefill": diff_dec,
+        "long_positions_diff_across_chunks_and_mixes": diff_long,
+        "timed_step_equals_checked_decode": last_equal,
+        "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+        "prefill": prefill, "roofline": roof, "cpu_baseline": cpu,
+    }
+
+
+WORKLOADS = {"gqa_decode_b64": bench_gqa, "mla_decode_b128": bench_mla, "sparse_mla_b32": bench_sparse,
+             "long_mix": bench_long}
 
 
 def main():
@@ -389,6 +487,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=12, help="rows of the oracle timing sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-comparator", action="store_true", help="skip the shape-derived comparator leg")
+    ap.add_argument("--long-all-chunks", action="store_true", help="long_mix: also run the 512-token chunks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")
     args = ap.parse_args()

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libril.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m invariant_rl_logprob_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python invariant_rl_logprob_amd/build.py` "
         "(or __graft_entry__.build()); there is no fallback path")
 _lib = ctypes.CDLL(LIB_PATH)
 

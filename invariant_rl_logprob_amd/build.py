@@ -1,6 +1,6 @@
 """Build libril.so (the HIP kernels + the C ABI) in-tree for gfx950.
 
-    python -m invariant_rl_logprob_amd.build
+    python invariant_rl_logprob_amd/build.py      (or __graft_entry__.build())
 
 Flags that are part of the numerical contract:
   -ffp-contract=off   the compiler fuses no multiply-add on its own: an FMA exists only
@@ -49,8 +49,23 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    _check_undefined(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_undefined(path: str) -> None:
+    """A shared library links with undefined symbols and fails only when loaded; a
+    kernel template whose host launch stub was not emitted shows up here as an
+    undefined ``__device_stub__`` symbol.  Refuse such a library at build time."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True)
+    if r.returncode != 0:
+        return  # no nm: the import check still fails loudly
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l or "_ZN3ril" in l]
+    if missing:
+        os.remove(path)
+        raise RuntimeError("libril.so would have undefined library symbols:\n  " + "\n  ".join(missing))
 
 
 if __name__ == "__main__":

@@ -3,8 +3,8 @@
 // Invariance rules these helpers encode (Bitwise-consistent RL post, section 2):
 //  * one MFMA instruction for every contraction (v_mfma_f32_16x16x32_bf16), so an
 //    output element's rounding never depends on which kernel or tile size computed it;
-//  * bf16 rounding is round-to-nearest-even, written out on the bits (section 4.4,
-//    condition 1: one elementwise round-to-nearest rule everywhere);
+//  * bf16 rounding is round-to-nearest-even everywhere (section 4.4, condition 1: one
+//    elementwise round-to-nearest rule);
 //  * every reduction is a fixed tree over a fixed element->lane map: lane-local
 //    sequential sums, then xor-butterflies whose adds are commutative, so all lanes
 //    of a butterfly end with the same bits;
@@ -40,16 +40,16 @@ __device__ __forceinline__ float log2f_hw(float x) { return __builtin_amdgcn_log
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quietened).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (the IEEE conversion, one v_cvt_pk_bf16_f32 per
+// pair on gfx950); NaN stays NaN.  The instruction's results equal the written-out rule
+// (add 0x7fff plus the lowest kept bit, truncate) for every non-NaN input, denormals
+// included.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

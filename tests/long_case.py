@@ -18,7 +18,7 @@ from invariant_rl_logprob_amd.session import Session
 class LongMixCase:
     def __init__(self, w: wl.LongMix = wl.LONG_MIX, *, n_seqs: int = None, seq_len: int = None,
                  rows: int = None, decode_ctx: Sequence[int] = None, device="cuda", shuffle_seed=99,
-                 max_chunk: int = None):
+                 max_chunk: int = None, progress=None):
         m = w.decode
         self.w, self.m, self.device = w, m, device
         self.L = seq_len or w.seq_len
@@ -52,6 +52,8 @@ class LongMixCase:
             self.dec[r].update({key: d[key][n:].clone() for key in ("k", "v")})
             torch.cuda.synchronize()
             del d
+            if progress is not None and (r + 1) % 32 == 0:
+                progress(f"decode-row history {r + 1}/{len(self.rows)} written")
 
     def decode_reference(self) -> torch.Tensor:
         """The decode rows' last nd positions by plain decode steps (all rows per call):
