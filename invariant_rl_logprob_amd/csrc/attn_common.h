@@ -86,24 +86,212 @@ __device__ __forceinline__ void merge_state(float &M, float &L, float (&O)[N], f
 
 // Split merge over stored fp32 partials, split 0 first then left to right; lane owns
 // PER consecutive dims.  Writes bf16(O / L).  Shared by every decode-style attention.
+// The loads of CH splits are issued together before they are folded (in the same order),
+// so a row's splits cost one memory latency per CH splits rather than one each.
 template <int D>
 __device__ __forceinline__ void merge_partials(const float *__restrict__ part_o,
                                                const float *__restrict__ part_ml, long base, int ns,
                                                bf16_t *__restrict__ op) {
   constexpr int PER = D / 64;
+  constexpr int CH = PER <= 2 ? 8 : 4;
   const int lane = threadIdx.x & 63;
-  float M = part_ml[base * 2], L = part_ml[base * 2 + 1];
+  float M = 0.f, L = 0.f;
   float O[PER];
+  for (int s0 = 0; s0 < ns; s0 += CH) {
+    float ms[CH], ls[CH], os[CH][PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) O[j] = part_o[base * D + lane * PER + j];
-  for (int s = 1; s < ns; ++s) {
-    float os[PER];
+    for (int c = 0; c < CH; ++c) {
+      const long s = base + min(s0 + c, ns - 1);  // past the last split: a repeat, not folded
+      ms[c] = part_ml[s * 2];
+      ls[c] = part_ml[s * 2 + 1];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) os[j] = part_o[(base + s) * D + lane * PER + j];
-    merge_state<PER>(M, L, O, part_ml[(base + s) * 2], part_ml[(base + s) * 2 + 1], os);
+      for (int j = 0; j < PER; ++j) os[c][j] = part_o[s * D + lane * PER + j];
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (s0 + c >= ns) break;
+      if (s0 + c == 0) {
+        M = ms[0];
+        L = ls[0];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) O[j] = os[0][j];
+      } else {
+        merge_state<PER>(M, L, O, ms[c], ls[c], os[c]);
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < PER; ++j) op[lane * PER + j] = f2bf(__fdiv_rn(O[j], L));
 }
+
+// ---------------------------------------------------------------------------
+// The tile routine shared by decode and prefill
+// ---------------------------------------------------------------------------
+
+// Half of a 64-token tile in MFMA operand registers (D/8 16-byte values per lane):
+// either its K half or its V half.
+//   K half, r[mb*(D/32) + c]  : A operand of S^T = K Q^T for M-block mb = 2kc + h,
+//                               dims 32c .. 32c+31; row r <-> token 32kc + 8(r/4) + 4h + r%4
+//   V half, r[kc*(D/16) + db] : A operand of o^T += V^T P^T for 32-token step kc, dims
+//                               16db .. 16db+15; k-slot 8(lane/16) + j <-> token 32kc + 8(lane/16) + j
+template <int D>
+struct Half {
+  u32x4 r[D / 8];
+};
+
+// Operand loads from global memory or from an LDS copy of the same page blocks.
+struct FromGlobal {
+  static __device__ __forceinline__ u32x4 ld(const bf16_t *p) { return ld16(p); }
+};
+struct FromLds {
+  static __device__ __forceinline__ u32x4 ld(const bf16_t *p) {
+    return *(const __attribute__((address_space(3))) u32x4 *)(p);
+  }
+};
+// LDS reads the compiler does not track: the waitcnt pass would otherwise make every LDS
+// read wait for all direct-to-LDS copies in flight (it cannot tell which LDS bytes they
+// write), serialising the copy pipeline.  The caller orders them after the copies they
+// read (its own vmcnt wait + barrier) and calls lds_settle before using the values.
+struct FromLdsUntracked {
+  static __device__ __forceinline__ u32x4 ld(const bf16_t *p) {
+    u32x4 r;
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t *)p;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+  }
+};
+
+// pg[k]: K block of the tile's k-th page (its V block follows at +16*D).
+template <int D, typename Mem = FromGlobal>
+__device__ __forceinline__ void load_k(Half<D> &t, const bf16_t *const (&pg)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int rq = r16 >> 2, ri = r16 & 3;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16_t *kb = pg[2 * kc + (rq >> 1)] + grp * 128 + h * 64 + (rq & 1) * 32 + ri * 8;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) t.r[(2 * kc + h) * (D / 32) + c] = Mem::ld(kb + c * 512);
+    }
+  }
+}
+
+template <int D, typename Mem = FromGlobal>
+__device__ __forceinline__ void load_v(Half<D> &t, const bf16_t *const (&pg)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const bf16_t *vb = pg[2 * kc + (grp >> 1)] + 16 * D + (grp & 1) * (8 * D) + r16 * 8;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) t.r[kc * (D / 16) + db] = Mem::ld(vb + db * 128);
+  }
+}
+
+// Wait for this wave's untracked LDS reads; each value passes through an empty asm after
+// the wait, so no use of it can be scheduled before the wait.
+template <int D>
+__device__ __forceinline__ void lds_settle(Half<D> &t) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: );
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) asm volatile("" : "+v"(t.r[i]));
+}
+
+// First half of the tile update for the 16 query rows (MFMA columns) of this wave:
+// scores from the K half, then the online-softmax step (tile_softmax).
+//   qop : B operand of S^T = K Q^T (lane: column lane%16, dims 32c + 8(lane/16) ..)
+//   pos : this lane's column's query position (-1: padding column)
+template <int D>
+__device__ __forceinline__ void attn_scores(const Half<D> &k, int tile_start, const bf16x8 (&qop)[D / 32],
+                                            int pos, float cscale, float m, float l, bf16x8 (&pop)[2],
+                                            float &alpha, float &m_new, float &l_new) {
+  f32x4 s[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) acc = mfma(as_bf16x8(k.r[mb * (D / 32) + c]), qop[c], acc);
+    s[mb] = acc;
+  }
+  tile_softmax(s, tile_start, pos, cscale, m, l, pop, alpha, m_new, l_new);
+}
+
+// Second half: o = o * alpha + MFMA(bf16 P, V), two 32-token steps in token order.
+//   vbound : V values of tokens >= vbound are read as 0 (beyond any column's context)
+// State per lane = its column's (m, l) and o^T[16db + 4(lane/16) + i].
+// MAYBE_INACTIVE: some column may have pos < tile_start; such columns keep their state.
+template <int D, bool MAYBE_INACTIVE>
+__device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, int pos, int vbound,
+                                            const bf16x8 (&pop)[2], float alpha, float m_new, float l_new,
+                                            float &m, float &l, f32x4 (&o)[D / 16]) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  f32x4 on[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) on[db] = o[db] * alpha;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const int n_valid = vbound - (tile_start + 32 * kc + 8 * grp);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      u32x4 vv = v.r[kc * (D / 16) + db];
+      if (n_valid < 8) vv = keep_first(vv, n_valid);
+      on[db] = mfma(as_bf16x8(vv), pop[kc], on[db]);
+    }
+  }
+  if (MAYBE_INACTIVE) {
+    const bool act = tile_start <= pos;
+    m = act ? m_new : m;
+    l = act ? l_new : l;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[db][i] = act ? on[db][i] : o[db][i];
+    }
+  } else {
+    m = m_new;
+    l = l_new;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db] = on[db];
+  }
+}
+
+// One whole 64-token tile update (both halves).
+template <int D, bool MAYBE_INACTIVE>
+__device__ __forceinline__ void attn_tile(const Half<D> &k, const Half<D> &v, int tile_start,
+                                          const bf16x8 (&qop)[D / 32], int pos, int vbound,
+                                          float cscale, float &m, float &l, f32x4 (&o)[D / 16]) {
+  bf16x8 pop[2];
+  float alpha, m_new, l_new;
+  attn_scores<D>(k, tile_start, qop, pos, cscale, m, l, pop, alpha, m_new, l_new);
+  attn_values<D, MAYBE_INACTIVE>(v, tile_start, pos, vbound, pop, alpha, m_new, l_new, m, l, o);
+}
+
+template <int D>
+__device__ __forceinline__ void load_qop(bf16x8 (&qop)[D / 32], const bf16_t *qrow, bool ok) {
+  const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    u32x4 v = ld16(qrow + c * 32 + grp * 8);
+    if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+    qop[c] = as_bf16x8(v);
+  }
+}
+
+// K block base of page slot `idx` of the split (0 .. 4*tiles-1): a wave-uniform readlane.
+__device__ __forceinline__ const bf16_t *page_base(const bf16_t *pool, int pid_lane, int idx, int Hkv,
+                                                   int g, int D) {
+  const int p = __builtin_amdgcn_readlane(pid_lane, idx);
+  return pool + ((long)p * Hkv + g) * (32 * D);
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pages(const bf16_t *(&pg)[4], const bf16_t *pool, int pid_lane,
+                                           int tile, int Hkv, int g) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pg[k] = page_base(pool, pid_lane, 4 * tile + k, Hkv, g, D);
+}
+
 
 }  // namespace ril

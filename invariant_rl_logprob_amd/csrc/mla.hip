@@ -6,9 +6,11 @@
 // form of the Bitwise-consistent RL post, section 3: MLA compresses KV before caching).
 //
 // The split is a model constant and splits merge left to right, as for GQA.  Decode
-// runs one workgroup per (row, split, group of 64 heads): 4 waves, wave w owning heads
-// 64*group + 16w .. +15 as its MFMA columns (one wave per SIMD: the 512-wide fp32
-// accumulator of 16 heads takes 128 registers per lane).  The trainer-side recompute
+// runs one workgroup per (row, split, group of 64 heads): 8 waves in 4 pairs, pair p
+// owning heads 64*group + 16p .. +15 as its MFMA columns.  The pair's first wave
+// computes the scores and the online-softmax step and hands P and the rescale factor to
+// its partner through LDS; each wave of the pair then accumulates half of the 512 value
+// dims (a column's o^T elements are independent, so the split of dims changes no bits).  The trainer-side recompute
 // runs the very same kernels with one "row" per query token (context = position + 1),
 // after writing the chunk's latents: prefill and decode are one code path.
 //
@@ -19,11 +21,16 @@
 //
 // Latent page (16 tokens) = one 16 x 576 block in the K-operand layout of attn_common.h
 // (k_page_offset); a sparse page also holds the 16 tokens' fp32 indexer keys after it.
-// Per 64-token tile the workgroup puts the tile into LDS in the same layout (73,728 B)
-// and writes a transposed copy of the 512 value dims, V^T[d][token] with a 72-element
-// row (73,728 B), so both MFMA operands are 16-byte LDS reads.  Entries at or beyond
-// the row's bound are written as 0 into V^T; their scores are masked.
+// Per 64-token tile the workgroup copies the tile into LDS in the same layout (double-
+// buffered: the next tile is loaded into registers while the current one is computed).
+// Score operands are 16-byte LDS reads.  Value operands come from the same tile through
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i%4 of the 8-byte chunks addressed by lanes 4e + i/4, e = 0..3, so
+// lanes pointing at 4 consecutive dims of 4 tokens hand each lane one dim of those 4
+// tokens -- the V^T operand -- with no transposed copy.  Value entries at or beyond the
+// row's bound are zeroed in the operand; their scores are masked.
 #include <algorithm>
+#include <utility>
 
 #include "attn_common.h"
 #include "kernels.h"
@@ -32,8 +39,8 @@ namespace ril {
 
 constexpr int kMlaDqk = 576, kMlaDv = 512;
 constexpr int kMlaPage = kPage * kMlaDqk;     // 9216 elements: one page's latent block
-constexpr int kVtRow = 72;                    // 64 tokens + 8 pad (bank spread)
-constexpr int kMlaThreads = 256;              // 4 waves x 16 heads (H % 64 == 0)
+constexpr int kMlaSlot = kMlaPage + 64;       // LDS slot of a page: +128 B spreads the banks
+constexpr int kMlaThreads = 512;              // 4 pairs of waves x 16 heads (H % 64 == 0)
 constexpr int kTileUnits = 4 * kMlaPage / 8;  // 4608 16-byte units per tile
 
 // ---------------------------------------------------------------------------
@@ -104,221 +111,306 @@ __device__ __forceinline__ void mla_load_q(bf16x8 (&qop)[kMlaDqk / 32], const bf
   }
 }
 
-// S^T = K Q^T for the 64-token tile in LDS (K layout, 4 virtual pages).
+// LDS reads the compiler's wait pass does not track (inline asm, no memory clobber): the
+// tiles arrive by direct-to-LDS loads, and a tracked LDS read would make the pass wait
+// for every such load in flight.  Callers order them after the copies they read (vmcnt
+// wait + barrier), wait for them with lds_wait<N> (LDS reads complete in order, so at
+// most the N newest are then pending) and pass each value through settle() before use.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t *)p;
+}
+// base: this lane's LDS byte address; OFF: a byte offset common to all lanes, folded into
+// the instruction (< 65536)
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_rd128(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+// transposing read: lane i of each 16-lane group gets element i%4 of the 8-byte chunks
+// addressed by lanes 4e + i/4 of its group, e = 0..3
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_rdtr(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N == 0 || N == 4, "add the count");
+  if constexpr (N == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+}
+template <typename T>
+__device__ __forceinline__ void settle(T &v) { asm volatile("" : "+v"(v)); }
+
+// S^T = K Q^T for the 64-token tile in LDS (K layout, 4 page slots).  K step outermost:
+// each step's four M-block operands are read while the previous step's MFMAs run; every
+// accumulator still runs c = 0, 1, ... in order.  M-block mb of step c sits at byte
+// (mb/2)*2*slot + (mb%2)*128 + c*1024 from this lane's base.
+constexpr int kSlotBytes = 2 * kMlaSlot;
 __device__ __forceinline__ void mla_tile_scores(f32x4 (&s)[4], const bf16_t *kt,
                                                 const bf16x8 (&qop)[kMlaDqk / 32]) {
   const int lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
   const int rq = r16 >> 2, ri = r16 & 3;
+  const uint32_t base = lds_addr(kt) + 2 * ((rq >> 1) * kMlaSlot + grp * 128 + (rq & 1) * 32 + ri * 8);
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bf16_t *kb = kt + (2 * kc + (rq >> 1)) * kMlaPage + grp * 128 + h * 64 + (rq & 1) * 32 + ri * 8;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < kMlaDqk / 32; ++c)
-        acc = mfma(as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + c * 512)), qop[c], acc);
-      s[2 * kc + h] = acc;
+  for (int mb = 0; mb < 4; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 a[2][4];
+  auto issue = [&](auto cc) {
+    constexpr int C = decltype(cc)::value;
+    a[C & 1][0] = lds_rd128<C * 1024>(base);
+    a[C & 1][1] = lds_rd128<C * 1024 + 128>(base);
+    a[C & 1][2] = lds_rd128<C * 1024 + 2 * kSlotBytes>(base);
+    a[C & 1][3] = lds_rd128<C * 1024 + 2 * kSlotBytes + 128>(base);
+  };
+  issue(std::integral_constant<int, 0>{});
+  static_for<kMlaDqk / 32>([&](auto cc) {
+    constexpr int C = decltype(cc)::value;
+    if constexpr (C + 1 < kMlaDqk / 32) {
+      issue(std::integral_constant<int, C + 1>{});
+      lds_wait<4>();
+    } else {
+      lds_wait<0>();
     }
-  }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      settle(a[C & 1][mb]);
+      s[mb] = mfma(as_bf16x8(a[C & 1][mb]), qop[C], s[mb]);
+    }
+  });
 }
 
-// o^T = o^T * alpha + V^T P^T with V^T from LDS.
-__device__ __forceinline__ void mla_tile_values(f32x4 (&o)[kMlaDv / 16], const bf16_t *vt,
-                                                const bf16x8 (&pop)[2], float alpha) {
-  const int lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
-#pragma unroll
-  for (int db = 0; db < kMlaDv / 16; ++db) {
-    f32x4 acc = o[db] * alpha;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const u32x4 vv = *reinterpret_cast<const u32x4 *>(vt + (16 * db + r16) * kVtRow + 32 * kc + 8 * grp);
-      acc = mfma(as_bf16x8(vv), pop[kc], acc);
-    }
-    o[db] = acc;
-  }
+// V^T operands for the value dims 256*half .. +255: block b (dims 16b ..) of the 32-token
+// step kc.  Lane (group g, i = lane % 16) gets V[32kc + 8g + j][256*half + 16b + i],
+// j = 0..7, by two transposing reads (tokens +0..3 at byte offset 0, +4..7 at +128); the
+// block adds 512*b bytes and the step 2 page slots.  Entries j >= n_valid read as 0.
+__device__ __forceinline__ uint32_t mla_v_base(const bf16_t *kt, int half) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, i = lane & 15;
+  const int tok = 8 * grp + (i >> 2);
+  return lds_addr(kt) + 2 * ((tok >> 4) * kMlaSlot + k_page_offset(tok & 15, 256 * half + 4 * (i & 3)));
+}
+template <int B, int KC>
+__device__ __forceinline__ void mla_v_issue(u32x2 (&r)[2], uint32_t base) {
+  r[0] = lds_rdtr<512 * B + 2 * kSlotBytes * KC>(base);
+  r[1] = lds_rdtr<512 * B + 2 * kSlotBytes * KC + 128>(base);
+}
+__device__ __forceinline__ bf16x8 mla_v_take(u32x2 (&r)[2], int n_valid) {
+  settle(r[0]);
+  settle(r[1]);
+  u32x4 v = {r[0].x, r[0].y, r[1].x, r[1].y};
+  if (n_valid < 8) v = keep_first(v, n_valid);  // entries at or beyond the bound read as 0
+  return as_bf16x8(v);
 }
 
-// V^T[d][token] for d < 512 from the K-layout tile in LDS; tile rows with index
-// >= n_live are written as 0.
-__device__ __forceinline__ void mla_tile_transpose(const bf16_t *kt, bf16_t *vt, int n_live) {
-  for (int u = threadIdx.x; u < kTileUnits; u += kMlaThreads) {
-    const int p = u / (kMlaPage / 8), e = (u % (kMlaPage / 8)) * 8;
-    const int dc = e >> 9, g = (e >> 7) & 3, h = (e >> 6) & 1, th = (e >> 5) & 1, i = (e >> 3) & 3;
-    const int d0 = 32 * dc + 8 * g;
-    if (d0 >= kMlaDv) continue;
-    const int tok = 16 * p + 8 * th + 4 * h + i;
-    u32x4 v = *reinterpret_cast<const u32x4 *>(kt + p * kMlaPage + e);
-    if (tok >= n_live) v = u32x4{0u, 0u, 0u, 0u};
-    bf16_t *dst = vt + d0 * kVtRow + tok;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      dst[(2 * w) * kVtRow] = (bf16_t)(v[w] & 0xffffu);
-      dst[(2 * w + 1) * kVtRow] = (bf16_t)(v[w] >> 16);
-    }
-  }
-}
-
-__device__ __forceinline__ void mla_store_partial(float *part_o, float *part_ml, long base,
-                                                  const f32x4 (&o)[kMlaDv / 16], float m, float l) {
+// o^T = o^T * alpha + V^T P^T for value dims 256*half .. +255.  MASK: some entries of the
+// tile are at or beyond the bound (n_live < 64).  The next dim block's operands are read
+// while this block's two MFMAs run.  (alpha = 1 for every column of the wave -- no new
+// maximum -- leaves o unchanged bit for bit, so the products are skipped then.)
+template <bool MASK>
+__device__ __forceinline__ void mla_tile_values(f32x4 (&o)[kMlaDv / 32], const bf16_t *kt, int half,
+                                                const bf16x8 (&pop)[2], float alpha, int n_live) {
   const int grp = (threadIdx.x & 63) >> 4;
-  float *po = part_o + base * kMlaDv + grp * 4;
+  const int nv0 = MASK ? n_live - 8 * grp : 8, nv1 = MASK ? n_live - (32 + 8 * grp) : 8;
+  const uint32_t base = mla_v_base(kt, half);
+  const bool scale = __any(alpha != 1.f);
+  u32x2 r[2][2][2];
+  mla_v_issue<0, 0>(r[0][0], base);
+  mla_v_issue<0, 1>(r[0][1], base);
+  static_for<kMlaDv / 32>([&](auto bb) {
+    constexpr int B = decltype(bb)::value;
+    if constexpr (B + 1 < kMlaDv / 32) {
+      mla_v_issue<B + 1, 0>(r[(B + 1) & 1][0], base);
+      mla_v_issue<B + 1, 1>(r[(B + 1) & 1][1], base);
+      lds_wait<4>();
+    } else {
+      lds_wait<0>();
+    }
+    f32x4 acc = scale ? o[B] * alpha : o[B];
+    acc = mfma(mla_v_take(r[B & 1][0], nv0), pop[0], acc);
+    acc = mfma(mla_v_take(r[B & 1][1], nv1), pop[1], acc);
+    o[B] = acc;
+  });
+}
+
+// This wave's half of the split's o (dims 256*half ..), and (m, l) from the scoring wave.
+__device__ __forceinline__ void mla_store_partial(float *part_o, float *part_ml, long base, int half,
+                                                  const f32x4 (&o)[kMlaDv / 32], float m, float l) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  float *po = part_o + base * kMlaDv + 256 * half + grp * 4;
 #pragma unroll
-  for (int db = 0; db < kMlaDv / 16; ++db) *reinterpret_cast<f32x4 *>(po + db * 16) = o[db];
-  if (grp == 0) {
+  for (int b = 0; b < kMlaDv / 32; ++b) *reinterpret_cast<f32x4 *>(po + b * 16) = o[b];
+  if (half == 0 && grp == 0) {
     part_ml[base * 2] = m;
     part_ml[base * 2 + 1] = l;
   }
 }
 
-// ---------------------------------------------------------------------------
-// S8, dense: grid (splits, H/64, rows), 256 threads.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void mla_split_kernel(
-    const bf16_t *__restrict__ q, int mode, int row0, const int32_t *__restrict__ ctx_len,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
-    const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool, int page_elems,
-    int n_pages, int H, int split_tokens, int ctx_bound, float cscale, float *__restrict__ part_o,
-    float *__restrict__ part_ml, int max_splits) {
-  __shared__ bf16_t kt[4 * kMlaPage];
-  __shared__ bf16_t vt[kMlaDv * kVtRow];
-  const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15;
-  int seq, ctx;
-  long qrow;
-  mla_row(mode, r, row0, ctx_len, cu, start_pos, n_seqs, seq, ctx, qrow);
-  const int s0 = split * split_tokens;
-  if (ctx < 1 || ctx > ctx_bound || s0 >= ctx) return;  // uniform over the workgroup
-  const int s1 = min(ctx, s0 + split_tokens);
-  const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
-  // page ids of the split: lane i of every wave holds page index s0/16 + i (+64 in pidB)
-  const int32_t *pt = page_table + (long)seq * page_stride;
-  const int first = s0 / kPage, last = (ctx - 1) / kPage;
-  int pidA = pt[min(first + lane, last)], pidB = pt[min(first + 64 + lane, last)];
-  bool bad = (unsigned)pidA >= (unsigned)n_pages || (unsigned)pidB >= (unsigned)n_pages;
-  pidA = ((unsigned)pidA < (unsigned)n_pages) ? pidA : 0;
-  pidB = ((unsigned)pidB < (unsigned)n_pages) ? pidB : 0;
-  bad = __syncthreads_or(bad);
-  const int head = 64 * hg + 16 * wave + r16;
-  const bool col_ok = head < H;
-  bf16x8 qop[kMlaDqk / 32];
-  mla_load_q(qop, q, qrow, H, head, col_ok);
-  // A tile = 4 pages = 72 blocks of 64 16-byte units; block b lies in page b/18.  Wave w
-  // issues blocks w, w+4, ...: each is one direct-to-LDS load (lane i -> 16 bytes at
-  // kt + 512*b + 8*i), so no registers hold the tile in flight.
-  constexpr int kBlocks = 4 * kMlaPage / 512;  // 72
-  auto issue = [&](int t) {
-    for (int b = wave; b < kBlocks; b += kMlaThreads / 64) {
-      const int p = b / (kMlaPage / 512);
-      const int idx = 4 * t + p;
-      const int pid = idx < 64 ? __builtin_amdgcn_readlane(pidA, idx) : __builtin_amdgcn_readlane(pidB, idx - 64);
-      const bf16_t *src = pool + (long)pid * page_elems + (b % (kMlaPage / 512)) * 512 + lane * 8;
-      __builtin_amdgcn_global_load_lds(src, kt + b * 512, 16, 0, 0);
-    }
-  };
-  float m = neg_inf(), l = 0.f;
-  f32x4 o[kMlaDv / 16];
-#pragma unroll
-  for (int db = 0; db < kMlaDv / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  issue(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  mla_tile_transpose(kt, vt, ctx - s0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int t0 = s0 + t * kTile;
-    f32x4 s[4];
-    mla_tile_scores(s, kt, qop);
-    __syncthreads();  // every wave has read the K tile: refill it while PV runs
-    if (t + 1 < n_tiles) issue(t + 1);
-    bf16x8 pop[2];
-    float alpha, m_new, l_new;
-    tile_softmax(s, t0, ctx - 1, cscale, m, l, pop, alpha, m_new, l_new);
-    mla_tile_values(o, vt, pop, alpha);
-    m = m_new;
-    l = l_new;
-    if (t + 1 < n_tiles) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // next K tile landed; every wave is done with V^T
-      mla_tile_transpose(kt, vt, ctx - (t0 + kTile));
-      __syncthreads();
-    }
-  }
-  if (bad) l = __builtin_nanf("");
-  if (!col_ok) return;
-  mla_store_partial(part_o, part_ml, ((long)r * H + head) * max_splits + split, o, m, l);
+// K-layout unit v (16 bytes, 0 .. 1151) of a page block -> (token t, first dim d0): the
+// inverse of k_page_offset.
+__device__ __forceinline__ void mla_unit_td(int v, int &t, int &d0) {
+  const int c = v >> 6, g = (v >> 4) & 3, a = (v >> 3) & 1, bq = (v >> 2) & 1, cc = v & 3;
+  t = 8 * bq + 4 * a + cc;
+  d0 = 32 * c + 8 * g;
 }
 
 // ---------------------------------------------------------------------------
-// S8, sparse: grid (splits of the selection, H/64, rows), 256 threads.  Tile entries
-// are gathered from their pages into LDS (K layout), then the dense tile routines run
-// with the entry index in place of the position.
+// S8: grid (splits, H/64, rows), 512 threads; SPARSE: splits of the row's selection.
+// Per tile: the scoring wave of each pair computes the scores of its 16 heads and the
+// online-softmax step and hands P and alpha over; both waves of the pair accumulate their
+// half of the value dims.  Tile t+1 is copied into the other LDS buffer (72 direct-to-LDS
+// loads of 1 KB, 9 per wave, each filling 64 consecutive K-layout units of one page slot)
+// while tile t is computed.  Sparse: each wave holds, one entry per lane, the positions of
+// the tile after next and the page ids of the next tile, so no copy waits on a lookup.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void mla_sparse_split_kernel(
+template <bool SPARSE>
+__global__ __launch_bounds__(512) void mla_split_kernel(
     const bf16_t *__restrict__ q, int mode, int row0, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
     const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool, int page_elems,
-    int n_pages, int H, const int32_t *__restrict__ sel, int topk, int split_entries, int ctx_bound,
+    int n_pages, int H, const int32_t *__restrict__ sel, int topk, int split_tokens, int ctx_bound,
     float cscale, float *__restrict__ part_o, float *__restrict__ part_ml, int max_splits) {
-  __shared__ bf16_t kt[4 * kMlaPage];
-  __shared__ bf16_t vt[kMlaDv * kVtRow];
+  __shared__ __attribute__((aligned(16))) bf16_t kt[2][4 * kMlaSlot];
+  __shared__ u32x4 xp[4][2][64];  // P^T operands handed from each pair's scoring wave
+  __shared__ float xa[4][64];     // and its rescale factor, per lane
   const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15;
+  const int pair = wave & 3, half = wave >> 2;  // waves p and p+4 share SIMD p
   int seq, ctx;
   long qrow;
   mla_row(mode, r, row0, ctx_len, cu, start_pos, n_seqs, seq, ctx, qrow);
-  const int n_sel = min(ctx, topk);
-  const int e0 = split * split_entries;
-  if (ctx < 1 || ctx > ctx_bound || e0 >= n_sel) return;  // uniform over the workgroup
-  const int e1 = min(n_sel, e0 + split_entries);
-  const int n_tiles = (e1 - e0 + kTile - 1) / kTile;
+  const int n_all = SPARSE ? min(ctx, topk) : ctx;  // positions, or selected entries
+  const int s0 = split * split_tokens;
+  if (ctx < 1 || ctx > ctx_bound || s0 >= n_all) return;  // uniform over the workgroup
+  const int s1 = min(n_all, s0 + split_tokens);
+  const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
   const int32_t *pt = page_table + (long)seq * page_stride;
-  const int32_t *rsel = sel + (long)r * topk;
-  const int head = 64 * hg + 16 * wave + r16;
+  const int32_t *rsel = SPARSE ? sel + (long)r * topk : nullptr;
+  bool bad = false;
+  // dense: page ids of the split, lane i holding page index s0/16 + i (+64 in pidB);
+  // pages past the context read as page 0 (their tokens are masked)
+  int pidA = 0, pidB = 0;
+  // sparse: per lane = entry of a tile: position (-1: none) and page id
+  int pos1 = -1, pid1 = 0, pos2 = -1;
+  auto entry_pos = [&](int t) {  // position of entry `lane` of tile t
+    const int e = s0 + t * kTile + lane;
+    int p = -1;
+    if (t < n_tiles && e < n_all) {
+      p = rsel[e];
+      if (p < 0 || p >= ctx) {
+        bad = true;  // a listed entry that is not a position of the row
+        p = -1;
+      }
+    }
+    return p;
+  };
+  auto entry_pid = [&](int p) {
+    if (p < 0) return 0;
+    const int id = pt[p / kPage];
+    const bool b = (unsigned)id >= (unsigned)n_pages;
+    bad |= b;
+    return b ? 0 : id;
+  };
+  if (!SPARSE) {
+    const int first = s0 / kPage, last = (ctx - 1) / kPage;
+    const int a = first + lane, b = first + 64 + lane;
+    pidA = pt[min(a, last)];
+    pidB = pt[min(b, last)];
+    bad = (a <= last && (unsigned)pidA >= (unsigned)n_pages) || (b <= last && (unsigned)pidB >= (unsigned)n_pages);
+    pidA = (a <= last && (unsigned)pidA < (unsigned)n_pages) ? pidA : 0;
+    pidB = (b <= last && (unsigned)pidB < (unsigned)n_pages) ? pidB : 0;
+  } else {
+    pos1 = entry_pos(0);
+    pid1 = entry_pid(pos1);
+    pos2 = entry_pos(1);
+  }
+  const int head = 64 * hg + 16 * pair + r16;
   const bool col_ok = head < H;
   bf16x8 qop[kMlaDqk / 32];
-  mla_load_q(qop, q, qrow, H, head, col_ok);
-  float m = neg_inf(), l = 0.f;
-  f32x4 o[kMlaDv / 16];
-#pragma unroll
-  for (int db = 0; db < kMlaDv / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool bad = false;
-  for (int t = 0; t < n_tiles; ++t) {
-    const int t0 = e0 + t * kTile;
-    __syncthreads();  // every wave is done with the previous tile
-    // unit u: entry u / 72 of the tile, latent dims 8 * (u % 72) .. +7
-    for (int u = threadIdx.x; u < kTileUnits; u += kMlaThreads) {
-      const int e = u / (kMlaDqk / 8), d0 = (u % (kMlaDqk / 8)) * 8;
-      const int entry = t0 + e;
-      const int pos = entry < n_sel ? rsel[entry] : -1;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (pos >= 0 && pos < ctx) {
-        const int pid = pt[pos / kPage];
-        if ((unsigned)pid < (unsigned)n_pages)
-          v = ld16(pool + (long)pid * page_elems + k_page_offset(pos % kPage, d0));
-        else
-          bad = true;
-      } else if (entry < n_sel) {
-        bad = true;  // a listed entry that is not a position of the row
+  if (half == 0) mla_load_q(qop, q, qrow, H, head, col_ok);
+
+  // copy tile t into buffer t&1: wave w issues pieces w, w+8, ..; piece pc = page slot
+  // pc / 18, units 64 * (pc % 18) + lane of it
+  constexpr int kPieces = kMlaPage / 512;  // 18 per page slot
+  auto copy_tile = [&](int t) {
+    bf16_t *buf = &kt[t & 1][0];
+    for (int pc = wave; pc < 4 * kPieces; pc += kMlaThreads / 64) {
+      const int ps = pc / kPieces, j = pc % kPieces;
+      const bf16_t *src;
+      if (!SPARSE) {
+        const int idx = 4 * t + ps;  // page index within the split (< 128)
+        const int pid = idx < 64 ? __builtin_amdgcn_readlane(pidA, idx) : __builtin_amdgcn_readlane(pidB, idx - 64);
+        src = pool + (long)pid * page_elems + j * 512 + lane * 8;
+      } else {
+        int tt, d0;
+        mla_unit_td(64 * j + lane, tt, d0);
+        const int e = 16 * ps + tt;  // entry of the tile
+        const int p = __shfl(pos1, e, 64), id = __shfl(pid1, e, 64);
+        src = pool + (long)id * page_elems + (p >= 0 ? k_page_offset(p % kPage, d0) : 0);
       }
-      *reinterpret_cast<u32x4 *>(kt + (e >> 4) * kMlaPage + k_page_offset(e & 15, d0)) = v;
+      bf16_t *dst = buf + ps * kMlaSlot + j * 512;
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
-    __syncthreads();
-    mla_tile_transpose(kt, vt, n_sel - t0);
-    __syncthreads();
-    f32x4 s[4];
-    mla_tile_scores(s, kt, qop);
+  };
+  float m = neg_inf(), l = 0.f;
+  f32x4 o[kMlaDv / 32];
+#pragma unroll
+  for (int b = 0; b < kMlaDv / 32; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  copy_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's pieces of tile t landed
+    __syncthreads();  // every piece of tile t is visible; every wave is done with tile t-1
+    if (t + 1 < n_tiles) {
+      if (SPARSE) {
+        pid1 = entry_pid(pos2);  // positions of tile t+1 were read last iteration
+        pos1 = pos2;
+        pos2 = entry_pos(t + 2);
+      }
+      copy_tile(t + 1);
+    }
+    const int t0 = s0 + t * kTile;
+    const bf16_t *tile = &kt[t & 1][0];
     bf16x8 pop[2];
-    float alpha, m_new, l_new;
-    tile_softmax(s, t0, n_sel - 1, cscale, m, l, pop, alpha, m_new, l_new);
-    mla_tile_values(o, vt, pop, alpha);
-    m = m_new;
-    l = l_new;
+    float alpha;
+    if (half == 0) {
+      f32x4 s[4];
+      mla_tile_scores(s, tile, qop);
+      float m_new, l_new;
+      tile_softmax(s, t0, n_all - 1, cscale, m, l, pop, alpha, m_new, l_new);
+      m = m_new;
+      l = l_new;
+      xp[pair][0][lane] = __builtin_bit_cast(u32x4, pop[0]);
+      xp[pair][1][lane] = __builtin_bit_cast(u32x4, pop[1]);
+      xa[pair][lane] = alpha;
+    }
+    __syncthreads();  // P and alpha of every pair are in LDS
+    if (half == 1) {
+      pop[0] = as_bf16x8(xp[pair][0][lane]);
+      pop[1] = as_bf16x8(xp[pair][1][lane]);
+      alpha = xa[pair][lane];
+    }
+    const int n_live = n_all - t0;
+    if (n_live >= kTile)
+      mla_tile_values<false>(o, tile, half, pop, alpha, n_live);
+    else
+      mla_tile_values<true>(o, tile, half, pop, alpha, n_live);
   }
   bad = __syncthreads_or(bad);
   if (bad) l = __builtin_nanf("");
   if (!col_ok) return;
-  mla_store_partial(part_o, part_ml, ((long)r * H + head) * max_splits + split, o, m, l);
+  mla_store_partial(part_o, part_ml, ((long)r * H + head) * max_splits + split, half, o, m, l);
 }
 
 // ---------------------------------------------------------------------------
@@ -364,15 +456,17 @@ hipError_t launch_mla_split(const MlaAttnArgs &a, hipStream_t st) {
   if (a.sel) {
     const int n_bound = std::min(a.ctx_bound, a.topk);
     dim3 grid((n_bound + a.split_tokens - 1) / a.split_tokens, a.H / 64, a.n_rows);
-    hipLaunchKernelGGL(mla_sparse_split_kernel, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0, a.ctx_len,
+    hipLaunchKernelGGL(mla_split_kernel<true>, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0, a.ctx_len,
                        a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.page_elems,
                        a.n_pages, a.H, a.sel, a.topk, a.split_tokens, a.ctx_bound, a.cscale, a.part_o,
                        a.part_ml, a.max_splits);
   } else {
+    if (a.split_tokens > 2048) return hipErrorInvalidValue;  // two 64-page id registers
     dim3 grid((a.ctx_bound + a.split_tokens - 1) / a.split_tokens, a.H / 64, a.n_rows);
-    hipLaunchKernelGGL(mla_split_kernel, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0, a.ctx_len, a.cu,
-                       a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.page_elems, a.n_pages,
-                       a.H, a.split_tokens, a.ctx_bound, a.cscale, a.part_o, a.part_ml, a.max_splits);
+    hipLaunchKernelGGL(mla_split_kernel<false>, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0, a.ctx_len,
+                       a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.page_elems,
+                       a.n_pages, a.H, nullptr, 0, a.split_tokens, a.ctx_bound, a.cscale, a.part_o,
+                       a.part_ml, a.max_splits);
   }
   return hipGetLastError();
 }
