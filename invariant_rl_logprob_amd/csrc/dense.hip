@@ -108,23 +108,25 @@ __device__ __forceinline__ void kloop(f32x4 (&acc)[MB][NB], const bf16_t *const 
   }
 }
 
-// The lm-head's K loop.  Every output column of vocabulary tile `tile` accumulates its
-// 32-wide K steps in the fixed rotated order r, r+1, ..., nk-1, 0, ..., r-1 with
-// r = (37 * tile) mod nk: one order per column, chosen by the column alone (never by M,
-// the batch or the grid), which spreads the 505 tiles' concurrent weight reads over the
-// HBM channels instead of having every tile read the same K offset at the same time.
+// The K loop with the activation operand staged through LDS, shared by the lm-head and
+// the few-row projections.  Every output column accumulates its 32-wide K steps in the
+// order r, r+1, ..., nk-1, 0, ..., r-1 (rot = r; 0 for the projections, so their order is
+// the plain 0, 32, 64, ... of kloop).  The lm-head picks r = (37 * tile) mod nk per
+// vocabulary tile: one order per column, chosen by the column alone (never by M, the
+// batch or the grid), which spreads the 505 tiles' concurrent weight reads over the HBM
+// channels instead of having every tile read the same K offset at the same time.
 // The activation operand is staged through LDS in chunks of 8 K steps (each of the four
 // waves loads two steps for the whole workgroup); weight operands run PF steps ahead in
-// a register ring.  wp[nb] points at the packed weight block of MFMA block nb (one
-// contiguous 1 KB operand per K step).  All four waves must call this (it synchronises
-// the workgroup).
+// a register ring.  wp[nb] points at MFMA block nb's first operand; step s's operand is
+// WSTEP elements further (512 in the lm-head's packed layout, 32 in a row-major
+// [N, K] matrix).  All four waves must call this (it synchronises the workgroup).
 constexpr int kLdsSteps = 8;
 __device__ __forceinline__ int lm_rot(int tile, int nk) { return (37 * tile) % nk; }
 
-template <int MB, int PF>
-__device__ __forceinline__ void kloop_lm(f32x4 (&acc)[MB][4], const bf16_t *const (&ap)[MB],
-                                         const bf16_t *const (&wp)[4], int K, int rot,
-                                         u32x4 (*lds)[kLdsSteps * MB * 64]) {
+template <int MB, int NB, int PF, int WSTEP>
+__device__ __forceinline__ void kloop_lds(f32x4 (&acc)[MB][NB], const bf16_t *const (&ap)[MB],
+                                          const bf16_t *const (&wp)[NB], int K, int rot,
+                                          u32x4 (*lds)[kLdsSteps * MB * 64]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int S = PF + 1;
   const int nk = K / 32;
@@ -132,12 +134,12 @@ __device__ __forceinline__ void kloop_lm(f32x4 (&acc)[MB][4], const bf16_t *cons
     const int t = s + rot;
     return t >= nk ? t - nk : t;
   };
-  u32x4 rb[S][4];
+  u32x4 rb[S][NB];
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
     if (s < nk) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) rb[s][nb] = ld16(wp[nb] + kidx(s) * 512);
+      for (int nb = 0; nb < NB; ++nb) rb[s][nb] = ld16(wp[nb] + (long)kidx(s) * WSTEP);
     }
   }
   for (int k0 = 0; k0 < nk; k0 += S) {
@@ -161,14 +163,14 @@ __device__ __forceinline__ void kloop_lm(f32x4 (&acc)[MB][4], const bf16_t *cons
         const int kp = ks + PF;
         if (kp < nk) {
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) rb[(j + PF) % S][nb] = ld16(wp[nb] + kidx(kp) * 512);
+          for (int nb = 0; nb < NB; ++nb) rb[(j + PF) % S][nb] = ld16(wp[nb] + (long)kidx(kp) * WSTEP);
         }
         const int buf = (ks / kLdsSteps) & 1, st = ks % kLdsSteps;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const bf16x8 a = as_bf16x8(lds[buf][(st * MB + mb) * 64 + lane]);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(a, as_bf16x8(rb[j][nb]), acc[mb][nb]);
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma(a, as_bf16x8(rb[j][nb]), acc[mb][nb]);
         }
       }
     }
@@ -224,6 +226,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t *__restrict__ A,
             C[(long)row * ldc + col] = f2bf(v);
           }
         }
+      }
+    }
+  }
+}
+
+// S4 for few rows: a workgroup of 4 waves covers 16*MB rows x 64 columns, wave w owning
+// columns 16w .. 16w+15.  The rows' activation operand is staged once per workgroup
+// through LDS and each wave streams its 16 weight rows through a 16-step register ring
+// (kloop_lds with no rotation: the same K order, hence the same bits, as gemm_kernel).
+template <int MB>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(const bf16_t *__restrict__ A, int lda,
+                                                        const bf16_t *__restrict__ W, int ldw,
+                                                        bf16_t *__restrict__ C, int ldc,
+                                                        const bf16_t *__restrict__ R, int ldr, int M, int N, int K) {
+  __shared__ u32x4 lds_a[2][kLdsSteps * MB * 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int m0 = blockIdx.y * 16 * MB;
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const bf16_t *ap[MB];
+  const bf16_t *wp[1];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) ap[mb] = A + (long)min(m0 + 16 * mb + r16, M - 1) * lda + grp * 8;
+  wp[0] = W + (long)min(n0 + r16, N - 1) * ldw + grp * 8;
+  f32x4 acc[MB][1];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop_lds<MB, 1, 15, 32>(acc, ap, wp, K, 0, lds_a);
+  const int col = n0 + r16;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + 16 * mb + 4 * grp + i;
+      if (row < M && col < N) {
+        float v = bf2f(f2bf(acc[mb][0][i]));
+        if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+        C[(long)row * ldc + col] = f2bf(v);
       }
     }
   }
@@ -297,7 +337,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  kloop_lm<MB, 7>(acc, ap, wp, K, lm_rot(tile, K / 32), lds_a);
+  kloop_lds<MB, 4, 7, 512>(acc, ap, wp, K, lm_rot(tile, K / 32), lds_a);
   bool cval[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) cval[nb] = (c0 + 16 * nb + r16) < V;
@@ -425,6 +465,21 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
     nz = (a.K + kchunk - 1) / kchunk;
     if (nz > 1) part = a.part;
     else kchunk = a.K;
+  }
+  if (!part && a.M <= 256 && a.K >= 1024) {
+    // few rows, long K: the rows' operand shared through LDS, 16 columns per wave
+    const int mb = a.M <= 64 ? 1 : (a.M <= 128 ? 2 : 4);
+    dim3 grid((a.N + 63) / 64, (a.M + 16 * mb - 1) / (16 * mb));
+    if (mb == 1)
+      hipLaunchKernelGGL((gemm_rows_kernel<1>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C, a.ldc, a.R,
+                         a.ldr, a.M, a.N, a.K);
+    else if (mb == 2)
+      hipLaunchKernelGGL((gemm_rows_kernel<2>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C, a.ldc, a.R,
+                         a.ldr, a.M, a.N, a.K);
+    else
+      hipLaunchKernelGGL((gemm_rows_kernel<4>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C, a.ldc, a.R,
+                         a.ldr, a.M, a.N, a.K);
+    return hipGetLastError();
   }
   if (a.M <= 16) {
     dim3 grid((a.N + 63) / 64, (a.M + 15) / 16, nz);
