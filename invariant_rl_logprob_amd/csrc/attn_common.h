@@ -143,6 +143,12 @@ struct Half {
 struct FromGlobal {
   static __device__ __forceinline__ u32x4 ld(const bf16_t *p) { return ld16(p); }
 };
+// Global loads with the nontemporal (streaming) cache policy, for data read once per call.
+struct NtGlobal {
+  static __device__ __forceinline__ u32x4 ld(const bf16_t *p) {
+    return __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(p));
+  }
+};
 struct FromLds {
   static __device__ __forceinline__ u32x4 ld(const bf16_t *p) {
     return *(const __attribute__((address_space(3))) u32x4 *)(p);
