@@ -3,6 +3,8 @@
 // instructions whichever kernel computes it.
 #pragma once
 
+#include <utility>
+
 #include "common.h"
 
 namespace ril {
@@ -31,6 +33,9 @@ __device__ __forceinline__ int k_page_offset(int t, int d) {
 //   pos     : the column's query position (tokens after it are masked)
 // Produces the bf16 P^T operands of the two 32-token PV steps (k-slot j of lane group
 // g <-> token 32kc + 8g + j), the rescale factor alpha = exp2(m - m'), and the new (m, l).
+// MASK = false: the caller knows every token of the tile is at or before pos (the mask
+// would keep every score), so the selects are left out; the values are the same.
+template <bool MASK = true>
 __device__ __forceinline__ void tile_softmax(f32x4 (&s)[4], int tile_start, int pos, float cscale,
                                              float m, float l, bf16x8 (&pop)[2], float &alpha,
                                              float &m_new, float &l_new) {
@@ -42,7 +47,7 @@ __device__ __forceinline__ void tile_softmax(f32x4 (&s)[4], int tile_start, int 
     for (int i = 0; i < 4; ++i) {
       const int tok = tile_start + 32 * (mb >> 1) + 8 * grp + 4 * (mb & 1) + i;
       const float x = s[mb][i] * cscale;
-      s[mb][i] = (tok <= pos) ? x : neg_inf();
+      s[mb][i] = (!MASK || tok <= pos) ? x : neg_inf();
       tmax = fmaxf(tmax, s[mb][i]);
     }
   }
@@ -139,6 +144,50 @@ struct Half {
   u32x4 r[D / 8];
 };
 
+// LDS reads the compiler's wait pass does not track (inline asm, no memory clobber): the
+// tiles arrive by direct-to-LDS loads, and a tracked LDS read would make the pass wait
+// for every such load in flight.  Callers order them after the copies they read (vmcnt
+// wait + barrier), wait for them with lds_wait<N> (LDS reads complete in order, so at
+// most the N newest are then pending) and pass each value through settle() before use.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t *)p;
+}
+// base: this lane's LDS byte address; OFF: a byte offset common to all lanes, folded into
+// the instruction (< 65536)
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_rd128(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+// transposing read: lane i of each 16-lane group gets element i%4 of the 8-byte chunks
+// addressed by lanes 4e + i/4 of its group, e = 0..3
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_rdtr(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void settle(T &v) { asm volatile("" : "+v"(v)); }
+
 // Operand loads from global memory or from an LDS copy of the same page blocks.
 struct FromGlobal {
   static __device__ __forceinline__ u32x4 ld(const bf16_t *p) { return ld16(p); }
@@ -209,11 +258,9 @@ __device__ __forceinline__ void lds_settle(Half<D> &t) {
 // scores from the K half, then the online-softmax step (tile_softmax).
 //   qop : B operand of S^T = K Q^T (lane: column lane%16, dims 32c + 8(lane/16) ..)
 //   pos : this lane's column's query position (-1: padding column)
+// The q.k MFMA chains of one tile: s[mb] = sum over c = 0, 1, ... of K_mb,c Q_c^T.
 template <int D>
-__device__ __forceinline__ void attn_scores(const Half<D> &k, int tile_start, const bf16x8 (&qop)[D / 32],
-                                            int pos, float cscale, float m, float l, bf16x8 (&pop)[2],
-                                            float &alpha, float &m_new, float &l_new) {
-  f32x4 s[4];
+__device__ __forceinline__ void attn_score_mfma(const Half<D> &k, const bf16x8 (&qop)[D / 32], f32x4 (&s)[4]) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -221,29 +268,45 @@ __device__ __forceinline__ void attn_scores(const Half<D> &k, int tile_start, co
     for (int c = 0; c < D / 32; ++c) acc = mfma(as_bf16x8(k.r[mb * (D / 32) + c]), qop[c], acc);
     s[mb] = acc;
   }
-  tile_softmax(s, tile_start, pos, cscale, m, l, pop, alpha, m_new, l_new);
+}
+
+template <int D, bool MASK = true>
+__device__ __forceinline__ void attn_scores(const Half<D> &k, int tile_start, const bf16x8 (&qop)[D / 32],
+                                            int pos, float cscale, float m, float l, bf16x8 (&pop)[2],
+                                            float &alpha, float &m_new, float &l_new) {
+  f32x4 s[4];
+  attn_score_mfma<D>(k, qop, s);
+  tile_softmax<MASK>(s, tile_start, pos, cscale, m, l, pop, alpha, m_new, l_new);
 }
 
 // Second half: o = o * alpha + MFMA(bf16 P, V), two 32-token steps in token order.
 //   vbound : V values of tokens >= vbound are read as 0 (beyond any column's context)
 // State per lane = its column's (m, l) and o^T[16db + 4(lane/16) + i].
 // MAYBE_INACTIVE: some column may have pos < tile_start; such columns keep their state.
-template <int D, bool MAYBE_INACTIVE>
+// VMASK = false: the caller knows the tile ends at or before vbound, so no V value needs
+// zeroing.
+template <int D, bool MAYBE_INACTIVE, bool VMASK = true>
 __device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, int pos, int vbound,
                                             const bf16x8 (&pop)[2], float alpha, float m_new, float l_new,
                                             float &m, float &l, f32x4 (&o)[D / 16]) {
   const int grp = (threadIdx.x & 63) >> 4;
-  f32x4 on[D / 16];
+  // o is rescaled and accumulated in place on every path (one register set for o, so
+  // the callers' variants need no copies); inactive columns get their old state back.
+  f32x4 keep[D / 16];
+  if (MAYBE_INACTIVE) {
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) on[db] = o[db] * alpha;
+    for (int db = 0; db < D / 16; ++db) keep[db] = o[db];
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) o[db] = o[db] * alpha;
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
     const int n_valid = vbound - (tile_start + 32 * kc + 8 * grp);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       u32x4 vv = v.r[kc * (D / 16) + db];
-      if (n_valid < 8) vv = keep_first(vv, n_valid);
-      on[db] = mfma(as_bf16x8(vv), pop[kc], on[db]);
+      if (VMASK && n_valid < 8) vv = keep_first(vv, n_valid);
+      o[db] = mfma(as_bf16x8(vv), pop[kc], o[db]);
     }
   }
   if (MAYBE_INACTIVE) {
@@ -253,13 +316,11 @@ __device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, in
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[db][i] = act ? on[db][i] : o[db][i];
+      for (int i = 0; i < 4; ++i) o[db][i] = act ? o[db][i] : keep[db][i];
     }
   } else {
     m = m_new;
     l = l_new;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db] = on[db];
   }
 }
 

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void pack_lm_head_kernel(const bf16_t *__restr
   st16(dst + i * 8, v);
 }
 
-template <int MB, bool NT>
+template <int MB, bool NT, bool ROWS_FAST>
 __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__ Z, int ldz,
                                                       const bf16_t *__restrict__ W, int K, int V,
                                                       const int32_t *__restrict__ target, int M,
@@ -329,8 +329,8 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
   __shared__ u32x4 lds_a[2][kLdsSteps * MB * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
-  const int tile = blockIdx.x;
-  const int m0 = blockIdx.y * 16 * MB;
+  const int tile = ROWS_FAST ? blockIdx.y : blockIdx.x;
+  const int m0 = (ROWS_FAST ? blockIdx.x : blockIdx.y) * 16 * MB;
   const int c0 = tile * kVocabTile + wave * 64;
   const bf16_t *ap[MB];
   const bf16_t *wp[4];
@@ -513,16 +513,25 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int n_vt = (a.V + kVocabTile - 1) / kVocabTile;
   const int mb = a.M <= 16 ? 1 : 4;
-  dim3 grid(n_vt, (a.M + 16 * mb - 1) / (16 * mb));
-  // Weights streamed with the nontemporal policy up to two row tiles (measured: 192 -> 171 us
-  // at 64 rows, 369 -> 329 us at 128 rows on the 4096 x 129280 head).
-  const bool nt = grid.y <= 2;
-#define RIL_LMH(MB_, NT_) \
-  hipLaunchKernelGGL((lm_head_kernel<MB_, NT_>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V, a.target, a.M, \
-                     a.part, a.tgt_logit, n_vt)
-  if (mb == 1) { if (nt) RIL_LMH(1, true); else RIL_LMH(1, false); }
-  else { if (nt) RIL_LMH(4, true); else RIL_LMH(4, false); }
-#undef RIL_LMH
+  const int n_rt = (a.M + 16 * mb - 1) / (16 * mb);
+  // Up to two row tiles the weights are read once (twice) and streamed with the
+  // nontemporal policy (measured: 192 -> 171 us at 64 rows, 369 -> 326 us at 128 rows on
+  // the 4096 x 129280 head).  With more row tiles the grid runs the row tiles of one
+  // vocabulary tile back to back, so its weight tile is read from HBM once and served
+  // from the caches to the other row tiles.  Neither choice changes a column's K order.
+  if (n_rt <= 2) {
+    dim3 grid(n_vt, n_rt);
+    if (mb == 1)
+      hipLaunchKernelGGL((lm_head_kernel<1, true, false>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
+                         a.target, a.M, a.part, a.tgt_logit, n_vt);
+    else
+      hipLaunchKernelGGL((lm_head_kernel<4, true, false>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
+                         a.target, a.M, a.part, a.tgt_logit, n_vt);
+  } else {
+    dim3 grid(n_rt, n_vt);
+    hipLaunchKernelGGL((lm_head_kernel<4, false, true>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
+                       a.target, a.M, a.part, a.tgt_logit, n_vt);
+  }
   return hipGetLastError();
 }
 

@@ -111,50 +111,6 @@ __device__ __forceinline__ void mla_load_q(bf16x8 (&qop)[kMlaDqk / 32], const bf
   }
 }
 
-// LDS reads the compiler's wait pass does not track (inline asm, no memory clobber): the
-// tiles arrive by direct-to-LDS loads, and a tracked LDS read would make the pass wait
-// for every such load in flight.  Callers order them after the copies they read (vmcnt
-// wait + barrier), wait for them with lds_wait<N> (LDS reads complete in order, so at
-// most the N newest are then pending) and pass each value through settle() before use.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t lds_addr(const bf16_t *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t *)p;
-}
-// base: this lane's LDS byte address; OFF: a byte offset common to all lanes, folded into
-// the instruction (< 65536)
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_rd128(uint32_t base) {
-  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
-  return r;
-}
-// transposing read: lane i of each 16-lane group gets element i%4 of the 8-byte chunks
-// addressed by lanes 4e + i/4 of its group, e = 0..3
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_rdtr(uint32_t base) {
-  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
-  return r;
-}
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-template <int N>
-__device__ __forceinline__ void lds_wait() {
-  static_assert(N == 0 || N == 4, "add the count");
-  if constexpr (N == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
-}
-template <typename T>
-__device__ __forceinline__ void settle(T &v) { asm volatile("" : "+v"(v)); }
 
 // S^T = K Q^T for the 64-token tile in LDS (K layout, 4 page slots).  K step outermost:
 // each step's four M-block operands are read while the previous step's MFMAs run; every

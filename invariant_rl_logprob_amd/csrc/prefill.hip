@@ -142,11 +142,38 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
   }
   if (NBUF - 1 < n_tiles) fetch_ids(NBUF - 1, idn);
 
+  // This lane's LDS byte addresses of its K and V operands in buffer 0 (the Half layouts
+  // of load_k / load_v over the 4 page slots); every read adds a constant offset.
+  const int r16 = lane & 15, rq = r16 >> 2, ri = r16 & 3;
+  const uint32_t kv0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t *)&kv[0][0];
+  const uint32_t kbase = kv0 + 2 * ((rq >> 1) * kSlot + grp * 128 + (rq & 1) * 32 + ri * 8);
+  const uint32_t vbase = kv0 + 2 * ((grp >> 1) * kSlot + 16 * D + (grp & 1) * (8 * D) + r16 * 8);
+  auto lds_tile_k = [&](Half<D> &t, uint32_t base) {
+    static_for<2>([&](auto kc_) {
+      static_for<2>([&](auto h_) {
+        static_for<D / 32>([&](auto c_) {
+          constexpr int kc = decltype(kc_)::value, h = decltype(h_)::value, c = decltype(c_)::value;
+          t.r[(2 * kc + h) * (D / 32) + c] = lds_rd128<2 * (2 * kc * kSlot + h * 64 + c * 512)>(base);
+        });
+      });
+    });
+  };
+  auto lds_tile_v = [&](Half<D> &t, uint32_t base) {
+    static_for<2>([&](auto kc_) {
+      static_for<D / 16>([&](auto db_) {
+        constexpr int kc = decltype(kc_)::value, db = decltype(db_)::value;
+        t.r[kc * (D / 16) + db] = lds_rd128<2 * (2 * kc * kSlot + db * 128)>(base);
+      });
+    });
+  };
+
   float M = neg_inf(), L = 0.f, m = neg_inf(), l = 0.f;
   float O[D / 4];
   f32x4 o[D / 16];
 #pragma unroll
   for (int e = 0; e < D / 4; ++e) O[e] = 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int T = 0; T < n_tiles; ++T) {
     // tile T landed (at most `ahead` later tiles still in flight), then the barrier:
     // every wave's pieces are visible and every wave is done with tile T-1's buffer
@@ -161,45 +188,56 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     }
     const int t0 = T * kTile;
     const int s0 = t0 - t0 % split_tokens;
-    if (t0 == s0) {
+    if (t0 <= w_max) {
+      const uint32_t boff = (uint32_t)(T % NBUF) * (4 * kSlot * 2);
+      Half<D> hk, hv;
+      lds_tile_k(hk, kbase + boff);
+      lds_wait<0>();
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) settle(hk.r[i]);
+      f32x4 sc[4];
+      attn_score_mfma<D>(hk, qop, sc);
+      lds_tile_v(hv, vbase + boff);  // lands while the softmax runs
+      bf16x8 pop[2];
+      float alpha, m_new, l_new;
+      // Uniform shortcuts that leave every value unchanged: no causal select when the whole
+      // tile is at or before the wave's first position, no V zeroing before the last tile.
+      if (t0 + kTile - 1 <= w_min)
+        tile_softmax<false>(sc, t0, pos, cscale, m, l, pop, alpha, m_new, l_new);
+      else
+        tile_softmax<true>(sc, t0, pos, cscale, m, l, pop, alpha, m_new, l_new);
+      lds_wait<0>();
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) settle(hv.r[i]);
+      if (t0 > w_min)
+        attn_values<D, true>(hv, t0, pos, p_max + 1, pop, alpha, m_new, l_new, m, l, o);
+      else if (t0 + kTile > p_max + 1)
+        attn_values<D, false, true>(hv, t0, pos, p_max + 1, pop, alpha, m_new, l_new, m, l, o);
+      else
+        attn_values<D, false, false>(hv, t0, pos, p_max + 1, pop, alpha, m_new, l_new, m, l, o);
+    }
+    // end of a split: fold its state into the merged state of every column it reached,
+    // then start the next split from the empty state
+    if (t0 + kTile >= min(s0 + split_tokens, p_max + 1)) {
+      if (s0 <= pos) {
+        float os[D / 4];
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) os[db * 4 + i] = o[db][i];
+        if (s0 == 0) {
+          M = m;
+          L = l;
+#pragma unroll
+          for (int e = 0; e < D / 4; ++e) O[e] = os[e];
+        } else {
+          merge_state<D / 4>(M, L, O, m, l, os);
+        }
+      }
       m = neg_inf();
       l = 0.f;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (t0 <= w_max) {
-      const bf16_t *pg[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pg[k] = &kv[T % NBUF][k * kSlot];
-      Half<D> hk;
-      load_k<D, FromLdsUntracked>(hk, pg);
-      lds_settle<D>(hk);
-      bf16x8 pop[2];
-      float alpha, m_new, l_new;
-      attn_scores<D>(hk, t0, qop, pos, cscale, m, l, pop, alpha, m_new, l_new);
-      Half<D> hv;
-      load_v<D, FromLdsUntracked>(hv, pg);
-      lds_settle<D>(hv);
-      if (t0 <= w_min)
-        attn_values<D, false>(hv, t0, pos, p_max + 1, pop, alpha, m_new, l_new, m, l, o);
-      else
-        attn_values<D, true>(hv, t0, pos, p_max + 1, pop, alpha, m_new, l_new, m, l, o);
-    }
-    // end of a split: fold its state into the merged state of every column it reached
-    if (t0 + kTile >= min(s0 + split_tokens, p_max + 1) && s0 <= pos) {
-      float os[D / 4];
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) os[db * 4 + i] = o[db][i];
-      if (s0 == 0) {
-        M = m;
-        L = l;
-#pragma unroll
-        for (int e = 0; e < D / 4; ++e) O[e] = os[e];
-      } else {
-        merge_state<D / 4>(M, L, O, m, l, os);
-      }
     }
   }
   // a page id outside the pool seen by any wave marks the whole workgroup's rows NaN
