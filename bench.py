@@ -68,22 +68,27 @@ def blas_threads():
 
 
 def timed_steps(launch, steps, warmup):
-    """Warm up, then time `steps` launches between two synchronisations with HIP events
-    on the launch stream; the library's trace hook times each kernel on that stream."""
+    """Warm up, then time `steps` launches between two synchronisations with HIP events on
+    the launch stream: that pass gives the step time.  A second pass of `steps` launches runs
+    with the library's trace hook (HIP events around every kernel on that stream) and gives
+    each kernel's average duration; the hook's events add about 10% to a step, so the step
+    time never comes from the traced pass."""
     import torch
     import invariant_rl_logprob_amd as ril
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    ril.ril_trace_enable(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for _ in range(steps):
         launch()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    ril.ril_trace_enable(True)
+    for _ in range(steps):
+        launch()
+    torch.cuda.synchronize()
     kern = {}
     for kid, name in enumerate(ril.KERNEL_NAMES):
         tot, cnt = ril.ril_trace_read(kid)
@@ -91,6 +96,74 @@ def timed_steps(launch, steps, warmup):
             kern[name] = {"avg_us": 1e3 * tot / cnt, "launches": cnt}
     ril.ril_trace_enable(False)
     return ms, kern
+
+
+def time_launch(launch, steps, warmup):
+    """ms per launch over `steps` launches between two HIP events (no per-kernel trace)."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        launch()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def graph_leg(sess, seqs, c, kw, eager_launch, eager_out, args):
+    """The same decode step captured in a HIP graph: replay time next to the eager call's
+    (both timed without the trace hook), and whether the replay's bits equal the eager ones."""
+    import numpy as np
+    import torch
+    def host_us(launch, n=20):  # host time to enqueue one step (the GPU queue never fills at n)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            launch()
+        dt = time.perf_counter() - t
+        torch.cuda.synchronize()
+        return 1e6 * dt / n
+
+    g = sess.decode_graph(seqs, max(c), ctx=c, **kw)
+    try:
+        eager_ms = time_launch(eager_launch, args.steps, args.warmup)
+        e_bits = eager_out.cpu().view(torch.int32).numpy().copy()
+        graph_ms = time_launch(g.replay, args.steps, args.warmup)
+        equal = bool(np.array_equal(g.out.cpu().view(torch.int32).numpy(), e_bits))
+        eager_host, graph_host = host_us(eager_launch), host_us(g.replay)
+    finally:
+        g.close()
+    return {"rows": len(seqs), "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
+            "graph_speedup": round(eager_ms / graph_ms, 3), "eager_host_enqueue_us": round(eager_host, 1),
+            "graph_host_enqueue_us": round(graph_host, 1), "bitwise_equal_to_eager": equal}
+
+
+def tiny_graph_leg(args):
+    """cfg-1 decoder (token input, one layer, 4 sequences): one decode step eager vs graph."""
+    import torch
+    import workloads as wl
+    from invariant_rl_logprob_amd import RIL_INPUT_TOKENS
+    from invariant_rl_logprob_amd.session import Session
+    W = wl.TINY
+    wts = wl.tiny_weights(W, device="cuda")
+    toks = [wl.tiny_tokens(i, W, device="cuda") for i in range(len(W.lengths))]
+    s = Session(n_q_heads=W.n_q_heads, n_kv_heads=W.n_kv_heads, head_dim=W.head_dim, vocab=W.vocab,
+                d_head=W.d_model, d_model=W.d_model, w_lm=wts["w_lm"], embed=wts["embed"], w_qkv=wts["w_qkv"],
+                w_o=wts["w_o"], norm_attn=wts["norm_attn"], norm_final=wts["norm_final"], max_rows=8,
+                max_tokens=512, max_ctx=max(W.lengths), pool_pages=4096, softmax_scale=1.0 / math.sqrt(W.head_dim),
+                rms_eps=W.rms_eps, shuffle_seed=3, input_mode=RIL_INPUT_TOKENS)
+    P = W.prompt_tokens
+    ids = list(range(len(W.lengths)))
+    seqs = [("t", i) for i in ids]
+    s.prefill(seqs, [0] * len(ids), targets=[toks[i][1:P + 1] for i in ids], tokens=[toks[i][:P] for i in ids])
+    tok = torch.stack([toks[i][P] for i in ids]).to(torch.int32)
+    tgt = torch.stack([toks[i][P + 1] for i in ids]).to(torch.int32)
+    c = [P + 1] * len(ids)
+    launch, out = s.prepare_decode(seqs, c, targets=tgt, tokens=tok)
+    return graph_leg(s, seqs, c, {"targets": tgt, "tokens": tok}, launch, out, args)
 
 
 def diff_check(case, rows, n=16):
@@ -205,6 +278,13 @@ def bench_gqa(args):
         x1 = comparator(case.sess, prepare, rows, dec[:, -1], kv_bytes + q_bytes + out_bytes, (256, 512, 1024), args)
         x1["invariant_over_x1_best"] = round(x1["best"]["ms_per_step"] / ms_step, 4)
 
+    graph = None
+    if not args.no_graph:
+        graph = {"gqa_decode_b64": graph_leg(case.sess, [("d", r) for r in rows], c,
+                                             {"targets": tgt, "q": q, "k": k, "v": v}, launch, out, args),
+                 "tiny_decoder": tiny_graph_leg(args)}
+        log(f"graph: {graph}")
+
     cpu = None
     if not args.no_cpu and args.cpu_rows > 0:
         import oracle  # the cpu_baseline leg: the fp64 oracle as it stands
@@ -231,7 +311,7 @@ def bench_gqa(args):
         "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "lm_head_gbps": round(lm_gbps, 1), "diff": diff, "timed_step_equals_checked_decode": last_equal,
         "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
-        "comparator_x1": x1, "roofline": roof, "cpu_baseline": cpu,
+        "comparator_x1": x1, "hip_graph": graph, "roofline": roof, "cpu_baseline": cpu,
     }
 
 
@@ -493,6 +573,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=12, help="rows of the oracle timing sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-comparator", action="store_true", help="skip the shape-derived comparator leg")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay leg")
     ap.add_argument("--long-all-chunks", action="store_true", help="long_mix: also run the 512-token chunks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")

@@ -247,6 +247,32 @@ ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const ril_prefil
 ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
                                     float *logprob_out, void *ws, size_t ws_bytes, void *stream);
 
+/* HIP-graph capture of one decode step, for steps whose launch overhead matters
+ * (small batches, short contexts).
+ *
+ * ril_decode_graph_create records the kernels ril_decode_step_logprobs(m, kv,
+ * b, logprob_out, ws, ws_bytes, stream) would enqueue into a graph, on a
+ * private stream, and instantiates it; nothing runs at creation.  The graph
+ * holds the batch's device pointers and its host values (n_rows,
+ * max_ctx_bound, page_stride), which size the grids.  Each replay
+ * (ril_graph_launch) reads the device buffers as they are at replay time, so
+ * the caller may rewrite in place, between replays, ctx_len (each <= the
+ * captured max_ctx_bound), page_table, target_ids, token_ids / q / k / v, the
+ * weights and the KV pool; n_rows and the addresses stay as captured.  A
+ * replay gives bitwise the logprobs of the uncaptured call on the same inputs
+ * (the same kernels with the same arguments).  Replays on one stream run in
+ * order; the workspace is shared with every other call that uses `ws`, so a
+ * replay and another call on the same workspace must be ordered (same stream).
+ * Errors: the arguments are checked as ril_decode_step_logprobs checks them
+ * (RIL_EINVAL / RIL_ERANGE, nothing captured); a capture or instantiation
+ * failure returns RIL_EHIP.  *out receives the graph, to be released with
+ * ril_graph_destroy (which must not run while a replay is pending). */
+typedef struct ril_graph ril_graph;
+ril_status ril_decode_graph_create(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                   float *logprob_out, void *ws, size_t ws_bytes, ril_graph **out);
+ril_status ril_graph_launch(ril_graph *g, void *stream);
+void ril_graph_destroy(ril_graph *g);
+
 /* The shared KV write path alone (S5): writes the batch's k/v (QKV layout
  * of ril_prefill_batch; target_ids, token_ids and q are ignored) into the
  * pages, nothing else.  Used to lay down history that no logprob is asked

@@ -86,6 +86,10 @@ _prefill = _sig("ril_prefill_logprobs", _c_int,
 _decode = _sig("ril_decode_step_logprobs", _c_int,
                [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp, ctypes.c_size_t, _vp])
 _kv_write = _sig("ril_kv_write", _c_int, [_vp, _vp, ctypes.POINTER(ril_prefill_batch), _vp])
+_graph_create = _sig("ril_decode_graph_create", _c_int,
+                     [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp, ctypes.c_size_t, ctypes.POINTER(_vp)])
+_graph_launch = _sig("ril_graph_launch", _c_int, [_vp, _vp])
+_graph_destroy = _sig("ril_graph_destroy", None, [_vp])
 _last_error = _sig("ril_last_error", ctypes.c_char_p, [])
 _set_policy = _sig("ril_set_policy", _c_int, [_vp, _c_int, _c_int])
 _trace_enable = _sig("ril_trace_enable", _c_int, [_c_int])
@@ -97,7 +101,7 @@ EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
             "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_set_policy", "ril_trace_enable",
-            "ril_trace_read")
+            "ril_trace_read", "ril_decode_graph_create", "ril_graph_launch", "ril_graph_destroy")
 
 # kernel ids of the trace hook
 RIL_K_KV_WRITE, RIL_K_ATTN_SPLIT, RIL_K_ATTN_MERGE, RIL_K_ATTN_PREFILL = 0, 1, 2, 3
@@ -229,6 +233,22 @@ def ril_decode_step_logprobs(model: int, kv: int, batch: ril_decode_batch, logpr
                              stream=None) -> None:
     _check(_decode(model, kv, ctypes.byref(batch), _ptr(logprob_out), _ptr(ws),
                    ws.numel() * ws.element_size(), _stream(stream)), "ril_decode_step_logprobs")
+
+
+def ril_decode_graph_create(model: int, kv: int, batch: ril_decode_batch, logprob_out, ws) -> int:
+    """Capture one decode step into a HIP graph (nothing runs); returns the graph handle."""
+    g = _vp()
+    _check(_graph_create(model, kv, ctypes.byref(batch), _ptr(logprob_out), _ptr(ws),
+                         ws.numel() * ws.element_size(), ctypes.byref(g)), "ril_decode_graph_create")
+    return g.value
+
+
+def ril_graph_launch(graph: int, stream=None) -> None:
+    _check(_graph_launch(graph, _stream(stream)), "ril_graph_launch")
+
+
+def ril_graph_destroy(graph: int) -> None:
+    _graph_destroy(graph)
 
 
 def ril_kv_write(model: int, kv: int, batch: ril_prefill_batch, stream=None) -> None:

@@ -369,9 +369,12 @@ void trace_drain() {  // caller holds g_tr_mu
 }
 
 // Launch `fn` and, while tracing, bracket it with events on `st`.
+// Set while this thread records a graph: launches are captured, never bracketed.
+thread_local bool g_capturing = false;
+
 template <typename F>
 hipError_t traced(int k, hipStream_t st, F fn) {
-  if (!g_tr_on) return fn();
+  if (!g_tr_on || g_capturing) return fn();
   std::lock_guard<std::mutex> lk(g_tr_mu);
   hipEvent_t a = trace_event(), b = trace_event();
   const bool ra = a && hipEventRecord(a, st) == hipSuccess;
@@ -610,8 +613,8 @@ extern "C" ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const
   return run_head(m, T, b->target_ids, logprob_out, ws, st);
 }
 
-extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
-                                               float *logprob_out, void *ws, size_t ws_bytes, void *stream) {
+static ril_status decode_enqueue(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                 float *logprob_out, void *ws, size_t ws_bytes, void *stream) {
   if (!b) return fail(RIL_EINVAL, "decode_step_logprobs: null batch");
   ril_status s = check_common(m, kv, ws, ws_bytes, b->max_ctx_bound, b->page_table, b->page_stride,
                               "decode_step_logprobs");
@@ -672,4 +675,71 @@ extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, c
   RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_attn_split(ad, st));
   RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_attn_merge(ad, st));
   return run_head(m, R, b->target_ids, logprob_out, ws, st);
+}
+
+extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                               float *logprob_out, void *ws, size_t ws_bytes, void *stream) {
+  return decode_enqueue(m, kv, b, logprob_out, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// HIP-graph capture of a decode step
+// ---------------------------------------------------------------------------
+
+struct ril_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" ril_status ril_decode_graph_create(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                              float *logprob_out, void *ws, size_t ws_bytes, ril_graph **out) {
+  if (!out) return fail(RIL_EINVAL, "decode_graph_create: null out");
+  *out = nullptr;
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return fail(RIL_EHIP, "decode_graph_create: stream: %s", hipGetErrorString(e));
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(RIL_EHIP, "decode_graph_create: begin capture: %s", hipGetErrorString(e));
+  }
+  g_capturing = true;
+  const ril_status s = decode_enqueue(m, kv, b, logprob_out, ws, ws_bytes, cs);
+  g_capturing = false;
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cs, &graph);
+  (void)hipStreamDestroy(cs);
+  if (s != RIL_OK) {  // the argument check's message stands
+    if (graph) (void)hipGraphDestroy(graph);
+    return s;
+  }
+  if (e != hipSuccess || !graph) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return fail(RIL_EHIP, "decode_graph_create: end capture: %s", hipGetErrorString(e));
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(RIL_EHIP, "decode_graph_create: instantiate: %s", hipGetErrorString(e));
+  }
+  ril_graph *g = new ril_graph;
+  g->graph = graph;
+  g->exec = exec;
+  *out = g;
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_graph_launch(ril_graph *g, void *stream) {
+  if (!g || !g->exec) return fail(RIL_EINVAL, "graph_launch: null graph");
+  const hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "graph_launch: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
+
+extern "C" void ril_graph_destroy(ril_graph *g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
 }

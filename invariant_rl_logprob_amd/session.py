@@ -14,7 +14,7 @@ from typing import Dict, List, Optional, Sequence
 import torch
 
 from . import (RIL_ATTN_GQA, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch, make_prefill_batch,
-               ril_decode_step_logprobs, ril_kv_alloc, ril_kv_assign, ril_kv_free, ril_kv_page_bytes,
+               ril_decode_graph_create, ril_decode_step_logprobs, ril_graph_destroy, ril_graph_launch, ril_kv_alloc, ril_kv_assign, ril_kv_free, ril_kv_page_bytes,
                ril_kv_release, ril_kv_write, ril_lm_head_packed_bytes, ril_model_create, ril_model_desc,
                ril_model_destroy, ril_pack_lm_head, ril_prefill_logprobs, ril_set_policy,
                ril_workspace_bytes, ril_ws_attn_offset)
@@ -195,8 +195,66 @@ class Session:
         launch.keep = keep  # the descriptor's tensors live as long as the launcher
         return launch, out
 
+    def decode_graph(self, seqs, ctx_bound: int, *, ctx, targets, q=None, k=None, v=None, tokens=None,
+                     q_index=None, k_index=None) -> "DecodeGraph":
+        """Capture a decode step of rows seqs into a HIP graph over fixed buffers (pages are
+        assigned up to ctx_bound now); replay it with DecodeGraph.run."""
+        return DecodeGraph(self, seqs, ctx_bound, ctx=ctx, targets=targets, q=q, k=k, v=v, tokens=tokens,
+                           q_index=q_index, k_index=k_index)
+
     def attn_out(self, rows: int) -> torch.Tensor:
         """bf16 [rows, Hq, D] attention output of the last call (a workspace view)."""
         off = ril_ws_attn_offset(self.model)
         n = rows * self.H * self.D
         return self.ws[off: off + 2 * n].view(torch.bfloat16).view(rows, self.H, self.D)
+
+
+class DecodeGraph:
+    """One captured decode step (ril_decode_graph_create) and the fixed device buffers its
+    replays read.  run() copies a step's inputs into those buffers on the current stream and
+    replays the graph there: the same kernels, with the same arguments, as Session.decode."""
+
+    def __init__(self, sess: Session, seqs, ctx_bound: int, *, ctx, targets, q, k, v, tokens, q_index, k_index):
+        self.sess = sess
+        b, keep = sess._decode_batch(seqs, ctx, targets, q, k, v, tokens, q_index, k_index, None, ctx_bound)
+        # the batch's tensors are fresh copies, owned here: replays read them in place
+        self.buf = {key: (t.clone() if t is not None else None) for key, t in keep.items()}
+        self.batch = make_decode_batch(ctx_len=self.buf["ctx"], page_table=self.buf["pt"], max_ctx_bound=ctx_bound,
+                                       target_ids=self.buf["tgt"], token_ids=self.buf["tok"], q=self.buf["q"],
+                                       k=self.buf["k"], v=self.buf["v"], q_index=self.buf["qi"],
+                                       k_index=self.buf["ki"], selected_out=None)
+        self.out = torch.empty(len(seqs), dtype=torch.float32, device=sess.device)
+        self.seqs = list(seqs)
+        self.bound = int(ctx_bound)
+        self.handle = ril_decode_graph_create(sess.model, sess.kv, self.batch, self.out, sess.ws)
+
+    def run(self, ctx, *, targets, q=None, k=None, v=None, tokens=None, q_index=None, k_index=None) -> torch.Tensor:
+        """Replay with new inputs; returns the (reused) fp32 [rows] output buffer."""
+        ctx = [int(c) for c in ctx]
+        if len(ctx) != len(self.seqs) or max(ctx) > self.bound or min(ctx) < 1:
+            raise ValueError(f"graph captured for {len(self.seqs)} rows with contexts <= {self.bound}")
+        for s_, c in zip(self.seqs, ctx):
+            self.sess.ensure(s_, c)
+        self.buf["pt"].copy_(self.sess.page_table(self.seqs, self.bound))  # same stride, pages as of now
+        self.buf["ctx"].copy_(torch.tensor(ctx, dtype=torch.int32), non_blocking=False)
+        self.buf["tgt"].copy_(targets.to(torch.int32))
+        for key, t in (("tok", tokens), ("q", q), ("k", k), ("v", v), ("qi", q_index), ("ki", k_index)):
+            if t is not None:
+                self.buf[key].copy_(t)
+        ril_graph_launch(self.handle, torch.cuda.current_stream(self.sess.device).cuda_stream)
+        return self.out
+
+    def replay(self) -> None:
+        """Replay on the current stream with the buffers as they are (for timed loops)."""
+        ril_graph_launch(self.handle, torch.cuda.current_stream(self.sess.device).cuda_stream)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            ril_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
