@@ -427,3 +427,83 @@ def test_planted_residual_dropped_is_caught():
         p["w_o"] = np.asarray(params["w_o"]) * 0.0
         return om.tiny_decoder_decode(p, tokens, targets, n_prompt, Hq, Hkv, D, eps)
     assert not check_tiny_prefill_vs_decode(oracle.tiny_decoder_prefill, bad_decode)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 storage of the KV cache (oracle/fp8.py)
+# ---------------------------------------------------------------------------
+
+from oracle import fp8 as of8  # noqa: E402
+
+
+def _all_bf16_values():
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    return bits.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_e4m3_codes_fixed_by_the_format():
+    cases = [(1.0, 0x38), (448.0, 0x7E), (-2.0, 0xC0), (0.5, 0x30), (3.0, 0x44), (2.0 ** -6, 0x08),
+             (2.0 ** -9, 0x01), (7 * 2.0 ** -9, 0x07), (2.0 ** -4, 0x18), (240.0, 0x77), (-448.0, 0xFE),
+             (0.0, 0x00), (-0.0, 0x80),
+             (1.0625, 0x38),            # tie between 1 (M=0) and 1.125 (M=1): even
+             (1.1875, 0x3A),            # tie between 1.125 (M=1) and 1.25 (M=2): even
+             (2.0 ** -10, 0x00),        # tie between 0 and 2^-9: even (0)
+             (3 * 2.0 ** -10, 0x02),    # tie between 2^-9 and 2^-8: even
+             (1.0625 + 2.0 ** -20, 0x39),
+             (464.0, 0x7E), (465.0, 0x7E), (1e30, 0x7E), (np.inf, 0x7E), (-np.inf, 0xFE)]  # satfinite
+    got = of8.e4m3_encode(np.array([v for v, _ in cases]))
+    assert [int(c) for c in got] == [c for _, c in cases]
+    assert int(of8.e4m3_encode(np.array([np.nan]))[0]) & 0x7F == 0x7F
+
+
+def test_e4m3_decode_all_codes_by_field_formula():
+    vals = of8.e4m3_decode(np.arange(256, dtype=np.uint8))
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            assert np.isnan(vals[c])
+            continue
+        mag = m * 2.0 ** -9 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8)
+        assert vals[c] == (-mag if s else mag), c
+    pos = vals[:127]
+    assert np.all(np.diff(pos) > 0) and pos[-1] == 448.0
+
+
+def test_e4m3_roundtrip_of_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(of8.e4m3_encode(of8.e4m3_decode(codes)), codes)
+
+
+def test_e4m3_matches_torch_on_every_bf16_value_within_range():
+    x = _all_bf16_values()
+    keep = np.isfinite(x) & (np.abs(x) <= 464.0)
+    ref = torch.from_numpy(x[keep]).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(of8.e4m3_encode(x[keep]), ref)
+
+
+def test_e4m3_is_nearest_with_even_ties():
+    pos = of8.e4m3_decode(np.arange(127, dtype=np.uint8))  # 0 .. 448
+    mids = (pos[:-1] + pos[1:]) / 2
+    lo_even = (np.arange(126) % 2) == 0                    # code parity = mantissa parity
+    want = np.where(lo_even, np.arange(126), np.arange(1, 127))
+    assert np.array_equal(of8.e4m3_encode(mids), want)
+    eps = np.minimum(np.diff(pos), 1.0) * 1e-3
+    assert np.array_equal(of8.e4m3_encode(mids - eps), np.arange(126))
+    assert np.array_equal(of8.e4m3_encode(mids + eps), np.arange(1, 127))
+
+
+def test_kv_fp8_scale_is_exact_power_of_two():
+    x = _all_bf16_values()
+    x = x[np.isfinite(x) & (np.abs(x) < 1e3)]
+    for s in (-3, 0, 2):
+        assert np.array_equal(of8.kv_fp8_store(x, s), of8.e4m3_encode(x * 2.0 ** -s))
+        back = of8.kv_fp8_roundtrip(x, s)
+        assert np.array_equal(back, of8.e4m3_decode(of8.e4m3_encode(x * 2.0 ** -s)) * 2.0 ** s)
+        assert np.array_equal(on.bf16(back[np.isfinite(back)]), back[np.isfinite(back)])  # bf16-exact
+
+
+def test_planted_e4m3_truncation_is_caught():
+    # a planted mistake: truncating instead of rounding must break a pin
+    x = np.array([1.0625 + 2.0 ** -20, 1.1875])
+    trunc = np.floor(x * 8) / 8
+    assert not np.array_equal(of8.e4m3_encode(trunc), of8.e4m3_encode(x))
