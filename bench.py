@@ -236,7 +236,11 @@ def comparator(sess, prepare, rows, ref_last, attn_bytes, splits, args):
 # GQA decode, 64 rows
 # ---------------------------------------------------------------------------
 
-def bench_gqa(args):
+def bench_gqa_fp8(args):
+    return bench_gqa(args, fp8=True)
+
+
+def bench_gqa(args, fp8=False):
     import numpy as np
     import torch
     import workloads as wl
@@ -245,7 +249,8 @@ def bench_gqa(args):
     w = wl.GQA_DECODE_B64
     rows = list(range(w.rows))
     t0 = time.time()
-    case = GQACase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_tokens=w.rows * 16)
+    case = GQACase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_tokens=w.rows * 16,
+                   kv_dtype=1 if fp8 else 0)
     ctx = [case.ctx(r) for r in rows]
     log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
     dec, diff = diff_check(case, rows)
@@ -257,7 +262,7 @@ def bench_gqa(args):
                                      dec[:, -1].cpu().view(torch.int32).numpy()))
 
     Hkv, D, Hq = w.n_kv_heads, w.head_dim, w.n_q_heads
-    kv_bytes = sum(ctx) * Hkv * D * 2 * 2           # each K/V byte once per kv head
+    kv_bytes = sum(ctx) * Hkv * D * 2 * (1 if fp8 else 2)  # each K/V byte once per kv head
     q_bytes = len(rows) * Hq * D * 2
     out_bytes = len(rows) * Hq * D * 2
     lm_bytes = w.vocab * w.d_head * 2 + len(rows) * w.d_head * 2
@@ -292,8 +297,11 @@ def bench_gqa(args):
         w_lm_cpu = case.head["w_lm"].cpu()
         host = {r: {key: case.data[r][key].cpu() for key in ("q", "k", "v", "target")} for r in sample}
         t1 = time.time()
-        got = [oracle.gqa_row_logprob(host[r]["q"][-1], host[r]["k"][: case.ctx(r)], host[r]["v"][: case.ctx(r)],
-                                      1.0 / math.sqrt(D), w_lm_cpu, int(host[r]["target"][-1]), w.rms_eps)
+        def kv(x):  # the FP8 cache gives back its decode of the stored codes
+            return oracle.kv_fp8_roundtrip(oracle.widen(x), 0) if fp8 else x
+        got = [oracle.gqa_row_logprob(host[r]["q"][-1], kv(host[r]["k"][: case.ctx(r)]),
+                                      kv(host[r]["v"][: case.ctx(r)]), 1.0 / math.sqrt(D), w_lm_cpu,
+                                      int(host[r]["target"][-1]), w.rms_eps)
                for r in sample]
         secs = time.time() - t1
         cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
@@ -304,8 +312,10 @@ def bench_gqa(args):
 
     return {
         "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
-        "config": {"workload": "gqa_decode_b64: 64 paged decode rows, 32 q / 8 kv heads, head_dim 128, "
-                               "ctx U[512,8192], 16-token pages, random page table, lm-head 4096x129280",
+        "config": {"workload": ("gqa_decode_b64_fp8" if fp8 else "gqa_decode_b64")
+                   + ": 64 paged decode rows, 32 q / 8 kv heads, head_dim 128, ctx U[512,8192], 16-token pages, "
+                     "random page table, lm-head 4096x129280"
+                   + (", FP8 E4M3 KV cache (scale 1)" if fp8 else ""),
                    "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 512, "vocab_tile": 256,
                    "parallelism": "none (1 GPU)"},
         "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
@@ -560,8 +570,8 @@ def bench_long(args):
     }
 
 
-WORKLOADS = {"gqa_decode_b64": bench_gqa, "mla_decode_b128": bench_mla, "sparse_mla_b32": bench_sparse,
-             "long_mix": bench_long}
+WORKLOADS = {"gqa_decode_b64": bench_gqa, "gqa_decode_b64_fp8": bench_gqa_fp8, "mla_decode_b128": bench_mla,
+             "sparse_mla_b32": bench_sparse, "long_mix": bench_long}
 
 
 def main():

@@ -27,6 +27,7 @@ RIL_OK, RIL_EINVAL, RIL_ERANGE, RIL_ENOSPC, RIL_EUNSUPPORTED, RIL_EHIP = 0, -1, 
 RIL_ATTN_GQA, RIL_ATTN_MLA, RIL_ATTN_MLA_SPARSE = 0, 1, 2
 RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
 RIL_POLICY_INVARIANT, RIL_POLICY_SHAPE_DERIVED = 0, 1
+RIL_KV_BF16, RIL_KV_FP8_E4M3 = 0, 1
 
 _c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -41,6 +42,7 @@ class ril_model_desc(ctypes.Structure):
         ("max_ctx", _c_int), ("softmax_scale", _c_float), ("rms_eps", _c_float),
         ("embed", _vp), ("w_qkv", _vp), ("w_o", _vp), ("norm_attn", _vp),
         ("norm_final", _vp), ("w_lm", _vp),
+        ("kv_dtype", _c_int), ("k_scale_exp", _c_int), ("v_scale_exp", _c_int),
     ]
 
 

@@ -24,6 +24,8 @@ struct ril_model {
   int max_splits;   // splits of the longest context
   float cscale;     // softmax_scale * log2(e), rounded once to fp32
   size_t page_bytes;
+  bool kv_fp8;      // GQA pages hold FP8 E4M3 codes
+  float k_scale, v_scale;  // 2^k_scale_exp, 2^v_scale_exp
   bool mla, sparse;
   // workspace segment offsets (bytes) and total
   size_t off_x, off_h, off_qkv, off_attn, off_y, off_z, off_vpart, off_tgt, off_po, off_pml;
@@ -102,6 +104,14 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
       return fail(RIL_EINVAL, "model_create: split_tokens %d (a multiple of 64, at most 1024)", d.split_tokens);
   }
   if (d.page_tokens != 16) return fail(RIL_EUNSUPPORTED, "model_create: page_tokens %d (16)", d.page_tokens);
+  if (d.kv_dtype != RIL_KV_BF16 && d.kv_dtype != RIL_KV_FP8_E4M3)
+    return fail(RIL_EINVAL, "model_create: kv_dtype %d", d.kv_dtype);
+  if (d.kv_dtype == RIL_KV_FP8_E4M3 && mla)
+    return fail(RIL_EUNSUPPORTED, "model_create: the FP8 KV cache is for GQA");
+  if (d.k_scale_exp < -32 || d.k_scale_exp > 32 || d.v_scale_exp < -32 || d.v_scale_exp > 32)
+    return fail(RIL_EINVAL, "model_create: k/v_scale_exp %d/%d (in [-32, 32])", d.k_scale_exp, d.v_scale_exp);
+  if (d.kv_dtype == RIL_KV_BF16 && (d.k_scale_exp || d.v_scale_exp))
+    return fail(RIL_EINVAL, "model_create: k/v_scale_exp are for the FP8 KV cache");
   if (d.vocab < 1) return fail(RIL_EINVAL, "model_create: vocab %d", d.vocab);
   if (d.max_rows < 1 || d.max_tokens < 1 || d.max_ctx < 1)
     return fail(RIL_EINVAL, "model_create: limits %d/%d/%d", d.max_rows, d.max_tokens, d.max_ctx);
@@ -129,12 +139,15 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->n_vt = (d.vocab + 255) / 256;
   m->max_splits = (d.max_ctx + d.split_tokens - 1) / d.split_tokens;
   m->cscale = (float)((double)d.softmax_scale * 1.4426950408889634);
+  m->kv_fp8 = d.kv_dtype == RIL_KV_FP8_E4M3;
+  m->k_scale = std::ldexp(1.0f, d.k_scale_exp);
+  m->v_scale = std::ldexp(1.0f, d.v_scale_exp);
   m->mla = mla;
   m->sparse = sparse;
   if (sparse)  // split count of the selection, not of the context
     m->max_splits = (std::min(d.max_ctx, d.topk) + d.split_tokens - 1) / d.split_tokens;
   m->page_bytes = mla ? (size_t)16 * (d.head_dim + d.rope_dim) * 2 + (sparse ? (size_t)16 * d.index_dim * 4 : 0)
-                      : (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * 2;
+                      : (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * (d.kv_dtype == RIL_KV_FP8_E4M3 ? 1 : 2);
   const size_t R = (size_t)std::max(d.max_rows, d.max_tokens);
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
   size_t o = 0;
@@ -563,7 +576,7 @@ extern "C" ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_pre
                          b->n_seqs, nullptr, b->page_table, b->page_stride, st);
   KvWriteArgs a{(const bf16_t *)b->k, (const bf16_t *)b->v, d.n_kv_heads * d.head_dim, b->total_tokens, 0,
                 b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table, b->page_stride,
-                (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
+                (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim, m->kv_fp8, m->k_scale, m->v_scale};
   RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(a, st));
   return RIL_OK;
 }
@@ -604,11 +617,12 @@ extern "C" ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const
     kv_stride = d.n_kv_heads * d.head_dim;
   }
   KvWriteArgs kw{k, v, kv_stride, T, 0, b->cu_tokens, b->start_pos, b->n_seqs, nullptr, b->page_table,
-                 b->page_stride, (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
+                 b->page_stride, (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim,
+                 m->kv_fp8, m->k_scale, m->v_scale};
   RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(kw, st));
   AttnPrefillArgs ap{q, q_stride, b->cu_tokens, b->start_pos, b->n_seqs, T, b->page_table, b->page_stride,
                      (const bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, m->G, d.head_dim, d.split_tokens,
-                     b->max_ctx_bound, m->cscale, wsb(ws, m->off_attn)};
+                     b->max_ctx_bound, m->cscale, wsb(ws, m->off_attn), m->kv_fp8, m->k_scale, m->v_scale};
   RIL_LAUNCH(RIL_K_ATTN_PREFILL, launch_attn_prefill(ap, st));
   return run_head(m, T, b->target_ids, logprob_out, ws, st);
 }
@@ -662,7 +676,7 @@ static ril_status decode_enqueue(const ril_model *m, ril_kv *kv, const ril_decod
     kv_stride = d.n_kv_heads * d.head_dim;
   }
   KvWriteArgs kw{k, v, kv_stride, R, 1, nullptr, nullptr, 0, b->ctx_len, b->page_table, b->page_stride,
-                 (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim};
+                 (bf16_t *)kv->pool, kv->n_pages, d.n_kv_heads, d.head_dim, m->kv_fp8, m->k_scale, m->v_scale};
   RIL_LAUNCH(RIL_K_KV_WRITE, launch_kv_write(kw, st));
   int split = d.split_tokens, max_splits = m->max_splits;
   if (m->policy == RIL_POLICY_SHAPE_DERIVED) {
@@ -671,7 +685,8 @@ static ril_status decode_enqueue(const ril_model *m, ril_kv *kv, const ril_decod
   }
   AttnDecodeArgs ad{q, q_stride, b->ctx_len, b->page_table, b->page_stride, (const bf16_t *)kv->pool,
                     kv->n_pages, d.n_kv_heads, m->G, d.head_dim, split, b->max_ctx_bound, R,
-                    max_splits, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn)};
+                    max_splits, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn),
+                    m->kv_fp8, m->k_scale, m->v_scale};
   RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_attn_split(ad, st));
   RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_attn_merge(ad, st));
   return run_head(m, R, b->target_ids, logprob_out, ws, st);

@@ -27,6 +27,8 @@
 //   K (t, d) -> (d/32)*512 + ((d%32)/8)*128 + ((t%8)/4)*64 + (t/8)*32 + (t%4)*8 + d%8
 //   V (t, d) -> (t/8)*8D + d*8 + t%8
 // A page of the pool holds all kv heads: page p, kv head g starts at (p*Hkv + g)*32D.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -38,12 +40,12 @@ namespace ril {
 
 // One thread per (token, kv head, 8-dim group).  mode 0: packed prefill tokens (cu,
 // start_pos); mode 1: decode rows (token r is row r at position ctx_len[r]-1).
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void kv_write_kernel(
     const bf16_t *__restrict__ k, const bf16_t *__restrict__ v, int row_stride, int n_tok,
     int mode, const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ page_table, int page_stride,
-    bf16_t *__restrict__ pool, int n_pages, int Hkv) {
+    bf16_t *__restrict__ pool, int n_pages, int Hkv, float k_inv_scale, float v_inv_scale) {
   const int per_tok = Hkv * (D / 8);
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)n_tok * per_tok) return;
@@ -62,6 +64,30 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   if (pos < 0 || pos / kPage >= page_stride) return;  // the attention marks the row NaN
   const int pid = page_table[(long)seq * page_stride + pos / kPage];
   if ((unsigned)pid >= (unsigned)n_pages) return;
+  if constexpr (FP8) {
+    uint8_t *pb = reinterpret_cast<uint8_t *>(pool) + ((long)pid * Hkv + g) * (32 * D);
+    const int t = pos % kPage;
+    const u32x4 kv8 = ld16(k + (long)j * row_stride + g * D + d0);
+    const u32x4 vv8 = ld16(v + (long)j * row_stride + g * D + d0);
+    uint32_t kw[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t lo = fp8_codes2(bf2f((bf16_t)(kv8[2 * w] & 0xffffu)) * k_inv_scale,
+                                     bf2f((bf16_t)(kv8[2 * w] >> 16)) * k_inv_scale);
+      const uint32_t hi = fp8_codes2(bf2f((bf16_t)(kv8[2 * w + 1] & 0xffffu)) * k_inv_scale,
+                                     bf2f((bf16_t)(kv8[2 * w + 1] >> 16)) * k_inv_scale);
+      kw[w] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint2 *>(pb + k_page_offset8(t, d0)) = make_uint2(kw[0], kw[1]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t c2 = fp8_codes2(bf2f((bf16_t)(vv8[w] & 0xffffu)) * v_inv_scale,
+                                     bf2f((bf16_t)(vv8[w] >> 16)) * v_inv_scale);
+      pb[v_page_offset8(t, d0 + 2 * w, D)] = (uint8_t)(c2 & 0xffu);
+      pb[v_page_offset8(t, d0 + 2 * w + 1, D)] = (uint8_t)(c2 >> 8);
+    }
+    return;
+  }
   bf16_t *kb = pool + ((long)pid * Hkv + g) * (32 * D);
   bf16_t *vb = kb + 16 * D;
   const int t = pos % kPage;
@@ -87,12 +113,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 // byte of the cache is read exactly once per step, and letting it displace other lines
 // from the L2 and the memory-side cache cost 8% of the kernel's time.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     const bf16_t *__restrict__ q, int q_row_stride, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool,
     int n_pages, int Hkv, int G, int split_tokens, int ctx_bound, int n_rows, int n_sg, float cscale,
-    float *__restrict__ part_o, float *__restrict__ part_ml, int max_splits) {
+    float *__restrict__ part_o, float *__restrict__ part_ml, int max_splits, float k_scale, float v_scale) {
   const int lane = threadIdx.x;
   const int per_s = Hkv * n_rows;
   const int b = blockIdx.x;
@@ -128,42 +154,81 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   const bool bad_lane = in_ctx && (unsigned)p_raw >= (unsigned)n_pages;
   const int pid = (in_ctx && !bad_lane) ? p_raw : 0;
   const bool bad = __any(bad_lane);
-  // Five half-tile slots: while the scores of tile t run, the V half of t and both halves
-  // of t+1 and the K half of t+2 are in flight (64 KB per wave for D = 128).
-  // Half-tile h (K of tile h/2 if h is even, else its V) lives in slot h % 5.
-  Half<D> ring[5];
+  // Ring of NR = 2*LA + 1 half-tile slots, LA = 2 tiles ahead: while the scores of tile t
+  // run, the V half of t, both halves of t+1 and the K half of t+2 are in flight (64 KB
+  // per wave for D = 128 in bf16, 32 KB in FP8; deeper FP8 rings measured slower).
+  // Half-tile h (K of tile h/2 if h is even, else its V) lives in slot h % NR; FP8 slots
+  // hold the codes, dequantized into bf16 operands just before use.
+  constexpr int LA = 2, NR = 2 * LA + 1;
+  using Slot = std::conditional_t<FP8, Half8<D>, Half<D>>;
+  Slot ring[NR];
   const bf16_t *pg[4];
-  tile_pages<D>(pg, pool, pid, 0, Hkv, g);
-  load_k<D, NtGlobal>(ring[0], pg);
-  load_v<D, NtGlobal>(ring[1], pg);
-  if (n_tiles > 1) {
-    tile_pages<D>(pg, pool, pid, 1, Hkv, g);
-    load_k<D, NtGlobal>(ring[2], pg);
-    load_v<D, NtGlobal>(ring[3], pg);
+  const uint8_t *pg8[4];
+  auto pages = [&](int tile) {
+    if constexpr (FP8) {
+      const uint8_t *p8 = reinterpret_cast<const uint8_t *>(pool);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        pg8[k] = p8 + ((long)__builtin_amdgcn_readlane(pid, 4 * tile + k) * Hkv + g) * (32 * D);
+    } else {
+      tile_pages<D>(pg, pool, pid, tile, Hkv, g);
+    }
+  };
+  auto ldk = [&](Slot &sl) {
+    if constexpr (FP8) load_k8<D, NtGlobal>(sl, pg8);
+    else load_k<D, NtGlobal>(sl, pg);
+  };
+  auto ldv = [&](Slot &sl) {
+    if constexpr (FP8) load_v8<D, NtGlobal>(sl, pg8);
+    else load_v<D, NtGlobal>(sl, pg);
+  };
+#pragma unroll
+  for (int u = 0; u < LA; ++u) {
+    if (u < n_tiles) {
+      pages(u);
+      ldk(ring[2 * u]);
+      ldv(ring[2 * u + 1]);
+    }
   }
   float m = neg_inf(), l = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int t0 = 0; t0 < n_tiles; t0 += 5) {
+  for (int t0 = 0; t0 < n_tiles; t0 += NR) {
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
+    for (int j = 0; j < NR; ++j) {
       const int t = t0 + j;
       if (t < n_tiles) {
-        const bool ahead = t + 2 < n_tiles;
+        const bool ahead = t + LA < n_tiles;
         if (ahead) {
-          tile_pages<D>(pg, pool, pid, t + 2, Hkv, g);
-          load_k<D, NtGlobal>(ring[(2 * j + 4) % 5], pg);  // the slot of V(t-1), already consumed
+          pages(t + LA);
+          ldk(ring[(2 * j + 2 * LA) % NR]);  // the slot of V(t-1), already consumed
         }
         bf16x8 pop[2];
         float alpha, m_new, l_new;
-        attn_scores<D>(ring[(2 * j) % 5], s0 + t * kTile, qop, ctx - 1, cscale, m, l, pop, alpha, m_new,
-                       l_new);
-        if (ahead) load_v<D, NtGlobal>(ring[(2 * j) % 5], pg);  // the slot of K(t), just consumed
-        attn_values<D, false>(ring[(2 * j + 1) % 5], s0 + t * kTile, ctx - 1, ctx, pop, alpha, m_new, l_new,
-                              m, l, o);
+        if constexpr (FP8) {
+          Half<D> kt;
+          dequant_k<D>(ring[(2 * j) % NR], kt);
+          attn_scores<D>(kt, s0 + t * kTile, qop, ctx - 1, cscale, m, l, pop, alpha, m_new, l_new);
+        } else {
+          attn_scores<D>(ring[(2 * j) % NR], s0 + t * kTile, qop, ctx - 1, cscale, m, l, pop, alpha, m_new,
+                         l_new);
+        }
+        if (ahead) ldv(ring[(2 * j) % NR]);  // the slot of K(t), just consumed
+        if constexpr (FP8) {
+          Half<D> vt;
+          dequant_v<D>(ring[(2 * j + 1) % NR], vt);
+          attn_values<D, false>(vt, s0 + t * kTile, ctx - 1, ctx, pop, alpha, m_new, l_new, m, l, o);
+        } else {
+          attn_values<D, false>(ring[(2 * j + 1) % NR], s0 + t * kTile, ctx - 1, ctx, pop, alpha, m_new, l_new,
+                                m, l, o);
+        }
       }
     }
+  }
+  if (FP8) {  // the V scale, on the fp32 state (exact)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db] = o[db] * v_scale;
   }
   if (bad) l = __builtin_nanf("");
   if (!col_ok) return;
@@ -206,14 +271,17 @@ hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t st) {
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const unsigned blocks = (unsigned)((total + threads - 1) / threads);
-  if (a.D == 128)
-    hipLaunchKernelGGL(kv_write_kernel<128>, dim3(blocks), dim3(threads), 0, st, a.k, a.v,
-                       a.row_stride, a.n_tok, a.mode, a.cu, a.start_pos, a.n_seqs, a.ctx_len,
-                       a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv);
-  else
-    hipLaunchKernelGGL(kv_write_kernel<64>, dim3(blocks), dim3(threads), 0, st, a.k, a.v,
-                       a.row_stride, a.n_tok, a.mode, a.cu, a.start_pos, a.n_seqs, a.ctx_len,
-                       a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv);
+  const float ki = 1.f / a.k_scale, vi = 1.f / a.v_scale;  // powers of two: exact
+#define RIL_KVW(D_, F_)                                                                                  \
+  hipLaunchKernelGGL((kv_write_kernel<D_, F_>), dim3(blocks), dim3(threads), 0, st, a.k, a.v, a.row_stride, \
+                     a.n_tok, a.mode, a.cu, a.start_pos, a.n_seqs, a.ctx_len, a.page_table, a.page_stride,  \
+                     a.pool, a.n_pages, a.Hkv, ki, vi)
+  if (a.D == 128) {
+    if (a.kv_fp8) RIL_KVW(128, true); else RIL_KVW(128, false);
+  } else {
+    if (a.kv_fp8) RIL_KVW(64, true); else RIL_KVW(64, false);
+  }
+#undef RIL_KVW
   return hipGetLastError();
 }
 
@@ -223,16 +291,17 @@ hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st) {
   const long slots = (long)(n_sg + a.split_tokens / kTile) * a.Hkv * a.n_rows;
   if (slots > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)slots);
-  if (a.D == 128)
-    hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(64), 0, st, a.q, a.q_row_stride,
-                       a.ctx_len, a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G,
-                       a.split_tokens, a.ctx_bound, a.n_rows, n_sg, a.cscale, a.part_o, a.part_ml,
-                       a.max_splits);
-  else
-    hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(64), 0, st, a.q, a.q_row_stride,
-                       a.ctx_len, a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G,
-                       a.split_tokens, a.ctx_bound, a.n_rows, n_sg, a.cscale, a.part_o, a.part_ml,
-                       a.max_splits);
+#define RIL_SPLIT(D_, F_)                                                                                      \
+  hipLaunchKernelGGL((attn_decode_split_kernel<D_, F_>), grid, dim3(64), 0, st, a.q, a.q_row_stride, a.ctx_len, \
+                     a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G, a.split_tokens, a.ctx_bound,    \
+                     a.n_rows, n_sg, a.kv_fp8 ? a.cscale * a.k_scale : a.cscale, a.part_o, a.part_ml, a.max_splits, \
+                     a.k_scale, a.v_scale)
+  if (a.D == 128) {
+    if (a.kv_fp8) RIL_SPLIT(128, true); else RIL_SPLIT(128, false);
+  } else {
+    if (a.kv_fp8) RIL_SPLIT(64, true); else RIL_SPLIT(64, false);
+  }
+#undef RIL_SPLIT
   return hipGetLastError();
 }
 

@@ -216,6 +216,120 @@ struct FromLdsUntracked {
   }
 };
 
+// ---------------------------------------------------------------------------
+// FP8 (OCP E4M3) KV pages (Bitwise-consistent RL post, section 4.2: FP8 storage, one write
+// path, one dequantizing read shared by every phase).  A page block (16 tokens, one kv
+// head) is 32*D bytes: K then V, 16*D bytes each, one byte per value, laid out so that a
+// 16-byte load holds two MFMA operands:
+//   K (t, d) -> 2*((d/64)*512 + ((d%32)/8)*128 + ((t%8)/4)*64 + (t/8)*32 + (t%4)*8)
+//               + ((d/32)%2)*8 + d%8                 (chunks c = 2j and 2j+1 side by side)
+//   V (t, d) -> 16*D + (t/8)*8*D + ((d/32)*16 + d%16)*16 + ((d/16)%2)*8 + t%8
+//                                                    (dims d and d+16 side by side)
+// The stored code is e4m3(x * 2^-s) (nearest even, magnitudes past 448 saturating, NaN
+// kept with its sign) with s a model constant per tensor; the value read back is
+// code * 2^s, which bf16 holds exactly, so dequantization adds no rounding (the 2^s is
+// applied outside the MFMA operands: see fp8_operand).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int k_page_offset8(int t, int d) {
+  return 2 * ((d >> 6) * 512 + ((d & 31) >> 3) * 128 + ((t & 7) >> 2) * 64 + (t >> 3) * 32 + (t & 3) * 8) +
+         ((d >> 5) & 1) * 8 + (d & 7);
+}
+__device__ __forceinline__ int v_page_offset8(int t, int d, int D) {
+  return 16 * D + (t >> 3) * 8 * D + ((d >> 5) * 16 + (d & 15)) * 16 + ((d >> 4) & 1) * 8 + (t & 7);
+}
+
+// One E4M3 code of x (already multiplied by 2^-s): the hardware conversion rounds to
+// nearest even but turns magnitudes past 464 into NaN, so the clamp to +-448 comes first;
+// NaN is encoded here with its sign.
+__device__ __forceinline__ uint32_t fp8_codes2(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.f), 448.f), cb = fminf(fmaxf(b, -448.f), 448.f);
+  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xffffu;
+  if (a != a) r = (r & 0xff00u) | (0x7fu | ((__float_as_uint(a) >> 24) & 0x80u));
+  if (b != b) r = (r & 0x00ffu) | ((0x7fu | ((__float_as_uint(b) >> 24) & 0x80u)) << 8);
+  return r;
+}
+
+// Eight E4M3 codes (two words) -> one bf16 MFMA operand holding the codes' values (exact:
+// the fp32 decode is exact for every code and the values are bf16 values).
+//
+// The scales 2^s are not applied here.  K's multiplies the softmax constant (scores =
+// (q . code) * (c * 2^s_k)) and V's multiplies the fp32 output state once, before it is
+// stored (decode partials) or divided (prefill).  A power of two commutes with every fp32
+// rounding between those points, so this equals attending over code * 2^s (outside the
+// subnormal and overflow ranges of fp32), and prefill and decode fold them identically.
+__device__ __forceinline__ u32x4 fp8_operand(uint32_t w0, uint32_t w1) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  u32x4 r;
+  r[0] = pack2(a[0], a[1]);
+  r[1] = pack2(b[0], b[1]);
+  r[2] = pack2(c[0], c[1]);
+  r[3] = pack2(d[0], d[1]);
+  return r;
+}
+
+// Raw FP8 half-tile: D/16 16-byte values per lane, each two operands of the bf16 Half.
+//   K: r[mb*(D/64) + j] = operands (mb, c = 2j) and (mb, 2j+1)
+//   V: r[kc*(D/32) + j] = operands (kc, db = 2j) and (kc, 2j+1)
+template <int D>
+struct Half8 {
+  u32x4 r[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void dequant_k(const Half8<D> &raw, Half<D> &t) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      const u32x4 w = raw.r[mb * (D / 64) + j];
+      t.r[mb * (D / 32) + 2 * j] = fp8_operand(w[0], w[1]);
+      t.r[mb * (D / 32) + 2 * j + 1] = fp8_operand(w[2], w[3]);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void dequant_v(const Half8<D> &raw, Half<D> &t) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const u32x4 w = raw.r[kc * (D / 32) + j];
+      t.r[kc * (D / 16) + 2 * j] = fp8_operand(w[0], w[1]);
+      t.r[kc * (D / 16) + 2 * j + 1] = fp8_operand(w[2], w[3]);
+    }
+}
+
+// pg8[k]: byte address of the FP8 K block of the tile's k-th page (V at +16*D bytes).
+template <int D, typename Mem = FromGlobal>
+__device__ __forceinline__ void load_k8(Half8<D> &t, const uint8_t *const (&pg8)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int rq = r16 >> 2, ri = r16 & 3;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint8_t *kb = pg8[2 * kc + (rq >> 1)] + 2 * (grp * 128 + h * 64 + (rq & 1) * 32 + ri * 8);
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j)
+        t.r[(2 * kc + h) * (D / 64) + j] = Mem::ld(reinterpret_cast<const bf16_t *>(kb + j * 1024));
+    }
+}
+
+template <int D, typename Mem = FromGlobal>
+__device__ __forceinline__ void load_v8(Half8<D> &t, const uint8_t *const (&pg8)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const uint8_t *vb = pg8[2 * kc + (grp >> 1)] + 16 * D + (grp & 1) * (8 * D) + r16 * 16;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) t.r[kc * (D / 32) + j] = Mem::ld(reinterpret_cast<const bf16_t *>(vb + j * 256));
+  }
+}
+
 // pg[k]: K block of the tile's k-th page (its V block follows at +16*D).
 template <int D, typename Mem = FromGlobal>
 __device__ __forceinline__ void load_k(Half<D> &t, const bf16_t *const (&pg)[4]) {

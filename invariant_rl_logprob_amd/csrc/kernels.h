@@ -19,6 +19,8 @@ struct KvWriteArgs {
   int page_stride;
   bf16_t *pool;
   int n_pages, Hkv, D;
+  int kv_fp8 = 0;                        // pool pages hold FP8 E4M3 codes
+  float k_scale = 1.f, v_scale = 1.f;    // stored code = e4m3(x / scale), scale a power of two
 };
 
 struct AttnDecodeArgs {
@@ -31,6 +33,8 @@ struct AttnDecodeArgs {
   float cscale;
   float *part_o, *part_ml;
   bf16_t *out;  // [rows, Hq, D]
+  int kv_fp8 = 0;
+  float k_scale = 1.f, v_scale = 1.f;
 };
 
 struct AttnPrefillArgs {
@@ -44,6 +48,8 @@ struct AttnPrefillArgs {
   int n_pages, Hkv, G, D, split_tokens, ctx_bound;
   float cscale;
   bf16_t *out;  // [n_tok, Hq, D]
+  int kv_fp8 = 0;
+  float k_scale = 1.f, v_scale = 1.f;
 };
 
 struct RmsNormArgs {

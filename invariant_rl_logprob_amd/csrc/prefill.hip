@@ -4,6 +4,8 @@
 // attn_common.h), with its states held in registers (Bitwise-consistent RL post,
 // section 2: phase consistency; section 4.2: one read path shared by prefill, decode
 // and the trainer).
+#include <type_traits>
+
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -20,35 +22,34 @@ namespace ril {
 // split's end, with per-column predication (MAYBE_INACTIVE) for tiles and splits past
 // the column's position.  Split and merged states stay in registers.
 // ---------------------------------------------------------------------------
-// LDS slot of one page block (K then V, 16*D bf16 each), padded by 128 bytes so the two
-// pages one K-operand load touches fall on different banks.
-template <int D>
-constexpr int lds_page() { return 32 * D + 64; }
+// LDS slot of one page block in bytes (K then V, 16*D values each, 2 bytes per value in
+// bf16 and 1 in FP8), padded by 128 bytes so the two pages one K-operand load touches fall
+// on different banks.
+template <int D, bool FP8>
+constexpr int lds_page_bytes() { return (FP8 ? 32 * D : 64 * D) + 128; }
 
 // s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this wave are
 // outstanding (they complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
-  static_assert(N == 0 || N == 2 || N == 4 || N == 8, "add the count");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
 
-template <int D, int NW, int NBUF>
+template <int D, int NW, int NBUF, bool FP8>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const bf16_t *__restrict__ q, int q_row_stride, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ start_pos, int n_seqs, const int32_t *__restrict__ page_table,
     int page_stride, const bf16_t *__restrict__ pool, int n_pages, int Hkv, int G,
-    int split_tokens, int ctx_bound, float cscale, bf16_t *__restrict__ out) {
+    int split_tokens, int ctx_bound, float cscale, bf16_t *__restrict__ out, float k_scale, float v_scale) {
   static_assert(NW >= 1 && NW <= 8, "at most 512 threads (the launch bound)");
   static_assert(NBUF >= 2 && NBUF <= 4, "tiles in flight");
-  constexpr int kSlot = lds_page<D>();
-  constexpr int kPieces = 32 * D / 512;       // 1 KB pieces per page block
+  constexpr int kSlotB = lds_page_bytes<D, FP8>();
+  constexpr int kPageB = FP8 ? 32 * D : 64 * D;  // bytes of one page block in the pool
+  constexpr int kPieces = kPageB / 1024;         // 1 KB pieces per page block
   static_assert((4 * kPieces) % NW == 0, "every wave copies the same number of pieces");
-  constexpr int kPer = 4 * kPieces / NW;      // pieces (= vector-memory ops) per wave per tile
-  __shared__ __attribute__((aligned(16))) bf16_t kv[NBUF][4 * kSlot];
+  constexpr int kPer = 4 * kPieces / NW;         // pieces (= vector-memory ops) per wave per tile
+  __shared__ __attribute__((aligned(16))) uint8_t kv[NBUF][4 * kSlotB];
   const int g = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int tpb = 16 / G;
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     for (int u = 0; u < kPer; ++u) raw[u] = pt[min(4 * T + (wave + u * NW) / kPieces, last_page)];
   };
   auto copy_tile = [&](int T, const int (&raw)[kPer]) {
-    bf16_t *buf = &kv[T % NBUF][0];
+    uint8_t *buf = &kv[T % NBUF][0];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = wave + u * NW;
@@ -130,8 +131,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
       bad |= b;
       const int pid = (P <= last_page && !b) ? raw[u] : 0;
       const int j = pc % kPieces;
-      const bf16_t *src = pool + ((long)pid * Hkv + g) * (32 * D) + j * 512 + lane * 8;
-      bf16_t *dst = buf + (pc / kPieces) * kSlot + j * 512;
+      const uint8_t *src = reinterpret_cast<const uint8_t *>(pool) + ((long)pid * Hkv + g) * kPageB + j * 1024 +
+                           lane * 16;
+      uint8_t *dst = buf + (pc / kPieces) * kSlotB + j * 1024;
       __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
   };
@@ -142,29 +144,52 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
   }
   if (NBUF - 1 < n_tiles) fetch_ids(NBUF - 1, idn);
 
-  // This lane's LDS byte addresses of its K and V operands in buffer 0 (the Half layouts
-  // of load_k / load_v over the 4 page slots); every read adds a constant offset.
+  // This lane's LDS byte addresses of its K and V operands in buffer 0 (the Half / Half8
+  // layouts of load_k / load_v / load_k8 / load_v8 over the 4 page slots); every read adds
+  // a constant offset.  FP8 reads bring two operands' codes, dequantized in registers.
   const int r16 = lane & 15, rq = r16 >> 2, ri = r16 & 3;
-  const uint32_t kv0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t *)&kv[0][0];
-  const uint32_t kbase = kv0 + 2 * ((rq >> 1) * kSlot + grp * 128 + (rq & 1) * 32 + ri * 8);
-  const uint32_t vbase = kv0 + 2 * ((grp >> 1) * kSlot + 16 * D + (grp & 1) * (8 * D) + r16 * 8);
-  auto lds_tile_k = [&](Half<D> &t, uint32_t base) {
-    static_for<2>([&](auto kc_) {
-      static_for<2>([&](auto h_) {
-        static_for<D / 32>([&](auto c_) {
-          constexpr int kc = decltype(kc_)::value, h = decltype(h_)::value, c = decltype(c_)::value;
-          t.r[(2 * kc + h) * (D / 32) + c] = lds_rd128<2 * (2 * kc * kSlot + h * 64 + c * 512)>(base);
+  const uint32_t kv0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)&kv[0][0];
+  const uint32_t kbase = kv0 + (rq >> 1) * kSlotB + 2 * (grp * 128 + (rq & 1) * 32 + ri * 8);  // both layouts
+  const uint32_t vbase = FP8 ? kv0 + (grp >> 1) * kSlotB + 16 * D + (grp & 1) * (8 * D) + r16 * 16
+                             : kv0 + (grp >> 1) * kSlotB + 2 * (16 * D + (grp & 1) * (8 * D) + r16 * 8);
+  using Raw = std::conditional_t<FP8, Half8<D>, Half<D>>;
+  auto lds_tile_k = [&](Raw &t, uint32_t base) {
+    if constexpr (FP8) {
+      static_for<2>([&](auto kc_) {
+        static_for<2>([&](auto h_) {
+          static_for<D / 64>([&](auto j_) {
+            constexpr int kc = decltype(kc_)::value, h = decltype(h_)::value, j = decltype(j_)::value;
+            t.r[(2 * kc + h) * (D / 64) + j] = lds_rd128<2 * kc * kSlotB + h * 128 + j * 1024>(base);
+          });
         });
       });
-    });
-  };
-  auto lds_tile_v = [&](Half<D> &t, uint32_t base) {
-    static_for<2>([&](auto kc_) {
-      static_for<D / 16>([&](auto db_) {
-        constexpr int kc = decltype(kc_)::value, db = decltype(db_)::value;
-        t.r[kc * (D / 16) + db] = lds_rd128<2 * (2 * kc * kSlot + db * 128)>(base);
+    } else {
+      static_for<2>([&](auto kc_) {
+        static_for<2>([&](auto h_) {
+          static_for<D / 32>([&](auto c_) {
+            constexpr int kc = decltype(kc_)::value, h = decltype(h_)::value, c = decltype(c_)::value;
+            t.r[(2 * kc + h) * (D / 32) + c] = lds_rd128<2 * kc * kSlotB + 2 * (h * 64 + c * 512)>(base);
+          });
+        });
       });
-    });
+    }
+  };
+  auto lds_tile_v = [&](Raw &t, uint32_t base) {
+    if constexpr (FP8) {
+      static_for<2>([&](auto kc_) {
+        static_for<D / 32>([&](auto j_) {
+          constexpr int kc = decltype(kc_)::value, j = decltype(j_)::value;
+          t.r[kc * (D / 32) + j] = lds_rd128<2 * kc * kSlotB + j * 256>(base);
+        });
+      });
+    } else {
+      static_for<2>([&](auto kc_) {
+        static_for<D / 16>([&](auto db_) {
+          constexpr int kc = decltype(kc_)::value, db = decltype(db_)::value;
+          t.r[kc * (D / 16) + db] = lds_rd128<2 * kc * kSlotB + 2 * db * 128>(base);
+        });
+      });
+    }
   };
 
   float M = neg_inf(), L = 0.f, m = neg_inf(), l = 0.f;
@@ -189,15 +214,18 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const int t0 = T * kTile;
     const int s0 = t0 - t0 % split_tokens;
     if (t0 <= w_max) {
-      const uint32_t boff = (uint32_t)(T % NBUF) * (4 * kSlot * 2);
+      const uint32_t boff = (uint32_t)(T % NBUF) * (4 * kSlotB);
       Half<D> hk, hv;
-      lds_tile_k(hk, kbase + boff);
+      Raw rk, rv;
+      lds_tile_k(rk, kbase + boff);
       lds_wait<0>();
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) settle(hk.r[i]);
+      for (int i = 0; i < (int)(sizeof(Raw) / 16); ++i) settle(rk.r[i]);
+      if constexpr (FP8) dequant_k<D>(rk, hk);
+      else hk = rk;
       f32x4 sc[4];
       attn_score_mfma<D>(hk, qop, sc);
-      lds_tile_v(hv, vbase + boff);  // lands while the softmax runs
+      lds_tile_v(rv, vbase + boff);  // lands while the softmax runs
       bf16x8 pop[2];
       float alpha, m_new, l_new;
       // Uniform shortcuts that leave every value unchanged: no causal select when the whole
@@ -208,7 +236,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
         tile_softmax<true>(sc, t0, pos, cscale, m, l, pop, alpha, m_new, l_new);
       lds_wait<0>();
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) settle(hv.r[i]);
+      for (int i = 0; i < (int)(sizeof(Raw) / 16); ++i) settle(rv.r[i]);
+      if constexpr (FP8) dequant_v<D>(rv, hv);
+      else hv = rv;
       if (t0 > w_min)
         attn_values<D, true>(hv, t0, pos, p_max + 1, pop, alpha, m_new, l_new, m, l, o);
       else if (t0 + kTile > p_max + 1)
@@ -243,6 +273,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
   // a page id outside the pool seen by any wave marks the whole workgroup's rows NaN
   if (__syncthreads_or(bad)) L = __builtin_nanf("");
   if (!col_ok) return;
+  if (FP8) {  // the V scale, on the fp32 state (exact), as the decode partials get it
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) O[e] = O[e] * v_scale;
+  }
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
     uint32_t w0 = pack2(__fdiv_rn(O[db * 4 + 0], L), __fdiv_rn(O[db * 4 + 1], L));
@@ -259,14 +293,17 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st) {
   const long blocks = (long)(a.n_tok + QT - 1) / QT + a.n_seqs;  // bound on sum of ceil(n_s / QT)
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks, a.Hkv);
-  if (a.D == 128)
-    hipLaunchKernelGGL((attn_prefill_kernel<128, NW, NBUF>), grid, dim3(64 * NW), 0, st, a.q, a.q_row_stride,
-                       a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.n_pages,
-                       a.Hkv, a.G, a.split_tokens, a.ctx_bound, a.cscale, a.out);
-  else
-    hipLaunchKernelGGL((attn_prefill_kernel<64, NW, NBUF>), grid, dim3(64 * NW), 0, st, a.q, a.q_row_stride,
-                       a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.n_pages,
-                       a.Hkv, a.G, a.split_tokens, a.ctx_bound, a.cscale, a.out);
+#define RIL_PF(D_, F_)                                                                                            \
+  hipLaunchKernelGGL((attn_prefill_kernel<D_, NW, NBUF, F_>), grid, dim3(64 * NW), 0, st, a.q, a.q_row_stride, a.cu, \
+                     a.start_pos, a.n_seqs, a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G,             \
+                     a.split_tokens, a.ctx_bound, a.kv_fp8 ? a.cscale * a.k_scale : a.cscale, a.out, a.k_scale, \
+                     a.v_scale)
+  if (a.D == 128) {
+    if (a.kv_fp8) RIL_PF(128, true); else RIL_PF(128, false);
+  } else {
+    if (a.kv_fp8) RIL_PF(64, true); else RIL_PF(64, false);
+  }
+#undef RIL_PF
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ class Session:
                  max_ctx, pool_pages, softmax_scale, rms_eps=1e-6, split_tokens=512, shuffle_seed=0,
                  input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
                  norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, index_heads=0, index_dim=0, topk=0,
-                 device="cuda"):
+                 kv_dtype=0, k_scale_exp=0, v_scale_exp=0, device="cuda"):
         self.device = torch.device(device)
         # the lm-head weight lives in the library's packed layout (w_lm stays row-major)
         w_lm = w_lm.contiguous()
@@ -53,7 +53,8 @@ class Session:
         self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
                                    index_heads, index_dim, topk, d_head, vocab, PAGE, split_tokens, max_rows,
                                    max_tokens, max_ctx, softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o),
-                                   p(norm_attn), p(norm_final), p(self.w_lm_packed))
+                                   p(norm_attn), p(norm_final), p(self.w_lm_packed), kv_dtype, k_scale_exp,
+                                   v_scale_exp)
         self.model = ril_model_create(self.desc)
         self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
         self.max_ctx = max_ctx

@@ -15,8 +15,10 @@ from invariant_rl_logprob_amd.session import Session
 
 class GQACase:
     def __init__(self, w: wl.GQADecode, rows: Sequence[int], *, ctx: Sequence[int] = None,
-                 device="cuda", shuffle_seed=1234, copies=2, max_tokens=None, head=None):
+                 device="cuda", shuffle_seed=1234, copies=2, max_tokens=None, head=None, kv_dtype=0,
+                 k_scale_exp=0, v_scale_exp=0):
         self.w = w
+        self.kv = (kv_dtype, k_scale_exp, v_scale_exp)
         self.rows = list(rows)
         self.device = device
         self.data: Dict[int, dict] = {}
@@ -30,7 +32,8 @@ class GQACase:
                             vocab=w.vocab, d_head=w.d_head, w_lm=self.head["w_lm"], w_o=self.head.get("w_o"),
                             max_rows=max(len(self.rows), 1), max_tokens=max_tokens or len(self.rows) * R,
                             max_ctx=max_ctx, pool_pages=pages, softmax_scale=1.0 / math.sqrt(w.head_dim),
-                            rms_eps=w.rms_eps, shuffle_seed=shuffle_seed, device=device)
+                            rms_eps=w.rms_eps, shuffle_seed=shuffle_seed, kv_dtype=kv_dtype,
+                            k_scale_exp=k_scale_exp, v_scale_exp=v_scale_exp, device=device)
 
     def ctx(self, r):
         return self.data[r]["ctx"]
@@ -103,6 +106,9 @@ class GQACase:
         q = oracle.widen(d["q"][R - back])
         K = oracle.widen(d["k"][: p + 1])
         V = oracle.widen(d["v"][: p + 1])
+        if self.kv[0] == 1:  # FP8 cache: the model attends over what the cache gives back
+            K = oracle.kv_fp8_roundtrip(K, self.kv[1])
+            V = oracle.kv_fp8_roundtrip(V, self.kv[2])
         scale = 1.0 / math.sqrt(self.w.head_dim)
         o = oracle.gqa_row_attention(q, K, V, scale)
         w_o = self.head.get("w_o")

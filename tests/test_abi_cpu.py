@@ -57,6 +57,20 @@ def test_model_create_validates():
         assert ril.ril_last_error()
 
 
+def test_fp8_kv_cache_descriptor():
+    m = ril.ril_model_create(_desc(kv_dtype=ril.RIL_KV_FP8_E4M3, k_scale_exp=-2, v_scale_exp=3))
+    assert ril.ril_kv_page_bytes(m) == 8 * 2 * 16 * 128  # one byte per value: half of bf16
+    ril.ril_model_destroy(m)
+    mla = dict(attn_kind=ril.RIL_ATTN_MLA, n_q_heads=128, n_kv_heads=1, head_dim=512, rope_dim=64,
+               d_head=65536, split_tokens=2048)
+    for b in (dict(kv_dtype=2), dict(kv_dtype=-1), dict(kv_dtype=ril.RIL_KV_FP8_E4M3, k_scale_exp=33),
+              dict(kv_dtype=ril.RIL_KV_FP8_E4M3, v_scale_exp=-40), dict(k_scale_exp=1),
+              dict(kv_dtype=ril.RIL_KV_FP8_E4M3, **mla)):
+        with pytest.raises(ril.RilError):
+            ril.ril_model_create(_desc(**b))
+        assert ril.ril_last_error()
+
+
 def test_workspace_monotone_in_limits():
     sizes = []
     for mr, mt, mc in [(8, 64, 1024), (16, 64, 1024), (16, 128, 1024), (16, 128, 4096)]:
