@@ -28,6 +28,8 @@ from .numerics import (  # noqa: F401
     log_softmax_at,
     lm_head_logprob,
     attention_row,
+    silu,
+    swiglu_rounded_once,
 )
 from .models import (  # noqa: F401
     tiny_decoder_prefill,

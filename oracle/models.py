@@ -14,7 +14,7 @@ import math
 
 import numpy as np
 
-from .numerics import attention_row, bf16, lm_head_logprob, log_softmax_at, rmsnorm, widen
+from .numerics import attention_row, bf16, lm_head_logprob, log_softmax_at, rmsnorm, swiglu_rounded_once, widen
 
 
 # ---------------------------------------------------------------------------
@@ -23,6 +23,22 @@ from .numerics import attention_row, bf16, lm_head_logprob, log_softmax_at, rmsn
 
 def _tiny_params(p):
     return {k: widen(v) for k, v in p.items()}
+
+
+def _mlp(P, y, eps):
+    """The SwiGLU block after the attention residual, when the parameters have one
+    (w_gate_up [2F, d]: gate rows then up rows; w_down [d, F]; norm_mlp [d]):
+        h = bf16(rms(y) g3);  [g|u] = bf16(h Wgu^T);  a = bf16(silu(g) u)  (rounded once)
+        y' = bf16(y + bf16(a Wdown^T))
+    Reading (the pages name the rounding of the activation, post section 4.4 condition 3,
+    not the block): pre-norm residual MLP of the same form as the attention block."""
+    if "w_gate_up" not in P:
+        return y
+    F = P["w_down"].shape[1]
+    h = bf16(rmsnorm(y, P["norm_mlp"], eps))
+    gu = bf16(h @ P["w_gate_up"].T)
+    a = swiglu_rounded_once(gu[..., :F], gu[..., F:])
+    return bf16(y + bf16(a @ P["w_down"].T))
 
 
 def tiny_decoder_prefill(params, tokens, targets, n_q_heads, n_kv_heads, head_dim,
@@ -35,8 +51,8 @@ def tiny_decoder_prefill(params, tokens, targets, n_q_heads, n_kv_heads, head_di
     no positional encoding, then a final RMSNorm and the lm-head:
         x = E[t];  h = bf16(rms(x) g1);  [q|k|v] = bf16(h Wqkv^T)
         o_i = bf16(softmax_j<=i(q_i . k_j / sqrt(D)) v)    (q head h -> kv head h*Hkv/Hq)
-        y = bf16(x + bf16(o Wo^T));  z = bf16(rms(y) g2);  l = z Wlm^T
-        lp_i = log_softmax(l_i)[targets[i]]
+        y = bf16(x + bf16(o Wo^T));  [y = the SwiGLU block of _mlp, when present]
+        z = bf16(rms(y) g2);  l = z Wlm^T;  lp_i = log_softmax(l_i)[targets[i]]
     Returns float64 [L].  Pinned by: agreement with ``tiny_decoder_decode``
     (coded separately) to 1e-12; closed forms with zeroed weights.
     """
@@ -59,6 +75,7 @@ def tiny_decoder_prefill(params, tokens, targets, n_q_heads, n_kv_heads, head_di
             o[i, hh] = attention_row(q[i, hh], k[: i + 1, g], v[: i + 1, g], scale)
     o = bf16(o).reshape(L, Hq * D)
     y = bf16(x + bf16(o @ P["w_o"].T))
+    y = _mlp(P, y, eps)
     z = bf16(rmsnorm(y, P["norm_final"], eps))
     logits = z @ P["w_lm"].T
     return np.array([log_softmax_at(logits[i], targets[i]) for i in range(L)])
@@ -104,6 +121,13 @@ def tiny_decoder_decode(params, tokens, targets, n_prompt, n_q_heads, n_kv_heads
             heads.append((w[:, None] * Vc).sum(axis=0) / w.sum())
         o = bf16(np.concatenate(heads))
         y = bf16(x + bf16(P["w_o"] @ o))
+        if "w_gate_up" in P:  # the same block, written per row with matrix-vector products
+            F = P["w_down"].shape[1]
+            h = bf16(rmsnorm(y, P["norm_mlp"], eps))
+            gu = bf16(P["w_gate_up"] @ h)
+            g, u = gu[:F], gu[F:]
+            a = bf16(g / (1.0 + np.exp(-g)) * u)
+            y = bf16(y + bf16(P["w_down"] @ a))
         z = bf16(rmsnorm(y, P["norm_final"], eps))
         return log_softmax_at(P["w_lm"] @ z, targets[pos])
 

@@ -104,3 +104,25 @@ def attention_row(q, K, V, scale: float) -> np.ndarray:
     p = np.exp(s)
     p = p / np.sum(p)
     return p @ V
+
+
+def silu(x) -> np.ndarray:
+    """SiLU (swish): x * sigmoid(x) = x / (1 + exp(-x)), float64.
+
+    Pinned by: torch.nn.functional.silu in float64, silu(0) = 0, and the odd part
+    silu(x) - silu(-x) = x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu_rounded_once(gate, up) -> np.ndarray:
+    """bf16(SiLU(gate) * up): the product is formed unrounded and rounded once.
+
+    The Bitwise-consistent RL post (section 4.4, condition 3) computes SiLU(gate) x up
+    between the two GEMMs in FP32 and rounds only the product to BF16: rounding SiLU to
+    BF16 before the multiply can move the result by one ulp.  Here the product is formed
+    in float64 and rounded once.  Pinned by: torch's float64 silu composition, and a
+    planted round-before-multiply variant that a test shows differing.
+    """
+    return bf16(silu(gate) * np.asarray(up, dtype=np.float64))

@@ -507,3 +507,50 @@ def test_planted_e4m3_truncation_is_caught():
     x = np.array([1.0625 + 2.0 ** -20, 1.1875])
     trunc = np.floor(x * 8) / 8
     assert not np.array_equal(of8.e4m3_encode(trunc), of8.e4m3_encode(x))
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU MLP block, activation rounded once (oracle/numerics.py, oracle/models.py)
+# ---------------------------------------------------------------------------
+
+def test_silu_pins():
+    x = np.linspace(-30, 30, 2001)
+    ref = F.silu(torch.from_numpy(x)).numpy()
+    assert np.allclose(on.silu(x), ref, rtol=1e-15, atol=1e-300)
+    assert on.silu(0.0) == 0.0
+    assert np.allclose(on.silu(x) - on.silu(-x), x, rtol=0, atol=1e-12)
+
+
+def test_swiglu_rounds_once_and_round_before_multiply_differs():
+    rng = np.random.default_rng(3)
+    g = on.bf16(rng.normal(size=20000))
+    u = on.bf16(rng.normal(size=20000))
+    once = on.swiglu_rounded_once(g, u)
+    assert np.array_equal(once, on.bf16(F.silu(torch.from_numpy(g)).numpy() * u))
+    twice = on.bf16(on.bf16(on.silu(g)) * u)   # the pitfall the pages name
+    assert np.any(once != twice)
+
+
+def test_tiny_decoder_with_mlp_prefill_equals_decode():
+    W = wl.TINY_MLP
+    wts = wl.tiny_weights(W)
+    t = wl.tiny_tokens(0, W).numpy()[:40]
+    tg = np.roll(t, -1)
+    a = oracle.tiny_decoder_prefill(wts, t, tg, W.n_q_heads, W.n_kv_heads, W.head_dim, W.rms_eps)
+    b = oracle.tiny_decoder_decode(wts, t, tg, W.prompt_tokens, W.n_q_heads, W.n_kv_heads, W.head_dim,
+                                   W.rms_eps)
+    assert np.max(np.abs(a - b)) <= 1e-12
+
+
+def test_tiny_decoder_mlp_with_zero_down_projection_is_the_plain_decoder():
+    W = wl.TINY_MLP
+    wts = wl.tiny_weights(W)
+    t = wl.tiny_tokens(1, W).numpy()[:24]
+    tg = np.roll(t, -1)
+    z = dict(wts, w_down=torch.zeros_like(wts["w_down"]))
+    plain = {k: v for k, v in wts.items() if k not in ("w_gate_up", "w_down", "norm_mlp")}
+    a = oracle.tiny_decoder_prefill(z, t, tg, W.n_q_heads, W.n_kv_heads, W.head_dim, W.rms_eps)
+    b = oracle.tiny_decoder_prefill(plain, t, tg, W.n_q_heads, W.n_kv_heads, W.head_dim, W.rms_eps)
+    assert np.array_equal(a, b)
+    full = oracle.tiny_decoder_prefill(wts, t, tg, W.n_q_heads, W.n_kv_heads, W.head_dim, W.rms_eps)
+    assert not np.array_equal(full, b)  # the block does act when its weights are there

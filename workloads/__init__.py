@@ -86,6 +86,7 @@ class TinyDecoder:
     rms_eps: float = 1e-6
     page_tokens: int = 16
     seed: int = 0
+    d_ff: int = 0                 # > 0: a SwiGLU MLP block (gate/up F each) after the attention block
 
 
 @dataclasses.dataclass(frozen=True)
@@ -108,6 +109,7 @@ class GQADecode:
 
 
 TINY = TinyDecoder()
+TINY_MLP = TinyDecoder(d_ff=512, seed=5)
 GQA_DECODE_B64 = GQADecode()
 # Long-context GQA (64 q / 8 kv heads) with an 8192 -> 4096 output projection.
 GQA_LONG = GQADecode(rows=256, n_q_heads=64, n_kv_heads=8, head_dim=128, ctx_lo=1024,
@@ -129,6 +131,9 @@ def tiny_weights(w: TinyDecoder = TINY, device="cpu") -> Dict[str, torch.Tensor]
         "norm_attn": torch.ones(d, dtype=torch.bfloat16, device=device),
         "norm_final": torch.ones(d, dtype=torch.bfloat16, device=device),
         "w_lm": randn((v, d), key(s, "w_lm"), w.init_std, device),
+        **({"w_gate_up": randn((2 * w.d_ff, d), key(s, "w_gate_up"), w.init_std, device),
+            "w_down": randn((d, w.d_ff), key(s, "w_down"), w.init_std, device),
+            "norm_mlp": torch.ones(d, dtype=torch.bfloat16, device=device)} if w.d_ff else {}),
     }
 
 
