@@ -128,6 +128,15 @@ typedef struct ril_model_desc {
   int32_t kv_dtype;       /* RIL_KV_BF16 (0) | RIL_KV_FP8_E4M3 (GQA only)                 */
   int32_t k_scale_exp;    /* FP8: K stored as e4m3(k * 2^-k_scale_exp), in [-32, 32]; BF16: 0 */
   int32_t v_scale_exp;    /* FP8: V likewise                                               */
+  /* TOKENS only: an optional SwiGLU MLP block after the attention block (d_ff = 0: none):
+   *   h = bf16(rms(y) norm_mlp);  [g|u] = bf16(h w_gate_up^T);  a = bf16(silu(g) * u)
+   *   y' = bf16(y + bf16(a w_down^T))
+   * where silu(g) * u is formed in fp32 and rounded once (Bitwise-consistent RL post,
+   * section 4.4, condition 3: SwiGLU's activation rounded once). */
+  int32_t d_ff;           /* F, a multiple of 32, or 0                                      */
+  const void *w_gate_up;  /* [2F, d_model]: gate rows 0..F-1, then up rows                  */
+  const void *w_down;     /* [d_model, F]                                                    */
+  const void *norm_mlp;   /* [d_model] RMSNorm gain; NULL = 1                                */
 } ril_model_desc;
 
 typedef struct ril_model ril_model;  /* opaque: copy of the description + derived sizes */
@@ -310,7 +319,8 @@ enum {
   RIL_K_VOCAB_MERGE = 7,  /* S12 */
   RIL_K_INDEXER = 8,      /* S6 */
   RIL_K_TOPK = 9,         /* S7 */
-  RIL_K_COUNT = 10
+  RIL_K_SILU_MUL = 10,    /* the SwiGLU activation */
+  RIL_K_COUNT = 11
 };
 ril_status ril_trace_enable(int on);
 ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches);

@@ -43,6 +43,7 @@ class ril_model_desc(ctypes.Structure):
         ("embed", _vp), ("w_qkv", _vp), ("w_o", _vp), ("norm_attn", _vp),
         ("norm_final", _vp), ("w_lm", _vp),
         ("kv_dtype", _c_int), ("k_scale_exp", _c_int), ("v_scale_exp", _c_int),
+        ("d_ff", _c_int), ("w_gate_up", _vp), ("w_down", _vp), ("norm_mlp", _vp),
     ]
 
 
@@ -108,9 +109,9 @@ EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril
 # kernel ids of the trace hook
 RIL_K_KV_WRITE, RIL_K_ATTN_SPLIT, RIL_K_ATTN_MERGE, RIL_K_ATTN_PREFILL = 0, 1, 2, 3
 RIL_K_RMSNORM, RIL_K_GEMM, RIL_K_LM_HEAD, RIL_K_VOCAB_MERGE = 4, 5, 6, 7
-RIL_K_INDEXER, RIL_K_TOPK, RIL_K_COUNT = 8, 9, 10
+RIL_K_INDEXER, RIL_K_TOPK, RIL_K_SILU_MUL, RIL_K_COUNT = 8, 9, 10, 11
 KERNEL_NAMES = ("kv_write", "attn_split", "attn_merge", "attn_prefill", "rmsnorm", "gemm", "lm_head",
-                "vocab_merge", "indexer", "topk")
+                "vocab_merge", "indexer", "topk", "silu_mul")
 
 
 class RilError(RuntimeError):

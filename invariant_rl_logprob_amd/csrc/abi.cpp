@@ -30,6 +30,7 @@ struct ril_model {
   // workspace segment offsets (bytes) and total
   size_t off_x, off_h, off_qkv, off_attn, off_y, off_z, off_vpart, off_tgt, off_po, off_pml;
   size_t off_scores, off_sel;  // sparse: indexer scores [max_rows, max_ctx], selections [max_rows, topk]
+  size_t off_gu = 0, off_act = 0, off_y2 = 0;  // SwiGLU MLP: [R, 2F], [R, F], [R, d_model] bf16
   size_t ws_base;   // end of the invariant path's segments
   size_t ws_total;  // ws_base + the comparator's split-K partials when that policy is on
   // comparator (benchmarking only): RIL_POLICY_SHAPE_DERIVED picks splits from the batch
@@ -104,6 +105,13 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
       return fail(RIL_EINVAL, "model_create: split_tokens %d (a multiple of 64, at most 1024)", d.split_tokens);
   }
   if (d.page_tokens != 16) return fail(RIL_EUNSUPPORTED, "model_create: page_tokens %d (16)", d.page_tokens);
+  if (d.d_ff < 0 || d.d_ff % 32)
+    return fail(RIL_EINVAL, "model_create: d_ff %d (0 or a multiple of 32)", d.d_ff);
+  if (d.d_ff && (d.input_mode != RIL_INPUT_TOKENS || !d.w_gate_up || !d.w_down ||
+                 ((uintptr_t)d.w_gate_up & 15) || ((uintptr_t)d.w_down & 15) || ((uintptr_t)d.norm_mlp & 15)))
+    return fail(RIL_EINVAL, "model_create: the MLP block needs TOKENS input and 16-byte aligned w_gate_up/w_down");
+  if (!d.d_ff && (d.w_gate_up || d.w_down || d.norm_mlp))
+    return fail(RIL_EINVAL, "model_create: MLP weights given with d_ff = 0");
   if (d.kv_dtype != RIL_KV_BF16 && d.kv_dtype != RIL_KV_FP8_E4M3)
     return fail(RIL_EINVAL, "model_create: kv_dtype %d", d.kv_dtype);
   if (d.kv_dtype == RIL_KV_FP8_E4M3 && mla)
@@ -158,6 +166,11 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->off_attn = seg(R * qw * 2);
   m->off_y = seg(d.w_o ? R * d.d_head * 2 : 0);
   m->off_z = seg(R * d.d_head * 2);
+  if (d.d_ff) {
+    m->off_gu = seg(R * 2 * (size_t)d.d_ff * 2);
+    m->off_act = seg(R * (size_t)d.d_ff * 2);
+    m->off_y2 = seg(R * (size_t)d.d_model * 2);
+  }
   m->off_vpart = seg(R * m->n_vt * 2 * sizeof(float));
   m->off_tgt = seg(R * sizeof(float));
   m->off_po = seg((size_t)d.max_rows * d.n_q_heads * m->max_splits * d.head_dim * sizeof(float));
@@ -460,6 +473,24 @@ static ril_status run_head(const ril_model *m, int rows, const int32_t *targets,
     RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
     src = wsb(ws, m->off_y);
     ld = d.d_head;
+  }
+  if (d.d_ff) {  // the SwiGLU block (TOKENS only: d_head = d_model)
+    const int F = d.d_ff;
+    RmsNormArgs rn{src, ld, nullptr, nullptr, d.vocab, d.d_model, (const bf16_t *)d.norm_mlp, d.rms_eps,
+                   wsb(ws, m->off_h), d.d_model, nullptr, 0, rows};
+    RIL_LAUNCH(RIL_K_RMSNORM, launch_rmsnorm(rn, st));
+    GemmArgs g1{wsb(ws, m->off_h), d.d_model, (const bf16_t *)d.w_gate_up, d.d_model, wsb(ws, m->off_gu), 2 * F,
+                nullptr, 0, rows, 2 * F, d.d_model};
+    shape_split_k(m, g1, ws);
+    RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g1, st));
+    SiluMulArgs sm{wsb(ws, m->off_gu), 2 * F, wsb(ws, m->off_act), F, rows, F};
+    RIL_LAUNCH(RIL_K_SILU_MUL, launch_silu_mul(sm, st));
+    GemmArgs g2{wsb(ws, m->off_act), F, (const bf16_t *)d.w_down, F, wsb(ws, m->off_y2), d.d_model,
+                src, ld, rows, d.d_model, F};
+    shape_split_k(m, g2, ws);
+    RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g2, st));
+    src = wsb(ws, m->off_y2);
+    ld = d.d_model;
   }
   RmsNormArgs r{src, ld, nullptr, nullptr, d.vocab, d.d_head, (const bf16_t *)d.norm_final, d.rms_eps,
                 wsb(ws, m->off_z), d.d_head, nullptr, 0, rows};

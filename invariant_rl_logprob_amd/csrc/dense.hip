@@ -67,6 +67,44 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// SwiGLU activation between the two MLP GEMMs: silu(g) * u formed in fp32 and rounded to
+// bf16 once (Bitwise-consistent RL post, section 4.4, condition 3: rounding silu before
+// the multiply can move the result by an ulp).  silu(g) = g / (1 + 2^(-g log2 e)) with the
+// hardware exp2 and an IEEE divide, the same instructions in every phase.  One thread per
+// 8 columns of a row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void silu_mul_kernel(const bf16_t *__restrict__ gu, int ldg,
+                                                       bf16_t *__restrict__ act, int lda, int rows, int F) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = F / 8;
+  if (idx >= (long)rows * per) return;
+  const int r = (int)(idx / per), j0 = (int)(idx % per) * 8;
+  const u32x4 g8 = ld16(gu + (long)r * ldg + j0), u8 = ld16(gu + (long)r * ldg + F + j0);
+  u32x4 out;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float g = bf2f((bf16_t)(h ? (g8[w] >> 16) : (g8[w] & 0xffffu)));
+      const float u = bf2f((bf16_t)(h ? (u8[w] >> 16) : (u8[w] & 0xffffu)));
+      const float sg = __fdiv_rn(g, 1.0f + exp2f_hw(-g * kLog2e));
+      v[h] = sg * u;
+    }
+    out[w] = pack2(v[0], v[1]);
+  }
+  st16(act + (long)r * lda + j0, out);
+}
+
+hipError_t launch_silu_mul(const SiluMulArgs &a, hipStream_t st) {
+  const long n = (long)a.rows * (a.F / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.gu, a.ldg, a.act,
+                     a.lda, a.rows, a.F);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // The K loop of every GEMM here: acc[mb][nb] += A_mb(k) B_nb(k)^T for k = 0, 32, 64, ...
 // in order, one v_mfma_f32_16x16x32_bf16 per step and block.  Operand loads run PF steps
 // ahead through a register ring (issue order only; the accumulation order is fixed).

@@ -52,6 +52,15 @@ struct AttnPrefillArgs {
   float k_scale = 1.f, v_scale = 1.f;
 };
 
+// SwiGLU activation: act[r, j] = bf16(silu(gu[r, j]) * gu[r, F + j]), formed in fp32.
+struct SiluMulArgs {
+  const bf16_t *gu;  // [rows, 2F] at row stride ldg
+  int ldg;
+  bf16_t *act;       // [rows, F] at row stride lda
+  int lda, rows, F;
+};
+hipError_t launch_silu_mul(const SiluMulArgs &a, hipStream_t st);
+
 struct RmsNormArgs {
   const bf16_t *x;
   int ldx;

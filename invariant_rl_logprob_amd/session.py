@@ -41,20 +41,21 @@ class Session:
                  max_ctx, pool_pages, softmax_scale, rms_eps=1e-6, split_tokens=512, shuffle_seed=0,
                  input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
                  norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, index_heads=0, index_dim=0, topk=0,
-                 kv_dtype=0, k_scale_exp=0, v_scale_exp=0, device="cuda"):
+                 kv_dtype=0, k_scale_exp=0, v_scale_exp=0, d_ff=0, w_gate_up=None, w_down=None, norm_mlp=None,
+                 device="cuda"):
         self.device = torch.device(device)
         # the lm-head weight lives in the library's packed layout (w_lm stays row-major)
         w_lm = w_lm.contiguous()
         self.w_lm_packed = torch.empty(ril_lm_head_packed_bytes(vocab, d_head), dtype=torch.uint8,
                                        device=self.device)
         ril_pack_lm_head(w_lm, self.w_lm_packed)
-        self._keep = [embed, w_qkv, w_o, norm_attn, norm_final]
+        self._keep = [embed, w_qkv, w_o, norm_attn, norm_final, w_gate_up, w_down, norm_mlp]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
                                    index_heads, index_dim, topk, d_head, vocab, PAGE, split_tokens, max_rows,
                                    max_tokens, max_ctx, softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o),
                                    p(norm_attn), p(norm_final), p(self.w_lm_packed), kv_dtype, k_scale_exp,
-                                   v_scale_exp)
+                                   v_scale_exp, d_ff, p(w_gate_up), p(w_down), p(norm_mlp))
         self.model = ril_model_create(self.desc)
         self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
         self.max_ctx = max_ctx

@@ -71,6 +71,24 @@ def test_fp8_kv_cache_descriptor():
         assert ril.ril_last_error()
 
 
+def test_mlp_block_descriptor():
+    tok = dict(input_mode=ril.RIL_INPUT_TOKENS, d_model=256, d_head=256, n_q_heads=4, n_kv_heads=4,
+               head_dim=64, vocab=2048, embed=0x20000, w_qkv=0x30000, w_o=0x40000)
+    m = ril.ril_model_create(_desc(**tok, d_ff=512, w_gate_up=0x50000, w_down=0x60000))
+    plain = ril.ril_model_create(_desc(**tok))
+    assert ril.ril_workspace_bytes(m) > ril.ril_workspace_bytes(plain)
+    ril.ril_model_destroy(m)
+    ril.ril_model_destroy(plain)
+    for b in (dict(tok, d_ff=500, w_gate_up=0x50000, w_down=0x60000),      # not a multiple of 32
+              dict(tok, d_ff=512, w_gate_up=0x50000),                        # no w_down
+              dict(tok, d_ff=512, w_gate_up=0x50008, w_down=0x60000),        # misaligned
+              dict(tok, w_gate_up=0x50000, w_down=0x60000),                  # weights without d_ff
+              dict(d_ff=512, w_gate_up=0x50000, w_down=0x60000)):            # QKV input
+        with pytest.raises(ril.RilError):
+            ril.ril_model_create(_desc(**b))
+        assert ril.ril_last_error()
+
+
 def test_workspace_monotone_in_limits():
     sizes = []
     for mr, mt, mc in [(8, 64, 1024), (16, 64, 1024), (16, 128, 1024), (16, 128, 4096)]:
