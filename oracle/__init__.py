@@ -45,3 +45,10 @@ from .models import (  # noqa: F401
 )
 from .metrics import diff_stats, k3_mean  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode, kv_fp8_roundtrip  # noqa: F401
+from .fp8block import (  # noqa: F401
+    block_exponent,
+    quantize_rows,
+    quantize_weight_blocks,
+    w8a8_matmul,
+    lm_head_logprob_w8a8,
+)

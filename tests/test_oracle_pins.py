@@ -554,3 +554,102 @@ def test_tiny_decoder_mlp_with_zero_down_projection_is_the_plain_decoder():
     assert np.array_equal(a, b)
     full = oracle.tiny_decoder_prefill(wts, t, tg, W.n_q_heads, W.n_kv_heads, W.head_dim, W.rms_eps)
     assert not np.array_equal(full, b)  # the block does act when its weights are there
+
+
+# ---------------------------------------------------------------------------
+# Block-FP8 W8A8 GEMM for the lm-head (oracle/fp8block.py)
+# ---------------------------------------------------------------------------
+
+from oracle import fp8block as ofb  # noqa: E402
+
+
+def _exponent_brute(a):
+    if a == 0:
+        return 0
+    return min(e for e in range(-200, 200) if a <= 448.0 * 2.0 ** e)
+
+
+def check_block_exponent(fn):
+    vals = [0.0, 448.0, 448.0 * 2 ** -7, 448.0 * 2 ** 5, 449.0, 447.0, 224.0, 224.0 + 2 ** -8, 1.0,
+            2 ** -133, 3.3895314e38, 0.0078125, 57.0]
+    vals += list(np.abs(RNG.standard_normal(300)) * 10.0 ** RNG.integers(-30, 30, 300))
+    vals += list(_all_bf16_values()[1:0x7F80:97])
+    got = fn(np.array(vals))
+    return all(int(g) == _exponent_brute(v) for g, v in zip(got, vals))
+
+
+def test_block_exponent_matches_brute_force():
+    assert check_block_exponent(ofb.block_exponent)
+
+
+def test_row_groups_in_range_with_max_in_upper_octave():
+    x = on.bf16(RNG.standard_normal((5, 512)) * np.array([1e-3, 1.0, 30.0, 1e4])[RNG.integers(0, 4, (5, 1))])
+    x[2, 128:256] = 0.0                                       # an all-zero group
+    codes, e = ofb.quantize_rows(x)
+    assert codes.shape == x.shape and codes.dtype == np.uint8 and e.shape == (5, 4)
+    vals = of8.e4m3_decode(codes)
+    assert np.all(np.isfinite(vals)) and np.all(np.abs(vals) <= 448.0)
+    gmax = np.max(np.abs(vals.reshape(5, 4, 128)), axis=-1)
+    nz = np.max(np.abs(x.reshape(5, 4, 128)), axis=-1) > 0
+    assert np.all((gmax[nz] >= 224.0) & (gmax[nz] <= 448.0))   # the scale is the tightest power of two
+    assert e[2, 1] == 0 and np.all(codes[2, 128:256] == 0)
+    # each value within half a spacing (relative 2^-4, or 2^-10 * 2^e for subnormals) of x
+    back = ofb.dequant_rows(codes, e)
+    ee = np.repeat(e, 128, axis=-1)
+    assert np.all(np.abs(back - x) <= np.maximum(np.abs(x) * 2.0 ** -4, np.ldexp(1.0, ee - 10)))
+
+
+def test_weight_blocks_match_elementwise_loop():
+    w = on.bf16(RNG.standard_normal((130, 256)) * 0.02)
+    w[129, :] *= 50.0                       # the ragged last block has its own scale
+    codes, e = ofb.quantize_weight_blocks(w)
+    assert e.shape == (2, 2) and codes.shape == w.shape
+    for n in range(0, 130, 3):
+        for k in range(0, 256, 5):
+            blk = w[(n // 128) * 128:(n // 128 + 1) * 128, (k // 128) * 128:(k // 128 + 1) * 128]
+            s = _exponent_brute(float(np.max(np.abs(blk))))
+            assert e[n // 128, k // 128] == s
+            assert codes[n, k] == of8.e4m3_encode(np.array([w[n, k] * 2.0 ** -s]))[0]
+    back = ofb.dequant_weight_blocks(codes, e)
+    assert np.array_equal(back[129], of8.e4m3_decode(codes[129]) * 2.0 ** np.repeat(e[1], 128))
+
+
+def test_w8a8_matmul_of_fp8_exact_integers_is_the_integer_product():
+    # integers of magnitude <= 16 have at most 4 significant bits, so every block scaling
+    # and E4M3 code is exact and the product must be the int64 one
+    a = RNG.integers(-16, 17, (7, 384))
+    w = RNG.integers(-16, 17, (200, 384))
+    a[:, 0] = 16                                               # the scales are then 2^-4
+    w[:, 0] = 16
+    ref = a.astype(np.int64) @ w.T.astype(np.int64)
+    assert np.array_equal(ofb.w8a8_matmul(a.astype(np.float64), w.astype(np.float64)), ref.astype(np.float64))
+    tg = 17
+    lp = ofb.lm_head_logprob_w8a8(a[3].astype(np.float64), w.astype(np.float64), tg)
+    assert abs(lp - scipy.special.log_softmax(ref[3].astype(np.float64))[tg]) < 1e-12
+
+
+def test_w8a8_matmul_within_quantization_bound_of_exact():
+    a = on.bf16(RNG.standard_normal((4, 256)))
+    w = on.bf16(RNG.standard_normal((64, 256)) * 0.02)
+    got = ofb.w8a8_matmul(a, w)
+    exact = a @ w.T
+    # |qa qw - a w| <= |a||w| (2 * 2^-4 + 2^-8) plus the subnormal terms (tiny at these scales)
+    bound = np.abs(a) @ np.abs(w).T * (2 * 2.0 ** -4 + 2.0 ** -8) + 1e-6
+    assert np.all(np.abs(got - exact) <= bound)
+    assert np.any(got != exact)
+
+
+def test_planted_floor_exponent_is_caught():
+    # a plausible mistake: e rounded down (amax > 448 * 2^e) saturates the group's largest values
+    def floor_exp(amax):
+        a = np.asarray(amax, dtype=np.float64)
+        return np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0) / 448.0)), 0).astype(np.int64)
+    assert not check_block_exponent(floor_exp)
+
+
+def test_planted_transposed_weight_blocks_are_caught():
+    # a plausible mistake: the weight block exponents indexed [k-block, n-block]
+    w = on.bf16(RNG.standard_normal((256, 256)) * 0.02)
+    w[:128, 128:] *= 100.0
+    codes, e = ofb.quantize_weight_blocks(w)
+    assert not np.array_equal(ofb.dequant_weight_blocks(codes, e.T), ofb.dequant_weight_blocks(codes, e))
