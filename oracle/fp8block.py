@@ -9,13 +9,18 @@ post names the scheme, not its constants; the readings here:
     weights in 128 x 128 blocks (128 output columns x 128 K values);
   * scales: one power of two 2^e per group / block, e the smallest integer with
     amax <= 448 * 2^e (amax = the group's largest magnitude; e = 0 for an all-zero
-    group), so x * 2^-e never exceeds the E4M3 range and scaling is exact;
+    group), so x * 2^-e never exceeds the E4M3 range and scaling is exact.  The scale is
+    an E8M0 value (the OCP microscaling scale format: a biased 8-bit exponent, 2^-127 to
+    2^127, code 255 = NaN), so e is raised to -127 where it would fall below (groups whose
+    largest magnitude is under 448 * 2^-128; bf16 values never need e > 120), and a group
+    holding an infinity or NaN gets the NaN scale, which makes every product it enters NaN;
   * codes: e4m3(x * 2^-e), nearest even (oracle/fp8.py), of the bf16 values;
   * product: out[m, n] = sum over K of dequant(A)[m, k] * dequant(W)[n, k].  The GPU sums
     each 128-wide K block in one FP8 MFMA and adds the blocks in a fixed order per column;
     the oracle's value is the exact sum (float64 of exactly representable products).
 
-Pinned by (tests/test_oracle_pins.py): the exponent rule against brute force, every code
+Pinned by (tests/test_oracle_pins.py): the exponent rule against brute force (the clamp
+and the NaN scale included), every code
 inside the E4M3 range with the group maximum in its upper octave, the block structure
 against an elementwise loop, and the GEMM of integer-valued operands against int64.
 """
@@ -27,14 +32,26 @@ import numpy as np
 from .fp8 import e4m3_decode, e4m3_encode
 
 GROUP = 128
+E_MIN = -127        # the smallest E8M0 scale, 2^-127
+E_NAN = 128         # the E8M0 NaN code (255) less the bias
 
 
 def block_exponent(amax) -> np.ndarray:
-    """Smallest integer e with amax <= 448 * 2^e (0 where amax is 0)."""
+    """Smallest integer e >= -127 with amax <= 448 * 2^e (0 where amax is 0, E_NAN where
+    amax is not finite)."""
     a = np.asarray(amax, dtype=np.float64)
-    m, E = np.frexp(a)                       # a = m * 2^E, 0.5 <= m < 1
+    fin = np.isfinite(a)
+    m, E = np.frexp(np.where(fin, a, 1.0))   # a = m * 2^E, 0.5 <= m < 1
     e = E - 9 + (m > 0.875).astype(np.int64)  # 448 * 2^(E-9) = 0.875 * 2^E
-    return np.where(a > 0, e, 0).astype(np.int64)
+    e = np.maximum(e, E_MIN)
+    e = np.where(a > 0, e, 0)
+    return np.where(fin, e, E_NAN).astype(np.int64)
+
+
+def _scale(e):
+    """2^e, NaN for the NaN scale."""
+    e = np.asarray(e)
+    return np.where(e == E_NAN, np.nan, np.ldexp(1.0, np.where(e == E_NAN, 0, e)))
 
 
 def quantize_rows(x):
@@ -45,7 +62,7 @@ def quantize_rows(x):
     assert K % GROUP == 0
     g = x.reshape(x.shape[:-1] + (K // GROUP, GROUP))
     e = block_exponent(np.max(np.abs(g), axis=-1))
-    codes = e4m3_encode(np.ldexp(g, -e[..., None]))
+    codes = e4m3_encode(np.ldexp(g, -np.where(e == E_NAN, 0, e)[..., None]))
     return codes.reshape(x.shape), e
 
 
@@ -59,7 +76,7 @@ def quantize_weight_blocks(w):
     pad[:N] = w
     blocks = pad.reshape(nb, GROUP, K // GROUP, GROUP)
     e = block_exponent(np.max(np.abs(blocks), axis=(1, 3)))
-    codes = e4m3_encode(np.ldexp(blocks, -e[:, None, :, None]))
+    codes = e4m3_encode(np.ldexp(blocks, -np.where(e == E_NAN, 0, e)[:, None, :, None]))
     return codes.reshape(nb * GROUP, K)[:N], e
 
 
@@ -67,7 +84,7 @@ def dequant_rows(codes, e):
     c = np.asarray(codes)
     K = c.shape[-1]
     v = e4m3_decode(c).reshape(c.shape[:-1] + (K // GROUP, GROUP))
-    return np.ldexp(v, np.asarray(e)[..., None]).reshape(c.shape)
+    return (v * _scale(e)[..., None]).reshape(c.shape)
 
 
 def dequant_weight_blocks(codes, e):
@@ -75,7 +92,7 @@ def dequant_weight_blocks(codes, e):
     N, K = c.shape
     v = e4m3_decode(c)
     rows = np.repeat(np.asarray(e), GROUP, axis=0)[:N]        # [N, K/128]
-    return np.ldexp(v.reshape(N, K // GROUP, GROUP), rows[:, :, None]).reshape(N, K)
+    return (v.reshape(N, K // GROUP, GROUP) * _scale(rows)[:, :, None]).reshape(N, K)
 
 
 def w8a8_matmul(a, w) -> np.ndarray:

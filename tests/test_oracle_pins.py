@@ -564,15 +564,18 @@ from oracle import fp8block as ofb  # noqa: E402
 
 
 def _exponent_brute(a):
+    if not np.isfinite(a):
+        return 128                       # the E8M0 NaN code less the bias
     if a == 0:
         return 0
-    return min(e for e in range(-200, 200) if a <= 448.0 * 2.0 ** e)
+    return max(-127, min(e for e in range(-300, 300) if a <= 448.0 * 2.0 ** e))
 
 
 def check_block_exponent(fn):
     vals = [0.0, 448.0, 448.0 * 2 ** -7, 448.0 * 2 ** 5, 449.0, 447.0, 224.0, 224.0 + 2 ** -8, 1.0,
-            2 ** -133, 3.3895314e38, 0.0078125, 57.0]
-    vals += list(np.abs(RNG.standard_normal(300)) * 10.0 ** RNG.integers(-30, 30, 300))
+            2 ** -133, 3.3895314e38, 0.0078125, 57.0, 448.0 * 2 ** -127, 448.0 * 2 ** -127 * 1.01,
+            448.0 * 2 ** -128, 2 ** -126, np.inf, np.nan]
+    vals += list(np.abs(RNG.standard_normal(300)) * 10.0 ** RNG.integers(-45, 30, 300))
     vals += list(_all_bf16_values()[1:0x7F80:97])
     got = fn(np.array(vals))
     return all(int(g) == _exponent_brute(v) for g, v in zip(got, vals))
@@ -580,6 +583,25 @@ def check_block_exponent(fn):
 
 def test_block_exponent_matches_brute_force():
     assert check_block_exponent(ofb.block_exponent)
+
+
+def test_non_finite_group_gives_nan_products_only_where_it_enters():
+    a = on.bf16(RNG.standard_normal((3, 256)))
+    w = on.bf16(RNG.standard_normal((5, 256)) * 0.02)
+    a[1, 200] = np.inf                   # row 1, second group
+    out = ofb.w8a8_matmul(a, w)
+    assert np.all(np.isnan(out[1])) and np.all(np.isfinite(out[[0, 2]]))
+    w[4, 3] = np.nan                     # column block 0, first K block: every column of it
+    out = ofb.w8a8_matmul(a, w)
+    assert np.all(np.isnan(out))
+
+
+def test_tiny_group_uses_the_smallest_scale():
+    x = np.zeros((1, 128))
+    x[0, :3] = [2.0 ** -125, -(2.0 ** -126), 3 * 2.0 ** -127]
+    codes, e = ofb.quantize_rows(x)
+    assert e[0, 0] == -127
+    assert np.array_equal(ofb.dequant_rows(codes, e)[0, :3], x[0, :3])  # 4, 2, 1.5 at 2^-127: exact
 
 
 def test_row_groups_in_range_with_max_in_upper_octave():
@@ -643,7 +665,9 @@ def test_planted_floor_exponent_is_caught():
     # a plausible mistake: e rounded down (amax > 448 * 2^e) saturates the group's largest values
     def floor_exp(amax):
         a = np.asarray(amax, dtype=np.float64)
-        return np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0) / 448.0)), 0).astype(np.int64)
+        ok = np.isfinite(a) & (a > 0)
+        e = np.maximum(np.floor(np.log2(np.where(ok, a, 1.0) / 448.0)), -127)
+        return np.where(ok, e, np.where(np.isfinite(a), 0, 128)).astype(np.int64)
     assert not check_block_exponent(floor_exp)
 
 
