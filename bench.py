@@ -240,7 +240,15 @@ def bench_gqa_fp8(args):
     return bench_gqa(args, fp8=True)
 
 
-def bench_gqa(args, fp8=False):
+def bench_gqa_w8a8(args):
+    return bench_gqa(args, lm8=True)
+
+
+def bench_gqa_fp8_w8a8(args):
+    return bench_gqa(args, fp8=True, lm8=True)
+
+
+def bench_gqa(args, fp8=False, lm8=False):
     import numpy as np
     import torch
     import workloads as wl
@@ -250,7 +258,7 @@ def bench_gqa(args, fp8=False):
     rows = list(range(w.rows))
     t0 = time.time()
     case = GQACase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_tokens=w.rows * 16,
-                   kv_dtype=1 if fp8 else 0)
+                   kv_dtype=1 if fp8 else 0, lm_dtype=1 if lm8 else 0)
     ctx = [case.ctx(r) for r in rows]
     log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
     dec, diff = diff_check(case, rows)
@@ -265,15 +273,20 @@ def bench_gqa(args, fp8=False):
     kv_bytes = sum(ctx) * Hkv * D * 2 * (1 if fp8 else 2)  # each K/V byte once per kv head
     q_bytes = len(rows) * Hq * D * 2
     out_bytes = len(rows) * Hq * D * 2
-    lm_bytes = w.vocab * w.d_head * 2 + len(rows) * w.d_head * 2
-    split_us, merge_us, lm_us = kern["attn_split"]["avg_us"], kern["attn_merge"]["avg_us"], kern["lm_head"]["avg_us"]
+    if lm8:  # E4M3 weight codes + their block scales, the rows' codes + scales
+        n_vt = (w.vocab + 255) // 256
+        lm_bytes = n_vt * 256 * w.d_head + 2 * n_vt * (w.d_head // 128) * 4 + len(rows) * w.d_head * (1 + 4 / 128)
+    else:
+        lm_bytes = w.vocab * w.d_head * 2 + len(rows) * w.d_head * 2
+    lm_name = "lm_head_fp8" if lm8 else "lm_head"
+    split_us, merge_us, lm_us = kern["attn_split"]["avg_us"], kern["attn_merge"]["avg_us"], kern[lm_name]["avg_us"]
     attn_gbps = (kv_bytes + q_bytes + out_bytes) / ((split_us + merge_us) * 1e-6) / 1e9
     split_gbps = (kv_bytes + q_bytes) / (split_us * 1e-6) / 1e9
     lm_gbps = lm_bytes / (lm_us * 1e-6) / 1e9
     if split_us >= lm_us:
         roof = roofline_hbm("attn_decode_split", split_gbps, kv_bytes + q_bytes, split_us)
     else:
-        roof = roofline_hbm("lm_head", lm_gbps, lm_bytes, lm_us)
+        roof = roofline_hbm(lm_name, lm_gbps, lm_bytes, lm_us)
 
     x1 = None
     if not args.no_comparator:
@@ -291,7 +304,9 @@ def bench_gqa(args, fp8=False):
         log(f"graph: {graph}")
 
     cpu = None
-    if not args.no_cpu and args.cpu_rows > 0:
+    if lm8:
+        log("oracle: not timed here (its W8A8 head quantizes the whole 129280 x 4096 weight per row)")
+    elif not args.no_cpu and args.cpu_rows > 0:
         import oracle  # the cpu_baseline leg: the fp64 oracle as it stands
         sample = rows[: args.cpu_rows]
         w_lm_cpu = case.head["w_lm"].cpu()
@@ -312,10 +327,12 @@ def bench_gqa(args, fp8=False):
 
     return {
         "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
-        "config": {"workload": ("gqa_decode_b64_fp8" if fp8 else "gqa_decode_b64")
+        "dtype": "bf16 (attention), e4m3 (lm-head)" if lm8 else "bf16",
+        "config": {"workload": "gqa_decode_b64" + ("_fp8" if fp8 else "") + ("_w8a8" if lm8 else "")
                    + ": 64 paged decode rows, 32 q / 8 kv heads, head_dim 128, ctx U[512,8192], 16-token pages, "
                      "random page table, lm-head 4096x129280"
-                   + (", FP8 E4M3 KV cache (scale 1)" if fp8 else ""),
+                   + (", FP8 E4M3 KV cache (scale 1)" if fp8 else "")
+                   + (", W8A8 block-FP8 lm-head (1x128 / 128x128 E8M0 scales)" if lm8 else ""),
                    "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 512, "vocab_tile": 256,
                    "parallelism": "none (1 GPU)"},
         "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
@@ -570,7 +587,8 @@ def bench_long(args):
     }
 
 
-WORKLOADS = {"gqa_decode_b64": bench_gqa, "gqa_decode_b64_fp8": bench_gqa_fp8, "mla_decode_b128": bench_mla,
+WORKLOADS = {"gqa_decode_b64": bench_gqa, "gqa_decode_b64_fp8": bench_gqa_fp8,
+             "gqa_decode_b64_w8a8": bench_gqa_w8a8, "gqa_decode_b64_fp8_w8a8": bench_gqa_fp8_w8a8, "mla_decode_b128": bench_mla,
              "sparse_mla_b32": bench_sparse, "long_mix": bench_long}
 
 
@@ -608,7 +626,7 @@ def main():
     res = WORKLOADS[args.workload](args)
     line = {"metric": METRIC, "value": res.pop("value"), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+            "scaling": "weak", "vs_baseline": None, "dtype": res.pop("dtype", "bf16"), "data": "synthetic"}
     line.update(res)
     print(json.dumps(line), flush=True)
 

@@ -86,6 +86,19 @@ enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1, RIL_ATTN_MLA_SPARSE = 2 };
  * page then takes n_kv_heads * 16 * 2 * head_dim bytes (half of BF16's).  The in-page
  * byte layout is documented in csrc/attn_common.h. */
 enum { RIL_KV_BF16 = 0, RIL_KV_FP8_E4M3 = 1 };
+
+/* lm-head arithmetic.  W8A8_FP8 follows the Bitwise-consistent RL post, section 4.1
+ * (the deployment GEMM is W8A8 with block-FP8 weights; the trainer quantizes its bf16
+ * weights to block FP8 by the same rule and calls the same GEMM, one accumulation order
+ * for every M): the normalised rows are quantized per group of 128 K values and the
+ * weight per block of 128 vocabulary columns x 128 K values, each group or block to OCP
+ * E4M3 codes e4m3(x * 2^-e) (nearest even) with one E8M0 scale 2^e, e the smallest
+ * integer >= -127 with max|x| <= 448 * 2^e (0 for an all-zero group, the E8M0 NaN code
+ * for a group holding an infinity or NaN, which makes every logit it enters NaN).  The
+ * logits are the fp32 sums over K of code products times both scales, accumulated one
+ * 128-wide K block at a time in the column's fixed order; the softmax partials and the
+ * logprob are then formed exactly as in the bf16 head. */
+enum { RIL_LM_BF16 = 0, RIL_LM_W8A8_FP8 = 1 };
 enum { RIL_INPUT_TOKENS = 0, RIL_INPUT_QKV = 1 };
 
 /* Model description.  All sizes are fixed for the life of the handle; the
@@ -137,6 +150,9 @@ typedef struct ril_model_desc {
   const void *w_gate_up;  /* [2F, d_model]: gate rows 0..F-1, then up rows                  */
   const void *w_down;     /* [d_model, F]                                                    */
   const void *norm_mlp;   /* [d_model] RMSNorm gain; NULL = 1                                */
+  int32_t lm_dtype;       /* RIL_LM_BF16 (0): w_lm as written by ril_pack_lm_head;
+                             RIL_LM_W8A8_FP8 (1): w_lm as written by ril_pack_lm_head_fp8,
+                             d_head a multiple of 128                                       */
 } ril_model_desc;
 
 typedef struct ril_model ril_model;  /* opaque: copy of the description + derived sizes */
@@ -192,6 +208,36 @@ ril_status ril_set_policy(ril_model *m, int32_t policy, int32_t attn_split_token
 size_t ril_lm_head_packed_bytes(int32_t vocab, int32_t d_head);
 ril_status ril_pack_lm_head(const void *src, int32_t vocab, int32_t d_head, void *dst, size_t packed_bytes,
                             void *stream);
+
+/* W8A8 weight layout (RIL_LM_W8A8_FP8).  One buffer: the E4M3 codes, then the biased
+ * E8M0 exponents (int32, 127 + e, 255 = NaN) of the 128 x 128 blocks,
+ * [2 * ceil(V/256), K/128], block b covering columns 128b .. 128b+127 (columns past V
+ * count as zero).  Codes: per vocabulary tile of 256 columns, per 128-wide K step, a
+ * contiguous 32 KB piece holding the 2 KB FP8 MFMA operands of the tile's sixteen
+ * 16-column blocks in lane order:
+ *   code(c, k) at ((c/256) * (K/128) + k/128) * 32768 + ((c%256)/16) * 2048
+ *                 + ((k%32)/16) * 1024 + (((k%128)/32) * 16 + c%16) * 16 + k%16
+ * ril_lm_head_fp8_packed_bytes: ceil(V/256)*256*K + 2*ceil(V/256)*(K/128)*4 bytes (0 for
+ * V < 1 or K not a positive multiple of 128).
+ * ril_pack_lm_head_fp8: enqueue, on `stream`, the quantization and packing of the
+ * row-major bf16 device matrix src[V, K] into dst (device, packed_bytes >= the size
+ * above, 16-byte aligned, not overlapping src); two kernels (block scales, then codes).
+ * Call it again after every weight update.  Returns RIL_EINVAL on bad sizes, alignment
+ * or a short dst, RIL_EHIP on a launch error. */
+size_t ril_lm_head_fp8_packed_bytes(int32_t vocab, int32_t d_head);
+
+/* The W8A8 head's activation quantization, for callers that quantize rows themselves
+ * (a trainer applying the deployment rule): enqueue, on `stream`, the block-FP8
+ * quantization of rows x rows of the bf16 device matrix src (row stride ld elements,
+ * K a positive multiple of 128, ld >= K and a multiple of 8) into the E4M3 codes
+ * codes[rows, K] (row-major, device) and the biased E8M0 exponents exps[rows, K/128]
+ * (int32 device, 127 + e, 255 = NaN), by the rule of RIL_LM_W8A8_FP8.  Pointers 16-byte
+ * (exps: 4-byte) aligned.  Returns RIL_EINVAL on bad sizes or pointers, RIL_EHIP on a
+ * launch error; rows = 0 enqueues nothing. */
+ril_status ril_quantize_rows_fp8(const void *src, int32_t rows, int32_t K, int32_t ld, void *codes, void *exps,
+                                 void *stream);
+ril_status ril_pack_lm_head_fp8(const void *src, int32_t vocab, int32_t d_head, void *dst, size_t packed_bytes,
+                                void *stream);
 
 /* S1: page assignment.  Wrap a caller-owned device pool of `pool_bytes`
  * bytes (16-byte aligned) as floor(pool_bytes / page_bytes) pages and build a
@@ -269,6 +315,19 @@ ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const ril_prefil
 ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
                                     float *logprob_out, void *ws, size_t ws_bytes, void *stream);
 
+/* The head alone (S11, S12): logprobs of target_ids[r] for normalised rows z (the final
+ * RMSNorm's output), through the model's lm-head (bf16 or W8A8 by lm_dtype), the same
+ * kernels and launch shapes the prefill and decode calls use for the same row count.  For
+ * callers that run the model body themselves and want the head's logprobs (and for
+ * checking the head at its own boundary).  z: device bf16 [rows, d_head], row stride ldz
+ * elements (>= d_head, a multiple of 8, 16-byte aligned); target_ids: device int32 [rows];
+ * logprob_out: device fp32 [rows] (NaN for a target outside [0, V)); rows in
+ * [0, max(max_rows, max_tokens)].  Returns RIL_EINVAL / RIL_ERANGE on bad arguments
+ * (nothing enqueued), RIL_EHIP on a launch error. */
+ril_status ril_lm_head_logprobs(const ril_model *m, int32_t rows, const void *z, int32_t ldz,
+                                const int32_t *target_ids, float *logprob_out, void *ws, size_t ws_bytes,
+                                void *stream);
+
 /* HIP-graph capture of one decode step, for steps whose launch overhead matters
  * (small batches, short contexts).
  *
@@ -320,7 +379,9 @@ enum {
   RIL_K_INDEXER = 8,      /* S6 */
   RIL_K_TOPK = 9,         /* S7 */
   RIL_K_SILU_MUL = 10,    /* the SwiGLU activation */
-  RIL_K_COUNT = 11
+  RIL_K_QUANT_ROWS = 11,  /* W8A8 head: block-FP8 activation quantization */
+  RIL_K_LM_HEAD_FP8 = 12, /* S11 in W8A8 block FP8 */
+  RIL_K_COUNT = 13
 };
 ril_status ril_trace_enable(int on);
 ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches);

@@ -28,6 +28,7 @@ RIL_ATTN_GQA, RIL_ATTN_MLA, RIL_ATTN_MLA_SPARSE = 0, 1, 2
 RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
 RIL_POLICY_INVARIANT, RIL_POLICY_SHAPE_DERIVED = 0, 1
 RIL_KV_BF16, RIL_KV_FP8_E4M3 = 0, 1
+RIL_LM_BF16, RIL_LM_W8A8_FP8 = 0, 1
 
 _c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -44,6 +45,7 @@ class ril_model_desc(ctypes.Structure):
         ("norm_final", _vp), ("w_lm", _vp),
         ("kv_dtype", _c_int), ("k_scale_exp", _c_int), ("v_scale_exp", _c_int),
         ("d_ff", _c_int), ("w_gate_up", _vp), ("w_down", _vp), ("norm_mlp", _vp),
+        ("lm_dtype", _c_int),
     ]
 
 
@@ -77,6 +79,11 @@ _workspace_bytes = _sig("ril_workspace_bytes", ctypes.c_size_t, [_vp])
 _kv_page_bytes = _sig("ril_kv_page_bytes", ctypes.c_size_t, [_vp])
 _lm_head_packed_bytes = _sig("ril_lm_head_packed_bytes", ctypes.c_size_t, [_c_int, _c_int])
 _pack_lm_head = _sig("ril_pack_lm_head", _c_int, [_vp, _c_int, _c_int, _vp, ctypes.c_size_t, _vp])
+_lm_head_fp8_packed_bytes = _sig("ril_lm_head_fp8_packed_bytes", ctypes.c_size_t, [_c_int, _c_int])
+_pack_lm_head_fp8 = _sig("ril_pack_lm_head_fp8", _c_int, [_vp, _c_int, _c_int, _vp, ctypes.c_size_t, _vp])
+_lm_head_logprobs = _sig("ril_lm_head_logprobs", _c_int,
+                         [_vp, _c_int, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp])
+_quantize_rows_fp8 = _sig("ril_quantize_rows_fp8", _c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
 _ws_attn_offset = _sig("ril_ws_attn_offset", ctypes.c_size_t, [_vp])
 _kv_alloc = _sig("ril_kv_alloc", _c_int, [_vp, _vp, ctypes.c_size_t, ctypes.c_uint64, ctypes.POINTER(_vp)])
 _kv_assign = _sig("ril_kv_assign", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)])
@@ -100,7 +107,8 @@ _trace_read = _sig("ril_trace_read", _c_int, [_c_int, ctypes.POINTER(ctypes.c_do
                                               ctypes.POINTER(ctypes.c_int64)])
 
 EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril_kv_page_bytes",
-            "ril_lm_head_packed_bytes", "ril_pack_lm_head",
+            "ril_lm_head_packed_bytes", "ril_pack_lm_head", "ril_lm_head_fp8_packed_bytes", "ril_pack_lm_head_fp8",
+            "ril_quantize_rows_fp8", "ril_lm_head_logprobs",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
             "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_set_policy", "ril_trace_enable",
@@ -109,9 +117,10 @@ EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril
 # kernel ids of the trace hook
 RIL_K_KV_WRITE, RIL_K_ATTN_SPLIT, RIL_K_ATTN_MERGE, RIL_K_ATTN_PREFILL = 0, 1, 2, 3
 RIL_K_RMSNORM, RIL_K_GEMM, RIL_K_LM_HEAD, RIL_K_VOCAB_MERGE = 4, 5, 6, 7
-RIL_K_INDEXER, RIL_K_TOPK, RIL_K_SILU_MUL, RIL_K_COUNT = 8, 9, 10, 11
+RIL_K_INDEXER, RIL_K_TOPK, RIL_K_SILU_MUL = 8, 9, 10
+RIL_K_QUANT_ROWS, RIL_K_LM_HEAD_FP8, RIL_K_COUNT = 11, 12, 13
 KERNEL_NAMES = ("kv_write", "attn_split", "attn_merge", "attn_prefill", "rmsnorm", "gemm", "lm_head",
-                "vocab_merge", "indexer", "topk", "silu_mul")
+                "vocab_merge", "indexer", "topk", "silu_mul", "quant_rows", "lm_head_fp8")
 
 
 class RilError(RuntimeError):
@@ -170,6 +179,40 @@ def ril_pack_lm_head(w, packed, stream=None) -> None:
     V, K = w.shape
     _check(_pack_lm_head(_ptr(w), V, K, _ptr(packed), packed.numel() * packed.element_size(), _stream(stream)),
            "ril_pack_lm_head")
+
+
+def ril_lm_head_fp8_packed_bytes(vocab: int, d_head: int) -> int:
+    return int(_lm_head_fp8_packed_bytes(vocab, d_head))
+
+
+def ril_pack_lm_head_fp8(w, packed, stream=None) -> None:
+    """Quantize the row-major bf16 device matrix w [V, K] to block FP8 and pack it into
+    `packed` (a device byte tensor of at least ril_lm_head_fp8_packed_bytes(V, K) bytes),
+    on the stream."""
+    V, K = w.shape
+    _check(_pack_lm_head_fp8(_ptr(w), V, K, _ptr(packed), packed.numel() * packed.element_size(),
+                             _stream(stream)), "ril_pack_lm_head_fp8")
+
+
+def ril_quantize_rows_fp8(x, codes, exps, stream=None) -> None:
+    """Block-FP8 quantization of the bf16 device rows x [rows, K] (row stride x.stride(0))
+    into codes (uint8 [rows, K]) and exps (int32 [rows, K/128], biased E8M0), on the
+    stream."""
+    rows, K = x.shape
+    if codes.numel() < rows * K or exps.numel() < rows * (K // 128):
+        raise ValueError("ril_quantize_rows_fp8: output tensors too small")
+    _check(_quantize_rows_fp8(_ptr(x), rows, K, x.stride(0), _ptr(codes), _ptr(exps), _stream(stream)),
+           "ril_quantize_rows_fp8")
+
+
+def ril_lm_head_logprobs(model: int, z, targets, logprob_out, ws, stream=None) -> None:
+    """The head alone: logprobs of targets (int32 device [rows]) for the normalised bf16
+    device rows z [rows, d_head] (row stride z.stride(0)) into logprob_out (fp32 [rows])."""
+    rows = z.shape[0]
+    if targets.numel() < rows or logprob_out.numel() < rows:
+        raise ValueError("ril_lm_head_logprobs: targets / logprob_out shorter than z")
+    _check(_lm_head_logprobs(model, rows, _ptr(z), z.stride(0), _ptr(targets), _ptr(logprob_out), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)), "ril_lm_head_logprobs")
 
 
 def ril_ws_attn_offset(model: int) -> int:

@@ -31,6 +31,8 @@ struct ril_model {
   size_t off_x, off_h, off_qkv, off_attn, off_y, off_z, off_vpart, off_tgt, off_po, off_pml;
   size_t off_scores, off_sel;  // sparse: indexer scores [max_rows, max_ctx], selections [max_rows, topk]
   size_t off_gu = 0, off_act = 0, off_y2 = 0;  // SwiGLU MLP: [R, 2F], [R, F], [R, d_model] bf16
+  bool lm_fp8 = false;                        // W8A8 block-FP8 lm-head
+  size_t off_a8 = 0, off_ea = 0;              // its activation codes [R, d_head], exponents [R, d_head/128]
   size_t ws_base;   // end of the invariant path's segments
   size_t ws_total;  // ws_base + the comparator's split-K partials when that policy is on
   // comparator (benchmarking only): RIL_POLICY_SHAPE_DERIVED picks splits from the batch
@@ -112,6 +114,10 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
     return fail(RIL_EINVAL, "model_create: the MLP block needs TOKENS input and 16-byte aligned w_gate_up/w_down");
   if (!d.d_ff && (d.w_gate_up || d.w_down || d.norm_mlp))
     return fail(RIL_EINVAL, "model_create: MLP weights given with d_ff = 0");
+  if (d.lm_dtype != RIL_LM_BF16 && d.lm_dtype != RIL_LM_W8A8_FP8)
+    return fail(RIL_EINVAL, "model_create: lm_dtype %d", d.lm_dtype);
+  if (d.lm_dtype == RIL_LM_W8A8_FP8 && (d.d_head <= 0 || d.d_head % 128))
+    return fail(RIL_EINVAL, "model_create: the W8A8 lm-head needs d_head a multiple of 128 (%d)", d.d_head);
   if (d.kv_dtype != RIL_KV_BF16 && d.kv_dtype != RIL_KV_FP8_E4M3)
     return fail(RIL_EINVAL, "model_create: kv_dtype %d", d.kv_dtype);
   if (d.kv_dtype == RIL_KV_FP8_E4M3 && mla)
@@ -170,6 +176,11 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
     m->off_gu = seg(R * 2 * (size_t)d.d_ff * 2);
     m->off_act = seg(R * (size_t)d.d_ff * 2);
     m->off_y2 = seg(R * (size_t)d.d_model * 2);
+  }
+  m->lm_fp8 = d.lm_dtype == RIL_LM_W8A8_FP8;
+  if (m->lm_fp8) {
+    m->off_a8 = seg(R * d.d_head);
+    m->off_ea = seg(R * (size_t)(d.d_head / 128) * sizeof(int32_t));
   }
   m->off_vpart = seg(R * m->n_vt * 2 * sizeof(float));
   m->off_tgt = seg(R * sizeof(float));
@@ -273,6 +284,39 @@ extern "C" ril_status ril_pack_lm_head(const void *src, int32_t vocab, int32_t d
   const hipError_t e = ril::launch_pack_lm_head((const bf16_t *)src, vocab, d_head, (bf16_t *)dst,
                                                 (hipStream_t)stream);
   if (e != hipSuccess) return fail(RIL_EHIP, "pack_lm_head: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
+extern "C" size_t ril_lm_head_fp8_packed_bytes(int32_t vocab, int32_t d_head) {
+  if (vocab < 1 || d_head < 128 || d_head % 128 != 0) return 0;
+  return (size_t)ril::lm_head_fp8_code_bytes(vocab, d_head) +
+         (size_t)ril::lm_head_fp8_exp_count(vocab, d_head) * sizeof(int32_t);
+}
+
+extern "C" ril_status ril_pack_lm_head_fp8(const void *src, int32_t vocab, int32_t d_head, void *dst,
+                                           size_t packed_bytes, void *stream) {
+  const size_t need = ril_lm_head_fp8_packed_bytes(vocab, d_head);
+  if (need == 0) return fail(RIL_EINVAL, "pack_lm_head_fp8: vocab must be >= 1 and d_head a positive multiple of 128");
+  if (!src || !dst) return fail(RIL_EINVAL, "pack_lm_head_fp8: src and dst are required");
+  if (((uintptr_t)src | (uintptr_t)dst) % 16) return fail(RIL_EINVAL, "pack_lm_head_fp8: pointers must be 16-byte aligned");
+  if (packed_bytes < need) return fail(RIL_EINVAL, "pack_lm_head_fp8: dst is smaller than ril_lm_head_fp8_packed_bytes");
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (size_t)vocab * d_head * 2, d0 = (uintptr_t)dst, d1 = d0 + need;
+  if (s0 < d1 && d0 < s1) return fail(RIL_EINVAL, "pack_lm_head_fp8: src and dst overlap");
+  uint8_t *codes = static_cast<uint8_t *>(dst);
+  int32_t *ew = reinterpret_cast<int32_t *>(codes + ril::lm_head_fp8_code_bytes(vocab, d_head));
+  const hipError_t e = ril::launch_pack_lm_head_fp8((const bf16_t *)src, vocab, d_head, codes, ew, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "pack_lm_head_fp8: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
+extern "C" ril_status ril_quantize_rows_fp8(const void *src, int32_t rows, int32_t K, int32_t ld, void *codes,
+                                            void *exps, void *stream) {
+  if (rows < 0 || K < 128 || K % 128 || ld < K || ld % 8)
+    return fail(RIL_EINVAL, "quantize_rows_fp8: rows %d, K %d, ld %d", rows, K, ld);
+  if (rows == 0) return RIL_OK;
+  if (!src || !codes || !exps || !aligned16(src) || !aligned16(codes) || !aligned4(exps))
+    return fail(RIL_EINVAL, "quantize_rows_fp8: null or misaligned pointer");
+  QuantRowsArgs q{(const bf16_t *)src, ld, rows, K, static_cast<uint8_t *>(codes), static_cast<int32_t *>(exps)};
+  const hipError_t e = launch_quant_rows_fp8(q, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "quantize_rows_fp8: %s", hipGetErrorString(e));
   return RIL_OK;
 }
 extern "C" size_t ril_ws_attn_offset(const ril_model *m) { return m ? m->off_attn : 0; }
@@ -458,6 +502,9 @@ static ril_status check_common(const ril_model *m, ril_kv *kv, void *ws, size_t 
   return RIL_OK;
 }
 
+static ril_status run_lm_head(const ril_model *m, int rows, const bf16_t *z, int ldz, const int32_t *targets,
+                              float *out, void *ws, hipStream_t st);
+
 // Attention output (in the workspace) -> [O GEMM (+ residual)] -> RMSNorm -> lm-head.
 static ril_status run_head(const ril_model *m, int rows, const int32_t *targets, float *out, void *ws,
                            hipStream_t st) {
@@ -495,9 +542,28 @@ static ril_status run_head(const ril_model *m, int rows, const int32_t *targets,
   RmsNormArgs r{src, ld, nullptr, nullptr, d.vocab, d.d_head, (const bf16_t *)d.norm_final, d.rms_eps,
                 wsb(ws, m->off_z), d.d_head, nullptr, 0, rows};
   RIL_LAUNCH(RIL_K_RMSNORM, launch_rmsnorm(r, st));
-  LmHeadArgs lh{wsb(ws, m->off_z), d.d_head, (const bf16_t *)d.w_lm, d.d_head, d.vocab, targets, rows,
+  return run_lm_head(m, rows, wsb(ws, m->off_z), d.d_head, targets, out, ws, st);
+}
+
+// Normalised rows z -> lm-head (bf16 or W8A8) -> vocabulary merge -> logprobs.
+static ril_status run_lm_head(const ril_model *m, int rows, const bf16_t *z, int ldz, const int32_t *targets,
+                              float *out, void *ws, hipStream_t st) {
+  const ril_model_desc &d = m->d;
+  LmHeadArgs lh{z, ldz, (const bf16_t *)d.w_lm, d.d_head, d.vocab, targets, rows,
                 wsf(ws, m->off_vpart), wsf(ws, m->off_tgt), out};
-  RIL_LAUNCH(RIL_K_LM_HEAD, launch_lm_head(lh, st));
+  if (m->lm_fp8) {
+    uint8_t *a8 = reinterpret_cast<uint8_t *>(ws) + m->off_a8;
+    int32_t *ea = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + m->off_ea);
+    QuantRowsArgs q{z, ldz, rows, d.d_head, a8, ea};
+    RIL_LAUNCH(RIL_K_QUANT_ROWS, launch_quant_rows_fp8(q, st));
+    lh.A8 = a8;
+    lh.ea = ea;
+    lh.W8 = static_cast<const uint8_t *>(d.w_lm);
+    lh.ew = reinterpret_cast<const int32_t *>(lh.W8 + ril::lm_head_fp8_code_bytes(d.vocab, d.d_head));
+    RIL_LAUNCH(RIL_K_LM_HEAD_FP8, launch_lm_head_fp8(lh, st));
+  } else {
+    RIL_LAUNCH(RIL_K_LM_HEAD, launch_lm_head(lh, st));
+  }
   RIL_LAUNCH(RIL_K_VOCAB_MERGE, launch_vocab_merge(lh, st));
   return RIL_OK;
 }
@@ -721,6 +787,23 @@ static ril_status decode_enqueue(const ril_model *m, ril_kv *kv, const ril_decod
   RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_attn_split(ad, st));
   RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_attn_merge(ad, st));
   return run_head(m, R, b->target_ids, logprob_out, ws, st);
+}
+
+extern "C" ril_status ril_lm_head_logprobs(const ril_model *m, int32_t rows, const void *z, int32_t ldz,
+                                           const int32_t *target_ids, float *logprob_out, void *ws,
+                                           size_t ws_bytes, void *stream) {
+  if (!m) return fail(RIL_EINVAL, "lm_head_logprobs: null model");
+  const int R = std::max(m->d.max_rows, m->d.max_tokens);
+  if (rows < 0 || rows > R) return fail(RIL_ERANGE, "lm_head_logprobs: rows %d outside [0, %d]", rows, R);
+  if (ldz < m->d.d_head || ldz % 8) return fail(RIL_EINVAL, "lm_head_logprobs: ldz %d", ldz);
+  if (!z || !aligned16(z) || !target_ids || !aligned4(target_ids) || !logprob_out || !aligned4(logprob_out))
+    return fail(RIL_EINVAL, "lm_head_logprobs: null or misaligned pointer");
+  if (!ws || !aligned16(ws)) return fail(RIL_EINVAL, "lm_head_logprobs: workspace null or misaligned");
+  if (ws_bytes < m->ws_total)
+    return fail(RIL_ERANGE, "lm_head_logprobs: workspace %zu bytes, %zu needed", ws_bytes, m->ws_total);
+  if (rows == 0) return RIL_OK;
+  hipStream_t st = (hipStream_t)stream;
+  return run_lm_head(m, rows, (const bf16_t *)z, ldz, target_ids, logprob_out, ws, st);
 }
 
 extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,

@@ -14,6 +14,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <utility>
 #include <stdint.h>
 
 namespace ril {
@@ -101,6 +102,62 @@ __device__ __forceinline__ float sum64(float v) {
   v = v + shfl_xor_f(v, 2);
   v = v + shfl_xor_f(v, 1);
   return v;
+}
+
+// LDS reads the compiler's wait pass does not track (inline asm, no memory clobber): the
+// data arrives by direct-to-LDS loads, and a tracked LDS read would make the pass wait
+// for every such load in flight.  Callers order them after the copies they read (vmcnt
+// wait + barrier), wait for them with lds_wait<N> (LDS reads complete in order, so at
+// most the N newest are then pending) and pass each value through settle() before use.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// base: this lane's LDS byte address; OFF: a byte offset common to all lanes, folded into
+// the instruction (< 65536)
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_rd128(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+// transposing read: lane i of each 16-lane group gets element i%4 of the 8-byte chunks
+// addressed by lanes 4e + i/4 of its group, e = 0..3
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_rdtr(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void settle(T &v) { asm volatile("" : "+v"(v)); }
+
+// Two OCP E4M3 codes (low 16 bits: a, then b) of values already multiplied by their
+// scale's inverse.  The hardware conversion rounds to nearest even but turns magnitudes
+// past 464 into NaN, so the clamp to +-448 (satfinite) comes first; NaN is encoded here
+// with its sign.
+__device__ __forceinline__ uint32_t fp8_codes2(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.f), 448.f), cb = fminf(fmaxf(b, -448.f), 448.f);
+  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xffffu;
+  if (a != a) r = (r & 0xff00u) | (0x7fu | ((__float_as_uint(a) >> 24) & 0x80u));
+  if (b != b) r = (r & 0x00ffu) | ((0x7fu | ((__float_as_uint(b) >> 24) & 0x80u)) << 8);
+  return r;
 }
 
 // Sequence lookup for packed token j: the s with cu[s] <= j < cu[s+1].

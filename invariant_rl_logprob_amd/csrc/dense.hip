@@ -10,6 +10,7 @@
 // never change that chain, and no K range is ever split across waves.
 #include "common.h"
 #include "kernels.h"
+#include "lm_head.h"
 
 namespace ril {
 
@@ -149,10 +150,7 @@ __device__ __forceinline__ void kloop(f32x4 (&acc)[MB][NB], const bf16_t *const 
 // The K loop with the activation operand staged through LDS, shared by the lm-head and
 // the few-row projections.  Every output column accumulates its 32-wide K steps in the
 // order r, r+1, ..., nk-1, 0, ..., r-1 (rot = r; 0 for the projections, so their order is
-// the plain 0, 32, 64, ... of kloop).  The lm-head picks r = (37 * tile) mod nk per
-// vocabulary tile: one order per column, chosen by the column alone (never by M, the
-// batch or the grid), which spreads the 505 tiles' concurrent weight reads over the HBM
-// channels instead of having every tile read the same K offset at the same time.
+// the plain 0, 32, 64, ... of kloop; lm_rot(tile) for the lm-head).
 // The activation operand is staged through LDS in chunks of 8 K steps (each of the four
 // waves loads two steps for the whole workgroup); weight operands run PF steps ahead in
 // a register ring.  wp[nb] points at MFMA block nb's first operand; step s's operand is
@@ -161,7 +159,6 @@ __device__ __forceinline__ void kloop(f32x4 (&acc)[MB][NB], const bf16_t *const 
 // grids that read each weight once.  All four waves must call this (it synchronises the
 // workgroup).
 constexpr int kLdsSteps = 8;
-__device__ __forceinline__ int lm_rot(int tile, int nk) { return (37 * tile) % nk; }
 
 template <int MB, int NB, int PF, int WSTEP, bool NT>
 __device__ __forceinline__ void kloop_lds(f32x4 (&acc)[MB][NB], const bf16_t *const (&ap)[MB],
@@ -328,13 +325,8 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restric
 }
 
 // ---------------------------------------------------------------------------
-// S11: logits of one 256-column vocabulary tile, never stored.  The tile's column
-// layout is fixed: wave w owns columns 64w .. 64w+63 as four 16-column MFMA blocks,
-// column 16nb + lane%16.  Per row: tile max, then
-//   s_t = ((S_0 + S_1) + S_2) + S_3,  S_w = xor-butterfly over 16 lanes of
-//         (((e_0 + e_1) + e_2) + e_3),  e = exp2((l - max) * log2 e)
-// and the target's logit if the target falls in the tile.  M rows per workgroup
-// (16*MB) are free: they never touch a row's reduction tree.
+// S11: logits of one 256-column vocabulary tile, never stored: the K loop here, the
+// tile's softmax partials in lm_tile_epilogue (lm_head.h).
 // ---------------------------------------------------------------------------
 // The weight W is in the packed layout written by pack_lm_head_kernel: per vocabulary
 // tile, per 16-column MFMA block, per 32-wide K step, the block's B operand in lane order
@@ -369,7 +361,6 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
   const int grp = lane >> 4, r16 = lane & 15;
   const int tile = ROWS_FAST ? blockIdx.y : blockIdx.x;
   const int m0 = (ROWS_FAST ? blockIdx.x : blockIdx.y) * 16 * MB;
-  const int c0 = tile * kVocabTile + wave * 64;
   const bf16_t *ap[MB];
   const bf16_t *wp[4];
 #pragma unroll
@@ -382,63 +373,7 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   kloop_lds<MB, 4, 7, 512, NT>(acc, ap, wp, K, lm_rot(tile, K / 32), lds_a);
-  bool cval[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) cval[nb] = (c0 + 16 * nb + r16) < V;
-  // tile max per row
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = neg_inf();
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) mx = fmaxf(mx, cval[nb] ? acc[mb][nb][i] : neg_inf());
-      mx = max16(mx);
-      if (r16 == 0) red[wave][16 * mb + 4 * grp + i] = mx;
-    }
-  }
-  __syncthreads();
-  float mt[MB][4];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mb + 4 * grp + i;
-      mt[mb][i] = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-    }
-  __syncthreads();
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float e[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        e[nb] = cval[nb] ? exp2f_hw((acc[mb][nb][i] - mt[mb][i]) * kLog2e) : 0.f;
-      float sm = ((e[0] + e[1]) + e[2]) + e[3];
-      sm = sum16(sm);
-      if (r16 == 0) red[wave][16 * mb + 4 * grp + i] = sm;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mb + 4 * grp + i;
-      const int row = m0 + r;
-      if (row >= M) continue;
-      if (wave == 0 && r16 == 0) {
-        const float st = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
-        part[((long)row * n_vt + tile) * 2] = mt[mb][i];
-        part[((long)row * n_vt + tile) * 2 + 1] = st;
-      }
-      const int tg = target[row];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        if (cval[nb] && c0 + 16 * nb + r16 == tg) tgt_logit[row] = acc[mb][nb][i];
-    }
-  }
+  lm_tile_epilogue<MB>(acc, red, tile, m0, M, V, target, part, tgt_logit, n_vt);
 }
 
 // ---------------------------------------------------------------------------

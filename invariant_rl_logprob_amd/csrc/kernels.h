@@ -98,6 +98,21 @@ struct LmHeadArgs {
   const int32_t *target;
   int M;
   float *part, *tgt_logit, *out;
+  // W8A8 head: activation codes [M, K] and biased E8M0 exponents [M, K/128]; the packed
+  // weight codes and their block exponents [2 * n_vt, K/128] (Z and W unused)
+  const uint8_t *A8 = nullptr;
+  const int32_t *ea = nullptr;
+  const uint8_t *W8 = nullptr;
+  const int32_t *ew = nullptr;
+};
+
+// Block-FP8 activation quantization: A8 = E4M3 codes of Z, ea = biased E8M0 exponents
+// of its 1 x 128 groups.
+struct QuantRowsArgs {
+  const bf16_t *Z;
+  int ldz, M, K;
+  uint8_t *A8;
+  int32_t *ea;
 };
 
 struct MlaKvWriteArgs {
@@ -162,5 +177,10 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);
 hipError_t launch_vocab_merge(const LmHeadArgs &a, hipStream_t st);
 long lm_head_packed_elems(int V, int K);
 hipError_t launch_pack_lm_head(const bf16_t *src, int V, int K, bf16_t *dst, hipStream_t st);
+hipError_t launch_quant_rows_fp8(const QuantRowsArgs &a, hipStream_t st);
+hipError_t launch_lm_head_fp8(const LmHeadArgs &a, hipStream_t st);
+long lm_head_fp8_code_bytes(int V, int K);
+long lm_head_fp8_exp_count(int V, int K);
+hipError_t launch_pack_lm_head_fp8(const bf16_t *src, int V, int K, uint8_t *codes, int32_t *ew, hipStream_t st);
 
 }  // namespace ril

@@ -1,0 +1,395 @@
+// W8A8 block-FP8 lm-head (Bitwise-consistent RL post, section 4.1: the deployment GEMM
+// is W8A8 with block-FP8 weights, and the trainer quantizes its bf16 weights to block
+// FP8 by the deployment rule and calls the same GEMM, one accumulation order for every M).
+//
+// Quantization (both operands, OCP E4M3 codes with E8M0 power-of-two scales):
+//   activations: per row, per group of 128 consecutive K values;
+//   weights:     per block of 128 vocabulary columns x 128 K values;
+//   scale 2^e, e the smallest integer >= -127 with amax <= 448 * 2^e (0 for an all-zero
+//   group; the E8M0 NaN code 255 for a group holding an infinity or NaN); the code of x
+//   is e4m3(x * 2^-e), nearest even, which never leaves the E4M3 range.
+// Product: one v_mfma_scale_f32_16x16x128_f8f6f4 per 128-wide K step and 16 x 16 block,
+// its E8M0 operands the row's and the weight block's scales, accumulating in fp32 in the
+// lm-head's fixed per-column K order (lm_rot).  A row's logits depend on its own codes,
+// its scales and the column's order only, never on M, the batch or the grid.
+#include "common.h"
+#include "kernels.h"
+#include "lm_head.h"
+
+namespace ril {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// D += A B^T over one 128-wide K step with per-lane E8M0 scales (biased exponents in the
+// low byte of sa, sb).  A lane's 32 code bytes are row (column) lane%16 at K offsets
+// 32*(lane/16) + 0..31; the hardware groups the K values into four 32-wide scale blocks
+// that straddle lane groups, which does not matter here: all four of a row's lanes carry
+// the same scale.
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Biased E8M0 exponent of a group from the bits of its largest magnitude (a
+// non-negative float): 127 + max(e, -127), e the smallest integer with amax <= 448 * 2^e
+// (amax = m 2^E with 1 <= m < 2 needs e = E - 8, or E - 7 when m > 1.75); 127 for 0;
+// 255 (NaN) when amax is not finite.
+__device__ __forceinline__ int e8m0_of_amax(uint32_t u) {
+  if (u >= 0x7f800000u) return 255;
+  if (u == 0) return 127;
+  const int ef = (int)(u >> 23);                 // 0 for subnormals: clamped below
+  const int e = ef - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return 127 + (e < -127 ? -127 : e);
+}
+
+// ---------------------------------------------------------------------------
+// Activation quantization: Z [M, K] bf16 (row stride ldz) -> A8 [M, K] codes and
+// ea [M, K/128] biased exponents.  16 lanes per group, 8 values per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const bf16_t *__restrict__ Z, int ldz, int M,
+                                                             int K, uint8_t *__restrict__ A8,
+                                                             int32_t *__restrict__ ea) {
+  const int nk = K >> 7;
+  const long gidx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long g = gidx >> 4;  // group (row, kb); every lane of a 16-lane group shares it
+  const int part = (int)(gidx & 15);
+  const bool live = g < (long)M * nk;
+  const int row = live ? (int)(g / nk) : 0, kb = live ? (int)(g % nk) : 0;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (live) v = ld16(Z + (long)row * ldz + kb * 128 + part * 8);
+  // largest magnitude as bits: integer order of |bf16| bits is value order, NaN above inf
+  uint32_t mag = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mag = max(mag, v[j] & 0x7fffu);
+    mag = max(mag, (v[j] >> 16) & 0x7fffu);
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
+  const int be = e8m0_of_amax(mag << 16);
+  const int sh = be == 255 ? 0 : 127 - be;  // multiply by 2^-e (exact: no overflow, see above)
+  uint32_t w[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t lo = fp8_codes2(__builtin_ldexpf(bf2f((bf16_t)(v[2 * j] & 0xffffu)), sh),
+                                   __builtin_ldexpf(bf2f((bf16_t)(v[2 * j] >> 16)), sh));
+    const uint32_t hi = fp8_codes2(__builtin_ldexpf(bf2f((bf16_t)(v[2 * j + 1] & 0xffffu)), sh),
+                                   __builtin_ldexpf(bf2f((bf16_t)(v[2 * j + 1] >> 16)), sh));
+    w[j] = lo | (hi << 16);
+  }
+  if (live) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    *(u32x2_t __attribute__((address_space(1))) *)(A8 + (long)row * K + kb * 128 + part * 8) = u32x2_t{w[0], w[1]};
+    if (part == 0) ea[(long)row * nk + kb] = be;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing.  Exponents: ew [2 * n_vt, K/128] biased, one per 128 x 128 block
+// (columns past V count as zero).  Codes, per vocabulary tile, per 128-wide K step, one
+// contiguous 32 KB piece: the step's B operands of the tile's sixteen 16-column MFMA
+// blocks in lane order, each lane's 32 bytes split in two 16-byte halves 1 KB apart, so
+// every weight load of a wave is one contiguous 1 KB and a workgroup's reads of a step
+// are one 32 KB run (measured: the full-rate streaming pattern; blocks kept apart by the
+// K extent read about 10% slower):
+//   W(c, k) -> ((c/256) * (K/128) + k/128) * 32768 + ((c%256)/16) * 2048
+//              + ((k%32)/16) * 1024 + (((k%128)/32) * 16 + c%16) * 16 + k%16
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_fp8_exp_kernel(const bf16_t *__restrict__ src, int V, int K,
+                                                           int32_t *__restrict__ ew) {
+  __shared__ uint32_t red[4];
+  const int b = blockIdx.x, kb = blockIdx.y, nk = K >> 7;
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const long c = (long)b * 128 + r;
+  uint32_t mag = 0;
+  if (c < V) {
+    const bf16_t *p = src + c * K + kb * 128 + half * 64;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 v = ld16(p + q * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mag = max(mag, v[j] & 0x7fffu);
+        mag = max(mag, (v[j] >> 16) & 0x7fffu);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mag;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+    ew[(long)b * nk + kb] = e8m0_of_amax(m << 16);
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_fp8_codes_kernel(const bf16_t *__restrict__ src, int V, int K,
+                                                             const int32_t *__restrict__ ew,
+                                                             uint8_t *__restrict__ dst, long n_pieces) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_pieces) return;
+  const int nk = K >> 7;
+  const int lane = (int)(i & 63), h = (int)((i >> 6) & 1), blk = (int)((i >> 7) & 15);
+  const long ts = i >> 11;  // tile * nk + step
+  const int step = (int)(ts % nk);
+  const long c = (ts / nk) * 256 + blk * 16 + (lane & 15);
+  const int k = step * 128 + (lane >> 4) * 32 + h * 16;
+  u32x4 out = u32x4{0u, 0u, 0u, 0u};
+  if (c < V) {
+    const int be = ew[(c >> 7) * nk + step];
+    const int sh = be == 255 ? 0 : 127 - be;
+    const u32x4 v0 = ld16(src + c * K + k), v1 = ld16(src + c * K + k + 8);
+    uint32_t hw[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hw[j] = fp8_codes2(__builtin_ldexpf(bf2f((bf16_t)(v0[j] & 0xffffu)), sh),
+                         __builtin_ldexpf(bf2f((bf16_t)(v0[j] >> 16)), sh));
+      hw[4 + j] = fp8_codes2(__builtin_ldexpf(bf2f((bf16_t)(v1[j] & 0xffffu)), sh),
+                             __builtin_ldexpf(bf2f((bf16_t)(v1[j] >> 16)), sh));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = hw[2 * j] | (hw[2 * j + 1] << 16);
+  }
+  st16(dst + i * 16, out);
+}
+
+// ---------------------------------------------------------------------------
+// The W8A8 lm-head: one 256-column vocabulary tile of 16*MB rows per workgroup, the same
+// column layout and epilogue as the bf16 head.  K runs in chunks of R = PF + 1 steps of
+// 128; weight operands run PF steps ahead in a register ring of R slots.  The activation
+// codes and row scales of chunk c+1 are loaded into registers during chunk c and written
+// to the other half of a double LDS buffer at the start of chunk c+1, so the weight
+// stream never waits for them.  Every load is unconditional (steps past the end re-read
+// the last step) and the LDS copy is one chunk ahead, which keeps the compiler's vmcnt
+// waits for the ring exact.  The MFMA operands are read from LDS by untracked inline asm
+// with counted lgkmcnt waits (the wave's own stores precede the barrier that publishes
+// them).  NT: the weights are streamed with the nontemporal policy (grids that read each
+// weight once).  The weight block scales of the tile's two 128-column blocks sit in LDS
+// for the whole kernel (K <= 128 * kF8MaxSteps).
+// ---------------------------------------------------------------------------
+constexpr int kF8MaxSteps = 256;
+
+// The LDS stores below are read only by untracked inline asm, which the compiler does not
+// see as a reader: without this fence it may drop them as dead.  An asm memory clobber
+// counts as a read of every LDS array whose address escaped into asm (all of them here).
+__device__ __forceinline__ void lds_publish() { asm volatile("" ::: "memory"); }
+
+template <int OFF>
+__device__ __forceinline__ int lds_rd32(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  int r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+
+template <int MB, bool NT, bool ROWS_FAST, int PF = 1>
+__global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restrict__ A8,
+                                                          const int32_t *__restrict__ ea, int K,
+                                                          const uint8_t *__restrict__ W8,
+                                                          const int32_t *__restrict__ ew, int V,
+                                                          const int32_t *__restrict__ target, int M,
+                                                          float *__restrict__ part,
+                                                          float *__restrict__ tgt_logit, int n_vt) {
+  constexpr int R = PF + 1;                   // ring slots = K steps per chunk
+  constexpr int ABLK = R * MB * 2;            // 1 KB activation blocks per chunk: (step, mb, half)
+  constexpr int NE = R * MB * 16;             // row scales per chunk: (step, mb, row)
+  constexpr int NEB = (NE + 63) / 64;         // ... in 64-entry copies
+  constexpr int ACOPY = (ABLK + 3) / 4, ECOPY = (NEB + 3) / 4;  // copies per wave per chunk
+  __shared__ float red[4][16 * MB];
+  __shared__ u32x4 lds_a[2][ABLK * 64];
+  __shared__ int32_t lds_e[2][NEB * 64];
+  __shared__ int32_t lds_w[2][kF8MaxSteps];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15;
+  const int tile = ROWS_FAST ? blockIdx.y : blockIdx.x;
+  const int m0 = (ROWS_FAST ? blockIdx.x : blockIdx.y) * 16 * MB;
+  const int nk = K >> 7;
+  const int rot = lm_rot(tile, nk);
+  auto kidx = [&](int s) {  // the K block of step s (steps past the end re-read the last)
+    const int t = (s < nk ? s : nk - 1) + rot;
+    return t >= nk ? t - nk : t;
+  };
+  auto ldw = [&](const uint8_t *p) -> u32x4 {
+    if (NT) return __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(p));
+    return ld16(p);
+  };
+  const uint8_t *wp[4];  // block nb of this wave in step 0 of the tile; step s is s * 32 KB on
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) wp[nb] = W8 + (long)tile * nk * 32768 + (wave * 4 + nb) * 2048 + lane * 16;
+
+  // Chunk c's activation blocks and row scales: loaded into registers (issue), then
+  // stored to buffer buf (commit).  Every wave takes the same number of pieces: where the
+  // blocks do not divide among the waves, the last block is copied again, with the same
+  // bytes.  Row scale entries past NE (a step index >= R) are copied but never read.
+  u32x4 sreg[ACOPY];
+  int ereg[ECOPY];
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < ACOPY; ++i) {
+      const int q = min(i * 4 + wave, ABLK - 1);
+      const int st = q / (2 * MB), mb = (q >> 1) % MB, h = q & 1;
+      const int row = min(m0 + 16 * mb + r16, M - 1);
+      sreg[i] = ld16(A8 + (long)row * K + kidx(c * R + st) * 128 + (lane >> 4) * 32 + h * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < ECOPY; ++i) {
+      const int b = min(i * 4 + wave, NEB - 1), e = b * 64 + lane;
+      const int st = e / (16 * MB), mb = (e >> 4) % MB, r = e & 15;
+      ereg[i] = ea[(long)min(m0 + 16 * mb + r, M - 1) * nk + kidx(c * R + st)];
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ACOPY; ++i) {
+      const int q = min(i * 4 + wave, ABLK - 1);
+      lds_a[buf][q * 64 + lane] = sreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < ECOPY; ++i) {
+      const int b = min(i * 4 + wave, NEB - 1);
+      lds_e[buf][b * 64 + lane] = ereg[i];
+    }
+    lds_publish();
+  };
+
+  // the weight block scales of the tile's two blocks, chunk 0 in buffer 0, chunk 1 in
+  // registers; the first barrier in the loop publishes them
+  for (int i = threadIdx.x; i < 2 * nk; i += 256) lds_w[i / nk][i % nk] = ew[(long)(tile * 2) * nk + i];
+  issue(0);
+  commit(0);
+  issue(1);
+  u32x4 rb[R][4][2];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    const long off = (long)kidx(s) * 32768;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      rb[s][nb][0] = ldw(wp[nb] + off);
+      rb[s][nb][1] = ldw(wp[nb] + off + 1024);
+    }
+  }
+
+  f32x4 acc[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t a_lane = lds_addr(&lds_a[0][0]) + lane * 16;
+  const uint32_t e_lane = lds_addr(&lds_e[0][0]) + r16 * 4;
+  const uint32_t w_base = lds_addr(&lds_w[wave >> 1][0]);
+  const int nck = (nk + R - 1) / R;
+  for (int c = 0; c < nck; ++c) {
+    const int buf = c & 1;
+    if (c > 0) {  // buffer buf was last read in chunk c-2, before the previous barrier
+      commit(buf);
+      issue(c + 1);
+    }
+    __syncthreads();  // chunk c (and, at c = 0, the weight scales) published
+    const uint32_t a_base = a_lane + buf * (ABLK * 1024), e_base = e_lane + buf * (NEB * 256);
+    static_for<R>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int ks = c * R + j;
+      {
+        const long off = (long)kidx(ks + PF) * 32768;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          rb[(j + PF) % R][nb][0] = ldw(wp[nb] + off);
+          rb[(j + PF) % R][nb][1] = ldw(wp[nb] + off + 1024);
+        }
+      }
+      if (ks < nk) {
+        int sb;
+        const uint32_t w_addr = w_base + kidx(ks) * 4;
+        asm volatile("ds_read_b32 %0, %1" : "=v"(sb) : "v"(w_addr));
+        u32x4 alo[MB], ahi[MB];
+        int sa[MB];
+        static_for<MB>([&](auto mc) {
+          constexpr int mb = decltype(mc)::value;
+          alo[mb] = lds_rd128<((j * MB + mb) * 2) * 1024>(a_base);
+          ahi[mb] = lds_rd128<((j * MB + mb) * 2 + 1) * 1024>(a_base);
+          sa[mb] = lds_rd32<(j * MB + mb) * 64>(e_base);
+        });
+        static_for<MB>([&](auto mc) {
+          constexpr int mb = decltype(mc)::value;
+          lds_wait<3 * (MB - 1 - mb)>();  // sb and the operands of blocks 0 .. mb are in
+          settle(alo[mb]);
+          settle(ahi[mb]);
+          settle(sa[mb]);
+          if (mb == 0) settle(sb);
+          const i32x8 a = cat8(alo[mb], ahi[mb]);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = mfma_fp8(a, cat8(rb[j][nb][0], rb[j][nb][1]), acc[mb][nb], sa[mb], sb);
+        });
+      }
+    });
+  }
+  lm_tile_epilogue<MB>(acc, red, tile, m0, M, V, target, part, tgt_logit, n_vt);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_quant_rows_fp8(const QuantRowsArgs &a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  const long threads = (long)a.M * (a.K / 128) * 16;
+  const long blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.Z, a.ldz, a.M, a.K, a.A8,
+                     a.ea);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_head_fp8(const LmHeadArgs &a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  const int n_vt = (a.V + kVocabTile - 1) / kVocabTile;
+  const int mb = a.M <= 16 ? 1 : 4;
+  const int n_rt = (a.M + 16 * mb - 1) / (16 * mb);
+  // the grid choice of the bf16 head: up to two row tiles stream the weights (NT), more
+  // run the row tiles of one vocabulary tile back to back; neither changes a K order
+  if (n_rt <= 2) {
+    dim3 grid(n_vt, n_rt);
+    if (mb == 1)
+      hipLaunchKernelGGL((lm_head_fp8_kernel<1, true, false>), grid, dim3(256), 0, st, a.A8, a.ea, a.K, a.W8,
+                         a.ew, a.V, a.target, a.M, a.part, a.tgt_logit, n_vt);
+    else
+      hipLaunchKernelGGL((lm_head_fp8_kernel<4, true, false>), grid, dim3(256), 0, st, a.A8, a.ea, a.K, a.W8,
+                         a.ew, a.V, a.target, a.M, a.part, a.tgt_logit, n_vt);
+  } else {
+    dim3 grid(n_rt, n_vt);
+    hipLaunchKernelGGL((lm_head_fp8_kernel<4, false, true>), grid, dim3(256), 0, st, a.A8, a.ea, a.K, a.W8, a.ew,
+                       a.V, a.target, a.M, a.part, a.tgt_logit, n_vt);
+  }
+  return hipGetLastError();
+}
+
+long lm_head_fp8_code_bytes(int V, int K) {
+  const long n_vt = (V + kVocabTile - 1) / kVocabTile;
+  return n_vt * kVocabTile * (long)K;
+}
+
+long lm_head_fp8_exp_count(int V, int K) {
+  const long n_vt = (V + kVocabTile - 1) / kVocabTile;
+  return n_vt * 2 * (long)(K / 128);
+}
+
+hipError_t launch_pack_lm_head_fp8(const bf16_t *src, int V, int K, uint8_t *codes, int32_t *ew, hipStream_t st) {
+  const int n_vt = (V + kVocabTile - 1) / kVocabTile;
+  const long n_pieces = lm_head_fp8_code_bytes(V, K) / 16;
+  if (n_pieces == 0) return hipSuccess;
+  const long blocks = (n_pieces + 255) / 256;
+  if (blocks > 0x7fffffffL || K / 128 > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_fp8_exp_kernel, dim3(2 * n_vt, K / 128), dim3(256), 0, st, src, V, K, ew);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_fp8_codes_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, V, K, ew, codes,
+                     n_pieces);
+  return hipGetLastError();
+}
+
+}  // namespace ril

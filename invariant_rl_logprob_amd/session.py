@@ -17,6 +17,8 @@ from . import (RIL_ATTN_GQA, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch,
                ril_decode_graph_create, ril_decode_step_logprobs, ril_graph_destroy, ril_graph_launch, ril_kv_alloc, ril_kv_assign, ril_kv_free, ril_kv_page_bytes,
                ril_kv_release, ril_kv_write, ril_lm_head_packed_bytes, ril_model_create, ril_model_desc,
                ril_model_destroy, ril_pack_lm_head, ril_prefill_logprobs, ril_set_policy,
+               ril_lm_head_fp8_packed_bytes, ril_pack_lm_head_fp8, RIL_LM_BF16, RIL_LM_W8A8_FP8,
+               ril_lm_head_logprobs,
                ril_workspace_bytes, ril_ws_attn_offset)
 
 PAGE = 16
@@ -42,20 +44,23 @@ class Session:
                  input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
                  norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, index_heads=0, index_dim=0, topk=0,
                  kv_dtype=0, k_scale_exp=0, v_scale_exp=0, d_ff=0, w_gate_up=None, w_down=None, norm_mlp=None,
-                 device="cuda"):
+                 lm_dtype=RIL_LM_BF16, device="cuda"):
         self.device = torch.device(device)
-        # the lm-head weight lives in the library's packed layout (w_lm stays row-major)
+        # the lm-head weight lives in the library's packed layout (w_lm stays row-major):
+        # bf16 operands, or block-FP8 codes and scales for the W8A8 head
         w_lm = w_lm.contiguous()
-        self.w_lm_packed = torch.empty(ril_lm_head_packed_bytes(vocab, d_head), dtype=torch.uint8,
-                                       device=self.device)
-        ril_pack_lm_head(w_lm, self.w_lm_packed)
+        fp8 = lm_dtype == RIL_LM_W8A8_FP8
+        nbytes = (ril_lm_head_fp8_packed_bytes if fp8 else ril_lm_head_packed_bytes)(vocab, d_head)
+        self.w_lm_packed = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.pack_lm_head = ril_pack_lm_head_fp8 if fp8 else ril_pack_lm_head
+        self.pack_lm_head(w_lm, self.w_lm_packed)
         self._keep = [embed, w_qkv, w_o, norm_attn, norm_final, w_gate_up, w_down, norm_mlp]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
                                    index_heads, index_dim, topk, d_head, vocab, PAGE, split_tokens, max_rows,
                                    max_tokens, max_ctx, softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o),
                                    p(norm_attn), p(norm_final), p(self.w_lm_packed), kv_dtype, k_scale_exp,
-                                   v_scale_exp, d_ff, p(w_gate_up), p(w_down), p(norm_mlp))
+                                   v_scale_exp, d_ff, p(w_gate_up), p(w_down), p(norm_mlp), lm_dtype)
         self.model = ril_model_create(self.desc)
         self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
         self.max_ctx = max_ctx
@@ -65,6 +70,12 @@ class Session:
         self.kv = ril_kv_alloc(self.model, self.pool, shuffle_seed)
         self.pages: Dict[object, List[int]] = {}
         self._ids: Dict[object, torch.Tensor] = {}  # page lists as int32 tensors, per sequence
+
+    def lm_head(self, z, targets) -> torch.Tensor:
+        """The head alone: logprobs (fp32 [rows]) of targets for normalised bf16 rows z."""
+        out = torch.empty(z.shape[0], dtype=torch.float32, device=self.device)
+        ril_lm_head_logprobs(self.model, z, _i32(targets, self.device), out, self.ws)
+        return out
 
     def set_policy(self, policy: int, attn_split_tokens: int = 0) -> None:
         """Switch the comparator policy (benchmarking only) and grow the workspace if

@@ -15,6 +15,7 @@ import math
 import numpy as np
 
 from .numerics import attention_row, bf16, lm_head_logprob, log_softmax_at, rmsnorm, swiglu_rounded_once, widen
+from .fp8block import lm_head_logprob_w8a8
 
 
 # ---------------------------------------------------------------------------
@@ -164,7 +165,7 @@ def gqa_row_attention(q, K, V, scale: float) -> np.ndarray:
     return out
 
 
-def gqa_row_logprob(q, K, V, scale, w_lm, target, eps=1e-6, w_o=None, gain=None) -> float:
+def gqa_row_logprob(q, K, V, scale, w_lm, target, eps=1e-6, w_o=None, gain=None, lm_w8a8=False) -> float:
     """Logprob of ``target`` for one decode row whose q/K/V are given.
 
     Reading of the head (the pages name none for this case): the attention
@@ -172,16 +173,19 @@ def gqa_row_logprob(q, K, V, scale, w_lm, target, eps=1e-6, w_o=None, gain=None)
     ``w_o`` (bf16 output), normalised by RMSNorm (gain 1 unless given, bf16
     output) and fed to the lm-head; logits stay float64.
     """
-    return head_logprob(gqa_row_attention(q, K, V, scale), w_lm, target, eps, w_o, gain)
+    return head_logprob(gqa_row_attention(q, K, V, scale), w_lm, target, eps, w_o, gain, lm_w8a8)
 
 
-def head_logprob(o, w_lm, target, eps=1e-6, w_o=None, gain=None) -> float:
+def head_logprob(o, w_lm, target, eps=1e-6, w_o=None, gain=None, lm_w8a8=False) -> float:
     """The head after attention: bf16 attention output, flattened head-major, an
-    optional projection (bf16 output), bf16(RMSNorm), then the lm-head logprob."""
+    optional projection (bf16 output), bf16(RMSNorm), then the lm-head logprob, with
+    bf16 weights or (lm_w8a8) the block-FP8 W8A8 product of fp8block.py."""
     o = bf16(np.asarray(o, dtype=np.float64)).reshape(-1)
     if w_o is not None:
         o = bf16(widen(w_o) @ o)
     z = bf16(rmsnorm(o, gain, eps))
+    if lm_w8a8:
+        return lm_head_logprob_w8a8(z, widen(w_lm), target)
     return lm_head_logprob(z, w_lm, target)
 
 

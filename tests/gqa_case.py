@@ -16,9 +16,10 @@ from invariant_rl_logprob_amd.session import Session
 class GQACase:
     def __init__(self, w: wl.GQADecode, rows: Sequence[int], *, ctx: Sequence[int] = None,
                  device="cuda", shuffle_seed=1234, copies=2, max_tokens=None, head=None, kv_dtype=0,
-                 k_scale_exp=0, v_scale_exp=0):
+                 k_scale_exp=0, v_scale_exp=0, lm_dtype=0):
         self.w = w
         self.kv = (kv_dtype, k_scale_exp, v_scale_exp)
+        self.lm_dtype = lm_dtype
         self.rows = list(rows)
         self.device = device
         self.data: Dict[int, dict] = {}
@@ -33,7 +34,7 @@ class GQACase:
                             max_rows=max(len(self.rows), 1), max_tokens=max_tokens or len(self.rows) * R,
                             max_ctx=max_ctx, pool_pages=pages, softmax_scale=1.0 / math.sqrt(w.head_dim),
                             rms_eps=w.rms_eps, shuffle_seed=shuffle_seed, kv_dtype=kv_dtype,
-                            k_scale_exp=k_scale_exp, v_scale_exp=v_scale_exp, device=device)
+                            k_scale_exp=k_scale_exp, v_scale_exp=v_scale_exp, lm_dtype=lm_dtype, device=device)
 
     def ctx(self, r):
         return self.data[r]["ctx"]
@@ -114,5 +115,6 @@ class GQACase:
         w_o = self.head.get("w_o")
         lp = oracle.gqa_row_logprob(q, K, V, scale, self.head["w_lm"].float().cpu().numpy(),
                                     int(d["target"][R - back]), self.w.rms_eps,
-                                    w_o=None if w_o is None else w_o.float().cpu().numpy())
+                                    w_o=None if w_o is None else w_o.float().cpu().numpy(),
+                                    lm_w8a8=self.lm_dtype == 1)
         return lp, o

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared():
     src = open(os.path.join(ROOT, "include", "ril.h")).read()
-    return sorted(set(re.findall(r"\b(ril_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ril_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -87,6 +87,47 @@ def test_mlp_block_descriptor():
         with pytest.raises(ril.RilError):
             ril.ril_model_create(_desc(**b))
         assert ril.ril_last_error()
+
+
+def test_w8a8_lm_head_descriptor_and_sizes():
+    m = ril.ril_model_create(_desc(lm_dtype=ril.RIL_LM_W8A8_FP8))
+    plain = ril.ril_model_create(_desc())
+    # activation codes (1 byte / value) and exponents (4 bytes / 128 values) per row
+    R = 1024
+    assert ril.ril_workspace_bytes(m) - ril.ril_workspace_bytes(plain) >= R * 4096 + R * 32 * 4
+    ril.ril_model_destroy(m)
+    ril.ril_model_destroy(plain)
+    for b in (dict(lm_dtype=2), dict(lm_dtype=-1), dict(lm_dtype=ril.RIL_LM_W8A8_FP8, d_head=4064)):
+        with pytest.raises(ril.RilError):
+            ril.ril_model_create(_desc(**b))
+        assert ril.ril_last_error()
+    n_vt = (129280 + 255) // 256
+    assert ril.ril_lm_head_fp8_packed_bytes(129280, 4096) == n_vt * 256 * 4096 + 2 * n_vt * 32 * 4
+    assert ril.ril_lm_head_fp8_packed_bytes(300, 128) == 512 * 128 + 4 * 1 * 4
+    for v, k in ((0, 128), (10, 96), (10, 0), (10, 4000)):
+        assert ril.ril_lm_head_fp8_packed_bytes(v, k) == 0
+
+
+def test_w8a8_pack_and_quantize_reject_bad_arguments():
+    lib = ctypes.CDLL(ril.LIB_PATH)
+    lib.ril_pack_lm_head_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+    lib.ril_quantize_rows_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    need = ril.ril_lm_head_fp8_packed_bytes(300, 256)
+    # every case fails validation before anything is enqueued
+    assert lib.ril_pack_lm_head_fp8(0x10000, 300, 200, 0x900000, need, None) == ril.RIL_EINVAL   # K % 128
+    assert lib.ril_pack_lm_head_fp8(0x10000, 300, 256, 0x900000, need - 1, None) == ril.RIL_EINVAL
+    assert lib.ril_pack_lm_head_fp8(0x10008, 300, 256, 0x900000, need, None) == ril.RIL_EINVAL   # misaligned
+    assert lib.ril_pack_lm_head_fp8(0x10000, 300, 256, 0x10000, need, None) == ril.RIL_EINVAL    # overlap
+    assert lib.ril_pack_lm_head_fp8(None, 300, 256, 0x900000, need, None) == ril.RIL_EINVAL
+    assert lib.ril_quantize_rows_fp8(0x10000, 4, 200, 256, 0x20000, 0x30000, None) == ril.RIL_EINVAL  # K % 128
+    assert lib.ril_quantize_rows_fp8(0x10000, 4, 256, 128, 0x20000, 0x30000, None) == ril.RIL_EINVAL  # ld < K
+    assert lib.ril_quantize_rows_fp8(0x10000, 4, 256, 260, 0x20000, 0x30000, None) == ril.RIL_EINVAL  # ld % 8
+    assert lib.ril_quantize_rows_fp8(0x10000, -1, 256, 256, 0x20000, 0x30000, None) == ril.RIL_EINVAL
+    assert lib.ril_quantize_rows_fp8(0x10000, 4, 256, 256, 0x20008, 0x30000, None) == ril.RIL_EINVAL  # codes align
+    assert lib.ril_quantize_rows_fp8(0x10000, 4, 256, 256, 0x20000, 0x30002, None) == ril.RIL_EINVAL  # exps align
+    assert lib.ril_quantize_rows_fp8(0x10000, 0, 256, 256, 0x20000, 0x30000, None) == ril.RIL_OK      # nothing to do
 
 
 def test_workspace_monotone_in_limits():
