@@ -255,12 +255,17 @@ __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restr
     lds_publish();
   };
 
-  // the weight block scales of the tile's two blocks, chunk 0 in buffer 0, chunk 1 in
-  // registers; the first barrier in the loop publishes them
-  for (int i = threadIdx.x; i < 2 * nk; i += 256) lds_w[i / nk][i % nk] = ew[(long)(tile * 2) * nk + i];
+  // Prologue: the loads of the weight block scales (the tile's two blocks), of chunk 0 and
+  // of the ring's first PF steps all go out before any of them is waited for; then the
+  // scales and chunk 0 go to LDS and chunk 1 is loaded.  The first barrier in the loop
+  // publishes the LDS contents.
+  int wsc[(2 * kF8MaxSteps + 255) / 256];
+#pragma unroll
+  for (int q = 0; q < (2 * kF8MaxSteps + 255) / 256; ++q) {
+    const int i = q * 256 + threadIdx.x;
+    wsc[q] = ew[(long)(tile * 2) * nk + min(i, 2 * nk - 1)];
+  }
   issue(0);
-  commit(0);
-  issue(1);
   u32x4 rb[R][4][2];
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
@@ -271,6 +276,13 @@ __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restr
       rb[s][nb][1] = ldw(wp[nb] + off + 1024);
     }
   }
+#pragma unroll
+  for (int q = 0; q < (2 * kF8MaxSteps + 255) / 256; ++q) {
+    const int i = q * 256 + threadIdx.x;
+    if (i < 2 * nk) lds_w[i / nk][i % nk] = wsc[q];
+  }
+  commit(0);
+  issue(1);
 
   f32x4 acc[MB][4];
 #pragma unroll
