@@ -284,7 +284,8 @@ def bench_gqa(args, fp8=False, lm8=False):
     split_gbps = (kv_bytes + q_bytes) / (split_us * 1e-6) / 1e9
     lm_gbps = lm_bytes / (lm_us * 1e-6) / 1e9
     if split_us >= lm_us:
-        roof = roofline_hbm("attn_decode_split", split_gbps, kv_bytes + q_bytes, split_us)
+        roof = roofline_hbm("attn_decode_split_fp8" if fp8 else "attn_decode_split", split_gbps, kv_bytes + q_bytes,
+                            split_us)
     else:
         roof = roofline_hbm(lm_name, lm_gbps, lm_bytes, lm_us)
 
