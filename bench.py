@@ -35,6 +35,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 METRIC = "invariant decode tokens/s + attn HBM GB/s at diff=0 (prefill vs decode)"
 
 
@@ -57,6 +58,86 @@ def measured_traffic(kernel: str):
     if h.hexdigest()[:16] != rec["source_sha16"]:
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def host_info():
+    """The host the oracle timing ran on: logical CPUs and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def measured_peaks():
+    """Practical HBM ceilings beside the published 8 TB/s, HIP events around 5 launches on
+    2 GiB: the library's nontemporal read probe (the path's streaming kernels read; this is
+    their ceiling) and a device copy (read + write bytes / time)."""
+    import torch
+    import invariant_rl_logprob_amd as ril
+    n = 2 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty(ril.ril_hbm_read_probe_words(), dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, moved in (("read_peak_gbps", lambda: ril.ril_hbm_read_probe(src, out), n),
+                            ("copy_peak_gbps", lambda: dst.copy_(src), 2 * n)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = round(moved * 5 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del src, dst, out
+    torch.cuda.empty_cache()
+    log(f"measured HBM ceilings: {res}")
+    return res
+
+
+def lm_head_sweep(w, lm8, args):
+    """The lm-head alone (ril_lm_head_logprobs) at M = 64, 1024, 8192 and 65536 normalised
+    rows: time per launch (HIP events, no trace hook), TFLOP/s against the dtype's dense
+    MFMA peak, weight-stream GB/s, and whether the first 64 rows' logprobs keep their bits
+    at every M (one K order per column)."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    from invariant_rl_logprob_amd.session import Session
+    Ms = [64, 1024, 8192, 65536]
+    w_lm = wl.gqa_head_weights(w, device="cuda")["w_lm"]
+    sess = Session(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, vocab=w.vocab,
+                   d_head=w.d_head, w_lm=w_lm, max_rows=64, max_tokens=max(Ms), max_ctx=64, pool_pages=8,
+                   softmax_scale=1.0, lm_dtype=1 if lm8 else 0)
+    del w_lm
+    g = torch.Generator(device="cuda").manual_seed(77)
+    z = torch.randn(max(Ms), w.d_head, generator=g, device="cuda").to(torch.bfloat16)
+    t = torch.randint(0, w.vocab, (max(Ms),), generator=g, device="cuda").to(torch.int32)
+    wbytes = ((w.vocab + 255) // 256) * 256 * w.d_head * (1 if lm8 else 2)
+    peak = MFMA_FP8_PEAK_TFLOPS if lm8 else MFMA_BF16_PEAK_TFLOPS
+    out, ref = [], None
+    for M in Ms:
+        launch = lambda: sess.lm_head(z[:M], t[:M])  # noqa: E731
+        first = launch()
+        bits = first[:64].cpu().view(torch.int32).numpy()
+        ref = bits if ref is None else ref
+        ms = time_launch(launch, 3 if M >= 8192 else 10, 1)
+        tf = 2.0 * M * w.d_head * w.vocab / (ms * 1e-3) / 1e12
+        out.append({"M": M, "us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / peak, 4),
+                    "weight_gbps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                    "first_64_rows_bitwise_equal": bool(np.array_equal(bits, ref))})
+    log(f"lm-head sweep ({'W8A8' if lm8 else 'bf16'}): {out}")
+    del z, sess
+    torch.cuda.empty_cache()
+    return {"head": "W8A8 block FP8 (e4m3, E8M0 scales)" if lm8 else "bf16", "mfma_peak_tflops": peak, "rows": out}
 
 
 def blas_threads():
@@ -297,6 +378,9 @@ def bench_gqa(args, fp8=False, lm8=False):
         x1 = comparator(case.sess, prepare, rows, dec[:, -1], kv_bytes + q_bytes + out_bytes, (256, 512, 1024), args)
         x1["invariant_over_x1_best"] = round(x1["best"]["ms_per_step"] / ms_step, 4)
 
+    sweep = None if args.no_lm_sweep else lm_head_sweep(w, lm8, args)
+    peaks = measured_peaks()
+
     graph = None
     if not args.no_graph:
         graph = {"gqa_decode_b64": graph_leg(case.sess, [("d", r) for r in rows], c,
@@ -321,6 +405,7 @@ def bench_gqa(args, fp8=False, lm8=False):
                for r in sample]
         secs = time.time() - t1
         cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               **host_info(),
                "sample": f"{len(sample)} of the {len(rows)} decode rows (full attention over each row's "
                          f"context + the 4096x129280 lm-head in fp64), {secs:.1f} s",
                "max_abs_diff_vs_gpu": float(np.max(np.abs(np.array(got) - out.cpu().numpy()[: len(sample)])))}
@@ -337,6 +422,8 @@ def bench_gqa(args, fp8=False, lm8=False):
                    "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 512, "vocab_tile": 256,
                    "parallelism": "none (1 GPU)"},
         "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        **peaks, "attn_frac_of_read_peak": round(attn_gbps / peaks["read_peak_gbps"], 4),
+        "lm_head_sweep": sweep,
         "lm_head_gbps": round(lm_gbps, 1), "diff": diff, "timed_step_equals_checked_decode": last_equal,
         "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
         "comparator_x1": x1, "hip_graph": graph, "roofline": roof, "cpu_baseline": cpu,
@@ -395,7 +482,7 @@ def bench_mla(args):
             got.append(oracle.head_logprob(o, w_lm_cpu, int(host[r]["target"][-1]), w.rms_eps, w_o=w_o_cpu))
         secs = time.time() - t1
         cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-               "sample": f"{len(sample)} of the {len(rows)} decode rows (MLA over each row's context, the "
+               **host_info(), "sample": f"{len(sample)} of the {len(rows)} decode rows (MLA over each row's context, the "
                          f"65536x4096 projection and the lm-head in fp64), {secs:.1f} s",
                "max_abs_diff_vs_gpu": float(np.max(np.abs(np.array(got) - out.cpu().numpy()[: len(sample)])))}
         log(f"oracle: {cpu}")
@@ -473,7 +560,7 @@ def bench_sparse(args):
         got = [case.oracle_row(r)[0] for r in sample]
         secs = time.time() - t1
         cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-               "sample": f"{len(sample)} of the {len(rows)} decode rows (fp32 indexer over 65536 positions, "
+               **host_info(), "sample": f"{len(sample)} of the {len(rows)} decode rows (fp32 indexer over 65536 positions, "
                          f"top-2048, sparse MLA, projection and lm-head in fp64), {secs:.1f} s",
                "max_abs_diff_vs_gpu": float(np.max(np.abs(np.array(got) - out.cpu().numpy()[: len(sample)])))}
         log(f"oracle: {cpu}")
@@ -569,7 +656,7 @@ def bench_long(args):
         secs = time.time() - t1
         gpu = long0.cpu().numpy()
         cpu = {"value": round(len(picks) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-               "sample": f"{len(picks)} long-sequence positions {picks} (attention over up to 131072 positions, "
+               **host_info(), "sample": f"{len(picks)} long-sequence positions {picks} (attention over up to 131072 positions, "
                          f"8192->4096 projection and lm-head in fp64), {secs:.1f} s",
                "max_abs_diff_vs_gpu": float(max(abs(gpu[s_, p_] - g_) for (s_, p_), g_ in zip(picks, got)))}
         log(f"oracle: {cpu}")
@@ -603,6 +690,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-comparator", action="store_true", help="skip the shape-derived comparator leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay leg")
+    ap.add_argument("--no-lm-sweep", action="store_true", help="skip the lm-head M sweep (gqa workloads)")
     ap.add_argument("--long-all-chunks", action="store_true", help="long_mix: also run the 512-token chunks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")

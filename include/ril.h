@@ -328,6 +328,15 @@ ril_status ril_lm_head_logprobs(const ril_model *m, int32_t rows, const void *z,
                                 const int32_t *target_ids, float *logprob_out, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* HBM read ceiling probe, for benchmarking only (like ril_set_policy): enqueue, on
+ * `stream`, one grid-stride read of the first floor(bytes / 16) * 16 bytes of the device
+ * buffer src (16-byte aligned) with the nontemporal policy, as the path's streaming
+ * kernels read, folding the data into out[ril_hbm_read_probe_words()] (device uint32)
+ * so the reads cannot be elided.  Time it with events to get the practical read rate.
+ * Returns RIL_EINVAL on a null or misaligned pointer, RIL_EHIP on a launch error. */
+int32_t ril_hbm_read_probe_words(void);
+ril_status ril_hbm_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream);
+
 /* HIP-graph capture of one decode step, for steps whose launch overhead matters
  * (small batches, short contexts).
  *

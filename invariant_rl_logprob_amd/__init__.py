@@ -83,6 +83,8 @@ _lm_head_fp8_packed_bytes = _sig("ril_lm_head_fp8_packed_bytes", ctypes.c_size_t
 _pack_lm_head_fp8 = _sig("ril_pack_lm_head_fp8", _c_int, [_vp, _c_int, _c_int, _vp, ctypes.c_size_t, _vp])
 _lm_head_logprobs = _sig("ril_lm_head_logprobs", _c_int,
                          [_vp, _c_int, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp])
+_hbm_read_probe_words = _sig("ril_hbm_read_probe_words", _c_int, [])
+_hbm_read_probe = _sig("ril_hbm_read_probe", _c_int, [_vp, ctypes.c_size_t, _vp, _vp])
 _quantize_rows_fp8 = _sig("ril_quantize_rows_fp8", _c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
 _ws_attn_offset = _sig("ril_ws_attn_offset", ctypes.c_size_t, [_vp])
 _kv_alloc = _sig("ril_kv_alloc", _c_int, [_vp, _vp, ctypes.c_size_t, ctypes.c_uint64, ctypes.POINTER(_vp)])
@@ -108,7 +110,7 @@ _trace_read = _sig("ril_trace_read", _c_int, [_c_int, ctypes.POINTER(ctypes.c_do
 
 EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril_kv_page_bytes",
             "ril_lm_head_packed_bytes", "ril_pack_lm_head", "ril_lm_head_fp8_packed_bytes", "ril_pack_lm_head_fp8",
-            "ril_quantize_rows_fp8", "ril_lm_head_logprobs",
+            "ril_quantize_rows_fp8", "ril_lm_head_logprobs", "ril_hbm_read_probe_words", "ril_hbm_read_probe",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
             "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_set_policy", "ril_trace_enable",
@@ -213,6 +215,19 @@ def ril_lm_head_logprobs(model: int, z, targets, logprob_out, ws, stream=None) -
         raise ValueError("ril_lm_head_logprobs: targets / logprob_out shorter than z")
     _check(_lm_head_logprobs(model, rows, _ptr(z), z.stride(0), _ptr(targets), _ptr(logprob_out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "ril_lm_head_logprobs")
+
+
+def ril_hbm_read_probe_words() -> int:
+    return int(_hbm_read_probe_words())
+
+
+def ril_hbm_read_probe(src, out, stream=None) -> None:
+    """Benchmarking only: one nontemporal grid-stride read of the device tensor src, folded
+    into out (device uint32/int32 of at least ril_hbm_read_probe_words() entries)."""
+    if out.numel() < ril_hbm_read_probe_words():
+        raise ValueError("ril_hbm_read_probe: out too small")
+    _check(_hbm_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(out), _stream(stream)),
+           "ril_hbm_read_probe")
 
 
 def ril_ws_attn_offset(model: int) -> int:

@@ -319,6 +319,14 @@ extern "C" ril_status ril_quantize_rows_fp8(const void *src, int32_t rows, int32
   if (e != hipSuccess) return fail(RIL_EHIP, "quantize_rows_fp8: %s", hipGetErrorString(e));
   return RIL_OK;
 }
+extern "C" int32_t ril_hbm_read_probe_words(void) { return ril::hbm_read_probe_blocks(); }
+
+extern "C" ril_status ril_hbm_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream) {
+  if (!src || !out || !aligned16(src) || !aligned4(out)) return fail(RIL_EINVAL, "hbm_read_probe: null or misaligned pointer");
+  const hipError_t e = ril::launch_hbm_read_probe(src, bytes, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "hbm_read_probe: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
 extern "C" size_t ril_ws_attn_offset(const ril_model *m) { return m ? m->off_attn : 0; }
 
 // ---------------------------------------------------------------------------

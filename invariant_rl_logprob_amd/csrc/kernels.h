@@ -181,6 +181,8 @@ hipError_t launch_quant_rows_fp8(const QuantRowsArgs &a, hipStream_t st);
 hipError_t launch_lm_head_fp8(const LmHeadArgs &a, hipStream_t st);
 long lm_head_fp8_code_bytes(int V, int K);
 long lm_head_fp8_exp_count(int V, int K);
+int hbm_read_probe_blocks();
+hipError_t launch_hbm_read_probe(const void *src, size_t bytes, uint32_t *out, hipStream_t st);
 hipError_t launch_pack_lm_head_fp8(const bf16_t *src, int V, int K, uint8_t *codes, int32_t *ew, hipStream_t st);
 
 }  // namespace ril

@@ -224,3 +224,12 @@ def test_lm_head_packed_bytes_and_pack_validation():
     for args in bad:
         assert f(*args, None) == ril.RIL_EINVAL, args
         assert ril.ril_last_error()
+
+
+def test_hbm_read_probe_rejects_bad_pointers():
+    lib = ctypes.CDLL(ril.LIB_PATH)
+    lib.ril_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert ril.ril_hbm_read_probe_words() > 0
+    assert lib.ril_hbm_read_probe(None, 1024, 0x20000, None) == ril.RIL_EINVAL
+    assert lib.ril_hbm_read_probe(0x10008, 1024, 0x20000, None) == ril.RIL_EINVAL
+    assert lib.ril_hbm_read_probe(0x10000, 1024, None, None) == ril.RIL_EINVAL
