@@ -21,8 +21,9 @@
 //
 // Latent page (16 tokens) = one 16 x 576 block in the K-operand layout of attn_common.h
 // (k_page_offset); a sparse page also holds the 16 tokens' fp32 indexer keys after it.
-// Per 64-token tile the workgroup copies the tile into LDS in the same layout (double-
-// buffered: the next tile is loaded into registers while the current one is computed).
+// Per 64-token tile the workgroup copies the tile into LDS (double-buffered: the next
+// tile is copied while the current one is computed) in the same layout up to a swizzle
+// of its 16-byte units: LDS unit u of a page slot holds page unit mla_swz(u).
 // Score operands are 16-byte LDS reads.  Value operands come from the same tile through
 // gfx950's transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
 // receives element i%4 of the 8-byte chunks addressed by lanes 4e + i/4, e = 0..3, so
@@ -42,6 +43,14 @@ constexpr int kMlaPage = kPage * kMlaDqk;     // 9216 elements: one page's laten
 constexpr int kMlaSlot = kMlaPage + 64;       // LDS slot of a page: +128 B spreads the banks
 constexpr int kMlaThreads = 512;              // 4 pairs of waves x 16 heads (H % 64 == 0)
 constexpr int kTileUnits = 4 * kMlaPage / 8;  // 4608 16-byte units per tile
+
+// Within a page slot, 16-byte unit u sits at LDS unit mla_swz(u) (an involution: it flips
+// bit 3, the token quad of the 8-token half, when bit 4, the parity of the 8-dim group, is
+// set).  Units of dims 8g .. 8g+7 and 8(g+1) .. of the same tokens then fall in different
+// LDS banks: the value operands' transposing reads, which take four tokens of each of two
+// adjacent 8-dim groups per 16 lanes, read 256 bytes apart without it (two-way bank
+// conflicts); the score reads stay conflict-free.
+__device__ __forceinline__ int mla_swz(int u) { return u ^ (((u >> 4) & 1) << 3); }
 
 // ---------------------------------------------------------------------------
 // S5 for MLA: one thread per (token, 16-byte unit): 72 latent units, then (sparse)
@@ -121,16 +130,19 @@ __device__ __forceinline__ void mla_tile_scores(f32x4 (&s)[4], const bf16_t *kt,
                                                 const bf16x8 (&qop)[kMlaDqk / 32]) {
   const int lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
   const int rq = r16 >> 2, ri = r16 & 3;
-  const uint32_t base = lds_addr(kt) + 2 * ((rq >> 1) * kMlaSlot + grp * 128 + (rq & 1) * 32 + ri * 8);
+  // this lane's page unit for M blocks 0/2 (token quad 0) and 1/3 (quad 1), swizzled
+  const int u0 = grp * 16 + (rq & 1) * 4 + ri;
+  const uint32_t slot = lds_addr(kt) + 2 * (rq >> 1) * kMlaSlot;
+  const uint32_t base0 = slot + 16 * mla_swz(u0), base1 = slot + 16 * mla_swz(u0 + 8);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 a[2][4];
   auto issue = [&](auto cc) {
     constexpr int C = decltype(cc)::value;
-    a[C & 1][0] = lds_rd128<C * 1024>(base);
-    a[C & 1][1] = lds_rd128<C * 1024 + 128>(base);
-    a[C & 1][2] = lds_rd128<C * 1024 + 2 * kSlotBytes>(base);
-    a[C & 1][3] = lds_rd128<C * 1024 + 2 * kSlotBytes + 128>(base);
+    a[C & 1][0] = lds_rd128<C * 1024>(base0);
+    a[C & 1][1] = lds_rd128<C * 1024>(base1);
+    a[C & 1][2] = lds_rd128<C * 1024 + 2 * kSlotBytes>(base0);
+    a[C & 1][3] = lds_rd128<C * 1024 + 2 * kSlotBytes>(base1);
   };
   issue(std::integral_constant<int, 0>{});
   static_for<kMlaDqk / 32>([&](auto cc) {
@@ -151,17 +163,24 @@ __device__ __forceinline__ void mla_tile_scores(f32x4 (&s)[4], const bf16_t *kt,
 
 // V^T operands for the value dims 256*half .. +255: block b (dims 16b ..) of the 32-token
 // step kc.  Lane (group g, i = lane % 16) gets V[32kc + 8g + j][256*half + 16b + i],
-// j = 0..7, by two transposing reads (tokens +0..3 at byte offset 0, +4..7 at +128); the
-// block adds 512*b bytes and the step 2 page slots.  Entries j >= n_valid read as 0.
-__device__ __forceinline__ uint32_t mla_v_base(const bf16_t *kt, int half) {
+// j = 0..7, by two transposing reads (tokens +0..3 from base 0, +4..7 from base 1: the
+// swizzle makes their distance lane-dependent); the block adds 512*b bytes (the swizzle
+// does not depend on it) and the step 2 page slots.  Entries j >= n_valid read as 0.
+struct MlaVBase {
+  uint32_t b0, b1;
+};
+__device__ __forceinline__ MlaVBase mla_v_base(const bf16_t *kt, int half) {
   const int lane = threadIdx.x & 63, grp = lane >> 4, i = lane & 15;
   const int tok = 8 * grp + (i >> 2);
-  return lds_addr(kt) + 2 * ((tok >> 4) * kMlaSlot + k_page_offset(tok & 15, 256 * half + 4 * (i & 3)));
+  const int e = k_page_offset(tok & 15, 256 * half + 4 * (i & 3));  // element; tokens +4..7: +64
+  const uint32_t slot = lds_addr(kt) + 2 * (tok >> 4) * kMlaSlot;
+  const int u = e >> 3, sub = 2 * (e & 7);  // unit, byte within it
+  return MlaVBase{slot + 16 * mla_swz(u) + sub, slot + 16 * mla_swz(u + 8) + sub};
 }
 template <int B, int KC>
-__device__ __forceinline__ void mla_v_issue(u32x2 (&r)[2], uint32_t base) {
-  r[0] = lds_rdtr<512 * B + 2 * kSlotBytes * KC>(base);
-  r[1] = lds_rdtr<512 * B + 2 * kSlotBytes * KC + 128>(base);
+__device__ __forceinline__ void mla_v_issue(u32x2 (&r)[2], MlaVBase base) {
+  r[0] = lds_rdtr<512 * B + 2 * kSlotBytes * KC>(base.b0);
+  r[1] = lds_rdtr<512 * B + 2 * kSlotBytes * KC>(base.b1);
 }
 __device__ __forceinline__ bf16x8 mla_v_take(u32x2 (&r)[2], int n_valid) {
   settle(r[0]);
@@ -180,7 +199,7 @@ __device__ __forceinline__ void mla_tile_values(f32x4 (&o)[kMlaDv / 32], const b
                                                 const bf16x8 (&pop)[2], float alpha, int n_live) {
   const int grp = (threadIdx.x & 63) >> 4;
   const int nv0 = MASK ? n_live - 8 * grp : 8, nv1 = MASK ? n_live - (32 + 8 * grp) : 8;
-  const uint32_t base = mla_v_base(kt, half);
+  const MlaVBase base = mla_v_base(kt, half);
   const bool scale = __any(alpha != 1.f);
   u32x2 r[2][2][2];
   mla_v_issue<0, 0>(r[0][0], base);
@@ -227,8 +246,8 @@ __device__ __forceinline__ void mla_unit_td(int v, int &t, int &d0) {
 // Per tile: the scoring wave of each pair computes the scores of its 16 heads and the
 // online-softmax step and hands P and alpha over; both waves of the pair accumulate their
 // half of the value dims.  Tile t+1 is copied into the other LDS buffer (72 direct-to-LDS
-// loads of 1 KB, 9 per wave, each filling 64 consecutive K-layout units of one page slot)
-// while tile t is computed.  Sparse: each wave holds, one entry per lane, the positions of
+// loads of 1 KB, 9 per wave, each filling 64 consecutive LDS units of one page slot with
+// the swizzled page units) while tile t is computed.  Sparse: each wave holds, one entry per lane, the positions of
 // the tile after next and the page ids of the next tile, so no copy waits on a lookup.
 // ---------------------------------------------------------------------------
 template <bool SPARSE>
@@ -297,27 +316,32 @@ __global__ __launch_bounds__(512) void mla_split_kernel(
   bf16x8 qop[kMlaDqk / 32];
   if (half == 0) mla_load_q(qop, q, qrow, H, head, col_ok);
 
-  // copy tile t into buffer t&1: wave w issues pieces w, w+8, ..; piece pc = page slot
-  // pc / 18, units 64 * (pc % 18) + lane of it
+  // copy tile t into buffer t&1: wave w copies page slot w % 4, its 1 KB pieces w / 4,
+  // w / 4 + 2, ... (LDS unit 64 j + lane of the slot takes page unit mla_swz(64 j + lane))
   constexpr int kPieces = kMlaPage / 512;  // 18 per page slot
+  const int my_ps = wave & 3, j0 = wave >> 2;
+  const int lane_unit = mla_swz(lane);     // dense: the swizzle stays within a piece
   auto copy_tile = [&](int t) {
-    bf16_t *buf = &kt[t & 1][0];
-    for (int pc = wave; pc < 4 * kPieces; pc += kMlaThreads / 64) {
-      const int ps = pc / kPieces, j = pc % kPieces;
-      const bf16_t *src;
-      if (!SPARSE) {
-        const int idx = 4 * t + ps;  // page index within the split (< 128)
-        const int pid = idx < 64 ? __builtin_amdgcn_readlane(pidA, idx) : __builtin_amdgcn_readlane(pidB, idx - 64);
-        src = pool + (long)pid * page_elems + j * 512 + lane * 8;
-      } else {
+    bf16_t *buf = &kt[t & 1][0] + my_ps * kMlaSlot;
+    if (!SPARSE) {
+      const int idx = 4 * t + my_ps;  // page index within the split (< 128), uniform
+      const int pid = idx < 64 ? __builtin_amdgcn_readlane(pidA, idx) : __builtin_amdgcn_readlane(pidB, idx - 64);
+      const bf16_t *page = pool + (long)pid * page_elems;  // uniform: one scalar base per tile
+      const int off = lane_unit * 8 + j0 * 512;
+#pragma unroll
+      for (int i = 0; i < kPieces / 2; ++i)
+        __builtin_amdgcn_global_load_lds(page + (off + i * 1024), buf + j0 * 512 + i * 1024, 16, 0, 0);
+    } else {
+#pragma unroll 1
+      for (int i = 0; i < kPieces / 2; ++i) {
+        const int j = j0 + 2 * i;
         int tt, d0;
-        mla_unit_td(64 * j + lane, tt, d0);
-        const int e = 16 * ps + tt;  // entry of the tile
+        mla_unit_td(mla_swz(64 * j + lane), tt, d0);
+        const int e = 16 * my_ps + tt;  // entry of the tile
         const int p = __shfl(pos1, e, 64), id = __shfl(pid1, e, 64);
-        src = pool + (long)id * page_elems + (p >= 0 ? k_page_offset(p % kPage, d0) : 0);
+        const bf16_t *src = pool + (long)id * page_elems + (p >= 0 ? k_page_offset(p % kPage, d0) : 0);
+        __builtin_amdgcn_global_load_lds(src, buf + j * 512, 16, 0, 0);
       }
-      bf16_t *dst = buf + ps * kMlaSlot + j * 512;
-      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
   };
   float m = neg_inf(), l = 0.f;
