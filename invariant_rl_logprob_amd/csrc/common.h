@@ -122,6 +122,13 @@ __device__ __forceinline__ u32x4 lds_rd128(uint32_t base) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
   return r;
 }
+template <int OFF>
+__device__ __forceinline__ int lds_rd32(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  int r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
 // transposing read: lane i of each 16-lane group gets element i%4 of the 8-byte chunks
 // addressed by lanes 4e + i/4 of its group, e = 0..3
 template <int OFF>

@@ -178,13 +178,6 @@ constexpr int kF8MaxSteps = 256;
 // counts as a read of every LDS array whose address escaped into asm (all of them here).
 __device__ __forceinline__ void lds_publish() { asm volatile("" ::: "memory"); }
 
-template <int OFF>
-__device__ __forceinline__ int lds_rd32(uint32_t base) {
-  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
-  int r;
-  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(base), "i"(OFF));
-  return r;
-}
 
 template <int MB, bool NT, bool ROWS_FAST, int PF = 1>
 __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restrict__ A8,

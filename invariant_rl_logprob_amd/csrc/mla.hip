@@ -161,6 +161,17 @@ __device__ __forceinline__ void mla_tile_scores(f32x4 (&s)[4], const bf16_t *kt,
   });
 }
 
+// The pair's exchange goes through LDS with untracked stores and loads and an asm barrier
+// that waits for LDS operations only: a compiler-visible LDS access or __syncthreads
+// would also wait for the next tile's copy in flight (vmcnt(0)) in the middle of a tile.
+__device__ __forceinline__ void lds_wr32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_wr128(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // V^T operands for the value dims 256*half .. +255: block b (dims 16b ..) of the 32-token
 // step kc.  Lane (group g, i = lane % 16) gets V[32kc + 8g + j][256*half + 16b + i],
 // j = 0..7, by two transposing reads (tokens +0..3 from base 0, +4..7 from base 1: the
@@ -344,6 +355,7 @@ __global__ __launch_bounds__(512) void mla_split_kernel(
       }
     }
   };
+  const uint32_t xp_lane = lds_addr(&xp[pair][0][0]) + 16 * lane, xa_lane = lds_addr(&xa[pair][0]) + 4 * lane;
   float m = neg_inf(), l = 0.f;
   f32x4 o[kMlaDv / 32];
 #pragma unroll
@@ -371,15 +383,21 @@ __global__ __launch_bounds__(512) void mla_split_kernel(
       tile_softmax(s, t0, n_all - 1, cscale, m, l, pop, alpha, m_new, l_new);
       m = m_new;
       l = l_new;
-      xp[pair][0][lane] = __builtin_bit_cast(u32x4, pop[0]);
-      xp[pair][1][lane] = __builtin_bit_cast(u32x4, pop[1]);
-      xa[pair][lane] = alpha;
+      lds_wr128(xp_lane, __builtin_bit_cast(u32x4, pop[0]));
+      lds_wr128(xp_lane + 1024, __builtin_bit_cast(u32x4, pop[1]));
+      lds_wr32(xa_lane, alpha);
     }
-    __syncthreads();  // P and alpha of every pair are in LDS
+    lds_barrier();  // P and alpha of every pair are in LDS
     if (half == 1) {
-      pop[0] = as_bf16x8(xp[pair][0][lane]);
-      pop[1] = as_bf16x8(xp[pair][1][lane]);
-      alpha = xa[pair][lane];
+      u32x4 p0 = lds_rd128<0>(xp_lane), p1 = lds_rd128<1024>(xp_lane);
+      int a = lds_rd32<0>(xa_lane);
+      lds_wait<0>();
+      settle(p0);
+      settle(p1);
+      settle(a);
+      pop[0] = as_bf16x8(p0);
+      pop[1] = as_bf16x8(p1);
+      alpha = __builtin_bit_cast(float, a);
     }
     const int n_live = n_all - t0;
     if (n_live >= kTile)
