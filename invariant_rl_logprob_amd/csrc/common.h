@@ -154,6 +154,13 @@ __device__ __forceinline__ void lds_wait() {
 }
 template <typename T>
 __device__ __forceinline__ void settle(T &v) { asm volatile("" : "+v"(v)); }
+// s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this wave are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
 
 // Two OCP E4M3 codes (low 16 bits: a, then b) of values already multiplied by their
 // scale's inverse.  The hardware conversion rounds to nearest even but turns magnitudes

@@ -349,18 +349,18 @@ __global__ __launch_bounds__(256) void pack_lm_head_kernel(const bf16_t *__restr
   st16(dst + i * 8, v);
 }
 
-template <int MB, bool NT, bool ROWS_FAST>
+template <int MB, bool NT>
 __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__ Z, int ldz,
                                                       const bf16_t *__restrict__ W, int K, int V,
                                                       const int32_t *__restrict__ target, int M,
                                                       float *__restrict__ part,
                                                       float *__restrict__ tgt_logit, int n_vt) {
-  __shared__ float red[4][16 * MB];
+  __shared__ float red[2][4][16 * MB];
   __shared__ u32x4 lds_a[2][kLdsSteps * MB * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
-  const int tile = ROWS_FAST ? blockIdx.y : blockIdx.x;
-  const int m0 = (ROWS_FAST ? blockIdx.x : blockIdx.y) * 16 * MB;
+  const int tile = blockIdx.x;
+  const int m0 = blockIdx.y * 16 * MB;
   const bf16_t *ap[MB];
   const bf16_t *wp[4];
 #pragma unroll
@@ -373,7 +373,140 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   kloop_lds<MB, 4, 7, 512, NT>(acc, ap, wp, K, lm_rot(tile, K / 32), lds_a);
-  lm_tile_epilogue<MB>(acc, red, tile, m0, M, V, target, part, tgt_logit, n_vt);
+  lm_tile_epilogue<MB>(acc, red, wave, tile, m0, M, V, target, part, tgt_logit, n_vt);
+}
+
+// S11 for many rows: a workgroup of 8 waves computes 256-row x 256-column tiles (kWideRows
+// rows of one vocabulary tile).  Both operands of a 32-wide K step (the rows' 16 row blocks
+// and the tile's 16 column blocks, 1 KB each in MFMA lane order) are copied once into LDS
+// by direct-to-LDS loads, kWideBuf-1 steps ahead of the step being computed, and every
+// block read from LDS feeds several MFMAs: wave w owns rows 128(w/4) .. +127 and columns
+// 64(w%4) .. +63 (8 x 4 blocks).  Each column's K order (lm_rot) and its MFMA per step are
+// those of lm_head_kernel, and the column group w%4 owns the same 64 columns in the
+// epilogue, so a row's partials have the same bits from either kernel at any M.
+//
+// The grid is kWideGrid persistent workgroups.  Workgroup g runs on XCD g%8 (workgroups
+// are dispatched to the 8 XCDs round-robin) and is its XCD's l = g/8; the 32 workgroups
+// of an XCD work through blocks of br x (32/br) tiles (row tiles x vocabulary tiles),
+// block b, b+8, ... for XCD b, one tile each per block.  Every workgroup starts its tiles
+// at about the same time as the others of its block, so the block's row and weight
+// slices are fetched once into the XCD's L2 and read there by all of them.  Which
+// workgroup computes a tile never changes the tile's arithmetic.
+constexpr int kWideRows = 256, kWideBuf = 5, kWideGrid = 256;
+
+// s_waitcnt vmcnt(PER * min(ahead, MAXA)): this wave's copies of a step landed while at
+// most `ahead` later steps of PER loads each may stay in flight
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_steps(int ahead) {
+  if constexpr (MAXA == 0) {
+    wait_vmem<0>();
+  } else {
+    if (ahead >= MAXA) wait_vmem<PER * MAXA>();
+    else wait_steps<PER, MAXA - 1>(ahead);
+  }
+}
+
+__global__ __launch_bounds__(512) void lm_head_wide_kernel(const bf16_t *__restrict__ Z, int ldz,
+                                                           const bf16_t *__restrict__ W, int K, int V,
+                                                           const int32_t *__restrict__ target, int M,
+                                                           float *__restrict__ part, float *__restrict__ tgt_logit,
+                                                           int n_vt, int br) {
+  constexpr int kStepB = 32 * 1024;  // one K step: row blocks 0..15, then column blocks 0..15
+  // the K loop's step buffers; the epilogue's reduction scratch reuses the first 8 KB
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kWideBuf][kStepB];
+  auto &red = *reinterpret_cast<float (*)[2][2][4][128]>(&buf[0][0]);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int rg = wave >> 2, cg = wave & 3;
+  const int nk = K / 32;
+  const int n_rt = (M + kWideRows - 1) / kWideRows;
+  const int bv = 32 / br;
+  const int nbr = (n_rt + br - 1) / br, n_blocks = nbr * ((n_vt + bv - 1) / bv);
+  const int xcd = blockIdx.x % 8, l = blockIdx.x / 8;
+  const uint32_t lds0 = lds_addr(&buf[0][0]);
+  const uint32_t abase = lds0 + rg * 8192 + lane * 16, wbase = lds0 + 16384 + cg * 4096 + lane * 16;
+  for (int blk = xcd; blk < n_blocks; blk += 8) {
+    const int rt = (blk % nbr) * br + l % br, tile = (blk / nbr) * bv + l / br;
+    if (rt >= n_rt || tile >= n_vt) continue;  // the same for the whole workgroup
+    const int m0 = rt * kWideRows;
+    const int rot = lm_rot(tile, nk);
+    auto kidx = [&](int s) {
+      const int t = s + rot;
+      return t >= nk ? t - nk : t;
+    };
+    // this wave copies row blocks 2w, 2w+1 and column blocks 2w, 2w+1 of every step (rows
+    // past M read row M-1; their results are dropped).  Sources: a wave-uniform base plus
+    // a 32-bit lane offset in elements (the row tile's rows span less than 2^31 elements)
+    const bf16_t *za = Z + (long)m0 * ldz;
+    const bf16_t *wt = W + (long)tile * 16 * nk * 512;
+    uint32_t aoff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) aoff[j] = (uint32_t)((min(m0 + 16 * (2 * wave + j) + r16, M - 1) - m0) * ldz + grp * 8);
+    const uint32_t woff = (uint32_t)((2 * wave) * nk * 512 + lane * 8);
+    auto copy_step = [&](int s) {
+      uint8_t *b = &buf[s % kWideBuf][0];
+      const int k = kidx(s);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_global_load_lds(za + (aoff[j] + k * 32), b + (2 * wave + j) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(wt + (woff + (uint32_t)(j * nk + k) * 512), b + 16384 + (2 * wave + j) * 1024,
+                                         16, 0, 0);
+      }
+    };
+    // every wave is done with the previous tile's epilogue (red lives in buf[0])
+    __syncthreads();
+    for (int s = 0; s < kWideBuf - 1 && s < nk; ++s) copy_step(s);
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The operands of step s+1 are read from LDS while the MFMAs of step s run: the four
+    // column blocks first (into the other of two register sets), then each row block
+    // right after the MFMAs that used its register for step s.
+    u32x4 bo[2][4], a[8];
+    auto read_b = [&](int s, u32x4 (&b)[4]) {
+      const uint32_t off = (uint32_t)(s % kWideBuf) * kStepB;
+      static_for<4>([&](auto nb_) { b[decltype(nb_)::value] = lds_rd128<decltype(nb_)::value * 1024>(wbase + off); });
+    };
+    // Iteration s: step s+1 landed (this wave's copies, then the barrier for everyone's;
+    // at most kWideBuf-3 later steps, 4 loads each, still in flight), the barrier also
+    // tells that every wave is done with step s-1's buffer, which the copy of step
+    // s + kWideBuf - 1 refills; then the MFMAs of step s with the reads of step s+1.
+    // The barrier is a plain s_barrier: every copy and read it orders is waited for
+    // explicitly (a fenced barrier would also drain the reads and copies in flight).
+    auto iteration = [&](int s, u32x4 (&cur)[4], u32x4 (&nxt)[4]) {
+      if (s + 1 < nk) wait_steps<4, kWideBuf - 3>(nk - 2 - s);
+      asm volatile("s_barrier" ::: "memory");
+      if (s + kWideBuf - 1 < nk) copy_step(s + kWideBuf - 1);
+      // (after the last step these reads fetch a buffer's stale contents, never used)
+      const uint32_t off = (uint32_t)((s + 1) % kWideBuf) * kStepB;
+      read_b(s + 1, nxt);
+      lds_wait<4>();  // step s's operands (read before these four) are in
+#pragma unroll
+      for (int i = 0; i < 4; ++i) settle(cur[i]);
+      static_for<8>([&](auto mb_) {
+        constexpr int mb = decltype(mb_)::value;
+        settle(a[mb]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(as_bf16x8(a[mb]), as_bf16x8(cur[nb]), acc[mb][nb]);
+        a[mb] = lds_rd128<mb * 1024>(abase + off);
+        __builtin_amdgcn_sched_barrier(0);  // keep this order: one register per row block
+      });
+    };
+    wait_steps<4, kWideBuf - 2>(nk - 1);  // step 0 landed
+    asm volatile("s_barrier" ::: "memory");
+    read_b(0, bo[0]);
+    static_for<8>([&](auto mb_) { a[decltype(mb_)::value] = lds_rd128<decltype(mb_)::value * 1024>(abase); });
+    for (int s = 0; s < nk; s += 2) {
+      iteration(s, bo[0], bo[1]);
+      if (s + 1 < nk) iteration(s + 1, bo[1], bo[0]);
+    }
+    lds_wait<0>();
+    // every wave's reads are done (each waited for its own) before red overwrites buf[0]
+    asm volatile("s_barrier" ::: "memory");
+    lm_tile_epilogue<8>(acc, red[rg], cg, tile, m0 + rg * 128, M, V, target, part, tgt_logit, n_vt);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -489,21 +622,23 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st) {
   const int n_rt = (a.M + 16 * mb - 1) / (16 * mb);
   // Up to two row tiles the weights are read once (twice) and streamed with the
   // nontemporal policy (measured: 192 -> 171 us at 64 rows, 369 -> 326 us at 128 rows on
-  // the 4096 x 129280 head).  With more row tiles the grid runs the row tiles of one
-  // vocabulary tile back to back, so its weight tile is read from HBM once and served
-  // from the caches to the other row tiles.  Neither choice changes a column's K order.
+  // the 4096 x 129280 head).  Past 128 rows the 256-row kernel shares both operands
+  // through LDS.  No choice changes a column's K order or its MFMA per step.
   if (n_rt <= 2) {
     dim3 grid(n_vt, n_rt);
     if (mb == 1)
-      hipLaunchKernelGGL((lm_head_kernel<1, true, false>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
+      hipLaunchKernelGGL((lm_head_kernel<1, true>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
                          a.target, a.M, a.part, a.tgt_logit, n_vt);
     else
-      hipLaunchKernelGGL((lm_head_kernel<4, true, false>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
+      hipLaunchKernelGGL((lm_head_kernel<4, true>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
                          a.target, a.M, a.part, a.tgt_logit, n_vt);
   } else {
-    dim3 grid(n_rt, n_vt);
-    hipLaunchKernelGGL((lm_head_kernel<4, false, true>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
-                       a.target, a.M, a.part, a.tgt_logit, n_vt);
+    // many rows: 256-row tiles with both operands shared through LDS, on persistent
+    // workgroups that take blocks of 4 x 8 tiles (fewer row tiles: 2 x 16 or 1 x 32)
+    const int n_wrt = (a.M + kWideRows - 1) / kWideRows;
+    const int br = n_wrt >= 4 ? 4 : (n_wrt >= 2 ? 2 : 1);
+    hipLaunchKernelGGL(lm_head_wide_kernel, dim3(kWideGrid), dim3(512), 0, st, a.Z, a.ldz, a.W, a.K, a.V, a.target,
+                       a.M, a.part, a.tgt_logit, n_vt, br);
   }
   return hipGetLastError();
 }

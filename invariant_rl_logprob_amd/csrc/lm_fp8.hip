@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restr
   constexpr int NE = R * MB * 16;             // row scales per chunk: (step, mb, row)
   constexpr int NEB = (NE + 63) / 64;         // ... in 64-entry copies
   constexpr int ACOPY = (ABLK + 3) / 4, ECOPY = (NEB + 3) / 4;  // copies per wave per chunk
-  __shared__ float red[4][16 * MB];
+  __shared__ float red[2][4][16 * MB];
   __shared__ u32x4 lds_a[2][ABLK * 64];
   __shared__ int32_t lds_e[2][NEB * 64];
   __shared__ int32_t lds_w[2][kF8MaxSteps];
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restr
       }
     });
   }
-  lm_tile_epilogue<MB>(acc, red, tile, m0, M, V, target, part, tgt_logit, n_vt);
+  lm_tile_epilogue<MB>(acc, red, wave, tile, m0, M, V, target, part, tgt_logit, n_vt);
 }
 
 // ---------------------------------------------------------------------------

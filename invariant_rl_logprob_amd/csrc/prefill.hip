@@ -28,14 +28,6 @@ namespace ril {
 template <int D, bool FP8>
 constexpr int lds_page_bytes() { return (FP8 ? 32 * D : 64 * D) + 128; }
 
-// s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this wave are
-// outstanding (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N <= 63, "vmcnt field");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
-}
-
 template <int D, int NW, int NBUF, bool FP8>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const bf16_t *__restrict__ q, int q_row_stride, const int32_t *__restrict__ cu,
