@@ -82,21 +82,41 @@ __device__ __forceinline__ float max16(float v) {
   v = fmaxf(v, shfl_xor_f(v, 8));
   return v;
 }
+// The value of lane l and of lane l^16 (xchg16) or l^32 (xchg32), as a pair whose order
+// depends on the lane: the row swaps of gfx950 (v_permlane16/32_swap, plain VALU work with
+// no LDS round trip) applied to two copies of v.  Callers combine the pair with a
+// commutative operation, so both lanes of a pair end with identical bits.  The whole wave
+// must be active.
+struct f32pair {
+  float a, b;
+};
+__device__ __forceinline__ f32pair xchg16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32pair xchg32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
 // Across the 4 lane groups (lanes l, l^16, l^32, l^48): xor 16 then xor 32.
 __device__ __forceinline__ float sum_groups(float v) {
-  v = v + shfl_xor_f(v, 16);
-  v = v + shfl_xor_f(v, 32);
-  return v;
+  f32pair p = xchg16(v);
+  v = p.a + p.b;
+  p = xchg32(v);
+  return p.a + p.b;
 }
 __device__ __forceinline__ float max_groups(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  v = fmaxf(v, shfl_xor_f(v, 32));
-  return v;
+  f32pair p = xchg16(v);
+  v = fmaxf(p.a, p.b);
+  p = xchg32(v);
+  return fmaxf(p.a, p.b);
 }
 // Whole-wave sum: xor 32, 16, 8, 4, 2, 1.
 __device__ __forceinline__ float sum64(float v) {
-  v = v + shfl_xor_f(v, 32);
-  v = v + shfl_xor_f(v, 16);
+  f32pair p = xchg32(v);
+  v = p.a + p.b;
+  p = xchg16(v);
+  v = p.a + p.b;
   v = v + shfl_xor_f(v, 8);
   v = v + shfl_xor_f(v, 4);
   v = v + shfl_xor_f(v, 2);
