@@ -140,6 +140,27 @@ def lm_head_sweep(w, lm8, args):
     return {"head": "W8A8 block FP8 (e4m3, E8M0 scales)" if lm8 else "bf16", "mfma_peak_tflops": peak, "rows": out}
 
 
+def lm_head_rows(M):
+    """One untimed and three timed launches of the bf16 lm-head (ril_lm_head_logprobs) on M
+    N(0,1) rows of the GQA workload's head: the command the lm-head kernel profiles use."""
+    import torch
+    import workloads as wl
+    from invariant_rl_logprob_amd.session import Session
+    w = wl.GQA_DECODE_B64
+    w_lm = wl.gqa_head_weights(w, device="cuda")["w_lm"]
+    sess = Session(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, vocab=w.vocab,
+                   d_head=w.d_head, w_lm=w_lm, max_rows=64, max_tokens=M, max_ctx=64, pool_pages=8,
+                   softmax_scale=1.0)
+    del w_lm
+    g = torch.Generator(device="cuda").manual_seed(77)
+    z = torch.randn(M, w.d_head, generator=g, device="cuda").to(torch.bfloat16)
+    t = torch.randint(0, w.vocab, (M,), generator=g, device="cuda").to(torch.int32)
+    ms = time_launch(lambda: sess.lm_head(z, t), 3, 1)
+    tf = 2.0 * M * w.d_head * w.vocab / (ms * 1e-3) / 1e12
+    return {"lm_head_rows": M, "us_per_launch": round(ms * 1e3, 1), "tflops": round(tf, 1),
+            "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -694,6 +715,9 @@ def main():
     ap.add_argument("--long-all-chunks", action="store_true", help="long_mix: also run the 512-token chunks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")
+    ap.add_argument("--lm-head-rows", type=int, default=0,
+                    help="only run the bf16 lm-head of the GQA workload on this many N(0,1) rows, one untimed "
+                         "and three timed launches (kernel profiles at a chosen M)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -710,6 +734,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return
+
+    if args.lm_head_rows > 0:
+        print(json.dumps(lm_head_rows(args.lm_head_rows)), flush=True)
         return
 
     res = WORKLOADS[args.workload](args)

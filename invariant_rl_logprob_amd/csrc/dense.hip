@@ -387,7 +387,8 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
 //
 // The grid is kWideGrid persistent workgroups.  Workgroup g runs on XCD g%8 (workgroups
 // are dispatched to the 8 XCDs round-robin) and is its XCD's l = g/8; the 32 workgroups
-// of an XCD work through blocks of br x (32/br) tiles (row tiles x vocabulary tiles),
+// of an XCD work through blocks of br x (32/br) tiles (row tiles x vocabulary tiles, the
+// vocabulary tiles an aligned run of lm_rot's groups of 8, so they share one K order),
 // block b, b+8, ... for XCD b, one tile each per block.  Every workgroup starts its tiles
 // at about the same time as the others of its block, so the block's row and weight
 // slices are fetched once into the XCD's L2 and read there by all of them.  Which

@@ -7,10 +7,13 @@
 namespace ril {
 
 // Every output column accumulates its K steps in the order r, r+1, ..., nk-1, 0, ..., r-1
-// with r = (37 * tile) mod nk: one order per column, chosen by the column's tile alone
-// (never by the batch, M or the grid), which spreads the tiles' concurrent weight reads
-// over the HBM channels instead of having every tile read the same K offset at once.
-__device__ __forceinline__ int lm_rot(int tile, int nk) { return (37 * tile) % nk; }
+// with r = (37 * (tile / 8)) mod nk: one order per column, chosen by the column's tile
+// alone (never by the batch, M or the grid).  Groups of 8 consecutive vocabulary tiles
+// share r, so workgroups on 8 tiles of a group read the same activation K slice at the same
+// time (one fetch into L2 serves all of them); different groups start at different K
+// offsets, which spreads the concurrent weight reads of a decode step over the HBM
+// channels instead of having every tile read the same K offset at once.
+__device__ __forceinline__ int lm_rot(int tile, int nk) { return (37 * (tile >> 3)) % nk; }
 
 // S11 epilogue: the logits acc of one 256-column vocabulary tile (the wave of column group
 // cg owns columns 64cg .. 64cg+63 as four 16-column MFMA blocks, column 16nb + lane%16;
