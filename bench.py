@@ -43,13 +43,16 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, bytes_per_launch=None):
     """HBM bytes per launch (fetch + write) from the committed rocprofv3 PMC summary,
-    scaled by the copy calibration; None if the kernel's sources changed since."""
+    scaled by the copy calibration; None if the kernel's sources changed since or if the
+    profiled launch moved other algorithmic bytes than this one (another shape)."""
     try:
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
             rec = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
+        return None
+    if bytes_per_launch is not None and int(bytes_per_launch) != rec.get("algorithmic_bytes"):
         return None
     h = hashlib.sha256()
     for s in rec["sources"]:
@@ -284,7 +287,7 @@ def diff_check(case, rows, n=16):
 
 def roofline_hbm(kernel, achieved_gbps, bytes_per_launch, avg_us):
     return {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(kernel),
+            "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(kernel, bytes_per_launch),
             "kernel": kernel, "algorithmic_bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(avg_us, 2)}
 
