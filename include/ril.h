@@ -99,6 +99,15 @@ enum { RIL_KV_BF16 = 0, RIL_KV_FP8_E4M3 = 1 };
  * 128-wide K block at a time in the column's fixed order; the softmax partials and the
  * logprob are then formed exactly as in the bf16 head. */
 enum { RIL_LM_BF16 = 0, RIL_LM_W8A8_FP8 = 1 };
+/* Projection precision (same post, section 4.1: the deployment's GEMMs are W8A8 with
+ * block-FP8 weights, and the trainer runs the same GEMMs).  RIL_PROJ_W8A8_FP8: every
+ * projection of the model (w_qkv, w_o, w_gate_up, w_down) multiplies the rows' block-FP8
+ * codes (1 x 128 groups by the rule above, quantized at each call) by the weight's
+ * block-FP8 codes (128 x 128 blocks, written by ril_quantize_weight_fp8): fp32 sums over
+ * K of code products times both scales, one 128-wide K block at a time in the order
+ * k = 0, 128, 256, ... for every M; the output is rounded to bf16 and the residual added
+ * as in the bf16 path.  Each projection's K (d_model, Hq*D, d_ff) is a multiple of 128. */
+enum { RIL_PROJ_BF16 = 0, RIL_PROJ_W8A8_FP8 = 1 };
 enum { RIL_INPUT_TOKENS = 0, RIL_INPUT_QKV = 1 };
 
 /* Model description.  All sizes are fixed for the life of the handle; the
@@ -153,6 +162,9 @@ typedef struct ril_model_desc {
   int32_t lm_dtype;       /* RIL_LM_BF16 (0): w_lm as written by ril_pack_lm_head;
                              RIL_LM_W8A8_FP8 (1): w_lm as written by ril_pack_lm_head_fp8,
                              d_head a multiple of 128                                       */
+  int32_t proj_dtype;     /* RIL_PROJ_BF16 (0): w_qkv, w_o, w_gate_up, w_down bf16 as above;
+                             RIL_PROJ_W8A8_FP8 (1): each written by ril_quantize_weight_fp8
+                             from that bf16 matrix (16-byte aligned)                        */
 } ril_model_desc;
 
 typedef struct ril_model ril_model;  /* opaque: copy of the description + derived sizes */
@@ -238,6 +250,30 @@ ril_status ril_quantize_rows_fp8(const void *src, int32_t rows, int32_t K, int32
                                  void *stream);
 ril_status ril_pack_lm_head_fp8(const void *src, int32_t vocab, int32_t d_head, void *dst, size_t packed_bytes,
                                 void *stream);
+
+/* Block-FP8 projection weight (RIL_PROJ_W8A8_FP8).  One buffer: the E4M3 codes [N, K]
+ * (row-major, one byte per weight), then the biased E8M0 exponents (int32, 127 + e,
+ * 255 = NaN) of the 128 x 128 blocks, [ceil(N/128), K/128]: block (b, kb) covers rows
+ * 128b .. 128b+127 and K values 128kb .. 128kb+127, rows past N counting as zero.
+ * ril_proj_fp8_bytes: N*K + ceil(N/128)*(K/128)*4 (0 for N < 1 or K not a positive
+ * multiple of 128).
+ * ril_quantize_weight_fp8: enqueue, on `stream`, the quantization of the row-major bf16
+ * device matrix src[N, K] into dst (device, dst_bytes >= the size above, 16-byte
+ * aligned, not overlapping src); two kernels (block scales, then codes).  Call it again
+ * after every weight update.  Returns RIL_EINVAL on bad sizes, alignment or a short dst,
+ * RIL_EHIP on a launch error. */
+size_t ril_proj_fp8_bytes(int32_t N, int32_t K);
+ril_status ril_quantize_weight_fp8(const void *src, int32_t N, int32_t K, void *dst, size_t dst_bytes, void *stream);
+
+/* The W8A8 projection GEMM alone, for callers that run a projection outside a model (a
+ * trainer's recompute, tests): enqueue out[rows, N] = bf16(A W^T) with A given as codes
+ * [rows, K] and exps [rows, K/128] (ril_quantize_rows_fp8) and W as written by
+ * ril_quantize_weight_fp8 (N rows, the same K).  out is bf16 device memory, row stride
+ * ldo >= N elements.  Each element's K order is k = 0, 128, ... for every rows.  Pointers
+ * 16-byte (exps: 4-byte; out: 2-byte) aligned.  Returns RIL_EINVAL on bad sizes or
+ * pointers, RIL_EHIP on a launch error; rows = 0 enqueues nothing. */
+ril_status ril_proj_w8a8(const void *codes, const void *exps, int32_t rows, int32_t K, const void *w, int32_t N,
+                         void *out, int32_t ldo, void *stream);
 
 /* S1: page assignment.  Wrap a caller-owned device pool of `pool_bytes`
  * bytes (16-byte aligned) as floor(pool_bytes / page_bytes) pages and build a
@@ -390,7 +426,8 @@ enum {
   RIL_K_SILU_MUL = 10,    /* the SwiGLU activation */
   RIL_K_QUANT_ROWS = 11,  /* W8A8 head: block-FP8 activation quantization */
   RIL_K_LM_HEAD_FP8 = 12, /* S11 in W8A8 block FP8 */
-  RIL_K_COUNT = 13
+  RIL_K_GEMM_FP8 = 13,    /* S4 in W8A8 block FP8 */
+  RIL_K_COUNT = 14
 };
 ril_status ril_trace_enable(int on);
 ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches);

@@ -29,6 +29,7 @@ RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
 RIL_POLICY_INVARIANT, RIL_POLICY_SHAPE_DERIVED = 0, 1
 RIL_KV_BF16, RIL_KV_FP8_E4M3 = 0, 1
 RIL_LM_BF16, RIL_LM_W8A8_FP8 = 0, 1
+RIL_PROJ_BF16, RIL_PROJ_W8A8_FP8 = 0, 1
 
 _c_int, _c_float, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -46,6 +47,7 @@ class ril_model_desc(ctypes.Structure):
         ("kv_dtype", _c_int), ("k_scale_exp", _c_int), ("v_scale_exp", _c_int),
         ("d_ff", _c_int), ("w_gate_up", _vp), ("w_down", _vp), ("norm_mlp", _vp),
         ("lm_dtype", _c_int),
+        ("proj_dtype", _c_int),
     ]
 
 
@@ -86,6 +88,9 @@ _lm_head_logprobs = _sig("ril_lm_head_logprobs", _c_int,
 _hbm_read_probe_words = _sig("ril_hbm_read_probe_words", _c_int, [])
 _hbm_read_probe = _sig("ril_hbm_read_probe", _c_int, [_vp, ctypes.c_size_t, _vp, _vp])
 _quantize_rows_fp8 = _sig("ril_quantize_rows_fp8", _c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
+_proj_fp8_bytes = _sig("ril_proj_fp8_bytes", ctypes.c_size_t, [_c_int, _c_int])
+_quantize_weight_fp8 = _sig("ril_quantize_weight_fp8", _c_int, [_vp, _c_int, _c_int, _vp, ctypes.c_size_t, _vp])
+_proj_w8a8 = _sig("ril_proj_w8a8", _c_int, [_vp, _vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp])
 _ws_attn_offset = _sig("ril_ws_attn_offset", ctypes.c_size_t, [_vp])
 _kv_alloc = _sig("ril_kv_alloc", _c_int, [_vp, _vp, ctypes.c_size_t, ctypes.c_uint64, ctypes.POINTER(_vp)])
 _kv_assign = _sig("ril_kv_assign", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)])
@@ -110,7 +115,8 @@ _trace_read = _sig("ril_trace_read", _c_int, [_c_int, ctypes.POINTER(ctypes.c_do
 
 EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril_kv_page_bytes",
             "ril_lm_head_packed_bytes", "ril_pack_lm_head", "ril_lm_head_fp8_packed_bytes", "ril_pack_lm_head_fp8",
-            "ril_quantize_rows_fp8", "ril_lm_head_logprobs", "ril_hbm_read_probe_words", "ril_hbm_read_probe",
+            "ril_quantize_rows_fp8", "ril_proj_fp8_bytes", "ril_quantize_weight_fp8", "ril_proj_w8a8",
+            "ril_lm_head_logprobs", "ril_hbm_read_probe_words", "ril_hbm_read_probe",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
             "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_set_policy", "ril_trace_enable",
@@ -122,7 +128,7 @@ RIL_K_RMSNORM, RIL_K_GEMM, RIL_K_LM_HEAD, RIL_K_VOCAB_MERGE = 4, 5, 6, 7
 RIL_K_INDEXER, RIL_K_TOPK, RIL_K_SILU_MUL = 8, 9, 10
 RIL_K_QUANT_ROWS, RIL_K_LM_HEAD_FP8, RIL_K_COUNT = 11, 12, 13
 KERNEL_NAMES = ("kv_write", "attn_split", "attn_merge", "attn_prefill", "rmsnorm", "gemm", "lm_head",
-                "vocab_merge", "indexer", "topk", "silu_mul", "quant_rows", "lm_head_fp8")
+                "vocab_merge", "indexer", "topk", "silu_mul", "quant_rows", "lm_head_fp8", "gemm_fp8")
 
 
 class RilError(RuntimeError):
@@ -205,6 +211,30 @@ def ril_quantize_rows_fp8(x, codes, exps, stream=None) -> None:
         raise ValueError("ril_quantize_rows_fp8: output tensors too small")
     _check(_quantize_rows_fp8(_ptr(x), rows, K, x.stride(0), _ptr(codes), _ptr(exps), _stream(stream)),
            "ril_quantize_rows_fp8")
+
+
+def ril_proj_fp8_bytes(N: int, K: int) -> int:
+    return int(_proj_fp8_bytes(N, K))
+
+
+def ril_quantize_weight_fp8(w, dst, stream=None) -> None:
+    """Block-FP8 quantization of the row-major bf16 device matrix w [N, K] into dst (a
+    device byte tensor of at least ril_proj_fp8_bytes(N, K) bytes: codes, then the block
+    exponents), on the stream."""
+    N, K = w.shape
+    _check(_quantize_weight_fp8(_ptr(w), N, K, _ptr(dst), dst.numel() * dst.element_size(), _stream(stream)),
+           "ril_quantize_weight_fp8")
+
+
+def ril_proj_w8a8(codes, exps, w8, N: int, out, stream=None) -> None:
+    """out[rows, N] = bf16(A W^T) for rows given as block-FP8 codes (uint8 [rows, K]) and
+    exps (int32 [rows, K/128]) and W as written by ril_quantize_weight_fp8 (N rows);
+    out is a bf16 device tensor [rows, >= N] (row stride out.stride(0))."""
+    rows, K = codes.shape
+    if exps.numel() < rows * (K // 128) or out.shape[0] < rows or out.shape[1] < N:
+        raise ValueError("ril_proj_w8a8: exps or out too small")
+    _check(_proj_w8a8(_ptr(codes), _ptr(exps), rows, K, _ptr(w8), N, _ptr(out), out.stride(0), _stream(stream)),
+           "ril_proj_w8a8")
 
 
 def ril_lm_head_logprobs(model: int, z, targets, logprob_out, ws, stream=None) -> None:

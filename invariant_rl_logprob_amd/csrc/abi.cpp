@@ -32,6 +32,8 @@ struct ril_model {
   size_t off_scores, off_sel;  // sparse: indexer scores [max_rows, max_ctx], selections [max_rows, topk]
   size_t off_gu = 0, off_act = 0, off_y2 = 0;  // SwiGLU MLP: [R, 2F], [R, F], [R, d_model] bf16
   bool lm_fp8 = false;                        // W8A8 block-FP8 lm-head
+  bool proj_fp8 = false;                      // W8A8 block-FP8 projections
+  size_t off_p8 = 0, off_pe = 0;              // projection rows' codes and exponents
   size_t off_a8 = 0, off_ea = 0;              // its activation codes [R, d_head], exponents [R, d_head/128]
   size_t ws_base;   // end of the invariant path's segments
   size_t ws_total;  // ws_base + the comparator's split-K partials when that policy is on
@@ -116,6 +118,15 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
     return fail(RIL_EINVAL, "model_create: MLP weights given with d_ff = 0");
   if (d.lm_dtype != RIL_LM_BF16 && d.lm_dtype != RIL_LM_W8A8_FP8)
     return fail(RIL_EINVAL, "model_create: lm_dtype %d", d.lm_dtype);
+  if (d.proj_dtype != RIL_PROJ_BF16 && d.proj_dtype != RIL_PROJ_W8A8_FP8)
+    return fail(RIL_EINVAL, "model_create: proj_dtype %d", d.proj_dtype);
+  if (d.proj_dtype == RIL_PROJ_W8A8_FP8) {
+    const bool tk = d.input_mode == RIL_INPUT_TOKENS;
+    const int qk = d.n_q_heads * d.head_dim;
+    if ((tk && d.d_model % 128) || (d.w_o && qk % 128) || (d.d_ff && d.d_ff % 128))
+      return fail(RIL_EINVAL, "model_create: W8A8 projections need every K (d_model %d, Hq*D %d, d_ff %d) a "
+                  "multiple of 128", d.d_model, qk, d.d_ff);
+  }
   if (d.lm_dtype == RIL_LM_W8A8_FP8 && (d.d_head <= 0 || d.d_head % 128))
     return fail(RIL_EINVAL, "model_create: the W8A8 lm-head needs d_head a multiple of 128 (%d)", d.d_head);
   if (d.kv_dtype != RIL_KV_BF16 && d.kv_dtype != RIL_KV_FP8_E4M3)
@@ -181,6 +192,14 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   if (m->lm_fp8) {
     m->off_a8 = seg(R * d.d_head);
     m->off_ea = seg(R * (size_t)(d.d_head / 128) * sizeof(int32_t));
+  }
+  m->proj_fp8 = d.proj_dtype == RIL_PROJ_W8A8_FP8;
+  if (m->proj_fp8) {
+    size_t kmax = d.w_o ? (size_t)qw : 0;
+    if (tok) kmax = std::max(kmax, (size_t)d.d_model);
+    if (d.d_ff) kmax = std::max(kmax, (size_t)d.d_ff);
+    m->off_p8 = seg(R * kmax);
+    m->off_pe = seg(R * (kmax / 128) * sizeof(int32_t));
   }
   m->off_vpart = seg(R * m->n_vt * 2 * sizeof(float));
   m->off_tgt = seg(R * sizeof(float));
@@ -319,6 +338,41 @@ extern "C" ril_status ril_quantize_rows_fp8(const void *src, int32_t rows, int32
   if (e != hipSuccess) return fail(RIL_EHIP, "quantize_rows_fp8: %s", hipGetErrorString(e));
   return RIL_OK;
 }
+extern "C" size_t ril_proj_fp8_bytes(int32_t N, int32_t K) { return (size_t)ril::proj_fp8_bytes(N, K); }
+
+extern "C" ril_status ril_quantize_weight_fp8(const void *src, int32_t N, int32_t K, void *dst, size_t dst_bytes,
+                                              void *stream) {
+  const size_t need = (size_t)ril::proj_fp8_bytes(N, K);
+  if (need == 0) return fail(RIL_EINVAL, "quantize_weight_fp8: N %d, K %d (K a positive multiple of 128)", N, K);
+  if (!src || !dst || !aligned16(src) || !aligned16(dst))
+    return fail(RIL_EINVAL, "quantize_weight_fp8: null or misaligned pointer");
+  if (dst_bytes < need) return fail(RIL_EINVAL, "quantize_weight_fp8: dst %zu bytes, %zu needed", dst_bytes, need);
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (size_t)N * K * 2, d0 = (uintptr_t)dst, d1 = d0 + need;
+  if (s0 < d1 && d0 < s1) return fail(RIL_EINVAL, "quantize_weight_fp8: src and dst overlap");
+  uint8_t *codes = static_cast<uint8_t *>(dst);
+  int32_t *ew = reinterpret_cast<int32_t *>(codes + (size_t)N * K);
+  const hipError_t e = ril::launch_quant_weight_fp8((const bf16_t *)src, N, K, codes, ew, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "quantize_weight_fp8: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_proj_w8a8(const void *codes, const void *exps, int32_t rows, int32_t K, const void *w,
+                                    int32_t N, void *out, int32_t ldo, void *stream) {
+  if (rows < 0 || N < 1 || K < 128 || K % 128 || ldo < N)
+    return fail(RIL_EINVAL, "proj_w8a8: rows %d, K %d, N %d, ldo %d", rows, K, N, ldo);
+  if (rows == 0) return RIL_OK;
+  if (!codes || !exps || !w || !out || !aligned16(codes) || !aligned4(exps) || !aligned16(w) ||
+      ((uintptr_t)out & 1))
+    return fail(RIL_EINVAL, "proj_w8a8: null or misaligned pointer");
+  const uint8_t *w8 = static_cast<const uint8_t *>(w);
+  GemmFp8Args f{static_cast<const uint8_t *>(codes), static_cast<const int32_t *>(exps), w8,
+                reinterpret_cast<const int32_t *>(w8 + (size_t)N * K), static_cast<bf16_t *>(out), ldo, nullptr, 0,
+                rows, N, K};
+  const hipError_t e = ril::launch_gemm_fp8(f, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "proj_w8a8: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
+
 extern "C" int32_t ril_hbm_read_probe_words(void) { return ril::hbm_read_probe_blocks(); }
 
 extern "C" ril_status ril_hbm_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream) {
@@ -513,6 +567,26 @@ static ril_status check_common(const ril_model *m, ril_kv *kv, void *ws, size_t 
 static ril_status run_lm_head(const ril_model *m, int rows, const bf16_t *z, int ldz, const int32_t *targets,
                               float *out, void *ws, hipStream_t st);
 
+// One projection C = bf16(A W^T) [+ residual]: the bf16 GEMM (with the comparator's
+// shape-derived split-K under that policy), or with W8A8 projections the rows' block-FP8
+// quantization and the W8A8 GEMM (no comparator form: its K order is always 0, 128, ...).
+static ril_status run_proj(const ril_model *m, GemmArgs g, void *ws, hipStream_t st) {
+  if (m->proj_fp8) {
+    uint8_t *a8 = reinterpret_cast<uint8_t *>(ws) + m->off_p8;
+    int32_t *ea = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + m->off_pe);
+    QuantRowsArgs q{g.A, g.lda, g.M, g.K, a8, ea};
+    RIL_LAUNCH(RIL_K_QUANT_ROWS, launch_quant_rows_fp8(q, st));
+    const uint8_t *w8 = reinterpret_cast<const uint8_t *>(g.W);
+    GemmFp8Args f{a8, ea, w8, reinterpret_cast<const int32_t *>(w8 + (size_t)g.N * g.K), g.C, g.ldc, g.R, g.ldr,
+                  g.M, g.N, g.K};
+    RIL_LAUNCH(RIL_K_GEMM_FP8, launch_gemm_fp8(f, st));
+    return RIL_OK;
+  }
+  shape_split_k(m, g, ws);
+  RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
+  return RIL_OK;
+}
+
 // Attention output (in the workspace) -> [O GEMM (+ residual)] -> RMSNorm -> lm-head.
 static ril_status run_head(const ril_model *m, int rows, const int32_t *targets, float *out, void *ws,
                            hipStream_t st) {
@@ -524,8 +598,8 @@ static ril_status run_head(const ril_model *m, int rows, const int32_t *targets,
     const bool tok = d.input_mode == RIL_INPUT_TOKENS;
     GemmArgs g{src, qw, (const bf16_t *)d.w_o, qw, wsb(ws, m->off_y), d.d_head,
                tok ? wsb(ws, m->off_x) : nullptr, d.d_model, rows, d.d_head, qw};
-    shape_split_k(m, g, ws);
-    RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
+    const ril_status s = run_proj(m, g, ws, st);
+    if (s != RIL_OK) return s;
     src = wsb(ws, m->off_y);
     ld = d.d_head;
   }
@@ -536,14 +610,14 @@ static ril_status run_head(const ril_model *m, int rows, const int32_t *targets,
     RIL_LAUNCH(RIL_K_RMSNORM, launch_rmsnorm(rn, st));
     GemmArgs g1{wsb(ws, m->off_h), d.d_model, (const bf16_t *)d.w_gate_up, d.d_model, wsb(ws, m->off_gu), 2 * F,
                 nullptr, 0, rows, 2 * F, d.d_model};
-    shape_split_k(m, g1, ws);
-    RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g1, st));
+    ril_status s = run_proj(m, g1, ws, st);
+    if (s != RIL_OK) return s;
     SiluMulArgs sm{wsb(ws, m->off_gu), 2 * F, wsb(ws, m->off_act), F, rows, F};
     RIL_LAUNCH(RIL_K_SILU_MUL, launch_silu_mul(sm, st));
     GemmArgs g2{wsb(ws, m->off_act), F, (const bf16_t *)d.w_down, F, wsb(ws, m->off_y2), d.d_model,
                 src, ld, rows, d.d_model, F};
-    shape_split_k(m, g2, ws);
-    RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g2, st));
+    s = run_proj(m, g2, ws, st);
+    if (s != RIL_OK) return s;
     src = wsb(ws, m->off_y2);
     ld = d.d_model;
   }
@@ -585,9 +659,7 @@ static ril_status run_token_front(const ril_model *m, int rows, const int32_t *t
   RIL_LAUNCH(RIL_K_RMSNORM, launch_rmsnorm(r, st));
   GemmArgs g{wsb(ws, m->off_h), d.d_model, (const bf16_t *)d.w_qkv, d.d_model, wsb(ws, m->off_qkv), wqkv,
              nullptr, 0, rows, wqkv, d.d_model};
-  shape_split_k(m, g, ws);
-  RIL_LAUNCH(RIL_K_GEMM, launch_gemm(g, st));
-  return RIL_OK;
+  return run_proj(m, g, ws, st);
 }
 
 static ril_status check_prefill(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b, void *ws,

@@ -108,6 +108,19 @@ struct LmHeadArgs {
 
 // Block-FP8 activation quantization: A8 = E4M3 codes of Z, ea = biased E8M0 exponents
 // of its 1 x 128 groups.
+// W8A8 projection: C = bf16(A W^T) (+ residual as GemmArgs) from block-FP8 codes and
+// biased E8M0 exponents (rows: [M, K] + [M, K/128]; weight: [N, K] + [ceil(N/128), K/128]).
+struct GemmFp8Args {
+  const uint8_t *A8;
+  const int32_t *ea;
+  const uint8_t *W8;
+  const int32_t *ew;
+  bf16_t *C;
+  int ldc;
+  const bf16_t *R;
+  int ldr, M, N, K;
+};
+
 struct QuantRowsArgs {
   const bf16_t *Z;
   int ldz, M, K;
@@ -184,5 +197,8 @@ long lm_head_fp8_exp_count(int V, int K);
 int hbm_read_probe_blocks();
 hipError_t launch_hbm_read_probe(const void *src, size_t bytes, uint32_t *out, hipStream_t st);
 hipError_t launch_pack_lm_head_fp8(const bf16_t *src, int V, int K, uint8_t *codes, int32_t *ew, hipStream_t st);
+long proj_fp8_bytes(int N, int K);
+hipError_t launch_quant_weight_fp8(const bf16_t *src, int N, int K, uint8_t *codes, int32_t *ew, hipStream_t st);
+hipError_t launch_gemm_fp8(const GemmFp8Args &a, hipStream_t st);
 
 }  // namespace ril

@@ -337,8 +337,160 @@ __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restr
 }
 
 // ---------------------------------------------------------------------------
+// W8A8 projections (the same deployment rule for the model's GEMMs).  Weight [N, K]
+// row-major bf16 -> codes [N, K] (one byte per weight, row-major) and biased exponents
+// ew [ceil(N/128), K/128] of the 128 x 128 blocks (pack_fp8_exp_kernel over 128-row
+// blocks).  16 codes per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_weight_fp8_codes_kernel(const bf16_t *__restrict__ src, int K,
+                                                                     const int32_t *__restrict__ ew,
+                                                                     uint8_t *__restrict__ dst, long n_pieces) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_pieces) return;
+  const int nk = K >> 7, per_row = K >> 4;
+  const long row = i / per_row;
+  const int k = (int)(i % per_row) * 16;
+  const int be = ew[(row >> 7) * nk + (k >> 7)];
+  const int sh = be == 255 ? 0 : 127 - be;
+  const u32x4 v0 = ld16(src + row * K + k), v1 = ld16(src + row * K + k + 8);
+  uint32_t hw[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hw[j] = fp8_codes2(__builtin_ldexpf(bf2f((bf16_t)(v0[j] & 0xffffu)), sh),
+                       __builtin_ldexpf(bf2f((bf16_t)(v0[j] >> 16)), sh));
+    hw[4 + j] = fp8_codes2(__builtin_ldexpf(bf2f((bf16_t)(v1[j] & 0xffffu)), sh),
+                           __builtin_ldexpf(bf2f((bf16_t)(v1[j] >> 16)), sh));
+  }
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = hw[2 * j] | (hw[2 * j + 1] << 16);
+  st16(dst + i * 16, out);
+}
+
+// C[M, N] = bf16(A W^T), or bf16(R + bf16(A W^T)), from the rows' codes A8 [M, K] and
+// exponents ea [M, K/128] and the weight's codes W8 [N, K] and exponents ew
+// [ceil(N/128), K/128].  Every output element is one chain of scaled FP8 MFMAs over K in
+// 128-wide steps k = 0, 128, 256, ... in order, from zero: the M tile a workgroup owns,
+// the grid and the number of rows never change it.  Workgroup = 4 waves side by side
+// along N, a wave owning MB x NB 16x16 blocks; the operands (two 16-byte loads per lane
+// per block) and the lane's scales of step s+1 are loaded while step s runs.
+template <int MB, int NB>
+__global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict__ A8, const int32_t *__restrict__ ea,
+                                                       const uint8_t *__restrict__ W8, const int32_t *__restrict__ ew,
+                                                       bf16_t *__restrict__ C, int ldc, const bf16_t *__restrict__ R,
+                                                       int ldr, int M, int N, int K) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int m0 = blockIdx.y * 16 * MB;
+  const int n0 = (blockIdx.x * 4 + wave) * 16 * NB;
+  if (n0 >= N) return;
+  const int nk = K >> 7;
+  const uint8_t *ap[MB], *wp[NB];
+  const int32_t *sap[MB], *swp[NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = min(m0 + 16 * mb + r16, M - 1);  // rows past M are computed and dropped
+    ap[mb] = A8 + (long)row * K + grp * 32;
+    sap[mb] = ea + (long)row * nk;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = min(n0 + 16 * nb + r16, N - 1);
+    wp[nb] = W8 + (long)col * K + grp * 32;
+    swp[nb] = ew + (long)(col >> 7) * nk;
+  }
+  struct Ops {
+    u32x4 a[MB][2], b[NB][2];
+    int sa[MB], sb[NB];
+  };
+  auto load = [&](int s, Ops &o) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      o.a[mb][0] = ld16(ap[mb] + s * 128);
+      o.a[mb][1] = ld16(ap[mb] + s * 128 + 16);
+      o.sa[mb] = sap[mb][s];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      o.b[nb][0] = ld16(wp[nb] + s * 128);
+      o.b[nb][1] = ld16(wp[nb] + s * 128 + 16);
+      o.sb[nb] = swp[nb][s];
+    }
+  };
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const Ops &o) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = mfma_fp8(cat8(o.a[mb][0], o.a[mb][1]), cat8(o.b[nb][0], o.b[nb][1]), acc[mb][nb], o.sa[mb],
+                               o.sb[nb]);
+  };
+  Ops o0, o1;
+  load(0, o0);
+  for (int s = 0; s < nk; s += 2) {
+    if (s + 1 < nk) load(s + 1, o1);
+    step(o0);
+    if (s + 1 < nk) {
+      if (s + 2 < nk) load(s + 2, o0);
+      step(o1);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = n0 + 16 * nb + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * mb + 4 * grp + i;
+        if (row < M && col < N) {
+          float v = bf2f(f2bf(acc[mb][nb][i]));
+          if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+          C[(long)row * ldc + col] = f2bf(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+
+long proj_fp8_bytes(int N, int K) {
+  if (N < 1 || K < 128 || K % 128) return 0;
+  return (long)N * K + (long)((N + 127) / 128) * (K / 128) * 4;
+}
+
+hipError_t launch_quant_weight_fp8(const bf16_t *src, int N, int K, uint8_t *codes, int32_t *ew, hipStream_t st) {
+  const long n_pieces = (long)N * K / 16;
+  if (n_pieces == 0) return hipSuccess;
+  const long blocks = (n_pieces + 255) / 256;
+  if (blocks > 0x7fffffffL || K / 128 > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_fp8_exp_kernel, dim3((N + 127) / 128, K / 128), dim3(256), 0, st, src, N, K, ew);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quant_weight_fp8_codes_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, K, ew, codes,
+                     n_pieces);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const GemmFp8Args &a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+#define RIL_G8(MB_, NB_)                                                                                         \
+  hipLaunchKernelGGL((gemm_fp8_kernel<MB_, NB_>), dim3((a.N + 64 * NB_ - 1) / (64 * NB_), (a.M + 16 * MB_ - 1) / (16 * MB_)), \
+                     dim3(256), 0, st, a.A8, a.ea, a.W8, a.ew, a.C, a.ldc, a.R, a.ldr, a.M, a.N, a.K)
+  if (a.M <= 16) RIL_G8(1, 1);
+  else if (a.M <= 64) RIL_G8(4, 1);
+  else RIL_G8(4, 2);
+#undef RIL_G8
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows_fp8(const QuantRowsArgs &a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;

@@ -18,7 +18,7 @@ from . import (RIL_ATTN_GQA, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch,
                ril_kv_release, ril_kv_write, ril_lm_head_packed_bytes, ril_model_create, ril_model_desc,
                ril_model_destroy, ril_pack_lm_head, ril_prefill_logprobs, ril_set_policy,
                ril_lm_head_fp8_packed_bytes, ril_pack_lm_head_fp8, RIL_LM_BF16, RIL_LM_W8A8_FP8,
-               ril_lm_head_logprobs,
+               ril_lm_head_logprobs, RIL_PROJ_BF16, RIL_PROJ_W8A8_FP8, ril_proj_fp8_bytes, ril_quantize_weight_fp8,
                ril_workspace_bytes, ril_ws_attn_offset)
 
 PAGE = 16
@@ -44,7 +44,7 @@ class Session:
                  input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
                  norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, index_heads=0, index_dim=0, topk=0,
                  kv_dtype=0, k_scale_exp=0, v_scale_exp=0, d_ff=0, w_gate_up=None, w_down=None, norm_mlp=None,
-                 lm_dtype=RIL_LM_BF16, device="cuda"):
+                 lm_dtype=RIL_LM_BF16, proj_dtype=RIL_PROJ_BF16, device="cuda"):
         self.device = torch.device(device)
         # the lm-head weight lives in the library's packed layout (w_lm stays row-major):
         # bf16 operands, or block-FP8 codes and scales for the W8A8 head
@@ -54,13 +54,24 @@ class Session:
         self.w_lm_packed = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.pack_lm_head = ril_pack_lm_head_fp8 if fp8 else ril_pack_lm_head
         self.pack_lm_head(w_lm, self.w_lm_packed)
+        if proj_dtype == RIL_PROJ_W8A8_FP8:
+            # each projection weight in its block-FP8 form (codes, then block exponents)
+            def q8(w):
+                if w is None:
+                    return None
+                w = w.contiguous()
+                out = torch.empty(ril_proj_fp8_bytes(*w.shape), dtype=torch.uint8, device=self.device)
+                ril_quantize_weight_fp8(w, out)
+                return out
+            w_qkv, w_o, w_gate_up, w_down = q8(w_qkv), q8(w_o), q8(w_gate_up), q8(w_down)
         self._keep = [embed, w_qkv, w_o, norm_attn, norm_final, w_gate_up, w_down, norm_mlp]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
                                    index_heads, index_dim, topk, d_head, vocab, PAGE, split_tokens, max_rows,
                                    max_tokens, max_ctx, softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o),
                                    p(norm_attn), p(norm_final), p(self.w_lm_packed), kv_dtype, k_scale_exp,
-                                   v_scale_exp, d_ff, p(w_gate_up), p(w_down), p(norm_mlp), lm_dtype)
+                                   v_scale_exp, d_ff, p(w_gate_up), p(w_down), p(norm_mlp), lm_dtype,
+                                   proj_dtype)
         self.model = ril_model_create(self.desc)
         self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
         self.max_ctx = max_ctx

@@ -15,7 +15,7 @@ import math
 import numpy as np
 
 from .numerics import attention_row, bf16, lm_head_logprob, log_softmax_at, rmsnorm, swiglu_rounded_once, widen
-from .fp8block import lm_head_logprob_w8a8
+from .fp8block import lm_head_logprob_w8a8, w8a8_matmul
 
 
 # ---------------------------------------------------------------------------
@@ -26,7 +26,17 @@ def _tiny_params(p):
     return {k: widen(v) for k, v in p.items()}
 
 
-def _mlp(P, y, eps):
+def _matmul(a, W, proj_w8a8: bool):
+    """a W^T: exact in fp64 from the bf16 values, or (proj_w8a8) the exact product of the
+    block-FP8 quantized operands (fp8block.w8a8_matmul: rows in 1 x 128 groups, the weight
+    in 128 x 128 blocks, the deployment rule of the Bitwise-consistent RL post, section
+    4.1).  a is [M, K] or one row [K]."""
+    if not proj_w8a8:
+        return a @ W.T
+    return w8a8_matmul(np.atleast_2d(a), W).reshape(a.shape[:-1] + (W.shape[0],))
+
+
+def _mlp(P, y, eps, proj_w8a8=False):
     """The SwiGLU block after the attention residual, when the parameters have one
     (w_gate_up [2F, d]: gate rows then up rows; w_down [d, F]; norm_mlp [d]):
         h = bf16(rms(y) g3);  [g|u] = bf16(h Wgu^T);  a = bf16(silu(g) u)  (rounded once)
@@ -37,13 +47,13 @@ def _mlp(P, y, eps):
         return y
     F = P["w_down"].shape[1]
     h = bf16(rmsnorm(y, P["norm_mlp"], eps))
-    gu = bf16(h @ P["w_gate_up"].T)
+    gu = bf16(_matmul(h, P["w_gate_up"], proj_w8a8))
     a = swiglu_rounded_once(gu[..., :F], gu[..., F:])
-    return bf16(y + bf16(a @ P["w_down"].T))
+    return bf16(y + bf16(_matmul(a, P["w_down"], proj_w8a8)))
 
 
 def tiny_decoder_prefill(params, tokens, targets, n_q_heads, n_kv_heads, head_dim,
-                         eps=1e-6):
+                         eps=1e-6, proj_w8a8=False):
     """Full-sequence (prefill / trainer recompute) logprobs of a 1-layer decoder.
 
     The trainer recomputes each sampled token's logprob over the whole prefix
@@ -54,6 +64,8 @@ def tiny_decoder_prefill(params, tokens, targets, n_q_heads, n_kv_heads, head_di
         o_i = bf16(softmax_j<=i(q_i . k_j / sqrt(D)) v)    (q head h -> kv head h*Hkv/Hq)
         y = bf16(x + bf16(o Wo^T));  [y = the SwiGLU block of _mlp, when present]
         z = bf16(rms(y) g2);  l = z Wlm^T;  lp_i = log_softmax(l_i)[targets[i]]
+    proj_w8a8: every projection (Wqkv, Wo and the MLP's) is the block-FP8 W8A8 product
+    (``_matmul``), its output rounded to bf16 as above.
     Returns float64 [L].  Pinned by: agreement with ``tiny_decoder_decode``
     (coded separately) to 1e-12; closed forms with zeroed weights.
     """
@@ -64,7 +76,7 @@ def tiny_decoder_prefill(params, tokens, targets, n_q_heads, n_kv_heads, head_di
     group = Hq // Hkv
     x = P["embed"][t]
     h = bf16(rmsnorm(x, P["norm_attn"], eps))
-    qkv = bf16(h @ P["w_qkv"].T)
+    qkv = bf16(_matmul(h, P["w_qkv"], proj_w8a8))
     q = qkv[:, : Hq * D].reshape(L, Hq, D)
     k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(L, Hkv, D)
     v = qkv[:, (Hq + Hkv) * D:].reshape(L, Hkv, D)
@@ -75,15 +87,15 @@ def tiny_decoder_prefill(params, tokens, targets, n_q_heads, n_kv_heads, head_di
             g = hh // group
             o[i, hh] = attention_row(q[i, hh], k[: i + 1, g], v[: i + 1, g], scale)
     o = bf16(o).reshape(L, Hq * D)
-    y = bf16(x + bf16(o @ P["w_o"].T))
-    y = _mlp(P, y, eps)
+    y = bf16(x + bf16(_matmul(o, P["w_o"], proj_w8a8)))
+    y = _mlp(P, y, eps, proj_w8a8)
     z = bf16(rmsnorm(y, P["norm_final"], eps))
     logits = z @ P["w_lm"].T
     return np.array([log_softmax_at(logits[i], targets[i]) for i in range(L)])
 
 
 def tiny_decoder_decode(params, tokens, targets, n_prompt, n_q_heads, n_kv_heads, head_dim,
-                        eps=1e-6):
+                        eps=1e-6, proj_w8a8=False):
     """Rollout-side logprobs: a prompt pass of ``n_prompt`` tokens, then one token per step.
 
     Coded separately from ``tiny_decoder_prefill`` on purpose: an explicit
@@ -104,7 +116,7 @@ def tiny_decoder_decode(params, tokens, targets, n_prompt, n_q_heads, n_kv_heads
     def step(pos):
         x = P["embed"][t[pos]]
         h = bf16(rmsnorm(x, P["norm_attn"], eps))
-        qkv = bf16(P["w_qkv"] @ h)
+        qkv = bf16(_matmul(h, P["w_qkv"], proj_w8a8) if proj_w8a8 else P["w_qkv"] @ h)
         for g in range(Hkv):
             cache_k[g].append(qkv[(Hq + g) * D:(Hq + g + 1) * D])
             cache_v[g].append(qkv[(Hq + Hkv + g) * D:(Hq + Hkv + g + 1) * D])
@@ -121,14 +133,15 @@ def tiny_decoder_decode(params, tokens, targets, n_prompt, n_q_heads, n_kv_heads
             w = np.exp(s - s.max())
             heads.append((w[:, None] * Vc).sum(axis=0) / w.sum())
         o = bf16(np.concatenate(heads))
-        y = bf16(x + bf16(P["w_o"] @ o))
+        mv = (lambda W, a: _matmul(a, W, True)) if proj_w8a8 else (lambda W, a: W @ a)  # noqa: E731
+        y = bf16(x + bf16(mv(P["w_o"], o)))
         if "w_gate_up" in P:  # the same block, written per row with matrix-vector products
             F = P["w_down"].shape[1]
             h = bf16(rmsnorm(y, P["norm_mlp"], eps))
-            gu = bf16(P["w_gate_up"] @ h)
+            gu = bf16(mv(P["w_gate_up"], h))
             g, u = gu[:F], gu[F:]
             a = bf16(g / (1.0 + np.exp(-g)) * u)
-            y = bf16(y + bf16(P["w_down"] @ a))
+            y = bf16(y + bf16(mv(P["w_down"], a)))
         z = bf16(rmsnorm(y, P["norm_final"], eps))
         return log_softmax_at(P["w_lm"] @ z, targets[pos])
 

@@ -108,6 +108,48 @@ def test_w8a8_lm_head_descriptor_and_sizes():
         assert ril.ril_lm_head_fp8_packed_bytes(v, k) == 0
 
 
+def test_w8a8_projection_descriptor_sizes_and_bad_arguments():
+    # QKV input with an o-projection (K = Hq*D = 4096): W8A8 projections accepted, and the
+    # workspace grows by the rows' codes and exponents
+    m = ril.ril_model_create(_desc(w_o=0x20000, proj_dtype=ril.RIL_PROJ_W8A8_FP8))
+    plain = ril.ril_model_create(_desc(w_o=0x20000))
+    assert ril.ril_workspace_bytes(m) - ril.ril_workspace_bytes(plain) >= 1024 * 4096 + 1024 * 32 * 4
+    ril.ril_model_destroy(m)
+    ril.ril_model_destroy(plain)
+    for b in (dict(proj_dtype=2), dict(proj_dtype=-1),
+              dict(w_o=0x20000, proj_dtype=ril.RIL_PROJ_W8A8_FP8, n_q_heads=8, n_kv_heads=8, head_dim=64),  # K 512: ok
+              dict(input_mode=ril.RIL_INPUT_TOKENS, d_model=160, d_head=160, embed=0x30000, w_qkv=0x40000,
+                   w_o=0x20000, proj_dtype=ril.RIL_PROJ_W8A8_FP8)):  # d_model 160: not a multiple of 128
+        if b.get("n_q_heads") == 8:
+            ril.ril_model_destroy(ril.ril_model_create(_desc(**b)))
+            continue
+        with pytest.raises(ril.RilError):
+            ril.ril_model_create(_desc(**b))
+        assert ril.ril_last_error()
+    assert ril.ril_proj_fp8_bytes(300, 256) == 300 * 256 + 3 * 2 * 4
+    assert ril.ril_proj_fp8_bytes(128, 128) == 128 * 128 + 4
+    for n, k in ((0, 128), (10, 96), (10, 0), (10, 4000)):
+        assert ril.ril_proj_fp8_bytes(n, k) == 0
+    lib = ctypes.CDLL(ril.LIB_PATH)
+    lib.ril_quantize_weight_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]
+    lib.ril_proj_w8a8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    need = ril.ril_proj_fp8_bytes(300, 256)
+    # every case fails validation before anything is enqueued
+    assert lib.ril_quantize_weight_fp8(0x10000, 300, 200, 0x900000, need, None) == ril.RIL_EINVAL     # K % 128
+    assert lib.ril_quantize_weight_fp8(0x10000, 300, 256, 0x900000, need - 1, None) == ril.RIL_EINVAL  # short
+    assert lib.ril_quantize_weight_fp8(0x10008, 300, 256, 0x900000, need, None) == ril.RIL_EINVAL     # misaligned
+    assert lib.ril_quantize_weight_fp8(0x10000, 300, 256, 0x10000, need, None) == ril.RIL_EINVAL      # overlap
+    assert lib.ril_quantize_weight_fp8(None, 300, 256, 0x900000, need, None) == ril.RIL_EINVAL
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 200, 0x30000, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # K % 128
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, 0x30000, 64, 0x40000, 32, None) == ril.RIL_EINVAL  # ldo < N
+    assert lib.ril_proj_w8a8(0x10008, 0x20000, 4, 256, 0x30000, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # codes align
+    assert lib.ril_proj_w8a8(0x10000, 0x20002, 4, 256, 0x30000, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # exps align
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, None, 64, 0x40000, 64, None) == ril.RIL_EINVAL
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 0, 256, 0x30000, 64, 0x40000, 64, None) == ril.RIL_OK      # nothing
+
+
 def test_w8a8_pack_and_quantize_reject_bad_arguments():
     lib = ctypes.CDLL(ril.LIB_PATH)
     lib.ril_pack_lm_head_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,

@@ -556,6 +556,32 @@ def test_tiny_decoder_mlp_with_zero_down_projection_is_the_plain_decoder():
     assert not np.array_equal(full, b)  # the block does act when its weights are there
 
 
+def test_tiny_decoder_w8a8_projections_prefill_equals_decode():
+    """Block-FP8 projections in both oracles (the whole-sequence matrices and the per-row
+    matrix-vector form) agree to 1e-12, and they do change the result."""
+    W = wl.TINY_MLP
+    wts = wl.tiny_weights(W)
+    t = wl.tiny_tokens(2, W).numpy()[:24]
+    tg = np.roll(t, -1)
+    a = oracle.tiny_decoder_prefill(wts, t, tg, W.n_q_heads, W.n_kv_heads, W.head_dim, W.rms_eps, proj_w8a8=True)
+    b = oracle.tiny_decoder_decode(wts, t, tg, W.prompt_tokens, W.n_q_heads, W.n_kv_heads, W.head_dim,
+                                   W.rms_eps, proj_w8a8=True)
+    assert np.max(np.abs(a - b)) <= 1e-12
+    plain = oracle.tiny_decoder_prefill(wts, t, tg, W.n_q_heads, W.n_kv_heads, W.head_dim, W.rms_eps)
+    assert not np.array_equal(a, plain)
+    assert np.max(np.abs(a - plain)) < 0.5  # a perturbation of the same model, not another one
+
+
+def test_w8a8_matmul_of_one_row_equals_the_rows_form():
+    """The per-row form the decode oracle uses is the same product as the matrix form."""
+    r = np.random.default_rng(21)
+    a = on.bf16(r.standard_normal((5, 256)))
+    w = on.bf16(r.standard_normal((300, 256)) * 0.1)
+    full = oracle.w8a8_matmul(a, w)
+    for i in range(5):
+        assert np.array_equal(oracle.w8a8_matmul(a[i][None], w)[0], full[i])
+
+
 # ---------------------------------------------------------------------------
 # Block-FP8 W8A8 GEMM for the lm-head (oracle/fp8block.py)
 # ---------------------------------------------------------------------------
