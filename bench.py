@@ -143,6 +143,44 @@ def lm_head_sweep(w, lm8, args):
     return {"head": "W8A8 block FP8 (e4m3, E8M0 scales)" if lm8 else "bf16", "mfma_peak_tflops": peak, "rows": out}
 
 
+def proj_w8a8_sweep():
+    """The W8A8 projection GEMM alone (ril_proj_w8a8, codes and exponents from
+    ril_quantize_rows_fp8 / ril_quantize_weight_fp8) on the long workload's o-projection
+    shape, K = 8192 -> N = 4096, at M = 256 (a decode step's rows) and 8192 (a prefill
+    chunk): time per launch (HIP events), TFLOP/s against the dense FP8 MFMA peak, and the
+    rows' bits at both M (one K order for every M)."""
+    import numpy as np
+    import torch
+    import invariant_rl_logprob_amd as ril
+    N, K = 4096, 8192
+    g = torch.Generator(device="cuda").manual_seed(91)
+    w = (torch.randn(N, K, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    w8 = torch.empty(ril.ril_proj_fp8_bytes(N, K), dtype=torch.uint8, device="cuda")
+    ril.ril_quantize_weight_fp8(w, w8)
+    del w
+    out, first = [], None
+    xs = torch.randn(8192, K, generator=g, device="cuda").to(torch.bfloat16)
+    for M in (256, 8192):
+        x = xs[:M]
+        codes = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        exps = torch.empty((M, K // 128), dtype=torch.int32, device="cuda")
+        ril.ril_quantize_rows_fp8(x, codes, exps)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ms = time_launch(lambda: ril.ril_proj_w8a8(codes, exps, w8, N, y), 10 if M <= 256 else 3, 1)
+        bits = y[:64].view(torch.int16).cpu().numpy()
+        first = bits if first is None else first
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out.append({"M": M, "us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                    "frac_of_fp8_mfma_peak": round(tf / MFMA_FP8_PEAK_TFLOPS, 4),
+                    "weight_gbps": round(N * K / (ms * 1e-3) / 1e9, 1),
+                    "first_64_rows_bitwise_equal": bool(np.array_equal(bits, first))})
+        del x, codes, exps, y
+    del xs
+    log(f"W8A8 projection sweep (K {K} -> N {N}): {out}")
+    torch.cuda.empty_cache()
+    return {"shape": f"K {K} -> N {N}", "rows": out}
+
+
 def lm_head_rows(M):
     """One untimed and three timed launches of the bf16 lm-head (ril_lm_head_logprobs) on M
     N(0,1) rows of the GQA workload's head: the command the lm-head kernel profiles use."""
@@ -403,6 +441,7 @@ def bench_gqa(args, fp8=False, lm8=False):
         x1["invariant_over_x1_best"] = round(x1["best"]["ms_per_step"] / ms_step, 4)
 
     sweep = None if args.no_lm_sweep else lm_head_sweep(w, lm8, args)
+    proj_sweep = None if args.no_lm_sweep else proj_w8a8_sweep()
     peaks = measured_peaks()
 
     graph = None
@@ -447,7 +486,7 @@ def bench_gqa(args, fp8=False, lm8=False):
                    "parallelism": "none (1 GPU)"},
         "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
         **peaks, "attn_frac_of_read_peak": round(attn_gbps / peaks["read_peak_gbps"], 4),
-        "lm_head_sweep": sweep,
+        "lm_head_sweep": sweep, "proj_w8a8_sweep": proj_sweep,
         "lm_head_gbps": round(lm_gbps, 1), "diff": diff, "timed_step_equals_checked_decode": last_equal,
         "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
         "comparator_x1": x1, "hip_graph": graph, "roofline": roof, "cpu_baseline": cpu,

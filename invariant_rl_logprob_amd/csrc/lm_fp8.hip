@@ -373,8 +373,8 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_codes_kernel(const bf16_
 // 128-wide steps k = 0, 128, 256, ... in order, from zero: the M tile a workgroup owns,
 // the grid and the number of rows never change it.  Workgroup = 4 waves side by side
 // along N, a wave owning MB x NB 16x16 blocks; the operands (two 16-byte loads per lane
-// per block) and the lane's scales of step s+1 are loaded while step s runs.
-template <int MB, int NB>
+// per block) and the lane's scales run S-1 steps ahead in a ring of S register sets.
+template <int MB, int NB, int S>
 __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict__ A8, const int32_t *__restrict__ ea,
                                                        const uint8_t *__restrict__ W8, const int32_t *__restrict__ ew,
                                                        bf16_t *__restrict__ C, int ldc, const bf16_t *__restrict__ R,
@@ -430,14 +430,18 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict
         acc[mb][nb] = mfma_fp8(cat8(o.a[mb][0], o.a[mb][1]), cat8(o.b[nb][0], o.b[nb][1]), acc[mb][nb], o.sa[mb],
                                o.sb[nb]);
   };
-  Ops o0, o1;
-  load(0, o0);
-  for (int s = 0; s < nk; s += 2) {
-    if (s + 1 < nk) load(s + 1, o1);
-    step(o0);
-    if (s + 1 < nk) {
-      if (s + 2 < nk) load(s + 2, o0);
-      step(o1);
+  // a ring of S operand sets: step ks + S - 1 is loaded while step ks runs.  Every load
+  // is unconditional (past the last step it re-reads the last step), which keeps the
+  // compiler's vmcnt waits for the ring exact instead of draining it at each step.
+  Ops ring[S];
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) load(min(j, nk - 1), ring[j]);
+  for (int k0 = 0; k0 < nk; k0 += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int ks = k0 + j;
+      load(min(ks + S - 1, nk - 1), ring[(j + S - 1) % S]);
+      if (ks < nk) step(ring[j]);
     }
   }
 #pragma unroll
@@ -482,12 +486,14 @@ hipError_t launch_quant_weight_fp8(const bf16_t *src, int N, int K, uint8_t *cod
 
 hipError_t launch_gemm_fp8(const GemmFp8Args &a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-#define RIL_G8(MB_, NB_)                                                                                         \
-  hipLaunchKernelGGL((gemm_fp8_kernel<MB_, NB_>), dim3((a.N + 64 * NB_ - 1) / (64 * NB_), (a.M + 16 * MB_ - 1) / (16 * MB_)), \
+#define RIL_G8(MB_, NB_, S_)                                                                                     \
+  hipLaunchKernelGGL((gemm_fp8_kernel<MB_, NB_, S_>), dim3((a.N + 64 * NB_ - 1) / (64 * NB_), (a.M + 16 * MB_ - 1) / (16 * MB_)), \
                      dim3(256), 0, st, a.A8, a.ea, a.W8, a.ew, a.C, a.ldc, a.R, a.ldr, a.M, a.N, a.K)
-  if (a.M <= 16) RIL_G8(1, 1);
-  else if (a.M <= 64) RIL_G8(4, 1);
-  else RIL_G8(4, 2);
+  // few rows: narrow tiles and a deep ring (the weight stream is the cost); many rows:
+  // 64 x 128 tiles
+  if (a.M <= 16) RIL_G8(1, 1, 8);
+  else if (a.M <= 512) RIL_G8(4, 1, 4);
+  else RIL_G8(4, 2, 3);
 #undef RIL_G8
   return hipGetLastError();
 }
