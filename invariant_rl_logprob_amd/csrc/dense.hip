@@ -407,11 +407,18 @@ __device__ __forceinline__ void wait_steps(int ahead) {
   }
 }
 
-__global__ __launch_bounds__(512) void lm_head_wide_kernel(const bf16_t *__restrict__ Z, int ldz,
-                                                           const bf16_t *__restrict__ W, int K, int V,
-                                                           const int32_t *__restrict__ target, int M,
-                                                           float *__restrict__ part, float *__restrict__ tgt_logit,
-                                                           int n_vt, int br) {
+// LM = true: the lm-head (W packed, the K order of lm_rot, the softmax-partials epilogue),
+// n_vt vocabulary tiles.  LM = false: a projection C[M, N] = bf16(Z W^T) [+ residual R]
+// with W row-major [N, ldw] (each 16-column block's operand copied by per-lane addresses
+// like the rows'), K order 0, 32, 64, ... (that of gemm_kernel and gemm_rows_kernel, so
+// the bits are theirs at any M), n_vt = ceil(N / 256) column tiles.
+template <bool LM>
+__global__ __launch_bounds__(512) void wide_kernel(const bf16_t *__restrict__ Z, int ldz,
+                                                   const bf16_t *__restrict__ W, int K, int V,
+                                                   const int32_t *__restrict__ target, int M,
+                                                   float *__restrict__ part, float *__restrict__ tgt_logit,
+                                                   int n_vt, int br, int ldw, bf16_t *__restrict__ C, int ldc,
+                                                   const bf16_t *__restrict__ R, int ldr) {
   constexpr int kStepB = 32 * 1024;  // one K step: row blocks 0..15, then column blocks 0..15
   // the K loop's step buffers; the epilogue's reduction scratch reuses the first 8 KB
   __shared__ __attribute__((aligned(16))) uint8_t buf[kWideBuf][kStepB];
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(512) void lm_head_wide_kernel(const bf16_t *__restr
     const int rt = (blk % nbr) * br + l % br, tile = (blk / nbr) * bv + l / br;
     if (rt >= n_rt || tile >= n_vt) continue;  // the same for the whole workgroup
     const int m0 = rt * kWideRows;
-    const int rot = lm_rot(tile, nk);
+    const int rot = LM ? lm_rot(tile, nk) : 0;
     auto kidx = [&](int s) {
       const int t = s + rot;
       return t >= nk ? t - nk : t;
@@ -439,10 +446,14 @@ __global__ __launch_bounds__(512) void lm_head_wide_kernel(const bf16_t *__restr
     // past M read row M-1; their results are dropped).  Sources: a wave-uniform base plus
     // a 32-bit lane offset in elements (the row tile's rows span less than 2^31 elements)
     const bf16_t *za = Z + (long)m0 * ldz;
-    const bf16_t *wt = W + (long)tile * 16 * nk * 512;
-    uint32_t aoff[2];
+    const bf16_t *wt = LM ? W + (long)tile * 16 * nk * 512 : W + (long)tile * 256 * ldw;
+    uint32_t aoff[2], woffs[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) aoff[j] = (uint32_t)((min(m0 + 16 * (2 * wave + j) + r16, M - 1) - m0) * ldz + grp * 8);
+    for (int j = 0; j < 2; ++j) {
+      aoff[j] = (uint32_t)((min(m0 + 16 * (2 * wave + j) + r16, M - 1) - m0) * ldz + grp * 8);
+      // projection: columns past N read column N-1; their results are dropped
+      woffs[j] = LM ? 0u : (uint32_t)((min(tile * 256 + 16 * (2 * wave + j) + r16, V - 1) - tile * 256) * ldw + grp * 8);
+    }
     const uint32_t woff = (uint32_t)((2 * wave) * nk * 512 + lane * 8);
     auto copy_step = [&](int s) {
       uint8_t *b = &buf[s % kWideBuf][0];
@@ -450,8 +461,8 @@ __global__ __launch_bounds__(512) void lm_head_wide_kernel(const bf16_t *__restr
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         __builtin_amdgcn_global_load_lds(za + (aoff[j] + k * 32), b + (2 * wave + j) * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(wt + (woff + (uint32_t)(j * nk + k) * 512), b + 16384 + (2 * wave + j) * 1024,
-                                         16, 0, 0);
+        const bf16_t *wsrc = LM ? wt + (woff + (uint32_t)(j * nk + k) * 512) : wt + (woffs[j] + (uint32_t)k * 32);
+        __builtin_amdgcn_global_load_lds(wsrc, b + 16384 + (2 * wave + j) * 1024, 16, 0, 0);
       }
     };
     // every wave is done with the previous tile's epilogue (red lives in buf[0])
@@ -506,7 +517,26 @@ __global__ __launch_bounds__(512) void lm_head_wide_kernel(const bf16_t *__restr
     lds_wait<0>();
     // every wave's reads are done (each waited for its own) before red overwrites buf[0]
     asm volatile("s_barrier" ::: "memory");
-    lm_tile_epilogue<8>(acc, red[rg], cg, tile, m0 + rg * 128, M, V, target, part, tgt_logit, n_vt);
+    if constexpr (LM) {
+      lm_tile_epilogue<8>(acc, red[rg], cg, tile, m0 + rg * 128, M, V, target, part, tgt_logit, n_vt);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = tile * 256 + cg * 64 + 16 * nb + r16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = m0 + rg * 128 + 16 * mb + 4 * grp + i;
+            if (row < M && col < V) {
+              float v = bf2f(f2bf(acc[mb][nb][i]));
+              if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+              C[(long)row * ldc + col] = f2bf(v);
+            }
+          }
+        }
+      }
+    }
   }
 }
 
@@ -579,6 +609,15 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
     if (nz > 1) part = a.part;
     else kchunk = a.K;
   }
+  if (!part && a.M > 256) {
+    // many rows: the 256 x 256 LDS-tiled kernel of the lm-head, on the same persistent
+    // grid (blocks of 4 row tiles x 8 column tiles per XCD); the K order is unchanged
+    const int n_rt = (a.M + kWideRows - 1) / kWideRows;
+    const int br = n_rt >= 4 ? 4 : (n_rt >= 2 ? 2 : 1);
+    hipLaunchKernelGGL(wide_kernel<false>, dim3(kWideGrid), dim3(512), 0, st, a.A, a.lda, a.W, a.K, a.N, nullptr,
+                       a.M, nullptr, nullptr, (a.N + 255) / 256, br, a.ldw, a.C, a.ldc, a.R, a.ldr);
+    return hipGetLastError();
+  }
   if (!part && a.M <= 256 && a.K >= 1024) {
     // few rows, long K: the rows' operand shared through LDS, 16 columns per wave
     const int mb = a.M <= 64 ? 1 : (a.M <= 128 ? 2 : 4);
@@ -638,8 +677,8 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st) {
     // workgroups that take blocks of 4 x 8 tiles (fewer row tiles: 2 x 16 or 1 x 32)
     const int n_wrt = (a.M + kWideRows - 1) / kWideRows;
     const int br = n_wrt >= 4 ? 4 : (n_wrt >= 2 ? 2 : 1);
-    hipLaunchKernelGGL(lm_head_wide_kernel, dim3(kWideGrid), dim3(512), 0, st, a.Z, a.ldz, a.W, a.K, a.V, a.target,
-                       a.M, a.part, a.tgt_logit, n_vt, br);
+    hipLaunchKernelGGL(wide_kernel<true>, dim3(kWideGrid), dim3(512), 0, st, a.Z, a.ldz, a.W, a.K, a.V, a.target,
+                       a.M, a.part, a.tgt_logit, n_vt, br, 0, nullptr, 0, nullptr, 0);
   }
   return hipGetLastError();
 }
