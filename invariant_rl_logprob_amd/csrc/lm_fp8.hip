@@ -462,6 +462,141 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict
   }
 }
 
+// W8A8 projections past 256 rows: 256-row x 256-column tiles on 8 waves (wave w: rows
+// 128(w/4) .., columns 64(w%4) .., 8 x 4 blocks), on the persistent XCD-blocked grid of the
+// bf16 wide kernel.  Each 128-wide K step's code operands (16 row blocks and 16 column
+// blocks of 2 KB, each in MFMA lane order as two 1 KB halves) are copied once into LDS
+// by direct-to-LDS loads, one step ahead in a 2-deep ring; the lanes' row and column
+// exponents of the next step are plain loads issued with the copy.  The K order and the
+// MFMA per step are those of gemm_fp8_kernel, so a row's bits are the same at any M.
+constexpr int kF8WideRows = 256, kF8WideGrid = 256;
+
+__global__ __launch_bounds__(512) void gemm_fp8_wide_kernel(const uint8_t *__restrict__ A8,
+                                                            const int32_t *__restrict__ ea,
+                                                            const uint8_t *__restrict__ W8,
+                                                            const int32_t *__restrict__ ew, bf16_t *__restrict__ C,
+                                                            int ldc, const bf16_t *__restrict__ R, int ldr, int M,
+                                                            int N, int K, int br) {
+  constexpr int kStepB = 64 * 1024;  // row blocks 0..15, then column blocks 0..15, 2 KB each
+  __shared__ __attribute__((aligned(16))) uint8_t buf[2][kStepB];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int rg = wave >> 2, cg = wave & 3;
+  const int nk = K >> 7;
+  const int n_rt = (M + kF8WideRows - 1) / kF8WideRows, n_ct = (N + 255) / 256;
+  const int bv = 32 / br;
+  const int nbr = (n_rt + br - 1) / br, n_blocks = nbr * ((n_ct + bv - 1) / bv);
+  const int xcd = blockIdx.x % 8, l = blockIdx.x / 8;
+  const uint32_t lds0 = lds_addr(&buf[0][0]);
+  const uint32_t abase = lds0 + rg * 16384 + lane * 16, bbase = lds0 + 32768 + cg * 8192 + lane * 16;
+  for (int blk = xcd; blk < n_blocks; blk += 8) {
+    const int rt = (blk % nbr) * br + l % br, tile = (blk / nbr) * bv + l / br;
+    if (rt >= n_rt || tile >= n_ct) continue;  // the same for the whole workgroup
+    const int m0 = rt * kF8WideRows, n0 = tile * 256;
+    // this wave copies row blocks 2w, 2w+1 and column blocks 2w, 2w+1 (rows past M read
+    // row M-1, columns past N column N-1; their results are dropped)
+    const uint8_t *asrc[2], *wsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      asrc[j] = A8 + (long)min(m0 + 16 * (2 * wave + j) + r16, M - 1) * K + grp * 32;
+      wsrc[j] = W8 + (long)min(n0 + 16 * (2 * wave + j) + r16, N - 1) * K + grp * 32;
+    }
+    // the lane's row exponent per row block, and the wave's column block exponent
+    const int32_t *sap[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) sap[mb] = ea + (long)min(m0 + rg * 128 + 16 * mb + r16, M - 1) * nk;
+    const int32_t *swp = ew + (long)(min(n0 + cg * 64, N - 1) >> 7) * nk;
+    auto copy_step = [&](int s) {
+      uint8_t *b = &buf[s & 1][0];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          __builtin_amdgcn_global_load_lds(asrc[j] + s * 128 + 16 * h, b + (2 * wave + j) * 2048 + h * 1024, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(wsrc[j] + s * 128 + 16 * h, b + 32768 + (2 * wave + j) * 2048 + h * 1024,
+                                           16, 0, 0);
+        }
+      }
+    };
+    int sa[8], sb, sa_n[8], sb_n = 0;
+    // every wave is done with the previous tile's buffers
+    __syncthreads();
+    copy_step(0);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) sa_n[mb] = sap[mb][0];
+    sb_n = swp[0];
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nk; ++s) {
+      // step s landed (this wave's copies and exponent loads), then the barrier: every
+      // wave's blocks are visible and every wave is done with step s-1's buffer, which
+      // the copy of step s+1 refills
+      wait_vmem<0>();
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) sa[mb] = sa_n[mb];
+      sb = sb_n;
+      asm volatile("s_barrier" ::: "memory");
+      if (s + 1 < nk) {
+        copy_step(s + 1);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) sa_n[mb] = sap[mb][s + 1];
+        sb_n = swp[s + 1];
+      }
+      const uint32_t off = (uint32_t)(s & 1) * kStepB;
+      u32x4 b[4][2];
+      static_for<4>([&](auto nb_) {
+        constexpr int nb = decltype(nb_)::value;
+        b[nb][0] = lds_rd128<nb * 2048>(bbase + off);
+        b[nb][1] = lds_rd128<nb * 2048 + 1024>(bbase + off);
+      });
+      u32x4 a[2][2];
+      a[0][0] = lds_rd128<0>(abase + off);
+      a[0][1] = lds_rd128<1024>(abase + off);
+      static_for<8>([&](auto mb_) {
+        constexpr int mb = decltype(mb_)::value;
+        if constexpr (mb + 1 < 8) {  // the next row block's operand while this one's MFMAs run
+          a[(mb + 1) & 1][0] = lds_rd128<(mb + 1) * 2048>(abase + off);
+          a[(mb + 1) & 1][1] = lds_rd128<(mb + 1) * 2048 + 1024>(abase + off);
+          lds_wait<2>();
+        } else {
+          lds_wait<0>();
+        }
+        if (mb == 0) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            settle(b[nb][0]);
+            settle(b[nb][1]);
+          }
+        }
+        settle(a[mb & 1][0]);
+        settle(a[mb & 1][1]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = mfma_fp8(cat8(a[mb & 1][0], a[mb & 1][1]), cat8(b[nb][0], b[nb][1]), acc[mb][nb], sa[mb], sb);
+      });
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int col = n0 + cg * 64 + 16 * nb + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m0 + rg * 128 + 16 * mb + 4 * grp + i;
+          if (row < M && col < N) {
+            float v = bf2f(f2bf(acc[mb][nb][i]));
+            if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+            C[(long)row * ldc + col] = f2bf(v);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -486,6 +621,15 @@ hipError_t launch_quant_weight_fp8(const bf16_t *src, int N, int K, uint8_t *cod
 
 hipError_t launch_gemm_fp8(const GemmFp8Args &a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  if (a.M > 256) {
+    // many rows: 256 x 256 tiles with the code operands shared through LDS, on the
+    // persistent XCD-blocked grid; the K order is unchanged
+    const int n_rt = (a.M + kF8WideRows - 1) / kF8WideRows;
+    const int br = n_rt >= 4 ? 4 : (n_rt >= 2 ? 2 : 1);
+    hipLaunchKernelGGL(gemm_fp8_wide_kernel, dim3(kF8WideGrid), dim3(512), 0, st, a.A8, a.ea, a.W8, a.ew, a.C, a.ldc,
+                       a.R, a.ldr, a.M, a.N, a.K, br);
+    return hipGetLastError();
+  }
 #define RIL_G8(MB_, NB_, S_)                                                                                     \
   hipLaunchKernelGGL((gemm_fp8_kernel<MB_, NB_, S_>), dim3((a.N + 64 * NB_ - 1) / (64 * NB_), (a.M + 16 * MB_ - 1) / (16 * MB_)), \
                      dim3(256), 0, st, a.A8, a.ea, a.W8, a.ew, a.C, a.ldc, a.R, a.ldr, a.M, a.N, a.K)
