@@ -42,7 +42,6 @@ constexpr int kMlaDqk = 576, kMlaDv = 512;
 constexpr int kMlaPage = kPage * kMlaDqk;     // 9216 elements: one page's latent block
 constexpr int kMlaSlot = kMlaPage + 64;       // LDS slot of a page: +128 B spreads the banks
 constexpr int kMlaThreads = 512;              // 4 pairs of waves x 16 heads (H % 64 == 0)
-constexpr int kTileUnits = 4 * kMlaPage / 8;  // 4608 16-byte units per tile
 
 // Within a page slot, 16-byte unit u sits at LDS unit mla_swz(u) (an involution: it flips
 // bit 3, the token quad of the 8-token half, when bit 4, the parity of the 8-dim group, is

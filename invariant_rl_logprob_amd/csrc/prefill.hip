@@ -277,8 +277,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
   }
 }
 
-constexpr int kPrefillNcb = 1, kPrefillWaves = 8;
-
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st) {
   constexpr int NW = 8, NBUF = 4;
   const int QT = NW * (16 / a.G);
