@@ -371,92 +371,89 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_codes_kernel(const bf16_
 // exponents ea [M, K/128] and the weight's codes W8 [N, K] and exponents ew
 // [ceil(N/128), K/128].  Every output element is one chain of scaled FP8 MFMAs over K in
 // 128-wide steps k = 0, 128, 256, ... in order, from zero: the M tile a workgroup owns,
-// the grid and the number of rows never change it.  Workgroup = 4 waves side by side
-// along N, a wave owning MB x NB 16x16 blocks; the operands (two 16-byte loads per lane
-// per block) and the lane's scales run S-1 steps ahead in a ring of S register sets.
-template <int MB, int NB, int S>
+// the grid and the number of rows never change it.
+// Up to 256 rows: a workgroup of 4 waves covers 16*MB rows x 64 columns, wave w the 16
+// columns n0 + 16w ..  The rows' codes and exponents of a chunk of kF8RowChunk steps are
+// staged through LDS once per workgroup (double-buffered, wave w loading step w of the
+// chunk); each wave streams its 16 weight rows' codes and their block exponent through a
+// register ring S steps deep (every load unconditional: past the last step it re-reads it).
+constexpr int kF8RowChunk = 4;
+
+template <int MB, int S>
 __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict__ A8, const int32_t *__restrict__ ea,
                                                        const uint8_t *__restrict__ W8, const int32_t *__restrict__ ew,
                                                        bf16_t *__restrict__ C, int ldc, const bf16_t *__restrict__ R,
                                                        int ldr, int M, int N, int K) {
+  static_assert(S % kF8RowChunk == 0, "a chunk starts at a ring slot 0 .. S-1 boundary");
+  __shared__ u32x4 lds_a[2][kF8RowChunk * MB * 2 * 64];
+  __shared__ int32_t lds_e[2][kF8RowChunk * 16 * MB];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
   const int m0 = blockIdx.y * 16 * MB;
-  const int n0 = (blockIdx.x * 4 + wave) * 16 * NB;
-  if (n0 >= N) return;
+  const int n0 = blockIdx.x * 64 + wave * 16;
   const int nk = K >> 7;
-  const uint8_t *ap[MB], *wp[NB];
-  const int32_t *sap[MB], *swp[NB];
+  const int col = min(n0 + r16, N - 1);  // columns past N are computed and dropped
+  const uint8_t *wp = W8 + (long)col * K + grp * 32;
+  const int32_t *swp = ew + (long)(col >> 7) * nk;
+  const uint8_t *arow[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int row = min(m0 + 16 * mb + r16, M - 1);  // rows past M are computed and dropped
-    ap[mb] = A8 + (long)row * K + grp * 32;
-    sap[mb] = ea + (long)row * nk;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = min(n0 + 16 * nb + r16, N - 1);
-    wp[nb] = W8 + (long)col * K + grp * 32;
-    swp[nb] = ew + (long)(col >> 7) * nk;
-  }
-  struct Ops {
-    u32x4 a[MB][2], b[NB][2];
-    int sa[MB], sb[NB];
+  for (int mb = 0; mb < MB; ++mb) arow[mb] = A8 + (long)min(m0 + 16 * mb + r16, M - 1) * K + grp * 32;
+  const int32_t *erow = ea + (long)min(m0 + min(lane, 16 * MB - 1), M - 1) * nk;
+  struct WOp {
+    u32x4 lo, hi;
+    int e;
   };
-  auto load = [&](int s, Ops &o) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      o.a[mb][0] = ld16(ap[mb] + s * 128);
-      o.a[mb][1] = ld16(ap[mb] + s * 128 + 16);
-      o.sa[mb] = sap[mb][s];
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      o.b[nb][0] = ld16(wp[nb] + s * 128);
-      o.b[nb][1] = ld16(wp[nb] + s * 128 + 16);
-      o.sb[nb] = swp[nb][s];
-    }
+  auto load_w = [&](int s, WOp &o) {
+    o.lo = ld16(wp + s * 128);
+    o.hi = ld16(wp + s * 128 + 16);
+    o.e = swp[s];
   };
-  f32x4 acc[MB][NB];
+  WOp ring[S];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int j = 0; j < S - 1; ++j) load_w(min(j, nk - 1), ring[j]);
+  f32x4 acc[MB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto step = [&](const Ops &o) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = mfma_fp8(cat8(o.a[mb][0], o.a[mb][1]), cat8(o.b[nb][0], o.b[nb][1]), acc[mb][nb], o.sa[mb],
-                               o.sb[nb]);
-  };
-  // a ring of S operand sets: step ks + S - 1 is loaded while step ks runs.  Every load
-  // is unconditional (past the last step it re-reads the last step), which keeps the
-  // compiler's vmcnt waits for the ring exact instead of draining it at each step.
-  Ops ring[S];
-#pragma unroll
-  for (int j = 0; j < S - 1; ++j) load(min(j, nk - 1), ring[j]);
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < nk; k0 += S) {
 #pragma unroll
     for (int j = 0; j < S; ++j) {
       const int ks = k0 + j;
-      load(min(ks + S - 1, nk - 1), ring[(j + S - 1) % S]);
-      if (ks < nk) step(ring[j]);
+      if (j % kF8RowChunk == 0 && ks < nk) {
+        __syncthreads();  // every wave is done with the buffer about to be refilled
+        const int buf = (ks / kF8RowChunk) & 1, st = ks + wave;
+        if (st < nk) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            lds_a[buf][((wave * MB + mb) * 2 + 0) * 64 + lane] = ld16(arow[mb] + st * 128);
+            lds_a[buf][((wave * MB + mb) * 2 + 1) * 64 + lane] = ld16(arow[mb] + st * 128 + 16);
+          }
+          if (lane < 16 * MB) lds_e[buf][wave * 16 * MB + lane] = erow[st];
+        }
+        __syncthreads();
+      }
+      load_w(min(ks + S - 1, nk - 1), ring[(j + S - 1) % S]);
+      if (ks < nk) {
+        const int buf = (ks / kF8RowChunk) & 1, st = ks % kF8RowChunk;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4 lo = lds_a[buf][((st * MB + mb) * 2 + 0) * 64 + lane];
+          const u32x4 hi = lds_a[buf][((st * MB + mb) * 2 + 1) * 64 + lane];
+          const int sa = lds_e[buf][st * 16 * MB + 16 * mb + r16];
+          acc[mb] = mfma_fp8(cat8(lo, hi), cat8(ring[j].lo, ring[j].hi), acc[mb], sa, ring[j].e);
+        }
+      }
     }
   }
+  const int c = n0 + r16;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = n0 + 16 * nb + r16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + 16 * mb + 4 * grp + i;
-        if (row < M && col < N) {
-          float v = bf2f(f2bf(acc[mb][nb][i]));
-          if (R) v = bf2f(R[(long)row * ldr + col]) + v;
-          C[(long)row * ldc + col] = f2bf(v);
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + 16 * mb + 4 * grp + i;
+      if (row < M && c < N) {
+        float v = bf2f(f2bf(acc[mb][i]));
+        if (R) v = bf2f(R[(long)row * ldr + c]) + v;
+        C[(long)row * ldc + c] = f2bf(v);
       }
     }
   }
@@ -630,14 +627,11 @@ hipError_t launch_gemm_fp8(const GemmFp8Args &a, hipStream_t st) {
                        a.R, a.ldr, a.M, a.N, a.K, br);
     return hipGetLastError();
   }
-#define RIL_G8(MB_, NB_, S_)                                                                                     \
-  hipLaunchKernelGGL((gemm_fp8_kernel<MB_, NB_, S_>), dim3((a.N + 64 * NB_ - 1) / (64 * NB_), (a.M + 16 * MB_ - 1) / (16 * MB_)), \
-                     dim3(256), 0, st, a.A8, a.ea, a.W8, a.ew, a.C, a.ldc, a.R, a.ldr, a.M, a.N, a.K)
-  // few rows: narrow tiles and a deep ring (the weight stream is the cost); many rows:
-  // 64 x 128 tiles
-  if (a.M <= 16) RIL_G8(1, 1, 8);
-  else if (a.M <= 512) RIL_G8(4, 1, 4);
-  else RIL_G8(4, 2, 3);
+#define RIL_G8(MB_, S_)                                                                                     \
+  hipLaunchKernelGGL((gemm_fp8_kernel<MB_, S_>), dim3((a.N + 63) / 64, (a.M + 16 * MB_ - 1) / (16 * MB_)), dim3(256), \
+                     0, st, a.A8, a.ea, a.W8, a.ew, a.C, a.ldc, a.R, a.ldr, a.M, a.N, a.K)
+  if (a.M <= 16) RIL_G8(1, 8);
+  else RIL_G8(4, 8);
 #undef RIL_G8
   return hipGetLastError();
 }
