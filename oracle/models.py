@@ -189,13 +189,14 @@ def gqa_row_logprob(q, K, V, scale, w_lm, target, eps=1e-6, w_o=None, gain=None,
     return head_logprob(gqa_row_attention(q, K, V, scale), w_lm, target, eps, w_o, gain, lm_w8a8)
 
 
-def head_logprob(o, w_lm, target, eps=1e-6, w_o=None, gain=None, lm_w8a8=False) -> float:
+def head_logprob(o, w_lm, target, eps=1e-6, w_o=None, gain=None, lm_w8a8=False, proj_w8a8=False) -> float:
     """The head after attention: bf16 attention output, flattened head-major, an
-    optional projection (bf16 output), bf16(RMSNorm), then the lm-head logprob, with
-    bf16 weights or (lm_w8a8) the block-FP8 W8A8 product of fp8block.py."""
+    optional projection (bf16 output; proj_w8a8: the block-FP8 W8A8 product of
+    ``_matmul``), bf16(RMSNorm), then the lm-head logprob, with bf16 weights or
+    (lm_w8a8) the block-FP8 W8A8 product of fp8block.py."""
     o = bf16(np.asarray(o, dtype=np.float64)).reshape(-1)
     if w_o is not None:
-        o = bf16(widen(w_o) @ o)
+        o = bf16(_matmul(o, widen(w_o), True)) if proj_w8a8 else bf16(widen(w_o) @ o)
     z = bf16(rmsnorm(o, gain, eps))
     if lm_w8a8:
         return lm_head_logprob_w8a8(z, widen(w_lm), target)

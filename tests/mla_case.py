@@ -15,7 +15,8 @@ from invariant_rl_logprob_amd.session import Session
 
 class MLACase:
     def __init__(self, w: wl.MLADecode, rows: Sequence[int], *, ctx: Sequence[int] = None, device="cuda",
-                 shuffle_seed=4321, copies=2, split_tokens=2048, max_rows=None, max_tokens=None, head=None):
+                 shuffle_seed=4321, copies=2, split_tokens=2048, max_rows=None, max_tokens=None, head=None,
+                 proj_dtype=0):
         self.w = w
         self.rows = list(rows)
         self.data: Dict[int, dict] = {}
@@ -31,7 +32,8 @@ class MLACase:
                             max_tokens=max_tokens or len(self.rows) * w.recompute_tokens, max_ctx=max_ctx,
                             pool_pages=pages, softmax_scale=self.scale, rms_eps=w.rms_eps,
                             shuffle_seed=shuffle_seed, split_tokens=split_tokens, attn_kind=RIL_ATTN_MLA,
-                            device=device)
+                            proj_dtype=proj_dtype, device=device)
+        self.proj_w8a8 = proj_dtype == 1
 
     def ctx(self, r):
         return self.data[r]["ctx"]
@@ -92,5 +94,6 @@ class MLACase:
         lp = None
         if with_logprob:
             lp = oracle.head_logprob(o, self.head["w_lm"].float().cpu().numpy(), int(d["target"][R - back]),
-                                     self.w.rms_eps, w_o=self.head["w_o"].float().cpu().numpy())
+                                     self.w.rms_eps, w_o=self.head["w_o"].float().cpu().numpy(),
+                                     proj_w8a8=self.proj_w8a8)
         return lp, o

@@ -165,3 +165,22 @@ def test_w8a8_proj_differs_from_bf16(w8_model):
     got16 = _prefill(b, "d16", [0], toks)[0].cpu().numpy()
     assert not np.array_equal(got8, got16)
     assert np.max(np.abs(got8[:-1] - got16[:-1])) < 0.5
+
+
+def test_w8a8_o_projection_with_mla():
+    """Absorbed MLA (64 heads x latent 512: the o-projection's K is 32768) with a W8A8
+    o-projection: 16 decode steps equal the prefill recompute bitwise, and the last
+    position's logprob is within the end-to-end bar of the oracle with the same
+    projection."""
+    from mla_case import MLACase
+    W = wl.scaled(wl.MLA_DECODE_B128, rows=4, n_heads=64, vocab=1000, d_head=256, recompute_tokens=16)
+    c = MLACase(W, [0, 1, 2, 3], ctx=[70, 700, 2100, 33], proj_dtype=1)
+    rows, n = [0, 1, 2, 3], 16
+    c.write_history("d", rows, n)
+    dec = torch.stack([c.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
+    c.write_history("p", rows, n)
+    pre = c.prefill_last("p", rows, n)
+    assert np.array_equal(_bits(dec), _bits(pre))
+    errs = [abs(float(dec[i, -1]) - c.oracle_row(r)[0]) for i, r in enumerate(rows)]
+    print("MLA with a W8A8 o-projection, |gpu - oracle|:", errs)
+    assert max(errs) <= TOL_E2E
