@@ -28,6 +28,7 @@ from .numerics import (  # noqa: F401
     log_softmax_at,
     lm_head_logprob,
     attention_row,
+    projection,
     silu,
     swiglu_rounded_once,
 )

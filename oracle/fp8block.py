@@ -17,7 +17,11 @@ post names the scheme, not its constants; the readings here:
   * codes: e4m3(x * 2^-e), nearest even (oracle/fp8.py), of the bf16 values;
   * product: out[m, n] = sum over K of dequant(A)[m, k] * dequant(W)[n, k].  The GPU sums
     each 128-wide K block in one FP8 MFMA and adds the blocks in a fixed order per column;
-    the oracle's value is the exact sum (float64 of exactly representable products).
+    the oracle forms every scaled code product exactly in float64 (two 4-bit significands
+    and a power of two) and adds them in float64.  That sum is exact while all partial
+    sums fit 53 significant bits (the products' exponents spanning at most about 45
+    binades, as for the operands here); beyond that it carries float64's rounding, some
+    2^-53 relative per addition, far below the fp32 accumulation it is compared with.
 
 Pinned by (tests/test_oracle_pins.py): the exponent rule against brute force (the clamp
 and the NaN scale included), every code
@@ -96,7 +100,8 @@ def dequant_weight_blocks(codes, e):
 
 
 def w8a8_matmul(a, w) -> np.ndarray:
-    """Exact product of the block-FP8 quantized a [M, K] and w [N, K] (float64 [M, N])."""
+    """Product of the block-FP8 quantized a [M, K] and w [N, K] (float64 [M, N]): exact
+    scaled code products summed in float64, exact while the partial sums fit 53 bits."""
     ca, ea = quantize_rows(a)
     cw, ew = quantize_weight_blocks(w)
     return dequant_rows(ca, ea) @ dequant_weight_blocks(cw, ew).T

@@ -106,6 +106,25 @@ def attention_row(q, K, V, scale: float) -> np.ndarray:
     return p @ V
 
 
+def projection(a, W, residual=None) -> np.ndarray:
+    """A projection GEMM with its storage points: bf16(a W^T), or with a residual
+    bf16(residual + bf16(a W^T)).
+
+    ``a`` is [M, K] (or one row [K]) and ``W`` is [N, K] in the nn.Linear layout, both
+    holding bf16 values.  Every product of two bf16 values is exact in float64 and the
+    float64 sum over K is exact for integer-valued operands (and carries at most K
+    float64 roundings otherwise, far below one bf16 step), so the value rounded is the
+    dense product (Bitwise-consistent RL post, section 4.1: one accumulation order for
+    every M; the order does not change this exact value).  Pinned by: integer operands
+    against the int64 product; the residual form against an explicit torch float64
+    composition.
+    """
+    y = bf16(np.asarray(a, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T)
+    if residual is not None:
+        y = bf16(np.asarray(residual, dtype=np.float64) + y)
+    return y
+
+
 def silu(x) -> np.ndarray:
     """SiLU (swish): x * sigmoid(x) = x / (1 + exp(-x)), float64.
 

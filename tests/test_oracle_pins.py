@@ -234,6 +234,75 @@ def test_gqa_row_with_output_projection_zero():
     assert abs(lp - _golden("closed_forms.json")["uniform_logprob"]["vocab_2048"]) < 1e-12
 
 
+def check_head_with_projection(fn):
+    """fn(o, w_lm, target, eps, w_o) must equal the head composed from torch float64
+    operations with the contract's bf16 points: bf16(o) flattened, bf16(W_o o),
+    bf16(rms_norm(.)), log_softmax(W_lm z)[target]."""
+    Hq, D, dh, V = 4, 16, 48, 333
+    o = RNG.standard_normal((Hq, D))
+    w_o = oracle.bf16(RNG.standard_normal((dh, Hq * D)) * 0.1)
+    w_lm = oracle.bf16(RNG.standard_normal((V, dh)) * 0.3)
+    ob = torch.from_numpy(oracle.bf16(o).reshape(-1))
+    y = torch.from_numpy(oracle.bf16((torch.from_numpy(w_o) @ ob).numpy()))
+    z = torch.from_numpy(oracle.bf16(F.rms_norm(y, (dh,), eps=1e-6).numpy()))
+    for t in (0, 5, 332):
+        want = float(torch.log_softmax(torch.from_numpy(w_lm) @ z, 0)[t])
+        if abs(fn(o, w_lm, t, 1e-6, w_o) - want) > 1e-12:
+            return False
+    return True
+
+
+def test_head_with_output_projection_matches_torch_composition():
+    assert check_head_with_projection(lambda o, w, t, eps, w_o: oracle.head_logprob(o, w, t, eps, w_o=w_o))
+
+
+def test_planted_projection_output_unrounded_is_caught():
+    def bad(o, w_lm, t, eps, w_o):
+        ob = oracle.bf16(np.asarray(o)).reshape(-1)
+        z = oracle.bf16(on.rmsnorm(oracle.widen(w_o) @ ob, None, eps))  # bf16() after W_o dropped
+        return on.lm_head_logprob(z, w_lm, t)
+    assert not check_head_with_projection(bad)
+
+
+def check_projection(fn):
+    """fn(a, W, residual) on integer-valued bf16 operands must equal the int64 product
+    rounded by torch's fp32 -> bf16 conversion (every value involved is an integer below
+    2^24, so fp32 holds it exactly), with the residual added after that rounding and the
+    sum rounded again; checked for K spanning several tile widths."""
+    for M, N, K in ((3, 5, 32), (17, 40, 96), (9, 7, 1024)):
+        # integers up to 40 in magnitude are bf16 values; products up to 1600 and sums up
+        # to 1600 K < 2^24 stay exact in fp32, and most sums need the bf16 rounding
+        a = RNG.integers(-40, 41, (M, K))
+        W = RNG.integers(-40, 41, (N, K))
+        R = RNG.integers(-3000, 3001, (M, N)) // 16 * 16  # bf16 values (8 significant bits)
+        p = a.astype(np.int64) @ W.astype(np.int64).T
+        pb = torch.from_numpy(p.astype(np.float32)).to(torch.bfloat16).to(torch.float32)
+        want = pb.to(torch.float64).numpy()
+        want_r = (torch.from_numpy(R.astype(np.float32)) + pb).to(torch.bfloat16).to(torch.float64).numpy()
+        got, got_r = fn(a.astype(np.float64), W.astype(np.float64), None), fn(a, W, R)
+        if not (np.array_equal(got, want) and np.array_equal(got_r, want_r)):
+            return False
+    return True
+
+
+def test_projection_integer_operands_exact():
+    assert check_projection(on.projection)
+
+
+def test_planted_projection_rounded_once_with_residual_is_caught():
+    def bad(a, W, R):
+        y = np.asarray(a, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+        return oracle.bf16(y if R is None else y + R)  # the inner bf16 before the residual dropped
+    assert not check_projection(bad)
+
+
+def test_planted_projection_transposed_weight_is_caught():
+    def bad(a, W, R):
+        W = np.asarray(W, dtype=np.float64)
+        return on.projection(a, W.reshape(W.shape[1], W.shape[0]).T, R)  # a wrong index map
+    assert not check_projection(bad)
+
+
 def test_mla_matches_sdpa():
     H, dqk, dv, n = 3, 576, 512, 19
     q = oracle.bf16(RNG.standard_normal((H, dqk)))
