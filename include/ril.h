@@ -267,13 +267,32 @@ ril_status ril_quantize_weight_fp8(const void *src, int32_t N, int32_t K, void *
 
 /* The W8A8 projection GEMM alone, for callers that run a projection outside a model (a
  * trainer's recompute, tests): enqueue out[rows, N] = bf16(A W^T) with A given as codes
- * [rows, K] and exps [rows, K/128] (ril_quantize_rows_fp8) and W as written by
- * ril_quantize_weight_fp8 (N rows, the same K).  out is bf16 device memory, row stride
- * ldo >= N elements.  Each element's K order is k = 0, 128, ... for every rows.  Pointers
- * 16-byte (exps: 4-byte; out: 2-byte) aligned.  Returns RIL_EINVAL on bad sizes or
- * pointers, RIL_EHIP on a launch error; rows = 0 enqueues nothing. */
-ril_status ril_proj_w8a8(const void *codes, const void *exps, int32_t rows, int32_t K, const void *w, int32_t N,
-                         void *out, int32_t ldo, void *stream);
+ * [rows, K] (row-major, row stride K) and exps [rows, K/128] (ril_quantize_rows_fp8) and W
+ * as written by ril_quantize_weight_fp8 (N rows, the same K) in a buffer of w_bytes bytes.
+ * out is bf16 device memory, row stride ldo >= N elements.  Each element's K order is
+ * k = 0, 128, ... for every rows.  Pointers 16-byte (exps: 4-byte; out: 2-byte) aligned.
+ * Returns RIL_EINVAL on bad sizes or pointers or w_bytes < ril_proj_fp8_bytes(N, K),
+ * RIL_EHIP on a launch error; rows = 0 enqueues nothing. */
+ril_status ril_proj_w8a8(const void *codes, const void *exps, int32_t rows, int32_t K, const void *w,
+                         size_t w_bytes, int32_t N, void *out, int32_t ldo, void *stream);
+
+/* S4 alone: the bf16 projection GEMM the model runs for its QKV, O and MLP projections,
+ * for callers that run a projection outside a model (a trainer's recompute, tests of the
+ * GEMM at its own boundary).  Enqueue, on `stream`,
+ *   out[r, n] = bf16(sum_k A[r, k] W[n, k])                      (residual == NULL)
+ *   out[r, n] = bf16(residual[r, n] + bf16(sum_k A[r, k] W[n, k]))
+ * with fp32 accumulation of bf16 x bf16 products in the order k = 0, 32, 64, ..., one
+ * 16x16x32 MFMA step at a time, never split: the Bitwise-consistent RL post, section 4.1
+ * (one accumulation order for every M, no split-K).  The kernel and tile shape follow
+ * `rows` (and K), the bits of a row never do: the same row gives the same output at any
+ * rows.  A is bf16 [rows, K] at row stride lda, W bf16 [N, K] (nn.Linear layout) at row
+ * stride ldw, residual and out bf16 [rows, N] at row strides ldr and ldo; all device
+ * memory.  K is a positive multiple of 32; lda, ldw >= K and multiples of 8; ldo (ldr)
+ * >= N.  A and W 16-byte aligned, out and residual 2-byte aligned; out must not overlap
+ * the inputs except that residual may equal out with ldr == ldo.  Returns RIL_EINVAL on
+ * bad sizes or pointers, RIL_EHIP on a launch error; rows = 0 enqueues nothing. */
+ril_status ril_proj_bf16(const void *A, int32_t rows, int32_t K, int32_t lda, const void *W, int32_t N,
+                         int32_t ldw, const void *residual, int32_t ldr, void *out, int32_t ldo, void *stream);
 
 /* S1: page assignment.  Wrap a caller-owned device pool of `pool_bytes`
  * bytes (16-byte aligned) as floor(pool_bytes / page_bytes) pages and build a

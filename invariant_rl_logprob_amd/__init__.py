@@ -90,7 +90,10 @@ _hbm_read_probe = _sig("ril_hbm_read_probe", _c_int, [_vp, ctypes.c_size_t, _vp,
 _quantize_rows_fp8 = _sig("ril_quantize_rows_fp8", _c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp])
 _proj_fp8_bytes = _sig("ril_proj_fp8_bytes", ctypes.c_size_t, [_c_int, _c_int])
 _quantize_weight_fp8 = _sig("ril_quantize_weight_fp8", _c_int, [_vp, _c_int, _c_int, _vp, ctypes.c_size_t, _vp])
-_proj_w8a8 = _sig("ril_proj_w8a8", _c_int, [_vp, _vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp])
+_proj_w8a8 = _sig("ril_proj_w8a8", _c_int,
+                  [_vp, _vp, _c_int, _c_int, _vp, ctypes.c_size_t, _c_int, _vp, _c_int, _vp])
+_proj_bf16 = _sig("ril_proj_bf16", _c_int,
+                  [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp])
 _ws_attn_offset = _sig("ril_ws_attn_offset", ctypes.c_size_t, [_vp])
 _kv_alloc = _sig("ril_kv_alloc", _c_int, [_vp, _vp, ctypes.c_size_t, ctypes.c_uint64, ctypes.POINTER(_vp)])
 _kv_assign = _sig("ril_kv_assign", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)])
@@ -115,7 +118,7 @@ _trace_read = _sig("ril_trace_read", _c_int, [_c_int, ctypes.POINTER(ctypes.c_do
 
 EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril_kv_page_bytes",
             "ril_lm_head_packed_bytes", "ril_pack_lm_head", "ril_lm_head_fp8_packed_bytes", "ril_pack_lm_head_fp8",
-            "ril_quantize_rows_fp8", "ril_proj_fp8_bytes", "ril_quantize_weight_fp8", "ril_proj_w8a8",
+            "ril_quantize_rows_fp8", "ril_proj_fp8_bytes", "ril_quantize_weight_fp8", "ril_proj_w8a8", "ril_proj_bf16",
             "ril_lm_head_logprobs", "ril_hbm_read_probe_words", "ril_hbm_read_probe",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
@@ -226,15 +229,46 @@ def ril_quantize_weight_fp8(w, dst, stream=None) -> None:
            "ril_quantize_weight_fp8")
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
 def ril_proj_w8a8(codes, exps, w8, N: int, out, stream=None) -> None:
-    """out[rows, N] = bf16(A W^T) for rows given as block-FP8 codes (uint8 [rows, K]) and
-    exps (int32 [rows, K/128]) and W as written by ril_quantize_weight_fp8 (N rows);
-    out is a bf16 device tensor [rows, >= N] (row stride out.stride(0))."""
+    """out[rows, N] = bf16(A W^T) for rows given as block-FP8 codes (uint8 [rows, K],
+    contiguous) and exps (int32 [rows, K/128], contiguous) and W as written by
+    ril_quantize_weight_fp8 (N rows, a uint8 device tensor); out is a bf16 device tensor
+    [rows, >= N] with unit column stride (row stride out.stride(0))."""
+    import torch
     rows, K = codes.shape
-    if exps.numel() < rows * (K // 128) or out.shape[0] < rows or out.shape[1] < N:
-        raise ValueError("ril_proj_w8a8: exps or out too small")
-    _check(_proj_w8a8(_ptr(codes), _ptr(exps), rows, K, _ptr(w8), N, _ptr(out), out.stride(0), _stream(stream)),
-           "ril_proj_w8a8")
+    _need(codes.dtype == torch.uint8 and codes.is_contiguous(), "ril_proj_w8a8: codes must be contiguous uint8")
+    _need(exps.dtype == torch.int32 and exps.is_contiguous() and exps.numel() >= rows * (K // 128),
+          "ril_proj_w8a8: exps must be contiguous int32 [rows, K/128]")
+    _need(w8.dtype == torch.uint8 and w8.is_contiguous(), "ril_proj_w8a8: w8 must be a contiguous uint8 buffer")
+    _need(out.dtype == torch.bfloat16 and out.dim() == 2 and out.stride(1) == 1 and out.shape[0] >= rows
+          and out.shape[1] >= N, "ril_proj_w8a8: out must be bf16 [rows, >= N] with unit column stride")
+    _check(_proj_w8a8(_ptr(codes), _ptr(exps), rows, K, _ptr(w8), w8.numel(), N, _ptr(out), out.stride(0),
+                      _stream(stream)), "ril_proj_w8a8")
+
+
+def ril_proj_bf16(a, w, out, residual=None, stream=None) -> None:
+    """out[rows, N] = bf16(a w^T), or bf16(residual + bf16(a w^T)): the model's bf16
+    projection GEMM alone.  a is bf16 [rows, K] and w bf16 [N, K] (unit column stride, row
+    strides a.stride(0), w.stride(0)); out and residual bf16 [rows, >= N] with unit column
+    stride; all device tensors."""
+    import torch
+    rows, K = a.shape
+    N = w.shape[0]
+    for t, nm in ((a, "a"), (w, "w"), (out, "out")) + (((residual, "residual"),) if residual is not None else ()):
+        _need(t.dtype == torch.bfloat16 and t.dim() == 2 and t.stride(1) == 1,
+              f"ril_proj_bf16: {nm} must be a 2-d bf16 tensor with unit column stride")
+    _need(w.shape[1] == K, "ril_proj_bf16: w must be [N, K]")
+    _need(out.shape[0] >= rows and out.shape[1] >= N, "ril_proj_bf16: out must be [rows, >= N]")
+    _need(residual is None or (residual.shape[0] >= rows and residual.shape[1] >= N),
+          "ril_proj_bf16: residual must be [rows, >= N]")
+    _check(_proj_bf16(_ptr(a), rows, K, a.stride(0), _ptr(w), N, w.stride(0), _ptr(residual),
+                      0 if residual is None else residual.stride(0), _ptr(out), out.stride(0), _stream(stream)),
+           "ril_proj_bf16")
 
 
 def ril_lm_head_logprobs(model: int, z, targets, logprob_out, ws, stream=None) -> None:

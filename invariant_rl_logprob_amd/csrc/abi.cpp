@@ -357,9 +357,12 @@ extern "C" ril_status ril_quantize_weight_fp8(const void *src, int32_t N, int32_
 }
 
 extern "C" ril_status ril_proj_w8a8(const void *codes, const void *exps, int32_t rows, int32_t K, const void *w,
-                                    int32_t N, void *out, int32_t ldo, void *stream) {
+                                    size_t w_bytes, int32_t N, void *out, int32_t ldo, void *stream) {
   if (rows < 0 || N < 1 || K < 128 || K % 128 || ldo < N)
     return fail(RIL_EINVAL, "proj_w8a8: rows %d, K %d, N %d, ldo %d", rows, K, N, ldo);
+  const size_t need = (size_t)ril::proj_fp8_bytes(N, K);
+  if (w_bytes < need) return fail(RIL_EINVAL, "proj_w8a8: weight %zu bytes, %zu needed for N %d, K %d", w_bytes,
+                                  need, N, K);
   if (rows == 0) return RIL_OK;
   if (!codes || !exps || !w || !out || !aligned16(codes) || !aligned4(exps) || !aligned16(w) ||
       ((uintptr_t)out & 1))
@@ -370,6 +373,26 @@ extern "C" ril_status ril_proj_w8a8(const void *codes, const void *exps, int32_t
                 rows, N, K};
   const hipError_t e = ril::launch_gemm_fp8(f, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RIL_EHIP, "proj_w8a8: %s", hipGetErrorString(e));
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_proj_bf16(const void *A, int32_t rows, int32_t K, int32_t lda, const void *W, int32_t N,
+                                    int32_t ldw, const void *residual, int32_t ldr, void *out, int32_t ldo,
+                                    void *stream) {
+  if (rows < 0 || N < 1 || K < 32 || K % 32 || lda < K || lda % 8 || ldw < K || ldw % 8 || ldo < N ||
+      (residual && ldr < N))
+    return fail(RIL_EINVAL, "proj_bf16: rows %d, K %d, N %d, lda %d, ldw %d, ldr %d, ldo %d", rows, K, N, lda, ldw,
+                ldr, ldo);
+  // the kernels form 32-bit element offsets inside a 256-row (256-column) tile
+  if ((long)lda * 256 + K >= (1L << 31) || (long)ldw * 256 + K >= (1L << 31))
+    return fail(RIL_EINVAL, "proj_bf16: row strides %d / %d too large", lda, ldw);
+  if (rows == 0) return RIL_OK;
+  if (!A || !W || !out || !aligned16(A) || !aligned16(W) || ((uintptr_t)out & 1) || ((uintptr_t)residual & 1))
+    return fail(RIL_EINVAL, "proj_bf16: null or misaligned pointer");
+  GemmArgs g{(const bf16_t *)A, lda, (const bf16_t *)W, ldw, (bf16_t *)out, ldo, (const bf16_t *)residual, ldr,
+             rows, N, K};
+  const hipError_t e = ril::launch_gemm(g, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RIL_EHIP, "proj_bf16: %s", hipGetErrorString(e));
   return RIL_OK;
 }
 

@@ -134,7 +134,7 @@ def test_w8a8_projection_descriptor_sizes_and_bad_arguments():
     lib.ril_quantize_weight_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]
     lib.ril_proj_w8a8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+                                  ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     need = ril.ril_proj_fp8_bytes(300, 256)
     # every case fails validation before anything is enqueued
     assert lib.ril_quantize_weight_fp8(0x10000, 300, 200, 0x900000, need, None) == ril.RIL_EINVAL     # K % 128
@@ -142,12 +142,43 @@ def test_w8a8_projection_descriptor_sizes_and_bad_arguments():
     assert lib.ril_quantize_weight_fp8(0x10008, 300, 256, 0x900000, need, None) == ril.RIL_EINVAL     # misaligned
     assert lib.ril_quantize_weight_fp8(0x10000, 300, 256, 0x10000, need, None) == ril.RIL_EINVAL      # overlap
     assert lib.ril_quantize_weight_fp8(None, 300, 256, 0x900000, need, None) == ril.RIL_EINVAL
-    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 200, 0x30000, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # K % 128
-    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, 0x30000, 64, 0x40000, 32, None) == ril.RIL_EINVAL  # ldo < N
-    assert lib.ril_proj_w8a8(0x10008, 0x20000, 4, 256, 0x30000, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # codes align
-    assert lib.ril_proj_w8a8(0x10000, 0x20002, 4, 256, 0x30000, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # exps align
-    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, None, 64, 0x40000, 64, None) == ril.RIL_EINVAL
-    assert lib.ril_proj_w8a8(0x10000, 0x20000, 0, 256, 0x30000, 64, 0x40000, 64, None) == ril.RIL_OK      # nothing
+    wn = ril.ril_proj_fp8_bytes(64, 256)
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 200, 0x30000, wn, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # K % 128
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, 0x30000, wn, 64, 0x40000, 32, None) == ril.RIL_EINVAL  # ldo < N
+    assert lib.ril_proj_w8a8(0x10008, 0x20000, 4, 256, 0x30000, wn, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # align
+    assert lib.ril_proj_w8a8(0x10000, 0x20002, 4, 256, 0x30000, wn, 64, 0x40000, 64, None) == ril.RIL_EINVAL  # exps
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, None, wn, 64, 0x40000, 64, None) == ril.RIL_EINVAL
+    # a weight buffer too short for N x K (a wrong N or K would read past it)
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, 0x30000, wn - 1, 64, 0x40000, 64, None) == ril.RIL_EINVAL
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 4, 256, 0x30000, wn, 65, 0x40000, 65, None) == ril.RIL_EINVAL
+    assert lib.ril_proj_w8a8(0x10000, 0x20000, 0, 256, 0x30000, wn, 64, 0x40000, 64, None) == ril.RIL_OK  # nothing
+
+
+def test_proj_bf16_rejects_bad_arguments():
+    lib = ctypes.CDLL(ril.LIB_PATH)
+    i, p = ctypes.c_int32, ctypes.c_void_p
+    lib.ril_proj_bf16.argtypes = [p, i, i, i, p, i, i, p, i, p, i, p]
+    A, W, R, C = 0x10000, 0x20000, 0x30000, 0x40000
+    ok = dict(A=A, rows=4, K=256, lda=256, W=W, N=64, ldw=256, R=None, ldr=0, C=C, ldo=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.ril_proj_bf16(a["A"], a["rows"], a["K"], a["lda"], a["W"], a["N"], a["ldw"], a["R"], a["ldr"],
+                                 a["C"], a["ldo"], None)
+    # every case fails validation before anything is enqueued
+    assert call(K=200, lda=200, ldw=200) == ril.RIL_EINVAL   # K % 32
+    assert call(lda=128) == ril.RIL_EINVAL                   # lda < K
+    assert call(lda=260) == ril.RIL_EINVAL                   # lda % 8
+    assert call(ldw=252) == ril.RIL_EINVAL                   # ldw < K
+    assert call(ldo=32) == ril.RIL_EINVAL                    # ldo < N
+    assert call(R=R, ldr=32) == ril.RIL_EINVAL               # ldr < N
+    assert call(A=A + 8) == ril.RIL_EINVAL                   # A misaligned
+    assert call(W=W + 2) == ril.RIL_EINVAL                   # W misaligned
+    assert call(C=C + 1) == ril.RIL_EINVAL                   # out misaligned
+    assert call(W=None) == ril.RIL_EINVAL
+    assert call(N=0) == ril.RIL_EINVAL
+    assert call(lda=1 << 24) == ril.RIL_EINVAL               # 32-bit tile offsets
+    assert call(rows=0) == ril.RIL_OK                        # nothing to do
 
 
 def test_w8a8_pack_and_quantize_reject_bad_arguments():

@@ -135,3 +135,22 @@ def test_fp8_differs_from_bf16_cache():
     a.write_history("d", rows, 1)
     b.write_history("d", rows, 1)
     assert not np.array_equal(_bits(a.decode_back("d", rows, 1)), _bits(b.decode_back("d", rows, 1)))
+
+
+def test_fp8_split_multiple_contexts_decode_equals_prefill_and_oracle():
+    # contexts at and across multiples of the 512-token split with the FP8 cache
+    from gqa_case import GQACase
+    c = GQACase(SMALL, list(range(4)), ctx=[512, 1030, 1536, 2048], kv_dtype=FP8, k_scale_exp=1, v_scale_exp=-1)
+    rows = list(range(4))
+    n = 16
+    c.write_history("d", rows, n)
+    dec = torch.stack([c.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
+    c.write_history("p", rows, n)
+    pre = c.prefill_last("p", rows, n)
+    assert np.array_equal(_bits(dec), _bits(pre))
+    dn = dec.cpu().numpy()
+    for i, r in enumerate(rows):
+        for back in range(1, n + 1):
+            if (c.ctx(r) - back + 1) % 512 == 0 or back == 1:
+                lp_o, _ = c.oracle_row(r, back)
+                assert abs(dn[i, n - back] - lp_o) <= TOL, (r, back)

@@ -130,3 +130,28 @@ def test_run_to_run_determinism():
     outs = [_bits(c.decode_back("d", rows, 1)) for _ in range(5)]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+# Contexts at and across exact multiples of the 512-token split (and of the 64-token
+# tile): the last split of a row is then full, and the decode grid has no partial split
+# for it (the branch a row with a ragged tail never takes).
+EDGE_CTX = [512, 520, 1024, 1030, 1536, 2048]
+
+
+def test_split_multiple_contexts_decode_equals_prefill_and_oracle():
+    from gqa_case import GQACase
+    c = GQACase(SMALL, list(range(6)), ctx=EDGE_CTX)
+    rows = list(range(6))
+    n = 16
+    c.write_history("d", rows, n)
+    dec = torch.stack([c.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
+    c.write_history("p", rows, n)
+    pre = c.prefill_last("p", rows, n)
+    assert np.array_equal(_bits(dec), _bits(pre)), "prefill != decode at split multiples"
+    dn = dec.cpu().numpy()
+    for i, r in enumerate(rows):
+        for back in range(1, n + 1):
+            ctx = c.ctx(r) - back + 1
+            if ctx % 512 == 0 or back == 1:
+                lp_o, _ = c.oracle_row(r, back)
+                assert abs(dn[i, n - back] - lp_o) <= TOL, (r, ctx, dn[i, n - back], lp_o)

@@ -81,3 +81,62 @@ def test_mla_128_heads_two_groups():
         assert abs(float(dec[i, -1]) - lp_o) <= 2e-2
     c.write_history("p", [0, 1], 4)
     assert np.array_equal(_bits(dec), _bits(c.prefill_last("p", [0, 1], 4)))
+
+
+def test_mla_split_multiple_contexts():
+    # contexts at and across multiples of the 2048-token MLA split (and of the 64-token
+    # tile): full last splits in decode, and the prefill chain's split boundary
+    from mla_case import MLACase
+    c = MLACase(SMALL, [0, 1, 2], ctx=[2048, 2056, 4096])
+    rows = [0, 1, 2]
+    n = 16
+    c.write_history("d", rows, n)
+    dec = torch.stack([c.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
+    att_last = c.attn_out(3).float().cpu().numpy()
+    c.write_history("p", rows, n)
+    pre = c.prefill_last("p", rows, n)
+    assert np.array_equal(_bits(dec), _bits(pre))
+    dn = dec.cpu().numpy()
+    for i, r in enumerate(rows):
+        lp_o, o_o = c.oracle_row(r)
+        assert np.max(np.abs(att_last[i] - o_o)) < 2e-2, r
+        assert abs(dn[i, -1] - lp_o) <= 2e-2, r
+    # the row whose window crosses 2048: the step at context exactly 2048 (back = 9)
+    lp_o, _ = c.oracle_row(1, back=9)
+    assert abs(dn[1, n - 9] - lp_o) <= 2e-2
+
+
+def test_mla_graph_replays_equal_eager():
+    # the captured MLA decode step: contexts cross the 2048-token split between replays
+    from mla_case import MLACase
+    c = MLACase(SMALL, [0, 1], ctx=[2050, 700], copies=3)
+    rows = [0, 1]
+    steps = 8
+    c.write_history("g", rows, steps)
+    seqs = [("g", r) for r in rows]
+
+    def inputs(back):
+        q, cc, t, ctx = [], [], [], []
+        for r in rows:
+            d = c.data[r]
+            R = d["q"].shape[0]
+            p = d["ctx"] - back
+            q.append(d["q"][R - back])
+            cc.append(d["c"][p])
+            t.append(d["target"][R - back])
+            ctx.append(p + 1)
+        return dict(q=torch.stack(q), k=torch.stack(cc), targets=torch.stack(t).to(torch.int32)), ctx
+
+    kw, ctx = inputs(steps)
+    g = c.sess.decode_graph(seqs, max(c.ctx(r) for r in rows), ctx=ctx, **kw)
+    try:
+        for back in range(steps, 0, -1):
+            kw, ctx = inputs(back)
+            lg = g.run(ctx, **kw).clone()
+            le = c.sess.decode(seqs, ctx, **kw)
+            assert np.array_equal(_bits(lg), _bits(le)), (back, ctx)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(_bits(g.out), _bits(le)), back
+    finally:
+        g.close()

@@ -93,16 +93,18 @@ def test_proj_rows_keep_their_bits_at_every_row_count():
     w8 = torch.empty(ril.ril_proj_fp8_bytes(N, K), dtype=torch.uint8, device="cuda")
     ril.ril_quantize_weight_fp8(w, w8)
     got = {}
-    for M in (1, 16, 17, 64, 65, 300):  # 16-row, 64-row and 64 x 128 tiles
+    # launch shapes: up to 16 rows one 16-row block per workgroup, up to 256 rows four
+    # 16-row blocks per workgroup, past 256 rows the 256 x 256 tiles of the wide kernel
+    # (its second 128-row group from row 128)
+    for M in (1, 16, 17, 256, 257, 300):
         codes, exps = _quant_rows(x[:M])
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         ril.ril_proj_w8a8(codes, exps, w8, N, out)
         torch.cuda.synchronize()
         got[M] = out.view(torch.int16).cpu().numpy()
-    for M, bits in got.items():
-        assert np.array_equal(bits[:1], got[1]), M
-        if M >= 16:
-            assert np.array_equal(bits[:16], got[16][:16]), M
+    for (M1, b1), (M2, b2) in itertools.combinations(got.items(), 2):
+        n = min(M1, M2)
+        assert np.array_equal(b1[:n], b2[:n]), (M1, M2)
 
 
 def _session(W, wts, proj_dtype):
