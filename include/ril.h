@@ -392,6 +392,27 @@ ril_status ril_lm_head_logprobs(const ril_model *m, int32_t rows, const void *z,
 int32_t ril_hbm_read_probe_words(void);
 ril_status ril_hbm_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream);
 
+/* The rollout step without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP-graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same as ril_decode_step_logprobs(m, kv, b, logprob_out, ws, ws_bytes,
+ * stream) -- the same kernels, the same bits -- with the workspace taken from a static
+ * device array of RIL_NOALLOC_SCRATCH_BYTES bytes inside the library: one per device,
+ * allocated when the library's code is loaded on that device and held until the process
+ * ends.  The call itself allocates and frees nothing.  The array's device address is
+ * looked up on the first call made with a device current.
+ * Limits: ril_workspace_bytes(m) must not exceed RIL_NOALLOC_SCRATCH_BYTES (create a
+ * decode model with small max_tokens; 64 decode rows of 32 x 128-dim heads at contexts up
+ * to 8192 with a 129280-word head need about 18 MiB); else RIL_ERANGE.
+ * Sharing: every call on a device uses that device's one array, which keeps the last
+ * call's contents.  Calls on one device whose work can overlap in time (different
+ * streams, or threads, without ordering between them) race on it: order them on one
+ * stream.  Nothing in the array needs clearing between calls (each call writes every
+ * part it reads).  Errors as ril_decode_step_logprobs, plus RIL_EHIP if the array's
+ * address cannot be looked up and RIL_EUNSUPPORTED for a device index of 64 or more. */
+#define RIL_NOALLOC_SCRATCH_BYTES (64u << 20)
+ril_status ril_decode_step_logprobs_noalloc(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                            float *logprob_out, void *stream);
+
 /* HIP-graph capture of one decode step, for steps whose launch overhead matters
  * (small batches, short contexts).
  *

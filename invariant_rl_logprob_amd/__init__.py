@@ -105,6 +105,8 @@ _prefill = _sig("ril_prefill_logprobs", _c_int,
                 [_vp, _vp, ctypes.POINTER(ril_prefill_batch), _vp, _vp, ctypes.c_size_t, _vp])
 _decode = _sig("ril_decode_step_logprobs", _c_int,
                [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp, ctypes.c_size_t, _vp])
+_decode_noalloc = _sig("ril_decode_step_logprobs_noalloc", _c_int,
+                       [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp])
 _kv_write = _sig("ril_kv_write", _c_int, [_vp, _vp, ctypes.POINTER(ril_prefill_batch), _vp])
 _graph_create = _sig("ril_decode_graph_create", _c_int,
                      [_vp, _vp, ctypes.POINTER(ril_decode_batch), _vp, _vp, ctypes.c_size_t, ctypes.POINTER(_vp)])
@@ -122,7 +124,7 @@ EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril
             "ril_lm_head_logprobs", "ril_hbm_read_probe_words", "ril_hbm_read_probe",
             "ril_ws_attn_offset", "ril_kv_alloc", "ril_kv_assign", "ril_kv_release",
             "ril_kv_free_pages", "ril_kv_total_pages", "ril_kv_free", "ril_prefill_logprobs",
-            "ril_decode_step_logprobs", "ril_kv_write", "ril_last_error", "ril_set_policy", "ril_trace_enable",
+            "ril_decode_step_logprobs", "ril_decode_step_logprobs_noalloc", "ril_kv_write", "ril_last_error", "ril_set_policy", "ril_trace_enable",
             "ril_trace_read", "ril_decode_graph_create", "ril_graph_launch", "ril_graph_destroy")
 
 # kernel ids of the trace hook
@@ -358,6 +360,16 @@ def ril_decode_step_logprobs(model: int, kv: int, batch: ril_decode_batch, logpr
                              stream=None) -> None:
     _check(_decode(model, kv, ctypes.byref(batch), _ptr(logprob_out), _ptr(ws),
                    ws.numel() * ws.element_size(), _stream(stream)), "ril_decode_step_logprobs")
+
+
+RIL_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/ril.h
+
+
+def ril_decode_step_logprobs_noalloc(model: int, kv: int, batch: ril_decode_batch, logprob_out,
+                                     stream=None) -> None:
+    """ril_decode_step_logprobs on the library's static device scratch (no workspace)."""
+    _check(_decode_noalloc(model, kv, ctypes.byref(batch), _ptr(logprob_out), _stream(stream)),
+           "ril_decode_step_logprobs_noalloc")
 
 
 def ril_decode_graph_create(model: int, kv: int, batch: ril_decode_batch, logprob_out, ws) -> int:

@@ -915,6 +915,57 @@ extern "C" ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, c
 }
 
 // ---------------------------------------------------------------------------
+// Decode step on the library's own device scratch, for callers that cannot allocate
+// ---------------------------------------------------------------------------
+
+// The workspace of ril_decode_step_logprobs_noalloc: one static array per device, held
+// until the process ends.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is a host-side stand-in, not a device address): it looks the device
+// address up once per device with hipGetSymbolAddress and uses that pointer.
+static __device__ __align__(256) unsigned char scratch[RIL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device, set on the first call with that device current
+}  // namespace
+
+// The device address of the current device's scratch array, looked up on the first call
+// made with that device current.
+static ril_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RIL_EHIP, "decode_step_logprobs_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RIL_EUNSUPPORTED, "decode_step_logprobs_noalloc: device %d (at most %d devices)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RIL_EHIP, "decode_step_logprobs_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RIL_OK;
+}
+
+extern "C" ril_status ril_decode_step_logprobs_noalloc(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
+                                                       float *logprob_out, void *stream) {
+  if (!m) return fail(RIL_EINVAL, "decode_step_logprobs_noalloc: null model");
+  if (m->ws_total > (size_t)RIL_NOALLOC_SCRATCH_BYTES)
+    return fail(RIL_ERANGE,
+                "decode_step_logprobs_noalloc: the model needs a %zu-byte workspace, above the library's %zu-byte "
+                "scratch (create the model with smaller max_rows / max_tokens / max_ctx)",
+                m->ws_total, (size_t)RIL_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  const ril_status s = scratch_for_current_device(&ws);
+  if (s != RIL_OK) return s;
+  // every segment is written before it is read within a call, so nothing is cleared
+  return decode_enqueue(m, kv, b, logprob_out, ws, (size_t)RIL_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+// ---------------------------------------------------------------------------
 // HIP-graph capture of a decode step
 // ---------------------------------------------------------------------------
 
