@@ -675,7 +675,7 @@ def bench_long(args):
     log(f"decode: {ms_step:.3f} ms/step, split {split_us:.1f} us ({split_gbps:.0f} GB/s)")
 
     # chunked prefill mixed with the decode rows; the trace hook times every kernel
-    sched = [(8192, 0), (2048, 1)] + ([(512, 2)] if args.long_all_chunks else [])
+    sched = [(8192, 0), (2048, 1), (512, 2)]
     runs, prefill = [], {}
     L, S = case.L, len(case.seqs)
     pos_sum = S * L * (L + 1) // 2  # sum over long positions of (p + 1)
@@ -738,6 +738,72 @@ def bench_long(args):
     }
 
 
+def long_decode_leg(args):
+    """The long-context workload's decode step at its own size, next to the headline line:
+    256 GQA decode rows (64 q / 8 kv heads, head_dim 128) at contexts U[1024, 131072]
+    (about 73.5 GB of KV per step), the 8192 -> 4096 output projection and the 4096 x 129280
+    lm-head.  Its 16 last positions are produced by 16 plain decode steps and by one prefill
+    recompute (diff, must be 0); the step is timed like the headline's; the oracle times a
+    sample of rows."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    from invariant_rl_logprob_amd.metrics import mismatch
+    from long_case import LongMixCase
+
+    w = wl.LONG_MIX
+    m = w.decode
+    t0 = time.time()
+    case = LongMixCase(w, n_seqs=0, progress=log, max_tokens=m.rows * w.decode_tokens)
+    rows = case.rows
+    ctx = [case.ctx[r] for r in rows]
+    log(f"long decode: data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
+    ref = case.decode_reference()
+    pre = case.decode_rows_recompute()
+    torch.cuda.synchronize()
+    diff = mismatch(ref, pre)
+    log(f"long decode: decode steps vs prefill recompute over {diff['tokens']} tokens: {diff}")
+    st = lambda key: torch.stack([case.dec[r][key][-1] for r in rows])  # noqa: E731
+    launch, out = case.sess.prepare_decode([("D", r) for r in rows], ctx, targets=st("target"), q=st("q"),
+                                           k=st("k"), v=st("v"))
+    ms_step, kern = timed_steps(launch, args.steps, args.warmup)
+    last_equal = bool(np.array_equal(out.cpu().view(torch.int32).numpy(), ref[:, -1].cpu().view(torch.int32).numpy()))
+    kv_bytes = sum(ctx) * m.n_kv_heads * m.head_dim * 2 * 2
+    q_bytes = len(rows) * m.n_q_heads * m.head_dim * 2
+    split_us, merge_us = kern["attn_split"]["avg_us"], kern["attn_merge"]["avg_us"]
+    split_gbps = (kv_bytes + q_bytes) / (split_us * 1e-6) / 1e9
+    attn_gbps = (kv_bytes + 2 * q_bytes) / ((split_us + merge_us) * 1e-6) / 1e9
+    roof = roofline_hbm("attn_decode_split__long_mix_b256", split_gbps, kv_bytes + q_bytes, split_us)
+    log(f"long decode: {ms_step:.3f} ms/step, split {split_us:.1f} us ({split_gbps:.0f} GB/s)")
+    cpu = None
+    if not args.no_cpu and args.cpu_rows > 0:
+        import oracle  # noqa: F401  (the cpu_baseline leg: case.oracle_decode runs the fp64 oracle)
+        by_ctx = sorted(rows, key=lambda r: case.ctx[r])
+        sample = [by_ctx[0], by_ctx[len(by_ctx) // 2]]
+        t1 = time.time()
+        got = [case.oracle_decode(r, case.nd - 1) for r in sample]
+        secs = time.time() - t1
+        gpu = ref[:, -1].cpu().numpy()
+        cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               **host_info(), "sample": f"decode rows {sample} at contexts {[case.ctx[r] for r in sample]} (attention "
+                                        f"over the whole context, 8192->4096 projection and lm-head in fp64), {secs:.1f} s",
+               "max_abs_diff_vs_gpu": float(max(abs(gpu[r] - g_) for r, g_ in zip(sample, got)))}
+        log(f"long decode oracle: {cpu}")
+    res = {"value": round(len(rows) / (ms_step * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4),
+           "config": {"workload": "long_mix decode: 256 GQA decode rows (64 q / 8 kv heads, head_dim 128) at contexts "
+                                  "U[1024,131072], 16-token pages, random page table, o-proj 8192x4096, "
+                                  "lm-head 4096x129280",
+                      "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 512},
+           "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+           "diff": diff, "timed_step_equals_checked_decode": last_equal,
+           "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+           "roofline": roof, "cpu_baseline": cpu}
+    case.sess.close()
+    del case, ref, pre, out, launch
+    torch.cuda.empty_cache()
+    return res
+
+
 WORKLOADS = {"gqa_decode_b64": bench_gqa, "gqa_decode_b64_fp8": bench_gqa_fp8,
              "gqa_decode_b64_w8a8": bench_gqa_w8a8, "gqa_decode_b64_fp8_w8a8": bench_gqa_fp8_w8a8, "mla_decode_b128": bench_mla,
              "sparse_mla_b32": bench_sparse, "long_mix": bench_long}
@@ -749,12 +815,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_decode_b64", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-rows", type=int, default=12, help="rows of the oracle timing sample")
+    ap.add_argument("--cpu-rows", type=int, default=30, help="rows of the oracle timing sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-comparator", action="store_true", help="skip the shape-derived comparator leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay leg")
     ap.add_argument("--no-lm-sweep", action="store_true", help="skip the lm-head M sweep (gqa workloads)")
-    ap.add_argument("--long-all-chunks", action="store_true", help="long_mix: also run the 512-token chunks")
+    ap.add_argument("--no-long", action="store_true",
+                    help="gqa_decode_b64: skip the long-context decode leg (256 rows at contexts to 131072)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")
     ap.add_argument("--lm-head-rows", type=int, default=0,
@@ -783,6 +850,9 @@ def main():
         return
 
     res = WORKLOADS[args.workload](args)
+    if args.workload == "gqa_decode_b64" and not args.no_long:
+        torch.cuda.empty_cache()
+        res["long_mix_decode"] = long_decode_leg(args)
     line = {"metric": METRIC, "value": res.pop("value"), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": res.pop("dtype", "bf16"), "data": "synthetic"}

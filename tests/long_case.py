@@ -18,7 +18,7 @@ from invariant_rl_logprob_amd.session import Session
 class LongMixCase:
     def __init__(self, w: wl.LongMix = wl.LONG_MIX, *, n_seqs: int = None, seq_len: int = None,
                  rows: int = None, decode_ctx: Sequence[int] = None, device="cuda", shuffle_seed=99,
-                 max_chunk: int = None, progress=None):
+                 max_chunk: int = None, progress=None, max_tokens: int = None):
         m = w.decode
         self.w, self.m, self.device = w, m, device
         self.L = seq_len or w.seq_len
@@ -37,7 +37,7 @@ class LongMixCase:
         self.sess = Session(n_q_heads=m.n_q_heads, n_kv_heads=m.n_kv_heads, head_dim=m.head_dim, vocab=m.vocab,
                             d_head=m.d_head, w_lm=self.head["w_lm"], w_o=self.head["w_o"],
                             max_rows=max(1, len(self.rows)),
-                            max_tokens=len(self.seqs) * max_chunk + len(self.rows),
+                            max_tokens=max_tokens or len(self.seqs) * max_chunk + len(self.rows),
                             max_ctx=max([self.L] + list(self.ctx.values())), pool_pages=pages,
                             softmax_scale=self.scale, rms_eps=m.rms_eps, shuffle_seed=shuffle_seed, device=device)
         # decode rows: history [0, ctx - nd) in the pool; keep the inputs of the last nd positions
@@ -65,6 +65,16 @@ class LongMixCase:
             out.append(self.sess.decode([("D", r) for r in self.rows], ctx, targets=st("target"), q=st("q"),
                                         k=st("k"), v=st("v")))
         return torch.stack(out, dim=1)
+
+    def decode_rows_recompute(self) -> torch.Tensor:
+        """The decode rows' last nd positions recomputed by one prefill call (each row one
+        segment of nd tokens after its history): fp32 [rows, nd]."""
+        seqs = [("D", r) for r in self.rows]
+        starts = [self.ctx[r] - self.nd for r in self.rows]
+        d = [self.dec[r] for r in self.rows]
+        out = self.sess.prefill(seqs, starts, targets=[x["target"] for x in d], qs=[x["q"] for x in d],
+                                ks=[x["k"] for x in d], vs=[x["v"] for x in d])
+        return out.view(len(self.rows), self.nd)
 
     def run_schedule(self, chunk: int, mix: int, tag) -> tuple:
         """Prefill every long sequence in chunks of `chunk` tokens, one prefill call per
