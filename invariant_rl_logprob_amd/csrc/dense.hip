@@ -147,15 +147,12 @@ __device__ __forceinline__ void kloop(f32x4 (&acc)[MB][NB], const bf16_t *const 
   }
 }
 
-// The K loop with the activation operand staged through LDS, shared by the lm-head and
-// the few-row projections.  Every output column accumulates its 32-wide K steps in the
-// order r, r+1, ..., nk-1, 0, ..., r-1 (rot = r; 0 for the projections, so their order is
-// the plain 0, 32, 64, ... of kloop; lm_rot(tile) for the lm-head).
-// The activation operand is staged through LDS in chunks of 8 K steps (each of the four
-// waves loads two steps for the whole workgroup); weight operands run PF steps ahead in
-// a register ring.  wp[nb] points at MFMA block nb's first operand; step s's operand is
-// WSTEP elements further (512 in the lm-head's packed layout, 32 in a row-major
-// [N, K] matrix).  NT: weight loads use the nontemporal (streaming) cache policy, for
+// The K loop of the lm-head up to 128 rows, the activation operand staged through LDS.
+// Every output column accumulates its 32-wide K steps in the order r, r+1, ..., nk-1, 0,
+// ..., r-1 (rot = lm_rot(tile)).  The activation operand is staged through LDS in chunks
+// of 8 K steps (each of the four waves loads two steps for the whole workgroup); weight
+// operands run PF steps ahead in a register ring.  wp[nb] points at MFMA block nb's first
+// operand; step s's operand is WSTEP elements further (512 in the packed layout).  NT: weight loads use the nontemporal (streaming) cache policy, for
 // grids that read each weight once.  All four waves must call this (it synchronises the
 // workgroup).
 constexpr int kLdsSteps = 8;
@@ -272,39 +269,195 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t *__restrict__ A,
   }
 }
 
-// S4 for few rows: a workgroup of 4 waves covers 16*MB rows x 64 columns, wave w owning
-// columns 16w .. 16w+15.  The rows' activation operand is staged once per workgroup
-// through LDS and each wave streams its 16 weight rows through a 16-step register ring
-// (kloop_lds with no rotation: the same K order, hence the same bits, as gemm_kernel).
-template <int MB, bool NT>
-__global__ __launch_bounds__(256) void gemm_rows_kernel(const bf16_t *__restrict__ A, int lda,
-                                                        const bf16_t *__restrict__ W, int ldw,
-                                                        bf16_t *__restrict__ C, int ldc,
-                                                        const bf16_t *__restrict__ R, int ldr, int M, int N, int K) {
-  __shared__ u32x4 lds_a[2][kLdsSteps * MB * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int grp = lane >> 4, r16 = lane & 15;
-  const int m0 = blockIdx.y * 16 * MB;
-  const int n0 = blockIdx.x * 64 + wave * 16;
-  const bf16_t *ap[MB];
-  const bf16_t *wp[1];
+// S4 for few rows and long K (M <= 256, K >= 1024): both operands streamed through LDS.
+// A workgroup owns a tile of 16*RB rows x 16*CB columns.  Three producer waves copy the
+// tile's operands into two LDS rings by direct-to-LDS loads -- one the rows' operand
+// (L2-resident: every column tile reads it), two the weight's (streamed from HBM, so its
+// ring is as deep as LDS allows) -- and four consumer waves read them back in the MFMA
+// lane layout.  Each copy instruction moves eight rows x 128 bytes: two 32-wide K steps of
+// each row, whole cache lines, which halves the L2 requests per byte against the one-step
+// operand load (the L2 request rate, not HBM, bounds this shape; measured 2.4x at 128
+// rows).  The 16-byte chunks of a row are rotated by the row index inside the copy, so
+// the operand reads hit eight distinct bank groups per eight lanes.  One barrier per
+// chunk of CH steps: each producer's copies of chunk c have landed, and every consumer is
+// done with chunk c-1's buffers, which the producers then refill.  Tiles are sized so a
+// 4096-column projection makes about 256 workgroups (one per CU), and the row tiles of
+// one column tile land on one XCD, so a weight byte comes from HBM once.  Every element's
+// K order is 0, 32, 64, ... with one v_mfma_f32_16x16x32_bf16 per step, the operands those
+// of gemm_kernel: its bits are those of gemm_kernel and wide_kernel<false> at any M.
+constexpr int kStreamProd = 3, kStreamCons = 4;
+constexpr int kStreamThreads = 64 * (kStreamCons + kStreamProd);
+constexpr int kStreamLds = 144 * 1024;
+template <int RB, int CB, int CH>
+struct StreamTile {
+  // per chunk of CH steps (CH/2 K-step pairs): the row operand's and the weight's bytes,
+  // and the copies of the row producer and of each of the two weight producers
+  static constexpr int kABytes = (CH / 2) * 2 * RB * 1024;
+  static constexpr int kWBytes = (CH / 2) * 2 * CB * 1024;
+  static constexpr int kALoads = (CH / 2) * 2 * RB;
+  static constexpr int kWLoads = (CH / 2) * CB;
+  // ring depths in chunks: the rows (L2-resident, short latency) four chunks if the vmcnt
+  // field allows, else three; the weight (from HBM) as deep as LDS and the field allow
+  static constexpr int kARing = 2 * kALoads <= 63 ? 4 : 3;
+  static_assert(kALoads <= 63, "the row producer's chunk fits the vmcnt field");
+  static constexpr int kWByLds = (kStreamLds - kARing * kABytes) / kWBytes;
+  static constexpr int kWByCnt = 63 / kWLoads + 2;
+  static constexpr int kWRing0 = kWByLds < kWByCnt ? kWByLds : kWByCnt;
+  static constexpr int kWRing = kWRing0 < 32 ? kWRing0 : 32;
+  static_assert(kWRing >= 3 && (kARing - 2) * kALoads <= 63, "ring depths");
+  // consumer wave w's blocks: RB >= 4: row blocks w, w+4, .. x every column block;
+  // else CB >= 4: column blocks w, w+4, .. x every row block; else block (w / CB, w % CB)
+  static constexpr int kWR = RB >= 4 ? RB / 4 : (CB >= 4 ? RB : 1);
+  static constexpr int kWC = RB >= 4 ? CB : (CB >= 4 ? CB / 4 : 1);
+};
+
+template <int RB, int CB, int CH>
+__global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(const bf16_t *__restrict__ A, int lda,
+                                                                     const bf16_t *__restrict__ W, int ldw,
+                                                                     bf16_t *__restrict__ C, int ldc,
+                                                                     const bf16_t *__restrict__ R, int ldr, int M,
+                                                                     int N, int K) {
+  using T = StreamTile<RB, CB, CH>;
+  constexpr int NA = T::kARing, NW = T::kWRing;
+  __shared__ __attribute__((aligned(16))) uint8_t aring[NA][T::kABytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wring[NW][T::kWBytes];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n0 = blockIdx.x * 16 * CB, m0 = blockIdx.y * 16 * RB;
+  const int nk = K / 32, nc = (nk + CH - 1) / CH;
+  if (wave >= kStreamCons) {
+    // producers: wave 0 of them copies the rows' operand, waves 1 and 2 the weight's
+    // (alternate eight-row pieces).  Per K-step pair an operand of 16*X rows is 2*X pieces
+    // of eight rows x 128 bytes; lane l moves 16 bytes of row l/8 of its piece: chunk
+    // c = (l - l/8) mod 8 of the row's 128 bytes, i.e. K values 8c .. 8c+7 of the pair,
+    // into slot l (the rotation).  Past the last step a copy re-reads the last pair (and
+    // K past the end is clamped into the row), so every chunk issues the same loads and
+    // each producer's vmcnt waits (on its own copies only) are exact.
+    const int p = wave - kStreamCons;
+    const int rho = lane >> 3, cch = (lane - rho) & 7;
+    const int npair = (nk + 1) / 2;
+    const bool rows = p == 0;
+    const bf16_t *base = rows ? A + (long)m0 * lda : W + (long)n0 * ldw;
+    const int ld = rows ? lda : ldw, lim = rows ? M - 1 - m0 : N - 1 - n0;
+    auto issue = [&](int c) {
+      uint8_t *dst = rows ? &aring[c % NA][0] : &wring[c % NW][0];
+      static_for<CH / 2>([&](auto q_) {
+        constexpr int q = decltype(q_)::value;
+        const int pair = min(c * (CH / 2) + q, npair - 1);
+        const int k = min(pair * 64 + 8 * cch, K - 8);
+        if (rows) {
+          static_for<2 * RB>([&](auto i_) {
+            constexpr int i = decltype(i_)::value;
+            const bf16_t *src = base + (long)min(8 * i + rho, lim) * ld + k;
+            __builtin_amdgcn_global_load_lds((void *)src, (void *)(dst + (q * 2 * RB + i) * 1024), 16, 0, 0);
+          });
+        } else {
+          static_for<CB>([&](auto i_) {
+            constexpr int i = 2 * decltype(i_)::value;
+            const int piece = i + (p - 1);
+            const bf16_t *src = base + (long)min(8 * piece + rho, lim) * ld + k;
+            __builtin_amdgcn_global_load_lds((void *)src, (void *)(dst + (q * 2 * CB + piece) * 1024), 16, 0, 0);
+          });
+        }
+      });
+    };
+    const int ahead = rows ? NA - 1 : NW - 1;
+    for (int c = 0; c < ahead; ++c) issue(c);
+    for (int c = 0; c < nc; ++c) {
+      // chunk c landed (the later chunks this producer issued may be in flight)
+      if (rows) wait_vmem<(NA - 2) * T::kALoads>();
+      else wait_vmem<(NW - 2) * T::kWLoads>();
+      asm volatile("s_barrier" ::: "memory");
+      issue(c + ahead);  // into chunk c-1's buffer, which every consumer is done with
+    }
+    wait_vmem<0>();  // no copy may still write this workgroup's LDS when it ends
+    return;
+  }
+  // consumer: blocks (rb0 + 4 i or rb0 + i, cb ...) as StreamTile describes
+  constexpr int WR = T::kWR, WC = T::kWC;
+  int rbs[WR], cbs[WC];
+  if constexpr (RB >= 4) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) ap[mb] = A + (long)min(m0 + 16 * mb + r16, M - 1) * lda + grp * 8;
-  wp[0] = W + (long)min(n0 + r16, N - 1) * ldw + grp * 8;
-  f32x4 acc[MB][1];
+    for (int i = 0; i < WR; ++i) rbs[i] = wave + 4 * i;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  kloop_lds<MB, 1, 15, 32, NT>(acc, ap, wp, K, 0, lds_a);
-  const int col = n0 + r16;
+    for (int i = 0; i < WC; ++i) cbs[i] = i;
+  } else if constexpr (CB >= 4) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
+    for (int i = 0; i < WR; ++i) rbs[i] = i;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * mb + 4 * grp + i;
-      if (row < M && col < N) {
-        float v = bf2f(f2bf(acc[mb][0][i]));
-        if (R) v = bf2f(R[(long)row * ldr + col]) + v;
-        C[(long)row * ldc + col] = f2bf(v);
+    for (int i = 0; i < WC; ++i) cbs[i] = wave + 4 * i;
+  } else {
+    rbs[0] = wave / CB;
+    cbs[0] = wave % CB;
+  }
+  // a wave with no block (fewer than four), or whose rows all lie past M, keeps the barriers
+  const bool idle = (RB < 4 && CB < 4 && wave >= RB * CB) || m0 + 16 * rbs[0] >= M;
+  if (idle) {
+    for (int c = 0; c < nc; ++c) asm volatile("s_barrier" ::: "memory");
+    return;
+  }
+  f32x4 acc[WR][WC];
+#pragma unroll
+  for (int i = 0; i < WR; ++i)
+#pragma unroll
+    for (int j = 0; j < WC; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this lane's operand (row r16 of a 16-row block, K chunk grp of step u of a pair):
+  // piece r16/8, row r16%8, 16-byte chunk 4u + grp, at its rotated slot
+  const int grp = lane >> 4, r16 = lane & 15, rho = r16 & 7;
+  uint32_t off[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) off[u] = (uint32_t)((r16 >> 3) * 1024 + (rho * 8 + ((4 * u + grp + rho) & 7)) * 16);
+  const uint32_t abase = lds_addr(&aring[0][0]), wbase = lds_addr(&wring[0][0]);
+  uint32_t a_off[WR], w_off[WC];
+#pragma unroll
+  for (int i = 0; i < WR; ++i) a_off[i] = (uint32_t)(rbs[i] * 2048);
+#pragma unroll
+  for (int j = 0; j < WC; ++j) w_off[j] = (uint32_t)(cbs[j] * 2048);
+  // one K-step pair: read both steps' operands, then the MFMAs of step 0, then step 1
+  auto pair_step = [&](uint32_t pa, uint32_t pw, int s0) {
+    u32x4 a[2][WR], b[2][WC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int i = 0; i < WR; ++i) a[u][i] = lds_rd128<0>(pa + a_off[i] + off[u]);
+#pragma unroll
+      for (int j = 0; j < WC; ++j) b[u][j] = lds_rd128<0>(pw + w_off[j] + off[u]);
+    }
+    lds_wait<0>();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && s0 + 1 >= nk) break;  // an odd last step
+#pragma unroll
+      for (int i = 0; i < WR; ++i) settle(a[u][i]);
+#pragma unroll
+      for (int j = 0; j < WC; ++j) settle(b[u][j]);
+#pragma unroll
+      for (int i = 0; i < WR; ++i)
+#pragma unroll
+        for (int j = 0; j < WC; ++j) acc[i][j] = mfma(as_bf16x8(a[u][i]), as_bf16x8(b[u][j]), acc[i][j]);
+    }
+  };
+  for (int c = 0; c < nc; ++c) {
+    asm volatile("s_barrier" ::: "memory");  // chunk c's operands are in LDS
+    const uint32_t ca = abase + (uint32_t)(c % NA) * T::kABytes, cw = wbase + (uint32_t)(c % NW) * T::kWBytes;
+#pragma unroll
+    for (int q = 0; q < CH / 2; ++q) {
+      const int s0 = c * CH + 2 * q;
+      if (s0 < nk) pair_step(ca + q * 2 * RB * 1024, cw + q * 2 * CB * 1024, s0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < WR; ++i) {
+#pragma unroll
+    for (int j = 0; j < WC; ++j) {
+      const int col = n0 + 16 * cbs[j] + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + 16 * rbs[i] + 4 * grp + e;
+        if (row < M && col < N) {
+          float v = bf2f(f2bf(acc[i][j][e]));
+          if (R) v = bf2f(R[(long)row * ldr + col]) + v;
+          C[(long)row * ldc + col] = f2bf(v);
+        }
       }
     }
   }
@@ -410,7 +563,7 @@ __device__ __forceinline__ void wait_steps(int ahead) {
 // LM = true: the lm-head (W packed, the K order of lm_rot, the softmax-partials epilogue),
 // n_vt vocabulary tiles.  LM = false: a projection C[M, N] = bf16(Z W^T) [+ residual R]
 // with W row-major [N, ldw] (each 16-column block's operand copied by per-lane addresses
-// like the rows'), K order 0, 32, 64, ... (that of gemm_kernel and gemm_rows_kernel, so
+// like the rows'), K order 0, 32, 64, ... (that of gemm_kernel and gemm_stream_kernel, so
 // the bits are theirs at any M), n_vt = ceil(N / 256) column tiles.
 template <bool LM>
 __global__ __launch_bounds__(512) void wide_kernel(const bf16_t *__restrict__ Z, int ldz,
@@ -619,19 +772,19 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
     return hipGetLastError();
   }
   if (!part && a.M <= 256 && a.K >= 1024) {
-    // few rows, long K: the rows' operand shared through LDS, 16 columns per wave
-    const int mb = a.M <= 64 ? 1 : (a.M <= 128 ? 2 : 4);
-    dim3 grid((a.N + 63) / 64, (a.M + 16 * mb - 1) / (16 * mb));
-    // one row block reads each weight once: stream it past the caches (more row blocks
-    // re-read it, and the caches then pay off)
-    const bool nt = grid.y == 1;
-#define RIL_ROWS(MB_, NT_) \
-  hipLaunchKernelGGL((gemm_rows_kernel<MB_, NT_>), grid, dim3(256), 0, st, a.A, a.lda, a.W, a.ldw, a.C, a.ldc, a.R, \
-                     a.ldr, a.M, a.N, a.K)
-    if (mb == 1) { if (nt) RIL_ROWS(1, true); else RIL_ROWS(1, false); }
-    else if (mb == 2) { if (nt) RIL_ROWS(2, true); else RIL_ROWS(2, false); }
-    else { if (nt) RIL_ROWS(4, true); else RIL_ROWS(4, false); }
-#undef RIL_ROWS
+    // few rows, long K: both operands streamed through LDS in whole cache lines; tiles of
+    // 16 x 16 .. 64 x 64 sized so that a 4096-column projection fills the CUs once
+#define RIL_STREAM(RB_, CB_, CH_)                                                                                \
+  hipLaunchKernelGGL((gemm_stream_kernel<RB_, CB_, CH_>), dim3((a.N + 16 * CB_ - 1) / (16 * CB_), (a.M + 16 * RB_ - 1) / (16 * RB_)), \
+                     dim3(kStreamThreads), 0, st, a.A, a.lda, a.W, a.ldw, a.C, a.ldc, a.R, a.ldr, a.M, a.N, a.K)
+    // (65536 -> 4096 at 16 / 32 / 64 / 128 / 256 rows: 101 / 125 / 157 / 206 / 286 us; larger
+    // chunks mean fewer barriers, bounded by the LDS the rings need)
+    if (a.M <= 16) RIL_STREAM(1, 1, 16);
+    else if (a.M <= 32) RIL_STREAM(2, 1, 16);
+    else if (a.M <= 64) RIL_STREAM(2, 2, 8);
+    else if (a.M <= 128) RIL_STREAM(4, 2, 8);
+    else RIL_STREAM(4, 4, 4);
+#undef RIL_STREAM
     return hipGetLastError();
   }
   if (a.M <= 16) {
