@@ -155,10 +155,12 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   const int pid = (in_ctx && !bad_lane) ? p_raw : 0;
   const bool bad = __any(bad_lane);
   // Ring of NR = 2*LA + 1 half-tile slots, LA = 2 tiles ahead: while the scores of tile t
-  // run, the V half of t, both halves of t+1 and the K half of t+2 are in flight (64 KB
-  // per wave for D = 128 in bf16, 32 KB in FP8; deeper FP8 rings measured slower).
-  // Half-tile h (K of tile h/2 if h is even, else its V) lives in slot h % NR; FP8 slots
-  // hold the codes, dequantized into bf16 operands just before use.
+  // run, the V half of t, both halves of t+1 and the K half of t+2 are in flight (64 KB per
+  // wave for D = 128 in bf16, 32 KB in FP8).  FP8 slots hold the codes, each operand
+  // dequantized just before its MFMA (no dequantized tile held in registers).  Measured
+  // and not kept for FP8: rings 3 and 4 tiles deep, and two or three waves per SIMD (the
+  // register cap then spills): 139-286 us against 139 us.  Half-tile h (K of tile h/2 if
+  // h is even, else its V) lives in slot h % NR.
   constexpr int LA = 2, NR = 2 * LA + 1;
   using Slot = std::conditional_t<FP8, Half8<D>, Half<D>>;
   Slot ring[NR];
@@ -207,18 +209,17 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
         bf16x8 pop[2];
         float alpha, m_new, l_new;
         if constexpr (FP8) {
-          Half<D> kt;
-          dequant_k<D>(ring[(2 * j) % NR], kt);
-          attn_scores<D>(kt, s0 + t * kTile, qop, ctx - 1, cscale, m, l, pop, alpha, m_new, l_new);
+          f32x4 s[4];
+          attn_score_mfma8<D>(ring[(2 * j) % NR], qop, s);
+          tile_softmax(s, s0 + t * kTile, ctx - 1, cscale, m, l, pop, alpha, m_new, l_new);
         } else {
           attn_scores<D>(ring[(2 * j) % NR], s0 + t * kTile, qop, ctx - 1, cscale, m, l, pop, alpha, m_new,
                          l_new);
         }
         if (ahead) ldv(ring[(2 * j) % NR]);  // the slot of K(t), just consumed
         if constexpr (FP8) {
-          Half<D> vt;
-          dequant_v<D>(ring[(2 * j + 1) % NR], vt);
-          attn_values<D, false>(vt, s0 + t * kTile, ctx - 1, ctx, pop, alpha, m_new, l_new, m, l, o);
+          attn_values8<D, false>(ring[(2 * j + 1) % NR], s0 + t * kTile, ctx - 1, ctx, pop, alpha, m_new, l_new,
+                                 m, l, o);
         } else {
           attn_values<D, false>(ring[(2 * j + 1) % NR], s0 + t * kTile, ctx - 1, ctx, pop, alpha, m_new, l_new,
                                 m, l, o);

@@ -329,6 +329,25 @@ __device__ __forceinline__ void attn_score_mfma(const Half<D> &k, const bf16x8 (
   }
 }
 
+// The same chains from an FP8 half-tile, each operand dequantized (fp8_operand, exact)
+// just before its MFMA: operand (mb, c = 2j) is words 0-1 of raw r[mb*(D/64) + j], c = 2j+1
+// words 2-3 -- the operands dequant_k would produce, in the same order, without holding a
+// dequantized tile in registers.
+template <int D>
+__device__ __forceinline__ void attn_score_mfma8(const Half8<D> &k, const bf16x8 (&qop)[D / 32], f32x4 (&s)[4]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      const u32x4 w = k.r[mb * (D / 64) + j];
+      acc = mfma(as_bf16x8(fp8_operand(w[0], w[1])), qop[2 * j], acc);
+      acc = mfma(as_bf16x8(fp8_operand(w[2], w[3])), qop[2 * j + 1], acc);
+    }
+    s[mb] = acc;
+  }
+}
+
 template <int D, bool MASK = true>
 __device__ __forceinline__ void attn_scores(const Half<D> &k, int tile_start, const bf16x8 (&qop)[D / 32],
                                             int pos, float cscale, float m, float l, bf16x8 (&pop)[2],
@@ -344,10 +363,10 @@ __device__ __forceinline__ void attn_scores(const Half<D> &k, int tile_start, co
 // MAYBE_INACTIVE: some column may have pos < tile_start; such columns keep their state.
 // VMASK = false: the caller knows the tile ends at or before vbound, so no V value needs
 // zeroing.
-template <int D, bool MAYBE_INACTIVE, bool VMASK = true>
-__device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, int pos, int vbound,
-                                            const bf16x8 (&pop)[2], float alpha, float m_new, float l_new,
-                                            float &m, float &l, f32x4 (&o)[D / 16]) {
+template <int D, bool MAYBE_INACTIVE, bool VMASK, typename VOp>
+__device__ __forceinline__ void attn_values_op(VOp vop, int tile_start, int pos, int vbound,
+                                               const bf16x8 (&pop)[2], float alpha, float m_new, float l_new,
+                                               float &m, float &l, f32x4 (&o)[D / 16]) {
   const int grp = (threadIdx.x & 63) >> 4;
   // o is rescaled and accumulated in place on every path (one register set for o, so
   // the callers' variants need no copies); inactive columns get their old state back.
@@ -363,7 +382,7 @@ __device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, in
     const int n_valid = vbound - (tile_start + 32 * kc + 8 * grp);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      u32x4 vv = v.r[kc * (D / 16) + db];
+      u32x4 vv = vop(kc, db);
       if (VMASK && n_valid < 8) vv = keep_first(vv, n_valid);
       o[db] = mfma(as_bf16x8(vv), pop[kc], o[db]);
     }
@@ -381,6 +400,28 @@ __device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, in
     m = m_new;
     l = l_new;
   }
+}
+
+template <int D, bool MAYBE_INACTIVE, bool VMASK = true>
+__device__ __forceinline__ void attn_values(const Half<D> &v, int tile_start, int pos, int vbound,
+                                            const bf16x8 (&pop)[2], float alpha, float m_new, float l_new,
+                                            float &m, float &l, f32x4 (&o)[D / 16]) {
+  attn_values_op<D, MAYBE_INACTIVE, VMASK>([&](int kc, int db) { return v.r[kc * (D / 16) + db]; }, tile_start,
+                                           pos, vbound, pop, alpha, m_new, l_new, m, l, o);
+}
+
+// The same from an FP8 half-tile: operand (kc, db) is dequantized just before its MFMA
+// (db = 2j: words 0-1 of raw r[kc*(D/32) + j], db = 2j+1: words 2-3, as dequant_v lays them).
+template <int D, bool MAYBE_INACTIVE, bool VMASK = true>
+__device__ __forceinline__ void attn_values8(const Half8<D> &v, int tile_start, int pos, int vbound,
+                                             const bf16x8 (&pop)[2], float alpha, float m_new, float l_new,
+                                             float &m, float &l, f32x4 (&o)[D / 16]) {
+  attn_values_op<D, MAYBE_INACTIVE, VMASK>(
+      [&](int kc, int db) {
+        const u32x4 w = v.r[kc * (D / 32) + (db >> 1)];
+        return (db & 1) ? fp8_operand(w[2], w[3]) : fp8_operand(w[0], w[1]);
+      },
+      tile_start, pos, vbound, pop, alpha, m_new, l_new, m, l, o);
 }
 
 // One whole 64-token tile update (both halves).
