@@ -210,23 +210,24 @@ __device__ __forceinline__ void mla_tile_values(f32x4 (&o)[kMlaDv / 32], const b
   const int grp = (threadIdx.x & 63) >> 4;
   const int nv0 = MASK ? n_live - 8 * grp : 8, nv1 = MASK ? n_live - (32 + 8 * grp) : 8;
   const MlaVBase base = mla_v_base(kt, half);
-  const bool scale = __any(alpha != 1.f);
-  u32x2 r[2][2][2];
-  mla_v_issue<0, 0>(r[0][0], base);
-  mla_v_issue<0, 1>(r[0][1], base);
-  static_for<kMlaDv / 32>([&](auto bb) {
-    constexpr int B = decltype(bb)::value;
-    if constexpr (B + 1 < kMlaDv / 32) {
-      mla_v_issue<B + 1, 0>(r[(B + 1) & 1][0], base);
-      mla_v_issue<B + 1, 1>(r[(B + 1) & 1][1], base);
-      lds_wait<4>();
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int b = 0; b < kMlaDv / 32; ++b) o[b] = o[b] * alpha;
+  }
+  // token step 0 for every dim block, then step 1: a block's two MFMAs are 16 apart, so
+  // the second never waits for the first (per element: rescale, step 0, step 1)
+  u32x2 r[2][2];
+  mla_v_issue<0, 0>(r[0], base);
+  static_for<2 * (kMlaDv / 32)>([&](auto ii) {
+    constexpr int I = decltype(ii)::value, KC = I / (kMlaDv / 32), B = I % (kMlaDv / 32);
+    if constexpr (I + 1 < 2 * (kMlaDv / 32)) {
+      constexpr int KN = (I + 1) / (kMlaDv / 32), BN = (I + 1) % (kMlaDv / 32);
+      mla_v_issue<BN, KN>(r[(I + 1) & 1], base);
+      lds_wait<2>();
     } else {
       lds_wait<0>();
     }
-    f32x4 acc = scale ? o[B] * alpha : o[B];
-    acc = mfma(mla_v_take(r[B & 1][0], nv0), pop[0], acc);
-    acc = mfma(mla_v_take(r[B & 1][1], nv1), pop[1], acc);
-    o[B] = acc;
+    o[B] = mfma(mla_v_take(r[I & 1], KC == 0 ? nv0 : nv1), pop[KC], o[B]);
   });
 }
 
