@@ -183,24 +183,6 @@ size_t ril_workspace_bytes(const ril_model *m);
 /* Bytes of one KV page: Hkv x 2 (K, V) x page_tokens x D x 2 bytes. */
 size_t ril_kv_page_bytes(const ril_model *m);
 
-/* Comparator, for benchmarking only.  RIL_POLICY_INVARIANT (the default) is the
- * method: every reduction order is fixed by the model alone.  RIL_POLICY_SHAPE_DERIVED
- * makes the same kernels choose their work split from the call's shape, as a
- * throughput-first engine would, so that the price of invariance can be measured:
- *   - decode attention's KV split (tokens): attn_split_tokens if non-zero (a multiple
- *     of 64, at most 1024 for GQA and 2048 for MLA), else enough splits for two waves
- *     per SIMD of the device, ceil(max_ctx_bound / splits) rounded up to 64, widened
- *     until the partials fit the invariant workspace;
- *   - projection GEMMs whose tile grid is smaller than the device's compute-unit count
- *     split their K loop (at most 16 chunks of at least 256) and add the fp32 chunk
- *     results in a second kernel.
- * Under it, results depend on the batch and decode no longer equals prefill.  Setting
- * it queries the current device's compute-unit count and enlarges
- * ril_workspace_bytes(m) by the split-K partial buffer.  Returns RIL_EINVAL for an
- * unknown policy or a bad override, RIL_EHIP if the device cannot be queried. */
-enum { RIL_POLICY_INVARIANT = 0, RIL_POLICY_SHAPE_DERIVED = 1 };
-ril_status ril_set_policy(ril_model *m, int32_t policy, int32_t attn_split_tokens);
-
 /* S11 weight layout.  The lm-head reads its weight in a packed form: per vocabulary
  * tile of 256 columns, per 16-column MFMA block, per 32-wide K step, that block's
  * MFMA operand in lane order, so each weight load of a wavefront is one contiguous
@@ -294,7 +276,13 @@ ril_status ril_proj_w8a8(const void *codes, const void *exps, int32_t rows, int3
 ril_status ril_proj_bf16(const void *A, int32_t rows, int32_t K, int32_t lda, const void *W, int32_t N,
                          int32_t ldw, const void *residual, int32_t ldr, void *out, int32_t ldo, void *stream);
 
-/* S1: page assignment.  Wrap a caller-owned device pool of `pool_bytes`
+/* S1: page assignment.  Decode reads a paged cache whose page placement
+ * must not change a single bit of the result (Bitwise-consistent RL post,
+ * section 4.3: prefill's contiguous and decode's paged reads are bitwise
+ * identical; section 4.2: the cache's storage sets concurrency).  The pages
+ * are position-independent blocks, so a sequence's bits are the same for any
+ * page ids, and a pool copied elsewhere (a restored checkpoint) serves the
+ * same results.  Wrap a caller-owned device pool of `pool_bytes`
  * bytes (16-byte aligned) as floor(pool_bytes / page_bytes) pages and build a
  * host free list over them.  shuffle_seed != 0 permutes the free list with a
  * seeded Fisher-Yates shuffle (random page tables); 0 hands pages out in
@@ -357,14 +345,20 @@ typedef struct ril_decode_batch {
   int32_t *selected_out;    /* MLA_SPARSE, optional: device int32 [n_rows, topk] */
 } ril_decode_batch;
 
-/* Trainer-side recompute: writes every batch token's K/V into its page
+/* Trainer-side recompute: the trainer's forward calls the rollout's kernels
+ * (Bitwise-consistent RL post, section 3.1), and a prefill chunk, a whole
+ * sequence or a decode row give one position the same bits (section 2, phase
+ * consistency).  Writes every batch token's K/V into its page
  * (S5), attends causally over the cache (S10), then the head (S4, S3, S11,
  * S12).  logprob_out: device fp32 [total_tokens].  ws: device workspace of at
  * least ril_workspace_bytes(m) bytes. */
 ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b,
                                 float *logprob_out, void *ws, size_t ws_bytes, void *stream);
 
-/* Rollout-side step: writes each row's new K/V into its page (S5), attends
+/* Rollout-side step: decode runs the same read path and arithmetic as
+ * prefill, with a work partition that never depends on the batch
+ * (Bitwise-consistent RL post, section 4.2; the zero-mismatch-rl README's
+ * fixed-split attention).  Writes each row's new K/V into its page (S5), attends
  * over the row's ctx_len[r] positions with fixed-size splits (S8) merged in
  * split order (S9), then the head.  logprob_out: device fp32 [n_rows]. */
 ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_decode_batch *b,
@@ -382,15 +376,6 @@ ril_status ril_decode_step_logprobs(const ril_model *m, ril_kv *kv, const ril_de
 ril_status ril_lm_head_logprobs(const ril_model *m, int32_t rows, const void *z, int32_t ldz,
                                 const int32_t *target_ids, float *logprob_out, void *ws, size_t ws_bytes,
                                 void *stream);
-
-/* HBM read ceiling probe, for benchmarking only (like ril_set_policy): enqueue, on
- * `stream`, one grid-stride read of the first floor(bytes / 16) * 16 bytes of the device
- * buffer src (16-byte aligned) with the nontemporal policy, as the path's streaming
- * kernels read, folding the data into out[ril_hbm_read_probe_words()] (device uint32)
- * so the reads cannot be elided.  Time it with events to get the practical read rate.
- * Returns RIL_EINVAL on a null or misaligned pointer, RIL_EHIP on a launch error. */
-int32_t ril_hbm_read_probe_words(void);
-ril_status ril_hbm_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream);
 
 /* The rollout step without a caller workspace, for callers that cannot allocate device
  * memory (code under HIP-graph capture, tight serving loops, harnesses that forbid
@@ -445,37 +430,6 @@ void ril_graph_destroy(ril_graph *g);
  * for.  Needs no workspace, so n_seqs and total_tokens are not bounded by
  * max_tokens. */
 ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b, void *stream);
-
-/* Kernel trace, a profiling hook.  While enabled, every launch of the kernels
- * below is bracketed by two hipEvents recorded on the launch stream (the
- * kernels themselves are unchanged).  ril_trace_read waits for the events
- * recorded so far -- a host wait, so call it outside a timed loop -- and
- * returns the summed elapsed milliseconds and the launch count of one kernel
- * since the last ril_trace_enable.  Process-wide; not for concurrent use. */
-enum {
-  RIL_K_KV_WRITE = 0,     /* S5 */
-  RIL_K_ATTN_SPLIT = 1,   /* S8  decode split-KV attention */
-  RIL_K_ATTN_MERGE = 2,   /* S9  decode split merge */
-  RIL_K_ATTN_PREFILL = 3, /* S10 */
-  RIL_K_RMSNORM = 4,      /* S2/S3 */
-  RIL_K_GEMM = 5,         /* S4 */
-  RIL_K_LM_HEAD = 6,      /* S11 */
-  RIL_K_VOCAB_MERGE = 7,  /* S12 */
-  RIL_K_INDEXER = 8,      /* S6 */
-  RIL_K_TOPK = 9,         /* S7 */
-  RIL_K_SILU_MUL = 10,    /* the SwiGLU activation */
-  RIL_K_QUANT_ROWS = 11,  /* W8A8 head: block-FP8 activation quantization */
-  RIL_K_LM_HEAD_FP8 = 12, /* S11 in W8A8 block FP8 */
-  RIL_K_GEMM_FP8 = 13,    /* S4 in W8A8 block FP8 */
-  RIL_K_COUNT = 14
-};
-ril_status ril_trace_enable(int on);
-ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches);
-
-/* Debug/test view: the attention output of the last call on this thread's
- * workspace is bf16 [rows, Hq, D] at byte offset ril_ws_attn_offset(m) of
- * `ws`.  Lets tests compare attention outputs, not just logprobs. */
-size_t ril_ws_attn_offset(const ril_model *m);
 
 /* Thread-local message describing the last non-OK status. */
 const char *ril_last_error(void);

@@ -14,6 +14,7 @@
 
 #include "kernels.h"
 #include "ril.h"
+#include "ril_bench.h"
 
 using namespace ril;
 

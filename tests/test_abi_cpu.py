@@ -1,4 +1,4 @@
-"""CPU tests of the C ABI: the library loads, exports every symbol ril.h declares,
+"""CPU tests of the C ABI: the library loads, exports every symbol include/*.h declares,
 validates descriptions and batches on the host, and its page allocator behaves.
 No kernel is launched: every call here either fails validation (nothing enqueued)
 or is host-only."""
@@ -16,7 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "ril.h")).read()
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     return sorted(set(re.findall(r"\b(ril_[a-z0-9_]+)\s*\(", src)))
 
 

@@ -112,6 +112,39 @@ def test_page_placement_invariance():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("kv_dtype", [0, 1], ids=["bf16", "fp8"])
+def test_checkpoint_restore_into_a_new_pool_continues_bitwise(kv_dtype):
+    """The first steps after a restore equal the run that never stopped (Bitwise-consistent
+    RL post, section 2 on a correct backward and restore, and section 5's check of the
+    first step after a checkpoint load).  Mid-decode the cache is checkpointed as the
+    pool's bytes on the host plus each sequence's page list; a second session (its own
+    pool at other addresses, another page shuffle) takes every sequence's pages back
+    under new page ids; both sessions then decode the same next steps."""
+    from gqa_case import GQACase
+    kw = dict(ctx=SMALL_CTX, kv_dtype=kv_dtype, k_scale_exp=1 if kv_dtype else 0)
+    a = GQACase(SMALL, list(range(6)), shuffle_seed=11, **kw)
+    rows = MULTI
+    a.write_history("s", rows, 4)
+    for back in (4, 3):
+        a.decode_back("s", rows, back)
+    torch.cuda.synchronize()
+    host = a.sess.pool.cpu()
+    lists = {seq: list(ids) for seq, ids in a.sess.pages.items()}
+
+    b = GQACase(SMALL, list(range(6)), shuffle_seed=977, **kw)
+    pb = a.sess.page_bytes
+    assert b.sess.page_bytes == pb and b.sess.pool.data_ptr() != a.sess.pool.data_ptr()
+    for seq, ids in lists.items():
+        b.sess.ensure(seq, len(ids) * 16)
+        for old, new in zip(ids, b.sess.pages[seq]):
+            b.sess.pool[new * pb:(new + 1) * pb].copy_(host[old * pb:(old + 1) * pb])
+    assert any(b.sess.pages[seq] != ids for seq, ids in lists.items())
+    for back in (2, 1):
+        x = _bits(a.decode_back("s", rows, back))
+        y = _bits(b.decode_back("s", rows, back))
+        assert np.array_equal(x, y), back
+
+
 def test_mixed_batch_prefill_with_decode_rows():
     """Decode rows inside a prefill call (one-token sequences) equal the decode path."""
     c = _case()

@@ -111,3 +111,42 @@ def test_strided_operands_and_residual_in_place():
     ril.ril_proj_bf16(a, w, res, residual=res)
     torch.cuda.synchronize()
     assert torch.equal(res.view(torch.int16), want.view(torch.int16))
+
+
+def test_output_rounding_is_nearest_even_on_ties():
+    """The projection's bf16 store rounds to nearest, ties to even (Bitwise-consistent RL
+    post, section 4.4, condition 1), checked through the GEMM itself.  Each output is
+    x + s*y*2^-j for bf16 x, y with y a few half-units of x's last place: two products
+    whose fp32 sum is exact, so the fp32 accumulator holds the exact value and the bf16
+    store alone decides the bits.  Many of these sums fall exactly halfway between two
+    bf16 values (both parities of x's last bit); two rows check the tie at the top of
+    the range (bf16's largest value plus half its spacing rounds to infinity) and the
+    value just below it.  Expected: the oracle's projection, bf16 of the exact sum."""
+    rng = np.random.default_rng(8)
+    M, K = 300, 1024  # M > 256: the 256 x 256 kernel; its first 256 / 64 / 16 rows: the others
+    E = rng.integers(-100, 101, M)
+    x = rng.choice([-1.0, 1.0], M) * (1 + rng.integers(0, 128, M) / 128.0) * np.ldexp(1.0, E)
+    y = rng.choice([-1.0, 1.0], M) * (1 + rng.integers(0, 8, M) / 8.0) * np.ldexp(1.0, E - 8 + rng.integers(0, 3, M))
+    x[-2:] = float.fromhex("0x1.fep127")          # bf16's largest finite value
+    y[-2:] = [2.0 ** 119, 2.0 ** 118]            # half its spacing (a tie), a quarter
+    a = np.zeros((M, K))
+    a[:, 0], a[:, 1] = x, y
+    w = np.zeros((16, K))
+    w[:, 0] = 1.0
+    w[:, 1] = np.where(np.arange(16) < 8, 1.0, -1.0) * np.ldexp(1.0, -(np.arange(16) % 8))
+    assert np.array_equal(oracle.bf16(a), a) and np.array_equal(oracle.bf16(w), w)
+    exact = a @ w.T
+    _, ex = np.frexp(exact)
+    frac = np.abs(exact) / np.ldexp(1.0, ex - 8) % 1.0
+    tie = frac == 0.5
+    assert tie.sum() >= 150                                # plenty of exact ties
+    want = oracle.projection(a, w)
+    assert np.isinf(want[-2, 0]) and want[-1, 0] == x[-1]
+    up = np.abs(want[tie]) > np.abs(exact[tie])
+    assert up.sum() >= 50 and (~up).sum() >= 50            # both ways to the even value
+    dev = lambda v: torch.from_numpy(v).to(torch.bfloat16).cuda()  # noqa: E731
+    A, W = dev(a), dev(w)
+    want_bits = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy()
+    for m in (M, 256, 64, 16):
+        got = _bits(_run(A[:m].contiguous(), W))
+        assert np.array_equal(got, want_bits[:m]), m
