@@ -132,8 +132,9 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
     return fail(RIL_EINVAL, "model_create: the W8A8 lm-head needs d_head a multiple of 128 (%d)", d.d_head);
   if (d.kv_dtype != RIL_KV_BF16 && d.kv_dtype != RIL_KV_FP8_E4M3)
     return fail(RIL_EINVAL, "model_create: kv_dtype %d", d.kv_dtype);
-  if (d.kv_dtype == RIL_KV_FP8_E4M3 && mla)
-    return fail(RIL_EUNSUPPORTED, "model_create: the FP8 KV cache is for GQA");
+  if (d.kv_dtype == RIL_KV_FP8_E4M3 && mla && d.k_scale_exp != d.v_scale_exp)
+    return fail(RIL_EINVAL, "model_create: an FP8 MLA latent has one scale (k_scale_exp %d != v_scale_exp %d)",
+                d.k_scale_exp, d.v_scale_exp);
   if (d.k_scale_exp < -32 || d.k_scale_exp > 32 || d.v_scale_exp < -32 || d.v_scale_exp > 32)
     return fail(RIL_EINVAL, "model_create: k/v_scale_exp %d/%d (in [-32, 32])", d.k_scale_exp, d.v_scale_exp);
   if (d.kv_dtype == RIL_KV_BF16 && (d.k_scale_exp || d.v_scale_exp))
@@ -172,8 +173,9 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->sparse = sparse;
   if (sparse)  // split count of the selection, not of the context
     m->max_splits = (std::min(d.max_ctx, d.topk) + d.split_tokens - 1) / d.split_tokens;
-  m->page_bytes = mla ? (size_t)16 * (d.head_dim + d.rope_dim) * 2 + (sparse ? (size_t)16 * d.index_dim * 4 : 0)
-                      : (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * (d.kv_dtype == RIL_KV_FP8_E4M3 ? 1 : 2);
+  const size_t kv_elem = d.kv_dtype == RIL_KV_FP8_E4M3 ? 1 : 2;  // bytes per cached value
+  m->page_bytes = mla ? (size_t)16 * (d.head_dim + d.rope_dim) * kv_elem + (sparse ? (size_t)16 * d.index_dim * 4 : 0)
+                      : (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * kv_elem;
   const size_t R = (size_t)std::max(d.max_rows, d.max_tokens);
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
   size_t o = 0;
@@ -723,7 +725,8 @@ static ril_status run_mla_write(const ril_model *m, ril_kv *kv, const bf16_t *c,
                                 const int32_t *ctx_len, const int32_t *page_table, int page_stride, hipStream_t st) {
   const ril_model_desc &d = m->d;
   MlaKvWriteArgs a{c, d.head_dim + d.rope_dim, m->sparse ? kidx : nullptr, n_tok, mode, cu, start_pos, n_seqs,
-                   ctx_len, page_table, page_stride, (bf16_t *)kv->pool, (int)(m->page_bytes / 2), kv->n_pages};
+                   ctx_len, page_table, page_stride, (bf16_t *)kv->pool, (int)(m->page_bytes / 2), kv->n_pages,
+                   m->kv_fp8, 1.0f / m->k_scale};
   RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(a, st));
   return RIL_OK;
 }
@@ -743,7 +746,8 @@ static ril_status run_mla(const ril_model *m, ril_kv *kv, const bf16_t *q, const
     if (m->sparse) {
       sel = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + m->off_sel);
       IndexerArgs ia{q_index, mode, r0, n, ctx_len, cu, start_pos, n_seqs, page_table, page_stride,
-                     (const bf16_t *)kv->pool, page_elems, kv->n_pages, ctx_bound, wsf(ws, m->off_scores),
+                     (const bf16_t *)kv->pool, page_elems, kv->n_pages, ctx_bound,
+                     16 * (d.head_dim + d.rope_dim) * (m->kv_fp8 ? 1 : 2) / 2, wsf(ws, m->off_scores),
                      d.max_ctx, d.topk, sel, sel_out};
       RIL_LAUNCH(RIL_K_INDEXER, launch_indexer(ia, st));
       RIL_LAUNCH(RIL_K_TOPK, launch_topk(ia, st));
@@ -757,7 +761,7 @@ static ril_status run_mla(const ril_model *m, ril_kv *kv, const bf16_t *q, const
     MlaAttnArgs a{q, mode, r0, n, ctx_len, cu, start_pos, n_seqs, page_table, page_stride,
                   (const bf16_t *)kv->pool, page_elems, kv->n_pages, d.n_q_heads, split, ctx_bound,
                   max_splits, sel, d.topk, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml),
-                  wsb(ws, m->off_attn)};
+                  wsb(ws, m->off_attn), m->kv_fp8, m->k_scale};
     RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_mla_split(a, st));
     RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_mla_merge(a, st));
   }

@@ -20,7 +20,6 @@
 namespace ril {
 
 constexpr int kIdxHeads = 64, kIdxDim = 128;
-constexpr int kIdxKeyOffset = kPage * 576;  // bf16 elements: the keys follow the latent block
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkMax = 4096;
 
@@ -45,7 +44,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const float *__restrict__ q, int mode, int row0, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
     const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool, int page_elems,
-    int n_pages, int ctx_bound, float *__restrict__ scores, int score_stride) {
+    int n_pages, int ctx_bound, int key_off, float *__restrict__ scores, int score_stride) {
   const int r = blockIdx.y;
   int seq, ctx;
   long qrow;
@@ -58,7 +57,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     *out = __builtin_nanf("");
     return;
   }
-  const float *kp = reinterpret_cast<const float *>(pool + (long)pid * page_elems + kIdxKeyOffset) + (s % kPage) * kIdxDim;
+  const float *kp = reinterpret_cast<const float *>(pool + (long)pid * page_elems + key_off) + (s % kPage) * kIdxDim;
   float k[kIdxDim];
 #pragma unroll
   for (int i = 0; i < kIdxDim / 4; ++i) {
@@ -209,7 +208,7 @@ hipError_t launch_indexer(const IndexerArgs &a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   dim3 grid((a.ctx_bound + 255) / 256, a.n_rows);
   hipLaunchKernelGGL(indexer_kernel, grid, dim3(256), 0, st, a.q, a.mode, a.row0, a.ctx_len, a.cu, a.start_pos,
-                     a.n_seqs, a.page_table, a.page_stride, a.pool, a.page_elems, a.n_pages, a.ctx_bound, a.scores,
+                     a.n_seqs, a.page_table, a.page_stride, a.pool, a.page_elems, a.n_pages, a.ctx_bound, a.key_off, a.scores,
                      a.score_stride);
   return hipGetLastError();
 }

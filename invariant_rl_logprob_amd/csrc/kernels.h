@@ -139,6 +139,8 @@ struct MlaKvWriteArgs {
   int page_stride;
   bf16_t *pool;
   int page_elems, n_pages;
+  bool fp8;         // the latent is stored as E4M3 codes of c * inv_scale (token-major)
+  float inv_scale;  // 2^-scale_exp
 };
 
 struct MlaAttnArgs {
@@ -155,6 +157,8 @@ struct MlaAttnArgs {
   float cscale;
   float *part_o, *part_ml;
   bf16_t *out;  // [rows or tokens, H, 512]
+  bool fp8;     // FP8 latent pages, read back as code * scale
+  float scale;  // 2^scale_exp
 };
 
 struct IndexerArgs {
@@ -166,6 +170,7 @@ struct IndexerArgs {
   int page_stride;
   const bf16_t *pool;
   int page_elems, n_pages, ctx_bound;
+  int key_off;    // bf16 elements from a page's start to its fp32 indexer keys
   float *scores;  // [n_rows, score_stride] (rows of this launch)
   int score_stride;
   int topk;

@@ -51,16 +51,30 @@ constexpr int kMlaThreads = 512;              // 4 pairs of waves x 16 heads (H 
 // conflicts); the score reads stay conflict-free.
 __device__ __forceinline__ int mla_swz(int u) { return u ^ (((u >> 4) & 1) << 3); }
 
+// FP8 latent pages (Bitwise-consistent RL post, section 4.2: FP8 storage, one write path,
+// one dequantizing read for every phase): a page's latent block is 16 x 576 E4M3 codes,
+// token-major (code of (t, d) at byte 576 t + d, 9216 bytes), each the code of
+// c * 2^-s (nearest even, magnitudes past 448 saturating, NaN kept with its sign) for the
+// model's one latent scale exponent s; the sparse kind's fp32 indexer keys follow at byte
+// 9216.  Every read takes code * 2^s, which bf16 holds exactly (|s| <= 32 keeps every
+// value a normal bf16), so the attention arithmetic is the bf16 path's, over those
+// values.  Token-major keeps each token's codes in whole 16-byte units, so the sparse
+// kind gathers a selected token with 16-byte copies.
+constexpr int kMla8Page = kPage * kMlaDqk;  // 9216 bytes of codes per page
+constexpr int kMla8Tile = kTile * kMlaDqk;  // 36864 bytes: one tile's codes
+
 // ---------------------------------------------------------------------------
-// S5 for MLA: one thread per (token, 16-byte unit): 72 latent units, then (sparse)
-// 32 units of the fp32 indexer key at page + 9216 elements + 256 * t elements.
+// S5 for MLA: one thread per (token, 16-byte unit) of the page: 72 latent units (bf16,
+// K layout) or 36 (FP8 codes, token-major), then (sparse) 32 units of the fp32 indexer
+// key, token t's at byte latent_bytes + 512 t of the page.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mla_kv_write_kernel(
     const bf16_t *__restrict__ c, int row_stride, const float *__restrict__ kidx, int n_tok, int mode,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ page_table, int page_stride,
-    bf16_t *__restrict__ pool, int page_elems, int n_pages) {
-  const int per_tok = kMlaDqk / 8 + (kidx ? 32 : 0);
+    bf16_t *__restrict__ pool, int page_elems, int n_pages, bool fp8, float inv_scale) {
+  const int n_lat = fp8 ? kMlaDqk / 16 : kMlaDqk / 8;
+  const int per_tok = n_lat + (kidx ? 32 : 0);
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)n_tok * per_tok) return;
   const int j = (int)(idx / per_tok);
@@ -77,12 +91,27 @@ __global__ __launch_bounds__(256) void mla_kv_write_kernel(
   const int pid = page_table[(long)seq * page_stride + pos / kPage];
   if ((unsigned)pid >= (unsigned)n_pages) return;
   bf16_t *page = pool + (long)pid * page_elems;
+  uint8_t *page8 = reinterpret_cast<uint8_t *>(page);
   const int t = pos % kPage;
-  if (u < kMlaDqk / 8) {
-    st16(page + k_page_offset(t, u * 8), ld16(c + (long)j * row_stride + u * 8));
+  if (u < n_lat) {
+    const bf16_t *src = c + (long)j * row_stride;
+    if (!fp8) {
+      st16(page + k_page_offset(t, u * 8), ld16(src + u * 8));
+    } else {
+      const u32x4 a = ld16(src + u * 16), b = ld16(src + u * 16 + 8);
+      u32x4 codes;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = w < 2 ? a[2 * w] : b[2 * w - 4], y = w < 2 ? a[2 * w + 1] : b[2 * w - 3];
+        const uint32_t lo = fp8_codes2(bf2f((bf16_t)(x & 0xffffu)) * inv_scale, bf2f((bf16_t)(x >> 16)) * inv_scale);
+        const uint32_t hi = fp8_codes2(bf2f((bf16_t)(y & 0xffffu)) * inv_scale, bf2f((bf16_t)(y >> 16)) * inv_scale);
+        codes[w] = lo | (hi << 16);
+      }
+      st16(page8 + t * kMlaDqk + u * 16, codes);
+    }
   } else {
-    const int w = u - kMlaDqk / 8;  // 4 floats per unit
-    st16(page + kMlaPage + t * 256 + w * 8, ld16(kidx + (long)j * 128 + w * 4));
+    const int w = u - n_lat;  // 4 floats per unit
+    st16(page8 + (fp8 ? kMla8Page : 2 * kMlaPage) + t * 512 + w * 16, ld16(kidx + (long)j * 128 + w * 4));
   }
 }
 
@@ -412,6 +441,214 @@ __global__ __launch_bounds__(512) void mla_split_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// S8 over FP8 latent pages: the same grid, waves, tile routines and order as
+// mla_split_kernel, with the tile dequantized into LDS before it is used.  Each tile's
+// codes (36 KB) are copied two tiles ahead into a 2-slot ring by direct-to-LDS loads (36
+// pieces of 1 KB: wave w copies pieces w, w + 8, ..), then all 512 threads turn them
+// into the bf16 tile in the K layout and swizzle mla_split_kernel reads (code * 2^s,
+// exact), and the scores and values run on it unchanged: the bits are those of the bf16
+// kernel over the cache's values.  Per tile: wait for this wave's pieces of the tile,
+// barrier (the codes are in, every wave is done with the previous bf16 tile),
+// dequantize, barrier (the bf16 tile is in, the codes' slot is free), copy tile t + 2
+// into that slot, compute.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x2 lds_rd64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+template <bool SPARSE>
+__global__ __launch_bounds__(512) void mla_split_fp8_kernel(
+    const bf16_t *__restrict__ q, int mode, int row0, const int32_t *__restrict__ ctx_len,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
+    const int32_t *__restrict__ page_table, int page_stride, const uint8_t *__restrict__ pool, int page_bytes,
+    int n_pages, int H, const int32_t *__restrict__ sel, int topk, int split_tokens, int ctx_bound,
+    float cscale, float scale, float *__restrict__ part_o, float *__restrict__ part_ml, int max_splits) {
+  __shared__ __attribute__((aligned(16))) bf16_t kt[4 * kMlaSlot];   // the tile, dequantized
+  __shared__ __attribute__((aligned(16))) uint8_t k8[2][kMla8Tile];  // codes of the next tiles
+  __shared__ u32x4 xp[4][2][64];
+  __shared__ float xa[4][64];
+  const int split = blockIdx.x, hg = blockIdx.y, r = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, r16 = lane & 15;
+  const int pair = wave & 3, half = wave >> 2;
+  int seq, ctx;
+  long qrow;
+  mla_row(mode, r, row0, ctx_len, cu, start_pos, n_seqs, seq, ctx, qrow);
+  const int n_all = SPARSE ? min(ctx, topk) : ctx;
+  const int s0 = split * split_tokens;
+  if (ctx < 1 || ctx > ctx_bound || s0 >= n_all) return;  // uniform over the workgroup
+  const int s1 = min(n_all, s0 + split_tokens);
+  const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
+  const int32_t *pt = page_table + (long)seq * page_stride;
+  const int32_t *rsel = SPARSE ? sel + (long)r * topk : nullptr;
+  bool bad = false;
+  int pidA = 0, pidB = 0;  // dense: page ids of the split (lane i: page s0/16 + i, +64)
+  int pos_c = -1, pid_c = 0, pos_n = -1;  // sparse, per lane = entry: the tile to copy next, the one after
+  auto entry_pos = [&](int t) {
+    const int e = s0 + t * kTile + lane;
+    int p = -1;
+    if (t < n_tiles && e < n_all) {
+      p = rsel[e];
+      if (p < 0 || p >= ctx) {
+        bad = true;
+        p = -1;
+      }
+    }
+    return p;
+  };
+  auto entry_pid = [&](int p) {
+    if (p < 0) return 0;
+    const int id = pt[p / kPage];
+    const bool b = (unsigned)id >= (unsigned)n_pages;
+    bad |= b;
+    return b ? 0 : id;
+  };
+  if (!SPARSE) {
+    const int first = s0 / kPage, last = (ctx - 1) / kPage;
+    const int a = first + lane, b = first + 64 + lane;
+    pidA = pt[min(a, last)];
+    pidB = pt[min(b, last)];
+    bad = (a <= last && (unsigned)pidA >= (unsigned)n_pages) || (b <= last && (unsigned)pidB >= (unsigned)n_pages);
+    pidA = (a <= last && (unsigned)pidA < (unsigned)n_pages) ? pidA : 0;
+    pidB = (b <= last && (unsigned)pidB < (unsigned)n_pages) ? pidB : 0;
+  } else {
+    pos_c = entry_pos(0);
+    pid_c = entry_pid(pos_c);
+  }
+  const int head = 64 * hg + 16 * pair + r16;
+  const bool col_ok = head < H;
+  bf16x8 qop[kMlaDqk / 32];
+  if (half == 0) mla_load_q(qop, q, qrow, H, head, col_ok);
+
+  // copy tile t's codes into slot t & 1: piece i (1 KB) = bytes 1024 i .. of the tile;
+  // dense: page i / 9 of the tile, its bytes 1024 (i % 9) ..; sparse: 16-byte unit
+  // u = 64 i + lane is chunk u % 36 of entry u / 36
+  constexpr int kPieces8 = kMla8Tile / 1024;  // 36
+  auto copy_tile = [&](int t) {
+    uint8_t *buf = &k8[t & 1][0];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int i = wave + 8 * k;
+      if (k < 4 || wave < kPieces8 - 32) {
+        const uint8_t *src;
+        if (!SPARSE) {
+          const int idx = 4 * t + i / 9;  // page index within the split (< 128), uniform
+          const int pid = idx < 64 ? __builtin_amdgcn_readlane(pidA, idx) : __builtin_amdgcn_readlane(pidB, idx - 64);
+          src = pool + (long)pid * page_bytes + (i % 9) * 1024 + lane * 16;
+        } else {
+          const int u = 64 * i + lane, e = u / 36, ch = u - 36 * e;
+          const int p = __shfl(pos_c, e, 64), id = __shfl(pid_c, e, 64);
+          src = pool + (long)id * page_bytes + (p >= 0 ? (p % kPage) * kMlaDqk + ch * 16 : 0);
+        }
+        __builtin_amdgcn_global_load_lds((void *)src, (void *)(buf + i * 1024), 16, 0, 0);
+      }
+    }
+  };
+  // dequantize slot t & 1 into kt: bf16 unit v = tid + 512 k of the tile (page slot
+  // v / 1152, unit v % 1152 of its K layout) holds dims d0 .. d0 + 7 of token t of that
+  // slot, read as 8 codes at byte 576 (16 slot + t) + d0
+  auto dequant = [&](int t) {
+    // the thread index through an opaque copy: the addresses are recomputed per tile
+    // instead of being held in registers across the loop
+    uint32_t tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const uint32_t src0 = lds_addr(&k8[t & 1][0]), dst0 = lds_addr(kt);
+    typedef float f2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int k0 = 0; k0 < 9; k0 += 3) {
+      u32x2 c[3];
+      uint32_t dst[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int v = tid + 512 * (k0 + k), ps = v / 1152, vv = v - 1152 * ps;
+        int tt, d0;
+        mla_unit_td(vv, tt, d0);
+        c[k] = lds_rd64(src0 + (16 * ps + tt) * kMlaDqk + d0);
+        dst[k] = dst0 + ps * (2 * kMlaSlot) + 16 * mla_swz(vv);
+      }
+      lds_wait<0>();
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        settle(c[k]);
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(c[k][h], false), b = __builtin_amdgcn_cvt_pk_f32_fp8(c[k][h], true);
+          w[2 * h] = pack2(a[0] * scale, a[1] * scale);
+          w[2 * h + 1] = pack2(b[0] * scale, b[1] * scale);
+        }
+        lds_wr128(dst[k], w);
+      }
+    }
+  };
+  const uint32_t xp_lane = lds_addr(&xp[pair][0][0]) + 16 * lane, xa_lane = lds_addr(&xa[pair][0]) + 4 * lane;
+  float m = neg_inf(), l = 0.f;
+  f32x4 o[kMlaDv / 32];
+#pragma unroll
+  for (int b = 0; b < kMlaDv / 32; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  copy_tile(0);
+  if (SPARSE) {
+    pos_c = entry_pos(1);
+    pid_c = entry_pid(pos_c);
+  }
+  if (n_tiles > 1) copy_tile(1);
+  if (SPARSE) pos_n = entry_pos(2);
+  for (int t = 0; t < n_tiles; ++t) {
+    // this wave's pieces of tile t have landed (those of tile t + 1, issued later, may not)
+    if (t + 1 < n_tiles) {
+      if (wave < kPieces8 - 32) wait_vmem<5>(); else wait_vmem<4>();
+    } else {
+      wait_vmem<0>();
+    }
+    asm volatile("s_barrier" ::: "memory");
+    if (SPARSE && t + 2 < n_tiles) pid_c = entry_pid(pos_n);  // tile t + 2's pages, used below
+    dequant(t);
+    lds_barrier();  // the bf16 tile is complete; slot t & 1 is free
+    if (t + 2 < n_tiles) {
+      if (SPARSE) pos_c = pos_n;
+      copy_tile(t + 2);
+      if (SPARSE) pos_n = entry_pos(t + 3);
+    }
+    const int t0 = s0 + t * kTile;
+    bf16x8 pop[2];
+    float alpha;
+    if (half == 0) {
+      f32x4 sc[4];
+      mla_tile_scores(sc, kt, qop);
+      float m_new, l_new;
+      tile_softmax(sc, t0, n_all - 1, cscale, m, l, pop, alpha, m_new, l_new);
+      m = m_new;
+      l = l_new;
+      lds_wr128(xp_lane, __builtin_bit_cast(u32x4, pop[0]));
+      lds_wr128(xp_lane + 1024, __builtin_bit_cast(u32x4, pop[1]));
+      lds_wr32(xa_lane, alpha);
+    }
+    lds_barrier();
+    if (half == 1) {
+      u32x4 p0 = lds_rd128<0>(xp_lane), p1 = lds_rd128<1024>(xp_lane);
+      int a = lds_rd32<0>(xa_lane);
+      lds_wait<0>();
+      settle(p0);
+      settle(p1);
+      settle(a);
+      pop[0] = as_bf16x8(p0);
+      pop[1] = as_bf16x8(p1);
+      alpha = __builtin_bit_cast(float, a);
+    }
+    const int n_live = n_all - t0;
+    if (n_live >= kTile)
+      mla_tile_values<false>(o, kt, half, pop, alpha, n_live);
+    else
+      mla_tile_values<true>(o, kt, half, pop, alpha, n_live);
+  }
+  bad = __syncthreads_or(bad);
+  if (bad) l = __builtin_nanf("");
+  if (!col_ok) return;
+  mla_store_partial(part_o, part_ml, ((long)r * H + head) * max_splits + split, half, o, m, l);
+}
+
+// ---------------------------------------------------------------------------
 // S9 for MLA: grid (H, rows), one wave; writes out[qrow][h][0..511].  The number of
 // splits is that of the row's positions (dense) or of its selection (sparse).
 // ---------------------------------------------------------------------------
@@ -440,17 +677,34 @@ __global__ __launch_bounds__(64) void mla_merge_kernel(
 // ---------------------------------------------------------------------------
 
 hipError_t launch_mla_kv_write(const MlaKvWriteArgs &a, hipStream_t st) {
-  const long total = (long)a.n_tok * (kMlaDqk / 8 + (a.kidx ? 32 : 0));
+  const long total = (long)a.n_tok * ((a.fp8 ? kMlaDqk / 16 : kMlaDqk / 8) + (a.kidx ? 32 : 0));
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(mla_kv_write_kernel, dim3(blocks), dim3(256), 0, st, a.c, a.row_stride, a.kidx, a.n_tok,
                      a.mode, a.cu, a.start_pos, a.n_seqs, a.ctx_len, a.page_table, a.page_stride, a.pool,
-                     a.page_elems, a.n_pages);
+                     a.page_elems, a.n_pages, a.fp8, a.inv_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_mla_split(const MlaAttnArgs &a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
+  if (a.fp8) {
+    if (!a.sel && a.split_tokens > 2048) return hipErrorInvalidValue;  // two 64-page id registers
+    const int n_bound = a.sel ? std::min(a.ctx_bound, a.topk) : a.ctx_bound;
+    dim3 grid((n_bound + a.split_tokens - 1) / a.split_tokens, a.H / 64, a.n_rows);
+    const uint8_t *pool = reinterpret_cast<const uint8_t *>(a.pool);
+    if (a.sel)
+      hipLaunchKernelGGL(mla_split_fp8_kernel<true>, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0,
+                         a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, pool,
+                         2 * a.page_elems, a.n_pages, a.H, a.sel, a.topk, a.split_tokens, a.ctx_bound, a.cscale,
+                         a.scale, a.part_o, a.part_ml, a.max_splits);
+    else
+      hipLaunchKernelGGL(mla_split_fp8_kernel<false>, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0,
+                         a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, pool,
+                         2 * a.page_elems, a.n_pages, a.H, nullptr, 0, a.split_tokens, a.ctx_bound, a.cscale,
+                         a.scale, a.part_o, a.part_ml, a.max_splits);
+    return hipGetLastError();
+  }
   if (a.sel) {
     const int n_bound = std::min(a.ctx_bound, a.topk);
     dim3 grid((n_bound + a.split_tokens - 1) / a.split_tokens, a.H / 64, a.n_rows);

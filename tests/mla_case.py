@@ -16,7 +16,7 @@ from invariant_rl_logprob_amd.session import Session
 class MLACase:
     def __init__(self, w: wl.MLADecode, rows: Sequence[int], *, ctx: Sequence[int] = None, device="cuda",
                  shuffle_seed=4321, copies=2, split_tokens=2048, max_rows=None, max_tokens=None, head=None,
-                 proj_dtype=0):
+                 proj_dtype=0, kv_dtype=0, scale_exp=0):
         self.w = w
         self.rows = list(rows)
         self.data: Dict[int, dict] = {}
@@ -32,8 +32,10 @@ class MLACase:
                             max_tokens=max_tokens or len(self.rows) * w.recompute_tokens, max_ctx=max_ctx,
                             pool_pages=pages, softmax_scale=self.scale, rms_eps=w.rms_eps,
                             shuffle_seed=shuffle_seed, split_tokens=split_tokens, attn_kind=RIL_ATTN_MLA,
-                            proj_dtype=proj_dtype, device=device)
+                            proj_dtype=proj_dtype, kv_dtype=kv_dtype, k_scale_exp=scale_exp,
+                            v_scale_exp=scale_exp, device=device)
         self.proj_w8a8 = proj_dtype == 1
+        self.fp8_exp = scale_exp if kv_dtype else None  # FP8 latent cache: its scale exponent
 
     def ctx(self, r):
         return self.data[r]["ctx"]
@@ -85,12 +87,20 @@ class MLACase:
         n = rows * self.w.n_heads * self.w.kv_rank
         return self.sess.ws[off: off + 2 * n].view(torch.bfloat16).view(rows, self.w.n_heads, self.w.kv_rank)
 
+    def cached(self, c):
+        """The latent rows as the cache gives them back: the bf16 values, or with an FP8
+        cache the oracle's E4M3 round trip of them at the cache's scale."""
+        if self.fp8_exp is None:
+            return c
+        import oracle
+        return oracle.kv_fp8_roundtrip(c.float().cpu().numpy(), self.fp8_exp)
+
     def oracle_row(self, r, back: int = 1, with_logprob=True):
         import oracle
         d = self.data[r]
         R = d["q"].shape[0]
         p = d["ctx"] - back
-        o = oracle.mla_row_attention(d["q"][R - back], d["c"][: p + 1], self.scale, self.w.kv_rank)
+        o = oracle.mla_row_attention(d["q"][R - back], self.cached(d["c"][: p + 1]), self.scale, self.w.kv_rank)
         lp = None
         if with_logprob:
             lp = oracle.head_logprob(o, self.head["w_lm"].float().cpu().numpy(), int(d["target"][R - back]),

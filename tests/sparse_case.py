@@ -15,7 +15,8 @@ from invariant_rl_logprob_amd.session import Session
 
 class SparseCase:
     def __init__(self, w: wl.SparseMLADecode, rows: Sequence[int], *, ctx: Sequence[int] = None, device="cuda",
-                 shuffle_seed=777, copies=2, split_entries=256, max_rows=None, max_tokens=None, head=None):
+                 shuffle_seed=777, copies=2, split_entries=256, max_rows=None, max_tokens=None, head=None,
+                 kv_dtype=0, scale_exp=0):
         self.w = w
         self.rows = list(rows)
         self.data: Dict[int, dict] = {}
@@ -34,7 +35,9 @@ class SparseCase:
                             max_tokens=max_tokens or len(self.rows) * w.recompute_tokens, max_ctx=max_ctx,
                             pool_pages=pages, softmax_scale=self.scale, rms_eps=w.rms_eps,
                             shuffle_seed=shuffle_seed, split_tokens=split_entries,
-                            attn_kind=RIL_ATTN_MLA_SPARSE, device=device)
+                            attn_kind=RIL_ATTN_MLA_SPARSE, kv_dtype=kv_dtype, k_scale_exp=scale_exp,
+                            v_scale_exp=scale_exp, device=device)
+        self.fp8_exp = scale_exp if kv_dtype else None  # FP8 latent cache: its scale exponent
 
     def ctx(self, r):
         return self.data[r]["ctx"]
@@ -91,6 +94,14 @@ class SparseCase:
         n = rows * self.w.n_heads * self.w.kv_rank
         return self.sess.ws[off: off + 2 * n].view(torch.bfloat16).view(rows, self.w.n_heads, self.w.kv_rank)
 
+    def cached(self, c):
+        """The latent rows as the cache gives them back: the bf16 values, or with an FP8
+        cache the oracle's E4M3 round trip of them at the cache's scale."""
+        if self.fp8_exp is None:
+            return c
+        import oracle
+        return oracle.kv_fp8_roundtrip(c.float().cpu().numpy(), self.fp8_exp)
+
     def oracle_row(self, r, back: int = 1, with_logprob=True):
         """(lp, attention output, fp32 indexer scores, selection) of row r at position ctx - back."""
         import oracle
@@ -99,7 +110,8 @@ class SparseCase:
         p = d["ctx"] - back
         scores = oracle.indexer_scores_fp32(d["q_index"][R - back], d["k_index"][: p + 1])
         sel = oracle.topk_select(scores, self.w.topk, tie="lowest")
-        o = oracle.sparse_mla_row_attention(d["q"][R - back], d["c"][: p + 1], sel, self.scale, self.w.kv_rank)
+        o = oracle.sparse_mla_row_attention(d["q"][R - back], self.cached(d["c"][: p + 1]), sel, self.scale,
+                                            self.w.kv_rank)
         lp = None
         if with_logprob:
             lp = oracle.head_logprob(o, self.head["w_lm"].float().cpu().numpy(), int(d["target"][R - back]),

@@ -64,9 +64,17 @@ def test_fp8_kv_cache_descriptor():
     ril.ril_model_destroy(m)
     mla = dict(attn_kind=ril.RIL_ATTN_MLA, n_q_heads=128, n_kv_heads=1, head_dim=512, rope_dim=64,
                d_head=65536, split_tokens=2048)
+    # the MLA latent in FP8: 16 x 576 codes per page (the sparse kind adds its fp32 keys)
+    m = ril.ril_model_create(_desc(kv_dtype=ril.RIL_KV_FP8_E4M3, k_scale_exp=2, v_scale_exp=2, **mla))
+    assert ril.ril_kv_page_bytes(m) == 16 * 576
+    ril.ril_model_destroy(m)
+    sp = dict(mla, attn_kind=ril.RIL_ATTN_MLA_SPARSE, index_heads=64, index_dim=128, topk=2048, split_tokens=256)
+    m = ril.ril_model_create(_desc(kv_dtype=ril.RIL_KV_FP8_E4M3, **sp))
+    assert ril.ril_kv_page_bytes(m) == 16 * 576 + 16 * 128 * 4
+    ril.ril_model_destroy(m)
     for b in (dict(kv_dtype=2), dict(kv_dtype=-1), dict(kv_dtype=ril.RIL_KV_FP8_E4M3, k_scale_exp=33),
               dict(kv_dtype=ril.RIL_KV_FP8_E4M3, v_scale_exp=-40), dict(k_scale_exp=1),
-              dict(kv_dtype=ril.RIL_KV_FP8_E4M3, **mla)):
+              dict(kv_dtype=ril.RIL_KV_FP8_E4M3, k_scale_exp=1, v_scale_exp=2, **mla)):  # one latent scale
         with pytest.raises(ril.RilError):
             ril.ril_model_create(_desc(**b))
         assert ril.ril_last_error()
