@@ -497,7 +497,7 @@ def bench_gqa(args, fp8=False, lm8=False):
 # absorbed MLA decode, 128 rows
 # ---------------------------------------------------------------------------
 
-def bench_mla(args):
+def bench_mla(args, fp8=False):
     import numpy as np
     import torch
     import workloads as wl
@@ -507,7 +507,7 @@ def bench_mla(args):
     rows = list(range(w.rows))
     t0 = time.time()
     case = MLACase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_rows=w.rows,
-                   max_tokens=w.rows * w.recompute_tokens)
+                   max_tokens=w.rows * w.recompute_tokens, kv_dtype=1 if fp8 else 0)
     ctx = [case.ctx(r) for r in rows]
     log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
     dec, diff = diff_check(case, rows)
@@ -521,13 +521,13 @@ def bench_mla(args):
                                      dec[:, -1].cpu().view(torch.int32).numpy()))
 
     H = w.n_heads
-    kv_bytes = sum(ctx) * (w.kv_rank + w.rope_dim) * 2
+    kv_bytes = sum(ctx) * (w.kv_rank + w.rope_dim) * (1 if fp8 else 2)
     flops = sum(ctx) * H * 2 * ((w.kv_rank + w.rope_dim) + w.kv_rank)
     split_us, merge_us = kern["attn_split"]["avg_us"], kern["attn_merge"]["avg_us"]
     attn_gbps = kv_bytes / ((split_us + merge_us) * 1e-6) / 1e9
     split_gbps = kv_bytes / (split_us * 1e-6) / 1e9
     tflops = flops / (split_us * 1e-6) / 1e12
-    roof = roofline_hbm("mla_split", split_gbps, kv_bytes, split_us)
+    roof = roofline_hbm("mla_split_fp8" if fp8 else "mla_split", split_gbps, kv_bytes, split_us)
     roof["mfma"] = {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": int(flops)}
 
@@ -541,7 +541,8 @@ def bench_mla(args):
         t1 = time.time()
         got = []
         for r in sample:
-            o = oracle.mla_row_attention(host[r]["q"][-1], host[r]["c"][: case.ctx(r)], case.scale, w.kv_rank)
+            o = oracle.mla_row_attention(host[r]["q"][-1], case.cached(host[r]["c"][: case.ctx(r)]), case.scale,
+                                         w.kv_rank)
             got.append(oracle.head_logprob(o, w_lm_cpu, int(host[r]["target"][-1]), w.rms_eps, w_o=w_o_cpu))
         secs = time.time() - t1
         cpu = {"value": round(len(sample) / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
@@ -552,8 +553,9 @@ def bench_mla(args):
 
     return {
         "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
-        "config": {"workload": "mla_decode_b128: 128 absorbed-MLA decode rows, 128 heads, latent 512 + rope 64, "
-                               "ctx U[4096,32768], 16-token pages, random page table, o-proj 65536x4096, "
+        "config": {"workload": ("mla_decode_b128_fp8" if fp8 else "mla_decode_b128") + ": 128 absorbed-MLA decode "
+                               "rows, 128 heads, latent 512 + rope 64" + (" in an FP8 E4M3 cache" if fp8 else "") +
+                               ", ctx U[4096,32768], 16-token pages, random page table, o-proj 65536x4096, "
                                "lm-head 4096x129280",
                    "rows": len(rows), "sum_ctx": sum(ctx), "split_tokens": 2048, "parallelism": "none (1 GPU)"},
         "attn_hbm_gbps": round(attn_gbps, 1), "attn_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
@@ -567,7 +569,7 @@ def bench_mla(args):
 # sparse MLA over the indexer's top-2048, 32 rows of 65536 positions
 # ---------------------------------------------------------------------------
 
-def bench_sparse(args):
+def bench_sparse(args, fp8=False):
     import numpy as np
     import torch
     import workloads as wl
@@ -577,7 +579,7 @@ def bench_sparse(args):
     rows = list(range(w.rows))
     t0 = time.time()
     case = SparseCase(w, rows, device="cuda", shuffle_seed=0x5EED, copies=2, max_rows=w.rows,
-                      max_tokens=w.rows * w.recompute_tokens)
+                      max_tokens=w.rows * w.recompute_tokens, kv_dtype=1 if fp8 else 0)
     ctx = [case.ctx(r) for r in rows]
     log(f"data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
     dec, diff = diff_check(case, rows)
@@ -612,7 +614,7 @@ def bench_sparse(args):
             "kernel": "indexer", "algorithmic_flops_per_launch": int(idx_flops), "avg_launch_us": round(idx_us, 2),
             "hbm_gbps": round(idx_gbps, 1)}
     sel_n = sum(min(c_, w.topk) for c_ in ctx)
-    attn_bytes = sel_n * (w.kv_rank + w.rope_dim) * 2
+    attn_bytes = sel_n * (w.kv_rank + w.rope_dim) * (1 if fp8 else 2)
     attn_us = kern["attn_split"]["avg_us"] + kern["attn_merge"]["avg_us"]
 
     cpu = None
@@ -630,9 +632,10 @@ def bench_sparse(args):
 
     return {
         "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
-        "config": {"workload": "sparse_mla_b32: 32 decode rows of 65536 positions, fp32 indexer 64 heads x 128, "
-                               "stable top-2048 (ties to the lower position), MLA 128 heads over the selection, "
-                               "o-proj 65536x4096, lm-head 4096x129280",
+        "config": {"workload": ("sparse_mla_b32_fp8" if fp8 else "sparse_mla_b32") + ": 32 decode rows of 65536 "
+                               "positions, fp32 indexer 64 heads x 128, stable top-2048 (ties to the lower "
+                               "position), MLA 128 heads over the selection" + (" from an FP8 E4M3 latent cache"
+                               if fp8 else "") + ", o-proj 65536x4096, lm-head 4096x129280",
                    "rows": len(rows), "sum_ctx": sum(ctx), "split_entries": 256, "parallelism": "none (1 GPU)"},
         "attn_hbm_gbps": round(attn_bytes / (attn_us * 1e-6) / 1e9, 1),
         "diff": diff, "timed_step_equals_checked_decode": last_equal,
@@ -804,9 +807,76 @@ def long_decode_leg(args):
     return res
 
 
+def bench_mla_prefill(args, fp8=False):
+    """The trainer-side recompute of one 32768-token absorbed-MLA sequence (128 heads,
+    latent 512 + rope 64): every position's logprob from one prefill pass in 2048-token
+    chunks, through the same split kernels decode runs (one query row per token).  Its last
+    four positions are also produced by four plain decode steps on a second copy of the
+    history (diff, must be 0).  Attention FLOPs count each (query, key) pair once per head:
+    2 x (576 + 512) per pair."""
+    import numpy as np
+    import torch
+    import invariant_rl_logprob_amd as ril
+    import workloads as wl
+    from invariant_rl_logprob_amd.metrics import mismatch
+    from mla_case import MLACase
+
+    L, CH, ND = 32768, 2048, 4
+    w = wl.scaled(wl.MLA_DECODE_B128, rows=1, recompute_tokens=L)
+    t0 = time.time()
+    case = MLACase(w, [0], ctx=[L], device="cuda", shuffle_seed=0x5EED, copies=2, max_rows=128, max_tokens=CH,
+                   kv_dtype=1 if fp8 else 0)
+    d = case.data[0]
+    log(f"mla prefill: data ready in {time.time() - t0:.1f}s")
+    case.write_history("d", [0], ND)
+    dec = torch.stack([case.decode_back("d", [0], b)[0] for b in range(ND, 0, -1)])
+
+    def recompute():
+        outs = []
+        for p0 in range(0, L, CH):
+            outs.append(case.sess.prefill([("p", 0)], [p0], targets=[d["target"][p0:p0 + CH]],
+                                          qs=[d["q"][p0:p0 + CH]], ks=[d["c"][p0:p0 + CH]]))
+        return torch.cat(outs)
+
+    case.sess.ensure(("p", 0), L)
+    lp = recompute()  # warm-up pass
+    torch.cuda.synchronize()
+    ril.ril_trace_enable(True)
+    t1 = time.time()
+    lp = recompute()
+    torch.cuda.synchronize()
+    secs = time.time() - t1
+    kt = {}
+    for kid, name in enumerate(ril.KERNEL_NAMES):
+        tot, cnt = ril.ril_trace_read(kid)
+        if cnt:
+            kt[name] = round(tot, 3)
+    ril.ril_trace_enable(False)
+    diff = mismatch(dec, lp[L - ND:])
+    attn_ms = kt.get("attn_split", float("nan"))
+    flops = (L * (L + 1) // 2) * w.n_heads * 2 * ((w.kv_rank + w.rope_dim) + w.kv_rank)
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    log(f"mla prefill: {secs:.2f} s for {L} tokens, kernels {kt}, diff {diff}")
+    res = {"value": round(L / secs, 1), "unit": "tokens/s", "ms_per_step": round(secs * 1e3, 3),
+           "config": {"workload": f"mla_prefill_32k{'_fp8' if fp8 else ''}: the recompute of one {L}-token "
+                                  "absorbed-MLA sequence, 128 heads, latent 512 + rope 64"
+                                  + (" in an FP8 E4M3 cache" if fp8 else "") + f", chunks of {CH} tokens, "
+                                  "o-proj 65536x4096, lm-head 4096x129280", "tokens": L, "chunk": CH},
+           "kernel_ms": kt, "attn_split_tflops": round(tflops, 1),
+           "attn_split_frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+           "last_positions_vs_decode_steps": diff}
+    case.sess.close()
+    del case, d, lp, dec
+    torch.cuda.empty_cache()
+    return res
+
+
 WORKLOADS = {"gqa_decode_b64": bench_gqa, "gqa_decode_b64_fp8": bench_gqa_fp8,
              "gqa_decode_b64_w8a8": bench_gqa_w8a8, "gqa_decode_b64_fp8_w8a8": bench_gqa_fp8_w8a8, "mla_decode_b128": bench_mla,
-             "sparse_mla_b32": bench_sparse, "long_mix": bench_long}
+             "sparse_mla_b32": bench_sparse, "long_mix": bench_long,
+             "mla_decode_b128_fp8": lambda a: bench_mla(a, fp8=True),
+             "sparse_mla_b32_fp8": lambda a: bench_sparse(a, fp8=True),
+             "mla_prefill_32k": bench_mla_prefill, "mla_prefill_32k_fp8": lambda a: bench_mla_prefill(a, fp8=True)}
 
 
 def main():

@@ -77,14 +77,17 @@ typedef enum ril_status {
  *        every position. */
 enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1, RIL_ATTN_MLA_SPARSE = 2 };
 
-/* KV cache storage (GQA).  FP8_E4M3 follows the Bitwise-consistent RL post, section
+/* KV cache storage (GQA, and the MLA latent).  FP8_E4M3 follows the Bitwise-consistent RL post, section
  * 4.2 (FP8 KV cache: FP8 storage, one write path, one dequantizing read shared by
  * prefill, decode and the trainer's recompute): each K (V) value x is stored as the OCP
  * E4M3 code of x * 2^-k_scale_exp (2^-v_scale_exp), rounded to nearest even, magnitudes
  * beyond 448 saturating to 448, NaN kept as NaN with its sign; every attention reads
  * code * 2^scale_exp, a bf16 value exactly, and runs the bf16 arithmetic unchanged.  A
  * page then takes n_kv_heads * 16 * 2 * head_dim bytes (half of BF16's).  The in-page
- * byte layout is documented in csrc/attn_common.h. */
+ * byte layout is documented in csrc/attn_common.h.  MLA (dense and sparse): the latent
+ * row (head_dim + rope_dim values) is one tensor with one scale, so k_scale_exp must equal
+ * v_scale_exp; a page holds 16 x 576 codes, token-major (code of (t, d) at byte 576 t + d),
+ * then, for the sparse kind, the fp32 indexer keys as with BF16 (csrc/mla.hip). */
 enum { RIL_KV_BF16 = 0, RIL_KV_FP8_E4M3 = 1 };
 
 /* lm-head arithmetic.  W8A8_FP8 follows the Bitwise-consistent RL post, section 4.1
@@ -147,7 +150,7 @@ typedef struct ril_model_desc {
   const void *norm_final; /* [d_head]  RMSNorm gain          NULL = 1                */
   const void *w_lm;       /* [V, d_head] in the packed lm-head layout written by
                              ril_pack_lm_head (ril_lm_head_packed_bytes)      required */
-  int32_t kv_dtype;       /* RIL_KV_BF16 (0) | RIL_KV_FP8_E4M3 (GQA only)                 */
+  int32_t kv_dtype;       /* RIL_KV_BF16 (0) | RIL_KV_FP8_E4M3                            */
   int32_t k_scale_exp;    /* FP8: K stored as e4m3(k * 2^-k_scale_exp), in [-32, 32]; BF16: 0 */
   int32_t v_scale_exp;    /* FP8: V likewise                                               */
   /* TOKENS only: an optional SwiGLU MLP block after the attention block (d_ff = 0: none):

@@ -56,10 +56,13 @@ __device__ __forceinline__ int mla_swz(int u) { return u ^ (((u >> 4) & 1) << 3)
 // token-major (code of (t, d) at byte 576 t + d, 9216 bytes), each the code of
 // c * 2^-s (nearest even, magnitudes past 448 saturating, NaN kept with its sign) for the
 // model's one latent scale exponent s; the sparse kind's fp32 indexer keys follow at byte
-// 9216.  Every read takes code * 2^s, which bf16 holds exactly (|s| <= 32 keeps every
-// value a normal bf16), so the attention arithmetic is the bf16 path's, over those
-// values.  Token-major keeps each token's codes in whole 16-byte units, so the sparse
-// kind gathers a selected token with 16-byte copies.
+// 9216.  Every read takes the codes' values (exact in bf16) as the MFMA operands and
+// applies 2^s outside them, as the GQA FP8 cache does: the scores' softmax constant
+// carries it, and the fp32 value state is multiplied by it once, before the split's
+// partial is stored.  A power of two commutes with every fp32 rounding in between, so
+// this is attention over code * 2^s (outside fp32's subnormal and overflow ranges), the
+// same in every phase.  Token-major keeps each token's codes in whole 16-byte units, so
+// the sparse kind gathers a selected token with 16-byte copies.
 constexpr int kMla8Page = kPage * kMlaDqk;  // 9216 bytes of codes per page
 constexpr int kMla8Tile = kTile * kMlaDqk;  // 36864 bytes: one tile's codes
 
@@ -445,17 +448,24 @@ __global__ __launch_bounds__(512) void mla_split_kernel(
 // mla_split_kernel, with the tile dequantized into LDS before it is used.  Each tile's
 // codes (36 KB) are copied two tiles ahead into a 2-slot ring by direct-to-LDS loads (36
 // pieces of 1 KB: wave w copies pieces w, w + 8, ..), then all 512 threads turn them
-// into the bf16 tile in the K layout and swizzle mla_split_kernel reads (code * 2^s,
-// exact), and the scores and values run on it unchanged: the bits are those of the bf16
-// kernel over the cache's values.  Per tile: wait for this wave's pieces of the tile,
+// into the bf16 tile in the K layout and swizzle mla_split_kernel reads (the codes'
+// values, exact), and the scores and values run on it unchanged, with 2^s in the
+// softmax constant and on the stored state.  Per tile: wait for this wave's pieces of the tile,
 // barrier (the codes are in, every wave is done with the previous bf16 tile),
 // dequantize, barrier (the bf16 tile is in, the codes' slot is free), copy tile t + 2
 // into that slot, compute.
 // ---------------------------------------------------------------------------
+template <int OFF>
 __device__ __forceinline__ u32x2 lds_rd64(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
   u32x2 r;
-  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
+}
+template <int OFF>
+__device__ __forceinline__ void lds_wr128(uint32_t addr, u32x4 v) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
 }
 
 template <bool SPARSE>
@@ -548,39 +558,29 @@ __global__ __launch_bounds__(512) void mla_split_fp8_kernel(
   // dequantize slot t & 1 into kt: bf16 unit v = tid + 512 k of the tile (page slot
   // v / 1152, unit v % 1152 of its K layout) holds dims d0 .. d0 + 7 of token t of that
   // slot, read as 8 codes at byte 576 (16 slot + t) + d0
+  // dequantize slot t & 1 into kt: thread i converts units (i & 127) + 128 k, k = 0..8,
+  // of page slot i / 128 (K layout: the unit holds dims d0 .. d0 + 7 of one token t of
+  // the slot, whose codes sit at byte 576 (16 slot + t) + d0 of the staged tile).  Adding
+  // 128 to a unit adds 64 to d0 and 2048 bytes to its swizzled LDS place, so the nine
+  // reads and writes share one address each with immediate offsets.
+  uint32_t dq_src, dq_dst;
+  {
+    const int ps = threadIdx.x >> 7, u0 = threadIdx.x & 127;
+    int tt, d0;
+    mla_unit_td(u0, tt, d0);
+    dq_src = (16 * ps + tt) * kMlaDqk + d0;
+    dq_dst = lds_addr(kt) + ps * (2 * kMlaSlot) + 16 * mla_swz(u0);
+  }
   auto dequant = [&](int t) {
-    // the thread index through an opaque copy: the addresses are recomputed per tile
-    // instead of being held in registers across the loop
-    uint32_t tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const uint32_t src0 = lds_addr(&k8[t & 1][0]), dst0 = lds_addr(kt);
-    typedef float f2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int k0 = 0; k0 < 9; k0 += 3) {
-      u32x2 c[3];
-      uint32_t dst[3];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int v = tid + 512 * (k0 + k), ps = v / 1152, vv = v - 1152 * ps;
-        int tt, d0;
-        mla_unit_td(vv, tt, d0);
-        c[k] = lds_rd64(src0 + (16 * ps + tt) * kMlaDqk + d0);
-        dst[k] = dst0 + ps * (2 * kMlaSlot) + 16 * mla_swz(vv);
-      }
-      lds_wait<0>();
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        settle(c[k]);
-        u32x4 w;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(c[k][h], false), b = __builtin_amdgcn_cvt_pk_f32_fp8(c[k][h], true);
-          w[2 * h] = pack2(a[0] * scale, a[1] * scale);
-          w[2 * h + 1] = pack2(b[0] * scale, b[1] * scale);
-        }
-        lds_wr128(dst[k], w);
-      }
-    }
+    const uint32_t src = lds_addr(&k8[t & 1][0]) + dq_src;
+    u32x2 c[9];
+    static_for<9>([&](auto k_) { c[decltype(k_)::value] = lds_rd64<64 * decltype(k_)::value>(src); });
+    lds_wait<0>();
+    static_for<9>([&](auto k_) {
+      constexpr int k = decltype(k_)::value;
+      settle(c[k]);
+      lds_wr128<2048 * k>(dq_dst, fp8_operand(c[k][0], c[k][1]));
+    });
   };
   const uint32_t xp_lane = lds_addr(&xp[pair][0][0]) + 16 * lane, xa_lane = lds_addr(&xa[pair][0]) + 4 * lane;
   float m = neg_inf(), l = 0.f;
@@ -645,6 +645,8 @@ __global__ __launch_bounds__(512) void mla_split_fp8_kernel(
   bad = __syncthreads_or(bad);
   if (bad) l = __builtin_nanf("");
   if (!col_ok) return;
+#pragma unroll
+  for (int b = 0; b < kMlaDv / 32; ++b) o[b] = o[b] * scale;  // 2^s: exact
   mla_store_partial(part_o, part_ml, ((long)r * H + head) * max_splits + split, half, o, m, l);
 }
 
@@ -696,13 +698,13 @@ hipError_t launch_mla_split(const MlaAttnArgs &a, hipStream_t st) {
     if (a.sel)
       hipLaunchKernelGGL(mla_split_fp8_kernel<true>, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0,
                          a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, pool,
-                         2 * a.page_elems, a.n_pages, a.H, a.sel, a.topk, a.split_tokens, a.ctx_bound, a.cscale,
-                         a.scale, a.part_o, a.part_ml, a.max_splits);
+                         2 * a.page_elems, a.n_pages, a.H, a.sel, a.topk, a.split_tokens, a.ctx_bound,
+                         a.cscale * a.scale, a.scale, a.part_o, a.part_ml, a.max_splits);
     else
       hipLaunchKernelGGL(mla_split_fp8_kernel<false>, grid, dim3(kMlaThreads), 0, st, a.q, a.mode, a.row0,
                          a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.page_table, a.page_stride, pool,
-                         2 * a.page_elems, a.n_pages, a.H, nullptr, 0, a.split_tokens, a.ctx_bound, a.cscale,
-                         a.scale, a.part_o, a.part_ml, a.max_splits);
+                         2 * a.page_elems, a.n_pages, a.H, nullptr, 0, a.split_tokens, a.ctx_bound,
+                         a.cscale * a.scale, a.scale, a.part_o, a.part_ml, a.max_splits);
     return hipGetLastError();
   }
   if (a.sel) {
