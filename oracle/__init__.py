@@ -45,6 +45,7 @@ from .models import (  # noqa: F401
     topk_select,
 )
 from .metrics import diff_stats, k3_mean  # noqa: F401
+from .ssd import ssd_scan, ssd_outputs  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode, kv_fp8_roundtrip  # noqa: F401
 from .fp8block import (  # noqa: F401
     block_exponent,

@@ -772,3 +772,114 @@ def test_planted_transposed_weight_blocks_are_caught():
     w[:128, 128:] *= 100.0
     codes, e = ofb.quantize_weight_blocks(w)
     assert not np.array_equal(ofb.dequant_weight_blocks(codes, e.T), ofb.dequant_weight_blocks(codes, e))
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 SSD mixer (oracle/ssd.py)
+# ---------------------------------------------------------------------------
+
+def _ssd_inputs(T=9, H=4, P=3, G=2, N=5, seed=0):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((T, H, P))
+    B = r.standard_normal((T, G, N))
+    C = r.standard_normal((T, G, N))
+    dt = np.log1p(np.exp(r.standard_normal((T, H)) - 1.0))   # softplus: positive
+    A = -np.exp(r.uniform(0.0, 1.5, H))
+    D = r.standard_normal(H)
+    return x, B, C, dt, A, D
+
+
+def _ssd_quadratic(x, B, C, dt, A, D):
+    """The same layer as one masked matrix product per head (the state-space / attention
+    duality): y_h = (L_h o (C_g B_g^T)) (dt_h x_h) + D_h x_h, L_h[t, s] the product of the
+    decays a_r over s < r <= t (0 above the diagonal), written out as explicit products."""
+    T, H, P = x.shape
+    G = B.shape[1]
+    y = np.empty((T, H, P))
+    for h in range(H):
+        g = h // (H // G)
+        a = np.exp(dt[:, h] * A[h])
+        L = np.zeros((T, T))
+        for t in range(T):
+            for s in range(t + 1):
+                L[t, s] = np.prod(a[s + 1:t + 1])
+        M = L * (C[:, g, :] @ B[:, g, :].T)
+        y[:, h, :] = M @ (dt[:, h, None] * x[:, h, :]) + D[h] * x[:, h, :]
+    return y
+
+
+def check_ssd(fn):
+    x, B, C, dt, A, D = _ssd_inputs()
+    y = fn(x, B, C, dt, A, D)[0]
+    assert np.allclose(y, _ssd_quadratic(x, B, C, dt, A, D), rtol=1e-12, atol=1e-12)
+    # one position: y_0 = dt_0 (C_0 . B_0) x_0 + D x_0 per head
+    y0 = fn(x[:1], B[:1], C[:1], dt[:1], A, D)[0][0]
+    H, G = x.shape[1], B.shape[1]
+    for h in range(H):
+        g = h // (H // G)
+        want = dt[0, h] * (C[0, g] @ B[0, g]) * x[0, h] + D[h] * x[0, h]
+        assert np.allclose(y0[h], want, rtol=1e-13, atol=1e-14)
+    # an infinitely fast decay forgets everything but the current position
+    yf = fn(x, B, C, dt, np.full_like(A, -1e6), D)[0]
+    for t in range(x.shape[0]):
+        for h in range(H):
+            g = h // (H // G)
+            want = dt[t, h] * (C[t, g] @ B[t, g]) * x[t, h] + D[h] * x[t, h]
+            assert np.allclose(yf[t, h], want, rtol=1e-12, atol=1e-13)
+
+
+def test_ssd_matches_quadratic_form_and_closed_forms():
+    check_ssd(oracle.ssd_scan)
+
+
+def test_ssd_state_by_brute_force_and_without_decay():
+    x, B, C, dt, A, D = _ssd_inputs(T=6, H=2, P=2, G=1, N=3, seed=4)
+    T, H, P = x.shape
+    y, S_last = oracle.ssd_scan(x, B, C, dt, A, D)
+    for t in range(T):   # the state as an explicit sum over past positions
+        for h in range(H):
+            S = np.zeros((3, P))
+            for s in range(t + 1):
+                w = dt[s, h] * math.prod(math.exp(dt[r, h] * A[h]) for r in range(s + 1, t + 1))
+                S += w * np.outer(B[s, 0], x[s, h])
+            assert np.allclose(y[t, h], C[t, 0] @ S + D[h] * x[t, h], rtol=1e-12, atol=1e-13)
+            if t == T - 1:
+                assert np.allclose(S_last[h], S, rtol=1e-12, atol=1e-13)
+    # A = 0: no decay, the state is a running sum
+    y0 = oracle.ssd_scan(x, B, C, dt, np.zeros(H), np.zeros(H))[0]
+    run = np.cumsum(dt[:, :, None, None] * B[:, 0][:, None, :, None] * x[:, :, None, :], axis=0)
+    assert np.allclose(y0, np.einsum("tn,thnp->thp", C[:, 0], run), rtol=1e-12, atol=1e-13)
+
+
+def test_ssd_state_carry_equals_one_pass():
+    x, B, C, dt, A, D = _ssd_inputs(T=13, seed=9)
+    y, S = oracle.ssd_scan(x, B, C, dt, A, D)
+    y1, S1 = oracle.ssd_scan(x[:5], B[:5], C[:5], dt[:5], A, D)
+    y2, S2 = oracle.ssd_scan(x[5:], B[5:], C[5:], dt[5:], A, D, state=S1)
+    assert np.allclose(np.concatenate([y1, y2]), y, rtol=1e-13, atol=1e-14)
+    assert np.allclose(S2, S, rtol=1e-13, atol=1e-14)
+    assert np.array_equal(oracle.ssd_outputs(x, B, C, dt, A, D), oracle.bf16(y))
+
+
+def _ssd_planted(kind):
+    def fn(x, B, C, dt, A, D, state=None):
+        T, H, P = x.shape
+        G, N = B.shape[1], B.shape[2]
+        grp = np.arange(H) % G if kind == "group" else np.arange(H) // (H // G)
+        S = np.zeros((H, N, P))
+        y = np.empty((T, H, P))
+        for t in range(T):
+            ta = max(t - 1, 0) if kind == "shift" else t
+            a = np.exp(dt[ta] * A)
+            Bt, Ct = (C[t][grp], B[t][grp]) if kind == "swap" else (B[t][grp], C[t][grp])
+            w = np.ones_like(dt[t]) if kind == "no_dt" else dt[t]
+            S = a[:, None, None] * S + (w[:, None, None] * Bt[:, :, None]) * x[t][:, None, :]
+            y[t] = np.einsum("hn,hnp->hp", Ct, S) + (0.0 if kind == "no_d" else D[:, None] * x[t])
+        return y, S
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["no_dt", "shift", "swap", "no_d", "group"])
+def test_planted_ssd_mistakes_are_caught(kind):
+    with pytest.raises(AssertionError):
+        check_ssd(_ssd_planted(kind))
