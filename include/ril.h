@@ -75,7 +75,26 @@ typedef enum ril_status {
  *        (-1 padding last) and the attention accumulates in that order, splitting it
  *        into runs of split_tokens entries.  Contexts of at most k positions select
  *        every position. */
-enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1, RIL_ATTN_MLA_SPARSE = 2 };
+/* RIL_ATTN_SSD: a Mamba-2 selective state-space mixer in place of attention
+ *   (Bitwise-consistent RL post, section 6: Nemotron's Mamba-2 layers, whose decode
+ *   replays the prefill's chunked arithmetic; the zero-mismatch-rl README's key
+ *   features).  H = n_q_heads heads of head_dim = 64 channels, G = n_kv_heads groups of
+ *   ssm_state = 128 state rows (head h reads group h / (H / G)); per position t, with
+ *   dt_t > 0 given per head and A (< 0), D model constants per head:
+ *     S_t = exp(dt_t A) S_{t-1} + dt_t B_t x_t^T,   y_t = S_t^T C_t + D x_t   (bf16)
+ *   y replaces the attention output of the QKV input mode (then [O GEMM], RMSNorm,
+ *   lm-head).  The batch's q holds C [tokens, G, 128], k holds B [tokens, G, 128], v holds
+ *   x [tokens, H, 64] (bf16), dt the fp32 [tokens, H] steps.  It is evaluated in chunks of
+ *   ssm_chunk = 128 positions counted from position 0, every phase through the same
+ *   kernels (csrc/ssd.hip), so a position's bits do not depend on how its sequence is cut
+ *   into calls.  The "KV pool" holds one cache slot per sequence (ril_kv_page_bytes: the
+ *   state entering the current chunk, fp32, and that chunk's earlier inputs): page_table
+ *   column 0 of a sequence is its slot, page_stride >= 1.  A slot's state is read only
+ *   when a sequence continues past its first chunk; a sequence restarted at position 0
+ *   starts from zero state.  Prefill calls carry at most max_rows sequences; history is
+ *   laid down by prefill calls (ril_kv_write does not apply: the state depends on every
+ *   position).  H a multiple of 4 and of G; bf16 cache only. */
+enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1, RIL_ATTN_MLA_SPARSE = 2, RIL_ATTN_SSD = 3 };
 
 /* KV cache storage (GQA, and the MLA latent).  FP8_E4M3 follows the Bitwise-consistent RL post, section
  * 4.2 (FP8 KV cache: FP8 storage, one write path, one dequantizing read shared by
@@ -168,6 +187,10 @@ typedef struct ril_model_desc {
   int32_t proj_dtype;     /* RIL_PROJ_BF16 (0): w_qkv, w_o, w_gate_up, w_down bf16 as above;
                              RIL_PROJ_W8A8_FP8 (1): each written by ril_quantize_weight_fp8
                              from that bf16 matrix (16-byte aligned)                        */
+  int32_t ssm_state;      /* SSD: state rows N (128); else 0                                 */
+  int32_t ssm_chunk;      /* SSD: chunk Q (128); else 0                                      */
+  const void *ssm_A;      /* SSD: device fp32 [H], negative; else NULL                       */
+  const void *ssm_D;      /* SSD: device fp32 [H]; else NULL                                 */
 } ril_model_desc;
 
 typedef struct ril_model ril_model;  /* opaque: copy of the description + derived sizes */
@@ -328,6 +351,7 @@ typedef struct ril_prefill_batch {
   const float *k_index;     /* MLA_SPARSE: device fp32 [total_tokens, index_dim] (cached per position) */
   int32_t *selected_out;    /* MLA_SPARSE, optional: device int32 [total_tokens, topk] receives each
                                token's selection list; NULL = not returned */
+  const float *dt;          /* SSD: device fp32 [total_tokens, H], 16-byte aligned; else unused */
 } ril_prefill_batch;
 
 /* A decode batch: n_rows rows, one new token each, at position ctx_len[r]-1. */
@@ -346,6 +370,7 @@ typedef struct ril_decode_batch {
   const float *q_index;     /* MLA_SPARSE: device fp32 [n_rows, index_heads, index_dim] */
   const float *k_index;     /* MLA_SPARSE: device fp32 [n_rows, index_dim] (the new token's) */
   int32_t *selected_out;    /* MLA_SPARSE, optional: device int32 [n_rows, topk] */
+  const float *dt;          /* SSD: device fp32 [n_rows, H], 16-byte aligned; else unused */
 } ril_decode_batch;
 
 /* Trainer-side recompute: the trainer's forward calls the rollout's kernels

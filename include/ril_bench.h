@@ -63,7 +63,9 @@ enum {
   RIL_K_QUANT_ROWS = 11,  /* W8A8 head: block-FP8 activation quantization */
   RIL_K_LM_HEAD_FP8 = 12, /* S11 in W8A8 block FP8 */
   RIL_K_GEMM_FP8 = 13,    /* S4 in W8A8 block FP8 */
-  RIL_K_COUNT = 14
+  RIL_K_SSD_CHUNK = 14,   /* SSD: plan, chunk state sums, state scan, commit, input write */
+  RIL_K_SSD_OUT = 15,     /* SSD: the positions' outputs */
+  RIL_K_COUNT = 16
 };
 ril_status ril_trace_enable(int on);
 ril_status ril_trace_read(int kernel, double *total_ms, int64_t *launches);

@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 RIL_OK, RIL_EINVAL, RIL_ERANGE, RIL_ENOSPC, RIL_EUNSUPPORTED, RIL_EHIP = 0, -1, -2, -3, -4, -5
-RIL_ATTN_GQA, RIL_ATTN_MLA, RIL_ATTN_MLA_SPARSE = 0, 1, 2
+RIL_ATTN_GQA, RIL_ATTN_MLA, RIL_ATTN_MLA_SPARSE, RIL_ATTN_SSD = 0, 1, 2, 3
 RIL_INPUT_TOKENS, RIL_INPUT_QKV = 0, 1
 RIL_POLICY_INVARIANT, RIL_POLICY_SHAPE_DERIVED = 0, 1
 RIL_KV_BF16, RIL_KV_FP8_E4M3 = 0, 1
@@ -48,6 +48,7 @@ class ril_model_desc(ctypes.Structure):
         ("d_ff", _c_int), ("w_gate_up", _vp), ("w_down", _vp), ("norm_mlp", _vp),
         ("lm_dtype", _c_int),
         ("proj_dtype", _c_int),
+        ("ssm_state", _c_int), ("ssm_chunk", _c_int), ("ssm_A", _vp), ("ssm_D", _vp),
     ]
 
 
@@ -56,7 +57,7 @@ class ril_prefill_batch(ctypes.Structure):
         ("n_seqs", _c_int), ("total_tokens", _c_int), ("max_ctx_bound", _c_int),
         ("cu_tokens", _vp), ("start_pos", _vp), ("page_table", _vp), ("page_stride", _c_int),
         ("target_ids", _vp), ("token_ids", _vp), ("q", _vp), ("k", _vp), ("v", _vp),
-        ("q_index", _vp), ("k_index", _vp), ("selected_out", _vp),
+        ("q_index", _vp), ("k_index", _vp), ("selected_out", _vp), ("dt", _vp),
     ]
 
 
@@ -65,6 +66,7 @@ class ril_decode_batch(ctypes.Structure):
         ("n_rows", _c_int), ("max_ctx_bound", _c_int), ("ctx_len", _vp), ("page_table", _vp),
         ("page_stride", _c_int), ("target_ids", _vp), ("token_ids", _vp),
         ("q", _vp), ("k", _vp), ("v", _vp), ("q_index", _vp), ("k_index", _vp), ("selected_out", _vp),
+        ("dt", _vp),
     ]
 
 
@@ -131,9 +133,11 @@ EXPORTED = ("ril_model_create", "ril_model_destroy", "ril_workspace_bytes", "ril
 RIL_K_KV_WRITE, RIL_K_ATTN_SPLIT, RIL_K_ATTN_MERGE, RIL_K_ATTN_PREFILL = 0, 1, 2, 3
 RIL_K_RMSNORM, RIL_K_GEMM, RIL_K_LM_HEAD, RIL_K_VOCAB_MERGE = 4, 5, 6, 7
 RIL_K_INDEXER, RIL_K_TOPK, RIL_K_SILU_MUL = 8, 9, 10
-RIL_K_QUANT_ROWS, RIL_K_LM_HEAD_FP8, RIL_K_COUNT = 11, 12, 13
+RIL_K_QUANT_ROWS, RIL_K_LM_HEAD_FP8, RIL_K_GEMM_FP8 = 11, 12, 13
+RIL_K_SSD_CHUNK, RIL_K_SSD_OUT, RIL_K_COUNT = 14, 15, 16
 KERNEL_NAMES = ("kv_write", "attn_split", "attn_merge", "attn_prefill", "rmsnorm", "gemm", "lm_head",
-                "vocab_merge", "indexer", "topk", "silu_mul", "quant_rows", "lm_head_fp8", "gemm_fp8")
+                "vocab_merge", "indexer", "topk", "silu_mul", "quant_rows", "lm_head_fp8", "gemm_fp8",
+                "ssd_chunk", "ssd_out")
 
 
 class RilError(RuntimeError):
@@ -333,21 +337,22 @@ def ril_kv_free(kv: int) -> None:
 
 def make_prefill_batch(*, cu_tokens, start_pos, page_table, max_ctx_bound, target_ids=None,
                        token_ids=None, q=None, k=None, v=None, q_index=None, k_index=None,
-                       selected_out=None, total_tokens=None) -> ril_prefill_batch:
+                       selected_out=None, total_tokens=None, dt=None) -> ril_prefill_batch:
     """Build the C descriptor from device tensors (the tensors must outlive the call)."""
     n = cu_tokens.numel() - 1
     if total_tokens is None:
         raise ValueError("total_tokens (a host integer) is required")
     return ril_prefill_batch(n, int(total_tokens), int(max_ctx_bound), _ptr(cu_tokens), _ptr(start_pos),
                              _ptr(page_table), page_table.shape[1], _ptr(target_ids), _ptr(token_ids),
-                             _ptr(q), _ptr(k), _ptr(v), _ptr(q_index), _ptr(k_index), _ptr(selected_out))
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(q_index), _ptr(k_index), _ptr(selected_out),
+                             _ptr(dt))
 
 
 def make_decode_batch(*, ctx_len, page_table, max_ctx_bound, target_ids, token_ids=None, q=None,
-                      k=None, v=None, q_index=None, k_index=None, selected_out=None) -> ril_decode_batch:
+                      k=None, v=None, q_index=None, k_index=None, selected_out=None, dt=None) -> ril_decode_batch:
     return ril_decode_batch(ctx_len.numel(), int(max_ctx_bound), _ptr(ctx_len), _ptr(page_table),
                             page_table.shape[1], _ptr(target_ids), _ptr(token_ids), _ptr(q), _ptr(k), _ptr(v),
-                            _ptr(q_index), _ptr(k_index), _ptr(selected_out))
+                            _ptr(q_index), _ptr(k_index), _ptr(selected_out), _ptr(dt))
 
 
 def ril_prefill_logprobs(model: int, kv: int, batch: ril_prefill_batch, logprob_out, ws,

@@ -22,7 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libril.so")
-SOURCES = ["abi.cpp", "attn.hip", "prefill.hip", "mla.hip", "index.hip", "dense.hip", "lm_fp8.hip", "probe.hip"]
+SOURCES = ["abi.cpp", "attn.hip", "prefill.hip", "mla.hip", "index.hip", "dense.hip", "lm_fp8.hip", "ssd.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

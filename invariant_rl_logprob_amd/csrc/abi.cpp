@@ -43,6 +43,10 @@ struct ril_model {
   int attn_split_override = 0;
   int n_cu = 0;
   size_t off_gpart = 0;
+  // SSD mixer: plan, completed chunks' state sums and exit states, their decays
+  bool ssd = false;
+  int ssd_max_done = 0;
+  size_t off_ssd_plan = 0, off_ssd_ds = 0, off_ssd_ent = 0, off_ssd_dec = 0;
 };
 
 struct ril_kv {
@@ -74,10 +78,26 @@ extern "C" const char *ril_last_error(void) { return g_err.c_str(); }
 extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **out) {
   if (!desc || !out) return fail(RIL_EINVAL, "model_create: null argument");
   const ril_model_desc &d = *desc;
-  if (d.attn_kind != RIL_ATTN_GQA && d.attn_kind != RIL_ATTN_MLA && d.attn_kind != RIL_ATTN_MLA_SPARSE)
+  if (d.attn_kind != RIL_ATTN_GQA && d.attn_kind != RIL_ATTN_MLA && d.attn_kind != RIL_ATTN_MLA_SPARSE &&
+      d.attn_kind != RIL_ATTN_SSD)
     return fail(RIL_EUNSUPPORTED, "model_create: attn_kind %d", d.attn_kind);
   const bool sparse = d.attn_kind == RIL_ATTN_MLA_SPARSE;
   const bool mla = d.attn_kind == RIL_ATTN_MLA || sparse;
+  const bool ssd = d.attn_kind == RIL_ATTN_SSD;
+  if (ssd) {
+    if (d.head_dim != kSsdP || d.ssm_state != kSsdN || d.ssm_chunk != kSsdQ)
+      return fail(RIL_EUNSUPPORTED, "model_create: SSD needs head_dim %d, ssm_state %d, ssm_chunk %d", kSsdP, kSsdN,
+                  kSsdQ);
+    if (d.n_q_heads < 4 || d.n_q_heads % 4 || d.n_kv_heads < 1 || d.n_q_heads % d.n_kv_heads)
+      return fail(RIL_EINVAL, "model_create: SSD heads %d / groups %d (heads a multiple of 4 and of groups)",
+                  d.n_q_heads, d.n_kv_heads);
+    if (d.input_mode != RIL_INPUT_QKV || d.rope_dim || d.kv_dtype != RIL_KV_BF16)
+      return fail(RIL_EUNSUPPORTED, "model_create: SSD takes given inputs, no rope, a bf16 cache");
+    if (!d.ssm_A || !d.ssm_D || !aligned4(d.ssm_A) || !aligned4(d.ssm_D))
+      return fail(RIL_EINVAL, "model_create: SSD needs ssm_A and ssm_D (fp32 [H])");
+  } else if (d.ssm_state || d.ssm_chunk || d.ssm_A || d.ssm_D) {
+    return fail(RIL_EINVAL, "model_create: ssm_* fields are for SSD");
+  }
   if (sparse) {
     if (d.index_heads != 64 || d.index_dim != 128)
       return fail(RIL_EUNSUPPORTED, "model_create: indexer must be 64 heads x 128 dims");
@@ -89,7 +109,9 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   if (d.input_mode != RIL_INPUT_TOKENS && d.input_mode != RIL_INPUT_QKV)
     return fail(RIL_EINVAL, "model_create: input_mode %d", d.input_mode);
   int G = 1;
-  if (mla) {
+  if (ssd) {
+    G = d.n_q_heads / d.n_kv_heads;
+  } else if (mla) {
     if (d.head_dim != 512 || d.rope_dim != 64 || d.n_kv_heads != 1)
       return fail(RIL_EUNSUPPORTED, "model_create: MLA needs head_dim 512, rope_dim 64, n_kv_heads 1");
     if (d.n_q_heads < 64 || d.n_q_heads % 64)
@@ -164,7 +186,7 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->d = d;
   m->G = G;
   m->n_vt = (d.vocab + 255) / 256;
-  m->max_splits = (d.max_ctx + d.split_tokens - 1) / d.split_tokens;
+  m->max_splits = ssd ? 1 : (d.max_ctx + d.split_tokens - 1) / d.split_tokens;
   m->cscale = (float)((double)d.softmax_scale * 1.4426950408889634);
   m->kv_fp8 = d.kv_dtype == RIL_KV_FP8_E4M3;
   m->k_scale = std::ldexp(1.0f, d.k_scale_exp);
@@ -176,6 +198,8 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   const size_t kv_elem = d.kv_dtype == RIL_KV_FP8_E4M3 ? 1 : 2;  // bytes per cached value
   m->page_bytes = mla ? (size_t)16 * (d.head_dim + d.rope_dim) * kv_elem + (sparse ? (size_t)16 * d.index_dim * 4 : 0)
                       : (size_t)d.n_kv_heads * 2 * 16 * d.head_dim * kv_elem;
+  m->ssd = ssd;
+  if (ssd) m->page_bytes = (size_t)ril::ssd_slot_bytes(d.n_q_heads, d.n_kv_heads);
   const size_t R = (size_t)std::max(d.max_rows, d.max_tokens);
   const bool tok = d.input_mode == RIL_INPUT_TOKENS;
   size_t o = 0;
@@ -210,6 +234,15 @@ extern "C" ril_status ril_model_create(const ril_model_desc *desc, ril_model **o
   m->off_pml = seg((size_t)d.max_rows * d.n_q_heads * m->max_splits * 2 * sizeof(float));
   m->off_scores = seg(sparse ? (size_t)d.max_rows * d.max_ctx * sizeof(float) : 0);
   m->off_sel = seg(sparse ? (size_t)d.max_rows * d.topk * sizeof(int32_t) : 0);
+  if (ssd) {
+    // a call completes at most one chunk per sequence beyond its whole chunks of tokens
+    m->ssd_max_done = d.max_rows + R / kSsdQ;
+    const size_t st = (size_t)d.n_q_heads * kSsdP * kSsdN * sizeof(float);
+    m->off_ssd_plan = seg((6 * (size_t)d.max_rows + 2) * sizeof(int32_t));
+    m->off_ssd_ds = seg((size_t)m->ssd_max_done * st);
+    m->off_ssd_ent = seg((size_t)m->ssd_max_done * st);
+    m->off_ssd_dec = seg((size_t)m->ssd_max_done * d.n_q_heads * sizeof(float));
+  }
   m->ws_base = m->ws_total = o;
   *out = m;
   return RIL_OK;
@@ -585,6 +618,10 @@ static ril_status check_common(const ril_model *m, ril_kv *kv, void *ws, size_t 
   if (ctx_bound < 1 || ctx_bound > m->d.max_ctx)
     return fail(RIL_ERANGE, "%s: max_ctx_bound %d outside [1, %d]", who, ctx_bound, m->d.max_ctx);
   if (!page_table || !aligned4(page_table)) return fail(RIL_EINVAL, "%s: page_table", who);
+  if (m->ssd) {  // one cache slot per sequence, in column 0
+    if (page_stride < 1) return fail(RIL_EINVAL, "%s: page_stride %d < 1", who, page_stride);
+    return RIL_OK;
+  }
   if (page_stride < (ctx_bound + 15) / 16)
     return fail(RIL_EINVAL, "%s: page_stride %d < %d pages", who, page_stride, (ctx_bound + 15) / 16);
   return RIL_OK;
@@ -711,6 +748,12 @@ static ril_status check_prefill(const ril_model *m, ril_kv *kv, const ril_prefil
   const bool need_v = !m->mla;
   if ((!tok || !need_logprob) && (!b->k || !aligned16(b->k) || (need_v && (!b->v || !aligned16(b->v)))))
     return fail(RIL_EINVAL, "%s: k/v", who);
+  if (m->ssd) {
+    if (b->n_seqs > m->d.max_rows)
+      return fail(RIL_ERANGE, "%s: n_seqs %d > max_rows %d (one cache slot per sequence)", who, b->n_seqs,
+                  m->d.max_rows);
+    if (!b->dt || !aligned16(b->dt)) return fail(RIL_EINVAL, "%s: dt", who);
+  }
   if (m->sparse) {
     if (!b->k_index || !aligned16(b->k_index)) return fail(RIL_EINVAL, "%s: k_index", who);
     if (need_logprob && (!b->q_index || !aligned16(b->q_index))) return fail(RIL_EINVAL, "%s: q_index", who);
@@ -768,10 +811,58 @@ static ril_status run_mla(const ril_model *m, ril_kv *kv, const bf16_t *q, const
   return RIL_OK;
 }
 
+// The SSD mixer for one call (mode 0: packed prefill sequences; 1: decode rows): plan,
+// the completed chunks' state sums, the state scan, the outputs (if asked), the slot
+// commit and the unfinished chunk's inputs, in that order on the stream.
+static ril_status run_ssd(const ril_model *m, ril_kv *kv, int mode, int n_seqs, int n_tok, const int32_t *cu,
+                          const int32_t *start_pos, const int32_t *ctx_len, const int32_t *page_table,
+                          int page_stride, const void *C, const void *B, const void *x, const float *dt, bool out,
+                          void *ws, hipStream_t st) {
+  const ril_model_desc &d = m->d;
+  SsdArgs a{};
+  a.mode = mode;
+  a.n_seqs = n_seqs;
+  a.n_tok = n_tok;
+  a.cu = cu;
+  a.start_pos = start_pos;
+  a.ctx_len = ctx_len;
+  a.page_table = page_table;
+  a.page_stride = page_stride;
+  a.pool = static_cast<uint8_t *>(kv->pool);
+  a.slot_bytes = (long)m->page_bytes;
+  a.n_slots = kv->n_pages;
+  a.H = d.n_q_heads;
+  a.G = d.n_kv_heads;
+  a.x = (const bf16_t *)x;
+  a.B = (const bf16_t *)B;
+  a.C = (const bf16_t *)C;
+  a.dt = dt;
+  a.A = (const float *)d.ssm_A;
+  a.D = (const float *)d.ssm_D;
+  // a sequence touches at most ceil(len / Q) + 1 chunks and completes at most len / Q + 1
+  a.max_chunks = std::min(n_tok, n_tok / kSsdQ + 2 * n_seqs);
+  a.max_done = std::min(m->ssd_max_done, n_tok / kSsdQ + n_seqs);
+  a.plan = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + m->off_ssd_plan);
+  a.dS = wsf(ws, m->off_ssd_ds);
+  a.entry = wsf(ws, m->off_ssd_ent);
+  a.dec = wsf(ws, m->off_ssd_dec);
+  a.y = wsb(ws, m->off_attn);
+  RIL_LAUNCH(RIL_K_SSD_CHUNK, launch_ssd_plan(a, st));
+  RIL_LAUNCH(RIL_K_SSD_CHUNK, launch_ssd_state(a, st));
+  RIL_LAUNCH(RIL_K_SSD_CHUNK, launch_ssd_scan(a, st));
+  if (out) RIL_LAUNCH(RIL_K_SSD_OUT, launch_ssd_out(a, st));
+  RIL_LAUNCH(RIL_K_SSD_CHUNK, launch_ssd_commit(a, st));
+  RIL_LAUNCH(RIL_K_SSD_CHUNK, launch_ssd_write(a, st));
+  return RIL_OK;
+}
+
 extern "C" ril_status ril_kv_write(const ril_model *m, ril_kv *kv, const ril_prefill_batch *b, void *stream) {
   if (!m) return fail(RIL_EINVAL, "kv_write: null model");
   // the history writer needs no workspace; pass a dummy aligned pointer through the checks
   static char dummy alignas(16)[16];
+  if (m->ssd)
+    return fail(RIL_EUNSUPPORTED, "kv_write: an SSD state depends on every position; lay history down with "
+                "prefill calls");
   ril_status s = check_prefill(m, kv, b, dummy, 0, false, "kv_write");
   if (s != RIL_OK) return s;
   const ril_model_desc &d = m->d;
@@ -794,6 +885,12 @@ extern "C" ril_status ril_prefill_logprobs(const ril_model *m, ril_kv *kv, const
   const ril_model_desc &d = m->d;
   hipStream_t st = (hipStream_t)stream;
   const int T = b->total_tokens;
+  if (m->ssd) {
+    s = run_ssd(m, kv, 0, b->n_seqs, T, b->cu_tokens, b->start_pos, nullptr, b->page_table, b->page_stride, b->q,
+                b->k, b->v, b->dt, true, ws, st);
+    if (s != RIL_OK) return s;
+    return run_head(m, T, b->target_ids, logprob_out, ws, st);
+  }
   if (m->mla) {
     s = run_mla_write(m, kv, (const bf16_t *)b->k, b->k_index, T, 0, b->cu_tokens, b->start_pos, b->n_seqs,
                       nullptr, b->page_table, b->page_stride, st);
@@ -852,8 +949,15 @@ static ril_status decode_enqueue(const ril_model *m, ril_kv *kv, const ril_decod
   if (m->sparse && (!b->q_index || !b->k_index || !aligned16(b->q_index) || !aligned16(b->k_index) ||
                     (b->selected_out && !aligned4(b->selected_out))))
     return fail(RIL_EINVAL, "decode_step_logprobs: q_index/k_index/selected_out");
+  if (m->ssd && (!b->dt || !aligned16(b->dt))) return fail(RIL_EINVAL, "decode_step_logprobs: dt");
   hipStream_t st = (hipStream_t)stream;
   const int R = b->n_rows;
+  if (m->ssd) {
+    s = run_ssd(m, kv, 1, R, R, nullptr, nullptr, b->ctx_len, b->page_table, b->page_stride, b->q, b->k, b->v,
+                b->dt, true, ws, st);
+    if (s != RIL_OK) return s;
+    return run_head(m, R, b->target_ids, logprob_out, ws, st);
+  }
   if (m->mla) {
     s = run_mla_write(m, kv, (const bf16_t *)b->k, b->k_index, R, 1, nullptr, nullptr, 0, b->ctx_len, b->page_table,
                       b->page_stride, st);

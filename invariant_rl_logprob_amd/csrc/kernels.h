@@ -178,6 +178,34 @@ struct IndexerArgs {
   int32_t *sel_copy;  // optional caller copy [all rows, topk] at row0, or null
 };
 
+// Mamba-2 SSD mixer (csrc/ssd.hip).  One call's sequences (prefill) or rows (decode),
+// their cache slots (state + the current chunk's inputs) and the workspace it plans in.
+constexpr int kSsdP = 64, kSsdN = 128, kSsdQ = 128;  // head channels, state size, chunk
+struct SsdArgs {
+  int mode;                  // 0: packed prefill tokens (cu, start_pos); 1: decode rows (ctx_len)
+  int n_seqs, n_tok;
+  const int32_t *cu, *start_pos, *ctx_len;
+  const int32_t *page_table;  // slot id of sequence s at [s * page_stride]
+  int page_stride;
+  uint8_t *pool;
+  long slot_bytes;
+  int n_slots, H, G;
+  const bf16_t *x, *B, *C;    // [n_tok, H, 64], [n_tok, G, 128], [n_tok, G, 128]
+  const float *dt;            // [n_tok, H], positive
+  const float *A, *D;         // [H]
+  int max_chunks, max_done;   // host bounds on the chunks the call touches / completes
+  int32_t *plan;              // [6 * n_seqs + 2]
+  float *dS, *entry, *dec;    // per completed chunk: [max_done][H][64][128] x 2, [max_done][H]
+  bf16_t *y;                  // [n_tok, H, 64]
+};
+long ssd_slot_bytes(int H, int G);
+hipError_t launch_ssd_plan(const SsdArgs &a, hipStream_t st);
+hipError_t launch_ssd_state(const SsdArgs &a, hipStream_t st);
+hipError_t launch_ssd_scan(const SsdArgs &a, hipStream_t st);
+hipError_t launch_ssd_out(const SsdArgs &a, hipStream_t st);
+hipError_t launch_ssd_commit(const SsdArgs &a, hipStream_t st);
+hipError_t launch_ssd_write(const SsdArgs &a, hipStream_t st);
+
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t st);
 hipError_t launch_topk(const IndexerArgs &a, hipStream_t st);
 

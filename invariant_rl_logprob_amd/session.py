@@ -13,7 +13,7 @@ from typing import Dict, List, Optional, Sequence
 
 import torch
 
-from . import (RIL_ATTN_GQA, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch, make_prefill_batch,
+from . import (RIL_ATTN_GQA, RIL_ATTN_SSD, RIL_INPUT_QKV, RIL_INPUT_TOKENS, make_decode_batch, make_prefill_batch,
                ril_decode_graph_create, ril_decode_step_logprobs, ril_graph_destroy, ril_graph_launch, ril_kv_alloc, ril_kv_assign, ril_kv_free, ril_kv_page_bytes,
                ril_kv_release, ril_kv_write, ril_lm_head_packed_bytes, ril_model_create, ril_model_desc,
                ril_model_destroy, ril_pack_lm_head, ril_prefill_logprobs, ril_set_policy,
@@ -44,8 +44,13 @@ class Session:
                  input_mode=RIL_INPUT_QKV, d_model=0, embed=None, w_qkv=None, w_o=None, norm_attn=None,
                  norm_final=None, attn_kind=RIL_ATTN_GQA, rope_dim=0, index_heads=0, index_dim=0, topk=0,
                  kv_dtype=0, k_scale_exp=0, v_scale_exp=0, d_ff=0, w_gate_up=None, w_down=None, norm_mlp=None,
-                 lm_dtype=RIL_LM_BF16, proj_dtype=RIL_PROJ_BF16, device="cuda"):
+                 lm_dtype=RIL_LM_BF16, proj_dtype=RIL_PROJ_BF16, ssm_A=None, ssm_D=None, device="cuda"):
         self.device = torch.device(device)
+        # SSD mixer: one cache slot ("page") per sequence; A and D fp32 [H] on the device
+        self.ssd = attn_kind == RIL_ATTN_SSD
+        if self.ssd:
+            ssm_A = ssm_A.to(self.device, torch.float32).contiguous()
+            ssm_D = ssm_D.to(self.device, torch.float32).contiguous()
         # the lm-head weight lives in the library's packed layout (w_lm stays row-major):
         # bf16 operands, or block-FP8 codes and scales for the W8A8 head
         w_lm = w_lm.contiguous()
@@ -64,14 +69,15 @@ class Session:
                 ril_quantize_weight_fp8(w, out)
                 return out
             w_qkv, w_o, w_gate_up, w_down = q8(w_qkv), q8(w_o), q8(w_gate_up), q8(w_down)
-        self._keep = [embed, w_qkv, w_o, norm_attn, norm_final, w_gate_up, w_down, norm_mlp]
+        self._keep = [embed, w_qkv, w_o, norm_attn, norm_final, w_gate_up, w_down, norm_mlp, ssm_A, ssm_D]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         self.desc = ril_model_desc(attn_kind, input_mode, d_model, n_q_heads, n_kv_heads, head_dim, rope_dim,
                                    index_heads, index_dim, topk, d_head, vocab, PAGE, split_tokens, max_rows,
                                    max_tokens, max_ctx, softmax_scale, rms_eps, p(embed), p(w_qkv), p(w_o),
                                    p(norm_attn), p(norm_final), p(self.w_lm_packed), kv_dtype, k_scale_exp,
                                    v_scale_exp, d_ff, p(w_gate_up), p(w_down), p(norm_mlp), lm_dtype,
-                                   proj_dtype)
+                                   proj_dtype, 128 if self.ssd else 0, 128 if self.ssd else 0, p(ssm_A),
+                                   p(ssm_D))
         self.model = ril_model_create(self.desc)
         self.H, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
         self.max_ctx = max_ctx
@@ -113,7 +119,7 @@ class Session:
     # -- pages ---------------------------------------------------------------
     def ensure(self, seq, n_tokens: int) -> None:
         have = self.pages.setdefault(seq, [])
-        need = math.ceil(n_tokens / PAGE) - len(have)
+        need = (1 if self.ssd else math.ceil(n_tokens / PAGE)) - len(have)
         if need > 0:
             have.extend(ril_kv_assign(self.kv, need))
 
@@ -132,7 +138,7 @@ class Session:
         return t
 
     def page_table(self, seqs: Sequence, ctx_bound: int) -> torch.Tensor:
-        stride = max(1, math.ceil(ctx_bound / PAGE))
+        stride = 1 if self.ssd else max(1, math.ceil(ctx_bound / PAGE))
         t = torch.full((len(seqs), stride), -1, dtype=torch.int32)
         for i, s in enumerate(seqs):
             ids = self._page_ids(s)
@@ -164,52 +170,55 @@ class Session:
         self._last = (k, v, ki, cu_t, st_t, pt)
 
     def prefill(self, seqs, starts, *, targets, qs=None, ks=None, vs=None, tokens=None, q_index=None,
-                k_index=None, selected_out=None, ctx_bound: Optional[int] = None) -> torch.Tensor:
+                k_index=None, selected_out=None, ctx_bound: Optional[int] = None, dts=None) -> torch.Tensor:
         """Packed prefill of sequences seqs[i] at positions starts[i].. ; returns fp32 [total]."""
         src = tokens if tokens is not None else qs
         lens = [t.shape[0] for t in src]
         cu, bound = self._packed(seqs, starts, lens)
         bound = ctx_bound or bound
-        q, k, v, tok, qi, ki = _cat(qs), _cat(ks), _cat(vs), _cat(tokens), _cat(q_index), _cat(k_index)
+        q, k, v, tok, qi, ki, dt = (_cat(qs), _cat(ks), _cat(vs), _cat(tokens), _cat(q_index), _cat(k_index),
+                                    _cat(dts))
         tgt = torch.cat(list(targets)).to(torch.int32).contiguous()
         cu_t, st_t = _i32(cu, self.device), _i32(list(starts), self.device)
         pt = self.page_table(seqs, bound)
         out = torch.empty(cu[-1], dtype=torch.float32, device=self.device)
         b = make_prefill_batch(cu_tokens=cu_t, start_pos=st_t, page_table=pt, max_ctx_bound=bound,
                                target_ids=tgt, token_ids=tok, q=q, k=k, v=v, q_index=qi, k_index=ki,
-                               selected_out=selected_out, total_tokens=cu[-1])
+                               selected_out=selected_out, total_tokens=cu[-1], dt=dt)
         ril_prefill_logprobs(self.model, self.kv, b, out, self.ws)
-        self._last = (q, k, v, tok, qi, ki, tgt, cu_t, st_t, pt)
+        self._last = (q, k, v, tok, qi, ki, tgt, cu_t, st_t, pt, dt)
         return out
 
-    def _decode_batch(self, seqs, ctx, targets, q, k, v, tokens, q_index, k_index, selected_out, ctx_bound):
+    def _decode_batch(self, seqs, ctx, targets, q, k, v, tokens, q_index, k_index, selected_out, ctx_bound,
+                      dt=None):
         ctx = [int(c) for c in ctx]
         for s, c in zip(seqs, ctx):
             self.ensure(s, c)
         bound = ctx_bound or max(ctx)
         keep = {"ctx": _i32(ctx, self.device), "pt": self.page_table(seqs, bound),
                 "tgt": targets.to(torch.int32).contiguous(), "tok": _c(tokens), "q": _c(q), "k": _c(k),
-                "v": _c(v), "qi": _c(q_index), "ki": _c(k_index)}
+                "v": _c(v), "qi": _c(q_index), "ki": _c(k_index), "dt": _c(dt)}
         b = make_decode_batch(ctx_len=keep["ctx"], page_table=keep["pt"], max_ctx_bound=bound,
                               target_ids=keep["tgt"], token_ids=keep["tok"], q=keep["q"], k=keep["k"],
-                              v=keep["v"], q_index=keep["qi"], k_index=keep["ki"], selected_out=selected_out)
+                              v=keep["v"], q_index=keep["qi"], k_index=keep["ki"], selected_out=selected_out,
+                              dt=keep["dt"])
         return b, keep
 
     def decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None, q_index=None, k_index=None,
-               selected_out=None, ctx_bound: Optional[int] = None) -> torch.Tensor:
+               selected_out=None, ctx_bound: Optional[int] = None, dt=None) -> torch.Tensor:
         """One decode step: row i of sequence seqs[i] at context ctx[i]; returns fp32 [rows]."""
         b, keep = self._decode_batch(seqs, ctx, targets, q, k, v, tokens, q_index, k_index, selected_out,
-                                     ctx_bound)
+                                     ctx_bound, dt)
         out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
         ril_decode_step_logprobs(self.model, self.kv, b, out, self.ws)
         self._last = keep
         return out
 
     def prepare_decode(self, seqs, ctx, *, targets, q=None, k=None, v=None, tokens=None, q_index=None,
-                       k_index=None, ctx_bound: Optional[int] = None):
+                       k_index=None, ctx_bound: Optional[int] = None, dt=None):
         """Build a decode batch once; returns (launch, out) where launch() enqueues the step
         on the current stream with no host-side tensor work (for timed loops)."""
-        b, keep = self._decode_batch(seqs, ctx, targets, q, k, v, tokens, q_index, k_index, None, ctx_bound)
+        b, keep = self._decode_batch(seqs, ctx, targets, q, k, v, tokens, q_index, k_index, None, ctx_bound, dt)
         out = torch.empty(len(seqs), dtype=torch.float32, device=self.device)
         stream = torch.cuda.current_stream(self.device).cuda_stream
 

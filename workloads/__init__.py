@@ -19,6 +19,7 @@ bits to the other side.
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Dict, Sequence, Tuple
 
 import torch
@@ -324,6 +325,69 @@ def sparse_row(row: int, w: SparseMLADecode = SPARSE_MLA_B32, device="cpu", ctx:
         "q_index": randn((R, w.index_heads, w.index_dim), key(s, "q_index", row, L), 1.0, device,
                          dtype=torch.float32),
         "target": randint(0, w.vocab - 1, (R,), key(s, "target", row, L), device),
+    }
+
+
+def randu(shape, k: int, lo: float, hi: float, device="cpu") -> torch.Tensor:
+    """Uniform fp32 draws in [lo, hi); keyed by ``k``."""
+    return torch.rand(tuple(shape), generator=_gen(k, device), device=device, dtype=torch.float32) * (hi - lo) + lo
+
+
+@dataclasses.dataclass(frozen=True)
+class SSDDecode:
+    """Mamba-2 mixer decode rows (the Nemotron family's SSD layer): H heads of 64
+    channels, G groups of 128 state rows, chunks of 128 positions; per position x [H, 64],
+    B and C [G, 128] (bf16, N(0, 1)) and dt [H] (fp32, log-uniform in [0.001, 0.1], the
+    Mamba time-step range); per head A = -exp(U[0, ln 16]) and D = 1 + 0.1 N(0, 1) (fp32);
+    the mixer output (H x 64 = 8192 wide) goes through an 8192 -> 4096 projection and the
+    4096 x 129280 lm-head."""
+    rows: int = 64
+    n_heads: int = 128
+    head_dim: int = 64
+    n_groups: int = 8
+    d_state: int = 128
+    chunk: int = 128
+    ctx_lo: int = 1024
+    ctx_hi: int = 8192
+    vocab: int = 129280
+    d_head: int = 4096
+    init_std: float = 0.02
+    rms_eps: float = 1e-6
+    recompute_tokens: int = 16
+    seed: int = 6
+
+
+SSD_DECODE_B64 = SSDDecode()
+
+
+def ssd_ctx(row: int, w: SSDDecode = SSD_DECODE_B64) -> int:
+    return int(randint(w.ctx_lo, w.ctx_hi, (1,), key(w.seed, "ctx", row))[0])
+
+
+def ssd_params(w: SSDDecode = SSD_DECODE_B64, device="cpu") -> Dict[str, torch.Tensor]:
+    """Per-head A (negative) and D, fp32, and the head: the projection [d_head, H*64] and
+    the lm-head [V, d_head]."""
+    H = w.n_heads
+    return {
+        "A": -torch.exp(randu((H,), key(w.seed, "A"), 0.0, math.log(16.0), device)),
+        "D": 1.0 + 0.1 * randn((H,), key(w.seed, "D"), 1.0, device, torch.float32),
+        "w_o": randn((w.d_head, H * w.head_dim), key(w.seed, "w_o"), w.init_std, device),
+        "w_lm": randn((w.vocab, w.d_head), key(w.seed, "w_lm"), w.init_std, device),
+    }
+
+
+def ssd_row(row: int, w: SSDDecode = SSD_DECODE_B64, device="cpu", ctx: int = None):
+    """Every position's inputs of one sequence of ctx positions: x [L, H, 64], B and C
+    [L, G, 128], dt [L, H] fp32 and the sampled ids [L] whose logprobs are asked for."""
+    L = ssd_ctx(row, w) if ctx is None else int(ctx)
+    s = w.seed
+    return {
+        "ctx": L,
+        "x": randn((L, w.n_heads, w.head_dim), key(s, "x", row, L), 1.0, device),
+        "B": randn((L, w.n_groups, w.d_state), key(s, "B", row, L), 1.0, device),
+        "C": randn((L, w.n_groups, w.d_state), key(s, "C", row, L), 1.0, device),
+        "dt": torch.exp(randu((L, w.n_heads), key(s, "dt", row, L), math.log(1e-3), math.log(1e-1), device)),
+        "target": randint(0, w.vocab - 1, (L,), key(s, "target", row, L), device),
     }
 
 
