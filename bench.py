@@ -871,12 +871,98 @@ def bench_mla_prefill(args, fp8=False):
     return res
 
 
+def bench_ssd(args):
+    """Mamba-2 SSD mixer decode, 64 rows at contexts U[1024, 8192]: H = 128 heads of 64
+    channels, 8 groups of 128 state rows, chunks of 128; the 8192 -> 4096 projection and
+    the 4096 x 129280 lm-head.  History is laid down by prefill calls of 4096 tokens (timed:
+    the trainer-side recompute rate of this mixer); the last 16 positions of every row are
+    decoded step by step and recomputed by one prefill call (diff, must be 0); the decode
+    step is timed like the other workloads.  The mixer-output kernel's algorithmic bytes
+    per row: the fp32 state entering the chunk (H x 64 x 128 x 4 = 4 MiB) plus the chunk's
+    earlier inputs (x, B, dt: 18.9 KB per position) and the row's own inputs."""
+    import numpy as np
+    import torch
+    import invariant_rl_logprob_amd as ril
+    import workloads as wl
+    from invariant_rl_logprob_amd.metrics import mismatch
+    from ssd_case import SSDCase
+
+    w = wl.SSD_DECODE_B64
+    rows = list(range(w.rows))
+    t0 = time.time()
+    case = SSDCase(w, rows, device="cuda", shuffle_seed=0x5EED, tags=2, max_rows=w.rows, max_tokens=4096)
+    ctx = [case.ctx(r) for r in rows]
+    log(f"ssd: data ready in {time.time() - t0:.1f}s; sum ctx = {sum(ctx)}")
+    n = w.recompute_tokens
+    torch.cuda.synchronize()
+    ril.ril_trace_enable(True)
+    t1 = time.time()
+    case.history("d", rows, n)
+    torch.cuda.synchronize()
+    hist_s = time.time() - t1
+    kt = {}
+    for kid, name in enumerate(ril.KERNEL_NAMES):
+        tot, cnt = ril.ril_trace_read(kid)
+        if cnt:
+            kt[name] = round(tot, 3)
+    ril.ril_trace_enable(False)
+    hist_tokens = sum(c_ - n for c_ in ctx)
+    log(f"ssd: history {hist_tokens} tokens in {hist_s:.2f} s, kernel ms {kt}")
+    dec = torch.stack([case.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
+    case.history("p", rows, n)
+    pre = case.prefill_last("p", rows, n)
+    torch.cuda.synchronize()
+    diff = mismatch(dec, pre)
+    log(f"ssd: prefill vs decode over {diff['tokens']} tokens: {diff}")
+
+    d = case.data
+    pick = lambda key: torch.stack([d[r][key][case.ctx(r) - 1] for r in rows])  # noqa: E731
+    launch, out = case.sess.prepare_decode([("d", r) for r in rows], ctx, targets=pick("target").to(torch.int32),
+                                           q=pick("C"), k=pick("B"), v=pick("x"), dt=pick("dt"))
+    ms_step, kern = timed_steps(launch, args.steps, args.warmup)
+    last_equal = bool(np.array_equal(out.cpu().view(torch.int32).numpy(),
+                                     dec[:, -1].cpu().view(torch.int32).numpy()))
+    H, P, N, G, Q = w.n_heads, w.head_dim, w.d_state, w.n_groups, w.chunk
+    per_pos = H * P * 2 + G * N * 2 + H * 4
+    out_bytes = sum(H * P * N * 4 + ((c_ - 1) % Q) * per_pos + per_pos + G * N * 2 for c_ in ctx)
+    out_us = kern["ssd_out"]["avg_us"]
+    gbps = out_bytes / (out_us * 1e-6) / 1e9
+    roof = roofline_hbm("ssd_out", gbps, out_bytes, out_us)
+
+    cpu = None
+    if not args.no_cpu and args.cpu_rows > 0:
+        import oracle  # noqa: F401  (the cpu_baseline leg: case.oracle_row runs the fp64 recurrence)
+        r0 = min(rows, key=lambda r: case.ctx(r))
+        t2 = time.time()
+        lp_o, _ = case.oracle_row(r0)
+        secs = time.time() - t2
+        cpu = {"value": round(1 / secs, 4), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               **host_info(), "sample": f"decode row {r0} at context {case.ctx(r0)} (the recurrence over every "
+                                        f"position, projection and lm-head in fp64), {secs:.1f} s",
+               "max_abs_diff_vs_gpu": float(abs(lp_o - out.cpu().numpy()[rows.index(r0)]))}
+        log(f"ssd oracle: {cpu}")
+    res = {
+        "value": round(len(rows) / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+        "config": {"workload": "ssd_decode_b64: 64 Mamba-2 mixer decode rows (128 heads x 64 channels, 8 groups "
+                               "x 128 state rows, chunks of 128) at contexts U[1024,8192], o-proj 8192x4096, "
+                               "lm-head 4096x129280", "rows": len(rows), "sum_ctx": sum(ctx), "chunk": Q},
+        "history_prefill": {"tokens": hist_tokens, "seconds": round(hist_s, 3),
+                            "tokens_per_s": round(hist_tokens / hist_s, 1), "kernel_ms": kt},
+        "diff": diff, "timed_step_equals_checked_decode": last_equal,
+        "kernels_avg_us": {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    case.sess.close()
+    return res
+
+
 WORKLOADS = {"gqa_decode_b64": bench_gqa, "gqa_decode_b64_fp8": bench_gqa_fp8,
              "gqa_decode_b64_w8a8": bench_gqa_w8a8, "gqa_decode_b64_fp8_w8a8": bench_gqa_fp8_w8a8, "mla_decode_b128": bench_mla,
              "sparse_mla_b32": bench_sparse, "long_mix": bench_long,
              "mla_decode_b128_fp8": lambda a: bench_mla(a, fp8=True),
              "sparse_mla_b32_fp8": lambda a: bench_sparse(a, fp8=True),
-             "mla_prefill_32k": bench_mla_prefill, "mla_prefill_32k_fp8": lambda a: bench_mla_prefill(a, fp8=True)}
+             "mla_prefill_32k": bench_mla_prefill, "mla_prefill_32k_fp8": lambda a: bench_mla_prefill(a, fp8=True),
+             "ssd_decode_b64": bench_ssd}
 
 
 def main():

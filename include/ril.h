@@ -88,7 +88,9 @@ typedef enum ril_status {
  *   ssm_chunk = 128 positions counted from position 0, every phase through the same
  *   kernels (csrc/ssd.hip), so a position's bits do not depend on how its sequence is cut
  *   into calls.  The "KV pool" holds one cache slot per sequence (ril_kv_page_bytes: the
- *   state entering the current chunk, fp32, and that chunk's earlier inputs): page_table
+ *   state entering the current chunk, fp32, kept in one of two buffers by the chunk's
+ *   parity so that a repeated decode step reads what it read before, and that chunk's
+ *   earlier inputs): page_table
  *   column 0 of a sequence is its slot, page_stride >= 1.  A slot's state is read only
  *   when a sequence continues past its first chunk; a sequence restarted at position 0
  *   starts from zero state.  Prefill calls carry at most max_rows sequences; history is

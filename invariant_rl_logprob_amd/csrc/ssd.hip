@@ -29,6 +29,9 @@
 //
 // Per sequence a cache slot holds the state entering the current chunk (fp32 [H][P][N])
 // and the current chunk's earlier inputs (x [Q][H][P], B [Q][G][N] bf16, dt [Q][H] fp32).
+// The state of chunk c sits in one of two buffers by the parity of c, so the step that
+// completes a chunk writes the next chunk's state beside the one it read: repeating a
+// decode step (a replay, a retry) reads and writes the same bytes again.
 // A call runs: plan (its chunks), state (the exit-state sums of the chunks it completes),
 // scan (states through those chunks, in order), out (every position's y), commit (the
 // new entry state into the slot), write (the inputs of an unfinished last chunk into the
@@ -39,11 +42,24 @@
 namespace ril {
 
 constexpr int kSsdPad = kSsdQ + 8;  // LDS row length (elements) of a 128-wide operand tile
+constexpr int kSsdXRow = kSsdP + 8;  // LDS row length (elements) of the x tile [s][p]
+
+// Transposing LDS reads of a tile stored position-major ([s][c], row length RL elements):
+// lane L = 4e + m of each 16-lane group addresses the 4 columns c0 + 4m .. of row s0 + e,
+// and ds_read_b64_tr_b16 hands lane i the column c0 + i of rows s0 .. s0 + 3 (4 values,
+// rows ascending): one MFMA operand half with K along the positions.  This returns the
+// lane's base address for row 0, column 0 of the tile; callers add s0 and c0 as an
+// immediate offset.
+template <int RL>
+__device__ __forceinline__ uint32_t ssd_tr_base(const bf16_t *tile) {
+  const int l = threadIdx.x & 15;
+  return lds_addr(tile) + 2 * ((l >> 2) * RL + 4 * (l & 3));
+}
 constexpr int kSsdThreads = 256;
 
 __host__ __device__ inline long ssd_state_bytes(int H) { return (long)H * kSsdP * kSsdN * 4; }
 long ssd_slot_bytes(int H, int G) {
-  const long b = ssd_state_bytes(H) + (long)kSsdQ * H * kSsdP * 2 + (long)kSsdQ * G * kSsdN * 2 + (long)kSsdQ * H * 4;
+  const long b = 2 * ssd_state_bytes(H) + (long)kSsdQ * H * kSsdP * 2 + (long)kSsdQ * G * kSsdN * 2 + (long)kSsdQ * H * 4;
   return (b + 255) / 256 * 256;
 }
 
@@ -82,7 +98,7 @@ __device__ __forceinline__ int ssd_owner(const int32_t *pre, int n, int b) {
 }
 
 struct SsdSlot {
-  float *state;
+  float *state;  // two [H][P][N] buffers: the state entering chunk c at state + (c & 1) * H P N
   bf16_t *x, *B;
   float *dt;
 };
@@ -90,7 +106,7 @@ __device__ __forceinline__ SsdSlot ssd_slot(uint8_t *pool, long slot_bytes, int 
   uint8_t *b = pool + (long)slot * slot_bytes;
   SsdSlot s;
   s.state = reinterpret_cast<float *>(b);
-  s.x = reinterpret_cast<bf16_t *>(b + ssd_state_bytes(H));
+  s.x = reinterpret_cast<bf16_t *>(b + 2 * ssd_state_bytes(H));
   s.B = s.x + (long)kSsdQ * H * kSsdP;
   s.dt = reinterpret_cast<float *>(s.B + (long)kSsdQ * G * kSsdN);
   return s;
@@ -187,8 +203,8 @@ __global__ void ssd_plan_kernel(SsdArgs a) {
 // 4 waves: wave w owns channels 16w .. 16w + 15 and all 128 state rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Xt[kSsdP][kSsdPad];  // x^T [p][s]
-  __shared__ __attribute__((aligned(16))) bf16_t Bt[kSsdN][kSsdPad];  // B^T [n][s]
+  __shared__ __attribute__((aligned(16))) bf16_t Xn[kSsdQ][kSsdXRow];  // x [s][p]
+  __shared__ __attribute__((aligned(16))) bf16_t Bn[kSsdQ][kSsdPad];   // B [s][n]
   __shared__ float dts[kSsdQ], Ls[kSsdQ], ws[kSsdQ];
   const int e_ = blockIdx.x, h = blockIdx.y, n = a.n_seqs;
   const int s_ = ssd_owner(a.plan + n + 1, n, e_);
@@ -199,27 +215,33 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
   const int g = h / (a.H / a.G);
   const SsdSlot sl = ssd_slot(a.pool, a.slot_bytes, q.slot, a.H, a.G);
   const int tid = threadIdx.x;
-  // x rows: 8 pieces of 8 channels per position; B rows: 16 pieces of 8 state rows
-  for (int it = tid; it < kSsdQ * 8; it += kSsdThreads) {
-    const int j = it >> 3, pc = it & 7;
-    const SsdTok tk = ssd_tok(a, q, sl, c0 + j, h, g);
-    const u32x4 v = ld16(tk.x + 8 * pc);
+  // x rows: 8 pieces of 8 channels per position; B rows: 16 pieces of 8 state rows; every
+  // load of a thread issued before its first store
+  constexpr int kXPer = kSsdQ * 8 / kSsdThreads, kBPer = kSsdQ * 16 / kSsdThreads;
+  u32x4 xv[kXPer], bv[kBPer];
+  float dv[kXPer];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Xt[8 * pc + 2 * e][j] = (bf16_t)(v[e] & 0xffffu);
-      Xt[8 * pc + 2 * e + 1][j] = (bf16_t)(v[e] >> 16);
-    }
-    if (pc == 0) dts[j] = tk.dt;
+  for (int k = 0; k < kXPer; ++k) {
+    const int it = tid + kSsdThreads * k;
+    const SsdTok tk = ssd_tok(a, q, sl, c0 + (it >> 3), h, g);
+    xv[k] = ld16(tk.x + 8 * (it & 7));
+    dv[k] = tk.dt;
   }
-  for (int it = tid; it < kSsdQ * 16; it += kSsdThreads) {
-    const int j = it >> 4, nc = it & 15;
-    const SsdTok tk = ssd_tok(a, q, sl, c0 + j, h, g);
-    const u32x4 v = ld16(tk.B + 8 * nc);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Bt[8 * nc + 2 * e][j] = (bf16_t)(v[e] & 0xffffu);
-      Bt[8 * nc + 2 * e + 1][j] = (bf16_t)(v[e] >> 16);
-    }
+  for (int k = 0; k < kBPer; ++k) {
+    const int it = tid + kSsdThreads * k;
+    bv[k] = ld16(ssd_tok(a, q, sl, c0 + (it >> 4), h, g).B + 8 * (it & 15));
+  }
+#pragma unroll
+  for (int k = 0; k < kXPer; ++k) {
+    const int it = tid + kSsdThreads * k, j = it >> 3, pc = it & 7;
+    *reinterpret_cast<u32x4 *>(&Xn[j][8 * pc]) = xv[k];
+    if (pc == 0) dts[j] = dv[k];
+  }
+#pragma unroll
+  for (int k = 0; k < kBPer; ++k) {
+    const int it = tid + kSsdThreads * k;
+    *reinterpret_cast<u32x4 *>(&Bn[it >> 4][8 * (it & 15)]) = bv[k];
   }
   __syncthreads();
   const float A = a.A[h];
@@ -229,27 +251,51 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
   if (tid == 0) a.dec[(long)e_ * a.H + h] = ssd_exp(Ls[kSsdQ - 1]);
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+  // x^T operand (rows p = 16 wave + i, K = s = 32 kk + 8 grp + 0..7) by transposing reads
+  const uint32_t xa = ssd_tr_base<kSsdXRow>(&Xn[8 * grp][16 * wave]);
+  u32x2 xr[2 * (kSsdQ / 32)];
+  static_for<kSsdQ / 32>([&](auto kk_) {
+    constexpr int kk = decltype(kk_)::value;
+    xr[2 * kk] = lds_rdtr<2 * 32 * kk * kSsdXRow>(xa);
+    xr[2 * kk + 1] = lds_rdtr<2 * (32 * kk + 4) * kSsdXRow>(xa);
+  });
+  lds_wait<0>();
   bf16x8 xop[kSsdQ / 32];
 #pragma unroll
-  for (int kk = 0; kk < kSsdQ / 32; ++kk)
-    xop[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Xt[16 * wave + r16][32 * kk + 8 * grp]));
+  for (int kk = 0; kk < kSsdQ / 32; ++kk) {
+    settle(xr[2 * kk]);
+    settle(xr[2 * kk + 1]);
+    xop[kk] = as_bf16x8(u32x4{xr[2 * kk][0], xr[2 * kk][1], xr[2 * kk + 1][0], xr[2 * kk + 1][1]});
+  }
+  const uint32_t ba = ssd_tr_base<kSsdPad>(&Bn[8 * grp][0]);
   float *out = a.dS + ((long)e_ * a.H + h) * (kSsdP * kSsdN);
-  for (int nb = 0; nb < kSsdN / 16; ++nb) {
+  static_for<kSsdN / 16>([&](auto nb_) {
+    constexpr int nb = decltype(nb_)::value;
+    // B operand (K = s, column n = 16 nb + i), each value times w_s, rounded to bf16
+    u32x2 br[2 * (kSsdQ / 32)];
+    static_for<kSsdQ / 32>([&](auto kk_) {
+      constexpr int kk = decltype(kk_)::value;
+      br[2 * kk] = lds_rdtr<2 * (32 * kk * kSsdPad + 16 * nb)>(ba);
+      br[2 * kk + 1] = lds_rdtr<2 * ((32 * kk + 4) * kSsdPad + 16 * nb)>(ba);
+    });
+    lds_wait<0>();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < kSsdQ / 32; ++kk) {
-      const u32x4 raw = *reinterpret_cast<const u32x4 *>(&Bt[16 * nb + r16][32 * kk + 8 * grp]);
       u32x4 op;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s0 = 32 * kk + 8 * grp + 2 * e;
-        op[e] = pack2(bf2f((bf16_t)(raw[e] & 0xffffu)) * ws[s0], bf2f((bf16_t)(raw[e] >> 16)) * ws[s0 + 1]);
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        u32x2 raw = br[2 * kk + hlf];
+        settle(raw);
+        const int s0 = 32 * kk + 8 * grp + 4 * hlf;
+        op[2 * hlf] = pack2(bf2f((bf16_t)(raw[0] & 0xffffu)) * ws[s0], bf2f((bf16_t)(raw[0] >> 16)) * ws[s0 + 1]);
+        op[2 * hlf + 1] = pack2(bf2f((bf16_t)(raw[1] & 0xffffu)) * ws[s0 + 2], bf2f((bf16_t)(raw[1] >> 16)) * ws[s0 + 3]);
       }
       acc = mfma(xop[kk], as_bf16x8(op), acc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[(16 * wave + 4 * grp + i) * kSsdN + 16 * nb + r16] = acc[i];
-  }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -264,7 +310,7 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(SsdArgs a) {
   const int cf = q.p0 / kSsdQ;
   constexpr int kPer = kSsdP * kSsdN / (4 * kSsdThreads);  // float4s per thread (8)
   const SsdSlot sl = ssd_slot(a.pool, a.slot_bytes, q.slot, a.H, a.G);
-  const float *s_in = sl.state + (long)h * kSsdP * kSsdN;
+  const float *s_in = sl.state + ((long)(cf & 1) * a.H + h) * kSsdP * kSsdN;
   f32x4 S[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k)
@@ -286,14 +332,14 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(SsdArgs a) {
 
 // ---------------------------------------------------------------------------
 // out: every position of the call in one chunk, one head.  Grid (chunks, H), 4 waves;
-// the chunk's inputs up to the call's last position are staged in LDS (x^T [p][s],
-// B [s][n], dt) with the entry state as bf16 [p][n]; 16-position column blocks go to
-// the waves in turn.  Per block: G^T (rows s, columns t), W^T from G^T's output layout
+// the chunk's inputs up to the call's last position (x [s][p], read transposed, B [s][n],
+// dt) and the entry state as bf16 [p][n] are staged in LDS; 16-position column blocks go
+// to the waves in turn.  Per block: G^T (rows s, columns t), W^T from G^T's output layout
 // (so the W product runs its 32-wide steps in the order s = 4g + i, 16 + 4g + i of each
 // step, lane group g), then Y2^T and Y1^T (rows p, columns t) and the epilogue.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(SsdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Xt[kSsdP][kSsdPad];  // x^T [p][s]
+  __shared__ __attribute__((aligned(16))) bf16_t Xn[kSsdQ][kSsdXRow];  // x [s][p]
   __shared__ __attribute__((aligned(16))) bf16_t Sb[kSsdP][kSsdPad];  // bf16(S_in) [p][n]
   __shared__ __attribute__((aligned(16))) bf16_t Bc[kSsdQ][kSsdPad];  // B [s][n]
   __shared__ float dts[kSsdQ], Ls[kSsdQ];
@@ -312,104 +358,165 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_out_kernel(SsdArgs a) {
     return;
   }
   const SsdSlot sl = ssd_slot(a.pool, a.slot_bytes, q.slot, a.H, a.G);
-  for (int it = tid; it < kSsdQ * 8; it += kSsdThreads) {
-    const int j = it >> 3, pc = it & 7;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    float d = 0.f;
-    if (j < tb) {
-      const SsdTok tk = ssd_tok(a, q, sl, c0 + j, h, g);
-      v = ld16(tk.x + 8 * pc);
-      d = tk.dt;
-    }
+  // Stage the chunk's inputs up to the call's last position and the entry state in LDS.
+  // Every load of a thread is issued before its first store, and a position past the
+  // call loads a valid one and stores zeros, so the loads carry no branches: a few memory
+  // round trips per workgroup instead of one per piece.
+  constexpr int kXPer = kSsdQ * 8 / kSsdThreads, kBPer = kSsdQ * 16 / kSsdThreads;
+  constexpr int kSPer = kSsdP * kSsdN / 8 / kSsdThreads;
+  const float *src = c == 0 ? nullptr
+                     : c == cf ? sl.state + ((long)(c & 1) * a.H + h) * kSsdP * kSsdN
+                               : a.entry + ((long)(q.done + (c - cf - 1)) * a.H + h) * (kSsdP * kSsdN);
+  u32x4 xv[kXPer], bv[kBPer];
+  float dv[kXPer];
+  f32x4 sv[2 * kSPer];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Xt[8 * pc + 2 * e][j] = (bf16_t)(v[e] & 0xffffu);
-      Xt[8 * pc + 2 * e + 1][j] = (bf16_t)(v[e] >> 16);
-    }
-    if (pc == 0) dts[j] = d;
+  for (int k = 0; k < kXPer; ++k) {
+    const int it = tid + kSsdThreads * k, j = it >> 3;
+    const SsdTok tk = ssd_tok(a, q, sl, c0 + min(j, tb - 1), h, g);
+    xv[k] = ld16(tk.x + 8 * (it & 7));
+    dv[k] = tk.dt;
   }
-  for (int it = tid; it < kSsdQ * 16; it += kSsdThreads) {
-    const int j = it >> 4, nc = it & 15;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (j < tb) v = ld16(ssd_tok(a, q, sl, c0 + j, h, g).B + 8 * nc);
-    *reinterpret_cast<u32x4 *>(&Bc[j][8 * nc]) = v;
+#pragma unroll
+  for (int k = 0; k < kBPer; ++k) {
+    const int it = tid + kSsdThreads * k, j = it >> 4;
+    bv[k] = ld16(ssd_tok(a, q, sl, c0 + min(j, tb - 1), h, g).B + 8 * (it & 15));
   }
-  {
-    const float *src = c == 0 ? nullptr
-                       : c == cf ? sl.state + (long)h * kSsdP * kSsdN
-                                 : a.entry + ((long)(q.done + (c - cf - 1)) * a.H + h) * (kSsdP * kSsdN);
-    for (int it = tid; it < kSsdP * kSsdN / 8; it += kSsdThreads) {
-      const int p = it >> 4, nc = it & 15;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (src) {
-        const f32x4 lo = *reinterpret_cast<const f32x4 *>(src + p * kSsdN + 8 * nc);
-        const f32x4 hi = *reinterpret_cast<const f32x4 *>(src + p * kSsdN + 8 * nc + 4);
-        w = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
-      }
-      *reinterpret_cast<u32x4 *>(&Sb[p][8 * nc]) = w;
-    }
+  const float *sp = src ? src : a.dec;  // any readable address when the state is zero
+#pragma unroll
+  for (int k = 0; k < kSPer; ++k) {
+    const int it = tid + kSsdThreads * k, off = src ? (it >> 4) * kSsdN + 8 * (it & 15) : 0;
+    sv[2 * k] = *reinterpret_cast<const f32x4 *>(sp + off);
+    sv[2 * k + 1] = *reinterpret_cast<const f32x4 *>(sp + off + 4);
+  }
+#pragma unroll
+  for (int k = 0; k < kXPer; ++k) {
+    const int it = tid + kSsdThreads * k, j = it >> 3, pc = it & 7;
+    *reinterpret_cast<u32x4 *>(&Xn[j][8 * pc]) = j < tb ? xv[k] : u32x4{0u, 0u, 0u, 0u};
+    if (pc == 0) dts[j] = j < tb ? dv[k] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < kBPer; ++k) {
+    const int it = tid + kSsdThreads * k, j = it >> 4;
+    *reinterpret_cast<u32x4 *>(&Bc[j][8 * (it & 15)]) = j < tb ? bv[k] : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < kSPer; ++k) {
+    const int it = tid + kSsdThreads * k;
+    const f32x4 lo = sv[2 * k], hi = sv[2 * k + 1];
+    const u32x4 w = src ? u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])}
+                        : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4 *>(&Sb[it >> 4][8 * (it & 15)]) = w;
   }
   __syncthreads();
   const float A = a.A[h], Dh = a.D[h];
   if (tid < 64) ssd_cumsum(dts, A, tb, Ls);
   __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
   const int cb0 = ta / 16, cb1 = (tb - 1) / 16;
-  for (int cb = cb0 + wave; cb <= cb1; cb += 4) {
-    const int t = 16 * cb + r16;  // this lane's column
-    const bool live = t >= ta && t < tb;
-    const long jt = q.tok0 + (c0 + t - q.p0);
-    // C^T operand (k = n, column t), zero for columns outside the call
+  // Column block cb: this lane's column t, the C^T operand (K = n, column t; zero for
+  // columns outside the call), L_t.
+  struct Col {
+    int t;
+    bool live;
+    long jt;
+    float Lt;
     bf16x8 cop[kSsdN / 32];
+  };
+  auto column = [&](int cb) {
+    Col c;
+    c.t = 16 * cb + r16;
+    c.live = c.t >= ta && c.t < tb;
+    c.jt = q.tok0 + (c0 + c.t - q.p0);
 #pragma unroll
     for (int kk = 0; kk < kSsdN / 32; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (live) v = ld16(a.C + (jt * a.G + g) * kSsdN + 32 * kk + 8 * grp);
-      cop[kk] = as_bf16x8(v);
+      if (c.live) v = ld16(a.C + (c.jt * a.G + g) * kSsdN + 32 * kk + 8 * grp);
+      c.cop[kk] = as_bf16x8(v);
     }
-    const float Lt = live ? Ls[t] : 0.f;
-    // W^T for s-blocks 0..7 (rows s = 16 sb + 4 grp + i), packed per 32-wide step
-    u32x4 wop[kSsdQ / 32];
+    c.Lt = c.live ? Ls[c.t] : 0.f;
+    return c;
+  };
+  // W^T of s-block sb (rows s = 16 sb + 4 grp + i): G^T's MFMA chain over n, then the
+  // decayed, dt-weighted value rounded to bf16 (0 past the column), as two packed words
+  auto wblock = [&](const Col &c, int sb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sb = 0; sb < kSsdQ / 16; ++sb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < kSsdN / 32; ++kk)
+      acc = mfma(as_bf16x8(*reinterpret_cast<const u32x4 *>(&Bc[16 * sb + r16][32 * kk + 8 * grp])), c.cop[kk], acc);
+    float w[4];
 #pragma unroll
-      for (int kk = 0; kk < kSsdN / 32; ++kk)
-        acc = mfma(as_bf16x8(*reinterpret_cast<const u32x4 *>(&Bc[16 * sb + r16][32 * kk + 8 * grp])), cop[kk], acc);
-      float w[4];
+    for (int i = 0; i < 4; ++i) {
+      const int s = 16 * sb + 4 * grp + i;
+      w[i] = (c.live && s <= c.t) ? acc[i] * ssd_exp(c.Lt - Ls[s]) * dts[s] : 0.f;
+    }
+    return u32x2{pack2(w[0], w[1]), pack2(w[2], w[3])};
+  };
+  // p-block pb: Y2^T (the W product, x^T read transposed in W's K order: s = 32 kk +
+  // 4 grp + 0..3, then 32 kk + 16 + 4 grp + 0..3), Y1^T (the state product) and the
+  // epilogue for channels 16 pb ..
+  const uint32_t xa = ssd_tr_base<kSsdXRow>(&Xn[4 * grp][0]);
+  auto outblock = [&](const Col &c, int pb, const u32x4 (&wop)[kSsdQ / 32]) {
+    const uint32_t xb = xa + 32 * pb;
+    u32x2 xr[2 * (kSsdQ / 32)];
+    static_for<kSsdQ / 32>([&](auto kk_) {
+      constexpr int kk = decltype(kk_)::value;
+      xr[2 * kk] = lds_rdtr<2 * 32 * kk * kSsdXRow>(xb);
+      xr[2 * kk + 1] = lds_rdtr<2 * (32 * kk + 16) * kSsdXRow>(xb);
+    });
+    lds_wait<0>();
+    f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = 16 * sb + 4 * grp + i;
-        w[i] = (live && s <= t) ? acc[i] * ssd_exp(Lt - Ls[s]) * dts[s] : 0.f;
+    for (int kk = 0; kk < kSsdQ / 32; ++kk) {
+      settle(xr[2 * kk]);
+      settle(xr[2 * kk + 1]);
+      const u32x2 lo = xr[2 * kk], hi = xr[2 * kk + 1];
+      y2 = mfma(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(wop[kk]), y2);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kSsdN / 32; ++kk)
+      y1 = mfma(as_bf16x8(*reinterpret_cast<const u32x4 *>(&Sb[16 * pb + r16][32 * kk + 8 * grp])), c.cop[kk], y1);
+    if (c.live) {
+      const float et = ssd_exp(c.Lt);
+      uint32_t o[2];
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int pp = 16 * pb + 4 * grp + i;
+        const float v0 = (y1[i] * et + y2[i]) + Dh * bf2f(Xn[c.t][pp]);
+        const float v1 = (y1[i + 1] * et + y2[i + 1]) + Dh * bf2f(Xn[c.t][pp + 1]);
+        o[i / 2] = pack2(v0, v1);
       }
-      wop[sb >> 1][2 * (sb & 1)] = pack2(w[0], w[1]);
-      wop[sb >> 1][2 * (sb & 1) + 1] = pack2(w[2], w[3]);
+      *reinterpret_cast<u32x2 *>(a.y + (c.jt * a.H + h) * kSsdP + 16 * pb + 4 * grp) = u32x2{o[0], o[1]};
     }
-    const float et = ssd_exp(Lt);
-#pragma unroll
-    for (int pb = 0; pb < kSsdP / 16; ++pb) {
-      const int p = 16 * pb + r16;
-      f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+  };
+  if (cb1 - cb0 + 1 >= 4) {
+    // many columns (prefill): each wave takes whole column blocks in turn
+    for (int cb = cb0 + wave; cb <= cb1; cb += 4) {
+      const Col c = column(cb);
+      u32x4 wop[kSsdQ / 32];
 #pragma unroll
       for (int kk = 0; kk < kSsdQ / 32; ++kk) {
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(&Xt[p][32 * kk + 4 * grp]);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(&Xt[p][32 * kk + 16 + 4 * grp]);
-        y2 = mfma(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(wop[kk]), y2);
+        const u32x2 lo = wblock(c, 2 * kk), hi = wblock(c, 2 * kk + 1);
+        wop[kk] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
 #pragma unroll
-      for (int kk = 0; kk < kSsdN / 32; ++kk)
-        y1 = mfma(as_bf16x8(*reinterpret_cast<const u32x4 *>(&Sb[p][32 * kk + 8 * grp])), cop[kk], y1);
-      if (live) {
-        uint32_t o[2];
+      for (int pb = 0; pb < kSsdP / 16; ++pb) outblock(c, pb, wop);
+    }
+  } else {
+    // few columns (decode): the four waves share each column block.  Wave w computes the
+    // W^T of s-blocks 2w and 2w + 1 -- step w of the W product's K -- and hands it over in
+    // LDS; then wave w runs p-block w.  The same MFMA chains as above, split over waves.
+    __shared__ u32x4 wx[4][64];
+    for (int cb = cb0; cb <= cb1; ++cb) {
+      const Col c = column(cb);
+      const u32x2 lo = wblock(c, 2 * wave), hi = wblock(c, 2 * wave + 1);
+      wx[wave][lane] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      __syncthreads();
+      u32x4 wop[kSsdQ / 32];
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const int pp = 16 * pb + 4 * grp + i;
-          const float v0 = (y1[i] * et + y2[i]) + Dh * bf2f(Xt[pp][t]);
-          const float v1 = (y1[i + 1] * et + y2[i + 1]) + Dh * bf2f(Xt[pp + 1][t]);
-          o[i / 2] = pack2(v0, v1);
-        }
-        *reinterpret_cast<u32x2 *>(a.y + (jt * a.H + h) * kSsdP + 16 * pb + 4 * grp) = u32x2{o[0], o[1]};
-      }
+      for (int kk = 0; kk < kSsdQ / 32; ++kk) wop[kk] = wx[kk][lane];
+      outblock(c, wave, wop);
+      __syncthreads();  // every wave has read wx before the next block overwrites it
     }
   }
 }
@@ -423,7 +530,8 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_commit_kernel(SsdArgs a) {
   if (q.slot < 0 || q.n_done <= 0) return;
   const SsdSlot sl = ssd_slot(a.pool, a.slot_bytes, q.slot, a.H, a.G);
   const float *fin = a.entry + ((long)(q.done + q.n_done - 1) * a.H + h) * (kSsdP * kSsdN);
-  float *dst = sl.state + (long)h * kSsdP * kSsdN;
+  const int c_next = q.p0 / kSsdQ + q.n_done;  // the chunk this state enters
+  float *dst = sl.state + ((long)(c_next & 1) * a.H + h) * kSsdP * kSsdN;
   for (int e = 4 * threadIdx.x; e < kSsdP * kSsdN; e += 4 * kSsdThreads)
     *reinterpret_cast<f32x4 *>(dst + e) = *reinterpret_cast<const f32x4 *>(fin + e);
 }

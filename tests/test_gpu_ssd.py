@@ -123,3 +123,19 @@ def test_ssd_reused_slot_starts_from_zero_state():
     assert c.sess.pages[("b", 1)] == [slot]
     again = _bits(c.decode_back("b", [1], 300))
     assert np.array_equal(first, again)
+
+
+def test_ssd_repeated_decode_step_gives_the_same_bits():
+    """A decode step can be replayed: the step that completes a chunk writes the next
+    chunk's state beside the one it reads (row 0's position 255 completes chunk 1)."""
+    c = _case(ctx=[256, 300])
+    rows = [0, 1]
+    c.history("d", rows, 2)
+    a1 = _bits(c.decode_back("d", rows, 2))
+    a2 = _bits(c.decode_back("d", rows, 2))
+    b1 = _bits(c.decode_back("d", rows, 1))
+    b2 = _bits(c.decode_back("d", rows, 1))
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+    c.history("p", rows, 2)
+    pre = _bits(c.prefill_last("p", rows, 2))
+    assert np.array_equal(pre[:, 0], a1) and np.array_equal(pre[:, 1], b1)
