@@ -43,13 +43,17 @@ constexpr int kMlaPage = kPage * kMlaDqk;     // 9216 elements: one page's laten
 constexpr int kMlaSlot = kMlaPage + 64;       // LDS slot of a page: +128 B spreads the banks
 constexpr int kMlaThreads = 512;              // 4 pairs of waves x 16 heads (H % 64 == 0)
 
-// Within a page slot, 16-byte unit u sits at LDS unit mla_swz(u) (an involution: it flips
-// bit 3, the token quad of the 8-token half, when bit 4, the parity of the 8-dim group, is
-// set).  Units of dims 8g .. 8g+7 and 8(g+1) .. of the same tokens then fall in different
-// LDS banks: the value operands' transposing reads, which take four tokens of each of two
-// adjacent 8-dim groups per 16 lanes, read 256 bytes apart without it (two-way bank
-// conflicts); the score reads stay conflict-free.
-__device__ __forceinline__ int mla_swz(int u) { return u ^ (((u >> 4) & 1) << 3); }
+// Within a page slot, 16-byte unit u sits at LDS unit mla_swz(u) (an involution: when
+// bit 4, the parity of the 8-dim group, is set, it flips bits 2 and 3, the token half and
+// the token quad within the page).  Without it the value operands' transposing reads,
+// which take four tokens of each of two adjacent 8-dim groups per 16 lanes, read 256
+// bytes apart: two-way LDS bank conflicts.  Of the maps that XOR one of bits 0-4 into
+// others, this is the one under which both those reads and the score reads (16 bytes
+// per lane, two page slots) run free of bank conflicts on gfx950's LDS (measured with
+// its bank-conflict counter); flipping bit 3 alone cleared the value reads but made the
+// score reads conflict two-way.  The map acts on bits 0-4 only, so adding 32 or more
+// units to a unit adds the same to its place.
+__device__ __forceinline__ int mla_swz(int u) { return u ^ (((u >> 4) & 1) * 12); }
 
 // FP8 latent pages (Bitwise-consistent RL post, section 4.2: FP8 storage, one write path,
 // one dequantizing read for every phase): a page's latent block is 16 x 576 E4M3 codes,
@@ -555,9 +559,6 @@ __global__ __launch_bounds__(512) void mla_split_fp8_kernel(
       }
     }
   };
-  // dequantize slot t & 1 into kt: bf16 unit v = tid + 512 k of the tile (page slot
-  // v / 1152, unit v % 1152 of its K layout) holds dims d0 .. d0 + 7 of token t of that
-  // slot, read as 8 codes at byte 576 (16 slot + t) + d0
   // dequantize slot t & 1 into kt: thread i converts units (i & 127) + 128 k, k = 0..8,
   // of page slot i / 128 (K layout: the unit holds dims d0 .. d0 + 7 of one token t of
   // the slot, whose codes sit at byte 576 (16 slot + t) + d0 of the staged tile).  Adding
