@@ -87,12 +87,22 @@ __device__ __forceinline__ uint32_t ord32(float f) {
 // 8-bit digits (histograms in LDS: their counts do not depend on thread order), then
 // the lowest-position ties at the threshold by a wave-ordered prefix count, then a
 // bitonic sort of the k positions into descending order.
+// Histograms: lane i of every wave counts into its own row of 257 counters, so the lanes
+// of one atomic instruction never share an address and lanes that hit the same bin sit
+// in different LDS banks (bin b of row i is in bank (i + b) mod 64); scores cluster in a
+// few digits, and one shared 256-bin histogram serialised most of its atomics.  The rows
+// are summed per bin, and one wave finds the threshold digit with a scan across lanes.
+// Selected positions are appended with one atomic per wave (a ballot gives each lane its
+// place); the sort fixes their order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *__restrict__ scores, int score_stride, int mode, int row0, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs, int ctx_bound, int K,
     int32_t *__restrict__ sel, int32_t *__restrict__ sel_copy) {
-  __shared__ int hist[256];
+  constexpr int kRow = 257;  // one lane's histogram row, padded against bank aliasing
+  constexpr int kUnroll = 8;  // score loads issued together per scan step
+  __shared__ int hist[64 * kRow];
+  __shared__ int part[4][256];
   __shared__ int buf[kTopkMax];
   __shared__ int wave_cnt[kTopkThreads / 64];
   __shared__ uint32_t s_prefix;
@@ -120,27 +130,60 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     s_prefix = 0u;
     s_need = K;
   }
+  const unsigned long long below_me = (1ull << lane) - 1ull;
   uint32_t mask = 0u;
+  int *my_row = hist + lane * kRow;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int b = tid; b < 256; b += kTopkThreads) hist[b] = 0;
+    for (int i = tid; i < 64 * kRow; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
-    for (int s = tid; s < n; s += kTopkThreads) {
-      const uint32_t u = ord32(sc[s]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+    for (int c0 = 0; c0 < n; c0 += kUnroll * kTopkThreads) {
+      uint32_t u[kUnroll];  // all loads of the batch in flight before the first count
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int s = c0 + j * kTopkThreads + tid;
+        u[j] = s < n ? ord32(sc[s]) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j)
+        if (c0 + j * kTopkThreads + tid < n && (u[j] & mask) == prefix) atomicAdd(&my_row[(u[j] >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, need = s_need;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + hist[b] >= need) {
-          s_prefix = prefix | ((uint32_t)b << shift);
+    {
+      const int b = tid & 255, q4 = tid >> 8;  // bin, quarter of the 64 rows
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c += hist[(16 * q4 + i) * kRow + b];
+      part[q4][b] = c;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds bins 255 - 4l .. 252 - 4l; the digit is the bin where the count of
+      // larger digits first reaches `need`
+      int cnt[4], loc = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = 255 - 4 * lane - j;
+        cnt[j] = part[0][b] + part[1][b] + part[2][b] + part[3][b];
+        loc += cnt[j];
+      }
+      int incl = loc;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+      }
+      const int need = s_need;
+      int cum = incl - loc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (cum < need && cum + cnt[j] >= need) {
+          s_prefix = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
           s_need = need - cum;
-          s_ties = hist[b];
-          break;
+          s_ties = cnt[j];
         }
-        cum += hist[b];
+        cum += cnt[j];
       }
     }
     mask |= 0xFFu << shift;
@@ -154,9 +197,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
   __syncthreads();
   // everything above the threshold, in any order (the sort below fixes the order)
-  for (int s = tid; s < n; s += kTopkThreads) {
-    const uint32_t u = ord32(sc[s]);
-    if (u > thr || (u == thr && need == ties)) buf[atomicAdd(&s_count, 1)] = s;
+  for (int c0 = 0; c0 < n; c0 += kUnroll * kTopkThreads) {
+    uint32_t u[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int s = c0 + j * kTopkThreads + tid;
+      u[j] = s < n ? ord32(sc[s]) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int s = c0 + j * kTopkThreads + tid;
+      const bool take = s < n && (u[j] > thr || (u[j] == thr && need == ties));
+      const unsigned long long bal = __ballot(take);
+      int base = 0;
+      if (lane == 0 && bal) base = atomicAdd(&s_count, __popcll(bal));
+      base = __shfl(base, 0, 64);
+      if (take) buf[base + __popcll(bal & below_me)] = s;
+    }
   }
   if (need < ties) {
     // the `need` lowest positions among the scores equal to the threshold
@@ -165,12 +222,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       const int s = c0 + tid;
       const bool flag = s < n && ord32(sc[s]) == thr;
       const unsigned long long bal = __ballot(flag);
-      const int below = __popcll(bal & ((1ull << lane) - 1ull));
+      const int below = __popcll(bal & below_me);
       if (lane == 0) wave_cnt[wave] = __popcll(bal);
       __syncthreads();
       int before = s_taken;
       for (int w = 0; w < wave; ++w) before += wave_cnt[w];
-      if (flag && before + below < need) buf[atomicAdd(&s_count, 1)] = s;
+      const bool take = flag && before + below < need;
+      const unsigned long long tb = __ballot(take);
+      int base = 0;
+      if (lane == 0 && tb) base = atomicAdd(&s_count, __popcll(tb));
+      base = __shfl(base, 0, 64);
+      if (take) buf[base + __popcll(tb & below_me)] = s;
       __syncthreads();
       if (tid == 0) {
         int t = 0;

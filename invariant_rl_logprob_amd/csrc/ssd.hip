@@ -41,8 +41,16 @@
 
 namespace ril {
 
-constexpr int kSsdPad = kSsdQ + 8;  // LDS row length (elements) of a 128-wide operand tile
-constexpr int kSsdXRow = kSsdP + 8;  // LDS row length (elements) of the x tile [s][p]
+// LDS row lengths (elements): 128-wide operand tiles (B, the entry state) and the x tile
+// [s][p].  The state kernel also groups rows in blocks of 8 with 64 elements (128 bytes)
+// after each block.  Measured with the LDS bank-conflict counter, per access: the
+// 16-byte reads of rows 16 sb + i take rows of 288 bytes (272 conflicted two-way); the
+// transposing reads take rows of 160 bytes, and the state kernel's, whose 16-lane groups
+// start 8 rows apart, also the block gap, which puts rows 8 apart half a bank row apart
+// (288- and 160-byte rows alone leave them two-way conflicted).
+constexpr int kSsdPad = kSsdQ + 16;
+constexpr int kSsdXRow = kSsdP + 16;
+constexpr int kSsdXBlk = 8 * kSsdXRow + 64, kSsdBBlk = 8 * kSsdPad + 64;  // elements per 8-row block
 
 // Transposing LDS reads of a tile stored position-major ([s][c], row length RL elements):
 // lane L = 4e + m of each 16-lane group addresses the 4 columns c0 + 4m .. of row s0 + e,
@@ -203,8 +211,8 @@ __global__ void ssd_plan_kernel(SsdArgs a) {
 // 4 waves: wave w owns channels 16w .. 16w + 15 and all 128 state rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Xn[kSsdQ][kSsdXRow];  // x [s][p]
-  __shared__ __attribute__((aligned(16))) bf16_t Bn[kSsdQ][kSsdPad];   // B [s][n]
+  __shared__ __attribute__((aligned(16))) bf16_t Xn[kSsdQ / 8][kSsdXBlk];  // x [s][p], 8-row blocks
+  __shared__ __attribute__((aligned(16))) bf16_t Bn[kSsdQ / 8][kSsdBBlk];  // B [s][n], 8-row blocks
   __shared__ float dts[kSsdQ], Ls[kSsdQ], ws[kSsdQ];
   const int e_ = blockIdx.x, h = blockIdx.y, n = a.n_seqs;
   const int s_ = ssd_owner(a.plan + n + 1, n, e_);
@@ -235,13 +243,14 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
 #pragma unroll
   for (int k = 0; k < kXPer; ++k) {
     const int it = tid + kSsdThreads * k, j = it >> 3, pc = it & 7;
-    *reinterpret_cast<u32x4 *>(&Xn[j][8 * pc]) = xv[k];
+    *reinterpret_cast<u32x4 *>(&Xn[j >> 3][(j & 7) * kSsdXRow + 8 * pc]) = xv[k];
     if (pc == 0) dts[j] = dv[k];
   }
 #pragma unroll
   for (int k = 0; k < kBPer; ++k) {
     const int it = tid + kSsdThreads * k;
-    *reinterpret_cast<u32x4 *>(&Bn[it >> 4][8 * (it & 15)]) = bv[k];
+    const int j = it >> 4;
+    *reinterpret_cast<u32x4 *>(&Bn[j >> 3][(j & 7) * kSsdPad + 8 * (it & 15)]) = bv[k];
   }
   __syncthreads();
   const float A = a.A[h];
@@ -252,12 +261,12 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
   // x^T operand (rows p = 16 wave + i, K = s = 32 kk + 8 grp + 0..7) by transposing reads
-  const uint32_t xa = ssd_tr_base<kSsdXRow>(&Xn[8 * grp][16 * wave]);
+  const uint32_t xa = ssd_tr_base<kSsdXRow>(&Xn[grp][16 * wave]);  // row 8 grp
   u32x2 xr[2 * (kSsdQ / 32)];
   static_for<kSsdQ / 32>([&](auto kk_) {
     constexpr int kk = decltype(kk_)::value;
-    xr[2 * kk] = lds_rdtr<2 * 32 * kk * kSsdXRow>(xa);
-    xr[2 * kk + 1] = lds_rdtr<2 * (32 * kk + 4) * kSsdXRow>(xa);
+    xr[2 * kk] = lds_rdtr<2 * 4 * kk * kSsdXBlk>(xa);  // rows 32 kk .., then 32 kk + 4 ..
+    xr[2 * kk + 1] = lds_rdtr<2 * (4 * kk * kSsdXBlk + 4 * kSsdXRow)>(xa);
   });
   lds_wait<0>();
   bf16x8 xop[kSsdQ / 32];
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
     settle(xr[2 * kk + 1]);
     xop[kk] = as_bf16x8(u32x4{xr[2 * kk][0], xr[2 * kk][1], xr[2 * kk + 1][0], xr[2 * kk + 1][1]});
   }
-  const uint32_t ba = ssd_tr_base<kSsdPad>(&Bn[8 * grp][0]);
+  const uint32_t ba = ssd_tr_base<kSsdPad>(&Bn[grp][0]);  // row 8 grp
   float *out = a.dS + ((long)e_ * a.H + h) * (kSsdP * kSsdN);
   static_for<kSsdN / 16>([&](auto nb_) {
     constexpr int nb = decltype(nb_)::value;
@@ -275,8 +284,8 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(SsdArgs a) {
     u32x2 br[2 * (kSsdQ / 32)];
     static_for<kSsdQ / 32>([&](auto kk_) {
       constexpr int kk = decltype(kk_)::value;
-      br[2 * kk] = lds_rdtr<2 * (32 * kk * kSsdPad + 16 * nb)>(ba);
-      br[2 * kk + 1] = lds_rdtr<2 * ((32 * kk + 4) * kSsdPad + 16 * nb)>(ba);
+      br[2 * kk] = lds_rdtr<2 * (4 * kk * kSsdBBlk + 16 * nb)>(ba);
+      br[2 * kk + 1] = lds_rdtr<2 * (4 * kk * kSsdBBlk + 4 * kSsdPad + 16 * nb)>(ba);
     });
     lds_wait<0>();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
