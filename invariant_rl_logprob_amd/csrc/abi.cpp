@@ -997,6 +997,13 @@ static ril_status decode_enqueue(const ril_model *m, ril_kv *kv, const ril_decod
                     max_splits, m->cscale, wsf(ws, m->off_po), wsf(ws, m->off_pml), wsb(ws, m->off_attn),
                     m->kv_fp8, m->k_scale, m->v_scale};
   RIL_LAUNCH(RIL_K_ATTN_SPLIT, launch_attn_split(ad, st));
+  if (!d.w_o && !d.d_ff && d.n_q_heads * d.head_dim <= ril::kMergeNormMaxD) {
+    // the attention output goes straight into the final RMSNorm: merge and normalise in
+    // one launch (the same arithmetic as the merge kernel followed by the RMSNorm kernel)
+    RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_attn_merge_norm(ad, (const bf16_t *)d.norm_final, d.rms_eps,
+                                                        wsb(ws, m->off_z), d.d_head, st));
+    return run_lm_head(m, R, wsb(ws, m->off_z), d.d_head, b->target_ids, logprob_out, ws, st);
+  }
   RIL_LAUNCH(RIL_K_ATTN_MERGE, launch_attn_merge(ad, st));
   return run_head(m, R, b->target_ids, logprob_out, ws, st);
 }

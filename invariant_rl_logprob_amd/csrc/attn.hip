@@ -31,6 +31,7 @@
 
 #include "attn_common.h"
 #include "kernels.h"
+#include "norm.h"
 
 namespace ril {
 
@@ -264,6 +265,76 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// S9 + S3 for decode rows whose attention output goes straight into the final RMSNorm
+// (no output projection, no MLP block): grid (rows), 16 waves.  The half-waves merge the
+// row's heads in turn (the merge kernel's arithmetic) into LDS and the attention output;
+// then wave 0 normalises the row (rmsnorm_row, the RMSNorm kernel's arithmetic on the
+// same bf16 values).  One launch instead of two.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(1024) void attn_merge_norm_kernel(
+    const int32_t *__restrict__ ctx_len, int ctx_bound, int split_tokens, int Hq, int max_splits,
+    const float *__restrict__ part_o, const float *__restrict__ part_ml, bf16_t *__restrict__ out,
+    const bf16_t *__restrict__ gain, float eps, bf16_t *__restrict__ z, int ldz) {
+  // each half-wave merges one head, a lane PER consecutive dims (the loads of CH splits
+  // issued together, folded split 0 first, then left to right: merge_partials' order and
+  // merge_state's arithmetic per element)
+  constexpr int PER = D / 32, CH = 8;
+  __shared__ __attribute__((aligned(16))) bf16_t xr[kMergeNormMaxD];
+  const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int hl = lane & 31, hw = lane >> 5;
+  const int d = Hq * D;
+  const int ctx = ctx_len[row];
+  const bool ok = ctx >= 1 && ctx <= ctx_bound;
+  const int ns = ok ? (ctx + split_tokens - 1) / split_tokens : 0;
+  for (int h0 = 2 * wave; h0 < Hq; h0 += 2 * nw) {
+    const int h = h0 + hw;
+    if (h >= Hq) continue;
+    bf16_t *xh = xr + h * D + hl * PER;
+    if (!ok) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) xh[j] = (bf16_t)0x7fc0u;
+      continue;
+    }
+    const long base = ((long)row * Hq + h) * max_splits;
+    float M = 0.f, L = 0.f, O[PER];
+    for (int s0 = 0; s0 < ns; s0 += CH) {
+      float ms[CH], ls[CH], os[CH][PER];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const long sidx = base + min(s0 + c, ns - 1);  // past the last split: a repeat, not folded
+        ms[c] = part_ml[sidx * 2];
+        ls[c] = part_ml[sidx * 2 + 1];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) os[c][j] = part_o[sidx * D + hl * PER + j];
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (s0 + c >= ns) break;
+        if (s0 + c == 0) {
+          M = ms[0];
+          L = ls[0];
+#pragma unroll
+          for (int j = 0; j < PER; ++j) O[j] = os[0][j];
+        } else {
+          merge_state<PER>(M, L, O, ms[c], ls[c], os[c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) xh[j] = f2bf(__fdiv_rn(O[j], L));
+  }
+  __syncthreads();
+  bf16_t *orow = out + (long)row * d;
+  for (int e = threadIdx.x; e < d / 8; e += blockDim.x) st16(orow + e * 8, *reinterpret_cast<const u32x4 *>(xr + e * 8));
+  if (wave == 0) {
+    bf16_t *zr = z + (long)row * ldz;
+    rmsnorm_row([&](int e) { return *reinterpret_cast<const u32x4 *>(xr + e * 8); },
+                [&](int e, u32x4 o, u32x4) { st16(zr + e * 8, o); }, d, gain, eps, false);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 
@@ -314,6 +385,19 @@ hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st) {
   else
     hipLaunchKernelGGL(attn_decode_merge_kernel<64>, grid, dim3(64), 0, st, a.ctx_len, a.ctx_bound,
                        a.split_tokens, a.Hkv * a.G, a.max_splits, a.part_o, a.part_ml, a.out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge_norm(const AttnDecodeArgs &a, const bf16_t *gain, float eps, bf16_t *z, int ldz,
+                                  hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  if (a.Hkv * a.G * a.D > kMergeNormMaxD) return hipErrorInvalidValue;
+  if (a.D == 128)
+    hipLaunchKernelGGL(attn_merge_norm_kernel<128>, dim3(a.n_rows), dim3(1024), 0, st, a.ctx_len, a.ctx_bound,
+                       a.split_tokens, a.Hkv * a.G, a.max_splits, a.part_o, a.part_ml, a.out, gain, eps, z, ldz);
+  else
+    hipLaunchKernelGGL(attn_merge_norm_kernel<64>, dim3(a.n_rows), dim3(1024), 0, st, a.ctx_len, a.ctx_bound,
+                       a.split_tokens, a.Hkv * a.G, a.max_splits, a.part_o, a.part_ml, a.out, gain, eps, z, ldz);
   return hipGetLastError();
 }
 

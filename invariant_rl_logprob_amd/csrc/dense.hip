@@ -11,19 +11,19 @@
 #include "common.h"
 #include "kernels.h"
 #include "lm_head.h"
+#include "norm.h"
 
 namespace ril {
 
 // ---------------------------------------------------------------------------
 // S2 + S3: y = bf16((x * rsqrt(mean(x^2) + eps)) * g), x = E[token] or a dense row.
-// One wave per row.  Lane l owns 8-element chunks l, l+64, ...; the sum of squares is
-// a lane-sequential fma chain followed by a whole-wave xor butterfly.
+// One wave per row, the arithmetic of rmsnorm_row (norm.h).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void rmsnorm_kernel(
     const bf16_t *__restrict__ x, int ldx, const int32_t *__restrict__ tok,
     const bf16_t *__restrict__ embed, int vocab, int d, const bf16_t *__restrict__ gain, float eps,
     bf16_t *__restrict__ y, int ldy, bf16_t *__restrict__ x_copy, int ldc) {
-  const int row = blockIdx.x, lane = threadIdx.x;
+  const int row = blockIdx.x;
   const bf16_t *src;
   bool poison = false;
   if (tok) {
@@ -36,35 +36,14 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(
   } else {
     src = x + (long)row * ldx;
   }
-  const int n8 = d / 8;
-  float acc = 0.f;
-  for (int e = lane; e < n8; e += 64) {
-    const u32x4 v = ld16(src + e * 8);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = bf2f((bf16_t)(v[w] & 0xffffu)), b = bf2f((bf16_t)(v[w] >> 16));
-      acc = __builtin_fmaf(a, a, acc);
-      acc = __builtin_fmaf(b, b, acc);
-    }
-  }
-  acc = sum64(acc);
-  const float mean = __fdiv_rn(acc, (float)d);
-  float r = __fdiv_rn(1.0f, __fsqrt_rn(mean + eps));
-  if (poison) r = __builtin_nanf("");
-  for (int e = lane; e < n8; e += 64) {
-    const u32x4 v = ld16(src + e * 8);
-    u32x4 g = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
-    if (gain) g = ld16(gain + e * 8);
-    u32x4 out;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = bf2f((bf16_t)(v[w] & 0xffffu)), b = bf2f((bf16_t)(v[w] >> 16));
-      const float ga = bf2f((bf16_t)(g[w] & 0xffffu)), gb = bf2f((bf16_t)(g[w] >> 16));
-      out[w] = pack2((a * r) * ga, (b * r) * gb);
-    }
-    st16(y + (long)row * ldy + e * 8, out);
-    if (x_copy) st16(x_copy + (long)row * ldc + e * 8, v);
-  }
+  bf16_t *yr = y + (long)row * ldy;
+  bf16_t *xc = x_copy ? x_copy + (long)row * ldc : nullptr;
+  rmsnorm_row([&](int e) { return ld16(src + e * 8); },
+              [&](int e, u32x4 out, u32x4 v) {
+                st16(yr + e * 8, out);
+                if (xc) st16(xc + e * 8, v);
+              },
+              d, gain, eps, poison);
 }
 
 // ---------------------------------------------------------------------------

@@ -217,6 +217,11 @@ hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st);
 hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t st);
 hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t st);
+// Decode merge + final RMSNorm in one launch (rows with no output projection or MLP block);
+// the row (Hq * D values) is staged in LDS.
+constexpr int kMergeNormMaxD = 16384;
+hipError_t launch_attn_merge_norm(const AttnDecodeArgs &a, const bf16_t *gain, float eps, bf16_t *z, int ldz,
+                                  hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 int gemm_tiles(int M, int N);
 hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);
