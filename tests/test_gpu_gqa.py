@@ -188,3 +188,30 @@ def test_split_multiple_contexts_decode_equals_prefill_and_oracle():
             if ctx % 512 == 0 or back == 1:
                 lp_o, _ = c.oracle_row(r, back)
                 assert abs(dn[i, n - back] - lp_o) <= TOL, (r, ctx, dn[i, n - back], lp_o)
+
+
+@pytest.mark.parametrize("kv_dtype", [0, 1])
+def test_rejected_rows_give_nan_and_leave_batch_mates_unchanged(kv_dtype):
+    """Rows the device-side checks reject come back NaN (ril.h: a context below 1 or past the
+    batch's bound, a page id outside the pool, a target outside [0, V)); the other rows of
+    the same batch keep their bits (batch invariance holds for broken batch-mates too)."""
+    c = _case(kv_dtype=kv_dtype)
+    rows = list(range(6))
+    seqs = [("d", r) for r in rows]
+    c.write_history("d", rows, 1)
+    q, k, v, t, ctx = c.step_inputs(rows, 1)
+    ref = _bits(c.sess.decode(seqs, ctx, targets=t, q=q, k=k, v=v))
+    launch, out = c.sess.prepare_decode(seqs, ctx, targets=t, q=q, k=k, v=v)
+    keep = launch.keep
+    bound = max(ctx)
+    stride = keep["pt"].shape[1]
+    assert stride == math.ceil(bound / 16)
+    keep["ctx"][1] = 0                      # no position
+    keep["ctx"][2] = 16 * stride + 1        # past the bound; its new token's page is past the table
+    keep["pt"][3, 1] = c.sess.pool.numel() // c.sess.page_bytes + 5  # outside the pool, inside row 3's context
+    keep["tgt"][4] = SMALL.vocab            # a target outside the vocabulary
+    launch()
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert bool(torch.isnan(got[1:5]).all()), got
+    assert np.array_equal(_bits(out)[[0, 5]], ref[[0, 5]])
