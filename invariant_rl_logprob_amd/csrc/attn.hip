@@ -112,10 +112,11 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 // wave computes a split never changes its arithmetic.  K/V loads run up to two tiles
 // ahead of the tile being computed, with the nontemporal (streaming) cache policy: each
 // byte of the cache is read exactly once per step, and letting it displace other lines
-// from the L2 and the memory-side cache cost 8% of the kernel's time.
+// from the L2 and the memory-side cache cost 8% of the kernel's time.  The bf16 and FP8
+// entry points below share this body; the FP8 one runs two waves per SIMD.
 // ---------------------------------------------------------------------------
 template <int D, bool FP8>
-__global__ __launch_bounds__(64) void attn_decode_split_kernel(
+__device__ __forceinline__ void attn_decode_split(
     const bf16_t *__restrict__ q, int q_row_stride, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool,
     int n_pages, int Hkv, int G, int split_tokens, int ctx_bound, int n_rows, int n_sg, float cscale,
@@ -155,14 +156,15 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   const bool bad_lane = in_ctx && (unsigned)p_raw >= (unsigned)n_pages;
   const int pid = (in_ctx && !bad_lane) ? p_raw : 0;
   const bool bad = __any(bad_lane);
-  // Ring of NR = 2*LA + 1 half-tile slots, LA = 2 tiles ahead: while the scores of tile t
-  // run, the V half of t, both halves of t+1 and the K half of t+2 are in flight (64 KB per
-  // wave for D = 128 in bf16, 32 KB in FP8).  FP8 slots hold the codes, each operand
-  // dequantized just before its MFMA (no dequantized tile held in registers).  Measured
-  // and not kept for FP8: rings 3 and 4 tiles deep, and two or three waves per SIMD (the
-  // register cap then spills): 139-286 us against 139 us.  Half-tile h (K of tile h/2 if
-  // h is even, else its V) lives in slot h % NR.
-  constexpr int LA = 2, NR = 2 * LA + 1;
+  // Ring of NR = 2*LA + 1 half-tile slots.  bf16: LA = 2 tiles ahead, one wave per SIMD:
+  // while the scores of tile t run, the V half of t, both halves of t+1 and the K half of
+  // t+2 are in flight (64 KB per wave for D = 128).  FP8: slots hold the codes, each
+  // operand dequantized just before its MFMA (no dequantized tile held in registers), and
+  // the ring is one tile ahead (3 slots, 16 KB in flight per wave) so that two waves fit
+  // each SIMD without spilling: 131 -> 118 us for the 64-row step, where two waves with
+  // the 5-slot ring spilled (148 us) and deeper rings at one wave were slower.  Half-tile
+  // h (K of tile h/2 if h is even, else its V) lives in slot h % NR.
+  constexpr int LA = FP8 ? 1 : 2, NR = 2 * LA + 1;
   using Slot = std::conditional_t<FP8, Half8<D>, Half<D>>;
   Slot ring[NR];
   const bf16_t *pg[4];
@@ -243,6 +245,26 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     part_ml[base * 2 + 1] = l;
   }
 }
+
+#define RIL_SPLIT_PARAMS                                                                                      \
+  const bf16_t *__restrict__ q, int q_row_stride, const int32_t *__restrict__ ctx_len,                         \
+      const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool, int n_pages,     \
+      int Hkv, int G, int split_tokens, int ctx_bound, int n_rows, int n_sg, float cscale,                      \
+      float *__restrict__ part_o, float *__restrict__ part_ml, int max_splits, float k_scale, float v_scale
+#define RIL_SPLIT_ARGS                                                                                         \
+  q, q_row_stride, ctx_len, page_table, page_stride, pool, n_pages, Hkv, G, split_tokens, ctx_bound, n_rows, n_sg, \
+      cscale, part_o, part_ml, max_splits, k_scale, v_scale
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_split_kernel(RIL_SPLIT_PARAMS) {
+  attn_decode_split<D, false>(RIL_SPLIT_ARGS);
+}
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_decode_split_fp8_kernel(
+    RIL_SPLIT_PARAMS) {
+  attn_decode_split<D, true>(RIL_SPLIT_ARGS);
+}
+#undef RIL_SPLIT_PARAMS
+#undef RIL_SPLIT_ARGS
 
 // ---------------------------------------------------------------------------
 // S9: decode merge kernel.  grid (Hq, rows), one wave; lane owns D/64 dims.
@@ -363,15 +385,15 @@ hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st) {
   const long slots = (long)(n_sg + a.split_tokens / kTile) * a.Hkv * a.n_rows;
   if (slots > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)slots);
-#define RIL_SPLIT(D_, F_)                                                                                      \
-  hipLaunchKernelGGL((attn_decode_split_kernel<D_, F_>), grid, dim3(64), 0, st, a.q, a.q_row_stride, a.ctx_len, \
-                     a.page_table, a.page_stride, a.pool, a.n_pages, a.Hkv, a.G, a.split_tokens, a.ctx_bound,    \
-                     a.n_rows, n_sg, a.kv_fp8 ? a.cscale * a.k_scale : a.cscale, a.part_o, a.part_ml, a.max_splits, \
-                     a.k_scale, a.v_scale)
+#define RIL_SPLIT(K_)                                                                                          \
+  hipLaunchKernelGGL(K_, grid, dim3(64), 0, st, a.q, a.q_row_stride, a.ctx_len, a.page_table, a.page_stride, a.pool, \
+                     a.n_pages, a.Hkv, a.G, a.split_tokens, a.ctx_bound, a.n_rows, n_sg,                          \
+                     a.kv_fp8 ? a.cscale * a.k_scale : a.cscale, a.part_o, a.part_ml, a.max_splits, a.k_scale,   \
+                     a.v_scale)
   if (a.D == 128) {
-    if (a.kv_fp8) RIL_SPLIT(128, true); else RIL_SPLIT(128, false);
+    if (a.kv_fp8) RIL_SPLIT(attn_decode_split_fp8_kernel<128>); else RIL_SPLIT(attn_decode_split_kernel<128>);
   } else {
-    if (a.kv_fp8) RIL_SPLIT(64, true); else RIL_SPLIT(64, false);
+    if (a.kv_fp8) RIL_SPLIT(attn_decode_split_fp8_kernel<64>); else RIL_SPLIT(attn_decode_split_kernel<64>);
   }
 #undef RIL_SPLIT
   return hipGetLastError();
