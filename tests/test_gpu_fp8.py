@@ -154,3 +154,36 @@ def test_fp8_split_multiple_contexts_decode_equals_prefill_and_oracle():
             if (c.ctx(r) - back + 1) % 512 == 0 or back == 1:
                 lp_o, _ = c.oracle_row(r, back)
                 assert abs(dn[i, n - back] - lp_o) <= TOL, (r, back)
+
+
+@pytest.mark.parametrize("v_exp", [0, -4])
+def test_fp8_read_path_returns_every_code_exactly(v_exp):
+    """Every E4M3 code read back through the attention, decode and prefill: with one
+    position of context and q = 0, each output element is that position's V value
+    exactly (softmax weight 1, the other MFMA entries zeroed), so the attention output
+    must equal the oracle's decode of the stored codes exactly -- subnormal codes, the
+    largest magnitudes -- and be NaN for both NaN codes.  (Zero compares by value: the
+    MFMA adds the other, zeroed entries, and -0 + 0 is +0.)"""
+    from invariant_rl_logprob_amd.session import Session
+    D, Hkv = 128, 8
+    codes = (np.arange(Hkv * D) % 256).astype(np.uint8)    # every code four times
+    vals = oracle.fp8.kv_fp8_load(codes, v_exp)             # exact in bf16; NaN for S.1111.111
+    nan = np.isnan(vals)
+    want = torch.from_numpy(vals).to(torch.bfloat16)
+    v = want.view(1, Hkv * D).cuda()
+    zeros = torch.zeros(1, Hkv * D, dtype=torch.bfloat16, device="cuda")
+    w_lm = torch.zeros(64, Hkv * D, dtype=torch.bfloat16, device="cuda")
+    s = Session(n_q_heads=Hkv, n_kv_heads=Hkv, head_dim=D, vocab=64, d_head=Hkv * D, w_lm=w_lm, max_rows=1,
+                max_tokens=1, max_ctx=16, pool_pages=8, softmax_scale=1.0, shuffle_seed=3, kv_dtype=FP8,
+                v_scale_exp=v_exp)
+    t0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s.decode(["d"], [1], targets=t0, q=zeros, k=zeros, v=v)
+    dec = s.attn_out(1).reshape(-1).cpu()
+    s.prefill(["p"], [0], targets=[t0], qs=[zeros], ks=[zeros], vs=[v])
+    pre = s.attn_out(1).reshape(-1).cpu()
+    torch.cuda.synchronize()
+    keep = ~torch.from_numpy(nan)
+    for got in (dec, pre):
+        assert np.array_equal(torch.isnan(got).numpy(), nan)
+        g, w = got[keep].double().numpy(), want[keep].double().numpy()
+        assert np.array_equal(g, w), (np.flatnonzero(g != w)[:8], codes[keep.numpy()][g != w][:8])
