@@ -215,3 +215,24 @@ def test_rejected_rows_give_nan_and_leave_batch_mates_unchanged(kv_dtype):
     got = out.cpu()
     assert bool(torch.isnan(got[1:5]).all()), got
     assert np.array_equal(_bits(out)[[0, 5]], ref[[0, 5]])
+
+
+def test_wide_rows_take_the_separate_merge_and_norm_and_stay_invariant():
+    """Rows wider than the merge + RMSNorm kernel stages in LDS (256 q heads x 128 =
+    32768 values) take the separate merge and RMSNorm launches: decode still equals the
+    prefill recompute bit for bit and matches the oracle."""
+    from gqa_case import GQACase
+    w = wl.scaled(wl.GQA_DECODE_B64, rows=4, n_q_heads=256, n_kv_heads=16, vocab=512, d_head=256 * 128,
+                  recompute_tokens=16)
+    c = GQACase(w, list(range(4)), ctx=[17, 40, 530, 100])
+    rows = list(range(4))
+    n = 16
+    c.write_history("d", rows, n)
+    dec = torch.stack([c.decode_back("d", rows, back) for back in range(n, 0, -1)], dim=1)
+    c.write_history("p", rows, n)
+    pre = c.prefill_last("p", rows, n)
+    assert np.array_equal(_bits(dec), _bits(pre))
+    dn = dec.cpu().numpy()
+    for i, r in enumerate(rows):
+        lp, _ = c.oracle_row(r, 1)
+        assert abs(dn[i, -1] - lp) <= TOL, (r, dn[i, -1], lp)
