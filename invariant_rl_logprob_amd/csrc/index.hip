@@ -38,19 +38,29 @@ __device__ __forceinline__ void index_row(int mode, int r, int row0, const int32
 }
 
 // ---------------------------------------------------------------------------
-// S6: grid (ceil(ctx_bound / 256), rows), one thread per history position.
+// S6: grid (ceil(ctx_bound / 256), rows), one thread per history position.  The row's q
+// (64 x 128 fp32, 32 KB) is staged in LDS once per workgroup and read back as 16-byte
+// broadcast reads (every lane the same address) that the compiler can issue ahead of the
+// multiplies; read as scalar loads it left every head waiting on a scalar-memory round
+// trip (the scalar registers hold only part of a head).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void indexer_kernel(
     const float *__restrict__ q, int mode, int row0, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
     const int32_t *__restrict__ page_table, int page_stride, const bf16_t *__restrict__ pool, int page_elems,
     int n_pages, int ctx_bound, int key_off, float *__restrict__ scores, int score_stride) {
+  __shared__ __attribute__((aligned(16))) float qs[kIdxHeads * kIdxDim];
   const int r = blockIdx.y;
   int seq, ctx;
   long qrow;
   index_row(mode, r, row0, ctx_len, cu, start_pos, n_seqs, seq, ctx, qrow);
+  if (ctx < 1 || ctx > ctx_bound || blockIdx.x * blockDim.x >= ctx) return;  // the same for the whole workgroup
+  const float *qr = q + qrow * (kIdxHeads * kIdxDim);
+  for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 4; i += blockDim.x)
+    reinterpret_cast<u32x4 *>(qs)[i] = ld16(qr + 4 * i);
+  __syncthreads();
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (ctx < 1 || ctx > ctx_bound || s >= ctx) return;
+  if (s >= ctx) return;
   float *out = scores + (long)r * score_stride + s;
   const int pid = page_table[(long)seq * page_stride + s / kPage];
   if ((unsigned)pid >= (unsigned)n_pages) {
@@ -65,12 +75,16 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) k[4 * i + j] = __uint_as_float(v[j]);
   }
-  const float *qr = q + qrow * (kIdxHeads * kIdxDim);  // the same for the whole workgroup
   float total = 0.f;
   for (int h = 0; h < kIdxHeads; ++h) {
+    const u32x4 *qh = reinterpret_cast<const u32x4 *>(qs + h * kIdxDim);
     float acc = 0.f;
 #pragma unroll
-    for (int d = 0; d < kIdxDim; ++d) acc = __fadd_rn(acc, __fmul_rn(qr[h * kIdxDim + d], k[d]));
+    for (int d4 = 0; d4 < kIdxDim / 4; ++d4) {
+      const u32x4 qv = qh[d4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = __fadd_rn(acc, __fmul_rn(__uint_as_float(qv[j]), k[4 * d4 + j]));
+    }
     total = __fadd_rn(total, acc > 0.f ? acc : 0.f);
   }
   *out = total;
