@@ -267,6 +267,7 @@ def test_calls_fail_validation_without_enqueueing():
         dict(ok, page_table=torch.zeros(2, 15, dtype=torch.int32)),  # stride too small
         dict(ok, ctx_len=i32(*range(5))),                 # 5 rows > max_rows
         dict(ok, q=None),
+        dict(ok, ctx_len=i32(), page_table=pt[:0], target_ids=i32()),  # an empty batch: rejected
     ]
     for c in cases:
         b = ril.make_decode_batch(**c)
@@ -280,6 +281,11 @@ def test_calls_fail_validation_without_enqueueing():
                                 target_ids=i32(1, 2, 3), q=q, k=q, v=q, total_tokens=33)
     with pytest.raises(ril.RilError):
         ril.ril_prefill_logprobs(m, kv, pb, out, ws, stream=0)
+    # an empty prefill (no sequence, no token) is rejected too, before anything is enqueued
+    pe = ril.make_prefill_batch(cu_tokens=i32(0), start_pos=i32(), page_table=pt[:0], max_ctx_bound=3,
+                                target_ids=i32(), q=q, k=q, v=q, total_tokens=0)
+    with pytest.raises(ril.RilError):
+        ril.ril_prefill_logprobs(m, kv, pe, out, ws, stream=0)
     ril.ril_kv_free(kv)
     ril.ril_model_destroy(m)
 
