@@ -267,23 +267,64 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #undef RIL_SPLIT_ARGS
 
 // ---------------------------------------------------------------------------
-// S9: decode merge kernel.  grid (Hq, rows), one wave; lane owns D/64 dims.
+// One head's split merge by a half-wave (lane hl of 32 owns dims hl*D/32 ..): the loads of
+// CH splits issued together, folded split 0 first, then left to right -- merge_partials'
+// order and merge_state's arithmetic per element; writes bf16(O / L) to dst (the lane's
+// first dim).  A whole wave thus merges two heads, each lane with 16-byte loads.
+// ---------------------------------------------------------------------------
+template <int D, int CH>
+__device__ __forceinline__ void merge_head_halfwave(const float *__restrict__ part_o,
+                                                    const float *__restrict__ part_ml, long base, int ns,
+                                                    bf16_t *dst, int hl) {
+  constexpr int PER = D / 32;
+  float M = 0.f, L = 0.f, O[PER];
+  for (int s0 = 0; s0 < ns; s0 += CH) {
+    float ms[CH], ls[CH], os[CH][PER];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const long sidx = base + min(s0 + c, ns - 1);  // past the last split: a repeat, not folded
+      ms[c] = part_ml[sidx * 2];
+      ls[c] = part_ml[sidx * 2 + 1];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) os[c][j] = part_o[sidx * D + hl * PER + j];
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (s0 + c >= ns) break;
+      if (s0 + c == 0) {
+        M = ms[0];
+        L = ls[0];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) O[j] = os[0][j];
+      } else {
+        merge_state<PER>(M, L, O, ms[c], ls[c], os[c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) dst[j] = f2bf(__fdiv_rn(O[j], L));
+}
+
+// ---------------------------------------------------------------------------
+// S9: decode merge kernel.  grid (ceil(Hq / 2), rows), one wave: its half-waves merge
+// heads 2x and 2x + 1.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
     const int32_t *__restrict__ ctx_len, int ctx_bound, int split_tokens, int Hq, int max_splits,
     const float *__restrict__ part_o, const float *__restrict__ part_ml, bf16_t *__restrict__ out) {
-  constexpr int PER = D / 64;
-  const int h = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
+  constexpr int PER = D / 32;
+  const int lane = threadIdx.x, hl = lane & 31, h = 2 * blockIdx.x + (lane >> 5), row = blockIdx.y;
+  if (h >= Hq) return;
   const int ctx = ctx_len[row];
-  bf16_t *op = out + ((long)row * Hq + h) * D + lane * PER;
+  bf16_t *op = out + ((long)row * Hq + h) * D + hl * PER;
   if (ctx < 1 || ctx > ctx_bound) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) op[j] = (bf16_t)0x7fc0u;
     return;
   }
   const int ns = (ctx + split_tokens - 1) / split_tokens;
-  merge_partials<D>(part_o, part_ml, ((long)row * Hq + h) * max_splits, ns, op - lane * PER);
+  merge_head_halfwave<D, 16>(part_o, part_ml, ((long)row * Hq + h) * max_splits, ns, op, hl);
 }
 
 // ---------------------------------------------------------------------------
@@ -298,10 +339,7 @@ __global__ __launch_bounds__(1024) void attn_merge_norm_kernel(
     const int32_t *__restrict__ ctx_len, int ctx_bound, int split_tokens, int Hq, int max_splits,
     const float *__restrict__ part_o, const float *__restrict__ part_ml, bf16_t *__restrict__ out,
     const bf16_t *__restrict__ gain, float eps, bf16_t *__restrict__ z, int ldz) {
-  // each half-wave merges one head, a lane PER consecutive dims (the loads of CH splits
-  // issued together, folded split 0 first, then left to right: merge_partials' order and
-  // merge_state's arithmetic per element)
-  constexpr int PER = D / 32, CH = 8;
+  constexpr int PER = D / 32;
   __shared__ __attribute__((aligned(16))) bf16_t xr[kMergeNormMaxD];
   const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int hl = lane & 31, hw = lane >> 5;
@@ -318,33 +356,7 @@ __global__ __launch_bounds__(1024) void attn_merge_norm_kernel(
       for (int j = 0; j < PER; ++j) xh[j] = (bf16_t)0x7fc0u;
       continue;
     }
-    const long base = ((long)row * Hq + h) * max_splits;
-    float M = 0.f, L = 0.f, O[PER];
-    for (int s0 = 0; s0 < ns; s0 += CH) {
-      float ms[CH], ls[CH], os[CH][PER];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const long sidx = base + min(s0 + c, ns - 1);  // past the last split: a repeat, not folded
-        ms[c] = part_ml[sidx * 2];
-        ls[c] = part_ml[sidx * 2 + 1];
-#pragma unroll
-        for (int j = 0; j < PER; ++j) os[c][j] = part_o[sidx * D + hl * PER + j];
-      }
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        if (s0 + c >= ns) break;
-        if (s0 + c == 0) {
-          M = ms[0];
-          L = ls[0];
-#pragma unroll
-          for (int j = 0; j < PER; ++j) O[j] = os[0][j];
-        } else {
-          merge_state<PER>(M, L, O, ms[c], ls[c], os[c]);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) xh[j] = f2bf(__fdiv_rn(O[j], L));
+    merge_head_halfwave<D, 8>(part_o, part_ml, ((long)row * Hq + h) * max_splits, ns, xh, hl);
   }
   __syncthreads();
   bf16_t *orow = out + (long)row * d;
@@ -400,7 +412,7 @@ hipError_t launch_attn_split(const AttnDecodeArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_attn_merge(const AttnDecodeArgs &a, hipStream_t st) {
-  dim3 grid(a.Hkv * a.G, a.n_rows);
+  dim3 grid((a.Hkv * a.G + 1) / 2, a.n_rows);
   if (a.D == 128)
     hipLaunchKernelGGL(attn_decode_merge_kernel<128>, grid, dim3(64), 0, st, a.ctx_len, a.ctx_bound,
                        a.split_tokens, a.Hkv * a.G, a.max_splits, a.part_o, a.part_ml, a.out);
