@@ -3,10 +3,13 @@
 // The indexer scores every history position of a query (Bitwise-consistent RL post,
 // sections 3 and 4.3).  Its formula is a reading (the pages give none):
 //   I[s] = sum_h relu(q_h . k_s),  64 heads x 128 dims, unit head weights,
-// computed in fp32 with one rounding per multiply and per add, in the fixed order
-// d = 0..127 inside a head and h = 0..63 across heads.  The selection is an integer
-// decided by these floats, so the arithmetic is kept reproducible exactly: the same
-// bits on every path, and in a float32 reference outside this library.
+// computed in fp32: each head's dot product a chain of fused multiply-adds (the exact
+// q k + acc rounded once, v_fma_f32) over d = 0..127 from +0, the heads summed with one
+// rounding per add over h = 0..63.  The selection is an integer decided by these floats,
+// so the arithmetic is kept reproducible exactly: the same bits on every path, and in a
+// float32 reference outside this library (C99 fmaf is the same operation).  One fused
+// operation per term is half the instructions of a multiply and an add (the kernel is
+// bound by them).
 //
 // The selection ranks positions by the unique key (score, position): higher score
 // first, equal scores broken toward the lower position (post section 4.3 breaks ties
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     for (int d4 = 0; d4 < kIdxDim / 4; ++d4) {
       const u32x4 qv = qh[d4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = __fadd_rn(acc, __fmul_rn(__uint_as_float(qv[j]), k[4 * d4 + j]));
+      for (int j = 0; j < 4; ++j) acc = __fmaf_rn(__uint_as_float(qv[j]), k[4 * d4 + j], acc);
     }
     total = __fadd_rn(total, acc > 0.f ? acc : 0.f);
   }

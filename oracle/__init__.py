@@ -9,7 +9,10 @@ code, constants or helpers with the HIP library and imports nothing from it.
 What it computes is the plain definition, per sequence *alone* (which is
 itself the batch-invariance reference): plain NumPy in float64; bf16 rounding
 (round-to-nearest-even, straight from float64) only where the numerical
-contract stores a bf16 value; everything else float64.
+contract stores a bf16 value; everything else float64.  The one exception is
+the indexer's float32 scores, which decide an integer selection and so take the
+kernel's float32 roundings: plain C loops over C99 ``fmaf`` (``indexer.c``,
+built and loaded by ``cbuild.py`` with the host compiler).
 
 Sources (cited by page title and section):
   * "vLLM Achieves Bitwise-Consistent RL Training: Eliminating Numerical Drift

@@ -10,6 +10,7 @@ pages leave open are stated where they are used.
 
 from __future__ import annotations
 
+import ctypes
 import math
 
 import numpy as np
@@ -233,27 +234,33 @@ def indexer_scores(q_idx, K_idx) -> np.ndarray:
 
 
 def indexer_scores_fp32(q_idx, K_idx) -> np.ndarray:
-    """The indexer in the precision the selection is decided in: float32, one rounding
-    per multiply and per add, accumulated in a fixed order.
+    """The indexer in the precision the selection is decided in: float32, one fused
+    multiply-add per term, accumulated in a fixed order.
 
     A top-k selection is an integer decided by floating point, so both sides must
     decide it in the same arithmetic (a one-ulp difference can swap a selected
     position, Bitwise-consistent RL post section 4.3).  The order: for head h = 0..63,
-    acc_h = (((0 + q_h0 k_0) + q_h1 k_1) + ...) over d = 0..D-1; then
-    I = (((0 + relu(acc_0)) + relu(acc_1)) + ...) over h.  relu(x) = x if x > 0 else +0.
-    q [Hi, D], K [n, D] (float32 values) -> float32 [n].  Pinned by: a pure-Python
-    float32 loop on tiny inputs; agreement with indexer_scores within the fp32 bound.
+    acc_h = fma(q_h,D-1, k_D-1, ... fma(q_h1, k_1, fma(q_h0, k_0, +0))) over d = 0..D-1,
+    each step the exact q k + acc rounded once to float32; then
+    I = (((0 + relu(acc_0)) + relu(acc_1)) + ...) over h, one rounding per add.
+    relu(x) = x if x > 0 else +0.  The loops run in C (oracle/indexer.c, C99 fmaf).
+    q [Hi, D], K [n, D] (float32 values) -> float32 [n].  Pinned by: an exact-rational
+    loop with round-to-nearest-even to float32 written from the definition, on random
+    inputs and on inputs where a fused and an unfused step differ; agreement with
+    indexer_scores within the fp32 bound.
     """
-    q = np.asarray(widen(q_idx), dtype=np.float32)
-    K = np.asarray(widen(K_idx), dtype=np.float32)
-    n = K.shape[0]
-    total = np.zeros(n, dtype=np.float32)
-    for h in range(q.shape[0]):
-        acc = np.zeros(n, dtype=np.float32)
-        for d in range(q.shape[1]):
-            acc = acc + q[h, d] * K[:, d]
-        total = total + np.where(acc > 0, acc, np.float32(0))
-    return total
+    from . import cbuild
+    q = np.ascontiguousarray(np.asarray(widen(q_idx), dtype=np.float32))
+    kt = np.ascontiguousarray(np.asarray(widen(K_idx), dtype=np.float32).T)
+    heads, dim = q.shape
+    n = kt.shape[1]
+    assert kt.shape[0] == dim
+    out = np.empty(n, dtype=np.float32)
+    acc = np.empty(n, dtype=np.float32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    cbuild.lib().oracle_indexer_fma(q.ctypes.data_as(fp), heads, dim, kt.ctypes.data_as(fp), n,
+                                    out.ctypes.data_as(fp), acc.ctypes.data_as(fp))
+    return out
 
 
 def sparse_mla_row_attention(q, C, selected, scale: float, dv: int) -> np.ndarray:

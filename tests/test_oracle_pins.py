@@ -11,6 +11,7 @@ function and assert that the matching pin rejects it.
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -320,21 +321,85 @@ def test_indexer_brute_force():
     assert np.allclose(oracle.indexer_scores(q, K), want, rtol=1e-14, atol=1e-14)
 
 
-def test_indexer_fp32_brute_force_float32_loop():
-    # pure-Python loop over numpy float32 scalars: one rounding per multiply and add
-    q = RNG.standard_normal((3, 5)).astype(np.float32)
-    K = RNG.standard_normal((7, 5)).astype(np.float32)
-    want = []
-    for s in range(7):
-        tot = np.float32(0)
-        for h in range(3):
-            acc = np.float32(0)
-            for d in range(5):
-                acc = np.float32(acc + np.float32(q[h, d] * K[s, d]))
-            tot = np.float32(tot + (acc if acc > 0 else np.float32(0)))
-        want.append(tot)
+def _round_f32(x: Fraction) -> float:
+    """x rounded to the nearest binary32 value, ties to the even significand, written from
+    the format's definition (24-bit significands, exponents down to -126, subnormals on a
+    2^-149 grid); the inputs here stay far from overflow."""
+    if x == 0:
+        return 0.0
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1  # now 2^e <= a < 2^(e+1)
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    m = a / quantum
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = float(fl * quantum)
+    return v if x > 0 else -v
+
+
+def _indexer_exact_rational(q, K):
+    """The indexer's float32 chain with every step's exact value taken as a rational:
+    acc <- round(q k + acc) per term, total <- round(total + relu(acc)) per head."""
+    out = []
+    for s in range(K.shape[0]):
+        tot = 0.0
+        for h in range(q.shape[0]):
+            acc = 0.0
+            for d in range(q.shape[1]):
+                acc = _round_f32(Fraction(float(q[h, d])) * Fraction(float(K[s, d])) + Fraction(acc))
+            tot = _round_f32(Fraction(tot) + Fraction(acc if acc > 0 else 0.0))
+        out.append(tot)
+    return np.array(out, dtype=np.float32)
+
+
+def test_round_f32_agrees_with_numpy_conversion():
+    # the rounding helper itself: on doubles, numpy's float64 -> float32 conversion is RNE
+    x = np.concatenate([RNG.standard_normal(2000), RNG.standard_normal(200) * 1e-40,
+                        np.array([1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, -(1 + 2.0 ** -24), 2.0 ** -150, 3 * 2.0 ** -150])])
+    want = x.astype(np.float32)
+    got = np.array([_round_f32(Fraction(float(v))) for v in x], dtype=np.float32)
+    assert np.array_equal(got, want)
+
+
+def test_indexer_fp32_brute_force_exact_rational():
+    q = RNG.standard_normal((3, 9)).astype(np.float32)
+    K = RNG.standard_normal((11, 9)).astype(np.float32)
     got = oracle.indexer_scores_fp32(q, K)
-    assert got.dtype == np.float32 and np.array_equal(got, np.array(want, dtype=np.float32))
+    assert got.dtype == np.float32 and np.array_equal(got, _indexer_exact_rational(q, K))
+
+
+def _fused_differs_case():
+    # d = 0: acc = -1; d = 1: (1 + 2^-12)^2 - 1 = 2^-11 + 2^-24 exactly (representable);
+    # an unfused step first rounds the product 1 + 2^-11 + 2^-24 (a tie) to 1 + 2^-11
+    a = np.float32(1 + 2.0 ** -12)
+    q = np.array([[1.0, a], [0.5, 0.25]], dtype=np.float32)
+    K = np.array([[-1.0, a], [2.0, 4.0]], dtype=np.float32)
+    return q, K
+
+
+def test_indexer_fp32_steps_are_fused():
+    q, K = _fused_differs_case()
+    got = oracle.indexer_scores_fp32(q, K)
+    assert got[0] == np.float32(2.0 ** -11 + 2.0 ** -24)  # head 1 scores -0.25 + 2^-14: relu 0
+    assert np.array_equal(got, _indexer_exact_rational(q, K))
+
+
+def test_planted_indexer_unfused_steps_are_caught():
+    # a plausible slip: multiply, round, then add (two roundings per term)
+    def unfused(q, K):
+        tot = np.zeros(K.shape[0], dtype=np.float32)
+        for h in range(q.shape[0]):
+            acc = np.zeros(K.shape[0], dtype=np.float32)
+            for d in range(q.shape[1]):
+                acc = acc + q[h, d] * K[:, d]
+            tot = tot + np.where(acc > 0, acc, np.float32(0))
+        return tot
+    q, K = _fused_differs_case()
+    assert not np.array_equal(unfused(q, K), _indexer_exact_rational(q, K))
 
 
 def test_indexer_fp32_within_error_bound_of_fp64():
