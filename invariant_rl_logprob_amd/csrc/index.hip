@@ -99,6 +99,62 @@ __device__ __forceinline__ uint32_t ord32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kTopkRow = 257;  // one lane's histogram row, padded against bank aliasing
+
+// A row of at most K positions (or an invalid row: n = 0) selects every position,
+// listed in descending order, -1 after them.
+__device__ __forceinline__ void topk_every_position(int32_t *out, int32_t *cpy, int K, int n) {
+  for (int i = threadIdx.x; i < K; i += kTopkThreads) {
+    const int v = i < n ? n - 1 - i : -1;
+    out[i] = v;
+    if (cpy) cpy[i] = v;
+  }
+}
+
+// One radix pass after the per-lane histogram rows are filled: sum the 64 rows per bin,
+// then wave 0 finds the digit (bits shift .. shift+7) where the count of keys with a
+// larger digit first reaches `need`, and narrows (prefix, need) to that digit; `ties` is
+// the digit's count.  The caller synchronises before reading the results.
+__device__ __forceinline__ void topk_pick_digit(const int *hist, int (&part)[4][256], int shift, uint32_t prefix,
+                                                uint32_t &s_prefix, int &s_need, int &s_ties) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  {
+    const int b = tid & 255, q4 = tid >> 8;  // bin, quarter of the 64 rows
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c += hist[(16 * q4 + i) * kTopkRow + b];
+    part[q4][b] = c;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // lane l holds bins 255 - 4l .. 252 - 4l
+    int cnt[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = 255 - 4 * lane - j;
+      cnt[j] = part[0][b] + part[1][b] + part[2][b] + part[3][b];
+      loc += cnt[j];
+    }
+    int incl = loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    const int need = s_need;
+    int cum = incl - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (cum < need && cum + cnt[j] >= need) {
+        s_prefix = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
+        s_need = need - cum;
+        s_ties = cnt[j];
+      }
+      cum += cnt[j];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // S7: grid (rows), 1024 threads.  Radix select of the k-th largest score over four
 // 8-bit digits (histograms in LDS: their counts do not depend on thread order), then
@@ -116,9 +172,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *__restrict__ scores, int score_stride, int mode, int row0, const int32_t *__restrict__ ctx_len,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs, int ctx_bound, int K,
     int32_t *__restrict__ sel, int32_t *__restrict__ sel_copy) {
-  constexpr int kRow = 257;  // one lane's histogram row, padded against bank aliasing
   constexpr int kUnroll = 8;  // score loads issued together per scan step
-  __shared__ int hist[64 * kRow];
+  __shared__ int hist[64 * kTopkRow];
   __shared__ int part[4][256];
   __shared__ int buf[kTopkMax];
   __shared__ int wave_cnt[kTopkThreads / 64];
@@ -133,12 +188,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   int32_t *cpy = sel_copy ? sel_copy + (row0 + (long)r) * K : nullptr;
   if (ctx < 1 || ctx > ctx_bound || ctx <= K) {
     // every position, descending (an invalid row selects nothing; its attention is NaN)
-    const int n = (ctx < 1 || ctx > ctx_bound) ? 0 : ctx;
-    for (int i = tid; i < K; i += kTopkThreads) {
-      const int v = i < n ? n - 1 - i : -1;
-      out[i] = v;
-      if (cpy) cpy[i] = v;
-    }
+    topk_every_position(out, cpy, K, (ctx < 1 || ctx > ctx_bound) ? 0 : ctx);
     return;
   }
   const int n = ctx;
@@ -149,10 +199,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
   const unsigned long long below_me = (1ull << lane) - 1ull;
   uint32_t mask = 0u;
-  int *my_row = hist + lane * kRow;
+  int *my_row = hist + lane * kTopkRow;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 64 * kRow; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < 64 * kTopkRow; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
     for (int c0 = 0; c0 < n; c0 += kUnroll * kTopkThreads) {
@@ -167,42 +217,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         if (c0 + j * kTopkThreads + tid < n && (u[j] & mask) == prefix) atomicAdd(&my_row[(u[j] >> shift) & 255u], 1);
     }
     __syncthreads();
-    {
-      const int b = tid & 255, q4 = tid >> 8;  // bin, quarter of the 64 rows
-      int c = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) c += hist[(16 * q4 + i) * kRow + b];
-      part[q4][b] = c;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds bins 255 - 4l .. 252 - 4l; the digit is the bin where the count of
-      // larger digits first reaches `need`
-      int cnt[4], loc = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int b = 255 - 4 * lane - j;
-        cnt[j] = part[0][b] + part[1][b] + part[2][b] + part[3][b];
-        loc += cnt[j];
-      }
-      int incl = loc;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-      }
-      const int need = s_need;
-      int cum = incl - loc;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (cum < need && cum + cnt[j] >= need) {
-          s_prefix = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
-          s_need = need - cum;
-          s_ties = cnt[j];
-        }
-        cum += cnt[j];
-      }
-    }
+    topk_pick_digit(hist, part, shift, prefix, s_prefix, s_need, s_ties);
     mask |= 0xFFu << shift;
     __syncthreads();
   }
@@ -283,6 +298,145 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// S7 for rows of at most kTopkThreads * kTopkPer positions: the same selection (the same
+// histograms, threshold digit by digit, and lowest-position ties), with the row's keys
+// read once into registers (thread t holds positions j * 1024 + t, j = 0 .. 63) and the
+// selected positions written straight to their places in descending order, with no sort.
+// Blocks of 64 consecutive positions (block b = 16 j + wave) count their keys above and
+// equal to the threshold; one pass over the 1024 blocks gives each block the ties at
+// lower positions (ascending: the ties taken are the `need` lowest) and the selected
+// positions above it (descending: its first output slot); each lane then adds the
+// selected lanes above it in its block.
+// ---------------------------------------------------------------------------
+constexpr int kTopkPer = 64;
+constexpr int kTopkBlocks = kTopkPer * (kTopkThreads / 64);  // 1024 blocks of 64 positions
+
+__global__ __launch_bounds__(kTopkThreads) void topk_regs_kernel(
+    const float *__restrict__ scores, int score_stride, int mode, int row0, const int32_t *__restrict__ ctx_len,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs, int ctx_bound, int K,
+    int32_t *__restrict__ sel, int32_t *__restrict__ sel_copy) {
+  static_assert(kTopkBlocks == kTopkThreads, "one thread per block of 64 positions in the block pass");
+  __shared__ int hist[64 * kTopkRow];
+  __shared__ int part[4][256];
+  __shared__ int n_gt[kTopkBlocks], n_eq[kTopkBlocks];  // per block: keys above / at the threshold
+  __shared__ int tie0[kTopkBlocks], out0[kTopkBlocks];   // ties below the block; its first output slot
+  __shared__ int wsum[kTopkThreads / 64];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need, s_ties;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int seq, ctx;
+  long qrow;
+  index_row(mode, r, row0, ctx_len, cu, start_pos, n_seqs, seq, ctx, qrow);
+  int32_t *out = sel + (long)r * K;
+  int32_t *cpy = sel_copy ? sel_copy + (row0 + (long)r) * K : nullptr;
+  if (ctx < 1 || ctx > ctx_bound || ctx <= K) {
+    topk_every_position(out, cpy, K, (ctx < 1 || ctx > ctx_bound) ? 0 : ctx);
+    return;
+  }
+  const int n = ctx;  // <= ctx_bound <= kTopkThreads * kTopkPer (the launcher's choice)
+  const float *sc = scores + (long)r * score_stride;
+  // Entries past the row (positions n ..) hold key 0, the smallest key.  A pass counts
+  // them in bin 0 whenever its prefix is 0, and one atomic subtracts them again, so the
+  // bin totals are those of the row's positions alone.  They are never selected: never
+  // above a threshold, and as ties they sit above every position of the row, while the
+  // ties taken are the lowest `need` of the row's own (need <= their count).  So no
+  // later step tests the bound.  Every load is issued at once (past the end a lane
+  // rereads the last position).
+  const int n_past = kTopkThreads * kTopkPer - n;
+  // this thread's entries j < nv are positions of the row (n > K >= 64 > tid - 1024)
+  const int nv = min(kTopkPer, (n - tid + kTopkThreads - 1) / kTopkThreads);
+  uint32_t u[kTopkPer];
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) {
+    const uint32_t v = ord32(sc[min(j * kTopkThreads + tid, n - 1)]);
+    u[j] = v & (uint32_t)((j - nv) >> 31);  // all ones for j < nv, else 0
+  }
+  if (tid == 0) {
+    s_prefix = 0u;
+    s_need = K;
+  }
+  uint32_t mask = 0u;
+  int *my_row = hist + lane * kTopkRow;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 64 * kTopkRow; i += kTopkThreads) hist[i] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+#pragma unroll
+    for (int j = 0; j < kTopkPer; ++j)
+      if ((u[j] & mask) == prefix) atomicAdd(&my_row[(u[j] >> shift) & 255u], 1);
+    if (tid == 0 && prefix == 0u && n_past > 0) atomicSub(&hist[0], n_past);
+    __syncthreads();
+    topk_pick_digit(hist, part, shift, prefix, s_prefix, s_need, s_ties);
+    mask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = s_prefix;
+  const int need = s_need;
+  const unsigned long long below_me = (1ull << lane) - 1ull;
+  const unsigned long long above_me = lane == 63 ? 0ull : ~0ull << (lane + 1);
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) {
+    const unsigned long long bg = __ballot(u[j] > thr), be = __ballot(u[j] == thr);
+    if (lane == 0) {
+      n_gt[j * 16 + wave] = __popcll(bg);
+      n_eq[j * 16 + wave] = __popcll(be);
+    }
+  }
+  __syncthreads();
+  {
+    // thread b = block b (positions 64 b ..): ties at lower positions (exclusive prefix
+    // of n_eq), then the selected count at higher positions (exclusive suffix)
+    const int b = tid, e = n_eq[b];
+    int inc = e;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += t;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int below = inc - e;
+    for (int w = 0; w < wave; ++w) below += wsum[w];
+    tie0[b] = below;
+    const int taken = n_gt[b] + min(max(need - below, 0), e);
+    __syncthreads();  // every wave has read wsum
+    int suf = taken;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += t;
+    }
+    if (lane == 0) wsum[wave] = suf;
+    __syncthreads();
+    int above = suf - taken;
+    for (int w = wave + 1; w < kTopkThreads / 64; ++w) above += wsum[w];
+    out0[b] = above;
+  }
+  __syncthreads();
+  // the threshold read again after the barrier: the compiler then recomputes each
+  // comparison here instead of keeping all 128 masks of the counting loop alive (and
+  // spilling them)
+  const uint32_t thr_w = s_prefix;
+  int tid_w;  // likewise the thread index (else the loads' positions stay alive, in scratch)
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid_w) : "v"(tid));
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) {
+    const int s = j * kTopkThreads + tid_w, b = j * 16 + wave;
+    const bool eq = u[j] == thr_w;
+    const unsigned long long be = __ballot(eq);
+    const bool take = u[j] > thr_w || (eq && tie0[b] + __popcll(be & below_me) < need);
+    const unsigned long long bt = __ballot(take);
+    if (take) {
+      const int i = out0[b] + __popcll(bt & above_me);
+      out[i] = s;
+      if (cpy) cpy[i] = s;
+    }
+  }
+}
+
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   dim3 grid((a.ctx_bound + 255) / 256, a.n_rows);
@@ -294,8 +448,14 @@ hipError_t launch_indexer(const IndexerArgs &a, hipStream_t st) {
 
 hipError_t launch_topk(const IndexerArgs &a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(a.n_rows), dim3(kTopkThreads), 0, st, a.scores, a.score_stride, a.mode,
-                     a.row0, a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.ctx_bound, a.topk, a.sel, a.sel_copy);
+  // rows up to 65536 positions keep their keys in registers; longer bounds stream them
+  if (a.ctx_bound <= kTopkThreads * kTopkPer)
+    hipLaunchKernelGGL(topk_regs_kernel, dim3(a.n_rows), dim3(kTopkThreads), 0, st, a.scores, a.score_stride,
+                       a.mode, a.row0, a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.ctx_bound, a.topk, a.sel,
+                       a.sel_copy);
+  else
+    hipLaunchKernelGGL(topk_kernel, dim3(a.n_rows), dim3(kTopkThreads), 0, st, a.scores, a.score_stride, a.mode,
+                       a.row0, a.ctx_len, a.cu, a.start_pos, a.n_seqs, a.ctx_bound, a.topk, a.sel, a.sel_copy);
   return hipGetLastError();
 }
 

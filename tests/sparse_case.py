@@ -16,7 +16,7 @@ from invariant_rl_logprob_amd.session import Session
 class SparseCase:
     def __init__(self, w: wl.SparseMLADecode, rows: Sequence[int], *, ctx: Sequence[int] = None, device="cuda",
                  shuffle_seed=777, copies=2, split_entries=256, max_rows=None, max_tokens=None, head=None,
-                 kv_dtype=0, scale_exp=0):
+                 kv_dtype=0, scale_exp=0, max_ctx=None):
         self.w = w
         self.rows = list(rows)
         self.data: Dict[int, dict] = {}
@@ -25,7 +25,7 @@ class SparseCase:
         self.head = head if head is not None else wl.mla_head_weights(
             wl.MLADecode(n_heads=w.n_heads, kv_rank=w.kv_rank, vocab=w.vocab, d_head=w.d_head, seed=w.seed),
             device=device)
-        max_ctx = max(d["ctx"] for d in self.data.values())
+        max_ctx = max_ctx or max(d["ctx"] for d in self.data.values())
         pages = sum(math.ceil(d["ctx"] / 16) for d in self.data.values()) * copies + 8
         self.scale = 1.0 / math.sqrt(w.scale_dim)
         self.sess = Session(n_q_heads=w.n_heads, n_kv_heads=1, head_dim=w.kv_rank, rope_dim=w.rope_dim,
@@ -57,7 +57,7 @@ class SparseCase:
         if seqs:
             self.sess.write_kv(seqs, starts, cs, None, k_index=ks)
 
-    def decode_back(self, tag, rows, back: int, selected_out=None) -> torch.Tensor:
+    def decode_back(self, tag, rows, back: int, selected_out=None, ctx_bound=None) -> torch.Tensor:
         q, c, qi, ki, t, ctx = [], [], [], [], [], []
         for r in rows:
             d = self.data[r]
@@ -71,7 +71,7 @@ class SparseCase:
             ctx.append(p + 1)
         st = torch.stack
         return self.sess.decode([(tag, r) for r in rows], ctx, targets=st(t).to(torch.int32), q=st(q), k=st(c),
-                                q_index=st(qi), k_index=st(ki), selected_out=selected_out)
+                                q_index=st(qi), k_index=st(ki), selected_out=selected_out, ctx_bound=ctx_bound)
 
     def prefill_last(self, tag, rows, n: int, selected_out=None) -> torch.Tensor:
         seqs, starts, qs, cs, qis, kis, ts = [], [], [], [], [], [], []

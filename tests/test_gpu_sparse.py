@@ -75,6 +75,31 @@ def test_sparse_forced_ties_follow_lowest_index_rule():
         assert np.array_equal(sel[i], sel_o)
 
 
+@pytest.mark.parametrize("stress", [0, 600])
+def test_topk_register_and_streaming_kernels_agree(stress):
+    """The top-k kernel is chosen by the launch's context bound: up to 65536 positions a
+    row's keys stay in registers and its list is written in place; past that bound they
+    are streamed, collected and sorted.  The same rows under both bounds give the same
+    lists (the oracle's) and the same logprob bits; with forced ties too."""
+    w = wl.scaled(SMALL, tie_stress=stress, seed=31) if stress else SMALL
+    ctx = [900, 3000] if stress else [300, 2100, 5000]
+    rows = list(range(len(ctx)))
+    c = _case(w=w, ctx=ctx, max_ctx=70000)
+    c.write_history("d", rows, 1)
+    out = []
+    for bound in (None, 70000):
+        s = torch.full((len(rows), w.topk), -7, dtype=torch.int32, device="cuda")
+        lp = c.decode_back("d", rows, 1, selected_out=s, ctx_bound=bound)
+        out.append((_bits(lp), s.cpu().numpy()))
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1], out[1][1])
+    for i in rows:
+        _, _, scores, sel_o = c.oracle_row(i, with_logprob=False)
+        if stress:
+            assert int(np.sum(scores == scores.max())) > w.topk
+        assert np.array_equal(out[0][1][i], sel_o), i
+
+
 def test_sparse_batch_invariance():
     c = _case()
     rows = list(range(4))
