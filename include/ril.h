@@ -105,7 +105,9 @@ enum { RIL_ATTN_GQA = 0, RIL_ATTN_MLA = 1, RIL_ATTN_MLA_SPARSE = 2, RIL_ATTN_SSD
  * beyond 448 saturating to 448, NaN kept as NaN with its sign; every attention reads
  * code * 2^scale_exp, a bf16 value exactly, and runs the bf16 arithmetic unchanged.  A
  * page then takes n_kv_heads * 16 * 2 * head_dim bytes (half of BF16's).  The in-page
- * byte layout is documented in csrc/attn_common.h.  MLA (dense and sparse): the latent
+ * byte layout is documented in csrc/attn_common.h (and, for the bf16 MLA latent, in
+ * csrc/mla.hip: the dense kind's pages in the K-operand layout, the sparse kind's
+ * token-major).  MLA (dense and sparse): the latent
  * row (head_dim + rope_dim values) is one tensor with one scale, so k_scale_exp must equal
  * v_scale_exp; a page holds 16 x 576 codes, token-major (code of (t, d) at byte 576 t + d),
  * then, for the sparse kind, the fp32 indexer keys as with BF16 (csrc/mla.hip). */

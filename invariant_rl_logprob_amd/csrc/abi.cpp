@@ -769,7 +769,7 @@ static ril_status run_mla_write(const ril_model *m, ril_kv *kv, const bf16_t *c,
   const ril_model_desc &d = m->d;
   MlaKvWriteArgs a{c, d.head_dim + d.rope_dim, m->sparse ? kidx : nullptr, n_tok, mode, cu, start_pos, n_seqs,
                    ctx_len, page_table, page_stride, (bf16_t *)kv->pool, (int)(m->page_bytes / 2), kv->n_pages,
-                   m->kv_fp8, 1.0f / m->k_scale};
+                   m->kv_fp8, 1.0f / m->k_scale, m->sparse};
   RIL_LAUNCH(RIL_K_KV_WRITE, launch_mla_kv_write(a, st));
   return RIL_OK;
 }

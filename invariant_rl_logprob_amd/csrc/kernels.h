@@ -141,6 +141,7 @@ struct MlaKvWriteArgs {
   int page_elems, n_pages;
   bool fp8;         // the latent is stored as E4M3 codes of c * inv_scale (token-major)
   float inv_scale;  // 2^-scale_exp
+  bool token_major;  // bf16 latent token-major (the sparse kind), else in the K-operand layout
 };
 
 struct MlaAttnArgs {

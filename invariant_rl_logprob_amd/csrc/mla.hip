@@ -19,11 +19,14 @@
 // (positions in descending order, -1 last: the list order is the accumulation order,
 // post section 4.3), in 64-entry tiles gathered from their pages.
 //
-// Latent page (16 tokens) = one 16 x 576 block in the K-operand layout of attn_common.h
-// (k_page_offset); a sparse page also holds the 16 tokens' fp32 indexer keys after it.
+// Latent page (16 tokens), dense kind: one 16 x 576 block in the K-operand layout of
+// attn_common.h (k_page_offset), so a tile's copy moves whole pages in that order.
+// Sparse kind: the 16 rows token-major (element (t, d) at 576 t + d), then the 16 tokens'
+// fp32 indexer keys: a selected token is gathered alone, and its 1152 bytes are then
+// 9 whole cache lines (in the K layout they spread over 72 lines, 16 bytes of each).
 // Per 64-token tile the workgroup copies the tile into LDS (double-buffered: the next
-// tile is copied while the current one is computed) in the same layout up to a swizzle
-// of its 16-byte units: LDS unit u of a page slot holds page unit mla_swz(u).
+// tile is copied while the current one is computed) in the K layout up to a swizzle of
+// its 16-byte units: LDS unit u of a page slot holds K-layout unit mla_swz(u).
 // Score operands are 16-byte LDS reads.  Value operands come from the same tile through
 // gfx950's transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
 // receives element i%4 of the 8-byte chunks addressed by lanes 4e + i/4, e = 0..3, so
@@ -71,15 +74,16 @@ constexpr int kMla8Page = kPage * kMlaDqk;  // 9216 bytes of codes per page
 constexpr int kMla8Tile = kTile * kMlaDqk;  // 36864 bytes: one tile's codes
 
 // ---------------------------------------------------------------------------
-// S5 for MLA: one thread per (token, 16-byte unit) of the page: 72 latent units (bf16,
-// K layout) or 36 (FP8 codes, token-major), then (sparse) 32 units of the fp32 indexer
-// key, token t's at byte latent_bytes + 512 t of the page.
+// S5 for MLA: one thread per (token, 16-byte unit) of the page: 72 latent units (bf16:
+// K layout for the dense kind, token-major for the sparse kind) or 36 (FP8 codes,
+// token-major), then (sparse) 32 units of the fp32 indexer key, token t's at byte
+// latent_bytes + 512 t of the page.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mla_kv_write_kernel(
     const bf16_t *__restrict__ c, int row_stride, const float *__restrict__ kidx, int n_tok, int mode,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ start_pos, int n_seqs,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ page_table, int page_stride,
-    bf16_t *__restrict__ pool, int page_elems, int n_pages, bool fp8, float inv_scale) {
+    bf16_t *__restrict__ pool, int page_elems, int n_pages, bool fp8, float inv_scale, bool token_major) {
   const int n_lat = fp8 ? kMlaDqk / 16 : kMlaDqk / 8;
   const int per_tok = n_lat + (kidx ? 32 : 0);
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void mla_kv_write_kernel(
   if (u < n_lat) {
     const bf16_t *src = c + (long)j * row_stride;
     if (!fp8) {
-      st16(page + k_page_offset(t, u * 8), ld16(src + u * 8));
+      st16(page + (token_major ? t * kMlaDqk + u * 8 : k_page_offset(t, u * 8)), ld16(src + u * 8));
     } else {
       const u32x4 a = ld16(src + u * 16), b = ld16(src + u * 16 + 8);
       u32x4 codes;
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(512) void mla_split_kernel(
         mla_unit_td(mla_swz(64 * j + lane), tt, d0);
         const int e = 16 * my_ps + tt;  // entry of the tile
         const int p = __shfl(pos1, e, 64), id = __shfl(pid1, e, 64);
-        const bf16_t *src = pool + (long)id * page_elems + (p >= 0 ? k_page_offset(p % kPage, d0) : 0);
+        const bf16_t *src = pool + (long)id * page_elems + (p >= 0 ? (p % kPage) * kMlaDqk + d0 : 0);
         __builtin_amdgcn_global_load_lds(src, buf + j * 512, 16, 0, 0);
       }
     }
@@ -685,7 +689,7 @@ hipError_t launch_mla_kv_write(const MlaKvWriteArgs &a, hipStream_t st) {
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(mla_kv_write_kernel, dim3(blocks), dim3(256), 0, st, a.c, a.row_stride, a.kidx, a.n_tok,
                      a.mode, a.cu, a.start_pos, a.n_seqs, a.ctx_len, a.page_table, a.page_stride, a.pool,
-                     a.page_elems, a.n_pages, a.fp8, a.inv_scale);
+                     a.page_elems, a.n_pages, a.fp8, a.inv_scale, a.token_major);
   return hipGetLastError();
 }
 
