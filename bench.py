@@ -107,7 +107,7 @@ def measured_peaks():
 
 
 def lm_head_sweep(w, lm8, args):
-    """The lm-head alone (ril_lm_head_logprobs) at M = 64, 1024, 8192 and 65536 normalised
+    """The lm-head alone (ril_lm_head_logprobs) at M = 64, 128, 1024, 8192 and 65536 normalised
     rows: time per launch (HIP events, no trace hook), TFLOP/s against the dtype's dense
     MFMA peak, weight-stream GB/s, and whether the first 64 rows' logprobs keep their bits
     at every M (one K order per column)."""
@@ -115,7 +115,7 @@ def lm_head_sweep(w, lm8, args):
     import torch
     import workloads as wl
     from invariant_rl_logprob_amd.session import Session
-    Ms = [64, 1024, 8192, 65536]
+    Ms = [64, 128, 1024, 8192, 65536]
     w_lm = wl.gqa_head_weights(w, device="cuda")["w_lm"]
     sess = Session(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, vocab=w.vocab,
                    d_head=w.d_head, w_lm=w_lm, max_rows=64, max_tokens=max(Ms), max_ctx=64, pool_pages=8,

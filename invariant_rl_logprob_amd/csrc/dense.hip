@@ -486,13 +486,22 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const bf16_t *__restrict__
                                                       const bf16_t *__restrict__ W, int K, int V,
                                                       const int32_t *__restrict__ target, int M,
                                                       float *__restrict__ part,
-                                                      float *__restrict__ tgt_logit, int n_vt) {
+                                                      float *__restrict__ tgt_logit, int n_vt, int paired) {
   __shared__ float red[2][4][16 * MB];
   __shared__ u32x4 lds_a[2][kLdsSteps * MB * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
-  const int tile = blockIdx.x;
-  const int m0 = blockIdx.y * 16 * MB;
+  int tile = blockIdx.x, rt = blockIdx.y;
+  if (paired) {
+    // two row tiles, one 1-D grid: workgroups 16k + x and 16k + 8 + x (x < 8) take row
+    // tiles 0 and 1 of vocabulary tile 8k + x.  Workgroups are dispatched to the 8 XCDs
+    // round-robin, so the pair shares an XCD and starts together: the second reads the
+    // weight slice from that XCD's L2.
+    tile = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    rt = (blockIdx.x >> 3) & 1;
+    if (tile >= n_vt) return;  // the grid's last group of 16 may overhang
+  }
+  const int m0 = rt * 16 * MB;
   const bf16_t *ap[MB];
   const bf16_t *wp[4];
 #pragma unroll
@@ -792,18 +801,25 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st) {
   const int n_vt = (a.V + kVocabTile - 1) / kVocabTile;
   const int mb = a.M <= 16 ? 1 : 4;
   const int n_rt = (a.M + 16 * mb - 1) / (16 * mb);
-  // Up to two row tiles the weights are read once (twice) and streamed with the
-  // nontemporal policy (measured: 192 -> 171 us at 64 rows, 369 -> 326 us at 128 rows on
-  // the 4096 x 129280 head).  Past 128 rows the 256-row kernel shares both operands
-  // through LDS.  No choice changes a column's K order or its MFMA per step.
-  if (n_rt <= 2) {
-    dim3 grid(n_vt, n_rt);
+  // One row tile: the weights are read once and streamed with the nontemporal policy
+  // (192 -> 171 us at 64 rows on the 4096 x 129280 head).  Two row tiles: the paired
+  // 1-D grid puts both tiles of a vocabulary tile on one XCD at the same time, and
+  // ordinary loads let the second read the weight slice from L2 (128 rows: 329 us on
+  // the 2-D grid with nontemporal loads, 274 paired with them, 252 paired without).
+  // Past 128 rows the 256-row kernel shares both operands through LDS.  No choice
+  // changes a column's K order or its MFMA per step.
+  if (n_rt == 2) {
+    const dim3 grid((unsigned)(16 * ((n_vt + 7) / 8)));
+    hipLaunchKernelGGL((lm_head_kernel<4, false>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V, a.target,
+                       a.M, a.part, a.tgt_logit, n_vt, 1);
+  } else if (n_rt == 1) {
+    const dim3 grid(n_vt, 1);
     if (mb == 1)
       hipLaunchKernelGGL((lm_head_kernel<1, true>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
-                         a.target, a.M, a.part, a.tgt_logit, n_vt);
+                         a.target, a.M, a.part, a.tgt_logit, n_vt, 0);
     else
       hipLaunchKernelGGL((lm_head_kernel<4, true>), grid, dim3(256), 0, st, a.Z, a.ldz, a.W, a.K, a.V,
-                         a.target, a.M, a.part, a.tgt_logit, n_vt);
+                         a.target, a.M, a.part, a.tgt_logit, n_vt, 0);
   } else {
     // many rows: 256-row tiles with both operands shared through LDS, on persistent
     // workgroups that take blocks of 4 x 8 tiles (fewer row tiles: 2 x 16 or 1 x 32)

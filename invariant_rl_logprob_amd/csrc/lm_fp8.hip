@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restr
                                                           const int32_t *__restrict__ ew, int V,
                                                           const int32_t *__restrict__ target, int M,
                                                           float *__restrict__ part,
-                                                          float *__restrict__ tgt_logit, int n_vt) {
+                                                          float *__restrict__ tgt_logit, int n_vt, int paired) {
   constexpr int R = PF + 1;                   // ring slots = K steps per chunk
   constexpr int ABLK = R * MB * 2;            // 1 KB activation blocks per chunk: (step, mb, half)
   constexpr int NE = R * MB * 16;             // row scales per chunk: (step, mb, row)
@@ -197,8 +197,14 @@ __global__ __launch_bounds__(256) void lm_head_fp8_kernel(const uint8_t *__restr
   __shared__ int32_t lds_e[2][NEB * 64];
   __shared__ int32_t lds_w[2][kF8MaxSteps];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15;
-  const int tile = ROWS_FAST ? blockIdx.y : blockIdx.x;
-  const int m0 = (ROWS_FAST ? blockIdx.x : blockIdx.y) * 16 * MB;
+  int tile = ROWS_FAST ? blockIdx.y : blockIdx.x;
+  int rt = ROWS_FAST ? blockIdx.x : blockIdx.y;
+  if (paired) {  // the bf16 head's paired 1-D grid: row tiles 0 and 1 of a vocabulary tile on one XCD
+    tile = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    rt = (blockIdx.x >> 3) & 1;
+    if (tile >= n_vt) return;
+  }
+  const int m0 = rt * 16 * MB;
   const int nk = K >> 7;
   const int rot = lm_rot(tile, nk);
   auto kidx = [&](int s) {  // the K block of step s (steps past the end re-read the last)
@@ -651,20 +657,25 @@ hipError_t launch_lm_head_fp8(const LmHeadArgs &a, hipStream_t st) {
   const int n_vt = (a.V + kVocabTile - 1) / kVocabTile;
   const int mb = a.M <= 16 ? 1 : 4;
   const int n_rt = (a.M + 16 * mb - 1) / (16 * mb);
-  // the grid choice of the bf16 head: up to two row tiles stream the weights (NT), more
-  // run the row tiles of one vocabulary tile back to back; neither changes a K order
-  if (n_rt <= 2) {
-    dim3 grid(n_vt, n_rt);
+  // the grid choice of the bf16 head: one row tile streams the weights (NT), two share
+  // each weight slice through an XCD's L2 (the paired grid, ordinary loads), more run
+  // the row tiles of one vocabulary tile back to back; none changes a K order
+  if (n_rt == 2) {
+    const dim3 grid((unsigned)(16 * ((n_vt + 7) / 8)));
+    hipLaunchKernelGGL((lm_head_fp8_kernel<4, false, false>), grid, dim3(256), 0, st, a.A8, a.ea, a.K, a.W8,
+                       a.ew, a.V, a.target, a.M, a.part, a.tgt_logit, n_vt, 1);
+  } else if (n_rt == 1) {
+    dim3 grid(n_vt, 1);
     if (mb == 1)
       hipLaunchKernelGGL((lm_head_fp8_kernel<1, true, false>), grid, dim3(256), 0, st, a.A8, a.ea, a.K, a.W8,
-                         a.ew, a.V, a.target, a.M, a.part, a.tgt_logit, n_vt);
+                         a.ew, a.V, a.target, a.M, a.part, a.tgt_logit, n_vt, 0);
     else
       hipLaunchKernelGGL((lm_head_fp8_kernel<4, true, false>), grid, dim3(256), 0, st, a.A8, a.ea, a.K, a.W8,
-                         a.ew, a.V, a.target, a.M, a.part, a.tgt_logit, n_vt);
+                         a.ew, a.V, a.target, a.M, a.part, a.tgt_logit, n_vt, 0);
   } else {
     dim3 grid(n_rt, n_vt);
     hipLaunchKernelGGL((lm_head_fp8_kernel<4, false, true>), grid, dim3(256), 0, st, a.A8, a.ea, a.K, a.W8, a.ew,
-                       a.V, a.target, a.M, a.part, a.tgt_logit, n_vt);
+                       a.V, a.target, a.M, a.part, a.tgt_logit, n_vt, 0);
   }
   return hipGetLastError();
 }
