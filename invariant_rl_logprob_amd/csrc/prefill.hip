@@ -399,12 +399,16 @@ __global__ __launch_bounds__(512) void attn_prefill2_kernel(
       __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
   };
+  // PF = NBUF - 2 tiles are copied ahead (not NBUF - 1): a lagging wave (below) still
+  // reads tile T-1 while tile T is current, so the copy issued at tile T may only take
+  // the buffer of tile T-2.
+  constexpr int PF = NBUF - 2;
   int idn[kPer];
-  for (int T = 0; T < NBUF - 1 && T < n_tiles; ++T) {
+  for (int T = 0; T < PF && T < n_tiles; ++T) {
     fetch_ids(T, idn);
     copy_tile(T, idn);
   }
-  if (NBUF - 1 < n_tiles) fetch_ids(NBUF - 1, idn);
+  if (PF < n_tiles) fetch_ids(PF, idn);
 
   // this lane's LDS byte addresses of its K and V operands in buffer 0 (the layouts of
   // attn_prefill_kernel); K operand (mb, c) and V operand (kc, db) add constant offsets
@@ -543,14 +547,14 @@ __global__ __launch_bounds__(512) void attn_prefill2_kernel(
   // wave's pieces are visible and every wave is done with tile T-1's buffer; then the copy
   // of tile T+NBUF-1.  Returns the tile's LDS byte offset.
   auto next_tile = [&](int T) {
-    const int ahead = min(NBUF - 2, n_tiles - 1 - T);
+    const int ahead = min(PF - 1, n_tiles - 1 - T);
     if (ahead >= 2) wait_vmem<2 * kPer>();
     else if (ahead == 1) wait_vmem<kPer>();
     else wait_vmem<0>();
     __syncthreads();
-    if (T + NBUF - 1 < n_tiles) {
-      copy_tile(T + NBUF - 1, idn);
-      if (T + NBUF < n_tiles) fetch_ids(T + NBUF, idn);
+    if (T + PF < n_tiles) {
+      copy_tile(T + PF, idn);
+      if (T + PF + 1 < n_tiles) fetch_ids(T + PF + 1, idn);
     }
     return (uint32_t)(T % NBUF) * (4 * kSlotB);
   };
@@ -585,23 +589,57 @@ __global__ __launch_bounds__(512) void attn_prefill2_kernel(
   };
   // Tiles wholly at or before the wave's first position (every barrier of the workgroup is
   // still taken once per tile by every wave: the two loops together run n_tiles steps).
+  // The second wave of each SIMD (waves NW/2 ..) runs half a tile behind the first: after
+  // a barrier it first finishes the value step of the previous tile, so while one wave
+  // of a SIMD is in its softmax the other issues MFMAs.  Per column the steps and their
+  // order are unchanged.
   const int n_fast = min(n_tiles, (w_min + 1) / kTile);
   int T = 0;
-  for (; T < n_fast; ++T) {
-    const uint32_t boff = next_tile(T);
-    const int t0 = T * kTile;
-    f32x4 s[2][4];
+  if (wave < NW / 2) {
+    for (; T < n_fast; ++T) {
+      const uint32_t boff = next_tile(T);
+      const int t0 = T * kTile;
+      f32x4 s[2][4];
+      bf16x8 pop[2][2];
+      float alpha[2], m_new[2], l_new[2];
+      u32x4 v[SLOTS];
+      scores(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, kbase + boff, s);
+      v_head(v, vbase + boff);  // lands while the softmax runs
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        tile_softmax<false>(s[b], t0, pos[b], cscale, m[b], l[b], pop[b], alpha[b], m_new[b], l_new[b]);
+      values(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, v, vbase + boff, pop, alpha,
+             m_new, l_new);
+      split_end(t0);
+    }
+  } else {
     bf16x8 pop[2][2];
     float alpha[2], m_new[2], l_new[2];
-    u32x4 v[SLOTS];
-    scores(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, kbase + boff, s);
-    v_head(v, vbase + boff);  // lands while the softmax runs
+    uint32_t pboff = 0;
+    for (; T < n_fast; ++T) {
+      const uint32_t boff = next_tile(T);
+      const int t0 = T * kTile;
+      if (T > 0) {  // the value step of tile T-1 (its buffer is kept while tile T is current)
+        u32x4 v[SLOTS];
+        v_head(v, vbase + pboff);
+        values(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, v, vbase + pboff, pop, alpha,
+               m_new, l_new);
+        split_end(t0 - kTile);
+      }
+      f32x4 s[2][4];
+      scores(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, kbase + boff, s);
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-      tile_softmax<false>(s[b], t0, pos[b], cscale, m[b], l[b], pop[b], alpha[b], m_new[b], l_new[b]);
-    values(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, v, vbase + boff, pop, alpha, m_new,
-           l_new);
-    split_end(t0);
+      for (int b = 0; b < 2; ++b)
+        tile_softmax<false>(s[b], t0, pos[b], cscale, m[b], l[b], pop[b], alpha[b], m_new[b], l_new[b]);
+      pboff = boff;
+    }
+    if (n_fast > 0) {
+      u32x4 v[SLOTS];
+      v_head(v, vbase + pboff);
+      values(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, v, vbase + pboff, pop, alpha,
+             m_new, l_new);
+      split_end((n_fast - 1) * kTile);
+    }
   }
   // the rest: each block alone with every mask, while the tile reaches one of its positions
   for (; T < n_tiles; ++T) {
