@@ -342,13 +342,16 @@ __global__ __launch_bounds__(512) void attn_prefill2_kernel(
   const int sp = __builtin_amdgcn_readfirstlane(start_pos[seq]);
   const int n = lane & 15, grp = lane >> 4;
   const int hh = n % G;
-  const int wtok0 = tok0 + wave * 2 * tpb;  // first token of this wave (block 0, then block 1)
+  // block b of wave w: tokens tok0 + b * NW * tpb + w * tpb .. + tpb - 1, so a segment of
+  // at most NW * tpb tokens leaves every wave's block 1 empty (those waves then run block 0
+  // alone, as many busy waves as with one block per wave)
+  auto first_tok = [&](int b) { return tok0 + b * NW * tpb + wave * tpb; };
   int pos[2];
   bool col_ok[2];
   long jrow[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int tok = wtok0 + b * tpb + n / G;
+    const int tok = first_tok(b) + n / G;
     col_ok[b] = tok < n_tok;
     jrow[b] = cu[seq] + (col_ok[b] ? tok : 0);
     pos[b] = col_ok[b] ? sp + tok : -1;
@@ -366,10 +369,13 @@ __global__ __launch_bounds__(512) void attn_prefill2_kernel(
     }
     return;
   }
-  const int w_min = sp + wtok0;  // this wave's first position
-  int w_max_b[2];                // each block's last position (< its first if none)
+  const int w_min = sp + first_tok(0);  // this wave's first position
+  int w_min_b[2], w_max_b[2];           // each block's first and last position (last < first: none)
 #pragma unroll
-  for (int b = 0; b < 2; ++b) w_max_b[b] = sp + min(wtok0 + (b + 1) * tpb, n_tok) - 1;
+  for (int b = 0; b < 2; ++b) {
+    w_min_b[b] = sp + first_tok(b);
+    w_max_b[b] = sp + min(first_tok(b) + tpb, n_tok) - 1;
+  }
   bf16x8 qop[2][KC];
 #pragma unroll
   for (int b = 0; b < 2; ++b) load_qop<D>(qop[b], q + jrow[b] * q_row_stride + (g * G + hh) * D, col_ok[b]);
@@ -595,7 +601,23 @@ __global__ __launch_bounds__(512) void attn_prefill2_kernel(
   // order are unchanged.
   const int n_fast = min(n_tiles, (w_min + 1) / kTile);
   int T = 0;
-  if (wave < NW / 2) {
+  if (w_max_b[1] < w_min_b[1]) {
+    // block 1 holds no token of the sequence (a short segment): block 0 alone
+    for (; T < n_fast; ++T) {
+      const uint32_t boff = next_tile(T);
+      const int t0 = T * kTile;
+      f32x4 s[2][4];
+      bf16x8 pop[2][2];
+      float alpha[2], m_new[2], l_new[2];
+      u32x4 v[SLOTS];
+      scores(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, kbase + boff, s);
+      v_head(v, vbase + boff);
+      tile_softmax<false>(s[0], t0, pos[0], cscale, m[0], l[0], pop[0], alpha[0], m_new[0], l_new[0]);
+      values(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, v, vbase + boff, pop, alpha,
+             m_new, l_new);
+      split_end(t0);
+    }
+  } else if (wave < NW / 2) {
     for (; T < n_fast; ++T) {
       const uint32_t boff = next_tile(T);
       const int t0 = T * kTile;
@@ -647,7 +669,7 @@ __global__ __launch_bounds__(512) void attn_prefill2_kernel(
     const int t0 = T * kTile;
     static_for<2>([&](auto bb) {
       constexpr int B = decltype(bb)::value;
-      if (t0 <= w_max_b[B] && w_max_b[B] >= w_min + B * tpb) {
+      if (t0 <= w_max_b[B] && w_max_b[B] >= w_min_b[B]) {
         f32x4 s[2][4];
         bf16x8 pop[2][2];
         float alpha[2], m_new[2], l_new[2];
