@@ -4,6 +4,10 @@
 // attn_common.h), with its states held in registers (Bitwise-consistent RL post,
 // section 2: phase consistency; section 4.2: one read path shared by prefill, decode
 // and the trainer).
+//
+// Two kernels, the same per-column arithmetic: attn_prefill2_kernel (bf16 cache: two
+// 16-column blocks per wave, each LDS operand read feeding both) and attn_prefill_kernel
+// (FP8 cache: one block per wave, the codes dequantized per operand).
 #include <type_traits>
 
 #include "attn_common.h"
@@ -12,7 +16,7 @@
 namespace ril {
 
 // ---------------------------------------------------------------------------
-// S10: prefill attention.  grid (workgroup bound, Hkv); a workgroup of NW waves covers
+// S10: prefill attention over the FP8 cache.  grid (workgroup bound, Hkv); a workgroup of NW waves covers
 // QT = NW*(16/G) consecutive query tokens of one sequence for one kv head, wave w owning
 // one block of 16 MFMA columns (16/G tokens x G heads).  The workgroup walks the 64-token
 // KV tiles of its context in order.  Each tile is copied once into LDS by direct-to-LDS
