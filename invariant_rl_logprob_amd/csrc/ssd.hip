@@ -164,44 +164,86 @@ __device__ __forceinline__ void ssd_cumsum(const float *dts, float A, int n_vali
 }
 
 // ---------------------------------------------------------------------------
-// plan: one thread walks the sequences in order
+// plan: one wave.  Sequence s's positions, tokens and chunk counts; off / done are the
+// running sums of the chunk counts in sequence order.  Lanes take 64 sequences at a time
+// and wave prefix sums give the running sums.  A sequence the grids cannot hold (only
+// with batch arrays inconsistent with the host's bounds) is dropped and adds nothing;
+// should one appear, lane 0 redoes the whole plan in order, so the plan is always that
+// of the in-order walk.
 // ---------------------------------------------------------------------------
-__global__ void ssd_plan_kernel(SsdArgs a) {
-  if (threadIdx.x != 0) return;
+struct SsdPlanRow {
+  bool ok;
+  int tok0, p0, p1, slot, n_ch, n_done;
+};
+__device__ __forceinline__ SsdPlanRow ssd_plan_row(const SsdArgs &a, int s) {
+  SsdPlanRow r;
+  int len;
+  if (a.mode == 0) {
+    r.tok0 = a.cu[s];
+    len = a.cu[s + 1] - r.tok0;
+    r.p0 = a.start_pos[s];
+  } else {
+    r.tok0 = s;
+    len = 1;
+    r.p0 = a.ctx_len[s] - 1;
+  }
+  r.ok = len >= 1 && r.p0 >= 0 && r.tok0 >= 0 && (long)r.tok0 + len <= a.n_tok && (long)r.p0 + len <= 0x7fffffffL;
+  r.slot = r.ok ? a.page_table[(long)s * a.page_stride] : -1;
+  r.p1 = r.ok ? r.p0 + len : r.p0;
+  r.n_ch = r.ok ? (r.p1 - 1) / kSsdQ - r.p0 / kSsdQ + 1 : 0;
+  r.n_done = r.ok ? r.p1 / kSsdQ - r.p0 / kSsdQ : 0;
+  return r;
+}
+__device__ __forceinline__ void ssd_plan_store(const SsdArgs &a, int s, const SsdPlanRow &r, bool ok, int off,
+                                               int done) {
   const int n = a.n_seqs;
   int32_t *plan = a.plan;
+  plan[s + 1] = off;
+  plan[n + 2 + s] = done;
+  plan[2 * n + 2 + s] = ok ? r.p0 : 0;
+  plan[3 * n + 2 + s] = ok ? r.p1 : 0;
+  plan[4 * n + 2 + s] = ok ? r.tok0 : 0;
+  plan[5 * n + 2 + s] = (ok && (unsigned)r.slot < (unsigned)a.n_slots) ? r.slot : -1;
+}
+__global__ __launch_bounds__(64) void ssd_plan_kernel(SsdArgs a) {
+  const int n = a.n_seqs, lane = threadIdx.x;
+  if (lane == 0) {
+    a.plan[0] = 0;
+    a.plan[n + 1] = 0;
+  }
+  int off0 = 0, done0 = 0;  // running sums before this group of 64
+  bool fits = true;
+  for (int base = 0; base < n && fits; base += 64) {
+    const int s = base + lane;
+    SsdPlanRow r = {false, 0, 0, 0, -1, 0, 0};
+    if (s < n) r = ssd_plan_row(a, s);
+    int ch = r.n_ch, dn = r.n_done;  // inclusive prefix sums over the group
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int uc = __shfl_up(ch, d, 64), ud = __shfl_up(dn, d, 64);
+      if (lane >= d) {
+        ch += uc;
+        dn += ud;
+      }
+    }
+    const int off = off0 + ch, done = done0 + dn;
+    fits = !__any(s < n && r.ok && (off > a.max_chunks || done > a.max_done));
+    if (fits && s < n) ssd_plan_store(a, s, r, r.ok, off, done);
+    off0 = __shfl(off, 63, 64);
+    done0 = __shfl(done, 63, 64);
+  }
+  if (fits) return;  // uniform over the wave
+  __threadfence();   // the stores above land before the in-order walk's
+  if (lane != 0) return;
   int off = 0, done = 0;
-  plan[0] = 0;
-  plan[n + 1] = 0;
   for (int s = 0; s < n; ++s) {
-    int tok0, len, p0;
-    if (a.mode == 0) {
-      tok0 = a.cu[s];
-      len = a.cu[s + 1] - tok0;
-      p0 = a.start_pos[s];
-    } else {
-      tok0 = s;
-      len = 1;
-      p0 = a.ctx_len[s] - 1;
-    }
-    bool ok = len >= 1 && p0 >= 0 && tok0 >= 0 && (long)tok0 + len <= a.n_tok && (long)p0 + len <= 0x7fffffffL;
-    int slot = ok ? a.page_table[(long)s * a.page_stride] : -1;
-    const int p1 = ok ? p0 + len : p0;
-    const int n_ch = ok ? (p1 - 1) / kSsdQ - p0 / kSsdQ + 1 : 0;
-    const int n_done = ok ? p1 / kSsdQ - p0 / kSsdQ : 0;
-    // a sequence the grids cannot hold (only with inconsistent batch arrays) is dropped
-    ok = ok && off + n_ch <= a.max_chunks && done + n_done <= a.max_done;
-    if (!ok || (unsigned)slot >= (unsigned)a.n_slots) slot = -1;
+    const SsdPlanRow r = ssd_plan_row(a, s);
+    const bool ok = r.ok && off + r.n_ch <= a.max_chunks && done + r.n_done <= a.max_done;
     if (ok) {
-      off += n_ch;
-      done += n_done;
+      off += r.n_ch;
+      done += r.n_done;
     }
-    plan[s + 1] = off;
-    plan[n + 2 + s] = done;
-    plan[2 * n + 2 + s] = ok ? p0 : 0;
-    plan[3 * n + 2 + s] = ok ? p1 : 0;
-    plan[4 * n + 2 + s] = ok ? tok0 : 0;
-    plan[5 * n + 2 + s] = slot;
+    ssd_plan_store(a, s, r, ok, off, done);
   }
 }
 
