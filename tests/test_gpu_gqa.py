@@ -236,3 +236,25 @@ def test_wide_rows_take_the_separate_merge_and_norm_and_stay_invariant():
     for i, r in enumerate(rows):
         lp, _ = c.oracle_row(r, 1)
         assert abs(dn[i, -1] - lp) <= TOL, (r, dn[i, -1], lp)
+
+
+@pytest.mark.parametrize("model", ["g4", "g8"])
+def test_prefill_segment_lengths_across_column_blocks(model):
+    """A prefill segment of n tokens fills a workgroup's two column blocks per wave in
+    every pattern (block 1 empty, partial, full; a second workgroup): n tokens of one
+    call equal n decode steps bitwise, for n around the blocks' sizes (32/G tokens per
+    wave block, 8 waves)."""
+    from gqa_case import GQACase
+    base = wl.GQA_DECODE_B64 if model == "g4" else wl.LONG_MIX.decode
+    n_max = 80
+    w = wl.scaled(base, rows=3, vocab=2100, recompute_tokens=n_max)
+    c = GQACase(w, [0, 1, 2], ctx=[n_max, 700, 1500])
+    rows = [0, 1, 2]
+    c.write_history("d", rows, n_max)
+    dec = torch.stack([c.decode_back("d", rows, back) for back in range(n_max, 0, -1)], dim=1)
+    c.write_history("p", rows, n_max)
+    for n in (80, 65, 64, 63, 40, 33, 32, 31, 17, 16, 15, 5, 1):
+        pre = c.prefill_last("p", rows, n)
+        assert np.array_equal(_bits(pre), _bits(dec[:, n_max - n:])), n
+    lp_o, _ = c.oracle_row(1, 33)
+    assert abs(float(dec[1, n_max - 33]) - lp_o) <= TOL
