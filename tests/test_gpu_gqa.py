@@ -238,14 +238,15 @@ def test_wide_rows_take_the_separate_merge_and_norm_and_stay_invariant():
         assert abs(dn[i, -1] - lp) <= TOL, (r, dn[i, -1], lp)
 
 
-@pytest.mark.parametrize("model", ["g4", "g8"])
+@pytest.mark.parametrize("model", ["g4", "g8", "g4_d64"])
 def test_prefill_segment_lengths_across_column_blocks(model):
     """A prefill segment of n tokens fills a workgroup's two column blocks per wave in
     every pattern (block 1 empty, partial, full; a second workgroup): n tokens of one
-    call equal n decode steps bitwise, for n around the blocks' sizes (32/G tokens per
-    wave block, 8 waves)."""
+    call equal n decode steps bitwise, for n around the blocks' sizes (16/G tokens per
+    wave block, 8 waves); head_dim 128 and 64."""
     from gqa_case import GQACase
-    base = wl.GQA_DECODE_B64 if model == "g4" else wl.LONG_MIX.decode
+    base = {"g4": wl.GQA_DECODE_B64, "g8": wl.LONG_MIX.decode,
+            "g4_d64": wl.scaled(wl.GQA_DECODE_B64, head_dim=64, d_head=32 * 64)}[model]
     n_max = 80
     w = wl.scaled(base, rows=3, vocab=2100, recompute_tokens=n_max)
     c = GQACase(w, [0, 1, 2], ctx=[n_max, 700, 1500])
